@@ -1,0 +1,138 @@
+"""CPU oracle for the GGUF block-quantized matmul -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product path (the HIP library in
+``gguf_block_quant_qmm_amd`` and its binding) never imports, links or runs it,
+and the oracle shares no code with that path.
+
+The arithmetic lives in ``oracle.c`` (plain C, f64 accumulation); this module
+only compiles it with gcc and marshals numpy arrays through ctypes.  See the
+header of ``oracle.c`` for what is computed and which page passage each part
+follows.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+# GGUF type ids, as the oracle's C source numbers them.
+Q4_0, Q8_0, Q4_K, Q6_K = 2, 8, 12, 14
+NAMES = {Q4_0: "Q4_0", Q8_0: "Q8_0", Q4_K: "Q4_K", Q6_K: "Q6_K"}
+BY_NAME = {v: k for k, v in NAMES.items()}
+
+_lib = None
+
+
+def build(force: bool = True, extra_flags: list[str] | None = None, out: str | None = None) -> str:
+    """Compile oracle.c into a shared library with gcc (-O2, no fast-math)."""
+    out = out or _LIB
+    if not force and os.path.exists(out) and os.path.getmtime(out) >= os.path.getmtime(_SRC):
+        return out
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", _SRC, "-o", out + ".tmp", "-lm"]
+    if extra_flags:
+        cmd[1:1] = list(extra_flags)
+    subprocess.run(cmd, check=True)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+def _bind(lib):
+    i64, vp = ctypes.c_int64, ctypes.c_void_p
+    lib.oracle_block_elems.argtypes = [ctypes.c_int]
+    lib.oracle_block_bytes.argtypes = [ctypes.c_int]
+    lib.oracle_half_to_double.argtypes = [ctypes.c_uint16]
+    lib.oracle_half_to_double.restype = ctypes.c_double
+    lib.oracle_dequant.argtypes = [ctypes.c_int, vp, i64, i64, vp]
+    lib.oracle_matmul_rows.argtypes = [ctypes.c_int, vp, i64, i64, i64, vp, i64, vp, vp, vp, vp]
+    lib.oracle_matmul.argtypes = [ctypes.c_int, vp, i64, i64, i64, vp, vp, vp, vp]
+    return lib
+
+
+def load_variant(path: str):
+    """Load a separately compiled build of oracle.c (used by the mutation test)."""
+    return _bind(ctypes.CDLL(path))
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        build(force=False)
+        _lib = _bind(ctypes.CDLL(_LIB))
+    return _lib
+
+
+def _ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+def block_elems(dtype: int, L=None) -> int:
+    return (L or lib()).oracle_block_elems(dtype)
+
+
+def block_bytes(dtype: int, L=None) -> int:
+    return (L or lib()).oracle_block_bytes(dtype)
+
+
+def blob_bytes(dtype: int, M: int, K: int, L=None) -> int:
+    bs = block_elems(dtype, L)
+    if bs == 0:
+        raise ValueError(f"unknown dtype {dtype}")
+    return M * (K // bs) * block_bytes(dtype, L)
+
+
+def half_to_double(h: int, L=None) -> float:
+    return (L or lib()).oracle_half_to_double(h)
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise ValueError(f"oracle {what} failed with code {rc}")
+
+
+def dequant(dtype: int, blob: np.ndarray, M: int, K: int, L=None) -> np.ndarray:
+    """W[M][K] in f64."""
+    blob = np.ascontiguousarray(blob, dtype=np.uint8)
+    if blob.size < blob_bytes(dtype, M, K, L):
+        raise ValueError("blob too small")
+    W = np.empty((M, K), dtype=np.float64)
+    _check((L or lib()).oracle_dequant(dtype, _ptr(blob), M, K, _ptr(W)), "dequant")
+    return W
+
+
+def matmul(dtype: int, blob: np.ndarray, M: int, K: int, X: np.ndarray, rows=None, L=None):
+    """Y[N][R] f32, Y64[N][R] f64 and S[N][R] f64 for rows R (default: all M).
+
+    X is f32 [N][K] (a 1-D x is treated as N=1).
+    """
+    blob = np.ascontiguousarray(blob, dtype=np.uint8)
+    X = np.ascontiguousarray(X, dtype=np.float32)
+    if X.ndim == 1:
+        X = X[None, :]
+    N = X.shape[0]
+    if X.shape[1] != K:
+        raise ValueError("X has the wrong K")
+    if blob.size < blob_bytes(dtype, M, K, L):
+        raise ValueError("blob too small")
+    if rows is None:
+        nrows, rows_p, rows_arr = M, None, None
+    else:
+        rows_arr = np.ascontiguousarray(rows, dtype=np.int64)
+        nrows, rows_p = rows_arr.size, _ptr(rows_arr)
+    Y = np.empty((N, nrows), dtype=np.float32)
+    Y64 = np.empty((N, nrows), dtype=np.float64)
+    S = np.empty((N, nrows), dtype=np.float64)
+    rc = (L or lib()).oracle_matmul_rows(dtype, _ptr(blob), M, K, N, _ptr(X), nrows, rows_p,
+                                         _ptr(Y), _ptr(Y64), _ptr(S))
+    _check(rc, "matmul")
+    return Y, Y64, S
+
+
+def num_threads() -> int:
+    return lib().oracle_num_threads()

@@ -1,0 +1,278 @@
+/*
+ * oracle.c -- plain, slow CPU oracle for the GGUF block-quantized matmul.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path (the HIP library and
+ * its Python binding) may link, load or call this file.  Only tests/, the
+ * smoke check in __graft_entry__.py and the cpu_baseline leg of bench.py use
+ * it.  It shares no code, header, table or constant with the HIP path.
+ *
+ * What it computes (the plain definition the method reaches):
+ *
+ *   W[m,k]  = dequant_t(blob, m, k)                       (exact in f64)
+ *   Y[n,m]  = sum_k W[m,k] * X[n,k]   accumulated in f64, sequential k,
+ *             then rounded once to f32 (round-to-nearest-even)
+ *   S[n,m]  = sum_k |W[m,k] * X[n,k]| in f64               (tolerance scale)
+ *
+ * Source of the definition: page "cera 0.5.2 src/backend/cpu.rs", section
+ * "Matrix multiplication" -- the scalar reference matmuls matmul_f32,
+ * matmul_q4_0_f32, matmul_q8_0_f32 and matmul_q4km_f32 define
+ * C = dequant(A) . B with A row-major in blocks, one block dot per step and
+ * the output overwritten (not accumulated).  Here the activation operand is
+ * stored token-major, X[N][K], and the output token-major, Y[N][M]; that is
+ * the same contraction with the operand transposed (page "cera 0.3.1
+ * src/model/gpu_lfm2.rs", batched-prefill scratch: contiguous token rows).
+ *
+ * Block formats (all little-endian; f16 is IEEE binary16, decoded exactly,
+ * subnormals included, Inf/NaN propagate):
+ *   Q8_0 (type 8,  32 weights, 34 B): d f16 @0, q int8[32] @2;   w = d*q
+ *   Q4_0 (type 2,  32 weights, 18 B): d f16 @0, qs u8[16] @2;
+ *        element e<16 is the low nibble of qs[e], e>=16 the high nibble of
+ *        qs[e-16];  w = d*(q-8)
+ *        (page "cera 0.5.2 src/backend/cpu.rs", Q4_0 weight repacking:
+ *         the nibble() helper of repack_q4_0_8x8 and the little-endian scale
+ *         read at the block start)
+ *   Q4_K (type 12, 256 weights, 144 B): d f16 @0, dmin f16 @2,
+ *        scales u8[12] @4, qs u8[128] @16.  Sub-block i = j/32, e = j%32;
+ *        q = low nibble of qs[(i/2)*32+e] if i even, high nibble if odd;
+ *        w = d*sc_i*q - dmin*m_i
+ *        (same page, repack_q4_k_8x8: nibble placement and the baked
+ *         products d*sc and dmin*mn).  The 6-bit (sc_i, m_i) packing of the
+ *        12 scale bytes is not printed on the pages (decode_q4km_scales is
+ *        only called); READING (standard GGUF k-quant packing):
+ *          i<4 : sc = s[i]&63,               m = s[i+4]&63
+ *          i>=4: sc = (s[i+4]&15)|((s[i-4]>>6)<<4),
+ *                m  = (s[i+4]>>4)|((s[i]>>6)<<4)
+ *   Q6_K (type 14, 256 weights, 210 B): ql u8[128] @0, qh u8[64] @128,
+ *        sc int8[16] @192, d f16 @208.  Only the 210-byte size is on the
+ *        pages (page "cera 0.3.1 src/model/gpu_lfm2.rs", upload_weight);
+ *        READING (standard GGUF layout): for element j,
+ *          h=j/128, r=j%128, g=r/32, l=r%32
+ *          lo4 = ql[64h+32(g&1)+l] low nibble if g<2 else high nibble
+ *          hi2 = (qh[32h+l] >> 2g) & 3
+ *          q   = lo4 | hi2<<4;       w = d*sc[j/16]*(q-32)
+ *
+ * Parity pins: hand-built blocks, the all-ones closed form, unit vectors and
+ * exact rational brute force (tests/test_oracle_pins.py).  The Q4_K scale
+ * packing and the Q6_K bit layout are a reading of the GGUF convention that
+ * no page value can confirm: for those two, "parity unpinned" against the
+ * pages; they are pinned only against the hand-built fixtures written from
+ * the same reading.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define OR_Q4_0 2
+#define OR_Q8_0 8
+#define OR_Q4_K 12
+#define OR_Q6_K 14
+
+/* ---- format geometry --------------------------------------------------- */
+
+int oracle_block_elems(int dtype) {
+    switch (dtype) {
+    case OR_Q4_0: return 32;
+    case OR_Q8_0: return 32;
+    case OR_Q4_K: return 256;
+    case OR_Q6_K: return 256;
+    default: return 0;
+    }
+}
+
+int oracle_block_bytes(int dtype) {
+    switch (dtype) {
+    case OR_Q4_0: return 18;
+    case OR_Q8_0: return 34;
+    case OR_Q4_K: return 144;
+    case OR_Q6_K: return 210;
+    default: return 0;
+    }
+}
+
+/* ---- IEEE binary16 -> double, exact ----------------------------------- */
+
+double oracle_half_to_double(uint16_t h) {
+    int sign = (h >> 15) & 1;
+    int expo = (h >> 10) & 31;
+    int frac = h & 1023;
+    double v;
+    if (expo == 0)
+        v = ldexp((double)frac, -24);               /* subnormal: frac * 2^-24 */
+    else if (expo == 31)
+        v = frac ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + frac), expo - 25); /* (1 + frac/1024) * 2^(e-15) */
+    return sign ? -v : v;
+}
+
+static double half_at(const uint8_t *p) {
+    return oracle_half_to_double((uint16_t)(p[0] | (p[1] << 8)));
+}
+
+/* ---- one block -> its weights, in f64 ---------------------------------- */
+
+static void dequant_q8_0(const uint8_t *b, double *w) {
+    double d = half_at(b);
+    for (int j = 0; j < 32; j++)
+        w[j] = d * (double)(int8_t)b[2 + j];
+}
+
+static void dequant_q4_0(const uint8_t *b, double *w) {
+    double d = half_at(b);
+    const uint8_t *qs = b + 2;
+    for (int j = 0; j < 32; j++) {
+        int q = (j < 16) ? (qs[j] & 15) : (qs[j - 16] >> 4);
+        w[j] = d * (double)(q - 8);
+    }
+}
+
+static void q4k_scale_min(const uint8_t *s, int i, int *sc, int *mn) {
+    if (i < 4) {
+        *sc = s[i] & 63;
+        *mn = s[i + 4] & 63;
+    } else {
+        *sc = (s[i + 4] & 15) | ((s[i - 4] >> 6) << 4);
+        *mn = (s[i + 4] >> 4) | ((s[i] >> 6) << 4);
+    }
+}
+
+static void dequant_q4_k(const uint8_t *b, double *w) {
+    double d = half_at(b);
+    double dmin = half_at(b + 2);
+    const uint8_t *s = b + 4;
+    const uint8_t *qs = b + 16;
+    for (int j = 0; j < 256; j++) {
+        int i = j / 32, e = j % 32;
+        int sc, mn;
+        q4k_scale_min(s, i, &sc, &mn);
+        uint8_t byte = qs[(i / 2) * 32 + e];
+        int q = (i % 2 == 0) ? (byte & 15) : (byte >> 4);
+        w[j] = d * (double)sc * (double)q - dmin * (double)mn;
+    }
+}
+
+static void dequant_q6_k(const uint8_t *b, double *w) {
+    const uint8_t *ql = b;
+    const uint8_t *qh = b + 128;
+    const int8_t *sc = (const int8_t *)(b + 192);
+    double d = half_at(b + 208);
+    for (int j = 0; j < 256; j++) {
+        int h = j / 128, r = j % 128, g = r / 32, l = r % 32;
+        uint8_t lob = ql[64 * h + 32 * (g & 1) + l];
+        int lo4 = (g < 2) ? (lob & 15) : (lob >> 4);
+        int hi2 = (qh[32 * h + l] >> (2 * g)) & 3;
+        int q = lo4 | (hi2 << 4);
+        w[j] = d * (double)sc[j / 16] * (double)(q - 32);
+    }
+}
+
+static int dequant_block(int dtype, const uint8_t *b, double *w) {
+    switch (dtype) {
+    case OR_Q8_0: dequant_q8_0(b, w); return 0;
+    case OR_Q4_0: dequant_q4_0(b, w); return 0;
+    case OR_Q4_K: dequant_q4_k(b, w); return 0;
+    case OR_Q6_K: dequant_q6_k(b, w); return 0;
+    default: return -2;
+    }
+}
+
+static int check_shape(int dtype, int64_t M, int64_t K) {
+    int bs = oracle_block_elems(dtype);
+    if (bs == 0) return -2;
+    if (M < 1 || K < bs || K % bs != 0) return -3;
+    return 0;
+}
+
+/* Row m of W: row m starts at byte m*row_bytes, row_bytes = (K/bs)*BB, and
+ * its blocks follow one another (page "cera 0.5.2 src/backend/cpu.rs",
+ * matmul_q4_0_f32: row_start = i*bytes_per_row, block_offset = row_start +
+ * bi*size_of block). */
+static int dequant_row(int dtype, const uint8_t *blob, int64_t K, int64_t m, double *out) {
+    int bs = oracle_block_elems(dtype), bb = oracle_block_bytes(dtype);
+    int64_t nb = K / bs;
+    const uint8_t *row = blob + m * nb * bb;
+    for (int64_t b = 0; b < nb; b++) {
+        int rc = dequant_block(dtype, row + b * bb, out + b * bs);
+        if (rc) return rc;
+    }
+    return 0;
+}
+
+/* ---- public entry points ----------------------------------------------- */
+
+/* W as f64 [M][K]. */
+int oracle_dequant(int dtype, const uint8_t *blob, int64_t M, int64_t K, double *W) {
+    int rc = check_shape(dtype, M, K);
+    if (rc) return rc;
+    for (int64_t m = 0; m < M; m++) {
+        rc = dequant_row(dtype, blob, K, m, W + m * K);
+        if (rc) return rc;
+    }
+    return 0;
+}
+
+/* Outputs for the listed rows only: for r in [0,nrows), m = rows[r],
+ * Y[n*nrows + r] = f32(sum_k W[m,k] X[n,k]), Y64 the f64 sum, S the f64
+ * sum of |W X|.  rows == NULL means all M rows in order (nrows == M).
+ * Y64 and S may be NULL.  Threads split the row list (OpenMP, if built
+ * with it); each output is still one sequential f64 sum over k. */
+int oracle_matmul_rows(int dtype, const uint8_t *blob, int64_t M, int64_t K, int64_t N,
+                       const float *X, int64_t nrows, const int64_t *rows,
+                       float *Y, double *Y64, double *S) {
+    int rc = check_shape(dtype, M, K);
+    if (rc) return rc;
+    if (N < 1 || nrows < 1) return -3;
+    if (rows) {
+        for (int64_t r = 0; r < nrows; r++)
+            if (rows[r] < 0 || rows[r] >= M) return -3;
+    } else if (nrows != M) {
+        return -3;
+    }
+    int err = 0;
+#pragma omp parallel
+    {
+        double *w = (double *)malloc(sizeof(double) * (size_t)K);
+        if (!w) {
+#pragma omp atomic write
+            err = -7;
+        }
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t r = 0; r < nrows; r++) {
+            if (!w) continue;
+            int64_t m = rows ? rows[r] : r;
+            if (dequant_row(dtype, blob, K, m, w)) continue;
+            for (int64_t n = 0; n < N; n++) {
+                const float *x = X + n * K;
+                double acc = 0.0, mag = 0.0;
+                for (int64_t k = 0; k < K; k++) {
+                    double p = w[k] * (double)x[k];
+                    acc += p;
+                    mag += fabs(p);
+                }
+                Y[n * nrows + r] = (float)acc;
+                if (Y64) Y64[n * nrows + r] = acc;
+                if (S) S[n * nrows + r] = mag;
+            }
+        }
+        free(w);
+    }
+    return err;
+}
+
+/* Full output Y[N][M] (token-major), with optional Y64 and S of the same shape. */
+int oracle_matmul(int dtype, const uint8_t *blob, int64_t M, int64_t K, int64_t N,
+                  const float *X, float *Y, double *Y64, double *S) {
+    return oracle_matmul_rows(dtype, blob, M, K, N, X, M, NULL, Y, Y64, S);
+}
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,351 @@
+"""Checks that pin the CPU oracle to something other than itself.
+
+Each ``pin_*`` function takes an oracle library handle (``None`` = the normal
+build) and raises AssertionError on a mismatch, so that the same checks can
+run against deliberately broken builds of the oracle (test_oracle_mutants).
+
+  pin_golden          hand-built blocks with design values (tests/golden/)
+  pin_unit_vectors    x = e_k on small blobs made of those blocks: y = W[:, k]
+  pin_closed_form     x = all ones: y = dequantized row sums, computed from
+                      the block fields with integer sums (no element placement)
+  pin_bruteforce      tiny random shapes against an exact rational result
+                      from a separately written decoder (fractions.Fraction)
+  pin_invariants      GEMM column == GEMV, 2x scales -> 2x output, row
+                      permutation, power-of-two scaling of x, additivity
+  pin_half            f16 decoding against Python's own binary16 unpacking
+  pin_sizes           block sizes and the page's ~205 MiB Q6_K head
+"""
+from __future__ import annotations
+
+import os
+import struct
+from fractions import Fraction
+
+import numpy as np
+
+import oracle
+from qmm_inputs import make_blob, make_x, rng_for
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+DTYPES = (oracle.Q4_0, oracle.Q8_0, oracle.Q4_K, oracle.Q6_K)
+
+
+# ----------------------------------------------------------------- fixtures
+
+def _expand(tokens, conv):
+    out = []
+    for t in tokens:
+        if "*" in t:
+            v, n = t.split("*")
+            out += [conv(v)] * int(n)
+        else:
+            out.append(conv(t))
+    return out
+
+
+def _num(s: str) -> float:
+    s = s.strip()
+    if s.lstrip("-").startswith("0x"):
+        return float.fromhex(s)
+    return float(s)
+
+
+def load_golden(dtype_name: str):
+    """[(record name, block bytes, expected weights)] from tests/golden/<dtype>_blocks.txt."""
+    path = os.path.join(GOLDEN, f"{dtype_name.lower()}_blocks.txt")
+    recs, cur, key = [], None, None
+    with open(path) as f:
+        for raw in f:
+            line = raw.rstrip("\n")
+            if not line.strip() or line.lstrip().startswith("#"):
+                continue
+            if line.startswith("["):
+                cur = {"name": line.strip("[] "), "block": [], "expect": []}
+                recs.append(cur)
+                continue
+            if line.startswith("block:"):
+                key, line = "block", line[len("block:"):]
+            elif line.startswith("expect:"):
+                key, line = "expect", line[len("expect:"):]
+            cur[key] += line.split()
+    out = []
+    for r in recs:
+        blk = bytes(_expand(r["block"], lambda s: int(s, 16)))
+        exp = np.array(_expand(r["expect"], _num), dtype=np.float64)
+        out.append((r["name"], blk, exp))
+    return out
+
+
+def pin_golden(L=None):
+    for dt in DTYPES:
+        name = oracle.NAMES[dt]
+        recs = load_golden(name)
+        assert recs, f"no fixtures for {name}"
+        for rname, blk, exp in recs:
+            bs, bb = oracle.block_elems(dt, L), oracle.block_bytes(dt, L)
+            assert len(blk) == bb, f"{rname}: fixture block is {len(blk)} bytes, format says {bb}"
+            assert exp.size == bs, f"{rname}: {exp.size} expected values for a {bs}-weight block"
+            W = oracle.dequant(dt, np.frombuffer(blk, np.uint8), 1, bs, L=L)[0]
+            bad = np.nonzero(W != exp)[0]
+            assert bad.size == 0, f"{rname}: weight {bad[0]} decodes to {W[bad[0]]}, design value {exp[bad[0]]}"
+
+
+def pin_unit_vectors(L=None):
+    """Blobs of 3 rows made of the fixture blocks in rotated order; X = I_K."""
+    for dt in DTYPES:
+        recs = load_golden(oracle.NAMES[dt])
+        bs = oracle.block_elems(dt, L)
+        nblk = 2 if bs == 256 else 4                       # K = 512 or 128
+        K, M = nblk * bs, 3
+        rows_b, rows_w = [], []
+        for m in range(M):
+            pick = [recs[(m + b) % len(recs)] for b in range(nblk)]
+            rows_b.append(b"".join(p[1] for p in pick))
+            rows_w.append(np.concatenate([p[2] for p in pick]))
+        blob = np.frombuffer(b"".join(rows_b), np.uint8)
+        W = np.stack(rows_w)
+        Y, _, _ = oracle.matmul(dt, blob, M, K, np.eye(K, dtype=np.float32), L=L)
+        assert Y.shape == (K, M)
+        bad = np.argwhere(Y.T != W.astype(np.float32))
+        assert bad.size == 0, f"{oracle.NAMES[dt]}: y[{bad[0][0]}] for x = e_{bad[0][1]} is wrong"
+
+
+# --------------------------------------------------------------- closed form
+
+def _f16(a: np.ndarray) -> np.ndarray:
+    return a.copy().view("<f2").astype(np.float64).reshape(-1)
+
+
+def closed_form_row_sums(dt: int, blob: np.ndarray, M: int, K: int) -> np.ndarray:
+    """y = W . ones, from the block fields: scale x (sum of integer codes)."""
+    bs, bb = {oracle.Q4_0: (32, 18), oracle.Q8_0: (32, 34),
+              oracle.Q4_K: (256, 144), oracle.Q6_K: (256, 210)}[dt]
+    nb = K // bs
+    B = blob[: M * nb * bb].reshape(M, nb, bb)
+    if dt == oracle.Q8_0:
+        d = _f16(np.ascontiguousarray(B[:, :, 0:2])).reshape(M, nb)
+        qsum = B[:, :, 2:34].view(np.int8).astype(np.int64).sum(axis=2)
+        per_block = d * qsum
+    elif dt == oracle.Q4_0:
+        d = _f16(np.ascontiguousarray(B[:, :, 0:2])).reshape(M, nb)
+        qs = B[:, :, 2:18].astype(np.int64)
+        qsum = (qs & 15).sum(axis=2) + (qs >> 4).sum(axis=2)
+        per_block = d * (qsum - 8 * 32)
+    elif dt == oracle.Q4_K:
+        d = _f16(np.ascontiguousarray(B[:, :, 0:2])).reshape(M, nb)
+        dmin = _f16(np.ascontiguousarray(B[:, :, 2:4])).reshape(M, nb)
+        s = B[:, :, 4:16].astype(np.int64)
+        sc = np.empty((M, nb, 8), np.int64)
+        mn = np.empty((M, nb, 8), np.int64)
+        sc[:, :, 0:4] = s[:, :, 0:4] & 63
+        mn[:, :, 0:4] = s[:, :, 4:8] & 63
+        sc[:, :, 4:8] = (s[:, :, 8:12] & 15) | ((s[:, :, 0:4] >> 6) << 4)
+        mn[:, :, 4:8] = (s[:, :, 8:12] >> 4) | ((s[:, :, 4:8] >> 6) << 4)
+        chunks = B[:, :, 16:144].astype(np.int64).reshape(M, nb, 4, 32)
+        qsum = np.empty((M, nb, 8), np.int64)
+        qsum[:, :, 0::2] = (chunks & 15).sum(axis=3)       # even sub-blocks: low nibbles
+        qsum[:, :, 1::2] = (chunks >> 4).sum(axis=3)       # odd sub-blocks: high nibbles
+        per_block = (d[:, :, None] * sc * qsum - 32 * dmin[:, :, None] * mn).sum(axis=2)
+    elif dt == oracle.Q6_K:
+        ql = B[:, :, 0:128].astype(np.int64).reshape(M, nb, 2, 2, 32)     # [h][c][l]
+        qh = B[:, :, 128:192].astype(np.int64).reshape(M, nb, 2, 32)      # [h][l]
+        sc = B[:, :, 192:208].view(np.int8).astype(np.int64).reshape(M, nb, 2, 4, 2)  # [h][g][l/16]
+        d = _f16(np.ascontiguousarray(B[:, :, 208:210])).reshape(M, nb)
+        lo = np.stack([ql[:, :, :, 0] & 15, ql[:, :, :, 1] & 15,
+                       ql[:, :, :, 0] >> 4, ql[:, :, :, 1] >> 4], axis=3)  # [h][g][l]
+        hi = np.stack([(qh >> (2 * g)) & 3 for g in range(4)], axis=3)   # [h][g][l]
+        q = (lo + 16 * hi).reshape(M, nb, 2, 4, 2, 16).sum(axis=5)        # per 16-group
+        per_block = d * (sc * (q - 32 * 16)).sum(axis=(2, 3, 4))
+    else:
+        raise ValueError(dt)
+    out = np.zeros(M, np.float64)
+    for b in range(nb):            # block terms are exact multiples of 2^-24: any order is exact
+        out += per_block[:, b]
+    return out
+
+
+def pin_closed_form(L=None):
+    for i, dt in enumerate(DTYPES):
+        bs = oracle.block_elems(dt, L)
+        M, K = 37, 8 * bs
+        blob = make_blob(dt, M, K, rng_for(900 + i, 0))
+        _, Y64, _ = oracle.matmul(dt, blob, M, K, np.ones((1, K), np.float32), L=L)
+        ref = closed_form_row_sums(dt, blob, M, K)
+        bad = np.nonzero(Y64[0] != ref)[0]
+        assert bad.size == 0, (f"{oracle.NAMES[dt]}: row {bad[0]} sum {Y64[0][bad[0]]!r} != "
+                               f"closed form {ref[bad[0]]!r}")
+
+
+# ---------------------------------------------------------------- brute force
+
+def _h(b: bytes, off: int) -> Fraction:
+    return Fraction(struct.unpack("<e", b[off:off + 2])[0])
+
+
+def exact_weights(dt: int, blk: bytes) -> list:
+    """One block -> its weights as exact rationals; written independently of oracle.c."""
+    if dt == oracle.Q8_0:
+        d = _h(blk, 0)
+        return [d * v for v in struct.unpack("<32b", blk[2:34])]
+    if dt == oracle.Q4_0:
+        d = _h(blk, 0)
+        lows = [(c & 0x0F) - 8 for c in blk[2:18]]
+        highs = [(c >> 4) - 8 for c in blk[2:18]]
+        return [d * v for v in lows + highs]
+    if dt == oracle.Q4_K:
+        d, dmin = _h(blk, 0), _h(blk, 2)
+        s = blk[4:16]
+        sc, mn = [], []
+        for i in range(8):
+            if i < 4:
+                sc.append(s[i] % 64)
+                mn.append(s[i + 4] % 64)
+            else:
+                sc.append(s[i + 4] % 16 + 16 * (s[i - 4] // 64))
+                mn.append(s[i + 4] // 16 + 16 * (s[i] // 64))
+        w = []
+        for i in range(8):
+            chunk = blk[16 + 32 * (i // 2): 16 + 32 * (i // 2) + 32]
+            for c in chunk:
+                q = c % 16 if i % 2 == 0 else c // 16
+                w.append(d * sc[i] * q - dmin * mn[i])
+        return w
+    if dt == oracle.Q6_K:
+        ql, qh = blk[0:128], blk[128:192]
+        sc = struct.unpack("<16b", blk[192:208])
+        d = _h(blk, 208)
+        w = [None] * 256
+        for h in range(2):
+            for g in range(4):
+                for l in range(32):
+                    byte = ql[64 * h + 32 * (g % 2) + l]
+                    lo = byte % 16 if g < 2 else byte // 16
+                    hi = (qh[32 * h + l] // (4 ** g)) % 4
+                    j = 128 * h + 32 * g + l
+                    w[j] = d * sc[j // 16] * (lo + 16 * hi - 32)
+        return w
+    raise ValueError(dt)
+
+
+def round_f32(v: Fraction) -> np.float32:
+    """Correctly rounded (nearest, ties to even) f32 of an exact rational."""
+    f = np.float32(float(v))
+    cands = {f, np.nextafter(f, np.float32(np.inf)), np.nextafter(f, np.float32(-np.inf))}
+    best = min(cands, key=lambda c: (abs(Fraction(float(c)) - v),
+                                     int(np.array(c, np.float32).view(np.uint32)) & 1))
+    return np.float32(best)
+
+
+def pin_bruteforce(L=None):
+    shapes = [(1, 1), (3, 2), (5, 4), (8, 3)]
+    for i, dt in enumerate(DTYPES):
+        bs, bb = oracle.block_elems(dt, L), oracle.block_bytes(dt, L)
+        for j, (M, N) in enumerate(shapes):
+            K = 2 * bs if bs == 256 else 8 * bs
+            blob = make_blob(dt, M, K, rng_for(950 + i, j))
+            X = make_x(N, K, rng_for(950 + i, 100 + j))
+            Y, Y64, S = oracle.matmul(dt, blob, M, K, X, L=L)
+            raw = blob.tobytes()
+            nb = K // bs
+            for m in range(M):
+                w = []
+                for b in range(nb):
+                    off = (m * nb + b) * bb
+                    w += exact_weights(dt, raw[off:off + bb])
+                for n in range(N):
+                    xs = [Fraction(float(v)) for v in X[n]]
+                    exact = sum((wk * xk for wk, xk in zip(w, xs)), Fraction(0))
+                    mag = sum((abs(wk * xk) for wk, xk in zip(w, xs)), Fraction(0))
+                    bound = Fraction(K) * Fraction(2) ** -53 * mag
+                    err = abs(Fraction(float(Y64[n, m])) - exact)
+                    assert err <= bound, (f"{oracle.NAMES[dt]} M={M} N={N}: y[{n},{m}] f64 off by "
+                                          f"{float(err):.3g} > {float(bound):.3g}")
+                    assert abs(Fraction(float(S[n, m])) - mag) <= bound, "S is not sum |w x|"
+                    want = round_f32(exact)
+                    if Y[n, m] != want:
+                        # allowed only when the exact value sits within the f64 bound of a tie
+                        lo = min(Y[n, m], want)
+                        mid = (Fraction(float(lo)) + Fraction(float(max(Y[n, m], want)))) / 2
+                        assert abs(mid - exact) <= bound, (f"{oracle.NAMES[dt]}: y[{n},{m}] = {Y[n, m]!r}, "
+                                                           f"correctly rounded {want!r}")
+
+
+# ---------------------------------------------------------------- invariants
+
+def _double_scales(dt: int, blob: np.ndarray, M: int, K: int) -> np.ndarray:
+    """Blob with every f16 scale (d, and dmin for Q4_K) multiplied by 2."""
+    bs, bb = {oracle.Q4_0: (32, 18), oracle.Q8_0: (32, 34),
+              oracle.Q4_K: (256, 144), oracle.Q6_K: (256, 210)}[dt]
+    B = blob.copy().reshape(-1, bb)
+    offs = {oracle.Q4_0: [0], oracle.Q8_0: [0], oracle.Q4_K: [0, 2], oracle.Q6_K: [208]}[dt]
+    for o in offs:
+        h = np.ascontiguousarray(B[:, o:o + 2]).view("<f2").reshape(-1)
+        h2 = (h.astype(np.float32) * 2).astype("<f2")
+        assert np.all(h2.astype(np.float64) == 2 * h.astype(np.float64)), "doubling must stay exact"
+        B[:, o:o + 2] = h2.view(np.uint8).reshape(-1, 2)
+    return B.reshape(-1)
+
+
+def pin_invariants(L=None):
+    for i, dt in enumerate(DTYPES):
+        bs = oracle.block_elems(dt, L)
+        M, K, N = 11, 4 * bs, 5
+        blob = make_blob(dt, M, K, rng_for(970 + i, 0))
+        X = make_x(N, K, rng_for(970 + i, 1))
+        Y, Y64, S = oracle.matmul(dt, blob, M, K, X, L=L)
+        name = oracle.NAMES[dt]
+        # GEMM column n is the GEMV on X[n]
+        for n in range(N):
+            y1, y164, _ = oracle.matmul(dt, blob, M, K, X[n], L=L)
+            assert np.array_equal(y164[0], Y64[n]), f"{name}: GEMM column {n} != GEMV"
+        # doubling every scale doubles y exactly
+        _, Yd, _ = oracle.matmul(dt, _double_scales(dt, blob, M, K), M, K, X, L=L)
+        assert np.array_equal(Yd, 2 * Y64), f"{name}: 2x scales did not give 2x output"
+        # power-of-two scaling of x is exact
+        _, Yx, _ = oracle.matmul(dt, blob, M, K, X * np.float32(0.25), L=L)
+        assert np.array_equal(Yx, 0.25 * Y64), f"{name}: y(x/4) != y(x)/4"
+        # additivity within the f64 bound
+        X2 = make_x(N, K, rng_for(970 + i, 2))
+        _, Ya, Sa = oracle.matmul(dt, blob, M, K, X2, L=L)
+        _, Ys, _ = oracle.matmul(dt, blob, M, K, (X.astype(np.float64) + X2).astype(np.float32), L=L)
+        Xs = (X.astype(np.float64) + X2).astype(np.float32)
+        rnd = Xs.astype(np.float64) - (X.astype(np.float64) + X2)       # rounding of the sum
+        assert np.all(np.abs(rnd) <= np.abs(Xs) * 2.0 ** -24)
+        # |y(X1+X2) - y(X1) - y(X2)| <= |W| |rnd| + f64 error
+        Wabs = np.abs(oracle.dequant(dt, blob, M, K, L=L))
+        lim = (np.abs(rnd) @ Wabs.T) + 4 * K * 2.0 ** -53 * (S + Sa + (np.abs(Xs) @ Wabs.T))
+        assert np.all(np.abs(Ys - Y64 - Ya) <= lim), f"{name}: not additive in x"
+        # permuting rows of the blob permutes y
+        bb = oracle.block_bytes(dt, L)
+        perm = np.random.default_rng(7).permutation(M)
+        pblob = blob.reshape(M, -1)[perm].reshape(-1)
+        assert pblob.size == M * (K // bs) * bb
+        _, Yp, _ = oracle.matmul(dt, pblob, M, K, X, L=L)
+        assert np.array_equal(Yp, Y64[:, perm]), f"{name}: row permutation not followed"
+        # row subsets give the same numbers as the full call
+        rows = [M - 1, 0, 5]
+        _, Yr, _ = oracle.matmul(dt, blob, M, K, X, rows=rows, L=L)
+        assert np.array_equal(Yr, Y64[:, rows]), f"{name}: row-subset call differs"
+
+
+def pin_half(L=None):
+    for h in list(range(0, 0x10000, 97)) + [0x0000, 0x0001, 0x03FF, 0x0400, 0x3C00, 0x7BFF,
+                                              0x8000, 0x8001, 0xC000, 0xFBFF, 0x7C00, 0xFC00]:
+        want = struct.unpack("<e", struct.pack("<H", h))[0]
+        got = oracle.half_to_double(h, L)
+        if want != want:
+            assert got != got, f"f16 {h:#06x} should be NaN"
+        else:
+            assert got == want and np.signbit(got) == np.signbit(want), f"f16 {h:#06x}: {got!r} != {want!r}"
+
+
+def pin_sizes(L=None):
+    assert [oracle.block_bytes(d, L) for d in DTYPES] == [18, 34, 144, 210]
+    assert [oracle.block_elems(d, L) for d in DTYPES] == [32, 32, 256, 256]
+    # tied Q6_K head, hidden size 2048 x vocab 128256, "~205 MiB" on the page
+    head = oracle.blob_bytes(oracle.Q6_K, 128256, 2048, L)
+    assert head == 215_470_080 and round(head / 2**20) == 205
+
+
+ALL_PINS = [pin_golden, pin_unit_vectors, pin_closed_form, pin_bruteforce, pin_invariants,
+            pin_half, pin_sizes]

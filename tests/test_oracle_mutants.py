@@ -1,0 +1,67 @@
+"""The pins must catch plausible mistakes in the oracle.
+
+Each case below plants one mistake in a copy of oracle.c (a dropped term, a
+wrong sign, index, shift or nibble half, a transposed operand), builds it
+with gcc into a temporary library and checks that at least one pin fails.
+CPU only; the oracle's own build is never touched.
+"""
+import os
+import subprocess
+import tempfile
+
+import pytest
+
+import oracle
+import pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+MUTANTS = {
+    "q4_0_offset": ("w[j] = d * (double)(q - 8);", "w[j] = d * (double)(q - 7);"),
+    "q4_0_nibble_halves": ("(j < 16) ? (qs[j] & 15) : (qs[j - 16] >> 4)", "(j < 16) ? (qs[j] >> 4) : (qs[j - 16] & 15)"),
+    "q8_0_unsigned": ("(double)(int8_t)b[2 + j]", "(double)(uint8_t)b[2 + j]"),
+    "q8_0_off_by_one": ("(int8_t)b[2 + j]", "(int8_t)b[1 + j]"),
+    "q4_k_scale_mask": ("*sc = s[i] & 63;", "*sc = s[i] & 31;"),
+    "q4_k_high_bits": ("*sc = (s[i + 4] & 15) | ((s[i - 4] >> 6) << 4);", "*sc = (s[i + 4] & 15) | ((s[i - 4] >> 6) << 5);"),
+    "q4_k_min_from_scale_byte": ("*mn = (s[i + 4] >> 4) | ((s[i] >> 6) << 4);", "*mn = (s[i + 4] >> 4) | ((s[i - 4] >> 6) << 4);"),
+    "q4_k_min_sign": ("- dmin * (double)mn", "+ dmin * (double)mn"),
+    "q4_k_nibble_parity": ("int q = (i % 2 == 0) ? (byte & 15) : (byte >> 4);", "int q = (i % 2 == 1) ? (byte & 15) : (byte >> 4);"),
+    "q4_k_chunk": ("qs[(i / 2) * 32 + e]", "qs[(i % 4) * 32 + e]"),
+    "q6_k_nibble_groups": ("int lo4 = (g < 2) ?", "int lo4 = (g < 1) ?"),
+    "q6_k_qh_shift": ("(qh[32 * h + l] >> (2 * g)) & 3", "(qh[32 * h + l] >> g) & 3"),
+    "q6_k_ql_half": ("ql[64 * h + 32 * (g & 1) + l]", "ql[32 * h + 32 * (g & 1) + l]"),
+    "q6_k_subscale": ("sc[j / 16]", "sc[j / 32]"),
+    "q6_k_offset": ("(double)(q - 32)", "(double)(q - 31)"),
+    "half_exponent": ("ldexp((double)(1024 + frac), expo - 25)", "ldexp((double)(1024 + frac), expo - 24)"),
+    "half_subnormal": ("ldexp((double)frac, -24)", "ldexp((double)frac, -25)"),
+    "row_offset": ("blob + m * nb * bb", "blob + m * nb * (bb - 2)"),
+    "transposed_x": ("const float *x = X + n * K;", "const float *x = X + n;"),
+    "dropped_term": ("for (int64_t k = 0; k < K; k++) {", "for (int64_t k = 1; k < K; k++) {"),
+    "magnitude_signed": ("mag += fabs(p);", "mag += p;"),
+    "f32_rounding": ("Y[n * nrows + r] = (float)acc;", "Y[n * nrows + r] = (float)(acc * (1.0 + 0x1p-23));"),
+}
+
+
+@pytest.fixture(scope="module")
+def source():
+    with open(SRC) as f:
+        return f.read()
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, source, tmp_path):
+    old, new = MUTANTS[name]
+    assert source.count(old) == 1, f"mutation site for {name} not found exactly once"
+    src = tmp_path / "oracle_mutant.c"
+    src.write_text(source.replace(old, new))
+    lib = tmp_path / "liboracle_mutant.so"
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", str(src), "-o", str(lib), "-lm"],
+                   check=True)
+    L = oracle.load_variant(str(lib))
+    caught = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(L)
+        except (AssertionError, ValueError, IndexError):
+            caught.append(pin.__name__)
+    assert caught, f"no pin caught the planted mistake {name!r}"
