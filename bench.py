@@ -1,0 +1,293 @@
+#!/usr/bin/env python3
+"""Benchmark of the GGUF block-quantized matmul on one MI355X.
+
+Metric: decode GEMV weight GB/s (share of HBM peak) + prefill GEMM TFLOP/s at
+N = 512.
+
+One step = the decode GEMVs of one LLaMA-8B layer in Q4_0 (q_proj 4096x4096,
+gate 14336x4096, up 14336x4096, down 4096x14336; x f32 ~ N(0,1)), each called
+through qmm_gemm with N = 1 (path selection -> the f32 GEMV).  `value` is the
+step's weight bytes over its measured GPU time.  Weight copies are rotated so
+that more than 1 GiB of distinct weights is cycled (more than the 256 MB
+last-level cache): every step streams its weights from HBM.  Inputs are
+resident in HBM before timing starts.
+
+After the decode loop the same number of steps of the Q4_K prefill GEMM
+(14336x4096, N = 512 tokens, f16 matrix cores) is timed and reported under
+"prefill_gemm".  The CPU oracle is timed on the host cores on a bounded
+sample of the same workloads ("cpu_baseline").
+
+Kernel durations come from HIP events recorded on the stream the kernels run
+on (torch's current stream), around every launch.
+
+Extra: ``--sweep`` prints one JSON line per (workload, N) for every
+configuration of the workload table (C1-C5) instead of the main line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+F16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense f16 matrix cores, TFLOP/s
+ROTATE_BYTES = 1 << 30
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gguf_block_quant_qmm_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(name: str, launches_per_unit: int = 1):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "counters.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(name)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle time budget per leg")
+    ap.add_argument("--sweep", action="store_true", help="per-config table instead of the main line")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(row sharding is described in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gguf_block_quant_qmm_amd as q
+    from qmm_inputs import WORKLOADS, make_blob, make_x, rng_for
+
+    q.lib()  # fail loudly if the HIP library is missing
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    props = torch.cuda.get_device_properties(0)
+
+    if args.sweep:
+        return sweep(args, q, np, torch, dev, WORKLOADS, make_blob, make_x, rng_for)
+
+    # ---------------------------------------------------------------- decode
+    layer = [("q_proj", 2, 0), ("gate", 3, 0), ("up", 3, 1), ("down", 4, 0)]
+    mats = []
+    for name, wid, tid in layer:
+        _, dt, M, K, _ = WORKLOADS[wid]
+        blob = make_blob(dt, M, K, rng_for(wid, tid))
+        mats.append((name, dt, M, K, torch.from_numpy(blob).to(dev)))
+    step_bytes = sum(m[4].numel() for m in mats)
+    R = -(-ROTATE_BYTES // step_bytes)
+    copies = [[m[4]] + [m[4].clone() for _ in range(R - 1)] for m in mats]
+    xs = [torch.from_numpy(make_x(1, m[3], rng_for(2, 1001 + i))).to(dev) for i, m in enumerate(mats)]
+    ys = [torch.empty((1, m[2]), device=dev) for m in mats]
+    stream = torch.cuda.current_stream()
+
+    def decode_step(s, evs=None):
+        c = s % R
+        for i, (name, dt, M, K, _) in enumerate(mats):
+            if evs is not None:
+                evs[i].record(stream)
+            q.qmm_gemm(copies[i][c], dt, M, K, 1, xs[i], ys[i], stream=stream)
+        if evs is not None:
+            evs[len(mats)].record(stream)
+
+    for s in range(args.warmup):
+        decode_step(s)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(mats) + 1)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        decode_step(args.warmup + s, ev[s])
+    torch.cuda.synchronize()
+    wall_dec = time.perf_counter() - t0
+    kern_ms = [sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)) for i in range(len(mats))]
+    span_ms = sum(ev[s][0].elapsed_time(ev[s][len(mats)]) for s in range(args.steps))
+    dec_bytes_total = step_bytes * args.steps
+    value = dec_bytes_total / (span_ms * 1e-3) / 1e9
+    kern_total_ms = sum(kern_ms)
+    avg_launch_us = kern_total_ms * 1e3 / (args.steps * len(mats))
+    achieved = dec_bytes_total / (kern_total_ms * 1e-3) / 1e9
+    traffic = load_traffic("gemv_q4_0_decode_layer")
+    per_matrix = {mats[i][0]: {"us": kern_ms[i] * 1e3 / args.steps,
+                               "GB/s": mats[i][4].numel() / (kern_ms[i] * 1e-3 / args.steps) / 1e9}
+                  for i in range(len(mats))}
+
+    # --------------------------------------------------------------- prefill
+    _, pdt, PM, PK, _ = WORKLOADS[6]
+    PN = 512
+    pblob = torch.from_numpy(make_blob(pdt, PM, PK, rng_for(6, 0))).to(dev)
+    PR = -(-ROTATE_BYTES // pblob.numel())
+    pcopies = [pblob] + [pblob.clone() for _ in range(PR - 1)]
+    PX = torch.from_numpy(make_x(PN, PK, rng_for(6, 1000 + PN))).to(dev)
+    PY = torch.empty((PN, PM), device=dev)
+    for s in range(args.warmup):
+        q.qmm_gemm(pcopies[s % PR], pdt, PM, PK, PN, PX, PY, stream=stream)
+    torch.cuda.synchronize()
+    pev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        pev[s][0].record(stream)
+        q.qmm_gemm(pcopies[(args.warmup + s) % PR], pdt, PM, PK, PN, PX, PY, stream=stream)
+        pev[s][1].record(stream)
+    torch.cuda.synchronize()
+    wall_pre = time.perf_counter() - t0
+    pre_ms = sum(a.elapsed_time(b) for a, b in pev)
+    flops = 2.0 * PM * PN * PK
+    tflops = flops * args.steps / (pre_ms * 1e-3) / 1e12
+    ptraffic = load_traffic("gemm_q4_k_n512")
+
+    out = {
+        "metric": "decode GEMV weight GB/s (% HBM peak) + prefill GEMM TFLOP/s at N=512",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round((wall_dec + wall_pre) * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "llama8b decode layer, Q4_0 GEMVs q_proj 4096x4096 + gate/up 14336x4096 + down "
+                        "4096x14336, N=1, x f32 ~ N(0,1), seed 0",
+            "weight_bytes_per_step": step_bytes,
+            "rotation_copies": R,
+            "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+            "decode_ms_per_step": round(span_ms / args.steps, 5),
+            "per_matrix": per_matrix,
+            "gpu": props.name,
+            "cus": props.multi_processor_count,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "qmm::gemv_kernel<Q4_0>",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "avg_launch_us": round(avg_launch_us, 3),
+            "algorithmic_bytes_per_launch": step_bytes / len(mats),
+        },
+        "prefill_gemm": {
+            "workload": "Q4_K 14336x4096, N=512 tokens, X f32 ~ N(0,1), f16 matrix cores, f32 accumulate",
+            "tflops": round(tflops, 2),
+            "ms_per_call": round(pre_ms / args.steps, 5),
+            "rotation_copies": PR,
+            "roofline": {
+                "bound": "mfma",
+                "kernel": "qmm::gemm_kernel<Q4_K,128,128>",
+                "achieved": round(tflops, 2),
+                "peak": F16_MFMA_PEAK_TFLOPS,
+                "unit": "TFLOP/s",
+                "frac": round(tflops / F16_MFMA_PEAK_TFLOPS, 4),
+                "traffic": ptraffic,
+                "avg_launch_us": round(pre_ms * 1e3 / args.steps, 3),
+                "algorithmic_flops_per_launch": flops,
+            },
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args, np, mats, WORKLOADS, make_blob, make_x, rng_for, step_bytes)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(args, np, mats, WORKLOADS, make_blob, make_x, rng_for, step_bytes):
+    """The oracle, as it stands, on the host cores: whole decode layers
+    (same shapes and seeds) repeated for about --cpu-seconds, plus a row
+    sample of the N=512 prefill GEMM."""
+    import oracle
+    host = []
+    for i, (name, dt, M, K, blob_d) in enumerate(mats):
+        host.append((dt, M, K, blob_d.cpu().numpy(), make_x(1, K, rng_for(2, 1001 + i))))
+    passes, t0 = 0, time.perf_counter()
+    while True:
+        for dt, M, K, blob, x in host:
+            oracle.matmul(dt, blob, M, K, x)
+        passes += 1
+        if time.perf_counter() - t0 >= args.cpu_seconds:
+            break
+    dt_dec = time.perf_counter() - t0
+    _, pdt, PM, PK, _ = WORKLOADS[6]
+    pblob = make_blob(pdt, PM, PK, rng_for(6, 0))
+    PX = make_x(512, PK, rng_for(6, 1512))
+    rows, t0 = 0, time.perf_counter()
+    while True:
+        oracle.matmul(pdt, pblob, PM, PK, PX, rows=np.arange(rows, rows + 64) % PM)
+        rows += 64
+        if time.perf_counter() - t0 >= args.cpu_seconds:
+            break
+    dt_pre = time.perf_counter() - t0
+    return {
+        "value": round(step_bytes * passes / dt_dec / 1e9, 4),
+        "unit": "GB/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"{passes} whole decode layers (4 Q4_0 GEMVs, same shapes and seeds) in {dt_dec:.1f} s",
+        "prefill_gemm_tflops": round(2.0 * rows * 512 * PK / dt_pre / 1e12, 6),
+        "prefill_sample": f"{rows} of {PM} rows x 512 tokens of the Q4_K GEMM in {dt_pre:.1f} s",
+    }
+
+
+def sweep(args, q, np, torch, dev, WORKLOADS, make_blob, make_x, rng_for):
+    stream = torch.cuda.current_stream()
+    for wid in sorted(WORKLOADS):
+        label, dt, M, K, ns = WORKLOADS[wid]
+        blob = torch.from_numpy(make_blob(dt, M, K, rng_for(wid, 0))).to(dev)
+        R = max(1, -(-ROTATE_BYTES // blob.numel()))
+        copies = [blob] + [blob.clone() for _ in range(R - 1)]
+        for N in ns:
+            X = torch.from_numpy(make_x(N, K, rng_for(wid, 1000 + N))).to(dev)
+            Y = torch.empty((N, M), device=dev)
+            for s in range(args.warmup):
+                q.qmm_gemm(copies[s % R], dt, M, K, N, X, Y, stream=stream)
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.steps)]
+            for s in range(args.steps):
+                evs[s][0].record(stream)
+                q.qmm_gemm(copies[s % R], dt, M, K, N, X, Y, stream=stream)
+                evs[s][1].record(stream)
+            torch.cuda.synchronize()
+            ts = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+            med, mn = ts[len(ts) // 2], ts[0]
+            wb = blob.numel()
+            rec = {"workload": label, "N": N, "dtype": {2: "Q4_0", 8: "Q8_0", 12: "Q4_K", 14: "Q6_K"}[dt],
+                   "M": M, "K": K, "path": "f16-mfma" if q.gemm_path(dt, M, K, N) else "f32-gemv",
+                   "us_median": round(med, 3), "us_min": round(mn, 3),
+                   "weight_GBps": round(wb / (med * 1e-6) / 1e9, 1),
+                   "hbm_frac": round(wb / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                   "TFLOPs": round(2.0 * M * N * K / (med * 1e-6) / 1e12, 2)}
+            print(json.dumps(rec), flush=True)
+        del copies, blob
+        torch.cuda.empty_cache()
+
+
+if __name__ == "__main__":
+    main()

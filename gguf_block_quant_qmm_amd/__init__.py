@@ -1,0 +1,129 @@
+"""Python binding of libqmm, the GGUF block-quantized matmul for MI355X.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI of include/qmm.h.  Tensors are PyTorch device
+tensors (PyTorch supplies device memory and streams); the functions also
+accept raw device addresses as ints.  If libqmm.so is missing the calls raise;
+there is no CPU fallback.
+
+    qmm_gemv(w, dtype, M, K, x, y, stream=None)      y[M] = W x
+    qmm_gemm(w, dtype, M, K, N, X, Y, stream=None)   Y[N][M] = X W^T
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqmm.so")
+
+# dtype tags (GGUF type ids) and status codes, as in include/qmm.h
+QMM_Q4_0, QMM_Q8_0, QMM_Q4_K, QMM_Q6_K = 2, 8, 12, 14
+DTYPES = {"Q4_0": QMM_Q4_0, "Q8_0": QMM_Q8_0, "Q4_K": QMM_Q4_K, "Q6_K": QMM_Q6_K}
+QMM_OK, QMM_ERR_NULL, QMM_ERR_DTYPE, QMM_ERR_SHAPE = 0, -1, -2, -3
+QMM_ERR_ALIGN, QMM_ERR_DEVICE, QMM_ERR_LAUNCH = -4, -5, -6
+
+EXPORTS = ("qmm_gemv", "qmm_gemm", "qmm_gemm_path", "qmm_blob_bytes", "qmm_block_elems",
+           "qmm_block_bytes", "qmm_strerror")
+
+_lib = None
+
+
+class QmmError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what}: {strerror(code)} (status {code})")
+        self.code = code
+
+
+def lib():
+    """The loaded libqmm.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m gguf_block_quant_qmm_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        i64, vp, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+        L.qmm_gemv.argtypes = [vp, ci, i64, i64, vp, vp, vp]
+        L.qmm_gemv.restype = ci
+        L.qmm_gemm.argtypes = [vp, ci, i64, i64, i64, vp, vp, vp]
+        L.qmm_gemm.restype = ci
+        L.qmm_gemm_path.argtypes = [ci, i64, i64, i64]
+        L.qmm_gemm_path.restype = ci
+        L.qmm_blob_bytes.argtypes = [ci, i64, i64]
+        L.qmm_blob_bytes.restype = i64
+        L.qmm_block_elems.argtypes = [ci]
+        L.qmm_block_bytes.argtypes = [ci]
+        L.qmm_strerror.argtypes = [ci]
+        L.qmm_strerror.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def strerror(code: int) -> str:
+    return lib().qmm_strerror(code).decode()
+
+
+def block_elems(dtype: int) -> int:
+    return lib().qmm_block_elems(dtype)
+
+
+def block_bytes(dtype: int) -> int:
+    return lib().qmm_block_bytes(dtype)
+
+
+def blob_bytes(dtype: int, M: int, K: int) -> int:
+    return lib().qmm_blob_bytes(dtype, M, K)
+
+
+def gemm_path(dtype: int, M: int, K: int, N: int) -> int:
+    return lib().qmm_gemm_path(dtype, M, K, N)
+
+
+def tolerance(dtype: int, M: int, K: int, N: int) -> float:
+    """Relative tolerance (of sum |w x|) that the chosen path guarantees."""
+    return 2e-3 if gemm_path(dtype, M, K, N) == 1 else 1e-5
+
+
+def _addr(t, nbytes: int | None, what: str, torch_dtype=None) -> int:
+    if t is None:
+        return 0
+    if isinstance(t, int):
+        return t
+    if not t.is_cuda:
+        raise ValueError(f"{what} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    if torch_dtype is not None and t.dtype != torch_dtype:
+        raise ValueError(f"{what} must be {torch_dtype}, got {t.dtype}")
+    if nbytes is not None and t.numel() * t.element_size() < nbytes:
+        raise ValueError(f"{what} holds {t.numel() * t.element_size()} bytes, needs {nbytes}")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def qmm_gemv(w, dtype: int, M: int, K: int, x, y, stream=None) -> None:
+    import torch
+    nb = blob_bytes(dtype, M, K)
+    rc = lib().qmm_gemv(_addr(w, nb or None, "w_blob"), dtype, M, K,
+                        _addr(x, 4 * K, "x", torch.float32), _addr(y, 4 * M, "y", torch.float32),
+                        _stream(stream))
+    if rc != QMM_OK:
+        raise QmmError(rc, "qmm_gemv")
+
+
+def qmm_gemm(w, dtype: int, M: int, K: int, N: int, X, Y, stream=None) -> None:
+    import torch
+    nb = blob_bytes(dtype, M, K)
+    rc = lib().qmm_gemm(_addr(w, nb or None, "w_blob"), dtype, M, K, N,
+                        _addr(X, 4 * N * K, "X", torch.float32), _addr(Y, 4 * N * M, "Y", torch.float32),
+                        _stream(stream))
+    if rc != QMM_OK:
+        raise QmmError(rc, "qmm_gemm")

@@ -1,0 +1,139 @@
+// qmm_api.hip -- the C ABI declared in include/qmm.h: argument checks, device
+// check, path selection, launch.  No allocation, no host synchronisation.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstring>
+#include <mutex>
+
+#include "qmm.h"
+#include "qmm_internal.hpp"
+
+namespace {
+
+struct DeviceInfo {
+    std::atomic<int> state{0};  // 0 unknown, 1 gfx950, 2 other
+    int cus = 0;
+};
+constexpr int kMaxDevices = 64;
+DeviceInfo g_dev[kMaxDevices];
+std::mutex g_dev_mu;
+
+int block_elems(int dtype) {
+    switch (dtype) {
+    case QMM_Q4_0:
+    case QMM_Q8_0: return 32;
+    case QMM_Q4_K:
+    case QMM_Q6_K: return 256;
+    default: return 0;
+    }
+}
+
+int block_bytes(int dtype) {
+    switch (dtype) {
+    case QMM_Q4_0: return 18;
+    case QMM_Q8_0: return 34;
+    case QMM_Q4_K: return 144;
+    case QMM_Q6_K: return 210;
+    default: return 0;
+    }
+}
+
+int check_shape(int dtype, int64_t M, int64_t K, int64_t N) {
+    const int bs = block_elems(dtype);
+    if (bs == 0) return QMM_ERR_DTYPE;
+    if (M < 1 || N < 1 || K < bs || K % bs != 0) return QMM_ERR_SHAPE;
+    // keep every byte offset and grid size inside 63 bits / the launch limits
+    if (M > (int64_t(1) << 40) || K > (int64_t(1) << 40) || N > (int64_t(1) << 40)) return QMM_ERR_SHAPE;
+    return QMM_OK;
+}
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// Current device must be gfx950; returns its compute-unit count through *cus.
+int current_device(int *cus) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return QMM_ERR_DEVICE;
+    DeviceInfo &d = g_dev[dev];
+    int st = d.state.load(std::memory_order_acquire);
+    if (st == 0) {
+        std::lock_guard<std::mutex> lk(g_dev_mu);
+        st = d.state.load(std::memory_order_relaxed);
+        if (st == 0) {
+            hipDeviceProp_t prop;
+            if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return QMM_ERR_DEVICE;
+            const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+            d.cus = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256;
+            st = ok ? 1 : 2;
+            d.state.store(st, std::memory_order_release);
+        }
+    }
+    if (st != 1) return QMM_ERR_DEVICE;
+    *cus = d.cus;
+    return QMM_OK;
+}
+
+// N at and above which the f16 matrix-core GEMM runs; below it the f32 GEMV.
+int64_t mfma_from_n(int /*dtype*/) { return 2; }
+
+}  // namespace
+
+extern "C" {
+
+int qmm_block_elems(int dtype) { return block_elems(dtype); }
+int qmm_block_bytes(int dtype) { return block_bytes(dtype); }
+
+int64_t qmm_blob_bytes(int dtype, int64_t M, int64_t K) {
+    if (check_shape(dtype, M, K, 1) != QMM_OK) return 0;
+    return M * (K / block_elems(dtype)) * block_bytes(dtype);
+}
+
+const char *qmm_strerror(int code) {
+    switch (code) {
+    case QMM_OK: return "ok";
+    case QMM_ERR_NULL: return "a required pointer is NULL";
+    case QMM_ERR_DTYPE: return "unsupported dtype (expected Q4_0=2, Q8_0=8, Q4_K=12 or Q6_K=14)";
+    case QMM_ERR_SHAPE: return "bad shape (need M >= 1, N >= 1, K a positive multiple of the block size)";
+    case QMM_ERR_ALIGN: return "misaligned pointer (blob and x/X need 16-byte, y/Y 4-byte alignment)";
+    case QMM_ERR_DEVICE: return "no current HIP device, or it is not gfx950";
+    case QMM_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status code";
+    }
+}
+
+int qmm_gemm_path(int dtype, int64_t M, int64_t K, int64_t N) {
+    const int rc = check_shape(dtype, M, K, N);
+    if (rc != QMM_OK) return rc;
+    return N >= mfma_from_n(dtype) ? 1 : 0;
+}
+
+int qmm_gemv(const void *w_blob, int dtype, int64_t M, int64_t K, const float *x, float *y, void *stream) {
+    int rc = check_shape(dtype, M, K, 1);
+    if (rc != QMM_OK) return rc;
+    if (!w_blob || !x || !y) return QMM_ERR_NULL;
+    if (!aligned(w_blob, 16) || !aligned(x, 16) || !aligned(y, 4)) return QMM_ERR_ALIGN;
+    int cus = 0;
+    rc = current_device(&cus);
+    if (rc != QMM_OK) return rc;
+    const hipError_t e = qmm::launch_gemv(dtype, w_blob, M, K, x, y, (hipStream_t)stream, cus);
+    return e == hipSuccess ? QMM_OK : QMM_ERR_LAUNCH;
+}
+
+int qmm_gemm(const void *w_blob, int dtype, int64_t M, int64_t K, int64_t N, const float *X, float *Y,
+             void *stream) {
+    int rc = check_shape(dtype, M, K, N);
+    if (rc != QMM_OK) return rc;
+    if (!w_blob || !X || !Y) return QMM_ERR_NULL;
+    if (!aligned(w_blob, 16) || !aligned(X, 16) || !aligned(Y, 4)) return QMM_ERR_ALIGN;
+    int cus = 0;
+    rc = current_device(&cus);
+    if (rc != QMM_OK) return rc;
+    hipError_t e;
+    if (N < mfma_from_n(dtype))
+        e = qmm::launch_gemv(dtype, w_blob, M, K, X, Y, (hipStream_t)stream, cus);  // N == 1: the GEMV's bits
+    else
+        e = qmm::launch_gemm_mfma(dtype, w_blob, M, K, N, X, Y, (hipStream_t)stream);
+    return e == hipSuccess ? QMM_OK : QMM_ERR_LAUNCH;
+}
+
+}  // extern "C"

@@ -1,0 +1,90 @@
+// qmm_device.hpp -- device helpers for the gfx950 kernels: raw block fetches
+// and the block geometry.  Included only by the HIP sources of libqmm.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "qmm.h"
+
+namespace qmm {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+// Block geometry (weights, bytes) per GGUF type id.
+template <int DT> struct Geo;
+template <> struct Geo<QMM_Q4_0> { static constexpr int BS = 32, BB = 18; };
+template <> struct Geo<QMM_Q8_0> { static constexpr int BS = 32, BB = 34; };
+template <> struct Geo<QMM_Q4_K> { static constexpr int BS = 256, BB = 144; };
+template <> struct Geo<QMM_Q6_K> { static constexpr int BS = 256, BB = 210; };
+
+__device__ __forceinline__ float h2f(uint32_t bits16) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(bits16 & 0xFFFFu));
+}
+
+// Bytes [p, p+4N) of memory whose start is 4-byte aligned, as N dwords.
+template <int N>
+__device__ __forceinline__ void fetch_al(const uint8_t *p, uint32_t (&out)[N]) {
+    const uint32_t *q = reinterpret_cast<const uint32_t *>(p);
+#pragma unroll
+    for (int i = 0; i < N; i++) out[i] = q[i];
+}
+
+// Bytes [p, p+4N) for a 2-byte aligned p: loads the N+1 aligned dwords that
+// cover them and funnel-shifts.  The caller guarantees that the dword holding
+// byte p+4N-1+(p&3) is inside the buffer.
+template <int N>
+__device__ __forceinline__ void fetch_un(const uint8_t *p, uint32_t (&out)[N]) {
+    const uint32_t sh = (uint32_t)((uintptr_t)p & 3u);
+    const uint32_t *q = reinterpret_cast<const uint32_t *>((uintptr_t)p & ~(uintptr_t)3);
+    uint32_t w[N + 1];
+#pragma unroll
+    for (int i = 0; i < N + 1; i++) w[i] = q[i];
+#pragma unroll
+    for (int i = 0; i < N; i++) out[i] = __builtin_amdgcn_alignbyte(w[i + 1], w[i], sh);
+}
+
+// Bytes [p, p+nbytes) by single-byte loads, any alignment; the rest of the
+// N dwords is zero.  Reads nothing outside [p, p+nbytes).
+template <int N>
+__device__ __forceinline__ void fetch_bytes(const uint8_t *p, int nbytes, uint32_t (&out)[N]) {
+#pragma unroll
+    for (int i = 0; i < N; i++) {
+        uint32_t v = 0;
+#pragma unroll
+        for (int b = 0; b < 4; b++) {
+            const int o = 4 * i + b;
+            if (o < nbytes) v |= (uint32_t)p[o] << (8 * b);
+        }
+        out[i] = v;
+    }
+}
+
+__device__ __forceinline__ uint32_t byte_of(uint32_t v, int i) { return (v >> (8 * i)) & 0xFFu; }
+
+// Q4_K sub-block i (0..7): 6-bit scale and min from the 12 packed bytes held
+// in dwords s0 (bytes 0-3), s1 (4-7), s2 (8-11).  Standard GGUF k-quant
+// packing: i<4 low 6 bits of byte i / i+4; i>=4 low/high nibble of byte i+4
+// plus the top 2 bits of byte i-4 / i.
+__device__ __forceinline__ void q4k_scale_min(uint32_t s0, uint32_t s1, uint32_t s2, int i,
+                                              int &sc, int &mn) {
+    if (i < 4) {
+        sc = (int)(byte_of(s0, i) & 63u);
+        mn = (int)(byte_of(s1, i) & 63u);
+    } else {
+        const int j = i - 4;
+        sc = (int)((byte_of(s2, j) & 15u) | ((byte_of(s0, j) >> 6) << 4));
+        mn = (int)((byte_of(s2, j) >> 4) | ((byte_of(s1, j) >> 6) << 4));
+    }
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+}  // namespace qmm

@@ -1,0 +1,117 @@
+/*
+ * qmm.h -- C ABI of the GGUF block-quantized matmul library for AMD MI355X
+ * (gfx950).  Library: gguf_block_quant_qmm_amd/libqmm.so.
+ *
+ * The operation (page "cera 0.5.2 src/backend/cpu.rs", section "Matrix
+ * multiplication": matmul_q4_0_f32 / matmul_q8_0_f32 / matmul_q4km_f32 define
+ * C = dequant(A) . B over a row-major blob of quantized blocks, overwriting C):
+ *
+ *     Y[n][m] = sum_k W[m][k] * X[n][k],   0 <= m < M, 0 <= n < N, 0 <= k < K
+ *
+ * where W[m][k] is weight k of row m decoded from the blob.  Activations and
+ * outputs are f32 and token-major (page "cera 0.3.1 src/model/gpu_lfm2.rs",
+ * batched prefill: contiguous token rows; at most 512 tokens per dispatch
+ * there, any N >= 1 here).
+ *
+ * Weight blob layout (page "cera 0.5.2 src/backend/cpu.rs", matmul_q4_0_f32:
+ * row i starts at i*bytes_per_row, its K/bs blocks follow back to back):
+ *     row_bytes = (K / block_elems) * block_bytes,  blob = M * row_bytes bytes
+ * Block formats (little-endian, f16 = IEEE binary16):
+ *     Q8_0 (32 weights, 34 B): f16 d, int8 q[32];            w = d*q
+ *     Q4_0 (32 weights, 18 B): f16 d, 16 nibble bytes;       w = d*(q-8)
+ *          weight e<16 = low nibble of byte e, e>=16 = high nibble of byte e-16
+ *          (same page, repack_q4_0_8x8)
+ *     Q4_K (256 weights, 144 B): f16 d, f16 dmin, 12 bytes of packed 6-bit
+ *          (scale, min) for 8 sub-blocks of 32, 128 nibble bytes;
+ *          w = d*sc*q - dmin*m  (same page, repack_q4_k_8x8; the 6-bit
+ *          packing follows the standard GGUF k-quant layout)
+ *     Q6_K (256 weights, 210 B): ql[128] low 4 bits, qh[64] high 2 bits,
+ *          int8 sub-scales[16], f16 d;  w = d*sc*(q-32)  (210-byte size:
+ *          page "cera 0.3.1 src/model/gpu_lfm2.rs", upload_weight; bit
+ *          placement: standard GGUF layout)
+ *
+ * Arguments and ownership.  Every buffer is caller-owned device memory on the
+ * current HIP device; the library never allocates, frees or keeps a pointer
+ * after a call returns.  Calls are asynchronous on `stream` (a hipStream_t;
+ * NULL = the null stream) and do not synchronise the host.  A call is
+ * stateless: concurrent calls on different streams are safe.
+ *
+ * Errors.  Every argument is checked before any launch (the pages use release
+ * asserts on the same conditions, cpu.rs gemm_preq_dispatch); a failed check
+ * returns a negative code and launches nothing.  The blob's length cannot be
+ * checked: the caller guarantees qmm_blob_bytes(dtype, M, K) readable bytes.
+ * A fault inside a kernel surfaces at the caller's next synchronisation.
+ * There is no silent fallback to another algorithm.
+ *
+ * Determinism.  Results are bitwise reproducible run to run (fixed reduction
+ * order, no float atomics), and qmm_gemm with N == 1 returns exactly the bits
+ * of qmm_gemv (page "cera 0.5.2 src/backend/cpu.rs", gemv_q4_1_f32: decode
+ * and prefill must agree bit for bit).
+ */
+#ifndef QMM_H
+#define QMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* dtype tags: the GGUF tensor type ids */
+#define QMM_Q4_0 2
+#define QMM_Q8_0 8
+#define QMM_Q4_K 12
+#define QMM_Q6_K 14
+
+/* status codes */
+#define QMM_OK 0
+#define QMM_ERR_NULL (-1)    /* a required pointer is NULL                          */
+#define QMM_ERR_DTYPE (-2)   /* dtype is not one of the four tags above             */
+#define QMM_ERR_SHAPE (-3)   /* M < 1, N < 1, K < block_elems or K % block_elems    */
+#define QMM_ERR_ALIGN (-4)   /* blob not 16-B aligned, x/X not 16-B, y/Y not 4-B    */
+#define QMM_ERR_DEVICE (-5)  /* no current HIP device, or it is not gfx950          */
+#define QMM_ERR_LAUNCH (-6)  /* the kernel launch itself failed                     */
+
+/* Decode GEMV (one token), page "cera 0.5.2 src/backend/cpu.rs", section
+ * "GEMV (matrix-vector multiply)": y[m] = sum_k W[m][k] * x[k].
+ *   w_blob  device, M*row_bytes bytes, 16-B aligned, row-major blocks
+ *   dtype   QMM_Q4_0 | QMM_Q8_0 | QMM_Q4_K | QMM_Q6_K
+ *   M, K    rows and weights per row; K a multiple of the block size
+ *   x       device f32 [K], 16-B aligned
+ *   y       device f32 [M], 4-B aligned; overwritten
+ * All f32 arithmetic: |y - exact| <= 1e-5 * sum_k |W[m][k] x[k]|. */
+int qmm_gemv(const void *w_blob, int dtype, int64_t M, int64_t K,
+             const float *x, float *y, void *stream);
+
+/* Prefill / verify GEMM over N tokens (page "cera 0.3.1 src/model/gpu_lfm2.rs",
+ * mul_mat_reg_tile: weights decoded once per k-tile and reused across all
+ * token columns):  Y[n][m] = sum_k W[m][k] * X[n][k].
+ *   X       device f32 [N][K] row-major, 16-B aligned
+ *   Y       device f32 [N][M] row-major, 4-B aligned; overwritten
+ * N == 1 runs the GEMV (same bits).  Other N run the path qmm_gemm_path
+ * names: 0 = all-f32 arithmetic (tolerance 1e-5 of sum |w x|), 1 = weights
+ * and activations rounded to f16 and multiplied on the matrix cores with f32
+ * accumulation (tolerance 2e-3 of sum |w x|; needs |w|, |x| < 65504). */
+int qmm_gemm(const void *w_blob, int dtype, int64_t M, int64_t K, int64_t N,
+             const float *X, float *Y, void *stream);
+
+/* Which arithmetic qmm_gemm uses for these sizes: 0 = f32 (GEMV family),
+ * 1 = f16 matrix-core GEMM, or a negative status for invalid arguments. */
+int qmm_gemm_path(int dtype, int64_t M, int64_t K, int64_t N);
+
+/* Bytes of a blob of M rows x K weights; 0 if dtype or shape is invalid. */
+int64_t qmm_blob_bytes(int dtype, int64_t M, int64_t K);
+
+/* Weights and bytes per block; 0 for an unknown dtype. */
+int qmm_block_elems(int dtype);
+int qmm_block_bytes(int dtype);
+
+/* Static text for a status code (never NULL). */
+const char *qmm_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QMM_H */

@@ -1,0 +1,102 @@
+"""Host-side checks of the C ABI (CPU only: no kernel is launched).
+
+The library must load, export every function include/qmm.h declares, report
+the block geometry, and reject bad arguments with the documented status codes
+before touching a device.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gguf_block_quant_qmm_amd as q
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qmm.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qmm_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_exports():
+    assert declared_functions() == sorted(q.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(q.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(L, name), f"libqmm.so does not export {name}"
+
+
+def test_geometry():
+    assert [q.block_elems(d) for d in (2, 8, 12, 14)] == [32, 32, 256, 256]
+    assert [q.block_bytes(d) for d in (2, 8, 12, 14)] == [18, 34, 144, 210]
+    assert q.block_elems(3) == 0 and q.block_bytes(99) == 0
+    # the tied Q6_K head of the 1B model on the pages: 2048 x 128256, ~205 MiB
+    assert q.blob_bytes(q.QMM_Q6_K, 128256, 2048) == 215_470_080
+    assert q.blob_bytes(q.QMM_Q4_0, 4096, 4096) == 4096 * 128 * 18
+    assert q.blob_bytes(q.QMM_Q4_0, 4096, 4100) == 0     # K % 32
+    assert q.blob_bytes(7, 4, 32) == 0                    # dtype
+
+
+def test_header_constants_match_binding():
+    text = open(HEADER).read()
+    consts = dict(re.findall(r"#define\s+(QMM_[A-Z0-9_]+)\s+\(?(-?\d+)\)?", text))
+    for name, val in consts.items():
+        assert getattr(q, name) == int(val), name
+
+
+def test_strerror_is_total():
+    for code in range(-8, 2):
+        assert isinstance(q.strerror(code), str) and q.strerror(code)
+
+
+A16 = 0x7F0000000000  # a 16-byte aligned fake device address: never dereferenced
+
+
+@pytest.mark.parametrize("args,code", [
+    ((A16, 5, 8, 32, A16, A16), q.QMM_ERR_DTYPE),
+    ((A16, 2, 0, 32, A16, A16), q.QMM_ERR_SHAPE),
+    ((A16, 2, 8, 0, A16, A16), q.QMM_ERR_SHAPE),
+    ((A16, 2, 8, 48, A16, A16), q.QMM_ERR_SHAPE),
+    ((A16, 12, 8, 128, A16, A16), q.QMM_ERR_SHAPE),
+    ((0, 2, 8, 64, A16, A16), q.QMM_ERR_NULL),
+    ((A16, 2, 8, 64, 0, A16), q.QMM_ERR_NULL),
+    ((A16, 2, 8, 64, A16, 0), q.QMM_ERR_NULL),
+    ((A16 + 2, 2, 8, 64, A16, A16), q.QMM_ERR_ALIGN),
+    ((A16, 2, 8, 64, A16 + 4, A16), q.QMM_ERR_ALIGN),
+    ((A16, 2, 8, 64, A16, A16 + 2), q.QMM_ERR_ALIGN),
+])
+def test_gemv_rejects(args, code):
+    assert q.lib().qmm_gemv(*args, None) == code
+
+
+@pytest.mark.parametrize("args,code", [
+    ((A16, 2, 8, 64, 0, A16, A16), q.QMM_ERR_SHAPE),
+    ((A16, 2, 8, 64, -3, A16, A16), q.QMM_ERR_SHAPE),
+    ((A16, 14, 8, 300, 4, A16, A16), q.QMM_ERR_SHAPE),
+    ((A16, 1, 8, 64, 4, A16, A16), q.QMM_ERR_DTYPE),
+    ((A16, 8, 8, 64, 4, 0, A16), q.QMM_ERR_NULL),
+    ((A16, 8, 8, 64, 4, A16 + 8, A16), q.QMM_ERR_ALIGN),
+])
+def test_gemm_rejects(args, code):
+    assert q.lib().qmm_gemm(*args, None) == code
+
+
+def test_gemm_path_selection():
+    # N == 1 is the f32 GEMV; the matrix-core path reports itself for N >= 2
+    assert q.gemm_path(q.QMM_Q4_K, 14336, 4096, 1) == 0
+    assert q.gemm_path(q.QMM_Q4_K, 14336, 4096, 512) == 1
+    assert q.gemm_path(q.QMM_Q4_K, 14336, 100, 512) == q.QMM_ERR_SHAPE
+    assert q.tolerance(q.QMM_Q4_0, 4096, 4096, 1) == 1e-5
+
+
+def test_valid_call_without_gpu_reports_device(monkeypatch):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; covered by the GPU tests")
+    assert q.lib().qmm_gemv(A16, 2, 8, 64, A16, A16, None) == q.QMM_ERR_DEVICE

@@ -1,0 +1,193 @@
+"""HIP path against the CPU oracle, element by element, through the C ABI.
+
+Bar: |Y_gpu - Y_exact| <= tau * S per output, with S = sum_k |W x| and
+Y_exact the oracle's f64 sum (within 1e-12 S of exact); tau = 1e-5 on the
+f32 path (qmm_gemv, qmm_gemm at N = 1) and 2e-3 on the f16 matrix-core path;
+S = 0 demands an exact 0.
+
+  * small shapes, full output: several tiles, ragged M/N/K tails, odd block
+    counts (the byte-load kernels), N beyond 512;
+  * every workload at its full size in the launch configuration the bench
+    times, compared on sampled rows (all N columns of each sampled row);
+  * bitwise: qmm_gemm at N = 1 equals qmm_gemv; two runs give equal bits.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gguf_block_quant_qmm_amd as q
+import oracle
+from qmm_inputs import WORKLOADS, make_blob, make_x, rng_for
+
+pytestmark = pytest.mark.gpu
+
+DTYPES = [q.QMM_Q4_0, q.QMM_Q8_0, q.QMM_Q4_K, q.QMM_Q6_K]
+NAME = {2: "Q4_0", 8: "Q8_0", 12: "Q4_K", 14: "Q6_K"}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.set_device(0)
+
+
+def to_dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def gpu_gemv(dt, blob_d, M, K, x):
+    y = torch.full((M,), float("nan"), device="cuda")
+    q.qmm_gemv(blob_d, dt, M, K, to_dev(x.reshape(-1)), y)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+def gpu_gemm(dt, blob_d, M, K, X):
+    N = X.shape[0]
+    Y = torch.full((N, M), float("nan"), device="cuda")
+    q.qmm_gemm(blob_d, dt, M, K, N, to_dev(X), Y)
+    torch.cuda.synchronize()
+    return Y.cpu().numpy()
+
+
+def check(Yg, Y64, S, tau, label):
+    assert Yg.shape == Y64.shape, label
+    assert np.all(np.isfinite(Yg)), f"{label}: non-finite output"
+    err = np.abs(Yg.astype(np.float64) - Y64)
+    zero = S == 0
+    assert np.all(Yg[zero] == 0), f"{label}: S = 0 but output is not exactly 0"
+    if (~zero).any():
+        ratio = err[~zero] / S[~zero]
+        worst = int(np.argmax(ratio))
+        assert ratio[worst] <= tau, f"{label}: |err|/S = {ratio[worst]:.3g} > {tau} at flat index {worst}"
+
+
+def bs_of(dt):
+    return 256 if dt in (q.QMM_Q4_K, q.QMM_Q6_K) else 32
+
+
+# ----------------------------------------------------------------- GEMV ----
+
+def gemv_shapes(dt):
+    if bs_of(dt) == 32:
+        # nb odd -> byte-load kernel; K = 65600 -> more units than threads
+        return [(1, 32), (1, 64), (3, 96), (67, 256), (300, 1024), (129, 4160), (50, 14336), (33, 16416),
+                (5, 65600)]
+    return [(1, 256), (3, 512), (67, 768), (300, 2048), (50, 4096), (9, 16640)]
+
+
+@pytest.mark.parametrize("dt", DTYPES, ids=NAME.get)
+def test_gemv_small(dt):
+    for i, (M, K) in enumerate(gemv_shapes(dt)):
+        blob = make_blob(dt, M, K, rng_for(500 + dt, i))
+        x = make_x(1, K, rng_for(500 + dt, 100 + i))
+        _, Y64, S = oracle.matmul(dt, blob, M, K, x)
+        yg = gpu_gemv(dt, to_dev(blob), M, K, x)
+        check(yg[None, :], Y64, S, 1e-5, f"{NAME[dt]} gemv M={M} K={K}")
+
+
+# ----------------------------------------------------------------- GEMM ----
+
+def gemm_shapes(dt):
+    if bs_of(dt) == 32:
+        return [(70, 96), (300, 1024), (129, 2080)]
+    return [(70, 512), (129, 768), (300, 1024)]
+
+
+@pytest.mark.parametrize("dt", DTYPES, ids=NAME.get)
+@pytest.mark.parametrize("N", [2, 3, 17, 32, 33, 64, 65, 130, 513])
+def test_gemm_small(dt, N):
+    for i, (M, K) in enumerate(gemm_shapes(dt)):
+        blob = make_blob(dt, M, K, rng_for(600 + dt, i))
+        X = make_x(N, K, rng_for(600 + dt, 1000 * N + i))
+        _, Y64, S = oracle.matmul(dt, blob, M, K, X)
+        Yg = gpu_gemm(dt, to_dev(blob), M, K, X)
+        check(Yg, Y64, S, q.tolerance(dt, M, K, N), f"{NAME[dt]} gemm M={M} K={K} N={N}")
+
+
+# ------------------------------------------------------------ properties ----
+
+@pytest.mark.parametrize("dt", DTYPES, ids=NAME.get)
+def test_gemm_n1_is_gemv_bitwise_and_deterministic(dt):
+    for i, (M, K) in enumerate([(300, 4 * bs_of(dt) * 4), (77, 3 * bs_of(dt))]):
+        blob_d = to_dev(make_blob(dt, M, K, rng_for(700 + dt, i)))
+        x = make_x(1, K, rng_for(700 + dt, 10 + i))
+        a = gpu_gemv(dt, blob_d, M, K, x)
+        b = gpu_gemm(dt, blob_d, M, K, x)[0]
+        c = gpu_gemv(dt, blob_d, M, K, x)
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), "qmm_gemm(N=1) != qmm_gemv"
+        assert np.array_equal(a.view(np.uint32), c.view(np.uint32)), "gemv not deterministic"
+        X = make_x(40, K, rng_for(700 + dt, 20 + i))
+        assert np.array_equal(gpu_gemm(dt, blob_d, M, K, X), gpu_gemm(dt, blob_d, M, K, X)), "gemm not deterministic"
+
+
+@pytest.mark.parametrize("dt", DTYPES, ids=NAME.get)
+def test_zero_scales_give_exact_zero(dt):
+    M, K = 45, 8 * bs_of(dt)
+    blob = make_blob(dt, M, K, rng_for(800 + dt, 0)).reshape(M * (K // bs_of(dt)), -1)
+    offs = {2: [0], 8: [0], 12: [0, 2], 14: [208]}[dt]
+    for o in offs:
+        blob[:, o:o + 2] = 0
+    blob = blob.reshape(-1)
+    x = make_x(3, K, rng_for(800 + dt, 1))
+    _, Y64, S = oracle.matmul(dt, blob, M, K, x)
+    assert np.all(S == 0)
+    bd = to_dev(blob)
+    assert np.all(gpu_gemv(dt, bd, M, K, x[0]) == 0)
+    assert np.all(gpu_gemm(dt, bd, M, K, x) == 0)
+
+
+def test_sparse_rows_keep_f32_bound():
+    # Q4_0 rows whose weights are all zero (nibble 8) but one: S is tiny, the
+    # f32 GEMV must still be within 1e-5 of it (no cancellation shortcuts).
+    M, K = 64, 1024
+    blob = make_blob(q.QMM_Q4_0, M, K, rng_for(810, 0)).reshape(M, K // 32, 18)
+    blob[:, :, 2:] = 0x88
+    blob[:, 3, 2] = 0x8F
+    blob = blob.reshape(-1)
+    x = make_x(1, K, rng_for(810, 1)) * np.float32(1e3)
+    _, Y64, S = oracle.matmul(q.QMM_Q4_0, blob, M, K, x)
+    check(gpu_gemv(q.QMM_Q4_0, to_dev(blob), M, K, x)[None, :], Y64, S, 1e-5, "sparse q4_0 rows")
+
+
+def test_streams_and_errors_on_device():
+    M, K = 64, 256
+    blob_d = to_dev(make_blob(q.QMM_Q4_K, M, K, rng_for(820, 0)))
+    x = to_dev(make_x(1, K, rng_for(820, 1)).reshape(-1))
+    y = torch.empty(M, device="cuda")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        q.qmm_gemv(blob_d, q.QMM_Q4_K, M, K, x, y, stream=s)
+    s.synchronize()
+    ref = torch.empty(M, device="cuda")
+    q.qmm_gemv(blob_d, q.QMM_Q4_K, M, K, x, ref)
+    torch.cuda.synchronize()
+    assert torch.equal(y, ref)
+    # misaligned device pointers are refused before any launch
+    with pytest.raises(q.QmmError) as e:
+        q.qmm_gemv(blob_d.data_ptr() + 2, q.QMM_Q4_K, M, K, x, y)
+    assert e.value.code == q.QMM_ERR_ALIGN
+
+
+# ------------------------------------------------- full-size workloads ----
+
+def sample_rows(M, n, seed):
+    r = np.random.default_rng(seed).choice(M, size=min(n, M), replace=False)
+    return np.unique(np.concatenate([r, [0, M - 1]]))
+
+
+@pytest.mark.parametrize("wid", sorted(WORKLOADS))
+def test_workload_full_size(wid):
+    label, dt, M, K, ns = WORKLOADS[wid]
+    blob = make_blob(dt, M, K, rng_for(wid, 0))
+    blob_d = to_dev(blob)
+    for N in ns:
+        X = make_x(N, K, rng_for(wid, 1000 + N))
+        rows = sample_rows(M, 96 if N <= 64 else 48, wid * 7919 + N)
+        _, Y64, S = oracle.matmul(dt, blob, M, K, X, rows=rows)
+        Yg = gpu_gemv(dt, blob_d, M, K, X)[None, :] if N == 1 else gpu_gemm(dt, blob_d, M, K, X)
+        assert np.all(np.isfinite(Yg)), f"{label} N={N}: non-finite output"
+        check(Yg[:, rows], Y64, S, q.tolerance(dt, M, K, N), f"{label} N={N}")
+    del blob_d
+    torch.cuda.empty_cache()
