@@ -18,7 +18,9 @@ After the decode loop the same number of steps of the Q4_K prefill GEMM
 sample of the same workloads ("cpu_baseline").
 
 Kernel durations come from HIP events recorded on the stream the kernels run
-on (torch's current stream), around every launch.
+on (torch's current stream) at the boundaries of the timed regions; a
+region's launches run back to back, and the per-launch figure is the region
+time over its launch count.
 
 Extra: ``--sweep`` prints one JSON line per (workload, N) for every
 configuration of the workload table (C1-C5) instead of the main line.
@@ -107,35 +109,40 @@ def main():
     ys = [torch.empty((1, m[2]), device=dev) for m in mats]
     stream = torch.cuda.current_stream()
 
-    def decode_step(s, evs=None):
+    def decode_step(s):
         c = s % R
         for i, (name, dt, M, K, _) in enumerate(mats):
-            if evs is not None:
-                evs[i].record(stream)
             q.qmm_gemm(copies[i][c], dt, M, K, 1, xs[i], ys[i], stream=stream)
-        if evs is not None:
-            evs[len(mats)].record(stream)
 
     for s in range(args.warmup):
         decode_step(s)
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(mats) + 1)] for _ in range(args.steps)]
+    # events only at step boundaries: the four GEMVs of a step run back to back
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t0 = time.perf_counter()
+    ev[0].record(stream)
     for s in range(args.steps):
-        decode_step(args.warmup + s, ev[s])
+        decode_step(args.warmup + s)
+        ev[s + 1].record(stream)
     torch.cuda.synchronize()
     wall_dec = time.perf_counter() - t0
-    kern_ms = [sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)) for i in range(len(mats))]
-    span_ms = sum(ev[s][0].elapsed_time(ev[s][len(mats)]) for s in range(args.steps))
+    span_ms = ev[0].elapsed_time(ev[args.steps])
     dec_bytes_total = step_bytes * args.steps
     value = dec_bytes_total / (span_ms * 1e-3) / 1e9
-    kern_total_ms = sum(kern_ms)
-    avg_launch_us = kern_total_ms * 1e3 / (args.steps * len(mats))
-    achieved = dec_bytes_total / (kern_total_ms * 1e-3) / 1e9
+    avg_launch_us = span_ms * 1e3 / (args.steps * len(mats))
+    achieved = value
     traffic = load_traffic("gemv_q4_0_decode_layer")
-    per_matrix = {mats[i][0]: {"us": kern_ms[i] * 1e3 / args.steps,
-                               "GB/s": mats[i][4].numel() / (kern_ms[i] * 1e-3 / args.steps) / 1e9}
-                  for i in range(len(mats))}
+    # per-matrix time: each shape alone, back to back, between two events
+    per_matrix = {}
+    for i, (name, dt, M, K, _) in enumerate(mats):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for s in range(args.steps):
+            q.qmm_gemm(copies[i][s % R], dt, M, K, 1, xs[i], ys[i], stream=stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / args.steps
+        per_matrix[name] = {"us": round(us, 3), "GB/s": round(copies[i][0].numel() / (us * 1e-6) / 1e9, 1)}
 
     # --------------------------------------------------------------- prefill
     _, pdt, PM, PK, _ = WORKLOADS[6]
@@ -148,15 +155,15 @@ def main():
     for s in range(args.warmup):
         q.qmm_gemm(pcopies[s % PR], pdt, PM, PK, PN, PX, PY, stream=stream)
     torch.cuda.synchronize()
-    pev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    pa, pb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    pa.record(stream)
     for s in range(args.steps):
-        pev[s][0].record(stream)
         q.qmm_gemm(pcopies[(args.warmup + s) % PR], pdt, PM, PK, PN, PX, PY, stream=stream)
-        pev[s][1].record(stream)
+    pb.record(stream)
     torch.cuda.synchronize()
     wall_pre = time.perf_counter() - t0
-    pre_ms = sum(a.elapsed_time(b) for a, b in pev)
+    pre_ms = pa.elapsed_time(pb)
     flops = 2.0 * PM * PN * PK
     tflops = flops * args.steps / (pre_ms * 1e-3) / 1e12
     ptraffic = load_traffic("gemm_q4_k_n512")
@@ -181,6 +188,7 @@ def main():
             "rotation_copies": R,
             "hbm_frac": round(value / HBM_PEAK_GBS, 4),
             "decode_ms_per_step": round(span_ms / args.steps, 5),
+            "timing": "HIP events on the launch stream at step boundaries; per-launch = span / launches",
             "per_matrix": per_matrix,
             "gpu": props.name,
             "cus": props.multi_processor_count,
@@ -252,7 +260,8 @@ def cpu_baseline(args, np, mats, WORKLOADS, make_blob, make_x, rng_for, step_byt
         "kind": "oracle",
         "sample": f"{passes} whole decode layers (4 Q4_0 GEMVs, same shapes and seeds) in {dt_dec:.1f} s",
         "prefill_gemm_tflops": round(2.0 * rows * 512 * PK / dt_pre / 1e12, 6),
-        "prefill_sample": f"{rows} of {PM} rows x 512 tokens of the Q4_K GEMM in {dt_pre:.1f} s",
+        "prefill_sample": f"{rows} output rows (64 at a time, cycling over the {PM}) x 512 tokens of the "
+                          f"Q4_K GEMM in {dt_pre:.1f} s",
     }
 
 
@@ -268,19 +277,17 @@ def sweep(args, q, np, torch, dev, WORKLOADS, make_blob, make_x, rng_for):
             Y = torch.empty((N, M), device=dev)
             for s in range(args.warmup):
                 q.qmm_gemm(copies[s % R], dt, M, K, N, X, Y, stream=stream)
-            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                   for _ in range(args.steps)]
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
             for s in range(args.steps):
-                evs[s][0].record(stream)
                 q.qmm_gemm(copies[s % R], dt, M, K, N, X, Y, stream=stream)
-                evs[s][1].record(stream)
+            b.record(stream)
             torch.cuda.synchronize()
-            ts = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
-            med, mn = ts[len(ts) // 2], ts[0]
+            med = a.elapsed_time(b) * 1e3 / args.steps
             wb = blob.numel()
             rec = {"workload": label, "N": N, "dtype": {2: "Q4_0", 8: "Q8_0", 12: "Q4_K", 14: "Q6_K"}[dt],
                    "M": M, "K": K, "path": "f16-mfma" if q.gemm_path(dt, M, K, N) else "f32-gemv",
-                   "us_median": round(med, 3), "us_min": round(mn, 3),
+                   "us_per_call": round(med, 3),
                    "weight_GBps": round(wb / (med * 1e-6) / 1e9, 1),
                    "hbm_frac": round(wb / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                    "TFLOPs": round(2.0 * M * N * K / (med * 1e-6) / 1e12, 2)}

@@ -26,23 +26,25 @@ __device__ __forceinline__ float h2f(uint32_t bits16) {
 }
 
 // Bytes [p, p+4N) of memory whose start is 4-byte aligned, as N dwords.
-template <int N>
+// NT: non-temporal loads (data streamed once, kept out of the caches).
+template <int N, bool NT = false>
 __device__ __forceinline__ void fetch_al(const uint8_t *p, uint32_t (&out)[N]) {
     const uint32_t *q = reinterpret_cast<const uint32_t *>(p);
 #pragma unroll
-    for (int i = 0; i < N; i++) out[i] = q[i];
+    for (int i = 0; i < N; i++) out[i] = NT ? __builtin_nontemporal_load(q + i) : q[i];
 }
 
 // Bytes [p, p+4N) for a 2-byte aligned p: loads the N+1 aligned dwords that
 // cover them and funnel-shifts.  The caller guarantees that the dword holding
 // byte p+4N-1+(p&3) is inside the buffer.
-template <int N>
+template <int N, bool NT = false>
 __device__ __forceinline__ void fetch_un(const uint8_t *p, uint32_t (&out)[N]) {
     const uint32_t sh = (uint32_t)((uintptr_t)p & 3u);
-    const uint32_t *q = reinterpret_cast<const uint32_t *>((uintptr_t)p & ~(uintptr_t)3);
+    // aligned down by pointer arithmetic, so the global address space is kept
+    const uint32_t *q = reinterpret_cast<const uint32_t *>(p - sh);
     uint32_t w[N + 1];
 #pragma unroll
-    for (int i = 0; i < N + 1; i++) w[i] = q[i];
+    for (int i = 0; i < N + 1; i++) w[i] = NT ? __builtin_nontemporal_load(q + i) : q[i];
 #pragma unroll
     for (int i = 0; i < N; i++) out[i] = __builtin_amdgcn_alignbyte(w[i + 1], w[i], sh);
 }
@@ -61,6 +63,11 @@ __device__ __forceinline__ void fetch_bytes(const uint8_t *p, int nbytes, uint32
         }
         out[i] = v;
     }
+}
+
+// The dword holding byte p (aligned down, global address space kept).
+__device__ __forceinline__ const uint32_t *dword_at(const uint8_t *p) {
+    return reinterpret_cast<const uint32_t *>(p - ((uintptr_t)p & 3u));
 }
 
 __device__ __forceinline__ uint32_t byte_of(uint32_t v, int i) { return (v >> (8 * i)) & 0xFFu; }
@@ -85,6 +92,30 @@ __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
     return v;
+}
+
+// Sum over the 64 lanes of a wavefront in a fixed order, result valid in
+// lane 63: DPP butterflies inside each row of 16 lanes, then the row
+// broadcasts of lane 15 / lane 31.
+__device__ __forceinline__ float wave_sum_to_lane63(float v) {
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));  // quad_perm 1,0,3,2
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true));  // quad_perm 2,3,0,1
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, true)); // row_half_mirror
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, true)); // row_mirror
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x142, 0xA, 0xF, false)); // row_bcast15
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x143, 0xC, 0xF, false)); // row_bcast31
+    return v;
+}
+
+// The f16 pairs {1024 + byte0, 1024 + byte2} and {1024 + byte1, 1024 + byte3}
+// of a dword, one v_perm_b32 each: 0x64 is the high byte of f16 1024.0 and the
+// byte lands in the low mantissa bits, so byte b becomes exactly 1024 + b.
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ half2_t bytes02_as_f16(uint32_t v) {
+    return __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, v, 0x04020400u));
+}
+__device__ __forceinline__ half2_t bytes13_as_f16(uint32_t v) {
+    return __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, v, 0x04030401u));
 }
 
 }  // namespace qmm

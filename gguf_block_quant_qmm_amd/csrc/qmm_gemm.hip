@@ -46,7 +46,7 @@ template <bool GEN> struct WTile<QMM_Q4_0, GEN> {
             fetch_bytes(p, 18, w);
         } else {
             sh = (uint32_t)((uintptr_t)p & 3u);
-            fetch_al(reinterpret_cast<const uint8_t *>((uintptr_t)p & ~(uintptr_t)3), w);
+            fetch_al(reinterpret_cast<const uint8_t *>(dword_at(p)), w);
         }
         v[0] = w[0] >> (8 * sh);
 #pragma unroll
@@ -81,7 +81,7 @@ template <bool GEN> struct WTile<QMM_Q8_0, GEN> {
             fetch_bytes(p, 34, w);
         } else {
             sh = (uint32_t)((uintptr_t)p & 3u);
-            fetch_al(reinterpret_cast<const uint8_t *>((uintptr_t)p & ~(uintptr_t)3), w);
+            fetch_al(reinterpret_cast<const uint8_t *>(dword_at(p)), w);
         }
         v[0] = w[0] >> (8 * sh);
 #pragma unroll
@@ -166,9 +166,9 @@ template <bool GEN> struct WTile<QMM_Q6_K, GEN> {
             fetch_un(p + 64 * h + 32 * (g & 1), a);
             fetch_un(p + 128 + 32 * h, c);
             const uint8_t *ps = p + 192 + 8 * h + 2 * g;
-            const uint32_t sw = *reinterpret_cast<const uint32_t *>((uintptr_t)ps & ~(uintptr_t)3);
+            const uint32_t sw = *dword_at(ps);
             const uint8_t *pd = p + 208;
-            const uint32_t dw = *reinterpret_cast<const uint32_t *>((uintptr_t)pd & ~(uintptr_t)3);
+            const uint32_t dw = *dword_at(pd);
             scd = ((sw >> (8 * ((uintptr_t)ps & 3))) & 0xFFFFu) | ((dw >> (8 * ((uintptr_t)pd & 3))) << 16);
         }
 #pragma unroll

@@ -15,6 +15,9 @@
 //     cross-lane shuffles and across wavefronts through LDS, in a fixed order.
 // The per-element weight is exact in f32 for Q8_0, Q4_0 and Q6_K and rounded
 // once for Q4_K (fma(d*sc, q, -dmin*m)).
+#include <algorithm>
+#include <cstdlib>
+
 #include "qmm_device.hpp"
 #include "qmm_internal.hpp"
 
@@ -29,9 +32,16 @@ namespace qmm {
 
 template <int DT> struct Unit;
 
+// Exact f16 of a small integer code c: bytes02/13_as_f16 give 1024 + c, and
+// one packed f16 add of -(1024 + bias) leaves c - bias with no rounding (all
+// values are integers below 2048).  v_fma_mix_f32 then multiplies the f16 by
+// the f32 activation inside an f32 FMA, so every product and sum is f32.
+__device__ __forceinline__ float fma_h(_Float16 h, float x, float acc) { return fmaf((float)h, x, acc); }
+
 template <> struct Unit<QMM_Q4_0> {
     static constexpr int NDW = 9;
-    __device__ static void load(const uint8_t *row, int u, uint32_t (&v)[NDW]) { fetch_al(row + 36 * u, v); }
+    template <bool NT>
+    __device__ static void load(const uint8_t *row, int u, uint32_t (&v)[NDW]) { fetch_al<NDW, NT>(row + 36 * u, v); }
     __device__ static void load_x(const float *x, int u, float (&xv)[64]) {
         const floatx4 *p = reinterpret_cast<const floatx4 *>(x + 64 * u);
 #pragma unroll
@@ -41,30 +51,23 @@ template <> struct Unit<QMM_Q4_0> {
         }
     }
     __device__ static float dot(const uint32_t (&v)[NDW], const float (&xv)[64], int) {
+        const half2_t bias = {(_Float16)-1032.0f, (_Float16)-1032.0f};  // q - 8
         float total = 0.f;
 #pragma unroll
         for (int b = 0; b < 2; b++) {
-            uint32_t q[4];
-            float d;
-            if (b == 0) {
-#pragma unroll
-                for (int i = 0; i < 4; i++) q[i] = __builtin_amdgcn_alignbyte(v[i + 1], v[i], 2);
-                d = h2f(v[0]);
-            } else {
-#pragma unroll
-                for (int i = 0; i < 4; i++) q[i] = v[5 + i];
-                d = h2f(v[4] >> 16);
-            }
+            const float d = b == 0 ? h2f(v[0]) : h2f(v[4] >> 16);
             float slo = 0.f, shi = 0.f;
 #pragma unroll
             for (int i = 0; i < 4; i++) {
-#pragma unroll
-                for (int c = 0; c < 4; c++) {
-                    const int lo = (int)((q[i] >> (8 * c)) & 15u) - 8;
-                    const int hi = (int)((q[i] >> (8 * c + 4)) & 15u) - 8;
-                    slo = fmaf((float)lo, xv[32 * b + 4 * i + c], slo);
-                    shi = fmaf((float)hi, xv[32 * b + 16 + 4 * i + c], shi);
-                }
+                const uint32_t q = b == 0 ? __builtin_amdgcn_alignbyte(v[i + 1], v[i], 2) : v[5 + i];
+                const uint32_t L = q & 0x0F0F0F0Fu, H = (q >> 4) & 0x0F0F0F0Fu;
+                const half2_t l02 = bytes02_as_f16(L) + bias, l13 = bytes13_as_f16(L) + bias;
+                const half2_t h02 = bytes02_as_f16(H) + bias, h13 = bytes13_as_f16(H) + bias;
+                const float *xl = xv + 32 * b + 4 * i, *xh = xl + 16;
+                slo = fma_h(l02.x, xl[0], slo); slo = fma_h(l13.x, xl[1], slo);
+                slo = fma_h(l02.y, xl[2], slo); slo = fma_h(l13.y, xl[3], slo);
+                shi = fma_h(h02.x, xh[0], shi); shi = fma_h(h13.x, xh[1], shi);
+                shi = fma_h(h02.y, xh[2], shi); shi = fma_h(h13.y, xh[3], shi);
             }
             total = fmaf(d, slo + shi, total);
         }
@@ -74,32 +77,24 @@ template <> struct Unit<QMM_Q4_0> {
 
 template <> struct Unit<QMM_Q8_0> {
     static constexpr int NDW = 17;
-    __device__ static void load(const uint8_t *row, int u, uint32_t (&v)[NDW]) { fetch_al(row + 68 * u, v); }
+    template <bool NT>
+    __device__ static void load(const uint8_t *row, int u, uint32_t (&v)[NDW]) { fetch_al<NDW, NT>(row + 68 * u, v); }
     __device__ static void load_x(const float *x, int u, float (&xv)[64]) { Unit<QMM_Q4_0>::load_x(x, u, xv); }
     __device__ static float dot(const uint32_t (&v)[NDW], const float (&xv)[64], int) {
+        const half2_t bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};  // (q + 128) - 128
         float total = 0.f;
 #pragma unroll
         for (int b = 0; b < 2; b++) {
-            uint32_t q[8];
-            float d;
-            if (b == 0) {
-#pragma unroll
-                for (int i = 0; i < 8; i++) q[i] = __builtin_amdgcn_alignbyte(v[i + 1], v[i], 2);
-                d = h2f(v[0]);
-            } else {
-#pragma unroll
-                for (int i = 0; i < 8; i++) q[i] = v[9 + i];
-                d = h2f(v[8] >> 16);
-            }
+            const float d = b == 0 ? h2f(v[0]) : h2f(v[8] >> 16);
             float s0 = 0.f, s1 = 0.f;
 #pragma unroll
             for (int i = 0; i < 8; i++) {
-#pragma unroll
-                for (int c = 0; c < 4; c++) {
-                    const float w = (float)(int8_t)(uint8_t)((q[i] >> (8 * c)) & 0xFFu);
-                    if (i < 4) s0 = fmaf(w, xv[32 * b + 4 * i + c], s0);
-                    else       s1 = fmaf(w, xv[32 * b + 4 * i + c], s1);
-                }
+                const uint32_t q = (b == 0 ? __builtin_amdgcn_alignbyte(v[i + 1], v[i], 2) : v[9 + i]) ^ 0x80808080u;
+                const half2_t p02 = bytes02_as_f16(q) + bias, p13 = bytes13_as_f16(q) + bias;
+                const float *xp = xv + 32 * b + 4 * i;
+                float &s = i < 4 ? s0 : s1;
+                s = fma_h(p02.x, xp[0], s); s = fma_h(p13.x, xp[1], s);
+                s = fma_h(p02.y, xp[2], s); s = fma_h(p13.y, xp[3], s);
             }
             total = fmaf(d, s0 + s1, total);
         }
@@ -109,11 +104,12 @@ template <> struct Unit<QMM_Q8_0> {
 
 template <> struct Unit<QMM_Q4_K> {
     static constexpr int NDW = 12;  // 4 header dwords (d, dmin, 12 scale bytes) + 8 nibble dwords
+    template <bool NT>
     __device__ static void load(const uint8_t *row, int u, uint32_t (&v)[NDW]) {
         const uint8_t *sb = row + 144 * (u >> 2);
         uint32_t h[4], q[8];
-        fetch_al(sb, h);
-        fetch_al(sb + 16 + 32 * (u & 3), q);
+        fetch_al<4, NT>(sb, h);
+        fetch_al<8, NT>(sb + 16 + 32 * (u & 3), q);
 #pragma unroll
         for (int i = 0; i < 4; i++) v[i] = h[i];
 #pragma unroll
@@ -121,6 +117,7 @@ template <> struct Unit<QMM_Q4_K> {
     }
     __device__ static void load_x(const float *x, int u, float (&xv)[64]) { Unit<QMM_Q4_0>::load_x(x, u, xv); }
     __device__ static float dot(const uint32_t (&v)[NDW], const float (&xv)[64], int u) {
+        const half2_t bias = {(_Float16)-1024.0f, (_Float16)-1024.0f};  // q
         const float d = h2f(v[0]), dmin = h2f(v[0] >> 16);
         const int c = u & 3;
         float total = 0.f;
@@ -132,13 +129,15 @@ template <> struct Unit<QMM_Q4_K> {
             float s0 = 0.f, s1 = 0.f;
 #pragma unroll
             for (int i = 0; i < 8; i++) {
-#pragma unroll
-                for (int b = 0; b < 4; b++) {
-                    const float q = (float)((v[4 + i] >> (8 * b + 4 * half)) & 15u);
-                    const float w = fmaf(dsc, q, ndm);
-                    if (i < 4) s0 = fmaf(w, xv[32 * half + 4 * i + b], s0);
-                    else       s1 = fmaf(w, xv[32 * half + 4 * i + b], s1);
-                }
+                const uint32_t n = (v[4 + i] >> (4 * half)) & 0x0F0F0F0Fu;
+                const half2_t q02 = bytes02_as_f16(n) + bias, q13 = bytes13_as_f16(n) + bias;
+                const float *xp = xv + 32 * half + 4 * i;
+                float &s = i < 4 ? s0 : s1;
+                // weight = d*sc*q - dmin*m, one f32 rounding; then the f32 FMA with x
+                s = fmaf(fmaf(dsc, (float)q02.x, ndm), xp[0], s);
+                s = fmaf(fmaf(dsc, (float)q13.x, ndm), xp[1], s);
+                s = fmaf(fmaf(dsc, (float)q02.y, ndm), xp[2], s);
+                s = fmaf(fmaf(dsc, (float)q13.y, ndm), xp[3], s);
             }
             total += s0 + s1;
         }
@@ -152,16 +151,18 @@ template <> struct Unit<QMM_Q6_K> {
     // super-blocks per row so that only even (4-aligned) blocks read past
     // their own last byte, and never past the blob.
     static constexpr int NDW = 4 + 4 + 4 + 2 + 1;
+    template <bool NT>
     __device__ static void load(const uint8_t *row, int u, uint32_t (&v)[NDW]) {
         const uint8_t *p = row + 210 * (u >> 2);
         const int h = (u >> 1) & 1, lh = u & 1;
         uint32_t a[4], b[4], c[4], s[2];
-        fetch_un(p + 64 * h + 16 * lh, a);
-        fetch_un(p + 64 * h + 32 + 16 * lh, b);
-        fetch_un(p + 128 + 32 * h + 16 * lh, c);
-        fetch_un(p + 192 + 8 * h, s);
+        fetch_un<4, NT>(p + 64 * h + 16 * lh, a);
+        fetch_un<4, NT>(p + 64 * h + 32 + 16 * lh, b);
+        fetch_un<4, NT>(p + 128 + 32 * h + 16 * lh, c);
+        fetch_un<2, NT>(p + 192 + 8 * h, s);
         const uint8_t *pd = p + 208;
-        const uint32_t dw = *reinterpret_cast<const uint32_t *>((uintptr_t)pd & ~(uintptr_t)3);
+        const uint32_t *pdw = dword_at(pd);
+        const uint32_t dw = NT ? __builtin_nontemporal_load(pdw) : *pdw;
 #pragma unroll
         for (int i = 0; i < 4; i++) { v[i] = a[i]; v[4 + i] = b[i]; v[8 + i] = c[i]; }
         v[12] = s[0]; v[13] = s[1];
@@ -182,6 +183,7 @@ template <> struct Unit<QMM_Q6_K> {
         }
     }
     __device__ static float dot(const uint32_t (&v)[NDW], const float (&xv)[64], int u) {
+        const half2_t bias = {(_Float16)-1056.0f, (_Float16)-1056.0f};  // q - 32
         const int lh = u & 1;
         const float d = h2f(v[14]);
         float total = 0.f;
@@ -193,14 +195,14 @@ template <> struct Unit<QMM_Q6_K> {
 #pragma unroll
             for (int t = 0; t < 4; t++) {
                 const uint32_t L = (g & 1) ? v[4 + t] : v[t];
+                const uint32_t lo = (g < 2 ? L : (L >> 4)) & 0x0F0F0F0Fu;
                 const uint32_t C = v[8 + t];
-#pragma unroll
-                for (int b = 0; b < 4; b++) {
-                    const uint32_t lo = (L >> (8 * b + (g >= 2 ? 4 : 0))) & 15u;
-                    const uint32_t hi = (C >> (8 * b + 2 * g)) & 3u;
-                    const float w = (float)((int)(lo | (hi << 4)) - 32);
-                    s = fmaf(w, xv[16 * g + 4 * t + b], s);
-                }
+                const uint32_t hi = (g < 2 ? (C << (4 - 2 * g)) : (C >> (2 * g - 4))) & 0x30303030u;
+                const uint32_t q = lo | hi;  // four 6-bit codes, one per byte
+                const half2_t q02 = bytes02_as_f16(q) + bias, q13 = bytes13_as_f16(q) + bias;
+                const float *xp = xv + 16 * g + 4 * t;
+                s = fma_h(q02.x, xp[0], s); s = fma_h(q13.x, xp[1], s);
+                s = fma_h(q02.y, xp[2], s); s = fma_h(q13.y, xp[3], s);
             }
             total = fmaf(dsc, s, total);
         }
@@ -209,41 +211,106 @@ template <> struct Unit<QMM_Q6_K> {
 };
 
 // ----------------------------------------------------------- fast kernel ----
-// R rows per group; ONE_UNIT: every thread owns at most one unit of the row,
-// so its activations are loaded once.
-template <int DT, int R, bool ONE_UNIT>
+// Every thread owns at most one unit of the row (U <= blockDim.x), so its 64
+// activations are loaded once and stay in registers while the workgroup
+// walks its row groups (R rows each, grid stride).  The raw bytes of the next
+// row group are fetched before the current one is decoded (two register
+// buffers, loop unrolled by two so neither is indexed dynamically).
+template <int DT, int R>
 __global__ void __launch_bounds__(256) gemv_kernel(const uint8_t *__restrict__ blob, int64_t M,
-                                                    int64_t row_bytes, int U,
-                                                    const float *__restrict__ x, float *__restrict__ y) {
+                                                   int64_t row_bytes, int U,
+                                                   const float *__restrict__ x, float *__restrict__ y) {
+    constexpr int NDW = Unit<DT>::NDW;
+    __shared__ float red[2][R][4];
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6, nwaves = blockDim.x >> 6;
+    const bool active = t < U;
+    const int64_t nrg = (M + R - 1) / R;
+    float xv[64];
+    if (active) Unit<DT>::load_x(x, t, xv);
+
+    auto fetch = [&](int64_t g, uint32_t (&raw)[R][NDW]) {
+#pragma unroll
+        for (int r = 0; r < R; r++) {
+            const int64_t row = g * R + r;
+            if (active && row < M) Unit<DT>::template load<false>(blob + row * row_bytes, t, raw[r]);
+        }
+    };
+    auto finish = [&](int64_t g, const uint32_t (&raw)[R][NDW], int parity) {
+        float acc[R];
+#pragma unroll
+        for (int r = 0; r < R; r++) {
+            acc[r] = (active && g * R + r < M) ? Unit<DT>::dot(raw[r], xv, t) : 0.f;
+            acc[r] = wave_sum_to_lane63(acc[r]);
+        }
+        if (nwaves == 1) {
+            if (lane == 63) {
+#pragma unroll
+                for (int r = 0; r < R; r++)
+                    if (g * R + r < M) y[g * R + r] = acc[r];
+            }
+        } else {
+            if (lane == 63) {
+#pragma unroll
+                for (int r = 0; r < R; r++) red[parity][r][wave] = acc[r];
+            }
+            __syncthreads();
+            if (t < R && g * R + t < M) {
+                float s = red[parity][t][0];
+                for (int w = 1; w < nwaves; w++) s += red[parity][t][w];
+                y[g * R + t] = s;
+            }
+        }
+    };
+
+    uint32_t ra[R][NDW], rb[R][NDW];
+    int64_t g = blockIdx.x;
+    if (g < nrg) fetch(g, ra);
+    while (g < nrg) {
+        const int64_t g1 = g + gridDim.x;
+        if (g1 < nrg) fetch(g1, rb);
+        finish(g, ra, 0);
+        if (g1 >= nrg) break;
+        const int64_t g2 = g1 + gridDim.x;
+        if (g2 < nrg) fetch(g2, ra);
+        finish(g1, rb, 1);
+        g = g2;
+    }
+}
+
+// More units than threads (K > 64 * 256): each thread loops over its units
+// and reloads their activations for every row group.
+template <int DT, int R>
+__global__ void __launch_bounds__(256) gemv_multi_kernel(const uint8_t *__restrict__ blob, int64_t M,
+                                                         int64_t row_bytes, int U,
+                                                         const float *__restrict__ x, float *__restrict__ y) {
     __shared__ float red[R][4];
     const int t = threadIdx.x, T = blockDim.x, lane = t & 63, wave = t >> 6, nwaves = T >> 6;
     const int64_t nrg = (M + R - 1) / R;
     float xv[64];
-    if (ONE_UNIT && t < U) Unit<DT>::load_x(x, t, xv);
     for (int64_t rg = blockIdx.x; rg < nrg; rg += gridDim.x) {
         const int64_t row0 = rg * R;
         float acc[R];
 #pragma unroll
         for (int r = 0; r < R; r++) acc[r] = 0.f;
         for (int u = t; u < U; u += T) {
-            if (!ONE_UNIT) Unit<DT>::load_x(x, u, xv);
+            Unit<DT>::load_x(x, u, xv);
             uint32_t raw[R][Unit<DT>::NDW];
 #pragma unroll
             for (int r = 0; r < R; r++)
-                if (row0 + r < M) Unit<DT>::load(blob + (row0 + r) * row_bytes, u, raw[r]);
+                if (row0 + r < M) Unit<DT>::template load<false>(blob + (row0 + r) * row_bytes, u, raw[r]);
 #pragma unroll
             for (int r = 0; r < R; r++)
                 if (row0 + r < M) acc[r] += Unit<DT>::dot(raw[r], xv, u);
         }
 #pragma unroll
         for (int r = 0; r < R; r++) {
-            const float s = wave_sum(acc[r]);
-            if (lane == 0) red[r][wave] = s;
+            const float s = wave_sum_to_lane63(acc[r]);
+            if (lane == 63) red[r][wave] = s;
         }
         __syncthreads();
         if (t < R && row0 + t < M) {
-            float s = 0.f;
-            for (int w = 0; w < nwaves; w++) s += red[t][w];
+            float s = red[t][0];
+            for (int w = 1; w < nwaves; w++) s += red[t][w];
             y[row0 + t] = s;
         }
         __syncthreads();
@@ -340,8 +407,8 @@ __global__ void __launch_bounds__(256) gemv_generic_kernel(const uint8_t *__rest
             for (int r = 0; r < R; r++)
                 if (row0 + r < M) acc[r] += block_dot_generic<DT>(blob + (row0 + r) * row_bytes + b * BB, x + b * BS);
         for (int r = 0; r < R; r++) {
-            const float s = wave_sum(acc[r]);
-            if (lane == 0) red[r][wave] = s;
+            const float s = wave_sum_to_lane63(acc[r]);
+            if (lane == 63) red[r][wave] = s;
         }
         __syncthreads();
         if (t < R && row0 + t < M) {
@@ -365,6 +432,17 @@ static bool fast_layout_ok(int dtype, int64_t nb) {
     }
 }
 
+// Resident workgroups per CU for the persistent GEMV; QMM_GEMV_WAVES_PER_CU
+// overrides the default (a tuning lever, read once).
+static int gemv_waves_per_cu() {
+    static int v = [] {
+        const char *e = getenv("QMM_GEMV_WAVES_PER_CU");
+        const int n = e ? atoi(e) : 0;
+        return (n >= 1 && n <= 32) ? n : 8;
+    }();
+    return v;
+}
+
 template <int DT, int R>
 static hipError_t launch_fast(const uint8_t *blob, int64_t M, int64_t K, const float *x, float *y,
                               hipStream_t st, int cus) {
@@ -374,12 +452,12 @@ static hipError_t launch_fast(const uint8_t *blob, int64_t M, int64_t K, const f
     const int T = (int)(U64 >= 256 ? 256 : ((U64 + 63) / 64) * 64);
     const int U = (int)U64;
     const int64_t nrg = (M + R - 1) / R;
-    const int64_t per_cu = (2048 / T) > 0 ? (2048 / T) : 1;  // up to 32 waves resident per CU
-    const int64_t grid = nrg < cus * per_cu ? nrg : cus * per_cu;
-    if (U <= T)
-        hipLaunchKernelGGL((gemv_kernel<DT, R, true>), dim3((unsigned)grid), dim3(T), 0, st, blob, M, row_bytes, U, x, y);
+    const int64_t wg_per_cu = std::max<int64_t>(1, gemv_waves_per_cu() / (T / 64));
+    const int64_t grid = std::min<int64_t>(nrg, (int64_t)cus * wg_per_cu);
+    if (U64 <= 256)
+        hipLaunchKernelGGL((gemv_kernel<DT, R>), dim3((unsigned)grid), dim3(T), 0, st, blob, M, row_bytes, U, x, y);
     else
-        hipLaunchKernelGGL((gemv_kernel<DT, R, false>), dim3((unsigned)grid), dim3(T), 0, st, blob, M, row_bytes, U, x, y);
+        hipLaunchKernelGGL((gemv_multi_kernel<DT, R>), dim3((unsigned)grid), dim3(T), 0, st, blob, M, row_bytes, U, x, y);
     return hipGetLastError();
 }
 
