@@ -3,16 +3,19 @@
 // Decode is a stream of the packed weight (page "cera 0.3.1
 // src/model/gpu_lfm2.rs", forward_inner_compute: decode is memory-bound inside
 // the quantized GEMVs).  Design for gfx950:
-//   * a workgroup owns R rows at a time and walks row groups with a grid stride;
-//   * its threads split each row into 64-weight units, every thread keeps the
-//     64 activations of its unit in registers and reuses them for all R rows
-//     (when a row has no more units than the workgroup has threads, the
-//     activations are loaded once for the workgroup's whole life);
-//   * weight bytes arrive as aligned dword loads; 18/34/210-byte blocks that
-//     straddle dwords are realigned in registers with v_alignbyte;
-//   * each unit is decoded in registers and accumulated with f32 FMAs in short
-//     chains (16 terms per chain), then reduced across the wavefront with
-//     cross-lane shuffles and across wavefronts through LDS, in a fixed order.
+//   * a row is cut into 64-weight units, one per lane; every lane keeps the 64
+//     activations of its unit in registers for the whole kernel (staged once
+//     per workgroup through LDS with coalesced loads);
+//   * a wavefront (K <= 4096) or a workgroup of up to 4 wavefronts splitting K
+//     (K <= 16384) owns a balanced contiguous range of row groups (R rows) and
+//     keeps D row groups in flight in registers while it decodes the current
+//     one, so memory and ALU work overlap;
+//   * weight bytes arrive as dword loads addressed from a uniform row pointer
+//     plus a per-lane 32-bit offset; 18/34/210-byte blocks that straddle
+//     dwords are realigned in registers with v_alignbyte;
+//   * codes become exact f16 values (v_perm_b32 + one packed f16 subtract) and
+//     multiply the f32 activations inside v_fma_mix_f32 (f32 FMA), in chains
+//     of 16 terms, reduced across the wavefront with DPP in a fixed order.
 // The per-element weight is exact in f32 for Q8_0, Q4_0 and Q6_K and rounded
 // once for Q4_K (fma(d*sc, q, -dmin*m)).
 #include <algorithm>
@@ -23,262 +26,334 @@
 
 namespace qmm {
 
+__device__ __forceinline__ float fma_h(_Float16 h, float x, float acc) { return fmaf((float)h, x, acc); }
+
+template <int N>
+__device__ __forceinline__ void ld(const uint8_t *p, uint32_t off, uint32_t (&v)[N]) {
+    const uint32_t *q = reinterpret_cast<const uint32_t *>(p + off);
+#pragma unroll
+    for (int i = 0; i < N; i++) v[i] = q[i];
+}
+
 // ----------------------------------------------------------------- units ----
 // A unit is 64 weights of one row.  Q8_0/Q4_0: a pair of consecutive blocks
-// (needs an even number of blocks per row so every pair is dword aligned).
-// Q4_K: one 64-weight chunk of a super-block (sub-blocks 2c and 2c+1).
-// Q6_K: the 64 weights {128h + 32g + 16lh + i : g < 4, i < 16} of one
-// super-block, which share one 16-byte slice of each ql half and of qh.
+// (an even number of blocks per row keeps every pair dword aligned).  Q4_K:
+// one 64-weight chunk of a super-block (sub-blocks 2c and 2c+1).  Q6_K: the 64
+// weights {128h + 32g + 16lh + i : g < 4, i < 16} of one super-block, which
+// share one 16-byte slice of each ql half and of qh.
+//   Off          per-lane byte offsets inside a row (computed once)
+//   load(row,o)  the unit's raw dwords (row pointer uniform across the wave)
+//   x4(u, i)     float4 index of local activations 4i..4i+3 of unit u
+//   dot(v,x,o)   the unit's dot product, f32
 
 template <int DT> struct Unit;
 
-// Exact f16 of a small integer code c: bytes02/13_as_f16 give 1024 + c, and
-// one packed f16 add of -(1024 + bias) leaves c - bias with no rounding (all
-// values are integers below 2048).  v_fma_mix_f32 then multiplies the f16 by
-// the f32 activation inside an f32 FMA, so every product and sum is f32.
-__device__ __forceinline__ float fma_h(_Float16 h, float x, float acc) { return fmaf((float)h, x, acc); }
-
 template <> struct Unit<QMM_Q4_0> {
-    static constexpr int NDW = 9;
-    template <bool NT>
-    __device__ static void load(const uint8_t *row, int u, uint32_t (&v)[NDW]) { fetch_al<NDW, NT>(row + 36 * u, v); }
-    __device__ static void load_x(const float *x, int u, float (&xv)[64]) {
-        const floatx4 *p = reinterpret_cast<const floatx4 *>(x + 64 * u);
-#pragma unroll
-        for (int i = 0; i < 16; i++) {
-            floatx4 t = p[i];
-            xv[4 * i] = t.x; xv[4 * i + 1] = t.y; xv[4 * i + 2] = t.z; xv[4 * i + 3] = t.w;
-        }
-    }
-    __device__ static float dot(const uint32_t (&v)[NDW], const float (&xv)[64], int) {
+    static constexpr int NL = 9;
+    struct Off { uint32_t a; };
+    __device__ static Off lane_off(int u) { return {36u * u}; }
+    __device__ static void load(const uint8_t *row, const Off &o, uint32_t (&v)[NL]) { ld(row, o.a, v); }
+    __device__ static int x4(int u, int i) { return 16 * u + i; }
+    __device__ static float dot(const uint32_t (&v)[NL], const float (&xv)[64], const Off &) {
+        // one accumulator per dword of codes (4 terms each): 16 independent
+        // FMA chains per unit keep the VALU pipeline full
         const half2_t bias = {(_Float16)-1032.0f, (_Float16)-1032.0f};  // q - 8
-        float total = 0.f;
+        float blk[2];
 #pragma unroll
         for (int b = 0; b < 2; b++) {
-            const float d = b == 0 ? h2f(v[0]) : h2f(v[4] >> 16);
-            float slo = 0.f, shi = 0.f;
+            // decode the block's 32 codes first, then issue the FMAs round-robin
+            // over 8 accumulators so that consecutive FMAs are independent
+            half2_t w[4][4];  // [dword][l02, l13, h02, h13]
 #pragma unroll
             for (int i = 0; i < 4; i++) {
                 const uint32_t q = b == 0 ? __builtin_amdgcn_alignbyte(v[i + 1], v[i], 2) : v[5 + i];
                 const uint32_t L = q & 0x0F0F0F0Fu, H = (q >> 4) & 0x0F0F0F0Fu;
-                const half2_t l02 = bytes02_as_f16(L) + bias, l13 = bytes13_as_f16(L) + bias;
-                const half2_t h02 = bytes02_as_f16(H) + bias, h13 = bytes13_as_f16(H) + bias;
-                const float *xl = xv + 32 * b + 4 * i, *xh = xl + 16;
-                slo = fma_h(l02.x, xl[0], slo); slo = fma_h(l13.x, xl[1], slo);
-                slo = fma_h(l02.y, xl[2], slo); slo = fma_h(l13.y, xl[3], slo);
-                shi = fma_h(h02.x, xh[0], shi); shi = fma_h(h13.x, xh[1], shi);
-                shi = fma_h(h02.y, xh[2], shi); shi = fma_h(h13.y, xh[3], shi);
+                w[i][0] = bytes02_as_f16(L) + bias; w[i][1] = bytes13_as_f16(L) + bias;
+                w[i][2] = bytes02_as_f16(H) + bias; w[i][3] = bytes13_as_f16(H) + bias;
             }
-            total = fmaf(d, slo + shi, total);
+            const float *xb = xv + 32 * b;
+            float s8[8];
+#pragma unroll
+            for (int i = 0; i < 4; i++) { s8[i] = fma_h(w[i][0].x, xb[4 * i], 0.f); s8[4 + i] = fma_h(w[i][2].x, xb[16 + 4 * i], 0.f); }
+#pragma unroll
+            for (int i = 0; i < 4; i++) { s8[i] = fma_h(w[i][1].x, xb[4 * i + 1], s8[i]); s8[4 + i] = fma_h(w[i][3].x, xb[16 + 4 * i + 1], s8[4 + i]); }
+#pragma unroll
+            for (int i = 0; i < 4; i++) { s8[i] = fma_h(w[i][0].y, xb[4 * i + 2], s8[i]); s8[4 + i] = fma_h(w[i][2].y, xb[16 + 4 * i + 2], s8[4 + i]); }
+#pragma unroll
+            for (int i = 0; i < 4; i++) { s8[i] = fma_h(w[i][1].y, xb[4 * i + 3], s8[i]); s8[4 + i] = fma_h(w[i][3].y, xb[16 + 4 * i + 3], s8[4 + i]); }
+            blk[b] = ((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7]));
         }
-        return total;
+        return fmaf(h2f(v[4] >> 16), blk[1], h2f(v[0]) * blk[0]);
     }
 };
 
 template <> struct Unit<QMM_Q8_0> {
-    static constexpr int NDW = 17;
-    template <bool NT>
-    __device__ static void load(const uint8_t *row, int u, uint32_t (&v)[NDW]) { fetch_al<NDW, NT>(row + 68 * u, v); }
-    __device__ static void load_x(const float *x, int u, float (&xv)[64]) { Unit<QMM_Q4_0>::load_x(x, u, xv); }
-    __device__ static float dot(const uint32_t (&v)[NDW], const float (&xv)[64], int) {
+    static constexpr int NL = 17;
+    struct Off { uint32_t a; };
+    __device__ static Off lane_off(int u) { return {68u * u}; }
+    __device__ static void load(const uint8_t *row, const Off &o, uint32_t (&v)[NL]) { ld(row, o.a, v); }
+    __device__ static int x4(int u, int i) { return 16 * u + i; }
+    __device__ static float dot(const uint32_t (&v)[NL], const float (&xv)[64], const Off &) {
         const half2_t bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};  // (q + 128) - 128
-        float total = 0.f;
+        float blk[2];
 #pragma unroll
         for (int b = 0; b < 2; b++) {
-            const float d = b == 0 ? h2f(v[0]) : h2f(v[8] >> 16);
-            float s0 = 0.f, s1 = 0.f;
+            half2_t w[8][2];  // [dword][p02, p13]
 #pragma unroll
             for (int i = 0; i < 8; i++) {
                 const uint32_t q = (b == 0 ? __builtin_amdgcn_alignbyte(v[i + 1], v[i], 2) : v[9 + i]) ^ 0x80808080u;
-                const half2_t p02 = bytes02_as_f16(q) + bias, p13 = bytes13_as_f16(q) + bias;
-                const float *xp = xv + 32 * b + 4 * i;
-                float &s = i < 4 ? s0 : s1;
-                s = fma_h(p02.x, xp[0], s); s = fma_h(p13.x, xp[1], s);
-                s = fma_h(p02.y, xp[2], s); s = fma_h(p13.y, xp[3], s);
+                w[i][0] = bytes02_as_f16(q) + bias; w[i][1] = bytes13_as_f16(q) + bias;
             }
-            total = fmaf(d, s0 + s1, total);
+            const float *xb = xv + 32 * b;
+            float s8[8];
+#pragma unroll
+            for (int i = 0; i < 8; i++) s8[i] = fma_h(w[i][0].x, xb[4 * i], 0.f);
+#pragma unroll
+            for (int i = 0; i < 8; i++) s8[i] = fma_h(w[i][1].x, xb[4 * i + 1], s8[i]);
+#pragma unroll
+            for (int i = 0; i < 8; i++) s8[i] = fma_h(w[i][0].y, xb[4 * i + 2], s8[i]);
+#pragma unroll
+            for (int i = 0; i < 8; i++) s8[i] = fma_h(w[i][1].y, xb[4 * i + 3], s8[i]);
+            blk[b] = ((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7]));
         }
-        return total;
+        return fmaf(h2f(v[8] >> 16), blk[1], h2f(v[0]) * blk[0]);
     }
 };
 
 template <> struct Unit<QMM_Q4_K> {
-    static constexpr int NDW = 12;  // 4 header dwords (d, dmin, 12 scale bytes) + 8 nibble dwords
-    template <bool NT>
-    __device__ static void load(const uint8_t *row, int u, uint32_t (&v)[NDW]) {
-        const uint8_t *sb = row + 144 * (u >> 2);
+    static constexpr int NL = 12;  // 4 header dwords (d, dmin, 12 scale bytes) + 8 nibble dwords
+    struct Off { uint32_t hdr, qs; int c; };
+    __device__ static Off lane_off(int u) {
+        const uint32_t h = 144u * (u >> 2);
+        return {h, h + 16u + 32u * (u & 3), u & 3};
+    }
+    __device__ static void load(const uint8_t *row, const Off &o, uint32_t (&v)[NL]) {
         uint32_t h[4], q[8];
-        fetch_al<4, NT>(sb, h);
-        fetch_al<8, NT>(sb + 16 + 32 * (u & 3), q);
+        ld(row, o.hdr, h);
+        ld(row, o.qs, q);
 #pragma unroll
         for (int i = 0; i < 4; i++) v[i] = h[i];
 #pragma unroll
         for (int i = 0; i < 8; i++) v[4 + i] = q[i];
     }
-    __device__ static void load_x(const float *x, int u, float (&xv)[64]) { Unit<QMM_Q4_0>::load_x(x, u, xv); }
-    __device__ static float dot(const uint32_t (&v)[NDW], const float (&xv)[64], int u) {
+    __device__ static int x4(int u, int i) { return 16 * u + i; }
+    __device__ static float dot(const uint32_t (&v)[NL], const float (&xv)[64], const Off &o) {
         const half2_t bias = {(_Float16)-1024.0f, (_Float16)-1024.0f};  // q
         const float d = h2f(v[0]), dmin = h2f(v[0] >> 16);
-        const int c = u & 3;
-        float total = 0.f;
+        float sub[2];
 #pragma unroll
         for (int half = 0; half < 2; half++) {  // sub-block 2c (low nibbles), 2c+1 (high nibbles)
             int sc, mn;
-            q4k_scale_min(v[1], v[2], v[3], 2 * c + half, sc, mn);
+            q4k_scale_min(v[1], v[2], v[3], 2 * o.c + half, sc, mn);
             const float dsc = d * (float)sc, ndm = -(dmin * (float)mn);
-            float s0 = 0.f, s1 = 0.f;
+            // weight = d*sc*q - dmin*m (one f32 rounding), then the f32 FMA with x;
+            // decode all 32 first, then the FMAs round-robin over 8 accumulators
+            float wf[8][4];
 #pragma unroll
             for (int i = 0; i < 8; i++) {
                 const uint32_t n = (v[4 + i] >> (4 * half)) & 0x0F0F0F0Fu;
                 const half2_t q02 = bytes02_as_f16(n) + bias, q13 = bytes13_as_f16(n) + bias;
-                const float *xp = xv + 32 * half + 4 * i;
-                float &s = i < 4 ? s0 : s1;
-                // weight = d*sc*q - dmin*m, one f32 rounding; then the f32 FMA with x
-                s = fmaf(fmaf(dsc, (float)q02.x, ndm), xp[0], s);
-                s = fmaf(fmaf(dsc, (float)q13.x, ndm), xp[1], s);
-                s = fmaf(fmaf(dsc, (float)q02.y, ndm), xp[2], s);
-                s = fmaf(fmaf(dsc, (float)q13.y, ndm), xp[3], s);
+                wf[i][0] = fmaf(dsc, (float)q02.x, ndm); wf[i][1] = fmaf(dsc, (float)q13.x, ndm);
+                wf[i][2] = fmaf(dsc, (float)q02.y, ndm); wf[i][3] = fmaf(dsc, (float)q13.y, ndm);
             }
-            total += s0 + s1;
+            const float *xb = xv + 32 * half;
+            float s[8];
+#pragma unroll
+            for (int i = 0; i < 8; i++) s[i] = wf[i][0] * xb[4 * i];
+#pragma unroll
+            for (int j = 1; j < 4; j++)
+#pragma unroll
+                for (int i = 0; i < 8; i++) s[i] = fmaf(wf[i][j], xb[4 * i + j], s[i]);
+            sub[half] = (((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7])));
         }
-        return total;
+        return sub[0] + sub[1];
     }
 };
 
 template <> struct Unit<QMM_Q6_K> {
-    // A = ql[64h+16lh ..+16], B = ql[64h+32+16lh ..+16], C = qh[32h+16lh ..+16],
-    // S = sc[8h .. 8h+8), D = dword holding d.  Needs an even number of
-    // super-blocks per row so that only even (4-aligned) blocks read past
-    // their own last byte, and never past the blob.
-    static constexpr int NDW = 4 + 4 + 4 + 2 + 1;
-    template <bool NT>
-    __device__ static void load(const uint8_t *row, int u, uint32_t (&v)[NDW]) {
-        const uint8_t *p = row + 210 * (u >> 2);
-        const int h = (u >> 1) & 1, lh = u & 1;
-        uint32_t a[4], b[4], c[4], s[2];
-        fetch_un<4, NT>(p + 64 * h + 16 * lh, a);
-        fetch_un<4, NT>(p + 64 * h + 32 + 16 * lh, b);
-        fetch_un<4, NT>(p + 128 + 32 * h + 16 * lh, c);
-        fetch_un<2, NT>(p + 192 + 8 * h, s);
-        const uint8_t *pd = p + 208;
-        const uint32_t *pdw = dword_at(pd);
-        const uint32_t dw = NT ? __builtin_nontemporal_load(pdw) : *pdw;
-#pragma unroll
-        for (int i = 0; i < 4; i++) { v[i] = a[i]; v[4 + i] = b[i]; v[8 + i] = c[i]; }
-        v[12] = s[0]; v[13] = s[1];
-        v[14] = dw >> (8 * ((uintptr_t)pd & 3));
+    // Windows of dwords starting at the super-block aligned down to 4 bytes
+    // (odd super-blocks start 2 bytes past a dword when rows are dword
+    // aligned): A = ql[64h+16lh ..+16], B = ql[64h+32+16lh ..+16],
+    // C = qh[32h+16lh ..+16] (5 dwords each), S = sc[8h .. 8h+8) (3 dwords),
+    // D = the dword holding d.  An even number of super-blocks per row keeps
+    // every window inside the blob.
+    static constexpr int NL = 5 + 5 + 5 + 3 + 1;
+    struct Off { uint32_t a, c, s, d; int sh, lh; };
+    __device__ static Off lane_off(int u) {
+        const int h = (u >> 1) & 1, lh = u & 1, sh = 2 * ((u >> 2) & 1);
+        const uint32_t base = 210u * (u >> 2) - sh;
+        return {base + 64u * h + 16u * lh, base + 128u + 32u * h + 16u * lh, base + 192u + 8u * h, base + 208u,
+                sh, lh};
     }
-    __device__ static void load_x(const float *x, int u, float (&xv)[64]) {
-        const int h = (u >> 1) & 1, lh = u & 1;
-        const float *base = x + 256 * (u >> 2) + 128 * h + 16 * lh;
+    __device__ static void load(const uint8_t *row, const Off &o, uint32_t (&v)[NL]) {
+        uint32_t a[5], b[5], c[5], s[3], d[1];
+        ld(row, o.a, a);
+        ld(row, o.a + 32u, b);
+        ld(row, o.c, c);
+        ld(row, o.s, s);
+        ld(row, o.d, d);
 #pragma unroll
-        for (int g = 0; g < 4; g++) {
-            const floatx4 *p = reinterpret_cast<const floatx4 *>(base + 32 * g);
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                floatx4 t = p[i];
-                xv[16 * g + 4 * i] = t.x; xv[16 * g + 4 * i + 1] = t.y;
-                xv[16 * g + 4 * i + 2] = t.z; xv[16 * g + 4 * i + 3] = t.w;
-            }
-        }
+        for (int i = 0; i < 5; i++) { v[i] = a[i]; v[5 + i] = b[i]; v[10 + i] = c[i]; }
+        v[15] = s[0]; v[16] = s[1]; v[17] = s[2]; v[18] = d[0];
     }
-    __device__ static float dot(const uint32_t (&v)[NDW], const float (&xv)[64], int u) {
+    __device__ static int x4(int u, int i) {
+        // unit u = 4b + 2h + lh covers x[256b + 128h + 32g + 16lh + j], g < 4, j < 16
+        return 64 * (u >> 2) + 32 * ((u >> 1) & 1) + 8 * (i >> 2) + 4 * (u & 1) + (i & 3);
+    }
+    __device__ static float dot(const uint32_t (&v)[NL], const float (&xv)[64], const Off &o) {
         const half2_t bias = {(_Float16)-1056.0f, (_Float16)-1056.0f};  // q - 32
-        const int lh = u & 1;
-        const float d = h2f(v[14]);
+        const uint32_t sh = (uint32_t)o.sh;
+        const float d = h2f(v[18] >> (8 * sh));
+        const uint32_t sc0 = __builtin_amdgcn_alignbyte(v[16], v[15], sh);  // sc[8h .. 8h+4)
+        const uint32_t sc1 = __builtin_amdgcn_alignbyte(v[17], v[16], sh);  // sc[8h+4 .. 8h+8)
+        float grp[4];
+#pragma unroll
+        for (int gp = 0; gp < 4; gp += 2) {  // two groups at a time: 8 independent chains
+            half2_t w[2][4][2];  // [group][dword][q02, q13]
+#pragma unroll
+            for (int k = 0; k < 2; k++) {
+                const int g = gp + k;
+#pragma unroll
+                for (int t = 0; t < 4; t++) {
+                    const uint32_t L = (g & 1) ? __builtin_amdgcn_alignbyte(v[6 + t], v[5 + t], sh)
+                                               : __builtin_amdgcn_alignbyte(v[1 + t], v[t], sh);
+                    const uint32_t C = __builtin_amdgcn_alignbyte(v[11 + t], v[10 + t], sh);
+                    const uint32_t lo = (g < 2 ? L : (L >> 4)) & 0x0F0F0F0Fu;
+                    const uint32_t hi = (g < 2 ? (C << (4 - 2 * g)) : (C >> (2 * g - 4))) & 0x30303030u;
+                    const uint32_t q = lo | hi;  // four 6-bit codes, one per byte
+                    w[k][t][0] = bytes02_as_f16(q) + bias; w[k][t][1] = bytes13_as_f16(q) + bias;
+                }
+            }
+            float s8[8];
+#pragma unroll
+            for (int k = 0; k < 2; k++)
+#pragma unroll
+                for (int t = 0; t < 4; t++) s8[4 * k + t] = fma_h(w[k][t][0].x, xv[16 * (gp + k) + 4 * t], 0.f);
+#pragma unroll
+            for (int k = 0; k < 2; k++)
+#pragma unroll
+                for (int t = 0; t < 4; t++) s8[4 * k + t] = fma_h(w[k][t][1].x, xv[16 * (gp + k) + 4 * t + 1], s8[4 * k + t]);
+#pragma unroll
+            for (int k = 0; k < 2; k++)
+#pragma unroll
+                for (int t = 0; t < 4; t++) s8[4 * k + t] = fma_h(w[k][t][0].y, xv[16 * (gp + k) + 4 * t + 2], s8[4 * k + t]);
+#pragma unroll
+            for (int k = 0; k < 2; k++)
+#pragma unroll
+                for (int t = 0; t < 4; t++) s8[4 * k + t] = fma_h(w[k][t][1].y, xv[16 * (gp + k) + 4 * t + 3], s8[4 * k + t]);
+            grp[gp] = (s8[0] + s8[1]) + (s8[2] + s8[3]);
+            grp[gp + 1] = (s8[4] + s8[5]) + (s8[6] + s8[7]);
+        }
         float total = 0.f;
 #pragma unroll
         for (int g = 0; g < 4; g++) {
-            const int sidx = 2 * g + lh;  // byte of sc[8h .. 8h+8)
-            const float dsc = d * (float)(int8_t)(uint8_t)byte_of(v[12 + (sidx >> 2)], sidx & 3);
-            float s = 0.f;
-#pragma unroll
-            for (int t = 0; t < 4; t++) {
-                const uint32_t L = (g & 1) ? v[4 + t] : v[t];
-                const uint32_t lo = (g < 2 ? L : (L >> 4)) & 0x0F0F0F0Fu;
-                const uint32_t C = v[8 + t];
-                const uint32_t hi = (g < 2 ? (C << (4 - 2 * g)) : (C >> (2 * g - 4))) & 0x30303030u;
-                const uint32_t q = lo | hi;  // four 6-bit codes, one per byte
-                const half2_t q02 = bytes02_as_f16(q) + bias, q13 = bytes13_as_f16(q) + bias;
-                const float *xp = xv + 16 * g + 4 * t;
-                s = fma_h(q02.x, xp[0], s); s = fma_h(q13.x, xp[1], s);
-                s = fma_h(q02.y, xp[2], s); s = fma_h(q13.y, xp[3], s);
-            }
-            total = fmaf(dsc, s, total);
+            const uint32_t scw = (g < 2) ? sc0 : sc1;
+            const int sbyte = __builtin_amdgcn_sbfe((int)scw, 16 * (g & 1) + 8 * o.lh, 8);  // sc[8h + 2g + lh]
+            total = fmaf(d * (float)sbyte, grp[g], total);
         }
         return total;
     }
 };
 
-// ----------------------------------------------------------- fast kernel ----
-// Every thread owns at most one unit of the row (U <= blockDim.x), so its 64
-// activations are loaded once and stay in registers while the workgroup
-// walks its row groups (R rows each, grid stride).  The raw bytes of the next
-// row group are fetched before the current one is decoded (two register
-// buffers, loop unrolled by two so neither is indexed dynamically).
-template <int DT, int R>
-__global__ void __launch_bounds__(256) gemv_kernel(const uint8_t *__restrict__ blob, int64_t M,
-                                                   int64_t row_bytes, int U,
-                                                   const float *__restrict__ x, float *__restrict__ y) {
-    constexpr int NDW = Unit<DT>::NDW;
-    __shared__ float red[2][R][4];
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6, nwaves = blockDim.x >> 6;
-    const bool active = t < U;
-    const int64_t nrg = (M + R - 1) / R;
-    float xv[64];
-    if (active) Unit<DT>::load_x(x, t, xv);
+// Activations go through LDS with the float4 index XOR-swizzled within groups
+// of 16, so that 16 lanes reading their own unit hit distinct banks.
+__device__ __forceinline__ int xslot(int f) { return (f & ~15) | ((f & 15) ^ ((f >> 4) & 15)); }
 
-    auto fetch = [&](int64_t g, uint32_t (&raw)[R][NDW]) {
-#pragma unroll
-        for (int r = 0; r < R; r++) {
-            const int64_t row = g * R + r;
-            if (active && row < M) Unit<DT>::template load<false>(blob + row * row_bytes, t, raw[r]);
-        }
-    };
-    auto finish = [&](int64_t g, const uint32_t (&raw)[R][NDW], int parity) {
-        float acc[R];
-#pragma unroll
-        for (int r = 0; r < R; r++) {
-            acc[r] = (active && g * R + r < M) ? Unit<DT>::dot(raw[r], xv, t) : 0.f;
-            acc[r] = wave_sum_to_lane63(acc[r]);
-        }
-        if (nwaves == 1) {
-            if (lane == 63) {
-#pragma unroll
-                for (int r = 0; r < R; r++)
-                    if (g * R + r < M) y[g * R + r] = acc[r];
-            }
-        } else {
-            if (lane == 63) {
-#pragma unroll
-                for (int r = 0; r < R; r++) red[parity][r][wave] = acc[r];
-            }
-            __syncthreads();
-            if (t < R && g * R + t < M) {
-                float s = red[parity][t][0];
-                for (int w = 1; w < nwaves; w++) s += red[parity][t][w];
-                y[g * R + t] = s;
-            }
-        }
-    };
+template <int DT>
+__device__ __forceinline__ void stage_x(const float *x, int U, floatx4 *xs) {
+    const floatx4 *xg = reinterpret_cast<const floatx4 *>(x);
+    for (int f = threadIdx.x; f < 16 * U; f += blockDim.x) xs[xslot(f)] = xg[f];
+}
 
-    uint32_t ra[R][NDW], rb[R][NDW];
-    int64_t g = blockIdx.x;
-    if (g < nrg) fetch(g, ra);
-    while (g < nrg) {
-        const int64_t g1 = g + gridDim.x;
-        if (g1 < nrg) fetch(g1, rb);
-        finish(g, ra, 0);
-        if (g1 >= nrg) break;
-        const int64_t g2 = g1 + gridDim.x;
-        if (g2 < nrg) fetch(g2, ra);
-        finish(g1, rb, 1);
-        g = g2;
+template <int DT>
+__device__ __forceinline__ void x_from_lds(const floatx4 *xs, int u, float (&xv)[64]) {
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+        const floatx4 v = xs[xslot(Unit<DT>::x4(u, i))];
+        xv[4 * i] = v.x; xv[4 * i + 1] = v.y; xv[4 * i + 2] = v.z; xv[4 * i + 3] = v.w;
     }
 }
 
-// More units than threads (K > 64 * 256): each thread loops over its units
-// and reloads their activations for every row group.
+// ------------------------------------------------------------ fast kernel ----
+// WAVE_ROWS: K <= 4096, 4 independent wavefronts per workgroup, each with its
+// own range of row groups.  Otherwise the workgroup's ceil(U/64) wavefronts
+// split K and reduce each row group through LDS.  D row groups are in flight
+// while one is decoded (a ring of D+1 register buffers, unrolled so that no
+// buffer is indexed dynamically).
+template <int DT, int R, int D, bool WAVE_ROWS>
+__global__ void __launch_bounds__(256) gemv_kernel(const uint8_t *__restrict__ blob, int64_t M, int64_t row_bytes,
+                                                   int U, const float *__restrict__ x, float *__restrict__ y,
+                                                   int64_t per_owner, int64_t extra) {
+    constexpr int NL = Unit<DT>::NL;
+    extern __shared__ __attribute__((aligned(16))) floatx4 xs[];
+    __shared__ float red[2][R][4];
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6), nwaves = blockDim.x >> 6;
+    const int u = WAVE_ROWS ? lane : t;
+    const bool active = u < U;
+    // owner o gets per_owner row groups, plus one more for the first `extra` owners
+    const int64_t owner = WAVE_ROWS ? (int64_t)blockIdx.x * nwaves + wave : (int64_t)blockIdx.x;
+    const int64_t g0 = owner * per_owner + (owner < extra ? owner : extra);
+    const int64_t n = per_owner + (owner < extra ? 1 : 0);
+    const typename Unit<DT>::Off off = Unit<DT>::lane_off(active ? u : 0);
+
+    uint32_t buf[D + 1][R][NL];
+    auto fetch = [&](int64_t g, uint32_t (&b)[R][NL]) {
+#pragma unroll
+        for (int r = 0; r < R; r++) {
+            const int64_t row = g * R + r;
+            if (active && row < M) Unit<DT>::load(blob + row * row_bytes, off, b[r]);
+        }
+    };
+#pragma unroll
+    for (int s = 0; s < D; s++)
+        if (s < n) fetch(g0 + s, buf[s]);
+
+    stage_x<DT>(x, U, xs);
+    __syncthreads();
+    float xv[64];
+    if (active) x_from_lds<DT>(xs, u, xv);
+
+    int parity = 0;
+    for (int64_t i0 = 0; i0 < n; i0 += D + 1) {
+#pragma unroll
+        for (int s = 0; s <= D; s++) {
+            const int64_t i = i0 + s;
+            if (i < n) {
+                if (i + D < n) fetch(g0 + i + D, buf[(s + D) % (D + 1)]);
+                const int64_t row0 = (g0 + i) * R;
+                float acc[R];
+#pragma unroll
+                for (int r = 0; r < R; r++) {
+                    acc[r] = (active && row0 + r < M) ? Unit<DT>::dot(buf[s][r], xv, off) : 0.f;
+                    acc[r] = wave_sum_to_lane63(acc[r]);
+                }
+                if (WAVE_ROWS) {
+                    if (lane == 63) {
+#pragma unroll
+                        for (int r = 0; r < R; r++)
+                            if (row0 + r < M) y[row0 + r] = acc[r];
+                    }
+                } else {
+                    if (lane == 63) {
+#pragma unroll
+                        for (int r = 0; r < R; r++) red[parity][r][wave] = acc[r];
+                    }
+                    __syncthreads();
+                    if (t < R && row0 + t < M) {
+                        float sum = red[parity][t][0];
+                        for (int w = 1; w < nwaves; w++) sum += red[parity][t][w];
+                        y[row0 + t] = sum;
+                    }
+                    parity ^= 1;
+                }
+            }
+        }
+    }
+}
+
+// More units than 4 wavefronts of lanes (K > 16384): each thread loops over
+// its units and reloads their activations for every row group.
 template <int DT, int R>
 __global__ void __launch_bounds__(256) gemv_multi_kernel(const uint8_t *__restrict__ blob, int64_t M,
                                                          int64_t row_bytes, int U,
@@ -286,6 +361,7 @@ __global__ void __launch_bounds__(256) gemv_multi_kernel(const uint8_t *__restri
     __shared__ float red[R][4];
     const int t = threadIdx.x, T = blockDim.x, lane = t & 63, wave = t >> 6, nwaves = T >> 6;
     const int64_t nrg = (M + R - 1) / R;
+    const floatx4 *xg = reinterpret_cast<const floatx4 *>(x);
     float xv[64];
     for (int64_t rg = blockIdx.x; rg < nrg; rg += gridDim.x) {
         const int64_t row0 = rg * R;
@@ -293,25 +369,30 @@ __global__ void __launch_bounds__(256) gemv_multi_kernel(const uint8_t *__restri
 #pragma unroll
         for (int r = 0; r < R; r++) acc[r] = 0.f;
         for (int u = t; u < U; u += T) {
-            Unit<DT>::load_x(x, u, xv);
-            uint32_t raw[R][Unit<DT>::NDW];
+#pragma unroll
+            for (int i = 0; i < 16; i++) {
+                const floatx4 v = xg[Unit<DT>::x4(u, i)];
+                xv[4 * i] = v.x; xv[4 * i + 1] = v.y; xv[4 * i + 2] = v.z; xv[4 * i + 3] = v.w;
+            }
+            const typename Unit<DT>::Off off = Unit<DT>::lane_off(u);
+            uint32_t raw[R][Unit<DT>::NL];
 #pragma unroll
             for (int r = 0; r < R; r++)
-                if (row0 + r < M) Unit<DT>::template load<false>(blob + (row0 + r) * row_bytes, u, raw[r]);
+                if (row0 + r < M) Unit<DT>::load(blob + (row0 + r) * row_bytes, off, raw[r]);
 #pragma unroll
             for (int r = 0; r < R; r++)
-                if (row0 + r < M) acc[r] += Unit<DT>::dot(raw[r], xv, u);
+                if (row0 + r < M) acc[r] += Unit<DT>::dot(raw[r], xv, off);
         }
 #pragma unroll
         for (int r = 0; r < R; r++) {
-            const float s = wave_sum_to_lane63(acc[r]);
-            if (lane == 63) red[r][wave] = s;
+            const float sum = wave_sum_to_lane63(acc[r]);
+            if (lane == 63) red[r][wave] = sum;
         }
         __syncthreads();
         if (t < R && row0 + t < M) {
-            float s = red[t][0];
-            for (int w = 1; w < nwaves; w++) s += red[t][w];
-            y[row0 + t] = s;
+            float sum = red[t][0];
+            for (int w = 1; w < nwaves; w++) sum += red[t][w];
+            y[row0 + t] = sum;
         }
         __syncthreads();
     }
@@ -432,8 +513,8 @@ static bool fast_layout_ok(int dtype, int64_t nb) {
     }
 }
 
-// Resident workgroups per CU for the persistent GEMV; QMM_GEMV_WAVES_PER_CU
-// overrides the default (a tuning lever, read once).
+// Resident wavefronts per CU for the GEMV; QMM_GEMV_WAVES_PER_CU overrides the
+// default (a tuning lever, read once).
 static int gemv_waves_per_cu() {
     static int v = [] {
         const char *e = getenv("QMM_GEMV_WAVES_PER_CU");
@@ -443,21 +524,36 @@ static int gemv_waves_per_cu() {
     return v;
 }
 
-template <int DT, int R>
+template <int DT, int R, int D>
 static hipError_t launch_fast(const uint8_t *blob, int64_t M, int64_t K, const float *x, float *y,
                               hipStream_t st, int cus) {
     constexpr int BS = Geo<DT>::BS, BB = Geo<DT>::BB;
-    const int64_t nb = K / BS, row_bytes = nb * BB;
-    const int64_t U64 = K / 64;
-    const int T = (int)(U64 >= 256 ? 256 : ((U64 + 63) / 64) * 64);
-    const int U = (int)U64;
+    const int64_t row_bytes = (K / BS) * BB;
+    const int U = (int)(K / 64);
     const int64_t nrg = (M + R - 1) / R;
-    const int64_t wg_per_cu = std::max<int64_t>(1, gemv_waves_per_cu() / (T / 64));
-    const int64_t grid = std::min<int64_t>(nrg, (int64_t)cus * wg_per_cu);
-    if (U64 <= 256)
-        hipLaunchKernelGGL((gemv_kernel<DT, R>), dim3((unsigned)grid), dim3(T), 0, st, blob, M, row_bytes, U, x, y);
-    else
-        hipLaunchKernelGGL((gemv_multi_kernel<DT, R>), dim3((unsigned)grid), dim3(T), 0, st, blob, M, row_bytes, U, x, y);
+    const size_t lds = (size_t)U * 256;  // the activations
+    const int64_t wpc = gemv_waves_per_cu();
+    if (U <= 64) {
+        const int64_t waves = std::min<int64_t>(nrg, (int64_t)cus * wpc);
+        const int64_t grid = (waves + 3) / 4, owners = grid * 4;
+        hipLaunchKernelGGL((gemv_kernel<DT, R, D, true>), dim3((unsigned)grid), dim3(256), lds, st, blob, M, row_bytes,
+                           U, x, y, nrg / owners, nrg % owners);
+    } else if (U <= 256) {
+        const int W = (U + 63) / 64;
+        const int64_t grid = std::min<int64_t>(nrg, (int64_t)cus * std::max<int64_t>(1, wpc / W));
+        if (lds > 64 * 1024) {
+            static const hipError_t attr = hipFuncSetAttribute(
+                reinterpret_cast<const void *>(&gemv_kernel<DT, R, D, false>),
+                hipFuncAttributeMaxDynamicSharedMemorySize, 64 * 1024 + 1024);
+            if (attr != hipSuccess) return attr;
+        }
+        hipLaunchKernelGGL((gemv_kernel<DT, R, D, false>), dim3((unsigned)grid), dim3(64 * W), lds, st, blob, M,
+                           row_bytes, U, x, y, nrg / grid, nrg % grid);
+    } else {
+        const int64_t grid = std::min<int64_t>(nrg, (int64_t)cus * 2);
+        hipLaunchKernelGGL((gemv_multi_kernel<DT, R>), dim3((unsigned)grid), dim3(256), 0, st, blob, M, row_bytes, U,
+                           x, y);
+    }
     return hipGetLastError();
 }
 
@@ -477,10 +573,10 @@ hipError_t launch_gemv(int dtype, const void *blob_v, int64_t M, int64_t K, cons
     const int64_t bs = (dtype == QMM_Q4_K || dtype == QMM_Q6_K) ? 256 : 32;
     const bool fast = fast_layout_ok(dtype, K / bs) && (K % 64) == 0;
     switch (dtype) {
-    case QMM_Q4_0: return fast ? launch_fast<QMM_Q4_0, 4>(blob, M, K, x, y, st, cus) : launch_generic<QMM_Q4_0>(blob, M, K, x, y, st, cus);
-    case QMM_Q8_0: return fast ? launch_fast<QMM_Q8_0, 4>(blob, M, K, x, y, st, cus) : launch_generic<QMM_Q8_0>(blob, M, K, x, y, st, cus);
-    case QMM_Q4_K: return fast ? launch_fast<QMM_Q4_K, 4>(blob, M, K, x, y, st, cus) : launch_generic<QMM_Q4_K>(blob, M, K, x, y, st, cus);
-    case QMM_Q6_K: return fast ? launch_fast<QMM_Q6_K, 4>(blob, M, K, x, y, st, cus) : launch_generic<QMM_Q6_K>(blob, M, K, x, y, st, cus);
+    case QMM_Q4_0: return fast ? launch_fast<QMM_Q4_0, 2, 3>(blob, M, K, x, y, st, cus) : launch_generic<QMM_Q4_0>(blob, M, K, x, y, st, cus);
+    case QMM_Q8_0: return fast ? launch_fast<QMM_Q8_0, 1, 4>(blob, M, K, x, y, st, cus) : launch_generic<QMM_Q8_0>(blob, M, K, x, y, st, cus);
+    case QMM_Q4_K: return fast ? launch_fast<QMM_Q4_K, 2, 3>(blob, M, K, x, y, st, cus) : launch_generic<QMM_Q4_K>(blob, M, K, x, y, st, cus);
+    case QMM_Q6_K: return fast ? launch_fast<QMM_Q6_K, 1, 4>(blob, M, K, x, y, st, cus) : launch_generic<QMM_Q6_K>(blob, M, K, x, y, st, cus);
     default: return hipErrorInvalidValue;
     }
 }
