@@ -195,7 +195,7 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "qmm::gemv_kernel<Q4_0>",
+            "kernel": "qmm::gemv_kernel<2,...> (Q4_0), the four decode-layer launches together",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
@@ -211,7 +211,7 @@ def main():
             "rotation_copies": PR,
             "roofline": {
                 "bound": "mfma",
-                "kernel": "qmm::gemm_kernel<Q4_K,128,128>",
+                "kernel": "qmm::gemm_wreg_kernel<12,32,128,3,8> (Q4_K)",
                 "achieved": round(tflops, 2),
                 "peak": F16_MFMA_PEAK_TFLOPS,
                 "unit": "TFLOP/s",

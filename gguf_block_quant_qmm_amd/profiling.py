@@ -1,0 +1,161 @@
+"""rocprofv3 summaries for the committed profiles.
+
+Subcommands (run from the repository root):
+
+  copy     --mib M --reps R
+           Runs torch's device-to-device copy of M MiB R times: the plain
+           copy kernel whose FETCH_SIZE / WRITE_SIZE readings calibrate the
+           counters (it reads M MiB and writes M MiB per dispatch).
+
+  stats    --csv <kernel_stats.csv> --cmd "<command>" --out <file.md>
+           Markdown table of a --kernel-trace --stats run, plus one
+           aggregate line per kernel group (--group NAME=REGEX, repeatable).
+
+  traffic  --fetch <counter_collection.csv> --write <counter_collection.csv>
+           --calib-fetch <csv> --calib-write <csv> --calib-bytes B
+           --key NAME=REGEX [--key ...] --out profiles/counters.json
+           HBM bytes per launch for each kernel group: the mean FETCH_SIZE
+           (and WRITE_SIZE) per dispatch of the group's kernels, each scaled
+           by (B / the same counter's reading for the calibration copy).
+           Stored under NAME with the hash of the kernel sources, so that a
+           reader can tell when a kernel has changed since the counters were
+           taken.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import json
+import os
+import re
+import sys
+from collections import defaultdict
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gguf_block_quant_qmm_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def _copy(args):
+    import torch
+    n = args.mib << 20
+    a = torch.ones(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(args.reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(f"copied {args.mib} MiB x {args.reps}", flush=True)
+
+
+def _groups(specs):
+    out = []
+    for s in specs or []:
+        name, rx = s.split("=", 1)
+        out.append((name, re.compile(rx)))
+    return out
+
+
+def _stats(args):
+    rows = list(csv.DictReader(open(args.csv)))
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    lines = [f"# {args.title}", "", "Command (from the repository root):", "", "```", args.cmd, "```", "",
+             "| kernel | calls | avg us | min us | max us | total ms | share |",
+             "|---|---:|---:|---:|---:|---:|---:|"]
+    for r in rows:
+        name = r["Name"]
+        if len(name) > 110:
+            name = name[:107] + "..."
+        lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.3f} | "
+                     f"{float(r['MinNs']) / 1e3:.3f} | {float(r['MaxNs']) / 1e3:.3f} | "
+                     f"{float(r['TotalDurationNs']) / 1e6:.3f} | {float(r['Percentage']):.2f}% |")
+    groups = _groups(args.group)
+    if groups:
+        lines += ["", "Kernel groups (total time over total calls):", "",
+                  "| group | calls | avg us |", "|---|---:|---:|"]
+        for name, rx in groups:
+            c = sum(int(r["Calls"]) for r in rows if rx.search(r["Name"]))
+            t = sum(float(r["TotalDurationNs"]) for r in rows if rx.search(r["Name"]))
+            lines.append(f"| {name} | {c} | {t / max(c, 1) / 1e3:.3f} |")
+    text = "\n".join(lines) + "\n"
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write(text)
+    print(text)
+
+
+def _per_dispatch(path, counter, rx):
+    vals = defaultdict(float)
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] == counter and rx.search(r["Kernel_Name"]):
+            vals[int(r["Dispatch_Id"])] += float(r["Counter_Value"])
+    return list(vals.values())
+
+
+def _traffic(args):
+    copy_rx = re.compile(args.calib_regex)
+    cf = _per_dispatch(args.calib_fetch, "FETCH_SIZE", copy_rx)
+    cw = _per_dispatch(args.calib_write, "WRITE_SIZE", copy_rx)
+    if not cf or not cw:
+        sys.exit("calibration copy dispatches not found")
+    # the copy's last dispatch (warm, steady state)
+    kf, kw = args.calib_bytes / cf[-1], args.calib_bytes / cw[-1]
+    try:
+        with open(args.out) as f:
+            db = json.load(f)
+    except (OSError, ValueError):
+        db = {}
+    db["_calibration"] = {"copy_bytes": args.calib_bytes, "fetch_kib_reading": cf[-1], "write_kib_reading": cw[-1],
+                          "bytes_per_fetch_unit": kf, "bytes_per_write_unit": kw}
+    for spec in args.key:
+        name, rx = spec.split("=", 1)
+        rx = re.compile(rx)
+        f = _per_dispatch(args.fetch, "FETCH_SIZE", rx)
+        w = _per_dispatch(args.write, "WRITE_SIZE", rx)
+        if not f or not w:
+            sys.exit(f"no dispatches for {name}")
+        fb = kf * sum(f) / len(f)
+        wb = kw * sum(w) / len(w)
+        db[name] = {"source_hash": kernel_source_hash(), "dispatches": len(f),
+                    "fetch_bytes_per_launch": round(fb), "write_bytes_per_launch": round(wb),
+                    "hbm_bytes_per_launch": round(fb + wb), "kernel_regex": rx.pattern}
+        print(name, db[name])
+    with open(args.out, "w") as fh:
+        json.dump(db, fh, indent=1, sort_keys=True)
+        fh.write("\n")
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd_name", required=True)
+    c = sub.add_parser("copy")
+    c.add_argument("--mib", type=int, default=512)
+    c.add_argument("--reps", type=int, default=3)
+    s = sub.add_parser("stats")
+    s.add_argument("--csv", required=True)
+    s.add_argument("--cmd", required=True)
+    s.add_argument("--title", default="rocprofv3 kernel statistics")
+    s.add_argument("--group", action="append")
+    s.add_argument("--out")
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--calib-fetch", required=True)
+    t.add_argument("--calib-write", required=True)
+    t.add_argument("--calib-bytes", type=int, required=True)
+    t.add_argument("--calib-regex", default=r"copy|elementwise")
+    t.add_argument("--key", action="append", required=True)
+    t.add_argument("--out", default=os.path.join(ROOT, "profiles", "counters.json"))
+    a = ap.parse_args(argv)
+    {"copy": _copy, "stats": _stats, "traffic": _traffic}[a.cmd_name](a)
+
+
+if __name__ == "__main__":
+    main()

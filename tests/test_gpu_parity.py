@@ -106,6 +106,21 @@ def test_gemm_small(dt, N):
         check(Yg, Y64, S, q.tolerance(dt, M, K, N), f"{NAME[dt]} gemm M={M} K={K} N={N}")
 
 
+@pytest.mark.parametrize("dt", [q.QMM_Q4_0, q.QMM_Q4_K], ids=NAME.get)
+def test_gemm_register_b_kernel_ragged(dt):
+    # M/256 x N/128 >= 224 workgroups selects the register-B kernel for the
+    # 4-bit formats; M and N both end in partial tiles.  Sampled rows include
+    # the last (partial) row tile.
+    M, K, N = 7200, 512, 1000
+    blob = make_blob(dt, M, K, rng_for(650 + dt, 0))
+    X = make_x(N, K, rng_for(650 + dt, 1))
+    rows = np.unique(np.concatenate([sample_rows(M, 40, 650 + dt), np.arange(M - 40, M)]))
+    _, Y64, S = oracle.matmul(dt, blob, M, K, X, rows=rows)
+    Yg = gpu_gemm(dt, to_dev(blob), M, K, X)
+    assert np.all(np.isfinite(Yg))
+    check(Yg[:, rows], Y64, S, q.tolerance(dt, M, K, N), f"{NAME[dt]} register-B gemm M={M} K={K} N={N}")
+
+
 # ------------------------------------------------------------ properties ----
 
 @pytest.mark.parametrize("dt", DTYPES, ids=NAME.get)
