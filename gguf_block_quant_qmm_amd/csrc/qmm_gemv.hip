@@ -28,11 +28,36 @@ namespace qmm {
 
 __device__ __forceinline__ float fma_h(_Float16 h, float x, float acc) { return fmaf((float)h, x, acc); }
 
+// Weight bytes are read with bounds-checked buffer loads: the resource covers
+// one row group, any dword at or past its byte count reads as 0 without a
+// memory access, so out-of-range rows and row groups need no branch.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x3_t __attribute__((ext_vector_type(3)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ Rsrc make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// N dwords at byte offset voff (per lane) + soff (uniform)
 template <int N>
-__device__ __forceinline__ void ld(const uint8_t *p, uint32_t off, uint32_t (&v)[N]) {
-    const uint32_t *q = reinterpret_cast<const uint32_t *>(p + off);
+__device__ __forceinline__ void ldb(Rsrc rs, uint32_t voff, uint32_t soff, uint32_t (&v)[N]) {
+    int i = 0;
 #pragma unroll
-    for (int i = 0; i < N; i++) v[i] = q[i];
+    for (; i + 4 <= N; i += 4) {
+        const u32x4_t q = __builtin_amdgcn_raw_buffer_load_b128(rs, voff + 4 * i, soff, 0);
+        v[i] = q.x; v[i + 1] = q.y; v[i + 2] = q.z; v[i + 3] = q.w;
+    }
+    if constexpr (N % 4 == 3) {
+        const u32x3_t q = __builtin_amdgcn_raw_buffer_load_b96(rs, voff + 4 * i, soff, 0);
+        v[i] = q.x; v[i + 1] = q.y; v[i + 2] = q.z;
+    } else if constexpr (N % 4 == 2) {
+        const u32x2_t q = __builtin_amdgcn_raw_buffer_load_b64(rs, voff + 4 * i, soff, 0);
+        v[i] = q.x; v[i + 1] = q.y;
+    } else if constexpr (N % 4 == 1) {
+        v[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, voff + 4 * i, soff, 0);
+    }
 }
 
 // ----------------------------------------------------------------- units ----
@@ -48,42 +73,57 @@ __device__ __forceinline__ void ld(const uint8_t *p, uint32_t off, uint32_t (&v)
 
 template <int DT> struct Unit;
 
+// 4-bit codes enter the f32 arithmetic (v_fma_mix_f32) as f16 subnormals: a
+// dword masked with 0x000F000F holds two codes c as c * 2^-24, masked with
+// 0x00F000F0 as c * 2^-20 -- one VOP2 instruction per two codes, exact.  Every
+// weight is formed exactly (Q4_0, Q8_0, Q6_K) or with one rounding (Q4_K)
+// before it meets its activation, so the usual f32 dot-product error bound
+// relative to sum |w x| holds: no offset is ever taken out through a sum of
+// activations (that would cancel when the weights do).
+__device__ __forceinline__ half2_t as_h2(uint32_t v) { return __builtin_bit_cast(half2_t, v); }
+
+constexpr float TWO24 = 16777216.0f, TWO20 = 1048576.0f;
+
 template <> struct Unit<QMM_Q4_0> {
     static constexpr int NL = 9;
     struct Off { uint32_t a; };
     __device__ static Off lane_off(int u) { return {36u * u}; }
-    __device__ static void load(const uint8_t *row, const Off &o, uint32_t (&v)[NL]) { ld(row, o.a, v); }
+    __device__ static void load(Rsrc rs, uint32_t row, const Off &o, uint32_t (&v)[NL]) { ldb(rs, o.a, row, v); }
     __device__ static int x4(int u, int i) { return 16 * u + i; }
     __device__ static float dot(const uint32_t (&v)[NL], const float (&xv)[64], const Off &) {
-        // one accumulator per dword of codes (4 terms each): 16 independent
-        // FMA chains per unit keep the VALU pipeline full
-        const half2_t bias = {(_Float16)-1032.0f, (_Float16)-1032.0f};  // q - 8
-        float blk[2];
+        // The unit is two blocks, 36 bytes: d0 qs0[16] d1 qs1[16].  Block 0's
+        // codes sit in dwords [qs0 qs1 qs14 qs15] (realigned from v0, v4) and
+        // v1..v3 = qs2..13; block 1's in v5..v8.  Element e < 16 is the low
+        // nibble of qs[e], element e + 16 its high nibble.  Low nibbles become
+        // (q - 8) 2^-24, high nibbles (q - 8) 2^-20: exact f16 subnormals.
+        const half2_t b24 = as_h2(0x80088008u), b20 = as_h2(0x80808080u);  // -8 * 2^-24, -128 * 2^-24
+        const uint32_t D[2][4] = {{__builtin_amdgcn_alignbyte(v[4], v[0], 2), v[1], v[2], v[3]},
+                                  {v[5], v[6], v[7], v[8]}};
+        float lo[2][2], hi[2][2];
 #pragma unroll
         for (int b = 0; b < 2; b++) {
-            // decode the block's 32 codes first, then issue the FMAs round-robin
-            // over 8 accumulators so that consecutive FMAs are independent
-            half2_t w[4][4];  // [dword][l02, l13, h02, h13]
+            const float *xb = xv + 32 * b;
 #pragma unroll
             for (int i = 0; i < 4; i++) {
-                const uint32_t q = b == 0 ? __builtin_amdgcn_alignbyte(v[i + 1], v[i], 2) : v[5 + i];
-                const uint32_t L = q & 0x0F0F0F0Fu, H = (q >> 4) & 0x0F0F0F0Fu;
-                w[i][0] = bytes02_as_f16(L) + bias; w[i][1] = bytes13_as_f16(L) + bias;
-                w[i][2] = bytes02_as_f16(H) + bias; w[i][3] = bytes13_as_f16(H) + bias;
+                // qs index of the dword's bytes 0..3
+                const int e0 = b == 1 ? 4 * i : (i == 0 ? 0 : 4 * i - 2);
+                const int e1 = e0 + 1;
+                const int e2 = (b == 0 && i == 0) ? 14 : e0 + 2, e3 = e2 + 1;
+                const uint32_t d = D[b][i], t = d >> 8;
+                const half2_t p0 = as_h2(d & 0x000F000Fu) + b24, p1 = as_h2(d & 0x00F000F0u) + b20;
+                const half2_t p2 = as_h2(t & 0x000F000Fu) + b24, p3 = as_h2(t & 0x00F000F0u) + b20;
+                const int c = i & 1;
+                float l = i < 2 ? 0.f : lo[b][c], h = i < 2 ? 0.f : hi[b][c];
+                l = fma_h(p0.x, xb[e0], l); h = fma_h(p1.x, xb[16 + e0], h);
+                l = fma_h(p0.y, xb[e2], l); h = fma_h(p1.y, xb[16 + e2], h);
+                l = fma_h(p2.x, xb[e1], l); h = fma_h(p3.x, xb[16 + e1], h);
+                l = fma_h(p2.y, xb[e3], l); h = fma_h(p3.y, xb[16 + e3], h);
+                lo[b][c] = l; hi[b][c] = h;
             }
-            const float *xb = xv + 32 * b;
-            float s8[8];
-#pragma unroll
-            for (int i = 0; i < 4; i++) { s8[i] = fma_h(w[i][0].x, xb[4 * i], 0.f); s8[4 + i] = fma_h(w[i][2].x, xb[16 + 4 * i], 0.f); }
-#pragma unroll
-            for (int i = 0; i < 4; i++) { s8[i] = fma_h(w[i][1].x, xb[4 * i + 1], s8[i]); s8[4 + i] = fma_h(w[i][3].x, xb[16 + 4 * i + 1], s8[4 + i]); }
-#pragma unroll
-            for (int i = 0; i < 4; i++) { s8[i] = fma_h(w[i][0].y, xb[4 * i + 2], s8[i]); s8[4 + i] = fma_h(w[i][2].y, xb[16 + 4 * i + 2], s8[4 + i]); }
-#pragma unroll
-            for (int i = 0; i < 4; i++) { s8[i] = fma_h(w[i][1].y, xb[4 * i + 3], s8[i]); s8[4 + i] = fma_h(w[i][3].y, xb[16 + 4 * i + 3], s8[4 + i]); }
-            blk[b] = ((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7]));
         }
-        return fmaf(h2f(v[4] >> 16), blk[1], h2f(v[0]) * blk[0]);
+        const float s0 = fmaf(lo[0][0] + lo[0][1], TWO24, (hi[0][0] + hi[0][1]) * TWO20);
+        const float s1 = fmaf(lo[1][0] + lo[1][1], TWO24, (hi[1][0] + hi[1][1]) * TWO20);
+        return fmaf(h2f(v[4] >> 16), s1, h2f(v[0]) * s0);
     }
 };
 
@@ -91,7 +131,7 @@ template <> struct Unit<QMM_Q8_0> {
     static constexpr int NL = 17;
     struct Off { uint32_t a; };
     __device__ static Off lane_off(int u) { return {68u * u}; }
-    __device__ static void load(const uint8_t *row, const Off &o, uint32_t (&v)[NL]) { ld(row, o.a, v); }
+    __device__ static void load(Rsrc rs, uint32_t row, const Off &o, uint32_t (&v)[NL]) { ldb(rs, o.a, row, v); }
     __device__ static int x4(int u, int i) { return 16 * u + i; }
     __device__ static float dot(const uint32_t (&v)[NL], const float (&xv)[64], const Off &) {
         const half2_t bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};  // (q + 128) - 128
@@ -127,10 +167,10 @@ template <> struct Unit<QMM_Q4_K> {
         const uint32_t h = 144u * (u >> 2);
         return {h, h + 16u + 32u * (u & 3), u & 3};
     }
-    __device__ static void load(const uint8_t *row, const Off &o, uint32_t (&v)[NL]) {
+    __device__ static void load(Rsrc rs, uint32_t row, const Off &o, uint32_t (&v)[NL]) {
         uint32_t h[4], q[8];
-        ld(row, o.hdr, h);
-        ld(row, o.qs, q);
+        ldb(rs, o.hdr, row, h);
+        ldb(rs, o.qs, row, q);
 #pragma unroll
         for (int i = 0; i < 4; i++) v[i] = h[i];
 #pragma unroll
@@ -138,35 +178,31 @@ template <> struct Unit<QMM_Q4_K> {
     }
     __device__ static int x4(int u, int i) { return 16 * u + i; }
     __device__ static float dot(const uint32_t (&v)[NL], const float (&xv)[64], const Off &o) {
-        const half2_t bias = {(_Float16)-1024.0f, (_Float16)-1024.0f};  // q
+        // sub-block 2c = low nibbles of qs[32c + j], 2c+1 = high nibbles.  Each
+        // weight d*sc*q - dmin*m is formed with one rounding (v_fma_mix_f32 of
+        // the subnormal code c*2^-24 or c*2^-20 with d*sc*2^24 or d*sc*2^20),
+        // then multiplied into x with an f32 FMA.
         const float d = h2f(v[0]), dmin = h2f(v[0] >> 16);
-        float sub[2];
+        int sc0, m0, sc1, m1;
+        q4k_scale_min(v[1], v[2], v[3], 2 * o.c, sc0, m0);
+        q4k_scale_min(v[1], v[2], v[3], 2 * o.c + 1, sc1, m1);
+        const float s0 = d * (float)sc0 * TWO24, n0 = -(dmin * (float)m0);
+        const float s1 = d * (float)sc1 * TWO20, n1 = -(dmin * (float)m1);
+        float acc[4];
 #pragma unroll
-        for (int half = 0; half < 2; half++) {  // sub-block 2c (low nibbles), 2c+1 (high nibbles)
-            int sc, mn;
-            q4k_scale_min(v[1], v[2], v[3], 2 * o.c + half, sc, mn);
-            const float dsc = d * (float)sc, ndm = -(dmin * (float)mn);
-            // weight = d*sc*q - dmin*m (one f32 rounding), then the f32 FMA with x;
-            // decode all 32 first, then the FMAs round-robin over 8 accumulators
-            float wf[8][4];
-#pragma unroll
-            for (int i = 0; i < 8; i++) {
-                const uint32_t n = (v[4 + i] >> (4 * half)) & 0x0F0F0F0Fu;
-                const half2_t q02 = bytes02_as_f16(n) + bias, q13 = bytes13_as_f16(n) + bias;
-                wf[i][0] = fmaf(dsc, (float)q02.x, ndm); wf[i][1] = fmaf(dsc, (float)q13.x, ndm);
-                wf[i][2] = fmaf(dsc, (float)q02.y, ndm); wf[i][3] = fmaf(dsc, (float)q13.y, ndm);
-            }
-            const float *xb = xv + 32 * half;
-            float s[8];
-#pragma unroll
-            for (int i = 0; i < 8; i++) s[i] = wf[i][0] * xb[4 * i];
-#pragma unroll
-            for (int j = 1; j < 4; j++)
-#pragma unroll
-                for (int i = 0; i < 8; i++) s[i] = fmaf(wf[i][j], xb[4 * i + j], s[i]);
-            sub[half] = (((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7])));
+        for (int i = 0; i < 8; i++) {
+            const uint32_t dw = v[4 + i], t = dw >> 8;
+            const half2_t p0 = as_h2(dw & 0x000F000Fu), p1 = as_h2(dw & 0x00F000F0u);
+            const half2_t p2 = as_h2(t & 0x000F000Fu), p3 = as_h2(t & 0x00F000F0u);
+            const int c = 2 * (i & 1);
+            float l = i < 2 ? 0.f : acc[c], h = i < 2 ? 0.f : acc[c + 1];
+            l = fmaf(fma_h(p0.x, s0, n0), xv[4 * i], l);     h = fmaf(fma_h(p1.x, s1, n1), xv[32 + 4 * i], h);
+            l = fmaf(fma_h(p0.y, s0, n0), xv[4 * i + 2], l); h = fmaf(fma_h(p1.y, s1, n1), xv[32 + 4 * i + 2], h);
+            l = fmaf(fma_h(p2.x, s0, n0), xv[4 * i + 1], l); h = fmaf(fma_h(p3.x, s1, n1), xv[32 + 4 * i + 1], h);
+            l = fmaf(fma_h(p2.y, s0, n0), xv[4 * i + 3], l); h = fmaf(fma_h(p3.y, s1, n1), xv[32 + 4 * i + 3], h);
+            acc[c] = l; acc[c + 1] = h;
         }
-        return sub[0] + sub[1];
+        return (acc[0] + acc[2]) + (acc[1] + acc[3]);
     }
 };
 
@@ -185,13 +221,13 @@ template <> struct Unit<QMM_Q6_K> {
         return {base + 64u * h + 16u * lh, base + 128u + 32u * h + 16u * lh, base + 192u + 8u * h, base + 208u,
                 sh, lh};
     }
-    __device__ static void load(const uint8_t *row, const Off &o, uint32_t (&v)[NL]) {
+    __device__ static void load(Rsrc rs, uint32_t row, const Off &o, uint32_t (&v)[NL]) {
         uint32_t a[5], b[5], c[5], s[3], d[1];
-        ld(row, o.a, a);
-        ld(row, o.a + 32u, b);
-        ld(row, o.c, c);
-        ld(row, o.s, s);
-        ld(row, o.d, d);
+        ldb(rs, o.a, row, a);
+        ldb(rs, o.a + 32u, row, b);
+        ldb(rs, o.c, row, c);
+        ldb(rs, o.s, row, s);
+        ldb(rs, o.d, row, d);
 #pragma unroll
         for (int i = 0; i < 5; i++) { v[i] = a[i]; v[5 + i] = b[i]; v[10 + i] = c[i]; }
         v[15] = s[0]; v[16] = s[1]; v[17] = s[2]; v[18] = d[0];
@@ -259,10 +295,28 @@ template <> struct Unit<QMM_Q6_K> {
 // of 16, so that 16 lanes reading their own unit hit distinct banks.
 __device__ __forceinline__ int xslot(int f) { return (f & ~15) | ((f & 15) ^ ((f >> 4) & 15)); }
 
-template <int DT>
-__device__ __forceinline__ void stage_x(const float *x, int U, floatx4 *xs) {
+// The activations are fetched into registers before any weight load is
+// issued and written to LDS afterwards: vector-memory loads return in order,
+// so fetching x after the weight prefetch would make the first product wait
+// for every prefetched weight byte.  XPT = float4 per thread (16 U <= XPT *
+// blockDim).
+template <int XPT>
+__device__ __forceinline__ void load_x(const float *x, int U, floatx4 (&r)[XPT]) {
     const floatx4 *xg = reinterpret_cast<const floatx4 *>(x);
-    for (int f = threadIdx.x; f < 16 * U; f += blockDim.x) xs[xslot(f)] = xg[f];
+    const int last = 16 * U - 1;
+#pragma unroll
+    for (int i = 0; i < XPT; i++) {
+        const int f = threadIdx.x + i * blockDim.x;
+        r[i] = xg[f < last ? f : last];  // unconditional: no divergent load to wait on
+    }
+}
+template <int XPT>
+__device__ __forceinline__ void store_x(const floatx4 (&r)[XPT], int U, floatx4 *xs) {
+#pragma unroll
+    for (int i = 0; i < XPT; i++) {
+        const int f = threadIdx.x + i * blockDim.x;
+        if (f < 16 * U) xs[xslot(f)] = r[i];
+    }
 }
 
 template <int DT>
@@ -280,7 +334,16 @@ __device__ __forceinline__ void x_from_lds(const floatx4 *xs, int u, float (&xv)
 // split K and reduce each row group through LDS.  D row groups are in flight
 // while one is decoded (a ring of D+1 register buffers, unrolled so that no
 // buffer is indexed dynamically).
-template <int DT, int R, int D, bool WAVE_ROWS>
+//
+// Every weight fetch is issued unconditionally as bounds-checked buffer loads
+// (rows past M and row groups past the wavefront's range read as zeros
+// without touching memory), so the loop has no branch around a load and the
+// compiler's wait counts stay exact: each decode waits for its own row group
+// only, never for the whole ring.
+//
+// FLAT: every wavefront (or workgroup) owns at most D+1 row groups; all of
+// them are fetched up front and decoded in order, with no fetch in the loop.
+template <int DT, int R, int D, bool WAVE_ROWS, bool FLAT>
 __global__ void __launch_bounds__(256) gemv_kernel(const uint8_t *__restrict__ blob, int64_t M, int64_t row_bytes,
                                                    int U, const float *__restrict__ x, float *__restrict__ y,
                                                    int64_t per_owner, int64_t extra) {
@@ -295,38 +358,40 @@ __global__ void __launch_bounds__(256) gemv_kernel(const uint8_t *__restrict__ b
     const int64_t owner = WAVE_ROWS ? (int64_t)blockIdx.x * nwaves + wave : (int64_t)blockIdx.x;
     const int64_t g0 = owner * per_owner + (owner < extra ? owner : extra);
     const int64_t n = per_owner + (owner < extra ? 1 : 0);
+    const int64_t nrg = (M + R - 1) / R;
+    const int64_t gend = g0 + n < nrg ? g0 + n : nrg;  // past the wavefront's last row group
     const typename Unit<DT>::Off off = Unit<DT>::lane_off(active ? u : 0);
 
     uint32_t buf[D + 1][R][NL];
     auto fetch = [&](int64_t g, uint32_t (&b)[R][NL]) {
+        // rows of group g that exist; none when g is past the range
+        const int64_t rows = g < gend ? (M - g * R < R ? M - g * R : R) : 0;
+        const Rsrc rs = make_rsrc(blob + (g < gend ? g : 0) * R * row_bytes, (uint32_t)(rows * row_bytes));
 #pragma unroll
-        for (int r = 0; r < R; r++) {
-            const int64_t row = g * R + r;
-            if (active && row < M) Unit<DT>::load(blob + row * row_bytes, off, b[r]);
-        }
+        for (int r = 0; r < R; r++) Unit<DT>::load(rs, (uint32_t)(r * row_bytes), off, b[r]);
     };
+    floatx4 xr[WAVE_ROWS ? 4 : 16];
+    load_x(x, U, xr);
 #pragma unroll
-    for (int s = 0; s < D; s++)
-        if (s < n) fetch(g0 + s, buf[s]);
-
-    stage_x<DT>(x, U, xs);
+    for (int s = 0; s < (FLAT ? D + 1 : D); s++) fetch(g0 + s, buf[s]);
+    store_x(xr, U, xs);
     __syncthreads();
     float xv[64];
-    if (active) x_from_lds<DT>(xs, u, xv);
+    x_from_lds<DT>(xs, active ? u : 0, xv);
 
     int parity = 0;
     for (int64_t i0 = 0; i0 < n; i0 += D + 1) {
 #pragma unroll
         for (int s = 0; s <= D; s++) {
             const int64_t i = i0 + s;
+            if (!FLAT) fetch(g0 + i + D, buf[(s + D) % (D + 1)]);
             if (i < n) {
-                if (i + D < n) fetch(g0 + i + D, buf[(s + D) % (D + 1)]);
                 const int64_t row0 = (g0 + i) * R;
                 float acc[R];
 #pragma unroll
                 for (int r = 0; r < R; r++) {
-                    acc[r] = (active && row0 + r < M) ? Unit<DT>::dot(buf[s][r], xv, off) : 0.f;
-                    acc[r] = wave_sum_to_lane63(acc[r]);
+                    const float d = Unit<DT>::dot(buf[s][r], xv, off);
+                    acc[r] = wave_sum_to_lane63(active ? d : 0.f);
                 }
                 if (WAVE_ROWS) {
                     if (lane == 63) {
@@ -376,9 +441,10 @@ __global__ void __launch_bounds__(256) gemv_multi_kernel(const uint8_t *__restri
             }
             const typename Unit<DT>::Off off = Unit<DT>::lane_off(u);
             uint32_t raw[R][Unit<DT>::NL];
+            const int64_t rows = M - row0 < R ? M - row0 : R;
+            const Rsrc rs = make_rsrc(blob + row0 * row_bytes, (uint32_t)(rows * row_bytes));
 #pragma unroll
-            for (int r = 0; r < R; r++)
-                if (row0 + r < M) Unit<DT>::load(blob + (row0 + r) * row_bytes, off, raw[r]);
+            for (int r = 0; r < R; r++) Unit<DT>::load(rs, (uint32_t)(r * row_bytes), off, raw[r]);
 #pragma unroll
             for (int r = 0; r < R; r++)
                 if (row0 + r < M) acc[r] += Unit<DT>::dot(raw[r], xv, off);
@@ -513,15 +579,38 @@ static bool fast_layout_ok(int dtype, int64_t nb) {
     }
 }
 
-// Resident wavefronts per CU for the GEMV; QMM_GEMV_WAVES_PER_CU overrides the
-// default (a tuning lever, read once).
-static int gemv_waves_per_cu() {
+// Wavefronts per CU for the GEMV (measured): 16 for Q4_0 and Q8_0 when each
+// wavefront owns whole rows (K <= 4096), else 8; QMM_GEMV_WAVES_PER_CU overrides it (a
+// tuning lever, read once).
+static int gemv_waves_per_cu(int dtype, bool wave_rows) {
     static int v = [] {
         const char *e = getenv("QMM_GEMV_WAVES_PER_CU");
         const int n = e ? atoi(e) : 0;
-        return (n >= 1 && n <= 32) ? n : 8;
+        return (n >= 1 && n <= 32) ? n : 0;
     }();
-    return v;
+    return v ? v : ((wave_rows && (dtype == QMM_Q4_0 || dtype == QMM_Q8_0)) ? 16 : 8);
+}
+
+// Launch one fast-kernel variant: FLAT with D+1 = the most row groups an
+// owner gets when that is at most 4, else the ring with D row groups ahead.
+template <int DT, int R, int D, bool WAVE_ROWS>
+static void launch_variant(int64_t nmax, dim3 grid, dim3 block, size_t lds, hipStream_t st, const uint8_t *blob,
+                           int64_t M, int64_t row_bytes, int U, const float *x, float *y, int64_t per_owner,
+                           int64_t extra) {
+#define QMM_GEMV_LAUNCH(F, DD) \
+    hipLaunchKernelGGL((gemv_kernel<DT, R, DD, WAVE_ROWS, F>), grid, block, lds, st, blob, M, row_bytes, U, x, y, \
+                       per_owner, extra)
+    // Q4_K: with more than one row group fetched up front the compiler hoists
+    // the scale unpacking of all of them and runs out of registers
+    constexpr int64_t flat_max = DT == QMM_Q4_K ? 1 : 4;
+    switch (nmax <= flat_max ? nmax : 0) {
+    case 1: QMM_GEMV_LAUNCH(true, 0); break;
+    case 2: if constexpr (flat_max >= 2) QMM_GEMV_LAUNCH(true, 1); break;
+    case 3: if constexpr (flat_max >= 3) QMM_GEMV_LAUNCH(true, 2); break;
+    case 4: if constexpr (flat_max >= 4) QMM_GEMV_LAUNCH(true, 3); break;
+    default: QMM_GEMV_LAUNCH(false, D); break;
+    }
+#undef QMM_GEMV_LAUNCH
 }
 
 template <int DT, int R, int D>
@@ -532,23 +621,35 @@ static hipError_t launch_fast(const uint8_t *blob, int64_t M, int64_t K, const f
     const int U = (int)(K / 64);
     const int64_t nrg = (M + R - 1) / R;
     const size_t lds = (size_t)U * 256;  // the activations
-    const int64_t wpc = gemv_waves_per_cu();
+    const int64_t wpc = gemv_waves_per_cu(DT, U <= 64);
     if (U <= 64) {
         const int64_t waves = std::min<int64_t>(nrg, (int64_t)cus * wpc);
         const int64_t grid = (waves + 3) / 4, owners = grid * 4;
-        hipLaunchKernelGGL((gemv_kernel<DT, R, D, true>), dim3((unsigned)grid), dim3(256), lds, st, blob, M, row_bytes,
-                           U, x, y, nrg / owners, nrg % owners);
+        const int64_t per = nrg / owners, extra = nrg % owners;
+        launch_variant<DT, R, D, true>(per + (extra ? 1 : 0), dim3((unsigned)grid), dim3(256), lds, st, blob, M,
+                                       row_bytes, U, x, y, per, extra);
     } else if (U <= 256) {
         const int W = (U + 63) / 64;
         const int64_t grid = std::min<int64_t>(nrg, (int64_t)cus * std::max<int64_t>(1, wpc / W));
         if (lds > 64 * 1024) {
-            static const hipError_t attr = hipFuncSetAttribute(
-                reinterpret_cast<const void *>(&gemv_kernel<DT, R, D, false>),
-                hipFuncAttributeMaxDynamicSharedMemorySize, 64 * 1024 + 1024);
+            static const hipError_t attr = [] {
+                auto big_lds = [](const void *f) {
+                    return hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, 64 * 1024 + 1024);
+                };
+                hipError_t e = big_lds(reinterpret_cast<const void *>(&gemv_kernel<DT, R, 0, false, true>));
+                if (e == hipSuccess) e = big_lds(reinterpret_cast<const void *>(&gemv_kernel<DT, R, D, false, false>));
+                if constexpr (DT != QMM_Q4_K) {
+                    if (e == hipSuccess) e = big_lds(reinterpret_cast<const void *>(&gemv_kernel<DT, R, 1, false, true>));
+                    if (e == hipSuccess) e = big_lds(reinterpret_cast<const void *>(&gemv_kernel<DT, R, 2, false, true>));
+                    if (e == hipSuccess) e = big_lds(reinterpret_cast<const void *>(&gemv_kernel<DT, R, 3, false, true>));
+                }
+                return e;
+            }();
             if (attr != hipSuccess) return attr;
         }
-        hipLaunchKernelGGL((gemv_kernel<DT, R, D, false>), dim3((unsigned)grid), dim3(64 * W), lds, st, blob, M,
-                           row_bytes, U, x, y, nrg / grid, nrg % grid);
+        const int64_t per = nrg / grid, extra = nrg % grid;
+        launch_variant<DT, R, D, false>(per + (extra ? 1 : 0), dim3((unsigned)grid), dim3(64 * W), lds, st, blob, M,
+                                        row_bytes, U, x, y, per, extra);
     } else {
         const int64_t grid = std::min<int64_t>(nrg, (int64_t)cus * 2);
         hipLaunchKernelGGL((gemv_multi_kernel<DT, R>), dim3((unsigned)grid), dim3(256), 0, st, blob, M, row_bytes, U,

@@ -87,6 +87,20 @@ def test_gemv_small(dt):
         check(yg[None, :], Y64, S, 1e-5, f"{NAME[dt]} gemv M={M} K={K}")
 
 
+@pytest.mark.parametrize("dt", DTYPES, ids=NAME.get)
+def test_gemv_rows_per_wavefront(dt):
+    # M spans the launch variants: 1..4 row groups per wavefront fetched up
+    # front, and the prefetch ring beyond; K = 4096 (independent wavefronts)
+    # and K = 8192 (a workgroup splits K), each with a ragged last group.
+    for K in (4096, 8192):
+        for i, M in enumerate((1001, 8193, 12003, 17001, 40001)):
+            blob = make_blob(dt, M, K, rng_for(520 + dt, 10 * i + K // 4096))
+            x = make_x(1, K, rng_for(520 + dt, 100 + 10 * i + K // 4096))
+            _, Y64, S = oracle.matmul(dt, blob, M, K, x)
+            yg = gpu_gemv(dt, to_dev(blob), M, K, x)
+            check(yg[None, :], Y64, S, 1e-5, f"{NAME[dt]} gemv M={M} K={K}")
+
+
 # ----------------------------------------------------------------- GEMM ----
 
 def gemm_shapes(dt):
