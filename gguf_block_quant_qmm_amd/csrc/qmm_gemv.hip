@@ -176,6 +176,7 @@ template <> struct Unit<QMM_Q4_K> {
 #pragma unroll
         for (int i = 0; i < 8; i++) v[4 + i] = q[i];
     }
+
     __device__ static int x4(int u, int i) { return 16 * u + i; }
     __device__ static float dot(const uint32_t (&v)[NL], const float (&xv)[64], const Off &o) {
         // sub-block 2c = low nibbles of qs[32c + j], 2c+1 = high nibbles.  Each
@@ -207,57 +208,54 @@ template <> struct Unit<QMM_Q4_K> {
 };
 
 template <> struct Unit<QMM_Q6_K> {
-    // Windows of dwords starting at the super-block aligned down to 4 bytes
-    // (odd super-blocks start 2 bytes past a dword when rows are dword
-    // aligned): A = ql[64h+16lh ..+16], B = ql[64h+32+16lh ..+16],
-    // C = qh[32h+16lh ..+16] (5 dwords each), S = sc[8h .. 8h+8) (3 dwords),
-    // D = the dword holding d.  An even number of super-blocks per row keeps
-    // every window inside the blob.
-    static constexpr int NL = 5 + 5 + 5 + 3 + 1;
-    struct Off { uint32_t a, c, s, d; int sh, lh; };
+    // Unit u = 4 sb + 2 h + lh: the 64 weights {128h + 32g + 16lh + i : g < 4,
+    // i < 16} of super-block sb, which share one 16-byte slice of each ql half
+    // and of qh.  Loads: A = ql[64h+16lh ..+16], B = ql[64h+32+16lh ..+16],
+    // C = qh[32h+16lh ..+16], S = sc[8h ..+8], D = d.  Super-blocks are 210
+    // bytes, so odd ones start 2 bytes off a dword: the loads are byte-
+    // addressed (unaligned buffer loads), which keeps every window at its
+    // own size and needs no realignment.
+    static constexpr int NL = 4 + 4 + 4 + 2 + 1;
+    struct Off { uint32_t a, c, s, d; int lh; };
     __device__ static Off lane_off(int u) {
-        const int h = (u >> 1) & 1, lh = u & 1, sh = 2 * ((u >> 2) & 1);
-        const uint32_t base = 210u * (u >> 2) - sh;
-        return {base + 64u * h + 16u * lh, base + 128u + 32u * h + 16u * lh, base + 192u + 8u * h, base + 208u,
-                sh, lh};
+        const int h = (u >> 1) & 1, lh = u & 1;
+        const uint32_t base = 210u * (u >> 2);
+        return {base + 64u * h + 16u * lh, base + 128u + 32u * h + 16u * lh, base + 192u + 8u * h, base + 208u, lh};
     }
     __device__ static void load(Rsrc rs, uint32_t row, const Off &o, uint32_t (&v)[NL]) {
-        uint32_t a[5], b[5], c[5], s[3], d[1];
-        ldb(rs, o.a, row, a);
-        ldb(rs, o.a + 32u, row, b);
-        ldb(rs, o.c, row, c);
-        ldb(rs, o.s, row, s);
-        ldb(rs, o.d, row, d);
-#pragma unroll
-        for (int i = 0; i < 5; i++) { v[i] = a[i]; v[5 + i] = b[i]; v[10 + i] = c[i]; }
-        v[15] = s[0]; v[16] = s[1]; v[17] = s[2]; v[18] = d[0];
+        const u32x4_t a = __builtin_amdgcn_raw_buffer_load_b128(rs, o.a, row, 0);
+        const u32x4_t b = __builtin_amdgcn_raw_buffer_load_b128(rs, o.a + 32u, row, 0);
+        const u32x4_t c = __builtin_amdgcn_raw_buffer_load_b128(rs, o.c, row, 0);
+        const u32x2_t sc = __builtin_amdgcn_raw_buffer_load_b64(rs, o.s, row, 0);
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+        v[8] = c.x; v[9] = c.y; v[10] = c.z; v[11] = c.w;
+        v[12] = sc.x; v[13] = sc.y;
+        v[14] = __builtin_amdgcn_raw_buffer_load_b16(rs, o.d, row, 0);
     }
     __device__ static int x4(int u, int i) {
         // unit u = 4b + 2h + lh covers x[256b + 128h + 32g + 16lh + j], g < 4, j < 16
         return 64 * (u >> 2) + 32 * ((u >> 1) & 1) + 8 * (i >> 2) + 4 * (u & 1) + (i & 3);
     }
     __device__ static float dot(const uint32_t (&v)[NL], const float (&xv)[64], const Off &o) {
-        const half2_t bias = {(_Float16)-1056.0f, (_Float16)-1056.0f};  // q - 32
-        const uint32_t sh = (uint32_t)o.sh;
-        const float d = h2f(v[18] >> (8 * sh));
-        const uint32_t sc0 = __builtin_amdgcn_alignbyte(v[16], v[15], sh);  // sc[8h .. 8h+4)
-        const uint32_t sc1 = __builtin_amdgcn_alignbyte(v[17], v[16], sh);  // sc[8h+4 .. 8h+8)
+        // code q = lo4 | hi2 << 4 per byte; (q - 32) 2^-24 as an exact f16 subnormal
+        const half2_t b32 = as_h2(0x80208020u);  // -32 * 2^-24
+        const float d = h2f(v[14]);
         float grp[4];
 #pragma unroll
         for (int gp = 0; gp < 4; gp += 2) {  // two groups at a time: 8 independent chains
-            half2_t w[2][4][2];  // [group][dword][q02, q13]
+            half2_t w[2][4][2];  // [group][dword][bytes 0,2 | bytes 1,3]
 #pragma unroll
             for (int k = 0; k < 2; k++) {
                 const int g = gp + k;
 #pragma unroll
                 for (int t = 0; t < 4; t++) {
-                    const uint32_t L = (g & 1) ? __builtin_amdgcn_alignbyte(v[6 + t], v[5 + t], sh)
-                                               : __builtin_amdgcn_alignbyte(v[1 + t], v[t], sh);
-                    const uint32_t C = __builtin_amdgcn_alignbyte(v[11 + t], v[10 + t], sh);
-                    const uint32_t lo = (g < 2 ? L : (L >> 4)) & 0x0F0F0F0Fu;
+                    const uint32_t L = (g & 1) ? v[4 + t] : v[t];
+                    const uint32_t C = v[8 + t];
                     const uint32_t hi = (g < 2 ? (C << (4 - 2 * g)) : (C >> (2 * g - 4))) & 0x30303030u;
-                    const uint32_t q = lo | hi;  // four 6-bit codes, one per byte
-                    w[k][t][0] = bytes02_as_f16(q) + bias; w[k][t][1] = bytes13_as_f16(q) + bias;
+                    const uint32_t q = ((g < 2 ? L : (L >> 4)) & 0x0F0F0F0Fu) | hi;
+                    w[k][t][0] = as_h2(q & 0x00FF00FFu) + b32;
+                    w[k][t][1] = as_h2(__builtin_amdgcn_perm(0u, q, 0x0C030C01u)) + b32;
                 }
             }
             float s8[8];
@@ -283,9 +281,9 @@ template <> struct Unit<QMM_Q6_K> {
         float total = 0.f;
 #pragma unroll
         for (int g = 0; g < 4; g++) {
-            const uint32_t scw = (g < 2) ? sc0 : sc1;
-            const int sbyte = __builtin_amdgcn_sbfe((int)scw, 16 * (g & 1) + 8 * o.lh, 8);  // sc[8h + 2g + lh]
-            total = fmaf(d * (float)sbyte, grp[g], total);
+            const uint32_t scw = (g < 2) ? v[12] : v[13];  // sc[8h .. 8h+4), sc[8h+4 .. 8h+8)
+            const int sbyte = (int)__builtin_amdgcn_sbfe((int)scw, 16 * (g & 1) + 8 * o.lh, 8);  // sc[8h + 2g + lh]
+            total = fmaf(d * 16777216.0f * (float)sbyte, grp[g], total);
         }
         return total;
     }
@@ -349,7 +347,8 @@ __global__ void __launch_bounds__(256) gemv_kernel(const uint8_t *__restrict__ b
                                                    int64_t per_owner, int64_t extra) {
     constexpr int NL = Unit<DT>::NL;
     extern __shared__ __attribute__((aligned(16))) floatx4 xs[];
-    __shared__ float red[2][R][4];
+    constexpr int RED_G = 16;
+    __shared__ float red[WAVE_ROWS ? 1 : RED_G][R][4];
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6), nwaves = blockDim.x >> 6;
     const int u = WAVE_ROWS ? lane : t;
@@ -379,7 +378,6 @@ __global__ void __launch_bounds__(256) gemv_kernel(const uint8_t *__restrict__ b
     float xv[64];
     x_from_lds<DT>(xs, active ? u : 0, xv);
 
-    int parity = 0;
     for (int64_t i0 = 0; i0 < n; i0 += D + 1) {
 #pragma unroll
         for (int s = 0; s <= D; s++) {
@@ -400,17 +398,25 @@ __global__ void __launch_bounds__(256) gemv_kernel(const uint8_t *__restrict__ b
                             if (row0 + r < M) y[row0 + r] = acc[r];
                     }
                 } else {
+                    // partial sums of up to RED_G row groups wait in LDS; one
+                    // barrier pair per RED_G groups (the count is uniform
+                    // across the workgroup)
+                    const int slot = (int)(i % RED_G);
                     if (lane == 63) {
 #pragma unroll
-                        for (int r = 0; r < R; r++) red[parity][r][wave] = acc[r];
+                        for (int r = 0; r < R; r++) red[slot][r][wave] = acc[r];
                     }
-                    __syncthreads();
-                    if (t < R && row0 + t < M) {
-                        float sum = red[parity][t][0];
-                        for (int w = 1; w < nwaves; w++) sum += red[parity][t][w];
-                        y[row0 + t] = sum;
+                    if (slot == RED_G - 1 || i == n - 1) {
+                        __syncthreads();
+                        if (t < (slot + 1) * R) {
+                            const int gi = t / R, r = t % R;
+                            const int64_t row = (g0 + i - slot + gi) * R + r;
+                            float sum = red[gi][r][0];
+                            for (int w = 1; w < nwaves; w++) sum += red[gi][r][w];
+                            if (row < M) y[row] = sum;
+                        }
+                        __syncthreads();
                     }
-                    parity ^= 1;
                 }
             }
         }
