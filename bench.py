@@ -211,7 +211,7 @@ def main():
             "rotation_copies": PR,
             "roofline": {
                 "bound": "mfma",
-                "kernel": "qmm::gemm_wreg_kernel<12,32,128,3,8> (Q4_K)",
+                "kernel": "qmm::gemm_wb_kernel<12,32,128,2,8,4,2> (Q4_K)",
                 "achieved": round(tflops, 2),
                 "peak": F16_MFMA_PEAK_TFLOPS,
                 "unit": "TFLOP/s",

@@ -118,4 +118,47 @@ __device__ __forceinline__ half2_t bytes13_as_f16(uint32_t v) {
     return __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, v, 0x04030401u));
 }
 
+// Bounds-checked buffer loads: a resource covers [base, base + bytes); any
+// dword at or past the byte count reads as 0 without a memory access, so
+// out-of-range rows, tokens and row groups need no branch around a load (a
+// branch around a load makes the compiler's wait counts conservative).
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x3_t __attribute__((ext_vector_type(3)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ Rsrc make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// The same from values known to be wave-uniform but not provably so to the
+// compiler: without the explicit readfirstlane it keeps the descriptor in
+// VGPRs and wraps every load in a waterfall loop.
+__device__ __forceinline__ Rsrc make_rsrc_uniform(const void *base, uint32_t bytes) {
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b), hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+    const uint64_t u = ((uint64_t)hi << 32) | lo;
+    return make_rsrc(reinterpret_cast<const void *>(u), __builtin_amdgcn_readfirstlane(bytes));
+}
+
+// N dwords at byte offset voff (per lane) + soff (uniform)
+template <int N>
+__device__ __forceinline__ void ldb(Rsrc rs, uint32_t voff, uint32_t soff, uint32_t (&v)[N]) {
+    int i = 0;
+#pragma unroll
+    for (; i + 4 <= N; i += 4) {
+        const u32x4_t q = __builtin_amdgcn_raw_buffer_load_b128(rs, voff + 4 * i, soff, 0);
+        v[i] = q.x; v[i + 1] = q.y; v[i + 2] = q.z; v[i + 3] = q.w;
+    }
+    if constexpr (N % 4 == 3) {
+        const u32x3_t q = __builtin_amdgcn_raw_buffer_load_b96(rs, voff + 4 * i, soff, 0);
+        v[i] = q.x; v[i + 1] = q.y; v[i + 2] = q.z;
+    } else if constexpr (N % 4 == 2) {
+        const u32x2_t q = __builtin_amdgcn_raw_buffer_load_b64(rs, voff + 4 * i, soff, 0);
+        v[i] = q.x; v[i + 1] = q.y;
+    } else if constexpr (N % 4 == 1) {
+        v[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, voff + 4 * i, soff, 0);
+    }
+}
+
 }  // namespace qmm

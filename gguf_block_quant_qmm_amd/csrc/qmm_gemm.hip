@@ -322,121 +322,42 @@ __global__ void __launch_bounds__(256) gemm_kernel(const uint8_t *__restrict__ b
     }
 }
 
-// ================================================= register-B GEMM ====
-// Each wavefront owns TM weight rows and decodes their k-tiles straight into
-// the B operand registers of v_mfma_f32_32x32x16_f16 (lane l: row l%32 of a
-// 32-row block, 8 consecutive k at 8*(l/32) of every 16-deep step), so a
-// weight is decoded exactly once per token tile and never passes through
-// LDS.  The f32 activations of a k-tile are converted once per workgroup
-// into a double-buffered f16 LDS tile that the 4 wavefronts share as the A
-// operand.  Raw weight bytes are prefetched WD k-tiles ahead, activations 2.
-//
-// Exact decode to f16: a code c (< 1024) placed in a 16-bit lane is the f16
-// subnormal c * 2^-24, so v_fma_mix_f32(c, scale * 2^24, bias) computes
-// scale * c + bias exactly and rounds once to f32 (then once to f16).
-
-__device__ __forceinline__ float sub_code(uint32_t bits16) {
-    return (float)__builtin_bit_cast(_Float16, (uint16_t)(bits16 & 0xFFFFu));
-}
-
-// 8 weights from two dwords of byte codes (bytes 0..3 of q0, then of q1):
-// w_j = scale * code_j + bias, rounded to f16.
-__device__ __forceinline__ half8 dec8(uint32_t q0, uint32_t q1, float scale24, float bias) {
-    const uint32_t a = q0 & 0x00FF00FFu, b = (q0 >> 8) & 0x00FF00FFu;
-    const uint32_t c = q1 & 0x00FF00FFu, d = (q1 >> 8) & 0x00FF00FFu;
-    half8 w;
-    w[0] = (_Float16)fmaf(sub_code(a), scale24, bias);
-    w[1] = (_Float16)fmaf(sub_code(b), scale24, bias);
-    w[2] = (_Float16)fmaf(sub_code(a >> 16), scale24, bias);
-    w[3] = (_Float16)fmaf(sub_code(b >> 16), scale24, bias);
-    w[4] = (_Float16)fmaf(sub_code(c), scale24, bias);
-    w[5] = (_Float16)fmaf(sub_code(d), scale24, bias);
-    w[6] = (_Float16)fmaf(sub_code(c >> 16), scale24, bias);
-    w[7] = (_Float16)fmaf(sub_code(d >> 16), scale24, bias);
-    return w;
-}
+// ================================================ weight decoders ====
+// Each wavefront decodes the k-tiles of its weight rows straight into the B
+// operand registers of v_mfma_f32_32x32x16_f16 (lane l: row l % 32 of a
+// 32-row block, 8 k values for lane half kh = l / 32 in every 16-deep step),
+// so a weight is decoded once per token tile and never passes through LDS.
+// Exact decode to f16: a code c placed in the low mantissa bits of a 16-bit
+// lane is an f16 subnormal (c * 2^-24, or c * 2^-20 for bits 4..7), so one
+// v_fma_mix_f32 with the scale * 2^24 (or 2^20) and the bias forms
+// scale * c + bias exactly before its single rounding.
 
 constexpr float TWO24 = 16777216.0f;
+
+__device__ __forceinline__ _Float16 mixw(_Float16 code, float scale, float bias) {
+    return (_Float16)fmaf((float)code, scale, bias);
+}
+// four weights from the two code pairs of a dword
+__device__ __forceinline__ void quad(uint32_t p02, uint32_t p13, float scale, float bias, half8 &f, int at) {
+    const half2_t a = __builtin_bit_cast(half2_t, p02), b = __builtin_bit_cast(half2_t, p13);
+    f[at] = mixw(a.x, scale, bias);
+    f[at + 1] = mixw(a.y, scale, bias);
+    f[at + 2] = mixw(b.x, scale, bias);
+    f[at + 3] = mixw(b.y, scale, bias);
+}
 
 // BDec<DT>: raw bytes of one row's 64-deep k-tile that lane half kh needs
 // (its k = 16s + 8kh + j, s < 4, j < 8), and their decode to 4 half8.
 template <int DT> struct BDec;
 
-template <> struct BDec<QMM_Q4_0> {
-    // blocks b0 = k0/32 (k < 32) and b0+1: a 36-byte dword-aligned pair
-    static constexpr int NW = 9;
-    __device__ static void load(const uint8_t *row, int64_t k0, int, uint32_t (&r)[NW]) {
-        const uint32_t *p = reinterpret_cast<const uint32_t *>(row + 18 * (k0 / 32));
-#pragma unroll
-        for (int i = 0; i < NW; i++) r[i] = p[i];
-    }
-    __device__ static void decode(const uint32_t (&r)[NW], int kh, int64_t, half8 (&f)[4]) {
-        // block 0: qs at bytes 2..17; block 1: d at bytes 18..19, qs at 20..35
-        const float d0 = h2f(r[0]), d1 = h2f(r[4] >> 16);
-        const uint32_t a0 = __builtin_amdgcn_alignbyte(r[1], r[0], 2), a1 = __builtin_amdgcn_alignbyte(r[2], r[1], 2);
-        const uint32_t a2 = __builtin_amdgcn_alignbyte(r[3], r[2], 2), a3 = __builtin_amdgcn_alignbyte(r[4], r[3], 2);
-        const uint32_t p0 = kh ? a2 : a0, p1 = kh ? a3 : a1;             // qs[8kh .. 8kh+8) of block 0
-        const uint32_t q0 = kh ? r[7] : r[5], q1 = kh ? r[8] : r[6];      // of block 1
-        // element e < 16: low nibble of qs[e]; e >= 16: high nibble of qs[e-16]
-        f[0] = dec8(p0 & 0x0F0F0F0Fu, p1 & 0x0F0F0F0Fu, d0 * TWO24, -8.f * d0);
-        f[1] = dec8((p0 >> 4) & 0x0F0F0F0Fu, (p1 >> 4) & 0x0F0F0F0Fu, d0 * TWO24, -8.f * d0);
-        f[2] = dec8(q0 & 0x0F0F0F0Fu, q1 & 0x0F0F0F0Fu, d1 * TWO24, -8.f * d1);
-        f[3] = dec8((q0 >> 4) & 0x0F0F0F0Fu, (q1 >> 4) & 0x0F0F0F0Fu, d1 * TWO24, -8.f * d1);
-    }
-};
 
-template <> struct BDec<QMM_Q8_0> {
-    // blocks b0 = k0/32 and b0+1: a 68-byte dword-aligned pair
-    static constexpr int NW = 17;
-    __device__ static void load(const uint8_t *row, int64_t k0, int, uint32_t (&r)[NW]) {
-        const uint32_t *p = reinterpret_cast<const uint32_t *>(row + 34 * (k0 / 32));
-#pragma unroll
-        for (int i = 0; i < NW; i++) r[i] = p[i];
-    }
-    __device__ static void decode(const uint32_t (&r)[NW], int kh, int64_t, half8 (&f)[4]) {
-        const float d0 = h2f(r[0]), d1 = h2f(r[8] >> 16);
-        // block 0: q at bytes 2..33 -> realigned dwords; block 1: q at bytes 36..67 = r[9..16]
-        uint32_t b0[8];
-#pragma unroll
-        for (int i = 0; i < 8; i++) b0[i] = __builtin_amdgcn_alignbyte(r[i + 1], r[i], 2);
-        const int o = 2 * kh;  // dword offset of q[8kh] within a 32-byte run
-        const uint32_t flip = 0x80808080u;  // q + 128 as an unsigned code
-        f[0] = dec8((kh ? b0[2] : b0[0]) ^ flip, (kh ? b0[3] : b0[1]) ^ flip, d0 * TWO24, -128.f * d0);
-        f[1] = dec8((kh ? b0[6] : b0[4]) ^ flip, (kh ? b0[7] : b0[5]) ^ flip, d0 * TWO24, -128.f * d0);
-        f[2] = dec8((kh ? r[11] : r[9]) ^ flip, (kh ? r[12] : r[10]) ^ flip, d1 * TWO24, -128.f * d1);
-        f[3] = dec8((kh ? r[15] : r[13]) ^ flip, (kh ? r[16] : r[14]) ^ flip, d1 * TWO24, -128.f * d1);
-        (void)o;
-    }
-};
 
-template <> struct BDec<QMM_Q4_K> {
-    // header (d, dmin, 12 scale bytes) + qs[32c + 8kh ..+8) + qs[32c + 16 + 8kh ..+8)
-    static constexpr int NW = 8;
-    __device__ static void load(const uint8_t *row, int64_t k0, int kh, uint32_t (&r)[NW]) {
-        const uint8_t *sb = row + 144 * (k0 / 256);
-        const int c = (int)((k0 % 256) / 64);
-        const uint32_t *h = reinterpret_cast<const uint32_t *>(sb);
-        const uint32_t *q = reinterpret_cast<const uint32_t *>(sb + 16 + 32 * c + 8 * kh);
-        r[0] = h[0]; r[1] = h[1]; r[2] = h[2]; r[3] = h[3];
-        r[4] = q[0]; r[5] = q[1]; r[6] = q[4]; r[7] = q[5];
-    }
-    __device__ static void decode(const uint32_t (&r)[NW], int, int64_t k0, half8 (&f)[4]) {
-        const int c = (int)((k0 % 256) / 64);
-        const float d = h2f(r[0]), dmin = h2f(r[0] >> 16);
-        int sc0, m0, sc1, m1;
-        q4k_scale_min(r[1], r[2], r[3], 2 * c, sc0, m0);
-        q4k_scale_min(r[1], r[2], r[3], 2 * c + 1, sc1, m1);
-        const float s0 = d * (float)sc0 * TWO24, b0 = -(dmin * (float)m0);
-        const float s1 = d * (float)sc1 * TWO24, b1 = -(dmin * (float)m1);
-        // sub-block 2c = low nibbles (k < 32), 2c+1 = high nibbles
-        f[0] = dec8(r[4] & 0x0F0F0F0Fu, r[5] & 0x0F0F0F0Fu, s0, b0);
-        f[1] = dec8(r[6] & 0x0F0F0F0Fu, r[7] & 0x0F0F0F0Fu, s0, b0);
-        f[2] = dec8((r[4] >> 4) & 0x0F0F0F0Fu, (r[5] >> 4) & 0x0F0F0F0Fu, s1, b1);
-        f[3] = dec8((r[6] >> 4) & 0x0F0F0F0Fu, (r[7] >> 4) & 0x0F0F0F0Fu, s1, b1);
-    }
-};
 
 template <> struct BDec<QMM_Q6_K> {
+    // 8 consecutive k per step, in sigma order within each group of 4
+    static constexpr bool SWAP = true;
+    __device__ static int xpos(int c4) { return 4 * c4; }
+    struct State {};
     // quarter qq of the super-block: h = qq/2, groups g0 = 2(qq&1) and g0+1.
     // Windows aligned down to the dword (odd super-blocks start 2 bytes into
     // one): ql[64h + 16s' + 8kh ..+8) for s' = 0..3 (3 dwords each),
@@ -460,6 +381,25 @@ template <> struct BDec<QMM_Q6_K> {
         r[18] = ps[0]; r[19] = ps[1];
         r[20] = *reinterpret_cast<const uint32_t *>(base + 208);
         (void)g0;
+    }
+    __device__ static void loadb(Rsrc rs, uint32_t roff, int64_t k0, int kh, int, uint32_t (&r)[NW]) {
+        const int64_t sb = k0 / 256;
+        const int qq = (int)((k0 % 256) / 64), h = qq >> 1, g0 = 2 * (qq & 1);
+        const uint32_t base = (uint32_t)(210 * sb - 2 * (sb & 1));  // dword aligned
+        uint32_t w3[3], w2[2], w1[1];
+#pragma unroll
+        for (int s = 0; s < 4; s++) {
+            ldb(rs, roff + 8u * kh, base + 64u * h + 16u * s, w3);
+            r[3 * s] = w3[0]; r[3 * s + 1] = w3[1]; r[3 * s + 2] = w3[2];
+        }
+        ldb(rs, roff + 8u * kh, base + 128u + 32u * h, w3);
+        r[12] = w3[0]; r[13] = w3[1]; r[14] = w3[2];
+        ldb(rs, roff + 8u * kh, base + 128u + 32u * h + 16u, w3);
+        r[15] = w3[0]; r[16] = w3[1]; r[17] = w3[2];
+        ldb(rs, roff, base + 192u + 8u * h + 2u * g0 - (2u * g0 & 3u), w2);
+        r[18] = w2[0]; r[19] = w2[1];
+        ldb(rs, roff, base + 208u, w1);
+        r[20] = w1[0];
     }
     __device__ static void decode(const uint32_t (&r)[NW], int, int64_t k0, half8 (&f)[4]) {
         const int64_t sb = k0 / 256;
@@ -485,62 +425,195 @@ template <> struct BDec<QMM_Q6_K> {
             const uint32_t hi0 = ((qh[li][0] >> (2 * g)) & 0x03030303u) << 4;
             const uint32_t hi1 = ((qh[li][1] >> (2 * g)) & 0x03030303u) << 4;
             const float dsc = d * (float)(int)__builtin_amdgcn_sbfe((int)scw, 8 * (2 * gi + li), 8);  // the builtin returns unsigned
-            f[s] = dec8(lo0 | hi0, lo1 | hi1, dsc * TWO24, -32.f * dsc);
+            const uint32_t q0 = lo0 | hi0, q1 = lo1 | hi1;  // four 6-bit codes each, one per byte
+            quad(q0 & 0x00FF00FFu, (q0 >> 8) & 0x00FF00FFu, dsc * TWO24, -32.f * dsc, f[s], 0);
+            quad(q1 & 0x00FF00FFu, (q1 >> 8) & 0x00FF00FFu, dsc * TWO24, -32.f * dsc, f[s], 4);
+        }
+    }
+    __device__ static void decode(const uint32_t (&r)[NW], State &, int kh, int, int64_t k0, half8 (&f)[4]) {
+        decode(r, kh, k0, f);
+    }
+};
+
+// ------------------------------------------- permuted-k decoders ----
+// The contraction only needs the A and B fragments of a 16-deep step to agree
+// on which k each of a lane's 8 elements is.  These decoders take each
+// lane's bytes in the order that is cheapest to unpack -- a dword d gives
+// the element pairs (byte 0, byte 2) = d & mask and (byte 1, byte 3) =
+// (d >> 8) & mask, one VOP2 instruction per two codes, low nibbles as
+// c * 2^-24 and high nibbles as c * 2^-20 (exact f16 subnormals) -- and the
+// activations are written to LDS in the same order: within every group of 8
+// the k order is sigma = (0 2 1 3 4 6 5 7), so a float4 of consecutive k
+// lands as [x0 x2 x1 x3] in 4 consecutive LDS slots.  Each weight is formed
+// by one v_fma_mix (scale * code + bias, then one rounding to f16).
+template <int DT> struct PDec;
+
+template <> struct PDec<QMM_Q4_K> {
+    // lane half kh: qs[32c + 16kh ..+16) of chunk c; step s: k = 32 (s >> 1) +
+    // 16 kh + 8 (s & 1) + sigma(j)  (low nibbles: sub-block 2c, high: 2c+1).
+    // The super-block header (d, dmin, 12 scale bytes) comes with chunk 0 and
+    // is unpacked once into State for the four chunks.
+    static constexpr int NW = 8;
+    static constexpr bool SWAP = true;
+    struct State { float s[8], n[8]; };
+    __device__ static int xpos(int c4) {
+        return 16 * (2 * (c4 >> 3) + ((c4 >> 1) & 1)) + 8 * ((c4 >> 2) & 1) + 4 * (c4 & 1);
+    }
+    __device__ static void loadb(Rsrc rs, uint32_t roff, int64_t k0, int kh, int c, uint32_t (&r)[NW]) {
+        const uint32_t sb = (uint32_t)(144 * (k0 / 256));
+        if (c == 0) {
+            uint32_t h[4];
+            ldb(rs, roff, sb, h);
+#pragma unroll
+            for (int i = 0; i < 4; i++) r[i] = h[i];
+        }
+        uint32_t q[4];
+        ldb(rs, roff + 16u * kh, sb + 16u + 32u * (uint32_t)c, q);
+#pragma unroll
+        for (int i = 0; i < 4; i++) r[4 + i] = q[i];
+    }
+    __device__ static void decode(const uint32_t (&r)[NW], State &st, int, int c, int64_t, half8 (&f)[4]) {
+        if (c == 0) {
+            const float d = h2f(r[0]), dmin = h2f(r[0] >> 16);
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                int sc, mn;
+                q4k_scale_min(r[1], r[2], r[3], i, sc, mn);
+                st.s[i] = d * (float)sc * ((i & 1) ? 1048576.0f : TWO24);  // high nibbles enter as c * 2^-20
+                st.n[i] = -(dmin * (float)mn);
+            }
+        }
+        const float s0 = st.s[2 * c], n0 = st.n[2 * c], s1 = st.s[2 * c + 1], n1 = st.n[2 * c + 1];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const uint32_t w = r[4 + i], t = w >> 8;
+            quad(w & 0x000F000Fu, t & 0x000F000Fu, s0, n0, f[i >> 1], 4 * (i & 1));
+            quad(w & 0x00F000F0u, t & 0x00F000F0u, s1, n1, f[2 + (i >> 1)], 4 * (i & 1));
         }
     }
 };
 
-// Workgroup: W wavefronts x TM weight rows, BN tokens; k-tiles of 64.  The
-// decode of k-tile kt+1 is issued in four slices between the four 16-deep
-// MFMA steps of k-tile kt, so the matrix cores and the vector ALUs overlap.
-template <int DT, int TM, int BN, int WD, int W>
-__global__ void __launch_bounds__(64 * W) gemm_wreg_kernel(const uint8_t *__restrict__ blob, int64_t M, int64_t K,
-                                                          int64_t N, int64_t row_bytes, const float *__restrict__ X,
-                                                          float *__restrict__ Y, int n_ntiles) {
+template <> struct PDec<QMM_Q4_0> {
+    // lane half kh: block 2 kt + kh (18 bytes, read from the dword at or just
+    // below it); step s: k = 32 kh + 8 s + sigma(j)
+    static constexpr int NW = 5;
+    static constexpr bool SWAP = true;
+    __device__ static int xpos(int c4) { return 16 * ((c4 >> 1) & 3) + 8 * (c4 >> 3) + 4 * (c4 & 1); }
+    struct State {};
+    __device__ static void loadb(Rsrc rs, uint32_t roff, int64_t k0, int kh, int, uint32_t (&r)[NW]) {
+        ldb(rs, roff + 16u * kh, (uint32_t)(36 * (k0 / 64)), r);
+    }
+    __device__ static void decode(const uint32_t (&r)[NW], State &, int kh, int, int64_t, half8 (&f)[4]) {
+        // block 0 starts at byte 0 of r (codes 2 bytes in), block 1 at byte 2
+        // (codes dword aligned from r[1])
+        const uint32_t sel = kh ? 0x07060504u : 0x05040302u;
+        const float d = h2f(kh ? r[0] >> 16 : r[0]);
+        const float s24 = d * TWO24, s20 = d * 1048576.0f, n = -8.f * d;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const uint32_t w = __builtin_amdgcn_perm(r[i + 1], r[i], sel), t = w >> 8;  // qs[4i .. 4i+4)
+            quad(w & 0x000F000Fu, t & 0x000F000Fu, s24, n, f[i >> 1], 4 * (i & 1));
+            quad(w & 0x00F000F0u, t & 0x00F000F0u, s20, n, f[2 + (i >> 1)], 4 * (i & 1));
+        }
+    }
+};
+
+template <> struct PDec<QMM_Q8_0> {
+    // lane half kh: block 2 kt + kh (34 bytes); step s: k = 32 kh + 8 s + sigma(j)
+    static constexpr int NW = 9;
+    static constexpr bool SWAP = true;
+    __device__ static int xpos(int c4) { return 16 * ((c4 >> 1) & 3) + 8 * (c4 >> 3) + 4 * (c4 & 1); }
+    struct State {};
+    __device__ static void loadb(Rsrc rs, uint32_t roff, int64_t k0, int kh, int, uint32_t (&r)[NW]) {
+        ldb(rs, roff + 32u * kh, (uint32_t)(68 * (k0 / 64)), r);
+    }
+    __device__ static void decode(const uint32_t (&r)[NW], State &, int kh, int, int64_t, half8 (&f)[4]) {
+        const uint32_t sel = kh ? 0x07060504u : 0x05040302u;
+        const float d = h2f(kh ? r[0] >> 16 : r[0]);
+        const float s24 = d * TWO24, n = -128.f * d;  // codes enter as q + 128
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const uint32_t w = __builtin_amdgcn_perm(r[i + 1], r[i], sel) ^ 0x80808080u;  // q[4i .. 4i+4) + 128
+            quad(w & 0x00FF00FFu, (w >> 8) & 0x00FF00FFu, s24, n, f[i >> 1], 4 * (i & 1));
+        }
+    }
+};
+
+template <int DT> struct WbDec { using type = PDec<DT>; };
+template <> struct WbDec<QMM_Q6_K> { using type = BDec<QMM_Q6_K>; };
+
+// ============================================= register-B GEMM, buffered ====
+// The register-B design above with every global access a bounds-checked
+// buffer load: weight rows past M and token rows past N read as zeros, and
+// the prefetch of k-tiles past the end is clamped onto the last one, so the
+// k-loop has no branch at all (K is a multiple of UNR k-tiles) and every
+// wait is for exactly the data the next step consumes.  Workgroups are
+// ordered so that the ones sharing a weight tile run on the same XCD (the
+// dispatcher sends workgroup b to XCD b % 8), whose L2 then serves the
+// weights to all token tiles.
+template <int DT, int TM, int BN, int WD, int W, int INTERLEAVE, int XD>
+__global__ void __launch_bounds__(64 * W) gemm_wb_kernel(const uint8_t *__restrict__ blob, int64_t M, int64_t K,
+                                                        int64_t N, int64_t row_bytes, const float *__restrict__ X,
+                                                        float *__restrict__ Y, int n_mtiles, int n_ntiles) {
     constexpr int FM = TM / 32, FN = BN / 32;
     constexpr int NT = 64 * W;
-    constexpr int NXF = BN * (BK / 4) / NT;  // float4 of X per thread per k-tile
-    static_assert(NXF >= 1 && BN * (BK / 4) % NT == 0, "activation tile split");
-    constexpr int XD = 2;                     // activation k-tiles in flight
-    using BD = BDec<DT>;
+    constexpr int NX4 = BN * (BK / 4);          // float4 of X per k-tile
+    constexpr int NXF = (NX4 + NT - 1) / NT;    // per thread (the last ones repeat a valid float4)
+    constexpr int UNR = 4;  // k-tiles per trip: a Q4_K super-block; K is a multiple of 4 k-tiles
+    static_assert(UNR % WD == 0 && UNR % XD == 0, "ring sizes");
+    using BD = typename WbDec<DT>::type;
     __shared__ __attribute__((aligned(16))) _Float16 Xs[2][BN * LDK];
 
     const int t = threadIdx.x, lane = t & 63, kh = lane >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-    const int64_t mt = blockIdx.x / n_ntiles, nt = blockIdx.x % n_ntiles;
+    const int total = n_mtiles * n_ntiles, b = blockIdx.x, xcd = b & 7, local = b >> 3;
+    const int tile = xcd * (total >> 3) + (xcd < (total & 7) ? xcd : (total & 7)) + local;
+    const int64_t mt = tile / n_ntiles, nt = tile % n_ntiles;
     const int64_t n0 = nt * BN, mw = mt * (W * TM) + wave * TM;
     const int64_t nkt = K / BK;
+
+    const int64_t wrows = M - mw < 0 ? 0 : (M - mw < TM ? M - mw : TM);
+    const Rsrc wrs = make_rsrc_uniform(blob + (wrows ? mw : 0) * row_bytes, (uint32_t)(wrows * row_bytes));
+    uint32_t roff[FM];
+#pragma unroll
+    for (int j = 0; j < FM; j++) roff[j] = (uint32_t)((32 * j + (lane & 31)) * row_bytes);
+    const int64_t xrows = N - n0 < BN ? N - n0 : BN;
+    const Rsrc xrs = make_rsrc_uniform(X + n0 * K, (uint32_t)(xrows * K * 4));
+    uint32_t xoff[NXF];
+#pragma unroll
+    for (int i = 0; i < NXF; i++) {
+        const int f = t + NT * i < NX4 ? t + NT * i : NX4 - 1, r = f >> 4, c4 = f & 15;
+        xoff[i] = (uint32_t)((r * K + 4 * c4) * 4);
+    }
 
     uint32_t wr[WD][FM][BD::NW];
     floatx4 xr[XD][NXF];
     half8 bf[2][FM][4];
+    typename BD::State st[FM];
 
-    auto wload = [&](int64_t kt, uint32_t (&w)[FM][BD::NW]) {
+    // c = kt % 4 (a compile-time constant at every call)
+    auto wload = [&](int64_t kt, int c, uint32_t (&w)[FM][BD::NW]) {
+        const int64_t kc = kt < nkt ? kt : nkt - 4 + c;
 #pragma unroll
-        for (int j = 0; j < FM; j++) {
-            const int64_t m = mw + 32 * j + (lane & 31);
-            if (m < M) {
-                BD::load(blob + m * row_bytes, kt * BK, kh, w[j]);
-            } else {
-#pragma unroll
-                for (int i = 0; i < BD::NW; i++) w[j][i] = 0u;
-            }
-        }
+        for (int j = 0; j < FM; j++) BD::loadb(wrs, roff[j], kc * BK, kh, c, w[j]);
     };
     auto xload = [&](int64_t kt, floatx4 (&x)[NXF]) {
+        const uint32_t kb = (uint32_t)((kt < nkt ? kt : nkt - 1) * BK * 4);
 #pragma unroll
-        for (int i = 0; i < NXF; i++) {
-            const int f = t + NT * i, r = f >> 4, c4 = f & 15;
-            const int64_t n = n0 + r;
-            x[i] = n < N ? *reinterpret_cast<const floatx4 *>(X + n * K + kt * BK + 4 * c4) : floatx4{0.f, 0.f, 0.f, 0.f};
-        }
+        for (int i = 0; i < NXF; i++)
+            x[i] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(xrs, xoff[i], kb, 0));
     };
     auto xstore = [&](const floatx4 (&x)[NXF], _Float16 *xs) {
 #pragma unroll
         for (int i = 0; i < NXF; i++) {
-            const int f = t + NT * i, r = f >> 4, c4 = f & 15;
-            half4 hv = {(_Float16)x[i].x, (_Float16)x[i].y, (_Float16)x[i].z, (_Float16)x[i].w};
-            *reinterpret_cast<half4 *>(xs + r * LDK + 4 * c4) = hv;
+            // a clamped repeat writes the same value to the same slot
+            const int f = t + NT * i < NX4 ? t + NT * i : NX4 - 1, r = f >> 4, c4 = f & 15;
+            half4 hv;
+            if constexpr (BD::SWAP)
+                hv = half4{(_Float16)x[i].x, (_Float16)x[i].z, (_Float16)x[i].y, (_Float16)x[i].w};
+            else
+                hv = half4{(_Float16)x[i].x, (_Float16)x[i].y, (_Float16)x[i].z, (_Float16)x[i].w};
+            *reinterpret_cast<half4 *>(xs + r * LDK + BD::xpos(c4)) = hv;
         }
     };
 
@@ -552,62 +625,57 @@ __global__ void __launch_bounds__(64 * W) gemm_wreg_kernel(const uint8_t *__rest
 #pragma unroll
             for (int v = 0; v < 16; v++) acc[i][j][v] = 0.f;
 
-    // prologue: weights k-tiles 0..WD-1, activations 0..XD-1 in flight;
-    // k-tile 0 decoded and staged
 #pragma unroll
-    for (int d = 0; d < WD; d++)
-        if (d < nkt) wload(d, wr[d]);
+    for (int d = 0; d < WD; d++) wload(d, d % 4, wr[d]);
 #pragma unroll
-    for (int d = 0; d < XD; d++)
-        if (d < nkt) xload(d, xr[d]);
+    for (int d = 0; d < XD; d++) xload(d, xr[d]);
 #pragma unroll
-    for (int j = 0; j < FM; j++) BD::decode(wr[0][j], kh, 0, bf[0][j]);
+    for (int j = 0; j < FM; j++) BD::decode(wr[0][j], st[j], kh, 0, 0, bf[0][j]);
     xstore(xr[0], Xs[0]);
-    if (WD < nkt) wload(WD, wr[0]);
-    if (XD < nkt) xload(XD, xr[0]);
+    wload(WD, WD % 4, wr[0]);
+    xload(XD, xr[0]);
     __syncthreads();
 
-    constexpr int UNR = (WD % 2 == 0) ? WD : 2 * WD;  // multiple of WD, XD (=2) and 2
     for (int64_t kb = 0; kb < nkt; kb += UNR) {
 #pragma unroll
         for (int u = 0; u < UNR; u++) {
             const int64_t kt = kb + u;
-            if (kt < nkt) {
-                // this k-tile on the matrix cores, with the next k-tile's weight
-                // decode (one slice per 16-deep step) and activation staging in
-                // between
-                const bool more = kt + 1 < nkt;
-                const _Float16 *xs = Xs[u & 1];
-                half8 nb[FM][4];
+            const _Float16 *xs = Xs[u & 1];
+            // all A fragments of the k-tile are read up front, so the MFMAs
+            // wait for LDS only once per k-tile
+            half8 a[BK / 16][FN];
 #pragma unroll
-                for (int s = 0; s < BK / 16; s++) {
-                    half8 a[FN];
+            for (int s = 0; s < BK / 16; s++)
 #pragma unroll
-                    for (int i = 0; i < FN; i++)
-                        a[i] = *reinterpret_cast<const half8 *>(xs + (32 * i + (lane & 31)) * LDK + 16 * s + 8 * kh);
+                for (int i = 0; i < FN; i++)
+                    a[s][i] = *reinterpret_cast<const half8 *>(xs + (32 * i + (lane & 31)) * LDK + 16 * s + 8 * kh);
+            __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the MFMAs
 #pragma unroll
-                    for (int i = 0; i < FN; i++)
+            for (int s = 0; s < BK / 16; s++) {
 #pragma unroll
-                        for (int j = 0; j < FM; j++)
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], bf[u & 1][j][s], acc[i][j], 0, 0, 0);
-                    if (more) {
-                        if (s == 0) {
+                for (int i = 0; i < FN; i++)
 #pragma unroll
-                            for (int j = 0; j < FM; j++) BD::decode(wr[(u + 1) % WD][j], kh, (kt + 1) * BK, nb[j]);
-                        }
-                        if (s == 1) {
+                    for (int j = 0; j < FM; j++)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[s][i], bf[u & 1][j][s], acc[i][j], 0, 0, 0);
+                // the next k-tile (its data for kt + 1 = nkt is a clamped repeat, never used)
+                if (s == 0) {
 #pragma unroll
-                            for (int j = 0; j < FM; j++)
-#pragma unroll
-                                for (int q = 0; q < 4; q++) bf[(u + 1) & 1][j][q] = nb[j][q];
-                            if (kt + 1 + WD < nkt) wload(kt + 1 + WD, wr[(u + 1) % WD]);
-                        }
-                        if (s == 2) xstore(xr[(u + 1) % XD], Xs[(u + 1) & 1]);
-                        if (s == 3 && kt + 1 + XD < nkt) xload(kt + 1 + XD, xr[(u + 1) % XD]);
-                    }
+                    for (int j = 0; j < FM; j++)
+                        BD::decode(wr[(u + 1) % WD][j], st[j], kh, (u + 1) % 4, (kt + 1) * BK, bf[(u + 1) & 1][j]);
                 }
-                __syncthreads();
+                if (s == 1) wload(kt + 1 + WD, (u + 1 + WD) % 4, wr[(u + 1) % WD]);
+                if (s == 2) xstore(xr[(u + 1) % XD], Xs[(u + 1) & 1]);
+                if (s == 3) xload(kt + 1 + XD, xr[(u + 1) % XD]);
             }
+            if constexpr (INTERLEAVE > 0) {
+                // one MFMA, then INTERLEAVE vector instructions, repeated
+#pragma unroll
+                for (int q = 0; q < (BK / 16) * FN * FM; q++) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, INTERLEAVE, 0);
+                }
+            }
+            __syncthreads();
         }
     }
 
@@ -655,24 +723,27 @@ static hipError_t launch_tile(const uint8_t *blob, int64_t M, int64_t K, int64_t
     return hipGetLastError();
 }
 
-template <int DT, int TM, int BN, int WD, int W>
-static hipError_t launch_wreg(const uint8_t *blob, int64_t M, int64_t K, int64_t N, const float *X, float *Y,
-                              hipStream_t st) {
+
+template <int DT, int TM, int BN, int WD, int W, int IL = 0, int XD = 2>
+static hipError_t launch_wb(const uint8_t *blob, int64_t M, int64_t K, int64_t N, const float *X, float *Y,
+                            hipStream_t st) {
     constexpr int BS = Geo<DT>::BS, BB = Geo<DT>::BB;
     const int64_t row_bytes = (K / BS) * BB;
     const int64_t mtiles = (M + W * TM - 1) / (W * TM), ntiles = (N + BN - 1) / BN;
     const int64_t grid = mtiles * ntiles;
     if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((gemm_wreg_kernel<DT, TM, BN, WD, W>), dim3((unsigned)grid), dim3(64 * W), 0, st, blob, M, K,
-                       N, row_bytes, X, Y, (int)ntiles);
+    hipLaunchKernelGGL((gemm_wb_kernel<DT, TM, BN, WD, W, IL, XD>), dim3((unsigned)grid), dim3(64 * W), 0, st, blob, M, K, N,
+                       row_bytes, X, Y, (int)mtiles, (int)ntiles);
     return hipGetLastError();
 }
 
-// Large-N kernel choice.  Measured on 14336 x 4096 at N = 512: the register-B
-// kernel with 8 wavefronts x 32 rows wins for the 4-bit formats once its grid
-// (M/256 x N/128 workgroups) nearly fills the chip; the LDS-staged kernel wins
-// otherwise.  QMM_GEMM_KERNEL = 0 / 1 / 2 forces LDS-staged / register-B 4x64
-// rows / register-B 8x32 rows (for measurement).
+// Kernel choice (measured): the buffered register-B kernel whenever the
+// layout allows it -- 8 wavefronts x 32 rows x 128 tokens when that grid
+// nearly fills the chip, else 4 x 32 rows x 64 tokens (x 32 tokens for N <=
+// 32) with deeper prefetch -- and the LDS-staged kernel otherwise (K not a
+// multiple of 256, odd block counts).  QMM_GEMM_KERNEL = 0 / 1 / 2 / 3 forces
+// LDS-staged / 8x32x128 / 4x32x64 / 4x32x32 where the layout allows (a
+// measurement lever, read once).
 static int gemm_kernel_choice() {
     static int v = [] {
         const char *e = getenv("QMM_GEMM_KERNEL");
@@ -685,19 +756,20 @@ template <int DT>
 static hipError_t launch_dt(const uint8_t *blob, int64_t M, int64_t K, int64_t N, const float *X, float *Y,
                             hipStream_t st) {
     const bool gen = !aligned_layout(DT, K / Geo<DT>::BS);
-    const bool wreg_ok = !gen && N > 64 && (K % BK) == 0;
+    // buffer resources cover at most 128 token rows of X: 32-bit byte counts
+    const bool wb_ok = !gen && (K % (4 * BK)) == 0 && K * 4 * 128 < ((int64_t)1 << 31);
     int choice = gemm_kernel_choice();
-    if (choice < 0) {
-        const bool four_bit = DT == QMM_Q4_0 || DT == QMM_Q4_K;
-        choice = (four_bit && ((M + 255) / 256) * ((N + 127) / 128) >= 224) ? 2 : 0;
+    if (choice < 0 || (choice > 0 && !wb_ok)) {
+        if (!wb_ok) choice = 0;
+        else if (N <= 32) choice = 3;
+        else if (((M + 255) / 256) * ((N + 127) / 128) >= 200) choice = 1;
+        else choice = 2;
     }
-    if (wreg_ok && choice == 1) {
-        if constexpr (DT == QMM_Q6_K || DT == QMM_Q8_0) return launch_wreg<DT, 32, 128, 2, 4>(blob, M, K, N, X, Y, st);
-        else return launch_wreg<DT, 64, 128, 4, 4>(blob, M, K, N, X, Y, st);
-    }
-    if (wreg_ok && choice == 2) {
-        if constexpr (DT == QMM_Q6_K) return launch_wreg<DT, 32, 128, 2, 8>(blob, M, K, N, X, Y, st);
-        else return launch_wreg<DT, 32, 128, 3, 8>(blob, M, K, N, X, Y, st);
+    switch (choice) {
+    case 1: return launch_wb<DT, 32, 128, 2, 8, 4, 2>(blob, M, K, N, X, Y, st);
+    case 2: return launch_wb<DT, 32, 64, 4, 4, 0, 4>(blob, M, K, N, X, Y, st);
+    case 3: return launch_wb<DT, 32, 32, 4, 4, 0, 4>(blob, M, K, N, X, Y, st);
+    default: break;
     }
     if (N <= 32) return launch_tile<DT, 128, 32, 1, 4>(blob, M, K, N, X, Y, st, gen);
     if (N <= 64) return launch_tile<DT, 128, 64, 1, 4>(blob, M, K, N, X, Y, st, gen);

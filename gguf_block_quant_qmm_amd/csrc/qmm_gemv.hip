@@ -28,37 +28,6 @@ namespace qmm {
 
 __device__ __forceinline__ float fma_h(_Float16 h, float x, float acc) { return fmaf((float)h, x, acc); }
 
-// Weight bytes are read with bounds-checked buffer loads: the resource covers
-// one row group, any dword at or past its byte count reads as 0 without a
-// memory access, so out-of-range rows and row groups need no branch.
-typedef __amdgpu_buffer_rsrc_t Rsrc;
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x3_t __attribute__((ext_vector_type(3)));
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ Rsrc make_rsrc(const void *base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-// N dwords at byte offset voff (per lane) + soff (uniform)
-template <int N>
-__device__ __forceinline__ void ldb(Rsrc rs, uint32_t voff, uint32_t soff, uint32_t (&v)[N]) {
-    int i = 0;
-#pragma unroll
-    for (; i + 4 <= N; i += 4) {
-        const u32x4_t q = __builtin_amdgcn_raw_buffer_load_b128(rs, voff + 4 * i, soff, 0);
-        v[i] = q.x; v[i + 1] = q.y; v[i + 2] = q.z; v[i + 3] = q.w;
-    }
-    if constexpr (N % 4 == 3) {
-        const u32x3_t q = __builtin_amdgcn_raw_buffer_load_b96(rs, voff + 4 * i, soff, 0);
-        v[i] = q.x; v[i + 1] = q.y; v[i + 2] = q.z;
-    } else if constexpr (N % 4 == 2) {
-        const u32x2_t q = __builtin_amdgcn_raw_buffer_load_b64(rs, voff + 4 * i, soff, 0);
-        v[i] = q.x; v[i + 1] = q.y;
-    } else if constexpr (N % 4 == 1) {
-        v[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, voff + 4 * i, soff, 0);
-    }
-}
 
 // ----------------------------------------------------------------- units ----
 // A unit is 64 weights of one row.  Q8_0/Q4_0: a pair of consecutive blocks
