@@ -694,6 +694,154 @@ __global__ void __launch_bounds__(64 * W) gemm_wb_kernel(const uint8_t *__restri
     }
 }
 
+// ============================================= skinny split-K GEMM ====
+// Small N (verify batches, N <= 64) and small grids: a workgroup owns 32
+// weight rows and BN tokens, and its W wavefronts split K into contiguous
+// ranges of whole super-blocks.  Each wavefront stages its own activations
+// in a private double-buffered LDS region (LDS operations of one wavefront
+// complete in order), so the k-loop has no barrier at all; the W partial
+// 32 x BN tiles are summed once at the end through LDS, in wavefront order
+// (deterministic).  Weights and activations use the same bounds-checked
+// buffer loads, decoders and permuted-k layout as the kernel above.
+template <int DT, int BN, int W, int WD, int XD>
+__global__ void __launch_bounds__(64 * W) gemm_sk_kernel(const uint8_t *__restrict__ blob, int64_t M, int64_t K,
+                                                        int64_t N, int64_t row_bytes, const float *__restrict__ X,
+                                                        float *__restrict__ Y, int n_ntiles) {
+    constexpr int FN = BN / 32;
+    constexpr int NX4 = BN * (BK / 4);  // float4 of X per k-tile
+    constexpr int NXF = NX4 / 64;       // per lane
+    constexpr int UNR = 4;
+    static_assert(UNR % WD == 0 && UNR % XD == 0 && NX4 % 64 == 0, "ring sizes");
+    using BD = typename WbDec<DT>::type;
+    extern __shared__ __attribute__((aligned(16))) _Float16 sk_lds[];
+
+    const int t = threadIdx.x, lane = t & 63, kh = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int64_t mt = blockIdx.x / n_ntiles, nt = blockIdx.x % n_ntiles;
+    const int64_t m0 = mt * 32, n0 = nt * BN;
+    const int64_t per = (K / BK) / W, kt0 = wave * per;  // per is a multiple of 4
+    _Float16 *xw = sk_lds + wave * (2 * BN * LDK);
+
+    const int64_t wrows = M - m0 < 32 ? M - m0 : 32;
+    const Rsrc wrs = make_rsrc_uniform(blob + m0 * row_bytes, (uint32_t)(wrows * row_bytes));
+    const uint32_t roff = (uint32_t)((lane & 31) * row_bytes);
+    const int64_t xrows = N - n0 < BN ? N - n0 : BN;
+    const Rsrc xrs = make_rsrc_uniform(X + n0 * K, (uint32_t)(xrows * K * 4));
+    uint32_t xoff[NXF];
+#pragma unroll
+    for (int i = 0; i < NXF; i++) {
+        const int f = lane + 64 * i, r = f >> 4, c4 = f & 15;
+        xoff[i] = (uint32_t)((r * K + 4 * c4) * 4);
+    }
+
+    uint32_t wr[WD][BD::NW];
+    floatx4 xr[XD][NXF];
+    half8 bf[2][4];
+    typename BD::State st;
+    const int64_t kend = kt0 + per;
+    // c = kt % 4 (a compile-time constant at every call); tiles past the
+    // range repeat its last super-block (never used)
+    auto wload = [&](int64_t kt, int c, uint32_t (&w)[BD::NW]) {
+        const int64_t kc = kt < kend ? kt : kend - 4 + c;
+        BD::loadb(wrs, roff, kc * BK, kh, c, w);
+    };
+    auto xload = [&](int64_t kt, floatx4 (&x)[NXF]) {
+        const uint32_t kb = (uint32_t)((kt < kend ? kt : kend - 1) * BK * 4);
+#pragma unroll
+        for (int i = 0; i < NXF; i++)
+            x[i] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(xrs, xoff[i], kb, 0));
+    };
+    auto xstore = [&](const floatx4 (&x)[NXF], _Float16 *xs) {
+#pragma unroll
+        for (int i = 0; i < NXF; i++) {
+            const int f = lane + 64 * i, r = f >> 4, c4 = f & 15;
+            half4 hv;
+            if constexpr (BD::SWAP)
+                hv = half4{(_Float16)x[i].x, (_Float16)x[i].z, (_Float16)x[i].y, (_Float16)x[i].w};
+            else
+                hv = half4{(_Float16)x[i].x, (_Float16)x[i].y, (_Float16)x[i].z, (_Float16)x[i].w};
+            *reinterpret_cast<half4 *>(xs + r * LDK + BD::xpos(c4)) = hv;
+        }
+    };
+
+    floatx16 acc[FN];
+#pragma unroll
+    for (int i = 0; i < FN; i++)
+#pragma unroll
+        for (int v = 0; v < 16; v++) acc[i][v] = 0.f;
+
+#pragma unroll
+    for (int d = 0; d < WD; d++) wload(kt0 + d, d % 4, wr[d]);
+#pragma unroll
+    for (int d = 0; d < XD; d++) xload(kt0 + d, xr[d]);
+    BD::decode(wr[0], st, kh, 0, kt0 * BK, bf[0]);
+    xstore(xr[0], xw);
+    wload(kt0 + WD, WD % 4, wr[0]);
+    xload(kt0 + XD, xr[0]);
+
+    for (int64_t kb = kt0; kb < kend; kb += UNR) {
+#pragma unroll
+        for (int u = 0; u < UNR; u++) {
+            const int64_t kt = kb + u;
+            const _Float16 *xs = xw + (u & 1) * (BN * LDK);
+            half8 a[BK / 16][FN];
+#pragma unroll
+            for (int s = 0; s < BK / 16; s++)
+#pragma unroll
+                for (int i = 0; i < FN; i++)
+                    a[s][i] = *reinterpret_cast<const half8 *>(xs + (32 * i + (lane & 31)) * LDK + 16 * s + 8 * kh);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int s = 0; s < BK / 16; s++) {
+#pragma unroll
+                for (int i = 0; i < FN; i++)
+                    acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[s][i], bf[u & 1][s], acc[i], 0, 0, 0);
+                if (s == 0) BD::decode(wr[(u + 1) % WD], st, kh, (u + 1) % 4, (kt + 1) * BK, bf[(u + 1) & 1]);
+                if (s == 1) wload(kt + 1 + WD, (u + 1 + WD) % 4, wr[(u + 1) % WD]);
+                if (s == 2) xstore(xr[(u + 1) % XD], xw + ((u + 1) & 1) * (BN * LDK));
+                if (s == 3) xload(kt + 1 + XD, xr[(u + 1) % XD]);
+            }
+        }
+    }
+
+    // sum the W partial tiles in wavefront order
+    __syncthreads();
+    float *red = reinterpret_cast<float *>(sk_lds);  // [W][FN * 16][64]
+#pragma unroll
+    for (int i = 0; i < FN; i++)
+#pragma unroll
+        for (int v = 0; v < 16; v++) red[(wave * FN * 16 + i * 16 + v) * 64 + lane] = acc[i][v];
+    __syncthreads();
+    for (int o = t; o < FN * 16 * 64; o += 64 * W) {
+        float sum = red[o];
+        for (int w = 1; w < W; w++) sum += red[w * FN * 16 * 64 + o];
+        const int L = o & 63, v = (o >> 6) & 15, i = o >> 10;
+        const int64_t m = m0 + (L & 31), n = n0 + 32 * i + 8 * (v >> 2) + 4 * (L >> 5) + (v & 3);
+        if (m < M && n < N) Y[n * M + m] = sum;
+    }
+}
+
+template <int DT, int BN, int W, int WD, int XD>
+static hipError_t launch_sk(const uint8_t *blob, int64_t M, int64_t K, int64_t N, const float *X, float *Y,
+                            hipStream_t st) {
+    constexpr int BS = Geo<DT>::BS, BB = Geo<DT>::BB;
+    const int64_t row_bytes = (K / BS) * BB;
+    const int64_t mtiles = (M + 31) / 32, ntiles = (N + BN - 1) / BN;
+    const int64_t grid = mtiles * ntiles;
+    if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    constexpr size_t xs_bytes = (size_t)W * 2 * BN * LDK * 2, red_bytes = (size_t)W * (BN / 32) * 16 * 64 * 4;
+    constexpr size_t lds = xs_bytes > red_bytes ? xs_bytes : red_bytes;
+    if (lds > 64 * 1024) {
+        static const hipError_t attr = hipFuncSetAttribute(
+            reinterpret_cast<const void *>(&gemm_sk_kernel<DT, BN, W, WD, XD>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (attr != hipSuccess) return attr;
+    }
+    hipLaunchKernelGGL((gemm_sk_kernel<DT, BN, W, WD, XD>), dim3((unsigned)grid), dim3(64 * W), lds, st, blob, M, K,
+                       N, row_bytes, X, Y, (int)ntiles);
+    return hipGetLastError();
+}
+
 // ------------------------------------------------------------ launcher ----
 
 static bool aligned_layout(int dtype, int64_t nb) {
@@ -737,13 +885,16 @@ static hipError_t launch_wb(const uint8_t *blob, int64_t M, int64_t K, int64_t N
     return hipGetLastError();
 }
 
-// Kernel choice (measured): the buffered register-B kernel whenever the
-// layout allows it -- 8 wavefronts x 32 rows x 128 tokens when that grid
-// nearly fills the chip, else 4 x 32 rows x 64 tokens (x 32 tokens for N <=
-// 32) with deeper prefetch -- and the LDS-staged kernel otherwise (K not a
-// multiple of 256, odd block counts).  QMM_GEMM_KERNEL = 0 / 1 / 2 / 3 forces
-// LDS-staged / 8x32x128 / 4x32x64 / 4x32x32 where the layout allows (a
-// measurement lever, read once).
+// Kernel choice (measured on 4096 x 4096 and 14336 x 4096 weights):
+//   * the skinny split-K kernel (32 rows x 32 tokens, 4 wavefronts splitting
+//     K) when N <= 32 or the 32 x 32 tile grid is small -- small N leaves too
+//     few row x token tiles to fill the chip otherwise;
+//   * the buffered kernel with 8 wavefronts x 32 rows x 128 tokens when that
+//     grid nearly fills the chip, else 4 x 32 rows x 64 tokens;
+//   * the LDS-staged kernel when the layout rules the others out (K not a
+//     multiple of 256, odd block counts).
+// QMM_GEMM_KERNEL = 0 / 1 / 2 / 3 / 4 forces LDS-staged / 8x32x128 / 4x32x64 /
+// 4x32x32 / skinny where the layout allows (a measurement lever, read once).
 static int gemm_kernel_choice() {
     static int v = [] {
         const char *e = getenv("QMM_GEMM_KERNEL");
@@ -758,9 +909,12 @@ static hipError_t launch_dt(const uint8_t *blob, int64_t M, int64_t K, int64_t N
     const bool gen = !aligned_layout(DT, K / Geo<DT>::BS);
     // buffer resources cover at most 128 token rows of X: 32-bit byte counts
     const bool wb_ok = !gen && (K % (4 * BK)) == 0 && K * 4 * 128 < ((int64_t)1 << 31);
+    const bool sk_ok = wb_ok && (K / BK) % 16 == 0;  // 4 wavefronts x whole super-blocks
     int choice = gemm_kernel_choice();
+    if (choice == 4 && !sk_ok) choice = -1;
     if (choice < 0 || (choice > 0 && !wb_ok)) {
         if (!wb_ok) choice = 0;
+        else if (sk_ok && (N <= 32 || ((M + 31) / 32) * ((N + 31) / 32) <= 512)) choice = 4;
         else if (N <= 32) choice = 3;
         else if (((M + 255) / 256) * ((N + 127) / 128) >= 200) choice = 1;
         else choice = 2;
@@ -769,6 +923,7 @@ static hipError_t launch_dt(const uint8_t *blob, int64_t M, int64_t K, int64_t N
     case 1: return launch_wb<DT, 32, 128, 2, 8, 4, 2>(blob, M, K, N, X, Y, st);
     case 2: return launch_wb<DT, 32, 64, 4, 4, 0, 4>(blob, M, K, N, X, Y, st);
     case 3: return launch_wb<DT, 32, 32, 4, 4, 0, 4>(blob, M, K, N, X, Y, st);
+    case 4: return launch_sk<DT, 32, 4, 2, 2>(blob, M, K, N, X, Y, st);
     default: break;
     }
     if (N <= 32) return launch_tile<DT, 128, 32, 1, 4>(blob, M, K, N, X, Y, st, gen);

@@ -89,10 +89,12 @@ int qmm_gemv(const void *w_blob, int dtype, int64_t M, int64_t K,
  * token columns):  Y[n][m] = sum_k W[m][k] * X[n][k].
  *   X       device f32 [N][K] row-major, 16-B aligned
  *   Y       device f32 [N][M] row-major, 4-B aligned; overwritten
- * N == 1 runs the GEMV (same bits).  Other N run the path qmm_gemm_path
- * names: 0 = all-f32 arithmetic (tolerance 1e-5 of sum |w x|), 1 = weights
- * and activations rounded to f16 and multiplied on the matrix cores with f32
- * accumulation (tolerance 2e-3 of sum |w x|; needs |w|, |x| < 65504). */
+ * Below a per-dtype crossover N (3 for Q4_0 and Q6_K, 2 for Q8_0 and Q4_K,
+ * measured) it runs the GEMV once per token (same bits as qmm_gemv).  The
+ * path qmm_gemm_path names: 0 = all-f32 arithmetic (tolerance 1e-5 of
+ * sum |w x|), 1 = weights and activations rounded to f16 and multiplied on
+ * the matrix cores with f32 accumulation (tolerance 2e-3 of sum |w x|; needs
+ * |w|, |x| < 65504). */
 int qmm_gemm(const void *w_blob, int dtype, int64_t M, int64_t K, int64_t N,
              const float *X, float *Y, void *stream);
 

@@ -88,8 +88,13 @@ def test_gemm_rejects(args, code):
 
 
 def test_gemm_path_selection():
-    # N == 1 is the f32 GEMV; the matrix-core path reports itself for N >= 2
+    # below the per-dtype crossover the f32 GEMV runs per token
     assert q.gemm_path(q.QMM_Q4_K, 14336, 4096, 1) == 0
+    assert q.gemm_path(q.QMM_Q4_K, 14336, 4096, 2) == 1
+    assert q.gemm_path(q.QMM_Q8_0, 4096, 4096, 2) == 1
+    assert q.gemm_path(q.QMM_Q4_0, 4096, 4096, 2) == 0
+    assert q.gemm_path(q.QMM_Q6_K, 4096, 4096, 2) == 0
+    assert q.gemm_path(q.QMM_Q6_K, 4096, 4096, 3) == 1
     assert q.gemm_path(q.QMM_Q4_K, 14336, 4096, 512) == 1
     assert q.gemm_path(q.QMM_Q4_K, 14336, 100, 512) == q.QMM_ERR_SHAPE
     assert q.tolerance(q.QMM_Q4_0, 4096, 4096, 1) == 1e-5

@@ -149,6 +149,12 @@ def test_gemm_n1_is_gemv_bitwise_and_deterministic(dt):
         assert np.array_equal(a.view(np.uint32), c.view(np.uint32)), "gemv not deterministic"
         X = make_x(40, K, rng_for(700 + dt, 20 + i))
         assert np.array_equal(gpu_gemm(dt, blob_d, M, K, X), gpu_gemm(dt, blob_d, M, K, X)), "gemm not deterministic"
+        # below the crossover qmm_gemm runs the GEMV per token: its bits
+        X2 = make_x(2, K, rng_for(700 + dt, 30 + i))
+        if q.gemm_path(dt, M, K, 2) == 0:
+            G = gpu_gemm(dt, blob_d, M, K, X2)
+            for n in range(2):
+                assert np.array_equal(G[n].view(np.uint32), gpu_gemv(dt, blob_d, M, K, X2[n]).view(np.uint32))
 
 
 @pytest.mark.parametrize("dt", DTYPES, ids=NAME.get)
