@@ -334,16 +334,37 @@ __global__ void __launch_bounds__(256) gemm_kernel(const uint8_t *__restrict__ b
 
 constexpr float TWO24 = 16777216.0f;
 
-__device__ __forceinline__ _Float16 mixw(_Float16 code, float scale, float bias) {
-    return (_Float16)fmaf((float)code, scale, bias);
+// Two weights (scale * code + bias, each rounded once to f16) from the two
+// f16 code lanes of a dword.  ASM: as one v_fma_mixlo_f16 / v_fma_mixhi_f16
+// pair (2 instructions); else as the compiler forms it (usually two f32
+// fma_mix and a pack).  Which is faster depends on the format (measured:
+// the pair for Q4_0, the compiler's form for Q4_K).
+template <bool ASM>
+__device__ __forceinline__ uint32_t mix_pair(uint32_t codes, float scale, float bias) {
+    if constexpr (ASM) {
+        uint32_t r;
+        asm("v_fma_mixlo_f16 %0, %1, %2, %3 op_sel_hi:[1,0,0]\n\t"
+            "v_fma_mixhi_f16 %0, %1, %2, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+            : "=&v"(r)
+            : "v"(codes), "v"(scale), "v"(bias));
+        return r;
+    } else {
+        const half2_t c = __builtin_bit_cast(half2_t, codes);
+        half2_t o;
+        o.x = (_Float16)fmaf((float)c.x, scale, bias);
+        o.y = (_Float16)fmaf((float)c.y, scale, bias);
+        return __builtin_bit_cast(uint32_t, o);
+    }
 }
-// four weights from the two code pairs of a dword
+// four weights from the two code pairs of a dword, into f[at .. at+4)
+template <bool ASM = true>
 __device__ __forceinline__ void quad(uint32_t p02, uint32_t p13, float scale, float bias, half8 &f, int at) {
-    const half2_t a = __builtin_bit_cast(half2_t, p02), b = __builtin_bit_cast(half2_t, p13);
-    f[at] = mixw(a.x, scale, bias);
-    f[at + 1] = mixw(a.y, scale, bias);
-    f[at + 2] = mixw(b.x, scale, bias);
-    f[at + 3] = mixw(b.y, scale, bias);
+    const half2_t a = __builtin_bit_cast(half2_t, mix_pair<ASM>(p02, scale, bias));
+    const half2_t b = __builtin_bit_cast(half2_t, mix_pair<ASM>(p13, scale, bias));
+    f[at] = a.x;
+    f[at + 1] = a.y;
+    f[at + 2] = b.x;
+    f[at + 3] = b.y;
 }
 
 // BDec<DT>: raw bytes of one row's 64-deep k-tile that lane half kh needs
@@ -487,8 +508,8 @@ template <> struct PDec<QMM_Q4_K> {
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             const uint32_t w = r[4 + i], t = w >> 8;
-            quad(w & 0x000F000Fu, t & 0x000F000Fu, s0, n0, f[i >> 1], 4 * (i & 1));
-            quad(w & 0x00F000F0u, t & 0x00F000F0u, s1, n1, f[2 + (i >> 1)], 4 * (i & 1));
+            quad<false>(w & 0x000F000Fu, t & 0x000F000Fu, s0, n0, f[i >> 1], 4 * (i & 1));
+            quad<false>(w & 0x00F000F0u, t & 0x00F000F0u, s1, n1, f[2 + (i >> 1)], 4 * (i & 1));
         }
     }
 };
@@ -912,7 +933,7 @@ static hipError_t launch_dt(const uint8_t *blob, int64_t M, int64_t K, int64_t N
     const bool sk_ok = wb_ok && (K / BK) % 16 == 0;  // 4 wavefronts x whole super-blocks
     int choice = gemm_kernel_choice();
     if (choice == 4 && !sk_ok) choice = -1;
-    if (choice < 0 || (choice > 0 && !wb_ok)) {
+    if (choice < 0 || choice > 4 || (choice > 0 && !wb_ok)) {
         if (!wb_ok) choice = 0;
         else if (sk_ok && (N <= 32 || ((M + 31) / 32) * ((N + 31) / 32) <= 512)) choice = 4;
         else if (N <= 32) choice = 3;
