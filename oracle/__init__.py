@@ -52,6 +52,9 @@ def _bind(lib):
     lib.oracle_dequant.argtypes = [ctypes.c_int, vp, i64, i64, vp]
     lib.oracle_matmul_rows.argtypes = [ctypes.c_int, vp, i64, i64, i64, vp, i64, vp, vp, vp, vp]
     lib.oracle_matmul.argtypes = [ctypes.c_int, vp, i64, i64, i64, vp, vp, vp, vp]
+    lib.oracle_silu.argtypes = [ctypes.c_double]
+    lib.oracle_silu.restype = ctypes.c_double
+    lib.oracle_swiglu_rows.argtypes = [ctypes.c_int, vp, vp, i64, i64, i64, vp, i64, vp, vp, vp, vp, vp, vp, vp]
     return lib
 
 
@@ -132,6 +135,42 @@ def matmul(dtype: int, blob: np.ndarray, M: int, K: int, X: np.ndarray, rows=Non
                                          _ptr(Y), _ptr(Y64), _ptr(S))
     _check(rc, "matmul")
     return Y, Y64, S
+
+
+def silu(v: float, L=None) -> float:
+    """v / (1 + e^-v) in f64 (oracle.c, oracle_silu)."""
+    return (L or lib()).oracle_silu(float(v))
+
+
+def swiglu(dtype: int, gate: np.ndarray, up: np.ndarray, M: int, K: int, X: np.ndarray, rows=None, L=None):
+    """The gate/up projection with SwiGLU: out = silu(W_gate x) * (W_up x).
+
+    Returns a dict of [N][R] arrays: ``out`` (f32), ``out64`` (f64), ``g`` and
+    ``u`` (the f64 projections) and ``sg``, ``su`` (their sums of |w x|).
+    """
+    gate = np.ascontiguousarray(gate, dtype=np.uint8)
+    up = np.ascontiguousarray(up, dtype=np.uint8)
+    X = np.ascontiguousarray(X, dtype=np.float32)
+    if X.ndim == 1:
+        X = X[None, :]
+    N = X.shape[0]
+    if X.shape[1] != K:
+        raise ValueError("X has the wrong K")
+    nb = blob_bytes(dtype, M, K, L)
+    if gate.size < nb or up.size < nb:
+        raise ValueError("blob too small")
+    if rows is None:
+        nrows, rows_p = M, None
+    else:
+        rows_arr = np.ascontiguousarray(rows, dtype=np.int64)
+        nrows, rows_p = rows_arr.size, _ptr(rows_arr)
+    r = {"out": np.empty((N, nrows), np.float32)}
+    for k in ("out64", "g", "u", "sg", "su"):
+        r[k] = np.empty((N, nrows), np.float64)
+    rc = (L or lib()).oracle_swiglu_rows(dtype, _ptr(gate), _ptr(up), M, K, N, _ptr(X), nrows, rows_p,
+                                         *(_ptr(r[k]) for k in ("out", "out64", "g", "u", "sg", "su")))
+    _check(rc, "swiglu")
+    return r
 
 
 def num_threads() -> int:

@@ -13,6 +13,11 @@
  *             then rounded once to f32 (round-to-nearest-even)
  *   S[n,m]  = sum_k |W[m,k] * X[n,k]| in f64               (tolerance scale)
  *
+ * and, for the gate/up projection with SwiGLU (two matrices of one shape),
+ *
+ *   out[n,m] = silu(G[n,m]) * U[n,m],  silu(v) = v / (1 + e^-v)  in f64,
+ *   G, U the f64 sums above for the gate and the up matrix.
+ *
  * Source of the definition: page "cera 0.5.2 src/backend/cpu.rs", section
  * "Matrix multiplication" -- the scalar reference matmuls matmul_f32,
  * matmul_q4_0_f32, matmul_q8_0_f32 and matmul_q4km_f32 define
@@ -52,7 +57,9 @@
  *          q   = lo4 | hi2<<4;       w = d*sc[j/16]*(q-32)
  *
  * Parity pins: hand-built blocks, the all-ones closed form, unit vectors and
- * exact rational brute force (tests/test_oracle_pins.py).  The Q4_K scale
+ * exact rational brute force (tests/test_oracle_pins.py); SiLU at closed-form
+ * points (sigmoid(ln 3) = 3/4, the minimum -W(1/e)) and SwiGLU on fixture
+ * blocks with unit vectors.  The Q4_K scale
  * packing and the Q6_K bit layout are a reading of the GGUF convention that
  * no page value can confirm: for those two, "parity unpinned" against the
  * pages; they are pinned only against the hand-built fixtures written from
@@ -275,4 +282,50 @@ int oracle_num_threads(void) {
 #else
     return 1;
 #endif
+}
+
+/* ---- fused gate/up projection with SwiGLU ------------------------------ */
+
+/* SiLU (page "cera 0.5.2 src/backend/cpu.rs", activation functions: the
+ * input times its logistic sigmoid), evaluated as v / (1 + e^-v) in f64.
+ * Below v ~ -709, e^-v overflows to +Inf and the quotient is -0, the
+ * function's limit. */
+double oracle_silu(double v) { return v / (1.0 + exp(-v)); }
+
+/* The gate/up projection with SwiGLU (same page, the fused gate + up GEMV
+ * with in-register SwiGLU, and silu_mul_inplace: gate = silu(gate) * up):
+ *     out[n][r] = silu(g) * u,   g = sum_k Wg[m,k] X[n,k],  u = sum_k Wu[m,k] X[n,k]
+ * for m = rows[r] (all rows when rows == NULL), g and u the f64 sums of
+ * oracle_matmul_rows.  out is the f32 rounding of the f64 product out64.
+ * G, U, SG, SU receive g, u and their sums of |w x| (for the tolerance);
+ * every output pointer but out may be NULL. */
+int oracle_swiglu_rows(int dtype, const uint8_t *gate, const uint8_t *up, int64_t M, int64_t K, int64_t N,
+                       const float *X, int64_t nrows, const int64_t *rows, float *out, double *out64,
+                       double *G, double *U, double *SG, double *SU) {
+    int rc = check_shape(dtype, M, K);
+    if (rc) return rc;
+    if (N < 1 || nrows < 1) return -3;
+    size_t cnt = (size_t)N * (size_t)nrows;
+    float *tmp = (float *)malloc(sizeof(float) * cnt);
+    double *g = (double *)malloc(sizeof(double) * cnt), *u = (double *)malloc(sizeof(double) * cnt);
+    double *sg = (double *)malloc(sizeof(double) * cnt), *su = (double *)malloc(sizeof(double) * cnt);
+    if (!tmp || !g || !u || !sg || !su) {
+        rc = -7;
+    } else {
+        rc = oracle_matmul_rows(dtype, gate, M, K, N, X, nrows, rows, tmp, g, sg);
+        if (!rc) rc = oracle_matmul_rows(dtype, up, M, K, N, X, nrows, rows, tmp, u, su);
+    }
+    if (!rc) {
+        for (size_t i = 0; i < cnt; i++) {
+            double o = oracle_silu(g[i]) * u[i];
+            out[i] = (float)o;
+            if (out64) out64[i] = o;
+            if (G) G[i] = g[i];
+            if (U) U[i] = u[i];
+            if (SG) SG[i] = sg[i];
+            if (SU) SU[i] = su[i];
+        }
+    }
+    free(tmp); free(g); free(u); free(sg); free(su);
+    return rc;
 }

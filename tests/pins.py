@@ -14,9 +14,14 @@ run against deliberately broken builds of the oracle (test_oracle_mutants).
                       permutation, power-of-two scaling of x, additivity
   pin_half            f16 decoding against Python's own binary16 unpacking
   pin_sizes           block sizes and the page's ~205 MiB Q6_K head
+  pin_silu            SiLU at closed-form points (sigmoid(ln 3) = 3/4, the
+                      minimum -W(1/e)), the odd-part identity and its limits
+  pin_swiglu          gate/up SwiGLU on fixture blocks with unit vectors:
+                      g and u are the fixtures' design values, out = silu(g) u
 """
 from __future__ import annotations
 
+import math
 import os
 import struct
 from fractions import Fraction
@@ -347,5 +352,68 @@ def pin_sizes(L=None):
     assert head == 215_470_080 and round(head / 2**20) == 205
 
 
+# ------------------------------------------------------------------- SwiGLU
+
+def pin_silu(L=None):
+    ln3 = math.log(3.0)
+    assert oracle.silu(0.0, L) == 0.0, "silu(0) must be 0"
+    # sigmoid(ln 3) = 1 / (1 + 1/3) = 3/4 and sigmoid(-ln 3) = 1/4
+    assert abs(oracle.silu(ln3, L) - 0.75 * ln3) <= 4e-16 * ln3, "silu(ln 3) != 3/4 ln 3"
+    assert abs(oracle.silu(-ln3, L) + 0.25 * ln3) <= 4e-16 * ln3, "silu(-ln 3) != -1/4 ln 3"
+    # the minimum: at v* = -1 - W(1/e) the value is -W(1/e), W = Lambert's W
+    w = 0.5
+    for _ in range(60):                       # Newton on w e^w = 1/e
+        w -= (w * math.exp(w) - math.exp(-1.0)) / (math.exp(w) * (1.0 + w))
+    assert abs(w - 0.2784645427610738) < 1e-15
+    assert abs(oracle.silu(-1.0 - w, L) + w) <= 1e-15, "silu minimum is not -W(1/e)"
+    # sigmoid(v) + sigmoid(-v) = 1, so silu(v) - silu(-v) = v
+    for v in (1e-3, 0.5, 1.0, 2.5, 10.0, 30.0):
+        assert abs(oracle.silu(v, L) - oracle.silu(-v, L) - v) <= 2e-16 * v, f"odd-part identity fails at {v}"
+    # limits: e^-v overflow gives -0, large v gives v
+    lo = oracle.silu(-1000.0, L)
+    assert lo == 0.0 and math.copysign(1.0, lo) < 0, "silu(-1000) should be -0"
+    assert oracle.silu(1000.0, L) == 1000.0 and oracle.silu(40.0, L) == 40.0
+
+
+def pin_swiglu(L=None):
+    """Gate and up blobs from the fixture blocks (up rotated against gate);
+    x = e_k picks column k, so g and u are design values."""
+    for dt in DTYPES:
+        recs = load_golden(oracle.NAMES[dt])
+        bs = oracle.block_elems(dt, L)
+        nblk = 2 if bs == 256 else 4
+        K, M = nblk * bs, 3
+
+        def make(shift):
+            rb, rw = [], []
+            for m in range(M):
+                pick = [recs[(m + b + shift) % len(recs)] for b in range(nblk)]
+                rb.append(b"".join(p[1] for p in pick))
+                rw.append(np.concatenate([p[2] for p in pick]))
+            return np.frombuffer(b"".join(rb), np.uint8), np.stack(rw)
+
+        gate, Wg = make(0)
+        up, Wu = make(1)
+        ks = list(range(0, K, 7)) + [K - 1]
+        X = np.eye(K, dtype=np.float32)[ks] * np.float32(8.0)
+        r = oracle.swiglu(dt, gate, up, M, K, X, L=L)
+        name = oracle.NAMES[dt]
+        assert np.array_equal(r["g"], 8.0 * Wg[:, ks].T), f"{name}: g is not the gate projection"
+        assert np.array_equal(r["u"], 8.0 * Wu[:, ks].T), f"{name}: u is not the up projection"
+        assert np.array_equal(r["sg"], np.abs(r["g"])) and np.array_equal(r["su"], np.abs(r["u"]))
+        for n in range(len(ks)):
+            for m in range(M):
+                g, u = 8.0 * Wg[m, ks[n]], 8.0 * Wu[m, ks[n]]
+                want = oracle.silu(g, L) * u
+                assert r["out64"][n, m] == want, f"{name}: out[{n},{m}] != silu(g) u"
+                assert r["out"][n, m] == np.float32(want)
+        # the order of the operands matters wherever g != u
+        swapped = np.array([[oracle.silu(8.0 * Wu[m, k], L) * 8.0 * Wg[m, k] for m in range(M)] for k in ks])
+        assert not np.array_equal(swapped, r["out64"]), f"{name}: fixtures cannot tell gate from up"
+        # a row subset gives the same numbers
+        rs = oracle.swiglu(dt, gate, up, M, K, X, rows=[2, 0], L=L)
+        assert np.array_equal(rs["out64"], r["out64"][:, [2, 0]])
+
+
 ALL_PINS = [pin_golden, pin_unit_vectors, pin_closed_form, pin_bruteforce, pin_invariants,
-            pin_half, pin_sizes]
+            pin_half, pin_sizes, pin_silu, pin_swiglu]

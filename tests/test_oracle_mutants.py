@@ -38,6 +38,11 @@ MUTANTS = {
     "transposed_x": ("const float *x = X + n * K;", "const float *x = X + n;"),
     "dropped_term": ("for (int64_t k = 0; k < K; k++) {", "for (int64_t k = 1; k < K; k++) {"),
     "magnitude_signed": ("mag += fabs(p);", "mag += p;"),
+    "silu_sign": ("return v / (1.0 + exp(-v));", "return v / (1.0 + exp(v));"),
+    "silu_no_factor": ("return v / (1.0 + exp(-v));", "return 1.0 / (1.0 + exp(-v));"),
+    "swiglu_swapped": ("double o = oracle_silu(g[i]) * u[i];", "double o = oracle_silu(u[i]) * g[i];"),
+    "swiglu_gate_twice": ("rc = oracle_matmul_rows(dtype, up, M, K, N, X, nrows, rows, tmp, u, su);",
+                          "rc = oracle_matmul_rows(dtype, gate, M, K, N, X, nrows, rows, tmp, u, su);"),
     "f32_rounding": ("Y[n * nrows + r] = (float)acc;", "Y[n * nrows + r] = (float)(acc * (1.0 + 0x1p-23));"),
 }
 
