@@ -5,9 +5,14 @@ Metric: decode GEMV weight GB/s (share of HBM peak) + prefill GEMM TFLOP/s at
 N = 512.
 
 One step = the decode GEMVs of one LLaMA-8B layer in Q4_0 (q_proj 4096x4096,
-gate 14336x4096, up 14336x4096, down 4096x14336; x f32 ~ N(0,1)), each called
-through qmm_gemm with N = 1 (path selection -> the f32 GEMV).  `value` is the
-step's weight bytes over its measured GPU time.  Weight copies are rotated so
+gate 14336x4096, up 14336x4096, down 4096x14336; x f32 ~ N(0,1)) in three
+launches: q_proj and down through qmm_gemv, gate and up together through
+qmm_gemv_concat (one launch, one read of x; each output has the bits of a
+separate qmm_gemv call).  `value` is the step's weight bytes over its measured
+GPU time.  The same layer as four separate launches (each through qmm_gemm
+with N = 1, i.e. path selection -> the f32 GEMV) is reported as
+"decode_unfused", and with gate/up through qmm_gemv_swiglu as
+"decode_swiglu".  Weight copies are rotated so
 that more than 1 GiB of distinct weights is cycled (more than the 256 MB
 last-level cache): every step streams its weights from HBM.  Inputs are
 resident in HBM before timing starts.
@@ -73,6 +78,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle time budget per leg")
     ap.add_argument("--sweep", action="store_true", help="per-config table instead of the main line")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="time only the headline decode step and the prefill GEMM (profiler runs: every GEMV "
+                         "launch then belongs to the headline step)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -109,40 +117,81 @@ def main():
     ys = [torch.empty((1, m[2]), device=dev) for m in mats]
     stream = torch.cuda.current_stream()
 
-    def decode_step(s):
-        c = s % R
+    gate_up_ys = [torch.empty(mats[1][2], device=dev), torch.empty(mats[2][2], device=dev)]
+    swiglu_y = torch.empty(mats[1][2], device=dev)
+
+    def step_unfused(c):
         for i, (name, dt, M, K, _) in enumerate(mats):
             q.qmm_gemm(copies[i][c], dt, M, K, 1, xs[i], ys[i], stream=stream)
 
-    for s in range(args.warmup):
-        decode_step(s)
-    torch.cuda.synchronize()
-    # events only at step boundaries: the four GEMVs of a step run back to back
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    t0 = time.perf_counter()
-    ev[0].record(stream)
-    for s in range(args.steps):
-        decode_step(args.warmup + s)
-        ev[s + 1].record(stream)
-    torch.cuda.synchronize()
-    wall_dec = time.perf_counter() - t0
-    span_ms = ev[0].elapsed_time(ev[args.steps])
+    def step_fused(c):
+        (_, dq, Mq, Kq, _), (_, dg, Mg, Kg, _), _, (_, dd, Md, Kd, _) = mats
+        q.qmm_gemv(copies[0][c], dq, Mq, Kq, xs[0], ys[0], stream=stream)
+        q.qmm_gemv_concat([copies[1][c], copies[2][c]], dg, [Mg, Mg], Kg, xs[1], gate_up_ys, stream=stream)
+        q.qmm_gemv(copies[3][c], dd, Md, Kd, xs[3], ys[3], stream=stream)
+
+    def step_swiglu(c):
+        (_, dq, Mq, Kq, _), (_, dg, Mg, Kg, _), _, (_, dd, Md, Kd, _) = mats
+        q.qmm_gemv(copies[0][c], dq, Mq, Kq, xs[0], ys[0], stream=stream)
+        q.qmm_gemv_swiglu(copies[1][c], copies[2][c], dg, Mg, Kg, xs[1], swiglu_y, stream=stream)
+        q.qmm_gemv(copies[3][c], dd, Md, Kd, xs[3], ys[3], stream=stream)
+
+    def time_layer(step):
+        """(span ms over args.steps steps, host seconds), events only at step boundaries."""
+        for s in range(args.warmup):
+            step(s % R)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        t0 = time.perf_counter()
+        ev[0].record(stream)
+        for s in range(args.steps):
+            step((args.warmup + s) % R)
+            ev[s + 1].record(stream)
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[args.steps]), time.perf_counter() - t0
+
+    span_ms, wall_dec = time_layer(step_fused)
+    span_unf = span_swi = None
+    if not args.headline_only:
+        span_unf, _ = time_layer(step_unfused)
+        span_swi, _ = time_layer(step_swiglu)
     dec_bytes_total = step_bytes * args.steps
     value = dec_bytes_total / (span_ms * 1e-3) / 1e9
-    avg_launch_us = span_ms * 1e3 / (args.steps * len(mats))
+    launches = 3
+    avg_launch_us = span_ms * 1e3 / (args.steps * launches)
     achieved = value
     traffic = load_traffic("gemv_q4_0_decode_layer")
     # per-matrix time: each shape alone, back to back, between two events
     per_matrix = {}
-    for i, (name, dt, M, K, _) in enumerate(mats):
+
+    def time_calls(fn, nbytes):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
         for s in range(args.steps):
-            q.qmm_gemm(copies[i][s % R], dt, M, K, 1, xs[i], ys[i], stream=stream)
+            fn(s % R)
         b.record(stream)
         torch.cuda.synchronize()
         us = a.elapsed_time(b) * 1e3 / args.steps
-        per_matrix[name] = {"us": round(us, 3), "GB/s": round(copies[i][0].numel() / (us * 1e-6) / 1e9, 1)}
+        return {"us": round(us, 3), "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1)}
+
+    for i, (name, dt, M, K, _) in enumerate(mats if not args.headline_only else []):
+        per_matrix[name] = time_calls(lambda c, i=i, dt=dt, M=M, K=K: q.qmm_gemm(copies[i][c], dt, M, K, 1, xs[i], ys[i],
+                                                                                 stream=stream),
+                                      copies[i][0].numel())
+    gu_bytes = copies[1][0].numel() + copies[2][0].numel()
+    (_, dg, Mg, Kg, _) = mats[1]
+    if not args.headline_only:
+        per_matrix["gate+up concat"] = time_calls(
+            lambda c: q.qmm_gemv_concat([copies[1][c], copies[2][c]], dg, [Mg, Mg], Kg, xs[1], gate_up_ys,
+                                        stream=stream), gu_bytes)
+        per_matrix["gate+up swiglu"] = time_calls(
+            lambda c: q.qmm_gemv_swiglu(copies[1][c], copies[2][c], dg, Mg, Kg, xs[1], swiglu_y, stream=stream),
+            gu_bytes)
+
+    def layer_rate(span):
+        if span is None:
+            return None
+        return {"GB/s": round(dec_bytes_total / (span * 1e-3) / 1e9, 2), "ms_per_step": round(span / args.steps, 5)}
 
     # --------------------------------------------------------------- prefill
     _, pdt, PM, PK, _ = WORKLOADS[6]
@@ -183,11 +232,14 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": "llama8b decode layer, Q4_0 GEMVs q_proj 4096x4096 + gate/up 14336x4096 + down "
-                        "4096x14336, N=1, x f32 ~ N(0,1), seed 0",
+                        "4096x14336, N=1, x f32 ~ N(0,1), seed 0; gate and up in one qmm_gemv_concat launch",
             "weight_bytes_per_step": step_bytes,
             "rotation_copies": R,
             "hbm_frac": round(value / HBM_PEAK_GBS, 4),
             "decode_ms_per_step": round(span_ms / args.steps, 5),
+            "decode_unfused": {"launches": 4, **(layer_rate(span_unf) or {})},
+            "decode_swiglu": {"launches": 3, **(layer_rate(span_swi) or {}),
+                              "note": "gate/up through qmm_gemv_swiglu (outputs silu(g)*u instead of g and u)"},
             "timing": "HIP events on the launch stream at step boundaries; per-launch = span / launches",
             "per_matrix": per_matrix,
             "gpu": props.name,
@@ -195,14 +247,15 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "qmm::gemv_kernel<2,...> (Q4_0), the four decode-layer launches together",
+            "kernel": "qmm::gemv_kernel<2,...> (Q4_0): q_proj, gate+up concatenated, down -- the three "
+                      "decode-layer launches together",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
             "avg_launch_us": round(avg_launch_us, 3),
-            "algorithmic_bytes_per_launch": step_bytes / len(mats),
+            "algorithmic_bytes_per_launch": step_bytes / launches,
         },
         "prefill_gemm": {
             "workload": "Q4_K 14336x4096, N=512 tokens, X f32 ~ N(0,1), f16 matrix cores, f32 accumulate",

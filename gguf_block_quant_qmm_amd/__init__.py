@@ -8,6 +8,10 @@ there is no CPU fallback.
 
     qmm_gemv(w, dtype, M, K, x, y, stream=None)      y[M] = W x
     qmm_gemm(w, dtype, M, K, N, X, Y, stream=None)   Y[N][M] = X W^T
+    qmm_gemv_concat(ws, dtype, Ms, K, x, ys, stream=None)
+                                                     ys[i] = W_i x, one launch
+    qmm_gemv_swiglu(gate, up, dtype, M, K, x, out, stream=None)
+                                                     out = silu(W_gate x) * (W_up x)
 """
 from __future__ import annotations
 
@@ -23,8 +27,10 @@ DTYPES = {"Q4_0": QMM_Q4_0, "Q8_0": QMM_Q8_0, "Q4_K": QMM_Q4_K, "Q6_K": QMM_Q6_K
 QMM_OK, QMM_ERR_NULL, QMM_ERR_DTYPE, QMM_ERR_SHAPE = 0, -1, -2, -3
 QMM_ERR_ALIGN, QMM_ERR_DEVICE, QMM_ERR_LAUNCH = -4, -5, -6
 
-EXPORTS = ("qmm_gemv", "qmm_gemm", "qmm_gemm_path", "qmm_blob_bytes", "qmm_block_elems",
-           "qmm_block_bytes", "qmm_strerror")
+QMM_GEMV_MAX_MATS = 4
+
+EXPORTS = ("qmm_gemv", "qmm_gemv_concat", "qmm_gemv_swiglu", "qmm_gemm", "qmm_gemm_path", "qmm_blob_bytes",
+           "qmm_block_elems", "qmm_block_bytes", "qmm_strerror")
 
 _lib = None
 
@@ -45,6 +51,10 @@ def lib():
         i64, vp, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
         L.qmm_gemv.argtypes = [vp, ci, i64, i64, vp, vp, vp]
         L.qmm_gemv.restype = ci
+        L.qmm_gemv_concat.argtypes = [ci, vp, vp, ci, i64, vp, vp, vp]
+        L.qmm_gemv_concat.restype = ci
+        L.qmm_gemv_swiglu.argtypes = [vp, vp, ci, i64, i64, vp, vp, vp]
+        L.qmm_gemv_swiglu.restype = ci
         L.qmm_gemm.argtypes = [vp, ci, i64, i64, i64, vp, vp, vp]
         L.qmm_gemm.restype = ci
         L.qmm_gemm_path.argtypes = [ci, i64, i64, i64]
@@ -127,3 +137,29 @@ def qmm_gemm(w, dtype: int, M: int, K: int, N: int, X, Y, stream=None) -> None:
                         _stream(stream))
     if rc != QMM_OK:
         raise QmmError(rc, "qmm_gemm")
+
+
+def qmm_gemv_concat(ws, dtype: int, Ms, K: int, x, ys, stream=None) -> None:
+    import torch
+    n = len(ws)
+    if not (len(Ms) == n == len(ys)):
+        raise ValueError("ws, Ms and ys need one entry per matrix")
+    blobs = (ctypes.c_void_p * max(n, 1))(*[_addr(w, blob_bytes(dtype, M, K) or None, f"ws[{i}]")
+                                            for i, (w, M) in enumerate(zip(ws, Ms))])
+    rows = (ctypes.c_int64 * max(n, 1))(*[int(M) for M in Ms])
+    outs = (ctypes.c_void_p * max(n, 1))(*[_addr(y, 4 * M, f"ys[{i}]", torch.float32)
+                                           for i, (y, M) in enumerate(zip(ys, Ms))])
+    rc = lib().qmm_gemv_concat(n, blobs, rows, dtype, K, _addr(x, 4 * K, "x", torch.float32), outs,
+                               _stream(stream))
+    if rc != QMM_OK:
+        raise QmmError(rc, "qmm_gemv_concat")
+
+
+def qmm_gemv_swiglu(gate, up, dtype: int, M: int, K: int, x, out, stream=None) -> None:
+    import torch
+    nb = blob_bytes(dtype, M, K) or None
+    rc = lib().qmm_gemv_swiglu(_addr(gate, nb, "gate"), _addr(up, nb, "up"), dtype, M, K,
+                               _addr(x, 4 * K, "x", torch.float32), _addr(out, 4 * M, "out", torch.float32),
+                               _stream(stream))
+    if rc != QMM_OK:
+        raise QmmError(rc, "qmm_gemv_swiglu")

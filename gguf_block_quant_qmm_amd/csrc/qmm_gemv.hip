@@ -310,14 +310,69 @@ __device__ __forceinline__ void x_from_lds(const floatx4 *xs, int u, float (&xv)
 //
 // FLAT: every wavefront (or workgroup) owns at most D+1 row groups; all of
 // them are fetched up front and decoded in order, with no fetch in the loop.
-template <int DT, int R, int D, bool WAVE_ROWS, bool FLAT>
-__global__ void __launch_bounds__(256) gemv_kernel(const uint8_t *__restrict__ blob, int64_t M, int64_t row_bytes,
-                                                   int U, const float *__restrict__ x, float *__restrict__ y,
-                                                   int64_t per_owner, int64_t extra) {
+//
+// MODE selects what a row group is and where its results go:
+//   GEMV_ONE     R rows of one matrix;  y = W x.
+//   GEMV_CONCAT  up to GEMV_MAX_MATS matrices that share K and x, run as one
+//                range of row groups, matrix after matrix (a matrix of M_i
+//                rows owns groups [g_lo[i], g_lo[i+1])); y_i = W_i x.  Each
+//                row's arithmetic is the single-matrix kernel's, so the bits
+//                match separate calls (page "cera 0.5.2 src/backend/cpu.rs",
+//                the fused dual and concatenated three-matrix GEMVs: one
+//                dispatch and one read of x for several projections).
+//   GEMV_SWIGLU  R rows of the gate matrix and the same R rows of the up
+//                matrix; out = silu(W_gate x) * (W_up x) (same page, the
+//                fused gate + up GEMV with in-register SwiGLU).
+enum { GEMV_ONE = 0, GEMV_CONCAT = 1, GEMV_SWIGLU = 2 };
+constexpr int GEMV_MAX_MATS = 4;
+
+struct GemvMats {
+    const uint8_t *blob[GEMV_MAX_MATS];
+    float *y[GEMV_MAX_MATS];
+    int64_t M[GEMV_MAX_MATS];
+    int64_t g_lo[GEMV_MAX_MATS + 1];  // unused entries hold the total group count
+};
+
+// Field i of a kernel-argument array, by selects (a dynamic index would copy
+// the argument block to scratch).
+template <typename T>
+__device__ __forceinline__ T pick(const T (&a)[GEMV_MAX_MATS], int i) {
+    T v = a[0];
+#pragma unroll
+    for (int j = 1; j < GEMV_MAX_MATS; j++) v = i == j ? a[j] : v;
+    return v;
+}
+__device__ __forceinline__ int mat_of(const GemvMats &m, int64_t g) {
+    int i = 0;
+#pragma unroll
+    for (int j = 1; j < GEMV_MAX_MATS; j++) i = g >= m.g_lo[j] ? j : i;
+    return i;
+}
+__device__ __forceinline__ int64_t lo_of(const GemvMats &m, int i) {
+    int64_t v = 0;
+#pragma unroll
+    for (int j = 1; j < GEMV_MAX_MATS; j++) v = i == j ? m.g_lo[j] : v;
+    return v;
+}
+
+// silu(v) = v * sigmoid(v) = v / (1 + e^-v) (page "cera 0.5.2
+// src/backend/cpu.rs", activation functions), evaluated with e = e^-|v| so
+// that the exponential never overflows: v / (1 + e) for v >= 0 and
+// v e / (1 + e) for v < 0 (the same function; tiny negative tails keep their
+// value instead of becoming -0 where e^-v would overflow).
+__device__ __forceinline__ float silu(float v) {
+    const float e = expf(-fabsf(v));
+    return (v >= 0.f ? v : v * e) / (1.0f + e);
+}
+
+template <int DT, int R, int D, bool WAVE_ROWS, bool FLAT, int MODE>
+__global__ void __launch_bounds__(256) gemv_kernel(const GemvMats mats, int64_t row_bytes, int U,
+                                                   const float *__restrict__ x, int64_t per_owner, int64_t extra) {
     constexpr int NL = Unit<DT>::NL;
+    constexpr int RR = MODE == GEMV_SWIGLU ? 2 * R : R;  // row dots per row group
     extern __shared__ __attribute__((aligned(16))) floatx4 xs[];
     constexpr int RED_G = 16;
-    __shared__ float red[WAVE_ROWS ? 1 : RED_G][R][4];
+    __shared__ float red[WAVE_ROWS ? 1 : RED_G][RR][4];
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6), nwaves = blockDim.x >> 6;
     const int u = WAVE_ROWS ? lane : t;
@@ -326,17 +381,39 @@ __global__ void __launch_bounds__(256) gemv_kernel(const uint8_t *__restrict__ b
     const int64_t owner = WAVE_ROWS ? (int64_t)blockIdx.x * nwaves + wave : (int64_t)blockIdx.x;
     const int64_t g0 = owner * per_owner + (owner < extra ? owner : extra);
     const int64_t n = per_owner + (owner < extra ? 1 : 0);
-    const int64_t nrg = (M + R - 1) / R;
+    const int64_t nrg = mats.g_lo[GEMV_MAX_MATS];
     const int64_t gend = g0 + n < nrg ? g0 + n : nrg;  // past the wavefront's last row group
     const typename Unit<DT>::Off off = Unit<DT>::lane_off(active ? u : 0);
 
-    uint32_t buf[D + 1][R][NL];
-    auto fetch = [&](int64_t g, uint32_t (&b)[R][NL]) {
-        // rows of group g that exist; none when g is past the range
-        const int64_t rows = g < gend ? (M - g * R < R ? M - g * R : R) : 0;
-        const Rsrc rs = make_rsrc(blob + (g < gend ? g : 0) * R * row_bytes, (uint32_t)(rows * row_bytes));
+    uint32_t buf[D + 1][RR][NL];
+    auto fetch = [&](int64_t g, uint32_t (&b)[RR][NL]) {
+        const bool in = g < gend;
+        const int mi = (MODE == GEMV_CONCAT && in) ? mat_of(mats, g) : 0;
+        const int64_t lg = in ? g - (MODE == GEMV_CONCAT ? lo_of(mats, mi) : 0) : 0;  // group within its matrix
+        const int64_t Mi = MODE == GEMV_CONCAT ? pick(mats.M, mi) : mats.M[0];
+        // rows of the group that exist; none when g is past the range
+        const int64_t rows = in ? (Mi - lg * R < R ? Mi - lg * R : R) : 0;
+        const uint8_t *base = MODE == GEMV_CONCAT ? pick(mats.blob, mi) : mats.blob[0];
+        const Rsrc rs = make_rsrc(base + lg * R * row_bytes, (uint32_t)(rows * row_bytes));
 #pragma unroll
         for (int r = 0; r < R; r++) Unit<DT>::load(rs, (uint32_t)(r * row_bytes), off, b[r]);
+        if constexpr (MODE == GEMV_SWIGLU) {
+            const Rsrc ru = make_rsrc(mats.blob[1] + lg * R * row_bytes, (uint32_t)(rows * row_bytes));
+#pragma unroll
+            for (int r = 0; r < R; r++) Unit<DT>::load(ru, (uint32_t)(r * row_bytes), off, b[R + r]);
+        }
+    };
+    // results of row r of group g (every lane that calls holds the sums)
+    auto put = [&](int64_t g, int r, float v, float vu) {
+        if constexpr (MODE == GEMV_SWIGLU) {
+            const int64_t row = g * R + r;
+            if (row < mats.M[0]) mats.y[0][row] = silu(v) * vu;
+        } else {
+            const int mi = MODE == GEMV_CONCAT ? mat_of(mats, g) : 0;
+            const int64_t row = (g - (MODE == GEMV_CONCAT ? lo_of(mats, mi) : 0)) * R + r;
+            if (row < (MODE == GEMV_CONCAT ? pick(mats.M, mi) : mats.M[0]))
+                (MODE == GEMV_CONCAT ? pick(mats.y, mi) : mats.y[0])[row] = v;
+        }
     };
     floatx4 xr[WAVE_ROWS ? 4 : 16];
     load_x(x, U, xr);
@@ -353,18 +430,16 @@ __global__ void __launch_bounds__(256) gemv_kernel(const uint8_t *__restrict__ b
             const int64_t i = i0 + s;
             if (!FLAT) fetch(g0 + i + D, buf[(s + D) % (D + 1)]);
             if (i < n) {
-                const int64_t row0 = (g0 + i) * R;
-                float acc[R];
+                float acc[RR];
 #pragma unroll
-                for (int r = 0; r < R; r++) {
+                for (int r = 0; r < RR; r++) {
                     const float d = Unit<DT>::dot(buf[s][r], xv, off);
                     acc[r] = wave_sum_to_lane63(active ? d : 0.f);
                 }
                 if (WAVE_ROWS) {
                     if (lane == 63) {
 #pragma unroll
-                        for (int r = 0; r < R; r++)
-                            if (row0 + r < M) y[row0 + r] = acc[r];
+                        for (int r = 0; r < R; r++) put(g0 + i, r, acc[r], acc[MODE == GEMV_SWIGLU ? R + r : r]);
                     }
                 } else {
                     // partial sums of up to RED_G row groups wait in LDS; one
@@ -373,16 +448,19 @@ __global__ void __launch_bounds__(256) gemv_kernel(const uint8_t *__restrict__ b
                     const int slot = (int)(i % RED_G);
                     if (lane == 63) {
 #pragma unroll
-                        for (int r = 0; r < R; r++) red[slot][r][wave] = acc[r];
+                        for (int r = 0; r < RR; r++) red[slot][r][wave] = acc[r];
                     }
                     if (slot == RED_G - 1 || i == n - 1) {
                         __syncthreads();
                         if (t < (slot + 1) * R) {
                             const int gi = t / R, r = t % R;
-                            const int64_t row = (g0 + i - slot + gi) * R + r;
-                            float sum = red[gi][r][0];
+                            float sum = red[gi][r][0], su = 0.f;
                             for (int w = 1; w < nwaves; w++) sum += red[gi][r][w];
-                            if (row < M) y[row] = sum;
+                            if constexpr (MODE == GEMV_SWIGLU) {
+                                su = red[gi][R + r][0];
+                                for (int w = 1; w < nwaves; w++) su += red[gi][R + r][w];
+                            }
+                            put(g0 + i - slot + gi, r, sum, su);
                         }
                         __syncthreads();
                     }
@@ -554,26 +632,39 @@ static bool fast_layout_ok(int dtype, int64_t nb) {
     }
 }
 
-// Wavefronts per CU for the GEMV (measured): 16 for Q4_0 and Q8_0 when each
-// wavefront owns whole rows (K <= 4096), else 8; QMM_GEMV_WAVES_PER_CU overrides it (a
+// How many wavefronts own row groups (measured on 4096- and 14336-row
+// matrices, single and concatenated, and a 128256-row head):
+//   * whole-row wavefronts (K <= 4096) and at most 64 row groups per CU: one
+//     row group per wavefront -- every group's loads are in flight at once
+//     and no wavefront waits for a second group (up to 1.4x faster than a
+//     ring for 14336 x 4096 and for concatenated gate + up);
+//   * larger matrices: a ring per wavefront, 16 wavefronts per CU for Q4_0
+//     and Q8_0, else 8;
+//   * a workgroup splitting K: 8 wavefronts per CU.
+// QMM_GEMV_WAVES_PER_CU = n (1..4096) replaces all of this with n per CU (a
 // tuning lever, read once).
-static int gemv_waves_per_cu(int dtype, bool wave_rows) {
+static int gemv_waves_lever() {
     static int v = [] {
         const char *e = getenv("QMM_GEMV_WAVES_PER_CU");
         const int n = e ? atoi(e) : 0;
-        return (n >= 1 && n <= 32) ? n : 0;
+        return (n >= 1 && n <= 4096) ? n : 0;
     }();
-    return v ? v : ((wave_rows && (dtype == QMM_Q4_0 || dtype == QMM_Q8_0)) ? 16 : 8);
+    return v;
+}
+static int64_t gemv_wave_owners(int dtype, int64_t nrg, int cus) {
+    const int lever = gemv_waves_lever();
+    if (lever) return std::min<int64_t>(nrg, (int64_t)cus * lever);
+    if (nrg <= (int64_t)cus * 64) return nrg;
+    return (int64_t)cus * ((dtype == QMM_Q4_0 || dtype == QMM_Q8_0) ? 16 : 8);
 }
 
 // Launch one fast-kernel variant: FLAT with D+1 = the most row groups an
 // owner gets when that is at most 4, else the ring with D row groups ahead.
-template <int DT, int R, int D, bool WAVE_ROWS>
-static void launch_variant(int64_t nmax, dim3 grid, dim3 block, size_t lds, hipStream_t st, const uint8_t *blob,
-                           int64_t M, int64_t row_bytes, int U, const float *x, float *y, int64_t per_owner,
-                           int64_t extra) {
+template <int DT, int R, int D, bool WAVE_ROWS, int MODE>
+static void launch_variant(int64_t nmax, dim3 grid, dim3 block, size_t lds, hipStream_t st, const GemvMats &mats,
+                           int64_t row_bytes, int U, const float *x, int64_t per_owner, int64_t extra) {
 #define QMM_GEMV_LAUNCH(F, DD) \
-    hipLaunchKernelGGL((gemv_kernel<DT, R, DD, WAVE_ROWS, F>), grid, block, lds, st, blob, M, row_bytes, U, x, y, \
+    hipLaunchKernelGGL((gemv_kernel<DT, R, DD, WAVE_ROWS, F, MODE>), grid, block, lds, st, mats, row_bytes, U, x, \
                        per_owner, extra)
     // Q4_K: with more than one row group fetched up front the compiler hoists
     // the scale unpacking of all of them and runs out of registers
@@ -588,49 +679,62 @@ static void launch_variant(int64_t nmax, dim3 grid, dim3 block, size_t lds, hipS
 #undef QMM_GEMV_LAUNCH
 }
 
-template <int DT, int R, int D>
-static hipError_t launch_fast(const uint8_t *blob, int64_t M, int64_t K, const float *x, float *y,
-                              hipStream_t st, int cus) {
+// The fast kernel over the row groups of `mats` (g_lo filled in by the caller).
+template <int DT, int R, int D, int MODE>
+static hipError_t launch_fast(const GemvMats &mats, int64_t K, const float *x, hipStream_t st, int cus) {
     constexpr int BS = Geo<DT>::BS, BB = Geo<DT>::BB;
     const int64_t row_bytes = (K / BS) * BB;
     const int U = (int)(K / 64);
-    const int64_t nrg = (M + R - 1) / R;
+    const int64_t nrg = mats.g_lo[GEMV_MAX_MATS];
     const size_t lds = (size_t)U * 256;  // the activations
-    const int64_t wpc = gemv_waves_per_cu(DT, U <= 64);
     if (U <= 64) {
-        const int64_t waves = std::min<int64_t>(nrg, (int64_t)cus * wpc);
+        const int64_t waves = gemv_wave_owners(DT, nrg, cus);
         const int64_t grid = (waves + 3) / 4, owners = grid * 4;
         const int64_t per = nrg / owners, extra = nrg % owners;
-        launch_variant<DT, R, D, true>(per + (extra ? 1 : 0), dim3((unsigned)grid), dim3(256), lds, st, blob, M,
-                                       row_bytes, U, x, y, per, extra);
+        launch_variant<DT, R, D, true, MODE>(per + (extra ? 1 : 0), dim3((unsigned)grid), dim3(256), lds, st, mats,
+                                             row_bytes, U, x, per, extra);
     } else if (U <= 256) {
         const int W = (U + 63) / 64;
-        const int64_t grid = std::min<int64_t>(nrg, (int64_t)cus * std::max<int64_t>(1, wpc / W));
+        const int lever = gemv_waves_lever();
+        const int64_t grid = std::min<int64_t>(nrg, (int64_t)cus * std::max(1, (lever ? lever : 8) / W));
         if (lds > 64 * 1024) {
             static const hipError_t attr = [] {
                 auto big_lds = [](const void *f) {
                     return hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, 64 * 1024 + 1024);
                 };
-                hipError_t e = big_lds(reinterpret_cast<const void *>(&gemv_kernel<DT, R, 0, false, true>));
-                if (e == hipSuccess) e = big_lds(reinterpret_cast<const void *>(&gemv_kernel<DT, R, D, false, false>));
+                hipError_t e = big_lds(reinterpret_cast<const void *>(&gemv_kernel<DT, R, 0, false, true, MODE>));
+                if (e == hipSuccess) e = big_lds(reinterpret_cast<const void *>(&gemv_kernel<DT, R, D, false, false, MODE>));
                 if constexpr (DT != QMM_Q4_K) {
-                    if (e == hipSuccess) e = big_lds(reinterpret_cast<const void *>(&gemv_kernel<DT, R, 1, false, true>));
-                    if (e == hipSuccess) e = big_lds(reinterpret_cast<const void *>(&gemv_kernel<DT, R, 2, false, true>));
-                    if (e == hipSuccess) e = big_lds(reinterpret_cast<const void *>(&gemv_kernel<DT, R, 3, false, true>));
+                    if (e == hipSuccess) e = big_lds(reinterpret_cast<const void *>(&gemv_kernel<DT, R, 1, false, true, MODE>));
+                    if (e == hipSuccess) e = big_lds(reinterpret_cast<const void *>(&gemv_kernel<DT, R, 2, false, true, MODE>));
+                    if (e == hipSuccess) e = big_lds(reinterpret_cast<const void *>(&gemv_kernel<DT, R, 3, false, true, MODE>));
                 }
                 return e;
             }();
             if (attr != hipSuccess) return attr;
         }
         const int64_t per = nrg / grid, extra = nrg % grid;
-        launch_variant<DT, R, D, false>(per + (extra ? 1 : 0), dim3((unsigned)grid), dim3(64 * W), lds, st, blob, M,
-                                        row_bytes, U, x, y, per, extra);
+        launch_variant<DT, R, D, false, MODE>(per + (extra ? 1 : 0), dim3((unsigned)grid), dim3(64 * W), lds, st,
+                                              mats, row_bytes, U, x, per, extra);
     } else {
+        if constexpr (MODE != GEMV_ONE) return hipErrorNotSupported;
+        const int64_t M = mats.M[0];
         const int64_t grid = std::min<int64_t>(nrg, (int64_t)cus * 2);
-        hipLaunchKernelGGL((gemv_multi_kernel<DT, R>), dim3((unsigned)grid), dim3(256), 0, st, blob, M, row_bytes, U,
-                           x, y);
+        hipLaunchKernelGGL((gemv_multi_kernel<DT, R>), dim3((unsigned)grid), dim3(256), 0, st, mats.blob[0], M,
+                           row_bytes, U, x, mats.y[0]);
     }
     return hipGetLastError();
+}
+
+template <int DT, int R, int D>
+static hipError_t launch_one(const uint8_t *blob, int64_t M, int64_t K, const float *x, float *y, hipStream_t st,
+                             int cus) {
+    GemvMats m{};
+    m.blob[0] = blob;
+    m.y[0] = y;
+    m.M[0] = M;
+    for (int j = 1; j <= GEMV_MAX_MATS; j++) m.g_lo[j] = (M + R - 1) / R;
+    return launch_fast<DT, R, D, GEMV_ONE>(m, K, x, st, cus);
 }
 
 template <int DT>
@@ -643,16 +747,76 @@ static hipError_t launch_generic(const uint8_t *blob, int64_t M, int64_t K, cons
     return hipGetLastError();
 }
 
+// Several matrices (CONCAT) or a gate/up pair (SWIGLU) in one launch.
+template <int DT, int R, int D, int MODE>
+static hipError_t launch_mats(int n, const void *const *blobs, const int64_t *Ms, int64_t K, const float *x,
+                              float *const *ys, hipStream_t st, int cus) {
+    GemvMats m{};
+    int64_t g = 0;
+    for (int i = 0; i < GEMV_MAX_MATS; i++) {
+        m.g_lo[i] = g;
+        if (i < n) {
+            m.blob[i] = static_cast<const uint8_t *>(blobs[i]);
+            m.y[i] = ys[i];
+            m.M[i] = Ms[i];
+            if (MODE == GEMV_CONCAT || i == 0) g += (Ms[i] + R - 1) / R;
+        }
+    }
+    m.g_lo[GEMV_MAX_MATS] = g;
+    return launch_fast<DT, R, D, MODE>(m, K, x, st, cus);
+}
+
+bool gemv_fused_ok(int dtype, int64_t K) {
+    const int64_t bs = (dtype == QMM_Q4_K || dtype == QMM_Q6_K) ? 256 : 32;
+    return fast_layout_ok(dtype, K / bs) && (K % 64) == 0 && K / 64 <= 256;
+}
+
+hipError_t launch_gemv_concat(int n, const void *const *blobs, const int64_t *Ms, int dtype, int64_t K,
+                              const float *x, float *const *ys, hipStream_t st, int cus) {
+    if (n < 1 || n > GEMV_MAX_MATS) return hipErrorInvalidValue;
+    if (!gemv_fused_ok(dtype, K)) {
+        // layouts the fast kernel does not take: one launch per matrix, same bits
+        for (int i = 0; i < n; i++) {
+            const hipError_t e = launch_gemv(dtype, blobs[i], Ms[i], K, x, ys[i], st, cus);
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }
+    switch (dtype) {
+    case QMM_Q4_0: return launch_mats<QMM_Q4_0, 2, 3, GEMV_CONCAT>(n, blobs, Ms, K, x, ys, st, cus);
+    case QMM_Q8_0: return launch_mats<QMM_Q8_0, 1, 4, GEMV_CONCAT>(n, blobs, Ms, K, x, ys, st, cus);
+    case QMM_Q4_K: return launch_mats<QMM_Q4_K, 2, 3, GEMV_CONCAT>(n, blobs, Ms, K, x, ys, st, cus);
+    case QMM_Q6_K: return launch_mats<QMM_Q6_K, 1, 4, GEMV_CONCAT>(n, blobs, Ms, K, x, ys, st, cus);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_gemv_swiglu(int dtype, const void *gate, const void *up, int64_t M, int64_t K, const float *x,
+                              float *out, hipStream_t st, int cus) {
+    if (!gemv_fused_ok(dtype, K)) return hipErrorInvalidValue;
+    const void *blobs[2] = {gate, up};
+    const int64_t Ms[2] = {M, M};
+    float *ys[2] = {out, out};
+    // one row of each matrix per group: the register footprint of two rows
+    switch (dtype) {
+    case QMM_Q4_0: return launch_mats<QMM_Q4_0, 1, 3, GEMV_SWIGLU>(2, blobs, Ms, K, x, ys, st, cus);
+    case QMM_Q8_0: return launch_mats<QMM_Q8_0, 1, 2, GEMV_SWIGLU>(2, blobs, Ms, K, x, ys, st, cus);
+    case QMM_Q4_K: return launch_mats<QMM_Q4_K, 1, 3, GEMV_SWIGLU>(2, blobs, Ms, K, x, ys, st, cus);
+    case QMM_Q6_K: return launch_mats<QMM_Q6_K, 1, 2, GEMV_SWIGLU>(2, blobs, Ms, K, x, ys, st, cus);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 hipError_t launch_gemv(int dtype, const void *blob_v, int64_t M, int64_t K, const float *x, float *y,
                        hipStream_t st, int cus) {
     const uint8_t *blob = static_cast<const uint8_t *>(blob_v);
     const int64_t bs = (dtype == QMM_Q4_K || dtype == QMM_Q6_K) ? 256 : 32;
     const bool fast = fast_layout_ok(dtype, K / bs) && (K % 64) == 0;
     switch (dtype) {
-    case QMM_Q4_0: return fast ? launch_fast<QMM_Q4_0, 2, 3>(blob, M, K, x, y, st, cus) : launch_generic<QMM_Q4_0>(blob, M, K, x, y, st, cus);
-    case QMM_Q8_0: return fast ? launch_fast<QMM_Q8_0, 1, 4>(blob, M, K, x, y, st, cus) : launch_generic<QMM_Q8_0>(blob, M, K, x, y, st, cus);
-    case QMM_Q4_K: return fast ? launch_fast<QMM_Q4_K, 2, 3>(blob, M, K, x, y, st, cus) : launch_generic<QMM_Q4_K>(blob, M, K, x, y, st, cus);
-    case QMM_Q6_K: return fast ? launch_fast<QMM_Q6_K, 1, 4>(blob, M, K, x, y, st, cus) : launch_generic<QMM_Q6_K>(blob, M, K, x, y, st, cus);
+    case QMM_Q4_0: return fast ? launch_one<QMM_Q4_0, 2, 3>(blob, M, K, x, y, st, cus) : launch_generic<QMM_Q4_0>(blob, M, K, x, y, st, cus);
+    case QMM_Q8_0: return fast ? launch_one<QMM_Q8_0, 1, 4>(blob, M, K, x, y, st, cus) : launch_generic<QMM_Q8_0>(blob, M, K, x, y, st, cus);
+    case QMM_Q4_K: return fast ? launch_one<QMM_Q4_K, 2, 3>(blob, M, K, x, y, st, cus) : launch_generic<QMM_Q4_K>(blob, M, K, x, y, st, cus);
+    case QMM_Q6_K: return fast ? launch_one<QMM_Q6_K, 1, 4>(blob, M, K, x, y, st, cus) : launch_generic<QMM_Q6_K>(blob, M, K, x, y, st, cus);
     default: return hipErrorInvalidValue;
     }
 }

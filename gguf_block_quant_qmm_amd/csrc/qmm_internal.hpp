@@ -10,6 +10,16 @@ namespace qmm {
 hipError_t launch_gemv(int dtype, const void *blob, int64_t M, int64_t K, const float *x, float *y,
                        hipStream_t st, int cus);
 
+// y_i = W_i x for n <= 4 matrices sharing K, in one launch where the layout
+// allows (else one launch per matrix); bits equal launch_gemv's.
+hipError_t launch_gemv_concat(int n, const void *const *blobs, const int64_t *Ms, int dtype, int64_t K,
+                              const float *x, float *const *ys, hipStream_t st, int cus);
+
+// out = silu(W_gate x) * (W_up x), one launch.  Needs gemv_fused_ok(dtype, K).
+hipError_t launch_gemv_swiglu(int dtype, const void *gate, const void *up, int64_t M, int64_t K, const float *x,
+                              float *out, hipStream_t st, int cus);
+bool gemv_fused_ok(int dtype, int64_t K);
+
 // Y[N][M] = X W^T on the matrix cores (f16 operands, f32 accumulation).
 hipError_t launch_gemm_mfma(int dtype, const void *blob, int64_t M, int64_t K, int64_t N, const float *X,
                             float *Y, hipStream_t st);

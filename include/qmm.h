@@ -84,6 +84,42 @@ extern "C" {
 int qmm_gemv(const void *w_blob, int dtype, int64_t M, int64_t K,
              const float *x, float *y, void *stream);
 
+/* Up to QMM_GEMV_MAX_MATS projections of one token in one launch, reading x
+ * once (page "cera 0.5.2 src/backend/cpu.rs", the fused dual GEMV and the
+ * concatenated three-matrix GEMV for the Q, K and V projections):
+ *     ys[i][m] = sum_k W_i[m][k] * x[k],   0 <= m < Ms[i],  0 <= i < n.
+ *   n       1 .. QMM_GEMV_MAX_MATS, else QMM_ERR_SHAPE
+ *   w_blobs host array of n device pointers (each as w_blob of qmm_gemv)
+ *   Ms      host array of n row counts
+ *   dtype,K shared by all matrices
+ *   x       device f32 [K], 16-B aligned
+ *   ys      host array of n device pointers, f32 [Ms[i]], 4-B aligned;
+ *           overwritten; the outputs must not overlap the blobs or x
+ * Each ys[i] holds exactly the bits qmm_gemv returns for matrix i.  The
+ * host arrays are read before the call returns and not kept.  Layouts that
+ * the one-launch kernel does not take (K not a multiple of 64, an odd number
+ * of blocks per row for Q4_0/Q8_0/Q6_K, K > 16384) run one launch per matrix
+ * with the same results. */
+#define QMM_GEMV_MAX_MATS 4
+int qmm_gemv_concat(int n, const void *const *w_blobs, const int64_t *Ms, int dtype, int64_t K,
+                    const float *x, float *const *ys, void *stream);
+
+/* The gate/up projection of a gated feed-forward block with SwiGLU, one
+ * token, one launch (page "cera 0.5.2 src/backend/cpu.rs", the fused gate +
+ * up GEMV with in-register SwiGLU):
+ *     out[m] = silu(g[m]) * u[m],  g = W_gate x,  u = W_up x,
+ *     silu(v) = v / (1 + e^-v)   (same page, activation functions)
+ *   gate_blob, up_blob  device blobs of one dtype and shape M x K
+ *   x                   device f32 [K], 16-B aligned
+ *   out                 device f32 [M], 4-B aligned; overwritten
+ * g and u are the f32 GEMV sums (bits of qmm_gemv); with S_g, S_u their
+ * sums of |w x| and tau = 1e-5:
+ *   |out - exact| <= tau*(1.1*S_g*(|u| + tau*S_u) + |silu(g)|*S_u) + 4*2^-24*|out|.
+ * Needs K a multiple of 64, at most 16384, and an even number of blocks per
+ * row for Q4_0, Q8_0 and Q6_K; otherwise QMM_ERR_SHAPE. */
+int qmm_gemv_swiglu(const void *gate_blob, const void *up_blob, int dtype, int64_t M, int64_t K,
+                    const float *x, float *out, void *stream);
+
 /* Prefill / verify GEMM over N tokens (page "cera 0.3.1 src/model/gpu_lfm2.rs",
  * mul_mat_reg_tile: weights decoded once per k-tile and reused across all
  * token columns):  Y[n][m] = sum_k W[m][k] * X[n][k].

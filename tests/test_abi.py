@@ -105,3 +105,56 @@ def test_valid_call_without_gpu_reports_device(monkeypatch):
     if torch.cuda.is_available():
         pytest.skip("a GPU is present; covered by the GPU tests")
     assert q.lib().qmm_gemv(A16, 2, 8, 64, A16, A16, None) == q.QMM_ERR_DEVICE
+
+
+def _concat(n, blobs, Ms, dtype, K, x, ys):
+    def arr(ct, v):
+        return (ct * len(v))(*v) if v is not None else None
+    return q.lib().qmm_gemv_concat(n, arr(ctypes.c_void_p, blobs), arr(ctypes.c_int64, Ms), dtype, K, x,
+                                   arr(ctypes.c_void_p, ys), None)
+
+
+@pytest.mark.parametrize("n,blobs,Ms,dtype,K,x,ys,code", [
+    (0, [A16], [8], 2, 64, A16, [A16], q.QMM_ERR_SHAPE),
+    (5, [A16] * 5, [8] * 5, 2, 64, A16, [A16] * 5, q.QMM_ERR_SHAPE),
+    (2, [A16, A16], [8, 0], 2, 64, A16, [A16, A16], q.QMM_ERR_SHAPE),
+    (2, [A16, A16], [8, 8], 2, 48, A16, [A16, A16], q.QMM_ERR_SHAPE),
+    (2, [A16, A16], [8, 8], 3, 64, A16, [A16, A16], q.QMM_ERR_DTYPE),
+    (2, None, [8, 8], 2, 64, A16, [A16, A16], q.QMM_ERR_NULL),
+    (2, [A16, A16], None, 2, 64, A16, [A16, A16], q.QMM_ERR_NULL),
+    (2, [A16, A16], [8, 8], 2, 64, A16, None, q.QMM_ERR_NULL),
+    (2, [A16, 0], [8, 8], 2, 64, A16, [A16, A16], q.QMM_ERR_NULL),
+    (2, [A16, A16], [8, 8], 2, 64, 0, [A16, A16], q.QMM_ERR_NULL),
+    (2, [A16, A16], [8, 8], 2, 64, A16, [A16, 0], q.QMM_ERR_NULL),
+    (2, [A16, A16 + 8], [8, 8], 2, 64, A16, [A16, A16], q.QMM_ERR_ALIGN),
+    (2, [A16, A16], [8, 8], 2, 64, A16 + 4, [A16, A16], q.QMM_ERR_ALIGN),
+    (2, [A16, A16], [8, 8], 2, 64, A16, [A16, A16 + 1], q.QMM_ERR_ALIGN),
+])
+def test_gemv_concat_rejects(n, blobs, Ms, dtype, K, x, ys, code):
+    assert _concat(n, blobs, Ms, dtype, K, x, ys) == code
+
+
+@pytest.mark.parametrize("args,code", [
+    ((A16, A16, 5, 8, 64, A16, A16), q.QMM_ERR_DTYPE),
+    ((A16, A16, 2, 0, 64, A16, A16), q.QMM_ERR_SHAPE),
+    ((A16, A16, 2, 8, 96, A16, A16), q.QMM_ERR_SHAPE),       # odd number of Q4_0 blocks
+    ((A16, A16, 14, 8, 256, A16, A16), q.QMM_ERR_SHAPE),     # odd number of Q6_K super-blocks
+    ((A16, A16, 12, 8, 16640, A16, A16), q.QMM_ERR_SHAPE),   # K > 16384
+    ((0, A16, 2, 8, 64, A16, A16), q.QMM_ERR_NULL),
+    ((A16, 0, 2, 8, 64, A16, A16), q.QMM_ERR_NULL),
+    ((A16, A16, 2, 8, 64, 0, A16), q.QMM_ERR_NULL),
+    ((A16, A16, 2, 8, 64, A16, 0), q.QMM_ERR_NULL),
+    ((A16, A16 + 2, 2, 8, 64, A16, A16), q.QMM_ERR_ALIGN),
+    ((A16, A16, 2, 8, 64, A16 + 8, A16), q.QMM_ERR_ALIGN),
+    ((A16, A16, 2, 8, 64, A16, A16 + 2), q.QMM_ERR_ALIGN),
+])
+def test_gemv_swiglu_rejects(args, code):
+    assert q.lib().qmm_gemv_swiglu(*args, None) == code
+
+
+def test_fused_calls_without_gpu_report_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; covered by the GPU tests")
+    assert _concat(2, [A16, A16], [8, 8], 2, 64, A16, [A16, A16]) == q.QMM_ERR_DEVICE
+    assert q.lib().qmm_gemv_swiglu(A16, A16, 2, 8, 64, A16, A16, None) == q.QMM_ERR_DEVICE

@@ -1,0 +1,215 @@
+"""Fused decode calls against the CPU oracle, through the C ABI.
+
+qmm_gemv_concat: several matrices that share x in one launch.  Each output
+must equal, bit for bit, what qmm_gemv returns for its matrix, and lie within
+1e-5 * sum |w x| of the oracle's exact sum.  Shapes put row-group ranges
+across matrix boundaries, cover both kernel shapes (K <= 4096: whole rows per
+wavefront; K <= 16384: a workgroup splits K), ragged tails, and the layouts
+that fall back to one launch per matrix.
+
+qmm_gemv_swiglu: out = silu(W_gate x) * (W_up x).  The bound follows from the
+GEMV bound (tau = 1e-5 of S_g and S_u) carried through silu (|silu'| < 1.1)
+and the product, plus 4 f32 roundings of the result:
+    |out - exact| <= tau*(1.1*S_g*(|u| + tau*S_u) + |silu(g)|*S_u) + 4*2^-24*|exact|
+(f32 underflow of silu in the far negative tail is far inside the first term,
+since there |g| > 87 and S_g >= |g|).
+It is also checked against silu(g)*u formed in f64 from the GPU's own GEMV
+outputs (which it must reproduce to f32 rounding), which fixes the order of
+the operands independently of the oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gguf_block_quant_qmm_amd as q
+import oracle
+from qmm_inputs import make_blob, make_x, rng_for
+
+pytestmark = pytest.mark.gpu
+
+DTYPES = [q.QMM_Q4_0, q.QMM_Q8_0, q.QMM_Q4_K, q.QMM_Q6_K]
+NAME = {2: "Q4_0", 8: "Q8_0", 12: "Q4_K", 14: "Q6_K"}
+TAU = 1e-5
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.set_device(0)
+
+
+def to_dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def bs_of(dt):
+    return 256 if dt in (q.QMM_Q4_K, q.QMM_Q6_K) else 32
+
+
+def gemv(dt, blob_d, M, K, x_d):
+    y = torch.full((M,), float("nan"), device="cuda")
+    q.qmm_gemv(blob_d, dt, M, K, x_d, y)
+    return y
+
+
+def check_f32(yg, Y64, S, label):
+    err = np.abs(yg.astype(np.float64) - Y64)
+    zero = S == 0
+    assert np.all(yg[zero] == 0), f"{label}: S = 0 but output is not exactly 0"
+    if (~zero).any():
+        r = err[~zero] / S[~zero]
+        assert r.max() <= TAU, f"{label}: |err|/S = {r.max():.3g} at {int(np.argmax(r))}"
+
+
+# ------------------------------------------------------------------ concat
+
+def concat_cases(dt):
+    bs = bs_of(dt)
+    if bs == 32:
+        return [([1], 64), ([3, 1, 2], 256), ([67, 300, 5, 129], 1024), ([1001, 513], 4096),
+                ([129, 64, 3], 8192), ([40, 7], 16384), ([5, 9], 96), ([4, 3], 16416)]
+    return [([1], 512), ([3, 1, 2], 512), ([67, 300, 5, 129], 1024), ([1001, 513], 4096),
+            ([129, 64, 3], 8192), ([40, 7], 16384), ([5, 9], 768), ([4, 3], 16896)]
+
+
+@pytest.mark.parametrize("dt", DTYPES, ids=NAME.get)
+def test_concat_small(dt):
+    for c, (Ms, K) in enumerate(concat_cases(dt)):
+        blobs = [make_blob(dt, M, K, rng_for(700 + dt, 10 * c + i)) for i, M in enumerate(Ms)]
+        x = make_x(1, K, rng_for(700 + dt, 1000 + c))
+        bd = [to_dev(b) for b in blobs]
+        xd = to_dev(x.reshape(-1))
+        ys = [torch.full((M,), float("nan"), device="cuda") for M in Ms]
+        q.qmm_gemv_concat(bd, dt, Ms, K, xd, ys)
+        torch.cuda.synchronize()
+        for i, (M, b) in enumerate(zip(Ms, blobs)):
+            label = f"{NAME[dt]} concat case {c} matrix {i} M={M} K={K}"
+            ref = gemv(dt, bd[i], M, K, xd)
+            torch.cuda.synchronize()
+            assert torch.equal(ys[i], ref), f"{label}: bits differ from qmm_gemv"
+            _, Y64, S = oracle.matmul(dt, b, M, K, x)
+            check_f32(ys[i].cpu().numpy()[None, :], Y64, S, label)
+
+
+@pytest.mark.parametrize("layout", ["gate_up", "qkv"])
+def test_concat_llama8b_shapes(layout):
+    """Q4_0, K = 4096: gate + up (2 x 14336 rows) and q, k, v (4096 + 1024 + 1024
+    rows, grouped-query attention); bitwise against qmm_gemv, sampled rows against
+    the oracle."""
+    dt, K = q.QMM_Q4_0, 4096
+    Ms = [14336, 14336] if layout == "gate_up" else [4096, 1024, 1024]
+    blobs = [make_blob(dt, M, K, rng_for(760, i + 10 * len(Ms))) for i, M in enumerate(Ms)]
+    x = make_x(1, K, rng_for(761, len(Ms)))
+    bd, xd = [to_dev(b) for b in blobs], to_dev(x.reshape(-1))
+    ys = [torch.full((M,), float("nan"), device="cuda") for M in Ms]
+    q.qmm_gemv_concat(bd, dt, Ms, K, xd, ys)
+    torch.cuda.synchronize()
+    for i, M in enumerate(Ms):
+        assert torch.equal(ys[i], gemv(dt, bd[i], M, K, xd)), f"{layout} matrix {i}: bits differ from qmm_gemv"
+        rows = np.unique(np.concatenate([np.arange(3), M - 1 - np.arange(3),
+                                         np.random.default_rng(762 + i).choice(M, 200, replace=False)]))
+        _, Y64, S = oracle.matmul(dt, blobs[i], M, K, x, rows=rows)
+        check_f32(ys[i].cpu().numpy()[rows][None, :], Y64, S, f"{layout} matrix {i}")
+
+
+# ------------------------------------------------------------------ SwiGLU
+
+def swiglu_shapes(dt):
+    if bs_of(dt) == 32:
+        return [(1, 64), (3, 256), (67, 512), (300, 1024), (129, 4096), (50, 8192), (33, 16384)]
+    return [(1, 512), (3, 512), (67, 1024), (300, 2048), (129, 4096), (50, 8192), (33, 16384)]
+
+
+def check_swiglu(out, r, g_gpu, u_gpu, label):
+    out = out.astype(np.float64)
+    g, u, sg, su, exact = r["g"][0], r["u"][0], r["sg"][0], r["su"][0], r["out64"][0]
+    with np.errstate(over="ignore"):
+        silu_g = g / (1.0 + np.exp(-g))
+    bound = TAU * (1.1 * sg * (np.abs(u) + TAU * su) + np.abs(silu_g) * su) + 4 * 2.0 ** -24 * np.abs(exact)
+    assert np.all(np.isfinite(out)), f"{label}: non-finite output"
+    zero = (sg == 0) | (su == 0)
+    assert np.all(out[zero] == 0), f"{label}: a zero projection must give exactly 0"
+    bad = np.abs(out - exact) > bound
+    assert not bad.any(), (f"{label}: row {int(np.argmax(bad))} off by "
+                           f"{np.abs(out - exact)[bad].max():.3g} > bound")
+    # against silu(g) * u from the GPU's own GEMV outputs, in f64
+    g2, u2 = g_gpu.astype(np.float64), u_gpu.astype(np.float64)
+    with np.errstate(over="ignore"):
+        mine = g2 / (1.0 + np.exp(-g2)) * u2
+    # (plus the f32 underflow of silu: |silu(g)| below ~104 * 2^-126 may be lost)
+    lim = 4 * 2.0 ** -24 * np.abs(mine) + 2.0 ** -119 * np.abs(u2)
+    assert np.all(np.abs(out - mine) <= lim), f"{label}: not silu(g) * u"
+
+
+@pytest.mark.parametrize("dt", DTYPES, ids=NAME.get)
+def test_swiglu_small(dt):
+    for i, (M, K) in enumerate(swiglu_shapes(dt)):
+        gate = make_blob(dt, M, K, rng_for(800 + dt, i))
+        up = make_blob(dt, M, K, rng_for(800 + dt, 100 + i))
+        x = make_x(1, K, rng_for(800 + dt, 200 + i))
+        gd, ud, xd = to_dev(gate), to_dev(up), to_dev(x.reshape(-1))
+        out = torch.full((M,), float("nan"), device="cuda")
+        q.qmm_gemv_swiglu(gd, ud, dt, M, K, xd, out)
+        g_gpu, u_gpu = gemv(dt, gd, M, K, xd), gemv(dt, ud, M, K, xd)
+        torch.cuda.synchronize()
+        r = oracle.swiglu(dt, gate, up, M, K, x)
+        check_swiglu(out.cpu().numpy(), r, g_gpu.cpu().numpy(), u_gpu.cpu().numpy(),
+                     f"{NAME[dt]} swiglu M={M} K={K}")
+
+
+@pytest.mark.parametrize("dt", DTYPES, ids=NAME.get)
+def test_swiglu_edge_values(dt):
+    """Zero gate rows and zero up rows give exact zeros; a large x drives silu
+    into both tails (exp overflow for very negative g)."""
+    M, K = 96, 1024
+    gate = make_blob(dt, M, K, rng_for(820 + dt, 0))
+    up = make_blob(dt, M, K, rng_for(820 + dt, 1))
+    rb = gate.size // M
+    gate.reshape(M, rb)[::7] = 0          # all-zero blocks: scales and codes 0
+    up.reshape(M, rb)[3::11] = 0
+    for scale in (1.0, 300.0):
+        x = (make_x(1, K, rng_for(820 + dt, 2)) * np.float32(scale)).astype(np.float32)
+        gd, ud, xd = to_dev(gate), to_dev(up), to_dev(x.reshape(-1))
+        out = torch.full((M,), float("nan"), device="cuda")
+        q.qmm_gemv_swiglu(gd, ud, dt, M, K, xd, out)
+        g_gpu, u_gpu = gemv(dt, gd, M, K, xd), gemv(dt, ud, M, K, xd)
+        torch.cuda.synchronize()
+        r = oracle.swiglu(dt, gate, up, M, K, x)
+        check_swiglu(out.cpu().numpy(), r, g_gpu.cpu().numpy(), u_gpu.cpu().numpy(),
+                     f"{NAME[dt]} swiglu edge x*{scale}")
+
+
+def test_swiglu_llama8b_full_size():
+    """The gate/up pair of a LLaMA-8B layer in Q4_0 (14336 x 4096 each), sampled rows."""
+    dt, M, K = q.QMM_Q4_0, 14336, 4096
+    gate = make_blob(dt, M, K, rng_for(840, 0))
+    up = make_blob(dt, M, K, rng_for(840, 1))
+    x = make_x(1, K, rng_for(840, 2))
+    gd, ud, xd = to_dev(gate), to_dev(up), to_dev(x.reshape(-1))
+    out = torch.full((M,), float("nan"), device="cuda")
+    q.qmm_gemv_swiglu(gd, ud, dt, M, K, xd, out)
+    g_gpu, u_gpu = gemv(dt, gd, M, K, xd), gemv(dt, ud, M, K, xd)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(3), M - 1 - np.arange(3),
+                                     np.random.default_rng(841).choice(M, 300, replace=False)]))
+    r = oracle.swiglu(dt, gate, up, M, K, x, rows=rows)
+    check_swiglu(out.cpu().numpy()[rows], r, g_gpu.cpu().numpy()[rows], u_gpu.cpu().numpy()[rows],
+                 "Q4_0 swiglu 14336x4096")
+
+
+def test_fused_calls_are_deterministic():
+    dt, K = q.QMM_Q4_K, 4096
+    Ms = [3000, 1000]
+    blobs = [to_dev(make_blob(dt, M, K, rng_for(860, i))) for i, M in enumerate(Ms)]
+    xd = to_dev(make_x(1, K, rng_for(860, 9)).reshape(-1))
+    runs = []
+    for _ in range(2):
+        ys = [torch.empty(M, device="cuda") for M in Ms]
+        q.qmm_gemv_concat(blobs, dt, Ms, K, xd, ys)
+        out = torch.empty(Ms[1], device="cuda")
+        q.qmm_gemv_swiglu(blobs[1], blobs[1], dt, Ms[1], K, xd, out)
+        torch.cuda.synchronize()
+        runs.append([t.cpu() for t in ys + [out]])
+    for a, b in zip(*runs):
+        assert torch.equal(a, b)
