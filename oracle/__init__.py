@@ -55,6 +55,7 @@ def _bind(lib):
     lib.oracle_silu.argtypes = [ctypes.c_double]
     lib.oracle_silu.restype = ctypes.c_double
     lib.oracle_swiglu_rows.argtypes = [ctypes.c_int, vp, vp, i64, i64, i64, vp, i64, vp, vp, vp, vp, vp, vp, vp]
+    lib.oracle_argmax.argtypes = [ctypes.c_int, vp, i64, i64, vp, vp, vp, vp]
     return lib
 
 
@@ -171,6 +172,21 @@ def swiglu(dtype: int, gate: np.ndarray, up: np.ndarray, M: int, K: int, X: np.n
                                          *(_ptr(r[k]) for k in ("out", "out64", "g", "u", "sg", "su")))
     _check(rc, "swiglu")
     return r
+
+
+def argmax(dtype: int, blob: np.ndarray, M: int, K: int, x: np.ndarray, L=None):
+    """(index, f64 maximum, its S) of the greedy argmax over y = W x (smallest index on ties)."""
+    blob = np.ascontiguousarray(blob, dtype=np.uint8)
+    x = np.ascontiguousarray(x, dtype=np.float32).reshape(-1)
+    if x.size != K:
+        raise ValueError("x has the wrong K")
+    if blob.size < blob_bytes(dtype, M, K, L):
+        raise ValueError("blob too small")
+    idx = np.zeros(1, np.int64)
+    best = np.zeros(1, np.float64)
+    bs = np.zeros(1, np.float64)
+    _check((L or lib()).oracle_argmax(dtype, _ptr(blob), M, K, _ptr(x), _ptr(idx), _ptr(best), _ptr(bs)), "argmax")
+    return int(idx[0]), float(best[0]), float(bs[0])
 
 
 def num_threads() -> int:

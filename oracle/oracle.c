@@ -16,7 +16,10 @@
  * and, for the gate/up projection with SwiGLU (two matrices of one shape),
  *
  *   out[n,m] = silu(G[n,m]) * U[n,m],  silu(v) = v / (1 + e^-v)  in f64,
- *   G, U the f64 sums above for the gate and the up matrix.
+ *   G, U the f64 sums above for the gate and the up matrix;
+ *
+ * and, for greedy decoding, the argmax over m of the f64 sums of one token
+ * (the smallest index among equal maxima).
  *
  * Source of the definition: page "cera 0.5.2 src/backend/cpu.rs", section
  * "Matrix multiplication" -- the scalar reference matmuls matmul_f32,
@@ -327,5 +330,42 @@ int oracle_swiglu_rows(int dtype, const uint8_t *gate, const uint8_t *up, int64_
         }
     }
     free(tmp); free(g); free(u); free(sg); free(su);
+    return rc;
+}
+
+/* ---- greedy argmax over the logits of one token ------------------------ */
+
+/* The greedy argmax GEMV (page "cera 0.5.2 src/backend/cpu.rs", the argmax
+ * GEMV that returns the index of the largest output without storing the
+ * outputs): the row m with the largest exact f64 sum y[m] = sum_k W[m,k] x[k].
+ * The pages give no rule for equal maxima; READING: the smallest index wins.
+ * NaN sums never win.  Writes the index, the f64 maximum and the S of that
+ * row; returns -3 when no row has a non-NaN sum. */
+int oracle_argmax(int dtype, const uint8_t *blob, int64_t M, int64_t K, const float *x,
+                  int64_t *index, double *best, double *best_s) {
+    int rc = check_shape(dtype, M, K);
+    if (rc) return rc;
+    float *y = (float *)malloc(sizeof(float) * (size_t)M);
+    double *y64 = (double *)malloc(sizeof(double) * (size_t)M), *s = (double *)malloc(sizeof(double) * (size_t)M);
+    if (!y || !y64 || !s) {
+        rc = -7;
+    } else {
+        rc = oracle_matmul_rows(dtype, blob, M, K, 1, x, M, NULL, y, y64, s);
+    }
+    if (!rc) {
+        int64_t bi = -1;
+        for (int64_t m = 0; m < M; m++) {
+            if (y64[m] != y64[m]) continue;
+            if (bi < 0 || y64[m] > y64[bi]) bi = m;
+        }
+        if (bi < 0) {
+            rc = -3;
+        } else {
+            *index = bi;
+            if (best) *best = y64[bi];
+            if (best_s) *best_s = s[bi];
+        }
+    }
+    free(y); free(y64); free(s);
     return rc;
 }

@@ -18,6 +18,9 @@ run against deliberately broken builds of the oracle (test_oracle_mutants).
                       minimum -W(1/e)), the odd-part identity and its limits
   pin_swiglu          gate/up SwiGLU on fixture blocks with unit vectors:
                       g and u are the fixtures' design values, out = silu(g) u
+  pin_argmax          greedy argmax on fixture blocks with unit vectors (the
+                      design values pick the winner), planted ties and a
+                      planted maximum in the last row
 """
 from __future__ import annotations
 
@@ -415,5 +418,43 @@ def pin_swiglu(L=None):
         assert np.array_equal(rs["out64"], r["out64"][:, [2, 0]])
 
 
+# ------------------------------------------------------------------- argmax
+
+def pin_argmax(L=None):
+    for dt in DTYPES:
+        recs = load_golden(oracle.NAMES[dt])
+        bs = oracle.block_elems(dt, L)
+        nblk = 2 if bs == 256 else 4
+        K, M = nblk * bs, 5
+        rb, rw = [], []
+        for m in range(M):
+            pick = [recs[(m + b) % len(recs)] for b in range(nblk)]
+            rb.append(b"".join(p[1] for p in pick))
+            rw.append(np.concatenate([p[2] for p in pick]))
+        blob, W = np.frombuffer(b"".join(rb), np.uint8), np.stack(rw)
+        name = oracle.NAMES[dt]
+        for k in list(range(0, K, 5)) + [K - 1]:
+            col = W[:, k]
+            want = int(np.flatnonzero(col == col.max())[0])      # first of the design maxima
+            for sgn in (1.0, -1.0):
+                x = np.zeros(K, np.float32)
+                x[k] = sgn
+                c = sgn * col
+                want = int(np.flatnonzero(c == c.max())[0])
+                idx, best, _ = oracle.argmax(dt, blob, M, K, x, L=L)
+                assert idx == want and best == c.max(), f"{name}: x = {sgn:+} e_{k}: argmax {idx}, design {want}"
+        # a planted maximum in the last row, and ties resolved to the smallest index
+        assert not np.array_equal(W[0], W[1]), f"{name}: fixture rows 0 and 1 must differ"
+        dup = np.frombuffer(b"".join([rb[1], rb[0], rb[1], rb[1]]), np.uint8)
+        x = np.zeros(K, np.float32)
+        k = int(np.argmax(np.abs(W[1] - W[0])))
+        x[k] = 1.0 if W[1, k] > W[0, k] else -1.0
+        idx, _, _ = oracle.argmax(dt, dup, 4, K, x, L=L)
+        assert idx == 0, f"{name}: three equal maxima at rows 0, 2, 3 should give 0, got {idx}"
+        last = np.frombuffer(b"".join([rb[0], rb[0], rb[1]]), np.uint8)
+        idx, _, _ = oracle.argmax(dt, last, 3, K, x, L=L)
+        assert idx == 2, f"{name}: the maximum sits in the last row, got {idx}"
+
+
 ALL_PINS = [pin_golden, pin_unit_vectors, pin_closed_form, pin_bruteforce, pin_invariants,
-            pin_half, pin_sizes, pin_silu, pin_swiglu]
+            pin_half, pin_sizes, pin_silu, pin_swiglu, pin_argmax]

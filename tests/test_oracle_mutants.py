@@ -43,6 +43,10 @@ MUTANTS = {
     "swiglu_swapped": ("double o = oracle_silu(g[i]) * u[i];", "double o = oracle_silu(u[i]) * g[i];"),
     "swiglu_gate_twice": ("rc = oracle_matmul_rows(dtype, up, M, K, N, X, nrows, rows, tmp, u, su);",
                           "rc = oracle_matmul_rows(dtype, gate, M, K, N, X, nrows, rows, tmp, u, su);"),
+    "argmax_last_tie": ("if (bi < 0 || y64[m] > y64[bi]) bi = m;", "if (bi < 0 || y64[m] >= y64[bi]) bi = m;"),
+    "argmax_min": ("if (bi < 0 || y64[m] > y64[bi]) bi = m;", "if (bi < 0 || y64[m] < y64[bi]) bi = m;"),
+    "argmax_skips_last": ("for (int64_t m = 0; m < M; m++) {\n            if (y64[m] != y64[m]) continue;",
+                          "for (int64_t m = 0; m + 1 < M; m++) {\n            if (y64[m] != y64[m]) continue;"),
     "f32_rounding": ("Y[n * nrows + r] = (float)acc;", "Y[n * nrows + r] = (float)(acc * (1.0 + 0x1p-23));"),
 }
 
