@@ -29,6 +29,10 @@ time over its launch count.
 
 Extra: ``--sweep`` prints one JSON line per (workload, N) for every
 configuration of the workload table (C1-C5) instead of the main line.
+``--spec-verify`` prints one JSON line per N = 1..9 for the Q6_K LM head
+(128256 x 4096): N separate GEMVs ("per-row") against one qmm_gemm call
+("batched"), the shape of a speculative-decoding verification round, plus
+the greedy argmax GEMV at N = 1.
 """
 from __future__ import annotations
 
@@ -78,6 +82,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle time budget per leg")
     ap.add_argument("--sweep", action="store_true", help="per-config table instead of the main line")
+    ap.add_argument("--spec-verify", action="store_true",
+                    help="LM-head verification table (per-row vs batched, N = 1..9) instead of the main line")
     ap.add_argument("--headline-only", action="store_true",
                     help="time only the headline decode step and the prefill GEMM (profiler runs: every GEMV "
                          "launch then belongs to the headline step)")
@@ -102,6 +108,8 @@ def main():
 
     if args.sweep:
         return sweep(args, q, np, torch, dev, WORKLOADS, make_blob, make_x, rng_for)
+    if args.spec_verify:
+        return spec_verify(args, q, torch, dev, WORKLOADS, make_blob, make_x, rng_for)
 
     # ---------------------------------------------------------------- decode
     layer = [("q_proj", 2, 0), ("gate", 3, 0), ("up", 3, 1), ("down", 4, 0)]
@@ -347,6 +355,42 @@ def sweep(args, q, np, torch, dev, WORKLOADS, make_blob, make_x, rng_for):
             print(json.dumps(rec), flush=True)
         del copies, blob
         torch.cuda.empty_cache()
+
+
+def spec_verify(args, q, torch, dev, WORKLOADS, make_blob, make_x, rng_for):
+    """Verification of N drafted positions on the LM head: per-row GEMVs vs one batched call."""
+    stream = torch.cuda.current_stream()
+    label, dt, M, K, _ = WORKLOADS[5]
+    blob = torch.from_numpy(make_blob(dt, M, K, rng_for(5, 0))).to(dev)
+    R = max(2, -(-ROTATE_BYTES // blob.numel()))
+    copies = [blob] + [blob.clone() for _ in range(R - 1)]
+
+    def timed(fn):
+        for s in range(args.warmup):
+            fn(s % R)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for s in range(args.steps):
+            fn(s % R)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / args.steps
+
+    work = torch.empty(q.QMM_ARGMAX_WORK_BYTES, dtype=torch.uint8, device=dev)
+    idx = torch.empty(1, dtype=torch.int64, device=dev)
+    for N in range(1, 10):
+        X = torch.from_numpy(make_x(N, K, rng_for(5, 2000 + N))).to(dev)
+        Y = torch.empty((N, M), device=dev)
+        per_row = timed(lambda c: [q.qmm_gemv(copies[c], dt, M, K, X[n], Y[n], stream=stream) for n in range(N)])
+        batched = timed(lambda c: q.qmm_gemm(copies[c], dt, M, K, N, X, Y, stream=stream))
+        rec = {"workload": f"{label}, verify {N} positions", "N": N, "M": M, "K": K, "dtype": "Q6_K",
+               "per_row_us": round(per_row, 2), "batched_us": round(batched, 2),
+               "batched_path": "f16-mfma" if q.gemm_path(dt, M, K, N) else "f32 (bits of the GEMV)",
+               "batched_weight_GBps": round(blob.numel() / (batched * 1e-6) / 1e9, 1)}
+        if N == 1:
+            rec["argmax_us"] = round(timed(lambda c: q.qmm_gemv_argmax(copies[c], dt, M, K, X[0], work, idx,
+                                                                        stream=stream)), 2)
+        print(json.dumps(rec), flush=True)
 
 
 if __name__ == "__main__":

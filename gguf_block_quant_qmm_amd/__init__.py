@@ -12,6 +12,8 @@ there is no CPU fallback.
                                                      ys[i] = W_i x, one launch
     qmm_gemv_swiglu(gate, up, dtype, M, K, x, out, stream=None)
                                                      out = silu(W_gate x) * (W_up x)
+    qmm_gemv_argmax(w, dtype, M, K, x, work, index, value=None, stream=None)
+                                                     index = argmax_m (W x)[m]
 """
 from __future__ import annotations
 
@@ -28,8 +30,9 @@ QMM_OK, QMM_ERR_NULL, QMM_ERR_DTYPE, QMM_ERR_SHAPE = 0, -1, -2, -3
 QMM_ERR_ALIGN, QMM_ERR_DEVICE, QMM_ERR_LAUNCH = -4, -5, -6
 
 QMM_GEMV_MAX_MATS = 4
+QMM_ARGMAX_WORK_BYTES = 32768
 
-EXPORTS = ("qmm_gemv", "qmm_gemv_concat", "qmm_gemv_swiglu", "qmm_gemm", "qmm_gemm_path", "qmm_blob_bytes",
+EXPORTS = ("qmm_gemv", "qmm_gemv_concat", "qmm_gemv_swiglu", "qmm_gemv_argmax", "qmm_gemm", "qmm_gemm_path", "qmm_blob_bytes",
            "qmm_block_elems", "qmm_block_bytes", "qmm_strerror")
 
 _lib = None
@@ -55,6 +58,8 @@ def lib():
         L.qmm_gemv_concat.restype = ci
         L.qmm_gemv_swiglu.argtypes = [vp, vp, ci, i64, i64, vp, vp, vp]
         L.qmm_gemv_swiglu.restype = ci
+        L.qmm_gemv_argmax.argtypes = [vp, ci, i64, i64, vp, vp, vp, vp, vp]
+        L.qmm_gemv_argmax.restype = ci
         L.qmm_gemm.argtypes = [vp, ci, i64, i64, i64, vp, vp, vp]
         L.qmm_gemm.restype = ci
         L.qmm_gemm_path.argtypes = [ci, i64, i64, i64]
@@ -163,3 +168,13 @@ def qmm_gemv_swiglu(gate, up, dtype: int, M: int, K: int, x, out, stream=None) -
                                _stream(stream))
     if rc != QMM_OK:
         raise QmmError(rc, "qmm_gemv_swiglu")
+
+
+def qmm_gemv_argmax(w, dtype: int, M: int, K: int, x, work, index, value=None, stream=None) -> None:
+    import torch
+    rc = lib().qmm_gemv_argmax(_addr(w, blob_bytes(dtype, M, K) or None, "w_blob"), dtype, M, K,
+                               _addr(x, 4 * K, "x", torch.float32), _addr(work, QMM_ARGMAX_WORK_BYTES, "work"),
+                               _addr(index, 8, "index", torch.int64), _addr(value, 4, "value", torch.float32),
+                               _stream(stream))
+    if rc != QMM_OK:
+        raise QmmError(rc, "qmm_gemv_argmax")

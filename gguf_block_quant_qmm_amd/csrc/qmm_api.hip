@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <cstdint>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 
@@ -74,10 +76,27 @@ int current_device(int *cus) {
 }
 
 // N at and above which the f16 matrix-core GEMM runs; below it the f32 GEMV
-// runs once per token.  Measured on 4096 x 4096 weights: two GEMVs tie with
-// the matrix-core GEMM at N = 2 for Q4_0 and beat it for Q6_K (whose GEMM
-// decode is the most expensive); for Q8_0 and Q4_K the GEMM already wins.
-int64_t mfma_from_n(int dtype) { return (dtype == QMM_Q4_0 || dtype == QMM_Q6_K) ? 3 : 2; }
+// arithmetic runs for every token.  Measured on 4096-, 14336- and
+// 128256-row weights:
+//   * where the several-token GEMV applies (K <= 4096): up to 4 tokens share
+//     one weight read and beat the matrix cores for Q4_0, Q8_0 and Q6_K
+//     (e.g. the 128256 x 4096 Q6_K head at N = 4: 194 vs 241 us; 14336 x 4096
+//     Q8_0: 26 vs 29 us), up to 2 for Q4_K (17 vs 21 us at N = 2, 21 vs 20 us
+//     at N = 3);
+//   * elsewhere one GEMV launch per token: two tie with the GEMM at N = 2
+//     for Q4_0 and beat it for Q6_K; for Q8_0 and Q4_K the GEMM already wins.
+// QMM_GEMM_MFMA_FROM_N = n overrides it (a measurement lever, read once).
+int64_t mfma_from_n(int dtype, int64_t M, int64_t K) {
+    static const int64_t lever = [] {
+        const char *e = getenv("QMM_GEMM_MFMA_FROM_N");
+        const long v = e ? atol(e) : 0;
+        return (int64_t)(v >= 1 && v <= 1024 ? v : 0);
+    }();
+    if (lever) return lever;
+    (void)M;
+    if (qmm::gemv_tokens_ok(dtype, K)) return dtype == QMM_Q4_K ? 3 : 5;
+    return (dtype == QMM_Q4_0 || dtype == QMM_Q6_K) ? 3 : 2;
+}
 
 }  // namespace
 
@@ -107,7 +126,7 @@ const char *qmm_strerror(int code) {
 int qmm_gemm_path(int dtype, int64_t M, int64_t K, int64_t N) {
     const int rc = check_shape(dtype, M, K, N);
     if (rc != QMM_OK) return rc;
-    return N >= mfma_from_n(dtype) ? 1 : 0;
+    return N >= mfma_from_n(dtype, M, K) ? 1 : 0;
 }
 
 int qmm_gemv(const void *w_blob, int dtype, int64_t M, int64_t K, const float *x, float *y, void *stream) {
@@ -154,6 +173,22 @@ int qmm_gemv_swiglu(const void *gate_blob, const void *up_blob, int dtype, int64
     return e == hipSuccess ? QMM_OK : QMM_ERR_LAUNCH;
 }
 
+int qmm_gemv_argmax(const void *w_blob, int dtype, int64_t M, int64_t K, const float *x, void *work,
+                    int64_t *index, float *value, void *stream) {
+    int rc = check_shape(dtype, M, K, 1);
+    if (rc != QMM_OK) return rc;
+    if (M > INT32_MAX || !qmm::gemv_fused_ok(dtype, K)) return QMM_ERR_SHAPE;
+    if (!w_blob || !x || !work || !index) return QMM_ERR_NULL;
+    if (!aligned(w_blob, 16) || !aligned(x, 16) || !aligned(work, 16) || !aligned(index, 8) ||
+        (value && !aligned(value, 4)))
+        return QMM_ERR_ALIGN;
+    int cus = 0;
+    rc = current_device(&cus);
+    if (rc != QMM_OK) return rc;
+    const hipError_t e = qmm::launch_gemv_argmax(dtype, w_blob, M, K, x, work, index, value, (hipStream_t)stream, cus);
+    return e == hipSuccess ? QMM_OK : QMM_ERR_LAUNCH;
+}
+
 int qmm_gemm(const void *w_blob, int dtype, int64_t M, int64_t K, int64_t N, const float *X, float *Y,
              void *stream) {
     int rc = check_shape(dtype, M, K, N);
@@ -164,10 +199,15 @@ int qmm_gemm(const void *w_blob, int dtype, int64_t M, int64_t K, int64_t N, con
     rc = current_device(&cus);
     if (rc != QMM_OK) return rc;
     hipError_t e = hipSuccess;
-    if (N < mfma_from_n(dtype)) {
-        // the GEMV per token: its bits, token by token (rows of X and Y stay aligned)
-        for (int64_t n = 0; n < N && e == hipSuccess; n++)
-            e = qmm::launch_gemv(dtype, w_blob, M, K, X + n * K, Y + n * M, (hipStream_t)stream, cus);
+    if (N < mfma_from_n(dtype, M, K)) {
+        // the GEMV's bits, token by token: several tokens per weight read where
+        // the layout allows, else one GEMV launch per token
+        if (N > 1 && qmm::gemv_tokens_ok(dtype, K)) {
+            e = qmm::launch_gemv_tokens(dtype, w_blob, M, K, N, X, Y, (hipStream_t)stream, cus);
+        } else {
+            for (int64_t n = 0; n < N && e == hipSuccess; n++)
+                e = qmm::launch_gemv(dtype, w_blob, M, K, X + n * K, Y + n * M, (hipStream_t)stream, cus);
+        }
     } else {
         e = qmm::launch_gemm_mfma(dtype, w_blob, M, K, N, X, Y, (hipStream_t)stream);
     }

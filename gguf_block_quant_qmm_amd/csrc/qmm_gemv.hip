@@ -323,7 +323,13 @@ __device__ __forceinline__ void x_from_lds(const floatx4 *xs, int u, float (&xv)
 //   GEMV_SWIGLU  R rows of the gate matrix and the same R rows of the up
 //                matrix; out = silu(W_gate x) * (W_up x) (same page, the
 //                fused gate + up GEMV with in-register SwiGLU).
-enum { GEMV_ONE = 0, GEMV_CONCAT = 1, GEMV_SWIGLU = 2 };
+//   GEMV_ARGMAX  R rows of one matrix; nothing is stored per row: every
+//                workgroup writes the best (value, row) of its rows to
+//                part[blockIdx.x] and gemv_argmax_finish picks the overall
+//                winner (same page, the greedy argmax GEMV that returns the
+//                index without storing the logits).  The values compared are
+//                the single-matrix kernel's f32 sums, bit for bit.
+enum { GEMV_ONE = 0, GEMV_CONCAT = 1, GEMV_SWIGLU = 2, GEMV_ARGMAX = 3 };
 constexpr int GEMV_MAX_MATS = 4;
 
 struct GemvMats {
@@ -331,7 +337,14 @@ struct GemvMats {
     float *y[GEMV_MAX_MATS];
     int64_t M[GEMV_MAX_MATS];
     int64_t g_lo[GEMV_MAX_MATS + 1];  // unused entries hold the total group count
+    float2 *part;                     // GEMV_ARGMAX: one (value, row bits) per workgroup
 };
+
+// The argmax order: a larger value wins; equal values go to the smaller row;
+// NaN never wins; row < 0 marks "nothing yet".
+__device__ __forceinline__ bool beats(float v, int row, float bv, int brow) {
+    return row >= 0 && v == v && (brow < 0 || v > bv || (v == bv && row < brow));
+}
 
 // Field i of a kernel-argument array, by selects (a dynamic index would copy
 // the argument block to scratch).
@@ -404,8 +417,16 @@ __global__ void __launch_bounds__(256) gemv_kernel(const GemvMats mats, int64_t 
         }
     };
     // results of row r of group g (every lane that calls holds the sums)
+    float best_v = 0.f;  // GEMV_ARGMAX: this thread's best row so far (rows < 2^31)
+    int best_row = -1;
     auto put = [&](int64_t g, int r, float v, float vu) {
-        if constexpr (MODE == GEMV_SWIGLU) {
+        if constexpr (MODE == GEMV_ARGMAX) {
+            const int64_t row = g * R + r;
+            if (row < mats.M[0] && beats(v, (int)row, best_v, best_row)) {
+                best_v = v;
+                best_row = (int)row;
+            }
+        } else if constexpr (MODE == GEMV_SWIGLU) {
             const int64_t row = g * R + r;
             if (row < mats.M[0]) mats.y[0][row] = silu(v) * vu;
         } else {
@@ -463,6 +484,141 @@ __global__ void __launch_bounds__(256) gemv_kernel(const GemvMats mats, int64_t 
                             put(g0 + i - slot + gi, r, sum, su);
                         }
                         __syncthreads();
+                    }
+                }
+            }
+        }
+    }
+    if constexpr (MODE == GEMV_ARGMAX) {
+        // the best of the workgroup: lane 63 of every wavefront (whole rows) or
+        // the reducing threads (split K) hold candidates
+        constexpr int NC = WAVE_ROWS ? 4 : RED_G * R;
+        __shared__ float cv[NC];
+        __shared__ int cr[NC];
+        const int c = WAVE_ROWS ? (lane == 63 ? wave : -1) : (t < NC ? t : -1);
+        if (c >= 0) {
+            cv[c] = best_v;
+            cr[c] = best_row;
+        }
+        __syncthreads();
+        if (t == 0) {
+            float bv = 0.f;
+            int br = -1;
+            const int nc = WAVE_ROWS ? nwaves : NC;
+            for (int i = 0; i < nc; i++)
+                if (beats(cv[i], cr[i], bv, br)) {
+                    bv = cv[i];
+                    br = cr[i];
+                }
+            mats.part[blockIdx.x] = float2{bv, __int_as_float(br)};
+        }
+    }
+}
+
+// The winner among the workgroups' candidates: one workgroup, a strided scan
+// per thread, then a tree over the threads with the same order.
+__global__ void __launch_bounds__(256) gemv_argmax_finish(const float2 *__restrict__ part, int nparts,
+                                                          int64_t *__restrict__ index, float *__restrict__ value) {
+    __shared__ float sv[256];
+    __shared__ int sr[256];
+    const int t = threadIdx.x;
+    float bv = 0.f;
+    int br = -1;
+    for (int i = t; i < nparts; i += 256) {
+        const float2 p = part[i];
+        const int r = __float_as_int(p.y);
+        if (beats(p.x, r, bv, br)) {
+            bv = p.x;
+            br = r;
+        }
+    }
+    sv[t] = bv;
+    sr[t] = br;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if (t < w && beats(sv[t + w], sr[t + w], sv[t], sr[t])) {
+            sv[t] = sv[t + w];
+            sr[t] = sr[t + w];
+        }
+        __syncthreads();
+    }
+    if (t == 0) {
+        *index = sr[0];
+        if (value) *value = sr[0] >= 0 ? sv[0] : __builtin_nanf("");
+    }
+}
+
+// ------------------------------------------------------- several tokens ----
+// Y[j][m] for up to NT tokens with whole-row wavefronts (K <= 4096): the
+// weights stream once for all of them, and every token's dot product is
+// computed with exactly the single-token kernel's arithmetic (the same unit
+// dot, the same cross-lane sum), so each output has the bits the GEMV
+// returns for that token alone -- a batch of draft tokens is verified with
+// the numbers greedy decoding produced (page "cera 0.5.0 src/model/llama.rs",
+// project_logits_batched: one read of the LM head for all verified
+// positions; page "cera 0.5.2 src/backend/cpu.rs": decode and prefill must
+// give the same bits).  The activations of all tokens wait in LDS; each
+// token's 64 values per lane are read back once per row group and shared by
+// the group's R rows.  Tokens past ntok are never computed or stored.
+template <int DT, int R, int D, int NT>
+__global__ void __launch_bounds__(256) gemv_tokens_kernel(const uint8_t *__restrict__ blob, int64_t M,
+                                                          int64_t row_bytes, int U, const float *__restrict__ X,
+                                                          float *__restrict__ Y, int ntok, int64_t per_owner,
+                                                          int64_t extra) {
+    constexpr int NL = Unit<DT>::NL;
+    extern __shared__ __attribute__((aligned(16))) floatx4 xs[];  // NT blocks of 16 U float4
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6), nwaves = blockDim.x >> 6;
+    const bool active = lane < U;
+    const int64_t owner = (int64_t)blockIdx.x * nwaves + wave;
+    const int64_t g0 = owner * per_owner + (owner < extra ? owner : extra);
+    const int64_t n = per_owner + (owner < extra ? 1 : 0);
+    const int64_t nrg = (M + R - 1) / R;
+    const int64_t gend = g0 + n < nrg ? g0 + n : nrg;
+    const typename Unit<DT>::Off off = Unit<DT>::lane_off(active ? lane : 0);
+    const int64_t K = (int64_t)U * 64;
+
+    uint32_t buf[D + 1][R][NL];
+    auto fetch = [&](int64_t g, uint32_t (&b)[R][NL]) {
+        const int64_t rows = g < gend ? (M - g * R < R ? M - g * R : R) : 0;
+        const Rsrc rs = make_rsrc(blob + (g < gend ? g : 0) * R * row_bytes, (uint32_t)(rows * row_bytes));
+#pragma unroll
+        for (int r = 0; r < R; r++) Unit<DT>::load(rs, (uint32_t)(r * row_bytes), off, b[r]);
+    };
+    {
+        floatx4 xr[NT][4];
+#pragma unroll
+        for (int j = 0; j < NT; j++) load_x(X + (j < ntok ? j : ntok - 1) * K, U, xr[j]);
+#pragma unroll
+        for (int s = 0; s < D; s++) fetch(g0 + s, buf[s]);
+#pragma unroll
+        for (int j = 0; j < NT; j++) store_x(xr[j], U, xs + j * 16 * U);
+    }
+    __syncthreads();
+    float xv[64];
+
+    for (int64_t i0 = 0; i0 < n; i0 += D + 1) {
+#pragma unroll
+        for (int s = 0; s <= D; s++) {
+            const int64_t i = i0 + s;
+            fetch(g0 + i + D, buf[(s + D) % (D + 1)]);
+            if (i < n) {
+                const int64_t row0 = (g0 + i) * R;
+#pragma unroll
+                for (int j = 0; j < NT; j++) {
+                    if (j < ntok) {
+                        x_from_lds<DT>(xs + j * 16 * U, active ? lane : 0, xv);
+                        float acc[R];
+#pragma unroll
+                        for (int r = 0; r < R; r++) {
+                            const float d = Unit<DT>::dot(buf[s][r], xv, off);
+                            acc[r] = wave_sum_to_lane63(active ? d : 0.f);
+                        }
+                        if (lane == 63) {
+#pragma unroll
+                            for (int r = 0; r < R; r++)
+                                if (row0 + r < M) Y[j * M + row0 + r] = acc[r];
+                        }
                     }
                 }
             }
@@ -679,9 +835,14 @@ static void launch_variant(int64_t nmax, dim3 grid, dim3 block, size_t lds, hipS
 #undef QMM_GEMV_LAUNCH
 }
 
-// The fast kernel over the row groups of `mats` (g_lo filled in by the caller).
+// Workgroup candidates the argmax workspace holds (QMM_ARGMAX_WORK_BYTES / 8).
+constexpr int64_t ARGMAX_PARTS = 4096;
+
+// The fast kernel over the row groups of `mats` (g_lo filled in by the
+// caller); *grid_out receives the workgroup count.
 template <int DT, int R, int D, int MODE>
-static hipError_t launch_fast(const GemvMats &mats, int64_t K, const float *x, hipStream_t st, int cus) {
+static hipError_t launch_fast(const GemvMats &mats, int64_t K, const float *x, hipStream_t st, int cus,
+                              int64_t *grid_out = nullptr) {
     constexpr int BS = Geo<DT>::BS, BB = Geo<DT>::BB;
     const int64_t row_bytes = (K / BS) * BB;
     const int U = (int)(K / 64);
@@ -691,6 +852,8 @@ static hipError_t launch_fast(const GemvMats &mats, int64_t K, const float *x, h
         const int64_t waves = gemv_wave_owners(DT, nrg, cus);
         const int64_t grid = (waves + 3) / 4, owners = grid * 4;
         const int64_t per = nrg / owners, extra = nrg % owners;
+        if (MODE == GEMV_ARGMAX && grid > ARGMAX_PARTS) return hipErrorInvalidConfiguration;
+        if (grid_out) *grid_out = grid;
         launch_variant<DT, R, D, true, MODE>(per + (extra ? 1 : 0), dim3((unsigned)grid), dim3(256), lds, st, mats,
                                              row_bytes, U, x, per, extra);
     } else if (U <= 256) {
@@ -714,6 +877,8 @@ static hipError_t launch_fast(const GemvMats &mats, int64_t K, const float *x, h
             if (attr != hipSuccess) return attr;
         }
         const int64_t per = nrg / grid, extra = nrg % grid;
+        if (MODE == GEMV_ARGMAX && grid > ARGMAX_PARTS) return hipErrorInvalidConfiguration;
+        if (grid_out) *grid_out = grid;
         launch_variant<DT, R, D, false, MODE>(per + (extra ? 1 : 0), dim3((unsigned)grid), dim3(64 * W), lds, st,
                                               mats, row_bytes, U, x, per, extra);
     } else {
@@ -750,8 +915,10 @@ static hipError_t launch_generic(const uint8_t *blob, int64_t M, int64_t K, cons
 // Several matrices (CONCAT) or a gate/up pair (SWIGLU) in one launch.
 template <int DT, int R, int D, int MODE>
 static hipError_t launch_mats(int n, const void *const *blobs, const int64_t *Ms, int64_t K, const float *x,
-                              float *const *ys, hipStream_t st, int cus) {
+                              float *const *ys, hipStream_t st, int cus, float2 *part = nullptr,
+                              int64_t *grid_out = nullptr) {
     GemvMats m{};
+    m.part = part;
     int64_t g = 0;
     for (int i = 0; i < GEMV_MAX_MATS; i++) {
         m.g_lo[i] = g;
@@ -763,7 +930,7 @@ static hipError_t launch_mats(int n, const void *const *blobs, const int64_t *Ms
         }
     }
     m.g_lo[GEMV_MAX_MATS] = g;
-    return launch_fast<DT, R, D, MODE>(m, K, x, st, cus);
+    return launch_fast<DT, R, D, MODE>(m, K, x, st, cus, grid_out);
 }
 
 bool gemv_fused_ok(int dtype, int64_t K) {
@@ -805,6 +972,80 @@ hipError_t launch_gemv_swiglu(int dtype, const void *gate, const void *up, int64
     case QMM_Q6_K: return launch_mats<QMM_Q6_K, 1, 2, GEMV_SWIGLU>(2, blobs, Ms, K, x, ys, st, cus);
     default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_gemv_argmax(int dtype, const void *blob, int64_t M, int64_t K, const float *x, void *work,
+                              int64_t *index, float *value, hipStream_t st, int cus) {
+    if (!gemv_fused_ok(dtype, K)) return hipErrorInvalidValue;
+    const void *blobs[1] = {blob};
+    const int64_t Ms[1] = {M};
+    float *ys[1] = {nullptr};
+    float2 *part = static_cast<float2 *>(work);
+    int64_t grid = 0;
+    hipError_t e;
+    switch (dtype) {
+    case QMM_Q4_0: e = launch_mats<QMM_Q4_0, 2, 3, GEMV_ARGMAX>(1, blobs, Ms, K, x, ys, st, cus, part, &grid); break;
+    case QMM_Q8_0: e = launch_mats<QMM_Q8_0, 1, 4, GEMV_ARGMAX>(1, blobs, Ms, K, x, ys, st, cus, part, &grid); break;
+    case QMM_Q4_K: e = launch_mats<QMM_Q4_K, 2, 3, GEMV_ARGMAX>(1, blobs, Ms, K, x, ys, st, cus, part, &grid); break;
+    case QMM_Q6_K: e = launch_mats<QMM_Q6_K, 1, 4, GEMV_ARGMAX>(1, blobs, Ms, K, x, ys, st, cus, part, &grid); break;
+    default: return hipErrorInvalidValue;
+    }
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(gemv_argmax_finish, dim3(1), dim3(256), 0, st, static_cast<const float2 *>(part), (int)grid,
+                       index, value);
+    return hipGetLastError();
+}
+
+// Tokens per pass of the several-token kernel and its shape limits.  Rows
+// per group (measured): 2 for Q4_0 and Q8_0, 1 for Q4_K and Q6_K (the
+// compiler keeps each row's decoded codes across the token loop, so more
+// rows cost occupancy).
+constexpr int GEMV_TOKENS = 4;
+
+bool gemv_tokens_ok(int dtype, int64_t K) {
+    const int64_t bs = (dtype == QMM_Q4_K || dtype == QMM_Q6_K) ? 256 : 32;
+    return fast_layout_ok(dtype, K / bs) && (K % 64) == 0 && K / 64 <= 64;
+}
+
+template <int DT, int R, int D>
+static hipError_t launch_tokens(const uint8_t *blob, int64_t M, int64_t K, int ntok, const float *X, float *Y,
+                                hipStream_t st, int cus) {
+    constexpr int BS = Geo<DT>::BS, BB = Geo<DT>::BB;
+    const int64_t row_bytes = (K / BS) * BB;
+    const int U = (int)(K / 64);
+    const int64_t nrg = (M + R - 1) / R;
+    const int64_t waves = std::min<int64_t>(nrg, (int64_t)cus * 8);
+    const int64_t grid = (waves + 3) / 4, owners = grid * 4;
+    const int64_t per = nrg / owners, extra = nrg % owners;
+    const size_t lds = (size_t)U * 256;  // per token
+    if (ntok <= 2)
+        hipLaunchKernelGGL((gemv_tokens_kernel<DT, R, D, 2>), dim3((unsigned)grid), dim3(256), 2 * lds, st, blob, M,
+                           row_bytes, U, X, Y, ntok, per, extra);
+    else
+        hipLaunchKernelGGL((gemv_tokens_kernel<DT, R, D, GEMV_TOKENS>), dim3((unsigned)grid), dim3(256),
+                           GEMV_TOKENS * lds, st, blob, M, row_bytes, U, X, Y, ntok, per, extra);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemv_tokens(int dtype, const void *blob_v, int64_t M, int64_t K, int64_t N, const float *X,
+                              float *Y, hipStream_t st, int cus) {
+    if (!gemv_tokens_ok(dtype, K)) return hipErrorInvalidValue;
+    const uint8_t *blob = static_cast<const uint8_t *>(blob_v);
+    for (int64_t n0 = 0; n0 < N; n0 += GEMV_TOKENS) {
+        const int nt = (int)std::min<int64_t>(GEMV_TOKENS, N - n0);
+        const float *Xp = X + n0 * K;
+        float *Yp = Y + n0 * M;
+        hipError_t e;
+        switch (dtype) {
+        case QMM_Q4_0: e = launch_tokens<QMM_Q4_0, 2, 1>(blob, M, K, nt, Xp, Yp, st, cus); break;
+        case QMM_Q8_0: e = launch_tokens<QMM_Q8_0, 2, 1>(blob, M, K, nt, Xp, Yp, st, cus); break;
+        case QMM_Q4_K: e = launch_tokens<QMM_Q4_K, 1, 1>(blob, M, K, nt, Xp, Yp, st, cus); break;
+        case QMM_Q6_K: e = launch_tokens<QMM_Q6_K, 1, 1>(blob, M, K, nt, Xp, Yp, st, cus); break;
+        default: return hipErrorInvalidValue;
+        }
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_gemv(int dtype, const void *blob_v, int64_t M, int64_t K, const float *x, float *y,

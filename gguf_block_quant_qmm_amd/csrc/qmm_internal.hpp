@@ -20,6 +20,19 @@ hipError_t launch_gemv_swiglu(int dtype, const void *gate, const void *up, int64
                               float *out, hipStream_t st, int cus);
 bool gemv_fused_ok(int dtype, int64_t K);
 
+// index = the smallest row with the largest f32 GEMV output (bits of
+// launch_gemv), value = that output; two launches (rows, then the winner
+// among QMM_ARGMAX_WORK_BYTES / 8 workgroup candidates in `work`).
+hipError_t launch_gemv_argmax(int dtype, const void *blob, int64_t M, int64_t K, const float *x, void *work,
+                              int64_t *index, float *value, hipStream_t st, int cus);
+
+// Y[N][M] for a few tokens with the GEMV's f32 arithmetic, the weights read
+// once per 4 tokens; each Y[n] has the bits launch_gemv gives for X[n].
+// Needs gemv_tokens_ok(dtype, K) (whole-row wavefronts: K <= 4096).
+bool gemv_tokens_ok(int dtype, int64_t K);
+hipError_t launch_gemv_tokens(int dtype, const void *blob, int64_t M, int64_t K, int64_t N, const float *X,
+                              float *Y, hipStream_t st, int cus);
+
 // Y[N][M] = X W^T on the matrix cores (f16 operands, f32 accumulation).
 hipError_t launch_gemm_mfma(int dtype, const void *blob, int64_t M, int64_t K, int64_t N, const float *X,
                             float *Y, hipStream_t st);

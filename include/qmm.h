@@ -120,14 +120,41 @@ int qmm_gemv_concat(int n, const void *const *w_blobs, const int64_t *Ms, int dt
 int qmm_gemv_swiglu(const void *gate_blob, const void *up_blob, int dtype, int64_t M, int64_t K,
                     const float *x, float *out, void *stream);
 
+/* Greedy decoding: the argmax over the GEMV's outputs, without storing them
+ * (page "cera 0.5.2 src/backend/cpu.rs", the greedy argmax GEMV):
+ *     *index = the smallest m with y[m] = max_m' y[m'],  *value = y[*index]
+ * where y is exactly the f32 output qmm_gemv returns (so the choice matches
+ * argmax over qmm_gemv's bits).  NaN outputs never win; if every output is
+ * NaN, *index = -1 and *value = NaN.  Ties: the smallest index (the pages
+ * do not say; this is a reading).
+ *   w_blob, dtype, M, K, x  as for qmm_gemv; M <= 2^31 - 1
+ *   work    device scratch of QMM_ARGMAX_WORK_BYTES bytes, 16-B aligned,
+ *           caller-owned; needs no initial value; clobbered
+ *   index   device int64, 8-B aligned
+ *   value   device f32 or NULL
+ * Two launches on `stream` (the rows, then the winner).  Needs K a multiple
+ * of 64, at most 16384, and an even number of blocks per row for Q4_0, Q8_0
+ * and Q6_K; otherwise QMM_ERR_SHAPE.  Concurrent calls need separate work
+ * buffers. */
+#define QMM_ARGMAX_WORK_BYTES 32768
+int qmm_gemv_argmax(const void *w_blob, int dtype, int64_t M, int64_t K, const float *x,
+                    void *work, int64_t *index, float *value, void *stream);
+
 /* Prefill / verify GEMM over N tokens (page "cera 0.3.1 src/model/gpu_lfm2.rs",
  * mul_mat_reg_tile: weights decoded once per k-tile and reused across all
  * token columns):  Y[n][m] = sum_k W[m][k] * X[n][k].
  *   X       device f32 [N][K] row-major, 16-B aligned
  *   Y       device f32 [N][M] row-major, 4-B aligned; overwritten
- * Below a per-dtype crossover N (3 for Q4_0 and Q6_K, 2 for Q8_0 and Q4_K,
- * measured) it runs the GEMV once per token (same bits as qmm_gemv).  The
- * path qmm_gemm_path names: 0 = all-f32 arithmetic (tolerance 1e-5 of
+ * Below a measured crossover N it computes every token with the GEMV's f32
+ * arithmetic, so Y[n] has exactly the bits qmm_gemv returns for X[n] (page
+ * "cera 0.5.0 src/model/llama.rs", project_logits_batched: verifying drafted
+ * tokens in one pass over the LM head; page "cera 0.5.2
+ * src/backend/cpu.rs": decode and prefill must agree bit for bit).  With K a
+ * multiple of 64 up to 4096 and an even number of blocks per row (Q4_0, Q8_0,
+ * Q6_K) up to 4 tokens share one read of the weights and the crossover is
+ * N = 5 (Q4_0, Q8_0, Q6_K) or 3 (Q4_K); otherwise each token is one GEMV
+ * launch and the crossover is 3 (Q4_0, Q6_K) or 2 (Q8_0, Q4_K).  The path
+ * qmm_gemm_path names: 0 = all-f32 arithmetic (tolerance 1e-5 of
  * sum |w x|), 1 = weights and activations rounded to f16 and multiplied on
  * the matrix cores with f32 accumulation (tolerance 2e-3 of sum |w x|; needs
  * |w|, |x| < 65504). */

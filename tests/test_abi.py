@@ -88,13 +88,20 @@ def test_gemm_rejects(args, code):
 
 
 def test_gemm_path_selection():
-    # below the per-dtype crossover the f32 GEMV runs per token
+    # below the crossover every token gets the GEMV's f32 arithmetic
     assert q.gemm_path(q.QMM_Q4_K, 14336, 4096, 1) == 0
-    assert q.gemm_path(q.QMM_Q4_K, 14336, 4096, 2) == 1
-    assert q.gemm_path(q.QMM_Q8_0, 4096, 4096, 2) == 1
-    assert q.gemm_path(q.QMM_Q4_0, 4096, 4096, 2) == 0
-    assert q.gemm_path(q.QMM_Q6_K, 4096, 4096, 2) == 0
-    assert q.gemm_path(q.QMM_Q6_K, 4096, 4096, 3) == 1
+    # K <= 4096: several tokens per weight read, crossover 5 (Q4_0, Q8_0, Q6_K) or 3 (Q4_K)
+    assert q.gemm_path(q.QMM_Q4_K, 14336, 4096, 2) == 0
+    assert q.gemm_path(q.QMM_Q4_K, 14336, 4096, 3) == 1
+    for dt in (q.QMM_Q4_0, q.QMM_Q8_0, q.QMM_Q6_K):
+        assert q.gemm_path(dt, 4096, 4096, 4) == 0
+        assert q.gemm_path(dt, 4096, 4096, 5) == 1
+    assert q.gemm_path(q.QMM_Q6_K, 128256, 4096, 4) == 0
+    # K > 4096: one GEMV launch per token, crossover 3 (Q4_0, Q6_K) or 2 (Q8_0, Q4_K)
+    assert q.gemm_path(q.QMM_Q4_0, 4096, 14336, 2) == 0
+    assert q.gemm_path(q.QMM_Q4_0, 4096, 14336, 3) == 1
+    assert q.gemm_path(q.QMM_Q8_0, 4096, 8192, 2) == 1
+    assert q.gemm_path(q.QMM_Q6_K, 4096, 8192, 2) == 0
     assert q.gemm_path(q.QMM_Q4_K, 14336, 4096, 512) == 1
     assert q.gemm_path(q.QMM_Q4_K, 14336, 100, 512) == q.QMM_ERR_SHAPE
     assert q.tolerance(q.QMM_Q4_0, 4096, 4096, 1) == 1e-5
@@ -158,3 +165,28 @@ def test_fused_calls_without_gpu_report_device():
         pytest.skip("a GPU is present; covered by the GPU tests")
     assert _concat(2, [A16, A16], [8, 8], 2, 64, A16, [A16, A16]) == q.QMM_ERR_DEVICE
     assert q.lib().qmm_gemv_swiglu(A16, A16, 2, 8, 64, A16, A16, None) == q.QMM_ERR_DEVICE
+
+
+@pytest.mark.parametrize("args,code", [
+    ((A16, 5, 8, 64, A16, A16, A16, A16), q.QMM_ERR_DTYPE),
+    ((A16, 2, 0, 64, A16, A16, A16, A16), q.QMM_ERR_SHAPE),
+    ((A16, 2, 8, 96, A16, A16, A16, A16), q.QMM_ERR_SHAPE),        # odd number of Q4_0 blocks
+    ((A16, 12, 8, 16640, A16, A16, A16, A16), q.QMM_ERR_SHAPE),    # K > 16384
+    ((A16, 2, 1 << 31, 64, A16, A16, A16, A16), q.QMM_ERR_SHAPE),  # M beyond int32
+    ((0, 2, 8, 64, A16, A16, A16, A16), q.QMM_ERR_NULL),
+    ((A16, 2, 8, 64, 0, A16, A16, A16), q.QMM_ERR_NULL),
+    ((A16, 2, 8, 64, A16, 0, A16, A16), q.QMM_ERR_NULL),
+    ((A16, 2, 8, 64, A16, A16, 0, A16), q.QMM_ERR_NULL),
+    ((A16, 2, 8, 64, A16, A16 + 8, A16, A16), q.QMM_ERR_ALIGN),
+    ((A16, 2, 8, 64, A16, A16, A16 + 4, A16), q.QMM_ERR_ALIGN),
+    ((A16, 2, 8, 64, A16, A16, A16, A16 + 2), q.QMM_ERR_ALIGN),
+])
+def test_gemv_argmax_rejects(args, code):
+    assert q.lib().qmm_gemv_argmax(*args, None) == code
+
+
+def test_argmax_without_value_and_gpu_reports_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; covered by the GPU tests")
+    assert q.lib().qmm_gemv_argmax(A16, 2, 8, 64, A16, A16, A16, None, None) == q.QMM_ERR_DEVICE

@@ -213,3 +213,89 @@ def test_fused_calls_are_deterministic():
         runs.append([t.cpu() for t in ys + [out]])
     for a, b in zip(*runs):
         assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------------ argmax
+#
+# qmm_gemv_argmax must pick exactly argmax over qmm_gemv's own f32 outputs
+# (smallest index among equal maxima) and return that output's bits; against
+# the oracle the chosen row must be a valid maximum: y64[i] >= y64[best] -
+# tau * (S[i] + S[best]), and the very row when the exact runner-up trails by
+# more than that.
+
+def first_argmax(y):
+    y = np.where(np.isnan(y), -np.inf, y)
+    return int(np.flatnonzero(y == y.max())[0])
+
+
+def run_argmax(dt, blob_d, M, K, x_d):
+    work = torch.empty(q.QMM_ARGMAX_WORK_BYTES, dtype=torch.uint8, device="cuda")
+    idx = torch.full((1,), -7, dtype=torch.int64, device="cuda")
+    val = torch.full((1,), float("nan"), device="cuda")
+    q.qmm_gemv_argmax(blob_d, dt, M, K, x_d, work, idx, val)
+    torch.cuda.synchronize()
+    return int(idx.item()), val.cpu().numpy()[0]
+
+
+def check_argmax(dt, blob, M, K, x, label, rows_sample=None):
+    bd, xd = to_dev(blob), to_dev(x.reshape(-1))
+    i, v = run_argmax(dt, bd, M, K, xd)
+    y = gemv(dt, bd, M, K, xd).cpu().numpy()
+    torch.cuda.synchronize()
+    want = first_argmax(y)
+    assert i == want, f"{label}: index {i}, argmax of qmm_gemv's output {want}"
+    assert np.float32(v).tobytes() == y[want].tobytes(), f"{label}: value is not qmm_gemv's output bits"
+    oi, obest, os_ = oracle.argmax(dt, blob, M, K, x)
+    _, Y64, S = oracle.matmul(dt, blob, M, K, x, rows=[i])
+    assert Y64[0, 0] >= obest - TAU * (S[0, 0] + os_), f"{label}: row {i} is not a maximum (oracle {oi})"
+    return i, oi
+
+
+@pytest.mark.parametrize("dt", DTYPES, ids=NAME.get)
+def test_argmax_small(dt):
+    for c, (M, K) in enumerate(swiglu_shapes(dt) + ([(40001, 4096)] if bs_of(dt) == 32 else [(40001, 2048)])):
+        blob = make_blob(dt, M, K, rng_for(880 + dt, c))
+        x = make_x(1, K, rng_for(880 + dt, 100 + c))
+        check_argmax(dt, blob, M, K, x, f"{NAME[dt]} argmax M={M} K={K}")
+
+
+@pytest.mark.parametrize("dt", DTYPES, ids=NAME.get)
+def test_argmax_ties_and_nan(dt):
+    M, K = 3000, 4096
+    blob = make_blob(dt, M, K, rng_for(890 + dt, 0))
+    x = make_x(1, K, rng_for(890 + dt, 1))
+    rb = blob.size // M
+    rows = blob.reshape(M, rb)
+    # the winning row copied to a later and an earlier position: the copies
+    # give bit-identical outputs, and the earliest copy wins
+    w = first_argmax(gemv(dt, to_dev(blob), M, K, to_dev(x.reshape(-1))).cpu().numpy())
+    for dst in (M - 1, w + 1 if w + 1 < M else 0, 17):
+        rows[dst] = rows[w]
+    i, _ = check_argmax(dt, blob, M, K, x, f"{NAME[dt]} argmax with copies of the winner")
+    assert i == min(w, 17), f"{NAME[dt]}: equal maxima at rows {w}, 17, ...: got {i}"
+    # a NaN scale makes that row's output NaN: it never wins
+    off = {q.QMM_Q4_0: 0, q.QMM_Q8_0: 0, q.QMM_Q4_K: 0, q.QMM_Q6_K: 208}[dt]
+    nan = np.frombuffer(np.float16(np.nan).tobytes(), np.uint8)
+    for r in (0, 17, min(w, 17)):
+        rows[r, off:off + 2] = nan
+    bd, xd = to_dev(blob), to_dev(x.reshape(-1))
+    i, v = run_argmax(dt, bd, M, K, xd)
+    y = gemv(dt, bd, M, K, xd).cpu().numpy()
+    assert np.isnan(y[17]) and i == first_argmax(y) and not np.isnan(v)
+    # every output NaN: index -1, value NaN
+    allnan = blob.copy().reshape(M, rb)
+    allnan[:, off:off + 2] = nan
+    i, v = run_argmax(dt, to_dev(allnan.reshape(-1)), M, K, xd)
+    assert i == -1 and np.isnan(v)
+
+
+def test_argmax_lm_head_full_size():
+    """The Q6_K LM head, 128256 x 4096, against the oracle's exact argmax."""
+    dt, M, K = q.QMM_Q6_K, 128256, 4096
+    blob = make_blob(dt, M, K, rng_for(5, 0))
+    x = make_x(1, K, rng_for(5, 1))
+    i, oi = check_argmax(dt, blob, M, K, x, "Q6_K LM head argmax")
+    _, Y64, S = oracle.matmul(dt, blob, M, K, x)
+    top2 = np.sort(Y64[0])[-2:]
+    if top2[1] - top2[0] > 2 * TAU * S.max():
+        assert i == oi, f"clear winner {oi}, got {i}"

@@ -226,3 +226,49 @@ def test_workload_full_size(wid):
         check(Yg[:, rows], Y64, S, q.tolerance(dt, M, K, N), f"{label} N={N}")
     del blob_d
     torch.cuda.empty_cache()
+
+
+# ------------------------------------------------- few tokens, f32 path ----
+#
+# Below the crossover qmm_gemm gives every token the GEMV's f32 arithmetic:
+# Y[n] must equal qmm_gemv(X[n]) bit for bit (several tokens share one weight
+# read where K <= 4096), and lie within 1e-5 * S of the oracle.
+
+def few_token_shapes(dt):
+    if bs_of(dt) == 32:
+        return [(1, 64), (67, 256), (1001, 1024), (300, 4096), (129, 8192)]
+    return [(1, 256), (67, 512), (1001, 1024), (300, 4096), (129, 8192)]
+
+
+@pytest.mark.parametrize("dt", DTYPES, ids=NAME.get)
+def test_gemm_few_tokens_match_gemv_bitwise(dt):
+    for i, (M, K) in enumerate(few_token_shapes(dt)):
+        blob = make_blob(dt, M, K, rng_for(640 + dt, i))
+        bd = to_dev(blob)
+        for N in range(2, 9):
+            if q.gemm_path(dt, M, K, N) != 0:
+                break
+            X = make_x(N, K, rng_for(640 + dt, 100 * N + i))
+            Yg = gpu_gemm(dt, bd, M, K, X)
+            for n in range(N):
+                yn = gpu_gemv(dt, bd, M, K, X[n])
+                assert np.array_equal(Yg[n].view(np.uint32), yn.view(np.uint32)), \
+                    f"{NAME[dt]} M={M} K={K} N={N}: token {n} differs from qmm_gemv"
+            _, Y64, S = oracle.matmul(dt, blob, M, K, X)
+            check(Yg, Y64, S, 1e-5, f"{NAME[dt]} few tokens M={M} K={K} N={N}")
+
+
+def test_lm_head_verify_batch_matches_decode():
+    """Verifying 4 drafted positions on the Q6_K LM head (128256 x 4096) gives
+    each position exactly the logits greedy decoding computed."""
+    dt, M, K, N = q.QMM_Q6_K, 128256, 4096, 4
+    assert q.gemm_path(dt, M, K, N) == 0
+    blob = make_blob(dt, M, K, rng_for(5, 0))
+    bd = to_dev(blob)
+    X = make_x(N, K, rng_for(5, 40))
+    Yg = gpu_gemm(dt, bd, M, K, X)
+    for n in range(N):
+        assert np.array_equal(Yg[n].view(np.uint32), gpu_gemv(dt, bd, M, K, X[n]).view(np.uint32))
+    rows = sample_rows(M, 256, 41)
+    _, Y64, S = oracle.matmul(dt, blob, M, K, X, rows=rows)
+    check(Yg[:, rows], Y64, S, 1e-5, "Q6_K LM head N=4")
