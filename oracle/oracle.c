@@ -33,6 +33,12 @@
  * Block formats (all little-endian; f16 is IEEE binary16, decoded exactly,
  * subnormals included, Inf/NaN propagate):
  *   Q8_0 (type 8,  32 weights, 34 B): d f16 @0, q int8[32] @2;   w = d*q
+ *   Q4_1 (type 3,  32 weights, 20 B): d f16 @0, m f16 @2, qs u8[16] @4;
+ *        nibbles placed as in Q4_0;  w = d*q + m
+ *        (the pages name the format and its GEMV -- page "cera 0.5.2
+ *         src/backend/cpu.rs", gemv_q4_1_f32 -- but print no layout;
+ *         READING: the standard GGUF Q4_1 block, "parity unpinned" against
+ *         the pages, pinned to hand-built fixtures written from the reading)
  *   Q4_0 (type 2,  32 weights, 18 B): d f16 @0, qs u8[16] @2;
  *        element e<16 is the low nibble of qs[e], e>=16 the high nibble of
  *        qs[e-16];  w = d*(q-8)
@@ -77,6 +83,7 @@
 #endif
 
 #define OR_Q4_0 2
+#define OR_Q4_1 3
 #define OR_Q8_0 8
 #define OR_Q4_K 12
 #define OR_Q6_K 14
@@ -86,6 +93,7 @@
 int oracle_block_elems(int dtype) {
     switch (dtype) {
     case OR_Q4_0: return 32;
+    case OR_Q4_1: return 32;
     case OR_Q8_0: return 32;
     case OR_Q4_K: return 256;
     case OR_Q6_K: return 256;
@@ -96,6 +104,7 @@ int oracle_block_elems(int dtype) {
 int oracle_block_bytes(int dtype) {
     switch (dtype) {
     case OR_Q4_0: return 18;
+    case OR_Q4_1: return 20;
     case OR_Q8_0: return 34;
     case OR_Q4_K: return 144;
     case OR_Q6_K: return 210;
@@ -180,10 +189,20 @@ static void dequant_q6_k(const uint8_t *b, double *w) {
     }
 }
 
+static void dequant_q4_1(const uint8_t *b, double *w) {
+    double d = half_at(b), m = half_at(b + 2);
+    const uint8_t *qs = b + 4;
+    for (int j = 0; j < 32; j++) {
+        int q = (j < 16) ? (qs[j] & 15) : (qs[j - 16] >> 4);
+        w[j] = d * (double)q + m;
+    }
+}
+
 static int dequant_block(int dtype, const uint8_t *b, double *w) {
     switch (dtype) {
     case OR_Q8_0: dequant_q8_0(b, w); return 0;
     case OR_Q4_0: dequant_q4_0(b, w); return 0;
+    case OR_Q4_1: dequant_q4_1(b, w); return 0;
     case OR_Q4_K: dequant_q4_k(b, w); return 0;
     case OR_Q6_K: dequant_q6_k(b, w); return 0;
     default: return -2;

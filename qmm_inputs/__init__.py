@@ -8,6 +8,9 @@ imports neither the oracle nor the HIP library.
 Distributions (the workload table the inputs stand in for):
   Q8_0: d ~ U[0.002, 0.02], q ~ U{-127..127}
   Q4_0: d ~ U[0.005, 0.05], 16 uniform nibble bytes
+  Q4_1: d ~ U[0.005, 0.05], m = -d * U[6, 9] (a block minimum below zero, so
+        the weights straddle zero as a quantized zero-mean row does), 16
+        uniform nibble bytes
   Q4_K: d, dmin ~ U[5e-4, 2e-3], 12 uniform scale bytes (so every 6-bit
         sc/m is uniform on 0..63), 128 uniform nibble bytes
   Q6_K: d ~ U[2e-4, 1e-3], uniform ql/qh bytes (so q is uniform on 0..63),
@@ -23,11 +26,11 @@ from __future__ import annotations
 
 import numpy as np
 
-Q4_0, Q8_0, Q4_K, Q6_K = 2, 8, 12, 14
-NAMES = {Q4_0: "Q4_0", Q8_0: "Q8_0", Q4_K: "Q4_K", Q6_K: "Q6_K"}
+Q4_0, Q4_1, Q8_0, Q4_K, Q6_K = 2, 3, 8, 12, 14
+NAMES = {Q4_0: "Q4_0", Q4_1: "Q4_1", Q8_0: "Q8_0", Q4_K: "Q4_K", Q6_K: "Q6_K"}
 BY_NAME = {v: k for k, v in NAMES.items()}
 # (weights per block, bytes per block) -- the GGUF block geometry.
-GEOMETRY = {Q4_0: (32, 18), Q8_0: (32, 34), Q4_K: (256, 144), Q6_K: (256, 210)}
+GEOMETRY = {Q4_0: (32, 18), Q4_1: (32, 20), Q8_0: (32, 34), Q4_K: (256, 144), Q6_K: (256, 210)}
 
 
 def rng_for(workload_id: int, tensor_id: int = 0) -> np.random.Generator:
@@ -58,6 +61,11 @@ def make_blob(dtype: int, M: int, K: int, rng: np.random.Generator) -> np.ndarra
     elif dtype == Q4_0:
         blk[:, 0:2] = _f16_bytes(rng.uniform(0.005, 0.05, nblk).astype(np.float32))
         blk[:, 2:18] = rng.integers(0, 256, size=(nblk, 16), dtype=np.uint8)
+    elif dtype == Q4_1:
+        d = rng.uniform(0.005, 0.05, nblk).astype(np.float32)
+        blk[:, 0:2] = _f16_bytes(d)
+        blk[:, 2:4] = _f16_bytes((-d * rng.uniform(6.0, 9.0, nblk)).astype(np.float32))
+        blk[:, 4:20] = rng.integers(0, 256, size=(nblk, 16), dtype=np.uint8)
     elif dtype == Q4_K:
         blk[:, 0:2] = _f16_bytes(rng.uniform(5e-4, 2e-3, nblk).astype(np.float32))
         blk[:, 2:4] = _f16_bytes(rng.uniform(5e-4, 2e-3, nblk).astype(np.float32))

@@ -35,7 +35,7 @@ import oracle
 from qmm_inputs import make_blob, make_x, rng_for
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
-DTYPES = (oracle.Q4_0, oracle.Q8_0, oracle.Q4_K, oracle.Q6_K)
+DTYPES = (oracle.Q4_0, oracle.Q8_0, oracle.Q4_K, oracle.Q6_K, oracle.Q4_1)
 
 
 # ----------------------------------------------------------------- fixtures
@@ -126,7 +126,7 @@ def _f16(a: np.ndarray) -> np.ndarray:
 
 def closed_form_row_sums(dt: int, blob: np.ndarray, M: int, K: int) -> np.ndarray:
     """y = W . ones, from the block fields: scale x (sum of integer codes)."""
-    bs, bb = {oracle.Q4_0: (32, 18), oracle.Q8_0: (32, 34),
+    bs, bb = {oracle.Q4_0: (32, 18), oracle.Q4_1: (32, 20), oracle.Q8_0: (32, 34),
               oracle.Q4_K: (256, 144), oracle.Q6_K: (256, 210)}[dt]
     nb = K // bs
     B = blob[: M * nb * bb].reshape(M, nb, bb)
@@ -139,6 +139,12 @@ def closed_form_row_sums(dt: int, blob: np.ndarray, M: int, K: int) -> np.ndarra
         qs = B[:, :, 2:18].astype(np.int64)
         qsum = (qs & 15).sum(axis=2) + (qs >> 4).sum(axis=2)
         per_block = d * (qsum - 8 * 32)
+    elif dt == oracle.Q4_1:
+        d = _f16(np.ascontiguousarray(B[:, :, 0:2])).reshape(M, nb)
+        m = _f16(np.ascontiguousarray(B[:, :, 2:4])).reshape(M, nb)
+        qs = B[:, :, 4:20].astype(np.int64)
+        qsum = (qs & 15).sum(axis=2) + (qs >> 4).sum(axis=2)
+        per_block = d * qsum + 32 * m
     elif dt == oracle.Q4_K:
         d = _f16(np.ascontiguousarray(B[:, :, 0:2])).reshape(M, nb)
         dmin = _f16(np.ascontiguousarray(B[:, :, 2:4])).reshape(M, nb)
@@ -200,6 +206,9 @@ def exact_weights(dt: int, blk: bytes) -> list:
         lows = [(c & 0x0F) - 8 for c in blk[2:18]]
         highs = [(c >> 4) - 8 for c in blk[2:18]]
         return [d * v for v in lows + highs]
+    if dt == oracle.Q4_1:
+        d, m = _h(blk, 0), _h(blk, 2)
+        return [d * (c & 0x0F) + m for c in blk[4:20]] + [d * (c >> 4) + m for c in blk[4:20]]
     if dt == oracle.Q4_K:
         d, dmin = _h(blk, 0), _h(blk, 2)
         s = blk[4:16]
@@ -282,10 +291,10 @@ def pin_bruteforce(L=None):
 
 def _double_scales(dt: int, blob: np.ndarray, M: int, K: int) -> np.ndarray:
     """Blob with every f16 scale (d, and dmin for Q4_K) multiplied by 2."""
-    bs, bb = {oracle.Q4_0: (32, 18), oracle.Q8_0: (32, 34),
+    bs, bb = {oracle.Q4_0: (32, 18), oracle.Q4_1: (32, 20), oracle.Q8_0: (32, 34),
               oracle.Q4_K: (256, 144), oracle.Q6_K: (256, 210)}[dt]
     B = blob.copy().reshape(-1, bb)
-    offs = {oracle.Q4_0: [0], oracle.Q8_0: [0], oracle.Q4_K: [0, 2], oracle.Q6_K: [208]}[dt]
+    offs = {oracle.Q4_0: [0], oracle.Q4_1: [0, 2], oracle.Q8_0: [0], oracle.Q4_K: [0, 2], oracle.Q6_K: [208]}[dt]
     for o in offs:
         h = np.ascontiguousarray(B[:, o:o + 2]).view("<f2").reshape(-1)
         h2 = (h.astype(np.float32) * 2).astype("<f2")
@@ -348,8 +357,8 @@ def pin_half(L=None):
 
 
 def pin_sizes(L=None):
-    assert [oracle.block_bytes(d, L) for d in DTYPES] == [18, 34, 144, 210]
-    assert [oracle.block_elems(d, L) for d in DTYPES] == [32, 32, 256, 256]
+    assert [oracle.block_bytes(d, L) for d in DTYPES] == [18, 34, 144, 210, 20]
+    assert [oracle.block_elems(d, L) for d in DTYPES] == [32, 32, 256, 256, 32]
     # tied Q6_K head, hidden size 2048 x vocab 128256, "~205 MiB" on the page
     head = oracle.blob_bytes(oracle.Q6_K, 128256, 2048, L)
     assert head == 215_470_080 and round(head / 2**20) == 205

@@ -17,8 +17,15 @@ import pins
 SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
 
 MUTANTS = {
+    "q4_1_min_sign": ("w[j] = d * (double)q + m;", "w[j] = d * (double)q - m;"),
+    "q4_1_min_offset": ("double d = half_at(b), m = half_at(b + 2);", "double d = half_at(b), m = half_at(b + 4);"),
+    "q4_1_codes_at_2": ("const uint8_t *qs = b + 4;\n    for (int j = 0; j < 32; j++) {\n        int q = (j < 16) ? (qs[j] & 15) : (qs[j - 16] >> 4);\n        w[j] = d * (double)q + m;",
+                        "const uint8_t *qs = b + 2;\n    for (int j = 0; j < 32; j++) {\n        int q = (j < 16) ? (qs[j] & 15) : (qs[j - 16] >> 4);\n        w[j] = d * (double)q + m;"),
     "q4_0_offset": ("w[j] = d * (double)(q - 8);", "w[j] = d * (double)(q - 7);"),
-    "q4_0_nibble_halves": ("(j < 16) ? (qs[j] & 15) : (qs[j - 16] >> 4)", "(j < 16) ? (qs[j] >> 4) : (qs[j - 16] & 15)"),
+    "q4_0_nibble_halves": ("(j < 16) ? (qs[j] & 15) : (qs[j - 16] >> 4);\n        w[j] = d * (double)(q - 8);",
+                           "(j < 16) ? (qs[j] >> 4) : (qs[j - 16] & 15);\n        w[j] = d * (double)(q - 8);"),
+    "q4_1_nibble_halves": ("(j < 16) ? (qs[j] & 15) : (qs[j - 16] >> 4);\n        w[j] = d * (double)q + m;",
+                           "(j < 16) ? (qs[j] >> 4) : (qs[j - 16] & 15);\n        w[j] = d * (double)q + m;"),
     "q8_0_unsigned": ("(double)(int8_t)b[2 + j]", "(double)(uint8_t)b[2 + j]"),
     "q8_0_off_by_one": ("(int8_t)b[2 + j]", "(int8_t)b[1 + j]"),
     "q4_k_scale_mask": ("*sc = s[i] & 63;", "*sc = s[i] & 31;"),
