@@ -24,6 +24,7 @@ std::mutex g_dev_mu;
 int block_elems(int dtype) {
     switch (dtype) {
     case QMM_Q4_0:
+    case QMM_Q4_1:
     case QMM_Q8_0: return 32;
     case QMM_Q4_K:
     case QMM_Q6_K: return 256;
@@ -34,6 +35,7 @@ int block_elems(int dtype) {
 int block_bytes(int dtype) {
     switch (dtype) {
     case QMM_Q4_0: return 18;
+    case QMM_Q4_1: return 20;
     case QMM_Q8_0: return 34;
     case QMM_Q4_K: return 144;
     case QMM_Q6_K: return 210;
@@ -81,8 +83,8 @@ int current_device(int *cus) {
 //   * where the several-token GEMV applies (K <= 4096): up to 4 tokens share
 //     one weight read and beat the matrix cores for Q4_0, Q8_0 and Q6_K
 //     (e.g. the 128256 x 4096 Q6_K head at N = 4: 194 vs 241 us; 14336 x 4096
-//     Q8_0: 26 vs 29 us), up to 2 for Q4_K (17 vs 21 us at N = 2, 21 vs 20 us
-//     at N = 3);
+//     Q8_0: 26 vs 29 us) and Q4_1 (14336 x 4096 at N = 4: 22.6 vs 24.4 us), up
+//     to 2 for Q4_K (17 vs 21 us at N = 2, 21 vs 20 us at N = 3);
 //   * elsewhere one GEMV launch per token: two tie with the GEMM at N = 2
 //     for Q4_0 and beat it for Q6_K; for Q8_0 and Q4_K the GEMM already wins.
 // QMM_GEMM_MFMA_FROM_N = n overrides it (a measurement lever, read once).
@@ -114,7 +116,7 @@ const char *qmm_strerror(int code) {
     switch (code) {
     case QMM_OK: return "ok";
     case QMM_ERR_NULL: return "a required pointer is NULL";
-    case QMM_ERR_DTYPE: return "unsupported dtype (expected Q4_0=2, Q8_0=8, Q4_K=12 or Q6_K=14)";
+    case QMM_ERR_DTYPE: return "unsupported dtype (expected Q4_0=2, Q4_1=3, Q8_0=8, Q4_K=12 or Q6_K=14)";
     case QMM_ERR_SHAPE: return "bad shape (need M >= 1, N >= 1, K a positive multiple of the block size)";
     case QMM_ERR_ALIGN: return "misaligned pointer (blob and x/X need 16-byte, y/Y 4-byte alignment)";
     case QMM_ERR_DEVICE: return "no current HIP device, or it is not gfx950";

@@ -71,6 +71,33 @@ template <bool GEN> struct WTile<QMM_Q4_0, GEN> {
     }
 };
 
+template <bool GEN> struct WTile<QMM_Q4_1, GEN> {
+    // part = block 2*(k0/64) + part; 20 bytes: d, m, 16 nibble bytes.  Every
+    // block of a 16-byte aligned blob is dword aligned (20 = 5 dwords).
+    static constexpr int NDW = 5;
+    __device__ static bool exists(int64_t K, int64_t k0, int part) { return k0 + 32 * part < K; }
+    __device__ static void load(const uint8_t *row, int64_t k0, int part, uint32_t (&v)[NDW]) {
+        const uint8_t *p = row + 20 * (k0 / 32 + part);
+        if (GEN) fetch_bytes(p, 20, v);
+        else fetch_al(p, v);
+    }
+    __device__ static void store(const uint32_t (&v)[NDW], int part, _Float16 *wrow) {
+        const float d = h2f(v[0]), m = h2f(v[0] >> 16);
+        half8 lo[2], hi[2];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+#pragma unroll
+            for (int c = 0; c < 4; c++) {
+                const int e = 4 * i + c;
+                lo[e >> 3][e & 7] = (_Float16)fmaf(d, (float)((v[1 + i] >> (8 * c)) & 15u), m);
+                hi[e >> 3][e & 7] = (_Float16)fmaf(d, (float)((v[1 + i] >> (8 * c + 4)) & 15u), m);
+            }
+        }
+        half8 *dst = reinterpret_cast<half8 *>(wrow + 32 * part);
+        dst[0] = lo[0]; dst[1] = lo[1]; dst[2] = hi[0]; dst[3] = hi[1];
+    }
+};
+
 template <bool GEN> struct WTile<QMM_Q8_0, GEN> {
     // part = block 2*(k0/64) + part; 34 bytes: d, 32 int8
     static constexpr int NDW = 9;
@@ -539,6 +566,28 @@ template <> struct PDec<QMM_Q4_0> {
     }
 };
 
+template <> struct PDec<QMM_Q4_1> {
+    // lane half kh: block 2 kt + kh (20 bytes, dword aligned: r[0] = d|m,
+    // r[1..4] = qs); step s: k = 32 kh + 8 s + sigma(j), as for Q4_0
+    static constexpr int NW = 5;
+    static constexpr bool SWAP = true;
+    __device__ static int xpos(int c4) { return 16 * ((c4 >> 1) & 3) + 8 * (c4 >> 3) + 4 * (c4 & 1); }
+    struct State {};
+    __device__ static void loadb(Rsrc rs, uint32_t roff, int64_t k0, int kh, int, uint32_t (&r)[NW]) {
+        ldb(rs, roff + 20u * kh, (uint32_t)(40 * (k0 / 64)), r);
+    }
+    __device__ static void decode(const uint32_t (&r)[NW], State &, int, int, int64_t, half8 (&f)[4]) {
+        const float d = h2f(r[0]), m = h2f(r[0] >> 16);
+        const float s24 = d * TWO24, s20 = d * 1048576.0f;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const uint32_t w = r[1 + i], t = w >> 8;  // qs[4i .. 4i+4)
+            quad(w & 0x000F000Fu, t & 0x000F000Fu, s24, m, f[i >> 1], 4 * (i & 1));
+            quad(w & 0x00F000F0u, t & 0x00F000F0u, s20, m, f[2 + (i >> 1)], 4 * (i & 1));
+        }
+    }
+};
+
 template <> struct PDec<QMM_Q8_0> {
     // lane half kh: block 2 kt + kh (34 bytes); step s: k = 32 kh + 8 s + sigma(j)
     static constexpr int NW = 9;
@@ -870,6 +919,7 @@ static bool aligned_layout(int dtype, int64_t nb) {
     case QMM_Q4_0:
     case QMM_Q8_0:
     case QMM_Q6_K: return (nb % 2) == 0;
+    case QMM_Q4_1:
     case QMM_Q4_K: return true;
     default: return false;
     }
@@ -959,6 +1009,7 @@ hipError_t launch_gemm_mfma(int dtype, const void *blob_v, int64_t M, int64_t K,
     const uint8_t *blob = static_cast<const uint8_t *>(blob_v);
     switch (dtype) {
     case QMM_Q4_0: return launch_dt<QMM_Q4_0>(blob, M, K, N, X, Y, st);
+    case QMM_Q4_1: return launch_dt<QMM_Q4_1>(blob, M, K, N, X, Y, st);
     case QMM_Q8_0: return launch_dt<QMM_Q8_0>(blob, M, K, N, X, Y, st);
     case QMM_Q4_K: return launch_dt<QMM_Q4_K>(blob, M, K, N, X, Y, st);
     case QMM_Q6_K: return launch_dt<QMM_Q6_K>(blob, M, K, N, X, Y, st);

@@ -96,6 +96,42 @@ template <> struct Unit<QMM_Q4_0> {
     }
 };
 
+template <> struct Unit<QMM_Q4_1> {
+    // The unit is two 20-byte blocks (d, m, qs[16]) -- every dword aligned:
+    // v0 = d0|m0, v1..v4 = qs0[0..16), v5 = d1|m1, v6..v9 = qs1.  Codes enter
+    // as exact f16 subnormals (low nibbles c 2^-24, high nibbles c 2^-20); each
+    // weight d*q + m is formed with one rounding (v_fma_mix_f32 with d*2^24 or
+    // d*2^20 and m), then multiplied into x with an f32 FMA -- as for Q4_K.
+    static constexpr int NL = 10;
+    struct Off { uint32_t a; };
+    __device__ static Off lane_off(int u) { return {40u * u}; }
+    __device__ static void load(Rsrc rs, uint32_t row, const Off &o, uint32_t (&v)[NL]) { ldb(rs, o.a, row, v); }
+    __device__ static int x4(int u, int i) { return 16 * u + i; }
+    __device__ static float dot(const uint32_t (&v)[NL], const float (&xv)[64], const Off &) {
+        float acc[4];
+#pragma unroll
+        for (int b = 0; b < 2; b++) {
+            const float d = h2f(v[5 * b]), m = h2f(v[5 * b] >> 16);
+            const float s24 = d * TWO24, s20 = d * TWO20;
+            const float *xb = xv + 32 * b;
+            float l = 0.f, h = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                // qs[4i .. 4i+4): elements 4i..4i+3 (low nibbles), 16+4i.. (high)
+                const uint32_t dw = v[5 * b + 1 + i], t = dw >> 8;
+                const half2_t p0 = as_h2(dw & 0x000F000Fu), p1 = as_h2(dw & 0x00F000F0u);
+                const half2_t p2 = as_h2(t & 0x000F000Fu), p3 = as_h2(t & 0x00F000F0u);
+                l = fmaf(fma_h(p0.x, s24, m), xb[4 * i], l);     h = fmaf(fma_h(p1.x, s20, m), xb[16 + 4 * i], h);
+                l = fmaf(fma_h(p0.y, s24, m), xb[4 * i + 2], l); h = fmaf(fma_h(p1.y, s20, m), xb[16 + 4 * i + 2], h);
+                l = fmaf(fma_h(p2.x, s24, m), xb[4 * i + 1], l); h = fmaf(fma_h(p3.x, s20, m), xb[16 + 4 * i + 1], h);
+                l = fmaf(fma_h(p2.y, s24, m), xb[4 * i + 3], l); h = fmaf(fma_h(p3.y, s20, m), xb[16 + 4 * i + 3], h);
+            }
+            acc[2 * b] = l;
+            acc[2 * b + 1] = h;
+        }
+        return (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    }
+};
 template <> struct Unit<QMM_Q8_0> {
     static constexpr int NL = 17;
     struct Off { uint32_t a; };
@@ -692,6 +728,18 @@ __device__ float block_dot_generic<QMM_Q4_0>(const uint8_t *p, const float *x) {
 }
 
 template <>
+__device__ float block_dot_generic<QMM_Q4_1>(const uint8_t *p, const float *x) {
+    const float d = h2f((uint32_t)p[0] | ((uint32_t)p[1] << 8));
+    const float m = h2f((uint32_t)p[2] | ((uint32_t)p[3] << 8));
+    float slo = 0.f, shi = 0.f;
+    for (int j = 0; j < 16; j++) {
+        slo = fmaf(fmaf(d, (float)(p[4 + j] & 15), m), x[j], slo);
+        shi = fmaf(fmaf(d, (float)(p[4 + j] >> 4), m), x[16 + j], shi);
+    }
+    return slo + shi;
+}
+
+template <>
 __device__ float block_dot_generic<QMM_Q8_0>(const uint8_t *p, const float *x) {
     const float d = h2f((uint32_t)p[0] | ((uint32_t)p[1] << 8));
     float s0 = 0.f, s1 = 0.f;
@@ -781,6 +829,7 @@ __global__ void __launch_bounds__(256) gemv_generic_kernel(const uint8_t *__rest
 static bool fast_layout_ok(int dtype, int64_t nb) {
     switch (dtype) {
     case QMM_Q4_0:
+    case QMM_Q4_1:
     case QMM_Q8_0:
     case QMM_Q6_K: return (nb % 2) == 0;
     case QMM_Q4_K: return true;
@@ -934,7 +983,7 @@ static hipError_t launch_mats(int n, const void *const *blobs, const int64_t *Ms
 }
 
 bool gemv_fused_ok(int dtype, int64_t K) {
-    const int64_t bs = (dtype == QMM_Q4_K || dtype == QMM_Q6_K) ? 256 : 32;
+    const int64_t bs = (dtype == QMM_Q4_K || dtype == QMM_Q6_K) ? 256 : 32;  // Q4_0, Q4_1, Q8_0: 32
     return fast_layout_ok(dtype, K / bs) && (K % 64) == 0 && K / 64 <= 256;
 }
 
@@ -951,6 +1000,7 @@ hipError_t launch_gemv_concat(int n, const void *const *blobs, const int64_t *Ms
     }
     switch (dtype) {
     case QMM_Q4_0: return launch_mats<QMM_Q4_0, 2, 3, GEMV_CONCAT>(n, blobs, Ms, K, x, ys, st, cus);
+    case QMM_Q4_1: return launch_mats<QMM_Q4_1, 2, 3, GEMV_CONCAT>(n, blobs, Ms, K, x, ys, st, cus);
     case QMM_Q8_0: return launch_mats<QMM_Q8_0, 1, 4, GEMV_CONCAT>(n, blobs, Ms, K, x, ys, st, cus);
     case QMM_Q4_K: return launch_mats<QMM_Q4_K, 2, 3, GEMV_CONCAT>(n, blobs, Ms, K, x, ys, st, cus);
     case QMM_Q6_K: return launch_mats<QMM_Q6_K, 1, 4, GEMV_CONCAT>(n, blobs, Ms, K, x, ys, st, cus);
@@ -967,6 +1017,7 @@ hipError_t launch_gemv_swiglu(int dtype, const void *gate, const void *up, int64
     // one row of each matrix per group: the register footprint of two rows
     switch (dtype) {
     case QMM_Q4_0: return launch_mats<QMM_Q4_0, 1, 3, GEMV_SWIGLU>(2, blobs, Ms, K, x, ys, st, cus);
+    case QMM_Q4_1: return launch_mats<QMM_Q4_1, 1, 3, GEMV_SWIGLU>(2, blobs, Ms, K, x, ys, st, cus);
     case QMM_Q8_0: return launch_mats<QMM_Q8_0, 1, 2, GEMV_SWIGLU>(2, blobs, Ms, K, x, ys, st, cus);
     case QMM_Q4_K: return launch_mats<QMM_Q4_K, 1, 3, GEMV_SWIGLU>(2, blobs, Ms, K, x, ys, st, cus);
     case QMM_Q6_K: return launch_mats<QMM_Q6_K, 1, 2, GEMV_SWIGLU>(2, blobs, Ms, K, x, ys, st, cus);
@@ -985,6 +1036,7 @@ hipError_t launch_gemv_argmax(int dtype, const void *blob, int64_t M, int64_t K,
     hipError_t e;
     switch (dtype) {
     case QMM_Q4_0: e = launch_mats<QMM_Q4_0, 2, 3, GEMV_ARGMAX>(1, blobs, Ms, K, x, ys, st, cus, part, &grid); break;
+    case QMM_Q4_1: e = launch_mats<QMM_Q4_1, 2, 3, GEMV_ARGMAX>(1, blobs, Ms, K, x, ys, st, cus, part, &grid); break;
     case QMM_Q8_0: e = launch_mats<QMM_Q8_0, 1, 4, GEMV_ARGMAX>(1, blobs, Ms, K, x, ys, st, cus, part, &grid); break;
     case QMM_Q4_K: e = launch_mats<QMM_Q4_K, 2, 3, GEMV_ARGMAX>(1, blobs, Ms, K, x, ys, st, cus, part, &grid); break;
     case QMM_Q6_K: e = launch_mats<QMM_Q6_K, 1, 4, GEMV_ARGMAX>(1, blobs, Ms, K, x, ys, st, cus, part, &grid); break;
@@ -1003,7 +1055,7 @@ hipError_t launch_gemv_argmax(int dtype, const void *blob, int64_t M, int64_t K,
 constexpr int GEMV_TOKENS = 4;
 
 bool gemv_tokens_ok(int dtype, int64_t K) {
-    const int64_t bs = (dtype == QMM_Q4_K || dtype == QMM_Q6_K) ? 256 : 32;
+    const int64_t bs = (dtype == QMM_Q4_K || dtype == QMM_Q6_K) ? 256 : 32;  // Q4_0, Q4_1, Q8_0: 32
     return fast_layout_ok(dtype, K / bs) && (K % 64) == 0 && K / 64 <= 64;
 }
 
@@ -1038,6 +1090,7 @@ hipError_t launch_gemv_tokens(int dtype, const void *blob_v, int64_t M, int64_t 
         hipError_t e;
         switch (dtype) {
         case QMM_Q4_0: e = launch_tokens<QMM_Q4_0, 2, 1>(blob, M, K, nt, Xp, Yp, st, cus); break;
+        case QMM_Q4_1: e = launch_tokens<QMM_Q4_1, 2, 1>(blob, M, K, nt, Xp, Yp, st, cus); break;
         case QMM_Q8_0: e = launch_tokens<QMM_Q8_0, 2, 1>(blob, M, K, nt, Xp, Yp, st, cus); break;
         case QMM_Q4_K: e = launch_tokens<QMM_Q4_K, 1, 1>(blob, M, K, nt, Xp, Yp, st, cus); break;
         case QMM_Q6_K: e = launch_tokens<QMM_Q6_K, 1, 1>(blob, M, K, nt, Xp, Yp, st, cus); break;
@@ -1051,10 +1104,11 @@ hipError_t launch_gemv_tokens(int dtype, const void *blob_v, int64_t M, int64_t 
 hipError_t launch_gemv(int dtype, const void *blob_v, int64_t M, int64_t K, const float *x, float *y,
                        hipStream_t st, int cus) {
     const uint8_t *blob = static_cast<const uint8_t *>(blob_v);
-    const int64_t bs = (dtype == QMM_Q4_K || dtype == QMM_Q6_K) ? 256 : 32;
+    const int64_t bs = (dtype == QMM_Q4_K || dtype == QMM_Q6_K) ? 256 : 32;  // Q4_0, Q4_1, Q8_0: 32
     const bool fast = fast_layout_ok(dtype, K / bs) && (K % 64) == 0;
     switch (dtype) {
     case QMM_Q4_0: return fast ? launch_one<QMM_Q4_0, 2, 3>(blob, M, K, x, y, st, cus) : launch_generic<QMM_Q4_0>(blob, M, K, x, y, st, cus);
+    case QMM_Q4_1: return fast ? launch_one<QMM_Q4_1, 2, 3>(blob, M, K, x, y, st, cus) : launch_generic<QMM_Q4_1>(blob, M, K, x, y, st, cus);
     case QMM_Q8_0: return fast ? launch_one<QMM_Q8_0, 1, 4>(blob, M, K, x, y, st, cus) : launch_generic<QMM_Q8_0>(blob, M, K, x, y, st, cus);
     case QMM_Q4_K: return fast ? launch_one<QMM_Q4_K, 2, 3>(blob, M, K, x, y, st, cus) : launch_generic<QMM_Q4_K>(blob, M, K, x, y, st, cus);
     case QMM_Q6_K: return fast ? launch_one<QMM_Q6_K, 1, 4>(blob, M, K, x, y, st, cus) : launch_generic<QMM_Q6_K>(blob, M, K, x, y, st, cus);

@@ -21,6 +21,9 @@
  *     Q4_0 (32 weights, 18 B): f16 d, 16 nibble bytes;       w = d*(q-8)
  *          weight e<16 = low nibble of byte e, e>=16 = high nibble of byte e-16
  *          (same page, repack_q4_0_8x8)
+ *     Q4_1 (32 weights, 20 B): f16 d, f16 m, 16 nibble bytes; w = d*q + m
+ *          (nibbles as Q4_0; the pages name the format, gemv_q4_1_f32, but
+ *          not its bytes: standard GGUF layout)
  *     Q4_K (256 weights, 144 B): f16 d, f16 dmin, 12 bytes of packed 6-bit
  *          (scale, min) for 8 sub-blocks of 32, 128 nibble bytes;
  *          w = d*sc*q - dmin*m  (same page, repack_q4_k_8x8; the 6-bit
@@ -60,6 +63,7 @@ extern "C" {
 
 /* dtype tags: the GGUF tensor type ids */
 #define QMM_Q4_0 2
+#define QMM_Q4_1 3
 #define QMM_Q8_0 8
 #define QMM_Q4_K 12
 #define QMM_Q6_K 14
@@ -67,7 +71,7 @@ extern "C" {
 /* status codes */
 #define QMM_OK 0
 #define QMM_ERR_NULL (-1)    /* a required pointer is NULL                          */
-#define QMM_ERR_DTYPE (-2)   /* dtype is not one of the four tags above             */
+#define QMM_ERR_DTYPE (-2)   /* dtype is not one of the five tags above             */
 #define QMM_ERR_SHAPE (-3)   /* M < 1, N < 1, K < block_elems or K % block_elems    */
 #define QMM_ERR_ALIGN (-4)   /* blob not 16-B aligned, x/X not 16-B, y/Y not 4-B    */
 #define QMM_ERR_DEVICE (-5)  /* no current HIP device, or it is not gfx950          */
@@ -76,7 +80,7 @@ extern "C" {
 /* Decode GEMV (one token), page "cera 0.5.2 src/backend/cpu.rs", section
  * "GEMV (matrix-vector multiply)": y[m] = sum_k W[m][k] * x[k].
  *   w_blob  device, M*row_bytes bytes, 16-B aligned, row-major blocks
- *   dtype   QMM_Q4_0 | QMM_Q8_0 | QMM_Q4_K | QMM_Q6_K
+ *   dtype   QMM_Q4_0 | QMM_Q4_1 | QMM_Q8_0 | QMM_Q4_K | QMM_Q6_K
  *   M, K    rows and weights per row; K a multiple of the block size
  *   x       device f32 [K], 16-B aligned
  *   y       device f32 [M], 4-B aligned; overwritten
@@ -98,7 +102,7 @@ int qmm_gemv(const void *w_blob, int dtype, int64_t M, int64_t K,
  * Each ys[i] holds exactly the bits qmm_gemv returns for matrix i.  The
  * host arrays are read before the call returns and not kept.  Layouts that
  * the one-launch kernel does not take (K not a multiple of 64, an odd number
- * of blocks per row for Q4_0/Q8_0/Q6_K, K > 16384) run one launch per matrix
+ * of blocks per row for Q4_0/Q4_1/Q8_0/Q6_K, K > 16384) run one launch per matrix
  * with the same results. */
 #define QMM_GEMV_MAX_MATS 4
 int qmm_gemv_concat(int n, const void *const *w_blobs, const int64_t *Ms, int dtype, int64_t K,
@@ -116,7 +120,7 @@ int qmm_gemv_concat(int n, const void *const *w_blobs, const int64_t *Ms, int dt
  * sums of |w x| and tau = 1e-5:
  *   |out - exact| <= tau*(1.1*S_g*(|u| + tau*S_u) + |silu(g)|*S_u) + 4*2^-24*|out|.
  * Needs K a multiple of 64, at most 16384, and an even number of blocks per
- * row for Q4_0, Q8_0 and Q6_K; otherwise QMM_ERR_SHAPE. */
+ * row for Q4_0, Q4_1, Q8_0 and Q6_K; otherwise QMM_ERR_SHAPE. */
 int qmm_gemv_swiglu(const void *gate_blob, const void *up_blob, int dtype, int64_t M, int64_t K,
                     const float *x, float *out, void *stream);
 
@@ -133,8 +137,8 @@ int qmm_gemv_swiglu(const void *gate_blob, const void *up_blob, int dtype, int64
  *   index   device int64, 8-B aligned
  *   value   device f32 or NULL
  * Two launches on `stream` (the rows, then the winner).  Needs K a multiple
- * of 64, at most 16384, and an even number of blocks per row for Q4_0, Q8_0
- * and Q6_K; otherwise QMM_ERR_SHAPE.  Concurrent calls need separate work
+ * of 64, at most 16384, and an even number of blocks per row for Q4_0, Q4_1,
+ * Q8_0 and Q6_K; otherwise QMM_ERR_SHAPE.  Concurrent calls need separate work
  * buffers. */
 #define QMM_ARGMAX_WORK_BYTES 32768
 int qmm_gemv_argmax(const void *w_blob, int dtype, int64_t M, int64_t K, const float *x,
@@ -150,10 +154,10 @@ int qmm_gemv_argmax(const void *w_blob, int dtype, int64_t M, int64_t K, const f
  * "cera 0.5.0 src/model/llama.rs", project_logits_batched: verifying drafted
  * tokens in one pass over the LM head; page "cera 0.5.2
  * src/backend/cpu.rs": decode and prefill must agree bit for bit).  With K a
- * multiple of 64 up to 4096 and an even number of blocks per row (Q4_0, Q8_0,
- * Q6_K) up to 4 tokens share one read of the weights and the crossover is
- * N = 5 (Q4_0, Q8_0, Q6_K) or 3 (Q4_K); otherwise each token is one GEMV
- * launch and the crossover is 3 (Q4_0, Q6_K) or 2 (Q8_0, Q4_K).  The path
+ * multiple of 64 up to 4096 and an even number of blocks per row (Q4_0, Q4_1,
+ * Q8_0, Q6_K) up to 4 tokens share one read of the weights and the crossover
+ * is N = 5 (Q4_0, Q4_1, Q8_0, Q6_K) or 3 (Q4_K); otherwise each token is one
+ * GEMV launch and the crossover is 3 (Q4_0, Q6_K) or 2 (Q4_1, Q8_0, Q4_K).  The path
  * qmm_gemm_path names: 0 = all-f32 arithmetic (tolerance 1e-5 of
  * sum |w x|), 1 = weights and activations rounded to f16 and multiplied on
  * the matrix cores with f32 accumulation (tolerance 2e-3 of sum |w x|; needs

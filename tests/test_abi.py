@@ -33,9 +33,10 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_geometry():
-    assert [q.block_elems(d) for d in (2, 8, 12, 14)] == [32, 32, 256, 256]
-    assert [q.block_bytes(d) for d in (2, 8, 12, 14)] == [18, 34, 144, 210]
-    assert q.block_elems(3) == 0 and q.block_bytes(99) == 0
+    assert [q.block_elems(d) for d in (2, 3, 8, 12, 14)] == [32, 32, 32, 256, 256]
+    assert [q.block_bytes(d) for d in (2, 3, 8, 12, 14)] == [18, 20, 34, 144, 210]
+    assert q.block_elems(4) == 0 and q.block_bytes(99) == 0
+    assert q.blob_bytes(q.QMM_Q4_1, 4096, 4096) == 4096 * 128 * 20
     # the tied Q6_K head of the 1B model on the pages: 2048 x 128256, ~205 MiB
     assert q.blob_bytes(q.QMM_Q6_K, 128256, 2048) == 215_470_080
     assert q.blob_bytes(q.QMM_Q4_0, 4096, 4096) == 4096 * 128 * 18
@@ -102,6 +103,9 @@ def test_gemm_path_selection():
     assert q.gemm_path(q.QMM_Q4_0, 4096, 14336, 3) == 1
     assert q.gemm_path(q.QMM_Q8_0, 4096, 8192, 2) == 1
     assert q.gemm_path(q.QMM_Q6_K, 4096, 8192, 2) == 0
+    assert q.gemm_path(q.QMM_Q4_1, 4096, 4096, 4) == 0
+    assert q.gemm_path(q.QMM_Q4_1, 4096, 4096, 5) == 1
+    assert q.gemm_path(q.QMM_Q4_1, 4096, 8192, 2) == 1
     assert q.gemm_path(q.QMM_Q4_K, 14336, 4096, 512) == 1
     assert q.gemm_path(q.QMM_Q4_K, 14336, 100, 512) == q.QMM_ERR_SHAPE
     assert q.tolerance(q.QMM_Q4_0, 4096, 4096, 1) == 1e-5
@@ -126,7 +130,7 @@ def _concat(n, blobs, Ms, dtype, K, x, ys):
     (5, [A16] * 5, [8] * 5, 2, 64, A16, [A16] * 5, q.QMM_ERR_SHAPE),
     (2, [A16, A16], [8, 0], 2, 64, A16, [A16, A16], q.QMM_ERR_SHAPE),
     (2, [A16, A16], [8, 8], 2, 48, A16, [A16, A16], q.QMM_ERR_SHAPE),
-    (2, [A16, A16], [8, 8], 3, 64, A16, [A16, A16], q.QMM_ERR_DTYPE),
+    (2, [A16, A16], [8, 8], 4, 64, A16, [A16, A16], q.QMM_ERR_DTYPE),
     (2, None, [8, 8], 2, 64, A16, [A16, A16], q.QMM_ERR_NULL),
     (2, [A16, A16], None, 2, 64, A16, [A16, A16], q.QMM_ERR_NULL),
     (2, [A16, A16], [8, 8], 2, 64, A16, None, q.QMM_ERR_NULL),

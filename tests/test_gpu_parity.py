@@ -21,8 +21,8 @@ from qmm_inputs import WORKLOADS, make_blob, make_x, rng_for
 
 pytestmark = pytest.mark.gpu
 
-DTYPES = [q.QMM_Q4_0, q.QMM_Q8_0, q.QMM_Q4_K, q.QMM_Q6_K]
-NAME = {2: "Q4_0", 8: "Q8_0", 12: "Q4_K", 14: "Q6_K"}
+DTYPES = [q.QMM_Q4_0, q.QMM_Q8_0, q.QMM_Q4_K, q.QMM_Q6_K, q.QMM_Q4_1]
+NAME = {2: "Q4_0", 3: "Q4_1", 8: "Q8_0", 12: "Q4_K", 14: "Q6_K"}
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -120,7 +120,7 @@ def test_gemm_small(dt, N):
         check(Yg, Y64, S, q.tolerance(dt, M, K, N), f"{NAME[dt]} gemm M={M} K={K} N={N}")
 
 
-@pytest.mark.parametrize("dt", [q.QMM_Q4_0, q.QMM_Q4_K], ids=NAME.get)
+@pytest.mark.parametrize("dt", [q.QMM_Q4_0, q.QMM_Q4_K, q.QMM_Q4_1], ids=NAME.get)
 def test_gemm_register_b_kernel_ragged(dt):
     # M/256 x N/128 >= 224 workgroups selects the register-B kernel for the
     # 4-bit formats; M and N both end in partial tiles.  Sampled rows include
@@ -161,7 +161,7 @@ def test_gemm_n1_is_gemv_bitwise_and_deterministic(dt):
 def test_zero_scales_give_exact_zero(dt):
     M, K = 45, 8 * bs_of(dt)
     blob = make_blob(dt, M, K, rng_for(800 + dt, 0)).reshape(M * (K // bs_of(dt)), -1)
-    offs = {2: [0], 8: [0], 12: [0, 2], 14: [208]}[dt]
+    offs = {2: [0], 3: [0, 2], 8: [0], 12: [0, 2], 14: [208]}[dt]
     for o in offs:
         blob[:, o:o + 2] = 0
     blob = blob.reshape(-1)
@@ -184,6 +184,21 @@ def test_sparse_rows_keep_f32_bound():
     x = make_x(1, K, rng_for(810, 1)) * np.float32(1e3)
     _, Y64, S = oracle.matmul(q.QMM_Q4_0, blob, M, K, x)
     check(gpu_gemv(q.QMM_Q4_0, to_dev(blob), M, K, x)[None, :], Y64, S, 1e-5, "sparse q4_0 rows")
+
+
+def test_sparse_q4_1_rows_keep_f32_bound():
+    # Q4_1 rows whose weights d*q + m are all exactly zero (m = -8d, nibble 8)
+    # but one per block: the kernel must form each weight before it meets x
+    M, K = 64, 4096
+    blob = make_blob(q.QMM_Q4_1, M, K, rng_for(811, 0)).reshape(M, K // 32, 20)
+    blob[:, :, 0:2] = np.frombuffer(np.float16(2.0 ** -6).tobytes(), np.uint8)
+    blob[:, :, 2:4] = np.frombuffer(np.float16(-(2.0 ** -3)).tobytes(), np.uint8)
+    blob[:, :, 4:20] = 0x88
+    blob[:, :, 4 + 3] = 0x8F          # element 3 of every block: q = 15 -> 7d
+    blob = blob.reshape(-1)
+    x = make_x(1, K, rng_for(811, 1)) * np.float32(1000.0)
+    _, Y64, S = oracle.matmul(q.QMM_Q4_1, blob, M, K, x)
+    check(gpu_gemv(q.QMM_Q4_1, to_dev(blob), M, K, x)[None, :], Y64, S, 1e-5, "sparse q4_1 rows")
 
 
 def test_streams_and_errors_on_device():
