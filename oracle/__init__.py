@@ -23,8 +23,8 @@ _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 # GGUF type ids, as the oracle's C source numbers them.
-Q4_0, Q4_1, Q8_0, Q4_K, Q6_K = 2, 3, 8, 12, 14
-NAMES = {Q4_0: "Q4_0", Q4_1: "Q4_1", Q8_0: "Q8_0", Q4_K: "Q4_K", Q6_K: "Q6_K"}
+Q4_0, Q4_1, Q8_0, Q4_K, Q5_K, Q6_K = 2, 3, 8, 12, 13, 14
+NAMES = {Q4_0: "Q4_0", Q4_1: "Q4_1", Q8_0: "Q8_0", Q4_K: "Q4_K", Q5_K: "Q5_K", Q6_K: "Q6_K"}
 BY_NAME = {v: k for k, v in NAMES.items()}
 
 _lib = None

@@ -56,6 +56,14 @@
  *          i<4 : sc = s[i]&63,               m = s[i+4]&63
  *          i>=4: sc = (s[i+4]&15)|((s[i-4]>>6)<<4),
  *                m  = (s[i+4]>>4)|((s[i]>>6)<<4)
+ *   Q5_K (type 13, 256 weights, 176 B): d f16 @0, dmin f16 @2,
+ *        scales u8[12] @4 (packed as Q4_K), qh u8[32] @16, qs u8[128] @48.
+ *        Sub-block i = j/32, e = j%32: low 4 bits as Q4_K's nibble, fifth
+ *        bit = bit i of qh[e];  q = lo | hi<<4;  w = d*sc_i*q - dmin*m_i
+ *        (the pages name Q5_K and its GEMV -- page "cera 0.5.2
+ *         src/backend/cpu.rs", gemv_q5km_f32 -- but print no layout;
+ *         READING: the standard GGUF Q5_K block, "parity unpinned" against
+ *         the pages, pinned to hand-built fixtures written from the reading)
  *   Q6_K (type 14, 256 weights, 210 B): ql u8[128] @0, qh u8[64] @128,
  *        sc int8[16] @192, d f16 @208.  Only the 210-byte size is on the
  *        pages (page "cera 0.3.1 src/model/gpu_lfm2.rs", upload_weight);
@@ -86,6 +94,7 @@
 #define OR_Q4_1 3
 #define OR_Q8_0 8
 #define OR_Q4_K 12
+#define OR_Q5_K 13
 #define OR_Q6_K 14
 
 /* ---- format geometry --------------------------------------------------- */
@@ -96,6 +105,7 @@ int oracle_block_elems(int dtype) {
     case OR_Q4_1: return 32;
     case OR_Q8_0: return 32;
     case OR_Q4_K: return 256;
+    case OR_Q5_K: return 256;
     case OR_Q6_K: return 256;
     default: return 0;
     }
@@ -107,6 +117,7 @@ int oracle_block_bytes(int dtype) {
     case OR_Q4_1: return 20;
     case OR_Q8_0: return 34;
     case OR_Q4_K: return 144;
+    case OR_Q5_K: return 176;
     case OR_Q6_K: return 210;
     default: return 0;
     }
@@ -174,6 +185,21 @@ static void dequant_q4_k(const uint8_t *b, double *w) {
     }
 }
 
+static void dequant_q5_k(const uint8_t *b, double *w) {
+    double d = half_at(b), dmin = half_at(b + 2);
+    const uint8_t *s = b + 4, *qh = b + 16, *qs = b + 48;
+    for (int i = 0; i < 8; i++) {
+        int sc, mn;
+        q4k_scale_min(s, i, &sc, &mn);
+        for (int e = 0; e < 32; e++) {
+            uint8_t byte = qs[(i / 2) * 32 + e];
+            int lo = (i % 2 == 0) ? (byte & 15) : (byte >> 4);
+            int hi = (qh[e] >> i) & 1;
+            w[32 * i + e] = d * (double)sc * (double)(lo | (hi << 4)) - dmin * (double)mn;
+        }
+    }
+}
+
 static void dequant_q6_k(const uint8_t *b, double *w) {
     const uint8_t *ql = b;
     const uint8_t *qh = b + 128;
@@ -204,6 +230,7 @@ static int dequant_block(int dtype, const uint8_t *b, double *w) {
     case OR_Q4_0: dequant_q4_0(b, w); return 0;
     case OR_Q4_1: dequant_q4_1(b, w); return 0;
     case OR_Q4_K: dequant_q4_k(b, w); return 0;
+    case OR_Q5_K: dequant_q5_k(b, w); return 0;
     case OR_Q6_K: dequant_q6_k(b, w); return 0;
     default: return -2;
     }

@@ -13,6 +13,7 @@ Distributions (the workload table the inputs stand in for):
         uniform nibble bytes
   Q4_K: d, dmin ~ U[5e-4, 2e-3], 12 uniform scale bytes (so every 6-bit
         sc/m is uniform on 0..63), 128 uniform nibble bytes
+  Q5_K: as Q4_K, plus 32 uniform fifth-bit bytes (so q is uniform on 0..31)
   Q6_K: d ~ U[2e-4, 1e-3], uniform ql/qh bytes (so q is uniform on 0..63),
         int8 sub-scales ~ U{-64..63}
   activations: f32 ~ N(0, 1)
@@ -26,11 +27,12 @@ from __future__ import annotations
 
 import numpy as np
 
-Q4_0, Q4_1, Q8_0, Q4_K, Q6_K = 2, 3, 8, 12, 14
-NAMES = {Q4_0: "Q4_0", Q4_1: "Q4_1", Q8_0: "Q8_0", Q4_K: "Q4_K", Q6_K: "Q6_K"}
+Q4_0, Q4_1, Q8_0, Q4_K, Q5_K, Q6_K = 2, 3, 8, 12, 13, 14
+NAMES = {Q4_0: "Q4_0", Q4_1: "Q4_1", Q8_0: "Q8_0", Q4_K: "Q4_K", Q5_K: "Q5_K", Q6_K: "Q6_K"}
 BY_NAME = {v: k for k, v in NAMES.items()}
 # (weights per block, bytes per block) -- the GGUF block geometry.
-GEOMETRY = {Q4_0: (32, 18), Q4_1: (32, 20), Q8_0: (32, 34), Q4_K: (256, 144), Q6_K: (256, 210)}
+GEOMETRY = {Q4_0: (32, 18), Q4_1: (32, 20), Q8_0: (32, 34), Q4_K: (256, 144), Q5_K: (256, 176),
+            Q6_K: (256, 210)}
 
 
 def rng_for(workload_id: int, tensor_id: int = 0) -> np.random.Generator:
@@ -70,6 +72,10 @@ def make_blob(dtype: int, M: int, K: int, rng: np.random.Generator) -> np.ndarra
         blk[:, 0:2] = _f16_bytes(rng.uniform(5e-4, 2e-3, nblk).astype(np.float32))
         blk[:, 2:4] = _f16_bytes(rng.uniform(5e-4, 2e-3, nblk).astype(np.float32))
         blk[:, 4:144] = rng.integers(0, 256, size=(nblk, 140), dtype=np.uint8)
+    elif dtype == Q5_K:
+        blk[:, 0:2] = _f16_bytes(rng.uniform(5e-4, 2e-3, nblk).astype(np.float32))
+        blk[:, 2:4] = _f16_bytes(rng.uniform(5e-4, 2e-3, nblk).astype(np.float32))
+        blk[:, 4:176] = rng.integers(0, 256, size=(nblk, 172), dtype=np.uint8)
     elif dtype == Q6_K:
         blk[:, 0:192] = rng.integers(0, 256, size=(nblk, 192), dtype=np.uint8)
         blk[:, 192:208] = rng.integers(-64, 64, size=(nblk, 16), dtype=np.int8).view(np.uint8)

@@ -35,7 +35,7 @@ import oracle
 from qmm_inputs import make_blob, make_x, rng_for
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
-DTYPES = (oracle.Q4_0, oracle.Q8_0, oracle.Q4_K, oracle.Q6_K, oracle.Q4_1)
+DTYPES = (oracle.Q4_0, oracle.Q8_0, oracle.Q4_K, oracle.Q6_K, oracle.Q4_1, oracle.Q5_K)
 
 
 # ----------------------------------------------------------------- fixtures
@@ -127,7 +127,7 @@ def _f16(a: np.ndarray) -> np.ndarray:
 def closed_form_row_sums(dt: int, blob: np.ndarray, M: int, K: int) -> np.ndarray:
     """y = W . ones, from the block fields: scale x (sum of integer codes)."""
     bs, bb = {oracle.Q4_0: (32, 18), oracle.Q4_1: (32, 20), oracle.Q8_0: (32, 34),
-              oracle.Q4_K: (256, 144), oracle.Q6_K: (256, 210)}[dt]
+              oracle.Q4_K: (256, 144), oracle.Q5_K: (256, 176), oracle.Q6_K: (256, 210)}[dt]
     nb = K // bs
     B = blob[: M * nb * bb].reshape(M, nb, bb)
     if dt == oracle.Q8_0:
@@ -159,6 +159,23 @@ def closed_form_row_sums(dt: int, blob: np.ndarray, M: int, K: int) -> np.ndarra
         qsum = np.empty((M, nb, 8), np.int64)
         qsum[:, :, 0::2] = (chunks & 15).sum(axis=3)       # even sub-blocks: low nibbles
         qsum[:, :, 1::2] = (chunks >> 4).sum(axis=3)       # odd sub-blocks: high nibbles
+        per_block = (d[:, :, None] * sc * qsum - 32 * dmin[:, :, None] * mn).sum(axis=2)
+    elif dt == oracle.Q5_K:
+        d = _f16(np.ascontiguousarray(B[:, :, 0:2])).reshape(M, nb)
+        dmin = _f16(np.ascontiguousarray(B[:, :, 2:4])).reshape(M, nb)
+        s = B[:, :, 4:16].astype(np.int64)
+        sc = np.empty((M, nb, 8), np.int64)
+        mn = np.empty((M, nb, 8), np.int64)
+        sc[:, :, 0:4] = s[:, :, 0:4] & 63
+        mn[:, :, 0:4] = s[:, :, 4:8] & 63
+        sc[:, :, 4:8] = (s[:, :, 8:12] & 15) | ((s[:, :, 0:4] >> 6) << 4)
+        mn[:, :, 4:8] = (s[:, :, 8:12] >> 4) | ((s[:, :, 4:8] >> 6) << 4)
+        qh = B[:, :, 16:48].astype(np.int64)                       # [e]
+        chunks = B[:, :, 48:176].astype(np.int64).reshape(M, nb, 4, 32)
+        qsum = np.empty((M, nb, 8), np.int64)
+        for i in range(8):
+            nib = (chunks[:, :, i // 2] & 15) if i % 2 == 0 else (chunks[:, :, i // 2] >> 4)
+            qsum[:, :, i] = nib.sum(axis=2) + 16 * ((qh >> i) & 1).sum(axis=2)
         per_block = (d[:, :, None] * sc * qsum - 32 * dmin[:, :, None] * mn).sum(axis=2)
     elif dt == oracle.Q6_K:
         ql = B[:, :, 0:128].astype(np.int64).reshape(M, nb, 2, 2, 32)     # [h][c][l]
@@ -227,6 +244,21 @@ def exact_weights(dt: int, blk: bytes) -> list:
                 q = c % 16 if i % 2 == 0 else c // 16
                 w.append(d * sc[i] * q - dmin * mn[i])
         return w
+    if dt == oracle.Q5_K:
+        d, dmin = _h(blk, 0), _h(blk, 2)
+        s, qh, qs = blk[4:16], blk[16:48], blk[48:176]
+        w = []
+        for i in range(8):
+            if i < 4:
+                sc, mn = s[i] % 64, s[i + 4] % 64
+            else:
+                sc = s[i + 4] % 16 + 16 * (s[i - 4] // 64)
+                mn = s[i + 4] // 16 + 16 * (s[i] // 64)
+            for e in range(32):
+                byte = qs[32 * (i // 2) + e]
+                q = (byte % 16 if i % 2 == 0 else byte // 16) + 16 * ((qh[e] >> i) & 1)
+                w.append(d * sc * q - dmin * mn)
+        return w
     if dt == oracle.Q6_K:
         ql, qh = blk[0:128], blk[128:192]
         sc = struct.unpack("<16b", blk[192:208])
@@ -292,9 +324,10 @@ def pin_bruteforce(L=None):
 def _double_scales(dt: int, blob: np.ndarray, M: int, K: int) -> np.ndarray:
     """Blob with every f16 scale (d, and dmin for Q4_K) multiplied by 2."""
     bs, bb = {oracle.Q4_0: (32, 18), oracle.Q4_1: (32, 20), oracle.Q8_0: (32, 34),
-              oracle.Q4_K: (256, 144), oracle.Q6_K: (256, 210)}[dt]
+              oracle.Q4_K: (256, 144), oracle.Q5_K: (256, 176), oracle.Q6_K: (256, 210)}[dt]
     B = blob.copy().reshape(-1, bb)
-    offs = {oracle.Q4_0: [0], oracle.Q4_1: [0, 2], oracle.Q8_0: [0], oracle.Q4_K: [0, 2], oracle.Q6_K: [208]}[dt]
+    offs = {oracle.Q4_0: [0], oracle.Q4_1: [0, 2], oracle.Q8_0: [0], oracle.Q4_K: [0, 2], oracle.Q5_K: [0, 2],
+            oracle.Q6_K: [208]}[dt]
     for o in offs:
         h = np.ascontiguousarray(B[:, o:o + 2]).view("<f2").reshape(-1)
         h2 = (h.astype(np.float32) * 2).astype("<f2")
@@ -357,8 +390,8 @@ def pin_half(L=None):
 
 
 def pin_sizes(L=None):
-    assert [oracle.block_bytes(d, L) for d in DTYPES] == [18, 34, 144, 210, 20]
-    assert [oracle.block_elems(d, L) for d in DTYPES] == [32, 32, 256, 256, 32]
+    assert [oracle.block_bytes(d, L) for d in DTYPES] == [18, 34, 144, 210, 20, 176]
+    assert [oracle.block_elems(d, L) for d in DTYPES] == [32, 32, 256, 256, 32, 256]
     # tied Q6_K head, hidden size 2048 x vocab 128256, "~205 MiB" on the page
     head = oracle.blob_bytes(oracle.Q6_K, 128256, 2048, L)
     assert head == 215_470_080 and round(head / 2**20) == 205

@@ -31,9 +31,14 @@ MUTANTS = {
     "q4_k_scale_mask": ("*sc = s[i] & 63;", "*sc = s[i] & 31;"),
     "q4_k_high_bits": ("*sc = (s[i + 4] & 15) | ((s[i - 4] >> 6) << 4);", "*sc = (s[i + 4] & 15) | ((s[i - 4] >> 6) << 5);"),
     "q4_k_min_from_scale_byte": ("*mn = (s[i + 4] >> 4) | ((s[i] >> 6) << 4);", "*mn = (s[i + 4] >> 4) | ((s[i - 4] >> 6) << 4);"),
-    "q4_k_min_sign": ("- dmin * (double)mn", "+ dmin * (double)mn"),
+    "q4_k_min_sign": ("(double)q - dmin * (double)mn", "(double)q + dmin * (double)mn"),
+    "q5_k_min_sign": ("(hi << 4)) - dmin * (double)mn", "(hi << 4)) + dmin * (double)mn"),
     "q4_k_nibble_parity": ("int q = (i % 2 == 0) ? (byte & 15) : (byte >> 4);", "int q = (i % 2 == 1) ? (byte & 15) : (byte >> 4);"),
-    "q4_k_chunk": ("qs[(i / 2) * 32 + e]", "qs[(i % 4) * 32 + e]"),
+    "q4_k_chunk": ("uint8_t byte = qs[(i / 2) * 32 + e];\n        int q =", "uint8_t byte = qs[(i % 4) * 32 + e];\n        int q ="),
+    "q5_k_chunk": ("uint8_t byte = qs[(i / 2) * 32 + e];\n            int lo =", "uint8_t byte = qs[(i % 4) * 32 + e];\n            int lo ="),
+    "q5_k_fifth_bit": ("int hi = (qh[e] >> i) & 1;", "int hi = (qh[e] >> (i / 2)) & 1;"),
+    "q5_k_fifth_bit_weight": ("(double)(lo | (hi << 4))", "(double)(lo | (hi << 3))"),
+    "q5_k_qh_offset": ("*qh = b + 16, *qs = b + 48;", "*qh = b + 16, *qs = b + 44;"),
     "q6_k_nibble_groups": ("int lo4 = (g < 2) ?", "int lo4 = (g < 1) ?"),
     "q6_k_qh_shift": ("(qh[32 * h + l] >> (2 * g)) & 3", "(qh[32 * h + l] >> g) & 3"),
     "q6_k_ql_half": ("ql[64 * h + 32 * (g & 1) + l]", "ql[32 * h + 32 * (g & 1) + l]"),
