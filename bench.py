@@ -346,7 +346,7 @@ def sweep(args, q, np, torch, dev, WORKLOADS, make_blob, make_x, rng_for):
             torch.cuda.synchronize()
             med = a.elapsed_time(b) * 1e3 / args.steps
             wb = blob.numel()
-            rec = {"workload": label, "N": N, "dtype": {2: "Q4_0", 3: "Q4_1", 8: "Q8_0", 12: "Q4_K", 14: "Q6_K"}[dt],
+            rec = {"workload": label, "N": N, "dtype": {2: "Q4_0", 3: "Q4_1", 8: "Q8_0", 12: "Q4_K", 13: "Q5_K", 14: "Q6_K"}[dt],
                    "M": M, "K": K, "path": "f16-mfma" if q.gemm_path(dt, M, K, N) else "f32-gemv",
                    "us_per_call": round(med, 3),
                    "weight_GBps": round(wb / (med * 1e-6) / 1e9, 1),

@@ -24,8 +24,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libqmm.so")
 
 # dtype tags (GGUF type ids) and status codes, as in include/qmm.h
-QMM_Q4_0, QMM_Q4_1, QMM_Q8_0, QMM_Q4_K, QMM_Q6_K = 2, 3, 8, 12, 14
-DTYPES = {"Q4_0": QMM_Q4_0, "Q4_1": QMM_Q4_1, "Q8_0": QMM_Q8_0, "Q4_K": QMM_Q4_K, "Q6_K": QMM_Q6_K}
+QMM_Q4_0, QMM_Q4_1, QMM_Q8_0, QMM_Q4_K, QMM_Q5_K, QMM_Q6_K = 2, 3, 8, 12, 13, 14
+DTYPES = {"Q4_0": QMM_Q4_0, "Q4_1": QMM_Q4_1, "Q8_0": QMM_Q8_0, "Q4_K": QMM_Q4_K, "Q5_K": QMM_Q5_K,
+          "Q6_K": QMM_Q6_K}
 QMM_OK, QMM_ERR_NULL, QMM_ERR_DTYPE, QMM_ERR_SHAPE = 0, -1, -2, -3
 QMM_ERR_ALIGN, QMM_ERR_DEVICE, QMM_ERR_LAUNCH = -4, -5, -6
 

@@ -27,6 +27,7 @@ int block_elems(int dtype) {
     case QMM_Q4_1:
     case QMM_Q8_0: return 32;
     case QMM_Q4_K:
+    case QMM_Q5_K:
     case QMM_Q6_K: return 256;
     default: return 0;
     }
@@ -38,6 +39,7 @@ int block_bytes(int dtype) {
     case QMM_Q4_1: return 20;
     case QMM_Q8_0: return 34;
     case QMM_Q4_K: return 144;
+    case QMM_Q5_K: return 176;
     case QMM_Q6_K: return 210;
     default: return 0;
     }
@@ -96,7 +98,7 @@ int64_t mfma_from_n(int dtype, int64_t M, int64_t K) {
     }();
     if (lever) return lever;
     (void)M;
-    if (qmm::gemv_tokens_ok(dtype, K)) return dtype == QMM_Q4_K ? 3 : 5;
+    if (qmm::gemv_tokens_ok(dtype, K)) return (dtype == QMM_Q4_K || dtype == QMM_Q5_K) ? 3 : 5;
     return (dtype == QMM_Q4_0 || dtype == QMM_Q6_K) ? 3 : 2;
 }
 
@@ -116,7 +118,7 @@ const char *qmm_strerror(int code) {
     switch (code) {
     case QMM_OK: return "ok";
     case QMM_ERR_NULL: return "a required pointer is NULL";
-    case QMM_ERR_DTYPE: return "unsupported dtype (expected Q4_0=2, Q4_1=3, Q8_0=8, Q4_K=12 or Q6_K=14)";
+    case QMM_ERR_DTYPE: return "unsupported dtype (expected Q4_0=2, Q4_1=3, Q8_0=8, Q4_K=12, Q5_K=13 or Q6_K=14)";
     case QMM_ERR_SHAPE: return "bad shape (need M >= 1, N >= 1, K a positive multiple of the block size)";
     case QMM_ERR_ALIGN: return "misaligned pointer (blob and x/X need 16-byte, y/Y 4-byte alignment)";
     case QMM_ERR_DEVICE: return "no current HIP device, or it is not gfx950";

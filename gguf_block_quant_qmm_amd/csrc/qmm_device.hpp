@@ -18,6 +18,7 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 template <int DT> struct Geo;
 template <> struct Geo<QMM_Q4_0> { static constexpr int BS = 32, BB = 18; };
 template <> struct Geo<QMM_Q4_1> { static constexpr int BS = 32, BB = 20; };
+template <> struct Geo<QMM_Q5_K> { static constexpr int BS = 256, BB = 176; };
 template <> struct Geo<QMM_Q8_0> { static constexpr int BS = 32, BB = 34; };
 template <> struct Geo<QMM_Q4_K> { static constexpr int BS = 256, BB = 144; };
 template <> struct Geo<QMM_Q6_K> { static constexpr int BS = 256, BB = 210; };

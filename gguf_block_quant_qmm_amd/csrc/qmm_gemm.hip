@@ -176,6 +176,53 @@ template <bool GEN> struct WTile<QMM_Q4_K, GEN> {
     }
 };
 
+template <bool GEN> struct WTile<QMM_Q5_K, GEN> {
+    // As Q4_K's k-tile (chunk c, part = which 16 of its 32 nibble bytes), plus
+    // the 16 qh bytes of those elements (bit 2c: sub-block 2c, bit 2c+1: 2c+1).
+    // Super-blocks are 16-byte aligned whenever the blob is (176 = 11*16).
+    static constexpr int NDW = 12;  // 4 header dwords + 4 qh dwords + 4 nibble dwords
+    __device__ static bool exists(int64_t, int64_t, int) { return true; }
+    __device__ static void load(const uint8_t *row, int64_t k0, int part, uint32_t (&v)[NDW]) {
+        const uint8_t *sb = row + 176 * (k0 / 256);
+        const int c = (int)((k0 % 256) / 64);
+        uint32_t h[4], qh[4], q[4];
+        if (GEN) {
+            fetch_bytes(sb, 16, h);
+            fetch_bytes(sb + 16 + 16 * part, 16, qh);
+            fetch_bytes(sb + 48 + 32 * c + 16 * part, 16, q);
+        } else {
+            fetch_al(sb, h);
+            fetch_al(sb + 16 + 16 * part, qh);
+            fetch_al(sb + 48 + 32 * c + 16 * part, q);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; i++) { v[i] = h[i]; v[4 + i] = qh[i]; v[8 + i] = q[i]; }
+    }
+    __device__ static void store(const uint32_t (&v)[NDW], int part, _Float16 *wrow, int c) {
+        const float d = h2f(v[0]), dmin = h2f(v[0] >> 16);
+#pragma unroll
+        for (int half = 0; half < 2; half++) {
+            const int sub = 2 * c + half;
+            int sc, mn;
+            q4k_scale_min(v[1], v[2], v[3], sub, sc, mn);
+            const float dsc = d * (float)sc, ndm = -(dmin * (float)mn);
+            half8 o[2];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+#pragma unroll
+                for (int b = 0; b < 4; b++) {
+                    const int e = 4 * i + b;
+                    const uint32_t lo = (v[8 + i] >> (8 * b + 4 * half)) & 15u;
+                    const uint32_t hi = (v[4 + i] >> (8 * b + sub)) & 1u;
+                    o[e >> 3][e & 7] = (_Float16)fmaf(dsc, (float)(lo | (hi << 4)), ndm);
+                }
+            }
+            half8 *dst = reinterpret_cast<half8 *>(wrow + 32 * half + 16 * part);
+            dst[0] = o[0]; dst[1] = o[1];
+        }
+    }
+};
+
 template <bool GEN> struct WTile<QMM_Q6_K, GEN> {
     // k-tile = quarter qq = (k0%256)/64 of the super-block: h = qq/2,
     // groups g = 2(qq&1) + part, elements l = 0..31 of each group.
@@ -230,7 +277,7 @@ template <bool GEN> struct WTile<QMM_Q6_K, GEN> {
 template <int DT, bool GEN>
 __device__ __forceinline__ void wtile_store(const uint32_t (&v)[WTile<DT, GEN>::NDW], int part, _Float16 *wrow,
                                             int64_t k0) {
-    if constexpr (DT == QMM_Q4_K || DT == QMM_Q6_K)
+    if constexpr (DT == QMM_Q4_K || DT == QMM_Q5_K || DT == QMM_Q6_K)
         WTile<DT, GEN>::store(v, part, wrow, (int)((k0 % 256) / 64));
     else
         WTile<DT, GEN>::store(v, part, wrow);
@@ -537,6 +584,53 @@ template <> struct PDec<QMM_Q4_K> {
             const uint32_t w = r[4 + i], t = w >> 8;
             quad<false>(w & 0x000F000Fu, t & 0x000F000Fu, s0, n0, f[i >> 1], 4 * (i & 1));
             quad<false>(w & 0x00F000F0u, t & 0x00F000F0u, s1, n1, f[2 + (i >> 1)], 4 * (i & 1));
+        }
+    }
+};
+
+template <> struct PDec<QMM_Q5_K> {
+    // As PDec<QMM_Q4_K> (lane half kh: qs[32c + 16kh ..+16), the header with
+    // chunk 0, unpacked once into State), plus qh[16kh ..+16) with every
+    // chunk: bits 2c and 2c+1 join the codes as bit 4 (low nibbles, c 2^-24)
+    // and bit 8 (high nibbles, c 2^-20).
+    static constexpr int NW = 12;
+    static constexpr bool SWAP = true;
+    struct State { float s[8], n[8]; };
+    __device__ static int xpos(int c4) { return PDec<QMM_Q4_K>::xpos(c4); }
+    __device__ static void loadb(Rsrc rs, uint32_t roff, int64_t k0, int kh, int c, uint32_t (&r)[NW]) {
+        const uint32_t sb = (uint32_t)(176 * (k0 / 256));
+        if (c == 0) {
+            uint32_t h[4];
+            ldb(rs, roff, sb, h);
+#pragma unroll
+            for (int i = 0; i < 4; i++) r[i] = h[i];
+        }
+        uint32_t qh[4], q[4];
+        ldb(rs, roff + 16u * kh, sb + 16u, qh);
+        ldb(rs, roff + 16u * kh, sb + 48u + 32u * (uint32_t)c, q);
+#pragma unroll
+        for (int i = 0; i < 4; i++) { r[4 + i] = q[i]; r[8 + i] = qh[i]; }
+    }
+    __device__ static void decode(const uint32_t (&r)[NW], State &st, int, int c, int64_t, half8 (&f)[4]) {
+        if (c == 0) {
+            const float d = h2f(r[0]), dmin = h2f(r[0] >> 16);
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                int sc, mn;
+                q4k_scale_min(r[1], r[2], r[3], i, sc, mn);
+                st.s[i] = d * (float)sc * ((i & 1) ? 1048576.0f : TWO24);  // high nibbles enter as c * 2^-20
+                st.n[i] = -(dmin * (float)mn);
+            }
+        }
+        const float s0 = st.s[2 * c], n0 = st.n[2 * c], s1 = st.s[2 * c + 1], n1 = st.n[2 * c + 1];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const uint32_t w = r[4 + i], t = w >> 8;
+            const uint32_t hq = r[8 + i] >> (2 * c), ht = hq >> 8;
+            quad<false>((w & 0x000F000Fu) | ((hq << 4) & 0x00100010u), (t & 0x000F000Fu) | ((ht << 4) & 0x00100010u),
+                        s0, n0, f[i >> 1], 4 * (i & 1));
+            quad<false>((w & 0x00F000F0u) | ((hq << 7) & 0x01000100u), (t & 0x00F000F0u) | ((ht << 7) & 0x01000100u),
+                        s1, n1, f[2 + (i >> 1)], 4 * (i & 1));
         }
     }
 };
@@ -920,7 +1014,8 @@ static bool aligned_layout(int dtype, int64_t nb) {
     case QMM_Q8_0:
     case QMM_Q6_K: return (nb % 2) == 0;
     case QMM_Q4_1:
-    case QMM_Q4_K: return true;
+    case QMM_Q4_K:
+    case QMM_Q5_K: return true;
     default: return false;
     }
 }
@@ -1012,6 +1107,7 @@ hipError_t launch_gemm_mfma(int dtype, const void *blob_v, int64_t M, int64_t K,
     case QMM_Q4_1: return launch_dt<QMM_Q4_1>(blob, M, K, N, X, Y, st);
     case QMM_Q8_0: return launch_dt<QMM_Q8_0>(blob, M, K, N, X, Y, st);
     case QMM_Q4_K: return launch_dt<QMM_Q4_K>(blob, M, K, N, X, Y, st);
+    case QMM_Q5_K: return launch_dt<QMM_Q5_K>(blob, M, K, N, X, Y, st);
     case QMM_Q6_K: return launch_dt<QMM_Q6_K>(blob, M, K, N, X, Y, st);
     default: return hipErrorInvalidValue;
     }

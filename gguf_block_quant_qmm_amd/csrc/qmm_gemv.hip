@@ -212,6 +212,55 @@ template <> struct Unit<QMM_Q4_K> {
     }
 };
 
+template <> struct Unit<QMM_Q5_K> {
+    // As Q4_K (unit = 64-weight chunk c of a super-block: sub-blocks 2c, 2c+1),
+    // plus the fifth bit of every weight: bit i of qh[e] for element e of
+    // sub-block i.  The bit joins the code while it is still an exact f16
+    // subnormal: bit 4 of a low-nibble pair (c 2^-24), bit 8 of a high-nibble
+    // pair (c 2^-20).  Super-blocks are 176 = 11 * 16 bytes: 16-byte aligned.
+    static constexpr int NL = 20;  // 4 header dwords, 8 qh dwords, 8 nibble dwords
+    struct Off { uint32_t hdr, qs; int c; };
+    __device__ static Off lane_off(int u) {
+        const uint32_t h = 176u * (u >> 2);
+        return {h, h + 48u + 32u * (u & 3), u & 3};
+    }
+    __device__ static void load(Rsrc rs, uint32_t row, const Off &o, uint32_t (&v)[NL]) {
+        uint32_t h[12], q[8];
+        ldb(rs, o.hdr, row, h);  // d, dmin, scales, qh
+        ldb(rs, o.qs, row, q);
+#pragma unroll
+        for (int i = 0; i < 12; i++) v[i] = h[i];
+#pragma unroll
+        for (int i = 0; i < 8; i++) v[12 + i] = q[i];
+    }
+    __device__ static int x4(int u, int i) { return 16 * u + i; }
+    __device__ static float dot(const uint32_t (&v)[NL], const float (&xv)[64], const Off &o) {
+        const float d = h2f(v[0]), dmin = h2f(v[0] >> 16);
+        int sc0, m0, sc1, m1;
+        q4k_scale_min(v[1], v[2], v[3], 2 * o.c, sc0, m0);
+        q4k_scale_min(v[1], v[2], v[3], 2 * o.c + 1, sc1, m1);
+        const float s0 = d * (float)sc0 * TWO24, n0 = -(dmin * (float)m0);
+        const float s1 = d * (float)sc1 * TWO20, n1 = -(dmin * (float)m1);
+        float acc[4];
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const uint32_t dw = v[12 + i], t = dw >> 8;
+            const uint32_t hq = v[4 + i] >> (2 * o.c), ht = hq >> 8;  // qh[4i .. 4i+4), bits 2c and 2c+1 at 0, 1
+            const half2_t p0 = as_h2((dw & 0x000F000Fu) | ((hq << 4) & 0x00100010u));
+            const half2_t p1 = as_h2((dw & 0x00F000F0u) | ((hq << 7) & 0x01000100u));
+            const half2_t p2 = as_h2((t & 0x000F000Fu) | ((ht << 4) & 0x00100010u));
+            const half2_t p3 = as_h2((t & 0x00F000F0u) | ((ht << 7) & 0x01000100u));
+            const int c = 2 * (i & 1);
+            float l = i < 2 ? 0.f : acc[c], h = i < 2 ? 0.f : acc[c + 1];
+            l = fmaf(fma_h(p0.x, s0, n0), xv[4 * i], l);     h = fmaf(fma_h(p1.x, s1, n1), xv[32 + 4 * i], h);
+            l = fmaf(fma_h(p0.y, s0, n0), xv[4 * i + 2], l); h = fmaf(fma_h(p1.y, s1, n1), xv[32 + 4 * i + 2], h);
+            l = fmaf(fma_h(p2.x, s0, n0), xv[4 * i + 1], l); h = fmaf(fma_h(p3.x, s1, n1), xv[32 + 4 * i + 1], h);
+            l = fmaf(fma_h(p2.y, s0, n0), xv[4 * i + 3], l); h = fmaf(fma_h(p3.y, s1, n1), xv[32 + 4 * i + 3], h);
+            acc[c] = l; acc[c + 1] = h;
+        }
+        return (acc[0] + acc[2]) + (acc[1] + acc[3]);
+    }
+};
 template <> struct Unit<QMM_Q6_K> {
     // Unit u = 4 sb + 2 h + lh: the 64 weights {128h + 32g + 16lh + i : g < 4,
     // i < 16} of super-block sb, which share one 16-byte slice of each ql half
@@ -777,6 +826,33 @@ __device__ float block_dot_generic<QMM_Q4_K>(const uint8_t *p, const float *x) {
 }
 
 template <>
+__device__ float block_dot_generic<QMM_Q5_K>(const uint8_t *p, const float *x) {
+    const float d = h2f((uint32_t)p[0] | ((uint32_t)p[1] << 8));
+    const float dmin = h2f((uint32_t)p[2] | ((uint32_t)p[3] << 8));
+    uint32_t s[3];
+    for (int i = 0; i < 3; i++)
+        s[i] = (uint32_t)p[4 + 4 * i] | ((uint32_t)p[5 + 4 * i] << 8) | ((uint32_t)p[6 + 4 * i] << 16) |
+               ((uint32_t)p[7 + 4 * i] << 24);
+    float total = 0.f;
+    for (int i = 0; i < 8; i++) {
+        int sc, mn;
+        q4k_scale_min(s[0], s[1], s[2], i, sc, mn);
+        const float dsc = d * (float)sc, ndm = -(dmin * (float)mn);
+        float s0 = 0.f, s1 = 0.f;
+        for (int e = 0; e < 16; e++) {
+            const uint8_t b0 = p[48 + 32 * (i >> 1) + e], b1 = p[48 + 32 * (i >> 1) + 16 + e];
+            const int h0 = (p[16 + e] >> i) & 1, h1 = (p[32 + e] >> i) & 1;
+            const float q0 = (float)(((i & 1) ? (b0 >> 4) : (b0 & 15)) | (h0 << 4));
+            const float q1 = (float)(((i & 1) ? (b1 >> 4) : (b1 & 15)) | (h1 << 4));
+            s0 = fmaf(fmaf(dsc, q0, ndm), x[32 * i + e], s0);
+            s1 = fmaf(fmaf(dsc, q1, ndm), x[32 * i + 16 + e], s1);
+        }
+        total += s0 + s1;
+    }
+    return total;
+}
+
+template <>
 __device__ float block_dot_generic<QMM_Q6_K>(const uint8_t *p, const float *x) {
     const float d = h2f((uint32_t)p[208] | ((uint32_t)p[209] << 8));
     float total = 0.f;
@@ -832,7 +908,8 @@ static bool fast_layout_ok(int dtype, int64_t nb) {
     case QMM_Q4_1:
     case QMM_Q8_0:
     case QMM_Q6_K: return (nb % 2) == 0;
-    case QMM_Q4_K: return true;
+    case QMM_Q4_K:
+    case QMM_Q5_K: return true;
     default: return false;
     }
 }
@@ -873,7 +950,7 @@ static void launch_variant(int64_t nmax, dim3 grid, dim3 block, size_t lds, hipS
                        per_owner, extra)
     // Q4_K: with more than one row group fetched up front the compiler hoists
     // the scale unpacking of all of them and runs out of registers
-    constexpr int64_t flat_max = DT == QMM_Q4_K ? 1 : 4;
+    constexpr int64_t flat_max = (DT == QMM_Q4_K || DT == QMM_Q5_K) ? 1 : 4;
     switch (nmax <= flat_max ? nmax : 0) {
     case 1: QMM_GEMV_LAUNCH(true, 0); break;
     case 2: if constexpr (flat_max >= 2) QMM_GEMV_LAUNCH(true, 1); break;
@@ -916,7 +993,7 @@ static hipError_t launch_fast(const GemvMats &mats, int64_t K, const float *x, h
                 };
                 hipError_t e = big_lds(reinterpret_cast<const void *>(&gemv_kernel<DT, R, 0, false, true, MODE>));
                 if (e == hipSuccess) e = big_lds(reinterpret_cast<const void *>(&gemv_kernel<DT, R, D, false, false, MODE>));
-                if constexpr (DT != QMM_Q4_K) {
+                if constexpr (DT != QMM_Q4_K && DT != QMM_Q5_K) {
                     if (e == hipSuccess) e = big_lds(reinterpret_cast<const void *>(&gemv_kernel<DT, R, 1, false, true, MODE>));
                     if (e == hipSuccess) e = big_lds(reinterpret_cast<const void *>(&gemv_kernel<DT, R, 2, false, true, MODE>));
                     if (e == hipSuccess) e = big_lds(reinterpret_cast<const void *>(&gemv_kernel<DT, R, 3, false, true, MODE>));
@@ -983,7 +1060,7 @@ static hipError_t launch_mats(int n, const void *const *blobs, const int64_t *Ms
 }
 
 bool gemv_fused_ok(int dtype, int64_t K) {
-    const int64_t bs = (dtype == QMM_Q4_K || dtype == QMM_Q6_K) ? 256 : 32;  // Q4_0, Q4_1, Q8_0: 32
+    const int64_t bs = (dtype == QMM_Q4_K || dtype == QMM_Q5_K || dtype == QMM_Q6_K) ? 256 : 32;
     return fast_layout_ok(dtype, K / bs) && (K % 64) == 0 && K / 64 <= 256;
 }
 
@@ -1003,6 +1080,7 @@ hipError_t launch_gemv_concat(int n, const void *const *blobs, const int64_t *Ms
     case QMM_Q4_1: return launch_mats<QMM_Q4_1, 2, 3, GEMV_CONCAT>(n, blobs, Ms, K, x, ys, st, cus);
     case QMM_Q8_0: return launch_mats<QMM_Q8_0, 1, 4, GEMV_CONCAT>(n, blobs, Ms, K, x, ys, st, cus);
     case QMM_Q4_K: return launch_mats<QMM_Q4_K, 2, 3, GEMV_CONCAT>(n, blobs, Ms, K, x, ys, st, cus);
+    case QMM_Q5_K: return launch_mats<QMM_Q5_K, 1, 3, GEMV_CONCAT>(n, blobs, Ms, K, x, ys, st, cus);
     case QMM_Q6_K: return launch_mats<QMM_Q6_K, 1, 4, GEMV_CONCAT>(n, blobs, Ms, K, x, ys, st, cus);
     default: return hipErrorInvalidValue;
     }
@@ -1020,6 +1098,7 @@ hipError_t launch_gemv_swiglu(int dtype, const void *gate, const void *up, int64
     case QMM_Q4_1: return launch_mats<QMM_Q4_1, 1, 3, GEMV_SWIGLU>(2, blobs, Ms, K, x, ys, st, cus);
     case QMM_Q8_0: return launch_mats<QMM_Q8_0, 1, 2, GEMV_SWIGLU>(2, blobs, Ms, K, x, ys, st, cus);
     case QMM_Q4_K: return launch_mats<QMM_Q4_K, 1, 3, GEMV_SWIGLU>(2, blobs, Ms, K, x, ys, st, cus);
+    case QMM_Q5_K: return launch_mats<QMM_Q5_K, 1, 2, GEMV_SWIGLU>(2, blobs, Ms, K, x, ys, st, cus);
     case QMM_Q6_K: return launch_mats<QMM_Q6_K, 1, 2, GEMV_SWIGLU>(2, blobs, Ms, K, x, ys, st, cus);
     default: return hipErrorInvalidValue;
     }
@@ -1039,6 +1118,7 @@ hipError_t launch_gemv_argmax(int dtype, const void *blob, int64_t M, int64_t K,
     case QMM_Q4_1: e = launch_mats<QMM_Q4_1, 2, 3, GEMV_ARGMAX>(1, blobs, Ms, K, x, ys, st, cus, part, &grid); break;
     case QMM_Q8_0: e = launch_mats<QMM_Q8_0, 1, 4, GEMV_ARGMAX>(1, blobs, Ms, K, x, ys, st, cus, part, &grid); break;
     case QMM_Q4_K: e = launch_mats<QMM_Q4_K, 2, 3, GEMV_ARGMAX>(1, blobs, Ms, K, x, ys, st, cus, part, &grid); break;
+    case QMM_Q5_K: e = launch_mats<QMM_Q5_K, 1, 3, GEMV_ARGMAX>(1, blobs, Ms, K, x, ys, st, cus, part, &grid); break;
     case QMM_Q6_K: e = launch_mats<QMM_Q6_K, 1, 4, GEMV_ARGMAX>(1, blobs, Ms, K, x, ys, st, cus, part, &grid); break;
     default: return hipErrorInvalidValue;
     }
@@ -1055,7 +1135,7 @@ hipError_t launch_gemv_argmax(int dtype, const void *blob, int64_t M, int64_t K,
 constexpr int GEMV_TOKENS = 4;
 
 bool gemv_tokens_ok(int dtype, int64_t K) {
-    const int64_t bs = (dtype == QMM_Q4_K || dtype == QMM_Q6_K) ? 256 : 32;  // Q4_0, Q4_1, Q8_0: 32
+    const int64_t bs = (dtype == QMM_Q4_K || dtype == QMM_Q5_K || dtype == QMM_Q6_K) ? 256 : 32;
     return fast_layout_ok(dtype, K / bs) && (K % 64) == 0 && K / 64 <= 64;
 }
 
@@ -1093,6 +1173,7 @@ hipError_t launch_gemv_tokens(int dtype, const void *blob_v, int64_t M, int64_t 
         case QMM_Q4_1: e = launch_tokens<QMM_Q4_1, 2, 1>(blob, M, K, nt, Xp, Yp, st, cus); break;
         case QMM_Q8_0: e = launch_tokens<QMM_Q8_0, 2, 1>(blob, M, K, nt, Xp, Yp, st, cus); break;
         case QMM_Q4_K: e = launch_tokens<QMM_Q4_K, 1, 1>(blob, M, K, nt, Xp, Yp, st, cus); break;
+        case QMM_Q5_K: e = launch_tokens<QMM_Q5_K, 1, 1>(blob, M, K, nt, Xp, Yp, st, cus); break;
         case QMM_Q6_K: e = launch_tokens<QMM_Q6_K, 1, 1>(blob, M, K, nt, Xp, Yp, st, cus); break;
         default: return hipErrorInvalidValue;
         }
@@ -1104,13 +1185,14 @@ hipError_t launch_gemv_tokens(int dtype, const void *blob_v, int64_t M, int64_t 
 hipError_t launch_gemv(int dtype, const void *blob_v, int64_t M, int64_t K, const float *x, float *y,
                        hipStream_t st, int cus) {
     const uint8_t *blob = static_cast<const uint8_t *>(blob_v);
-    const int64_t bs = (dtype == QMM_Q4_K || dtype == QMM_Q6_K) ? 256 : 32;  // Q4_0, Q4_1, Q8_0: 32
+    const int64_t bs = (dtype == QMM_Q4_K || dtype == QMM_Q5_K || dtype == QMM_Q6_K) ? 256 : 32;
     const bool fast = fast_layout_ok(dtype, K / bs) && (K % 64) == 0;
     switch (dtype) {
     case QMM_Q4_0: return fast ? launch_one<QMM_Q4_0, 2, 3>(blob, M, K, x, y, st, cus) : launch_generic<QMM_Q4_0>(blob, M, K, x, y, st, cus);
     case QMM_Q4_1: return fast ? launch_one<QMM_Q4_1, 2, 3>(blob, M, K, x, y, st, cus) : launch_generic<QMM_Q4_1>(blob, M, K, x, y, st, cus);
     case QMM_Q8_0: return fast ? launch_one<QMM_Q8_0, 1, 4>(blob, M, K, x, y, st, cus) : launch_generic<QMM_Q8_0>(blob, M, K, x, y, st, cus);
     case QMM_Q4_K: return fast ? launch_one<QMM_Q4_K, 2, 3>(blob, M, K, x, y, st, cus) : launch_generic<QMM_Q4_K>(blob, M, K, x, y, st, cus);
+    case QMM_Q5_K: return fast ? launch_one<QMM_Q5_K, 1, 3>(blob, M, K, x, y, st, cus) : launch_generic<QMM_Q5_K>(blob, M, K, x, y, st, cus);
     case QMM_Q6_K: return fast ? launch_one<QMM_Q6_K, 1, 4>(blob, M, K, x, y, st, cus) : launch_generic<QMM_Q6_K>(blob, M, K, x, y, st, cus);
     default: return hipErrorInvalidValue;
     }

@@ -28,6 +28,10 @@
  *          (scale, min) for 8 sub-blocks of 32, 128 nibble bytes;
  *          w = d*sc*q - dmin*m  (same page, repack_q4_k_8x8; the 6-bit
  *          packing follows the standard GGUF k-quant layout)
+ *     Q5_K (256 weights, 176 B): as Q4_K with 32 bytes qh after the scales:
+ *          the fifth bit of element e of sub-block i is bit i of qh[e] (the
+ *          pages name the format, gemv_q5km_f32, but not its bytes: standard
+ *          GGUF layout)
  *     Q6_K (256 weights, 210 B): ql[128] low 4 bits, qh[64] high 2 bits,
  *          int8 sub-scales[16], f16 d;  w = d*sc*(q-32)  (210-byte size:
  *          page "cera 0.3.1 src/model/gpu_lfm2.rs", upload_weight; bit
@@ -66,12 +70,13 @@ extern "C" {
 #define QMM_Q4_1 3
 #define QMM_Q8_0 8
 #define QMM_Q4_K 12
+#define QMM_Q5_K 13
 #define QMM_Q6_K 14
 
 /* status codes */
 #define QMM_OK 0
 #define QMM_ERR_NULL (-1)    /* a required pointer is NULL                          */
-#define QMM_ERR_DTYPE (-2)   /* dtype is not one of the five tags above             */
+#define QMM_ERR_DTYPE (-2)   /* dtype is not one of the six tags above              */
 #define QMM_ERR_SHAPE (-3)   /* M < 1, N < 1, K < block_elems or K % block_elems    */
 #define QMM_ERR_ALIGN (-4)   /* blob not 16-B aligned, x/X not 16-B, y/Y not 4-B    */
 #define QMM_ERR_DEVICE (-5)  /* no current HIP device, or it is not gfx950          */
@@ -80,7 +85,7 @@ extern "C" {
 /* Decode GEMV (one token), page "cera 0.5.2 src/backend/cpu.rs", section
  * "GEMV (matrix-vector multiply)": y[m] = sum_k W[m][k] * x[k].
  *   w_blob  device, M*row_bytes bytes, 16-B aligned, row-major blocks
- *   dtype   QMM_Q4_0 | QMM_Q4_1 | QMM_Q8_0 | QMM_Q4_K | QMM_Q6_K
+ *   dtype   QMM_Q4_0 | QMM_Q4_1 | QMM_Q8_0 | QMM_Q4_K | QMM_Q5_K | QMM_Q6_K
  *   M, K    rows and weights per row; K a multiple of the block size
  *   x       device f32 [K], 16-B aligned
  *   y       device f32 [M], 4-B aligned; overwritten
@@ -156,8 +161,9 @@ int qmm_gemv_argmax(const void *w_blob, int dtype, int64_t M, int64_t K, const f
  * src/backend/cpu.rs": decode and prefill must agree bit for bit).  With K a
  * multiple of 64 up to 4096 and an even number of blocks per row (Q4_0, Q4_1,
  * Q8_0, Q6_K) up to 4 tokens share one read of the weights and the crossover
- * is N = 5 (Q4_0, Q4_1, Q8_0, Q6_K) or 3 (Q4_K); otherwise each token is one
- * GEMV launch and the crossover is 3 (Q4_0, Q6_K) or 2 (Q4_1, Q8_0, Q4_K).  The path
+ * is N = 5 (Q4_0, Q4_1, Q8_0, Q6_K) or 3 (Q4_K, Q5_K); otherwise each token is
+ * one GEMV launch and the crossover is 3 (Q4_0, Q6_K) or 2 (Q4_1, Q8_0, Q4_K,
+ * Q5_K).  The path
  * qmm_gemm_path names: 0 = all-f32 arithmetic (tolerance 1e-5 of
  * sum |w x|), 1 = weights and activations rounded to f16 and multiplied on
  * the matrix cores with f32 accumulation (tolerance 2e-3 of sum |w x|; needs

@@ -103,8 +103,9 @@ WORKLOADS = {
     8: ("sweep q4_0 4096x4096", Q4_0, 4096, 4096, [1, 2, 4, 8, 16, 32, 64, 128, 256, 512]),
     9: ("sweep q4_k 4096x4096", Q4_K, 4096, 4096, [1, 2, 4, 8, 16, 32, 64, 128, 256, 512]),
     10: ("sweep q6_k 4096x4096", Q6_K, 4096, 4096, [1, 2, 4, 8, 16, 32, 64, 128, 256, 512]),
-    # not a workload of the pages' tables: the remaining dtype, same sweep
+    # not workloads of the pages' tables: the added dtypes, same sweep
     11: ("sweep q4_1 4096x4096", Q4_1, 4096, 4096, [1, 2, 4, 8, 16, 32, 64, 128, 256, 512]),
+    12: ("sweep q5_k 4096x4096", Q5_K, 4096, 4096, [1, 2, 4, 8, 16, 32, 64, 128, 256, 512]),
 }
 
 

@@ -33,8 +33,8 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_geometry():
-    assert [q.block_elems(d) for d in (2, 3, 8, 12, 14)] == [32, 32, 32, 256, 256]
-    assert [q.block_bytes(d) for d in (2, 3, 8, 12, 14)] == [18, 20, 34, 144, 210]
+    assert [q.block_elems(d) for d in (2, 3, 8, 12, 13, 14)] == [32, 32, 32, 256, 256, 256]
+    assert [q.block_bytes(d) for d in (2, 3, 8, 12, 13, 14)] == [18, 20, 34, 144, 176, 210]
     assert q.block_elems(4) == 0 and q.block_bytes(99) == 0
     assert q.blob_bytes(q.QMM_Q4_1, 4096, 4096) == 4096 * 128 * 20
     # the tied Q6_K head of the 1B model on the pages: 2048 x 128256, ~205 MiB
@@ -106,6 +106,8 @@ def test_gemm_path_selection():
     assert q.gemm_path(q.QMM_Q4_1, 4096, 4096, 4) == 0
     assert q.gemm_path(q.QMM_Q4_1, 4096, 4096, 5) == 1
     assert q.gemm_path(q.QMM_Q4_1, 4096, 8192, 2) == 1
+    assert q.gemm_path(q.QMM_Q5_K, 4096, 4096, 2) == 0
+    assert q.gemm_path(q.QMM_Q5_K, 4096, 4096, 3) == 1
     assert q.gemm_path(q.QMM_Q4_K, 14336, 4096, 512) == 1
     assert q.gemm_path(q.QMM_Q4_K, 14336, 100, 512) == q.QMM_ERR_SHAPE
     assert q.tolerance(q.QMM_Q4_0, 4096, 4096, 1) == 1e-5

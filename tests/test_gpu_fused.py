@@ -27,8 +27,8 @@ from qmm_inputs import make_blob, make_x, rng_for
 
 pytestmark = pytest.mark.gpu
 
-DTYPES = [q.QMM_Q4_0, q.QMM_Q8_0, q.QMM_Q4_K, q.QMM_Q6_K, q.QMM_Q4_1]
-NAME = {2: "Q4_0", 3: "Q4_1", 8: "Q8_0", 12: "Q4_K", 14: "Q6_K"}
+DTYPES = [q.QMM_Q4_0, q.QMM_Q8_0, q.QMM_Q4_K, q.QMM_Q6_K, q.QMM_Q4_1, q.QMM_Q5_K]
+NAME = {2: "Q4_0", 3: "Q4_1", 8: "Q8_0", 12: "Q4_K", 13: "Q5_K", 14: "Q6_K"}
 TAU = 1e-5
 
 
@@ -44,7 +44,7 @@ def to_dev(a):
 
 
 def bs_of(dt):
-    return 256 if dt in (q.QMM_Q4_K, q.QMM_Q6_K) else 32
+    return 256 if dt in (q.QMM_Q4_K, q.QMM_Q5_K, q.QMM_Q6_K) else 32
 
 
 def gemv(dt, blob_d, M, K, x_d):
@@ -274,7 +274,7 @@ def test_argmax_ties_and_nan(dt):
     i, _ = check_argmax(dt, blob, M, K, x, f"{NAME[dt]} argmax with copies of the winner")
     assert i == min(w, 17), f"{NAME[dt]}: equal maxima at rows {w}, 17, ...: got {i}"
     # a NaN scale makes that row's output NaN: it never wins
-    off = {q.QMM_Q4_0: 0, q.QMM_Q4_1: 0, q.QMM_Q8_0: 0, q.QMM_Q4_K: 0, q.QMM_Q6_K: 208}[dt]
+    off = {q.QMM_Q4_0: 0, q.QMM_Q4_1: 0, q.QMM_Q8_0: 0, q.QMM_Q4_K: 0, q.QMM_Q5_K: 0, q.QMM_Q6_K: 208}[dt]
     nan = np.frombuffer(np.float16(np.nan).tobytes(), np.uint8)
     for r in (0, 17, min(w, 17)):
         rows[r, off:off + 2] = nan

@@ -21,8 +21,8 @@ from qmm_inputs import WORKLOADS, make_blob, make_x, rng_for
 
 pytestmark = pytest.mark.gpu
 
-DTYPES = [q.QMM_Q4_0, q.QMM_Q8_0, q.QMM_Q4_K, q.QMM_Q6_K, q.QMM_Q4_1]
-NAME = {2: "Q4_0", 3: "Q4_1", 8: "Q8_0", 12: "Q4_K", 14: "Q6_K"}
+DTYPES = [q.QMM_Q4_0, q.QMM_Q8_0, q.QMM_Q4_K, q.QMM_Q6_K, q.QMM_Q4_1, q.QMM_Q5_K]
+NAME = {2: "Q4_0", 3: "Q4_1", 8: "Q8_0", 12: "Q4_K", 13: "Q5_K", 14: "Q6_K"}
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -64,7 +64,7 @@ def check(Yg, Y64, S, tau, label):
 
 
 def bs_of(dt):
-    return 256 if dt in (q.QMM_Q4_K, q.QMM_Q6_K) else 32
+    return 256 if dt in (q.QMM_Q4_K, q.QMM_Q5_K, q.QMM_Q6_K) else 32
 
 
 # ----------------------------------------------------------------- GEMV ----
@@ -120,7 +120,7 @@ def test_gemm_small(dt, N):
         check(Yg, Y64, S, q.tolerance(dt, M, K, N), f"{NAME[dt]} gemm M={M} K={K} N={N}")
 
 
-@pytest.mark.parametrize("dt", [q.QMM_Q4_0, q.QMM_Q4_K, q.QMM_Q4_1], ids=NAME.get)
+@pytest.mark.parametrize("dt", [q.QMM_Q4_0, q.QMM_Q4_K, q.QMM_Q4_1, q.QMM_Q5_K], ids=NAME.get)
 def test_gemm_register_b_kernel_ragged(dt):
     # M/256 x N/128 >= 224 workgroups selects the register-B kernel for the
     # 4-bit formats; M and N both end in partial tiles.  Sampled rows include
@@ -161,7 +161,7 @@ def test_gemm_n1_is_gemv_bitwise_and_deterministic(dt):
 def test_zero_scales_give_exact_zero(dt):
     M, K = 45, 8 * bs_of(dt)
     blob = make_blob(dt, M, K, rng_for(800 + dt, 0)).reshape(M * (K // bs_of(dt)), -1)
-    offs = {2: [0], 3: [0, 2], 8: [0], 12: [0, 2], 14: [208]}[dt]
+    offs = {2: [0], 3: [0, 2], 8: [0], 12: [0, 2], 13: [0, 2], 14: [208]}[dt]
     for o in offs:
         blob[:, o:o + 2] = 0
     blob = blob.reshape(-1)
