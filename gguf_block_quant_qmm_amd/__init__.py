@@ -14,6 +14,8 @@ there is no CPU fallback.
                                                      out = silu(W_gate x) * (W_up x)
     qmm_gemv_argmax(w, dtype, M, K, x, work, index, value=None, stream=None)
                                                      index = argmax_m (W x)[m]
+    qmm_gemm_swiglu(gate, up, dtype, M, K, N, X, out, stream=None)
+                                                     out = silu(X Wg^T) * (X Wu^T)
 """
 from __future__ import annotations
 
@@ -33,8 +35,8 @@ QMM_ERR_ALIGN, QMM_ERR_DEVICE, QMM_ERR_LAUNCH = -4, -5, -6
 QMM_GEMV_MAX_MATS = 4
 QMM_ARGMAX_WORK_BYTES = 32768
 
-EXPORTS = ("qmm_gemv", "qmm_gemv_concat", "qmm_gemv_swiglu", "qmm_gemv_argmax", "qmm_gemm", "qmm_gemm_path", "qmm_blob_bytes",
-           "qmm_block_elems", "qmm_block_bytes", "qmm_strerror")
+EXPORTS = ("qmm_gemv", "qmm_gemv_concat", "qmm_gemv_swiglu", "qmm_gemv_argmax", "qmm_gemm", "qmm_gemm_swiglu",
+           "qmm_gemm_path", "qmm_blob_bytes", "qmm_block_elems", "qmm_block_bytes", "qmm_strerror")
 
 _lib = None
 
@@ -61,6 +63,8 @@ def lib():
         L.qmm_gemv_swiglu.restype = ci
         L.qmm_gemv_argmax.argtypes = [vp, ci, i64, i64, vp, vp, vp, vp, vp]
         L.qmm_gemv_argmax.restype = ci
+        L.qmm_gemm_swiglu.argtypes = [vp, vp, ci, i64, i64, i64, vp, vp, vp]
+        L.qmm_gemm_swiglu.restype = ci
         L.qmm_gemm.argtypes = [vp, ci, i64, i64, i64, vp, vp, vp]
         L.qmm_gemm.restype = ci
         L.qmm_gemm_path.argtypes = [ci, i64, i64, i64]
@@ -179,3 +183,13 @@ def qmm_gemv_argmax(w, dtype: int, M: int, K: int, x, work, index, value=None, s
                                _stream(stream))
     if rc != QMM_OK:
         raise QmmError(rc, "qmm_gemv_argmax")
+
+
+def qmm_gemm_swiglu(gate, up, dtype: int, M: int, K: int, N: int, X, out, stream=None) -> None:
+    import torch
+    nb = blob_bytes(dtype, M, K) or None
+    rc = lib().qmm_gemm_swiglu(_addr(gate, nb, "gate"), _addr(up, nb, "up"), dtype, M, K, N,
+                               _addr(X, 4 * N * K, "X", torch.float32), _addr(out, 4 * N * M, "out", torch.float32),
+                               _stream(stream))
+    if rc != QMM_OK:
+        raise QmmError(rc, "qmm_gemm_swiglu")

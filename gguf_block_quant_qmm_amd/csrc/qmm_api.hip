@@ -193,6 +193,29 @@ int qmm_gemv_argmax(const void *w_blob, int dtype, int64_t M, int64_t K, const f
     return e == hipSuccess ? QMM_OK : QMM_ERR_LAUNCH;
 }
 
+int qmm_gemm_swiglu(const void *gate_blob, const void *up_blob, int dtype, int64_t M, int64_t K, int64_t N,
+                    const float *X, float *out, void *stream) {
+    int rc = check_shape(dtype, M, K, N);
+    if (rc != QMM_OK) return rc;
+    const bool f32 = N < mfma_from_n(dtype, M, K);
+    if (f32 ? !qmm::gemv_fused_ok(dtype, K) : !qmm::gemm_swiglu_ok(dtype, K)) return QMM_ERR_SHAPE;
+    if (!gate_blob || !up_blob || !X || !out) return QMM_ERR_NULL;
+    if (!aligned(gate_blob, 16) || !aligned(up_blob, 16) || !aligned(X, 16) || !aligned(out, 4)) return QMM_ERR_ALIGN;
+    int cus = 0;
+    rc = current_device(&cus);
+    if (rc != QMM_OK) return rc;
+    hipError_t e = hipSuccess;
+    if (f32) {
+        // the decode form per token: its bits, token by token
+        for (int64_t n = 0; n < N && e == hipSuccess; n++)
+            e = qmm::launch_gemv_swiglu(dtype, gate_blob, up_blob, M, K, X + n * K, out + n * M, (hipStream_t)stream,
+                                        cus);
+    } else {
+        e = qmm::launch_gemm_swiglu(dtype, gate_blob, up_blob, M, K, N, X, out, (hipStream_t)stream);
+    }
+    return e == hipSuccess ? QMM_OK : QMM_ERR_LAUNCH;
+}
+
 int qmm_gemm(const void *w_blob, int dtype, int64_t M, int64_t K, int64_t N, const float *X, float *Y,
              void *stream) {
     int rc = check_shape(dtype, M, K, N);

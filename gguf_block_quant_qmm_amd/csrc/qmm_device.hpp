@@ -99,6 +99,16 @@ __device__ __forceinline__ float wave_sum(float v) {
 // Sum over the 64 lanes of a wavefront in a fixed order, result valid in
 // lane 63: DPP butterflies inside each row of 16 lanes, then the row
 // broadcasts of lane 15 / lane 31.
+// silu(v) = v * sigmoid(v) = v / (1 + e^-v) (page "cera 0.5.2
+// src/backend/cpu.rs", activation functions), evaluated with e = e^-|v| so
+// that the exponential never overflows: v / (1 + e) for v >= 0 and
+// v e / (1 + e) for v < 0 (the same function; tiny negative tails keep their
+// value instead of becoming -0 where e^-v would overflow).
+__device__ __forceinline__ float silu(float v) {
+    const float e = expf(-fabsf(v));
+    return (v >= 0.f ? v : v * e) / (1.0f + e);
+}
+
 __device__ __forceinline__ float wave_sum_to_lane63(float v) {
     v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));  // quad_perm 1,0,3,2
     v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true));  // quad_perm 2,3,0,1

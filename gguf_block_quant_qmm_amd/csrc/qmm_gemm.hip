@@ -715,11 +715,20 @@ template <> struct WbDec<QMM_Q6_K> { using type = BDec<QMM_Q6_K>; };
 // ordered so that the ones sharing a weight tile run on the same XCD (the
 // dispatcher sends workgroup b to XCD b % 8), whose L2 then serves the
 // weights to all token tiles.
-template <int DT, int TM, int BN, int WD, int W, int INTERLEAVE, int XD>
-__global__ void __launch_bounds__(64 * W) gemm_wb_kernel(const uint8_t *__restrict__ blob, int64_t M, int64_t K,
+//
+// SWI (gate/up projection with SwiGLU, page "cera 0.5.2 src/backend/cpu.rs":
+// the fused gate + up + SiLU GEMM dispatch): TM = 64 and each wavefront's
+// two 32-row fragments are the same 32 rows of the gate matrix (blob) and of
+// the up matrix (blob_up); the epilogue writes silu(gate) * up for those 32
+// output rows, so neither projection is ever stored.
+template <int DT, int TM, int BN, int WD, int W, int INTERLEAVE, int XD, bool SWI = false>
+__global__ void __launch_bounds__(64 * W) gemm_wb_kernel(const uint8_t *__restrict__ blob,
+                                                        const uint8_t *__restrict__ blob_up, int64_t M, int64_t K,
                                                         int64_t N, int64_t row_bytes, const float *__restrict__ X,
                                                         float *__restrict__ Y, int n_mtiles, int n_ntiles) {
     constexpr int FM = TM / 32, FN = BN / 32;
+    constexpr int OT = SWI ? 32 : TM;  // output rows per wavefront
+    static_assert(!SWI || FM == 2, "the SwiGLU form pairs one gate and one up fragment");
     constexpr int NT = 64 * W;
     constexpr int NX4 = BN * (BK / 4);          // float4 of X per k-tile
     constexpr int NXF = (NX4 + NT - 1) / NT;    // per thread (the last ones repeat a valid float4)
@@ -733,14 +742,16 @@ __global__ void __launch_bounds__(64 * W) gemm_wb_kernel(const uint8_t *__restri
     const int total = n_mtiles * n_ntiles, b = blockIdx.x, xcd = b & 7, local = b >> 3;
     const int tile = xcd * (total >> 3) + (xcd < (total & 7) ? xcd : (total & 7)) + local;
     const int64_t mt = tile / n_ntiles, nt = tile % n_ntiles;
-    const int64_t n0 = nt * BN, mw = mt * (W * TM) + wave * TM;
+    const int64_t n0 = nt * BN, mw = mt * (W * OT) + wave * OT;
     const int64_t nkt = K / BK;
 
-    const int64_t wrows = M - mw < 0 ? 0 : (M - mw < TM ? M - mw : TM);
+    const int64_t wrows = M - mw < 0 ? 0 : (M - mw < OT ? M - mw : OT);
     const Rsrc wrs = make_rsrc_uniform(blob + (wrows ? mw : 0) * row_bytes, (uint32_t)(wrows * row_bytes));
+    const Rsrc wrs_up = make_rsrc_uniform((SWI ? blob_up : blob) + (wrows ? mw : 0) * row_bytes,
+                                          (uint32_t)(wrows * row_bytes));
     uint32_t roff[FM];
 #pragma unroll
-    for (int j = 0; j < FM; j++) roff[j] = (uint32_t)((32 * j + (lane & 31)) * row_bytes);
+    for (int j = 0; j < FM; j++) roff[j] = (uint32_t)(((SWI ? 0 : 32 * j) + (lane & 31)) * row_bytes);
     const int64_t xrows = N - n0 < BN ? N - n0 : BN;
     const Rsrc xrs = make_rsrc_uniform(X + n0 * K, (uint32_t)(xrows * K * 4));
     uint32_t xoff[NXF];
@@ -759,7 +770,7 @@ __global__ void __launch_bounds__(64 * W) gemm_wb_kernel(const uint8_t *__restri
     auto wload = [&](int64_t kt, int c, uint32_t (&w)[FM][BD::NW]) {
         const int64_t kc = kt < nkt ? kt : nkt - 4 + c;
 #pragma unroll
-        for (int j = 0; j < FM; j++) BD::loadb(wrs, roff[j], kc * BK, kh, c, w[j]);
+        for (int j = 0; j < FM; j++) BD::loadb(SWI && j ? wrs_up : wrs, roff[j], kc * BK, kh, c, w[j]);
     };
     auto xload = [&](int64_t kt, floatx4 (&x)[NXF]) {
         const uint32_t kb = (uint32_t)((kt < nkt ? kt : nkt - 1) * BK * 4);
@@ -843,16 +854,29 @@ __global__ void __launch_bounds__(64 * W) gemm_wb_kernel(const uint8_t *__restri
         }
     }
 
+    if constexpr (SWI) {
 #pragma unroll
-    for (int i = 0; i < FN; i++) {
-#pragma unroll
-        for (int j = 0; j < FM; j++) {
-            const int64_t m = mw + 32 * j + (lane & 31);
+        for (int i = 0; i < FN; i++) {
+            const int64_t m = mw + (lane & 31);
             if (m >= M) continue;
 #pragma unroll
             for (int v = 0; v < 16; v++) {
                 const int64_t n = n0 + 32 * i + 8 * (v >> 2) + 4 * kh + (v & 3);
-                if (n < N) Y[n * M + m] = acc[i][j][v];
+                if (n < N) Y[n * M + m] = silu(acc[i][0][v]) * acc[i][1][v];
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < FN; i++) {
+#pragma unroll
+            for (int j = 0; j < FM; j++) {
+                const int64_t m = mw + 32 * j + (lane & 31);
+                if (m >= M) continue;
+#pragma unroll
+                for (int v = 0; v < 16; v++) {
+                    const int64_t n = n0 + 32 * i + 8 * (v >> 2) + 4 * kh + (v & 3);
+                    if (n < N) Y[n * M + m] = acc[i][j][v];
+                }
             }
         }
     }
@@ -1038,16 +1062,17 @@ static hipError_t launch_tile(const uint8_t *blob, int64_t M, int64_t K, int64_t
 }
 
 
-template <int DT, int TM, int BN, int WD, int W, int IL = 0, int XD = 2>
+template <int DT, int TM, int BN, int WD, int W, int IL = 0, int XD = 2, bool SWI = false>
 static hipError_t launch_wb(const uint8_t *blob, int64_t M, int64_t K, int64_t N, const float *X, float *Y,
-                            hipStream_t st) {
+                            hipStream_t st, const uint8_t *blob_up = nullptr) {
     constexpr int BS = Geo<DT>::BS, BB = Geo<DT>::BB;
+    constexpr int OT = SWI ? 32 : TM;
     const int64_t row_bytes = (K / BS) * BB;
-    const int64_t mtiles = (M + W * TM - 1) / (W * TM), ntiles = (N + BN - 1) / BN;
+    const int64_t mtiles = (M + W * OT - 1) / (W * OT), ntiles = (N + BN - 1) / BN;
     const int64_t grid = mtiles * ntiles;
     if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((gemm_wb_kernel<DT, TM, BN, WD, W, IL, XD>), dim3((unsigned)grid), dim3(64 * W), 0, st, blob, M, K, N,
-                       row_bytes, X, Y, (int)mtiles, (int)ntiles);
+    hipLaunchKernelGGL((gemm_wb_kernel<DT, TM, BN, WD, W, IL, XD, SWI>), dim3((unsigned)grid), dim3(64 * W), 0, st,
+                       blob, blob_up, M, K, N, row_bytes, X, Y, (int)mtiles, (int)ntiles);
     return hipGetLastError();
 }
 
@@ -1097,6 +1122,61 @@ static hipError_t launch_dt(const uint8_t *blob, int64_t M, int64_t K, int64_t N
     if (N <= 32) return launch_tile<DT, 128, 32, 1, 4>(blob, M, K, N, X, Y, st, gen);
     if (N <= 64) return launch_tile<DT, 128, 64, 1, 4>(blob, M, K, N, X, Y, st, gen);
     return launch_tile<DT, 128, 128, 2, 2>(blob, M, K, N, X, Y, st, gen);
+}
+
+// The gate/up projection with SwiGLU on the matrix cores: 4 wavefronts x 32
+// output rows (64 decoded weight rows each) x 64 tokens.  Needs K a multiple
+// of 256 with the register-B layout (gemm_swiglu_ok).
+bool gemm_swiglu_ok(int dtype, int64_t K) {
+    const int64_t bs = (dtype == QMM_Q4_K || dtype == QMM_Q5_K || dtype == QMM_Q6_K) ? 256 : 32;
+    return aligned_layout(dtype, K / bs) && (K % (4 * BK)) == 0 && K * 4 * 128 < ((int64_t)1 << 31);
+}
+
+static int swiglu_choice() {
+    static int v = [] {
+        const char *e = getenv("QMM_SWIGLU_KERNEL");
+        return e ? atoi(e) : 0;
+    }();
+    return v;
+}
+
+// Tile for the SwiGLU form (4 wavefronts x 32 output rows; tokens per tile
+// BN), measured on the 14336 x 4096 gate/up pair against two plain GEMMs:
+//   N <= 64:          BN = 32   (Q4_K N = 64: 51.6 vs 71.8 us)
+//   N <= 160:         BN = 64   (N = 128: 66.0 vs 76.8 us)
+//   N <= 320:         BN = 128  (N = 256: 91.8 vs 124.5 us)
+//   N <= 448:         BN = 64   (N = 384: 172 vs 199 us)
+//   beyond:           BN = 128  (N = 512: 201 vs 176 us: the one case where
+//                     two GEMMs plus a separate pass would be faster, given
+//                     scratch for both projections)
+// QMM_SWIGLU_KERNEL = 1..4 forces BN = 32 / 64 / 128 / 64 with 8 wavefronts
+// (a measurement lever, read once).
+template <int DT>
+static hipError_t launch_swiglu_dt(const uint8_t *g, const uint8_t *u, int64_t M, int64_t K, int64_t N,
+                                   const float *X, float *Y, hipStream_t st) {
+    int choice = swiglu_choice();
+    if (choice < 1 || choice > 4) choice = N <= 64 ? 1 : N <= 160 ? 2 : N <= 320 ? 3 : N <= 448 ? 2 : 3;
+    switch (choice) {
+    case 1: return launch_wb<DT, 64, 32, 2, 4, 0, 2, true>(g, M, K, N, X, Y, st, u);
+    case 2: return launch_wb<DT, 64, 64, 2, 4, 0, 2, true>(g, M, K, N, X, Y, st, u);
+    case 3: return launch_wb<DT, 64, 128, 2, 4, 4, 2, true>(g, M, K, N, X, Y, st, u);
+    default: return launch_wb<DT, 64, 64, 2, 8, 0, 2, true>(g, M, K, N, X, Y, st, u);
+    }
+}
+
+hipError_t launch_gemm_swiglu(int dtype, const void *gate, const void *up, int64_t M, int64_t K, int64_t N,
+                              const float *X, float *Y, hipStream_t st) {
+    if (!gemm_swiglu_ok(dtype, K)) return hipErrorInvalidValue;
+    const uint8_t *g = static_cast<const uint8_t *>(gate), *u = static_cast<const uint8_t *>(up);
+    switch (dtype) {
+    case QMM_Q4_0: return launch_swiglu_dt<QMM_Q4_0>(g, u, M, K, N, X, Y, st);
+    case QMM_Q4_1: return launch_swiglu_dt<QMM_Q4_1>(g, u, M, K, N, X, Y, st);
+    case QMM_Q8_0: return launch_swiglu_dt<QMM_Q8_0>(g, u, M, K, N, X, Y, st);
+    case QMM_Q4_K: return launch_swiglu_dt<QMM_Q4_K>(g, u, M, K, N, X, Y, st);
+    case QMM_Q5_K: return launch_swiglu_dt<QMM_Q5_K>(g, u, M, K, N, X, Y, st);
+    case QMM_Q6_K: return launch_swiglu_dt<QMM_Q6_K>(g, u, M, K, N, X, Y, st);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_gemm_mfma(int dtype, const void *blob_v, int64_t M, int64_t K, int64_t N, const float *X, float *Y,

@@ -453,16 +453,6 @@ __device__ __forceinline__ int64_t lo_of(const GemvMats &m, int i) {
     return v;
 }
 
-// silu(v) = v * sigmoid(v) = v / (1 + e^-v) (page "cera 0.5.2
-// src/backend/cpu.rs", activation functions), evaluated with e = e^-|v| so
-// that the exponential never overflows: v / (1 + e) for v >= 0 and
-// v e / (1 + e) for v < 0 (the same function; tiny negative tails keep their
-// value instead of becoming -0 where e^-v would overflow).
-__device__ __forceinline__ float silu(float v) {
-    const float e = expf(-fabsf(v));
-    return (v >= 0.f ? v : v * e) / (1.0f + e);
-}
-
 template <int DT, int R, int D, bool WAVE_ROWS, bool FLAT, int MODE>
 __global__ void __launch_bounds__(256) gemv_kernel(const GemvMats mats, int64_t row_bytes, int U,
                                                    const float *__restrict__ x, int64_t per_owner, int64_t extra) {

@@ -33,6 +33,11 @@ bool gemv_tokens_ok(int dtype, int64_t K);
 hipError_t launch_gemv_tokens(int dtype, const void *blob, int64_t M, int64_t K, int64_t N, const float *X,
                               float *Y, hipStream_t st, int cus);
 
+// Y[N][M] = silu(X Wg^T) * (X Wu^T) on the matrix cores (one launch).
+bool gemm_swiglu_ok(int dtype, int64_t K);
+hipError_t launch_gemm_swiglu(int dtype, const void *gate, const void *up, int64_t M, int64_t K, int64_t N,
+                              const float *X, float *Y, hipStream_t st);
+
 // Y[N][M] = X W^T on the matrix cores (f16 operands, f32 accumulation).
 hipError_t launch_gemm_mfma(int dtype, const void *blob, int64_t M, int64_t K, int64_t N, const float *X,
                             float *Y, hipStream_t st);

@@ -171,6 +171,22 @@ int qmm_gemv_argmax(const void *w_blob, int dtype, int64_t M, int64_t K, const f
 int qmm_gemm(const void *w_blob, int dtype, int64_t M, int64_t K, int64_t N,
              const float *X, float *Y, void *stream);
 
+/* The gate/up projection with SwiGLU for N tokens, one launch on the matrix
+ * cores (page "cera 0.5.2 src/backend/cpu.rs", the fused gate + up + SiLU
+ * GEMM dispatch; cpu.rs silu_mul_inplace for the activation):
+ *     out[n][m] = silu(G[n][m]) * U[n][m],  G = X W_gate^T,  U = X W_up^T
+ * Below the crossover that qmm_gemm_path reports as 0, each token runs
+ * qmm_gemv_swiglu (same bits, same bound); on path 1 G and U are the f16
+ * matrix-core sums (tolerance 2e-3 of their sum |w x|) carried into the
+ * SwiGLU bound of qmm_gemv_swiglu with tau = 2e-3.  Neither projection is
+ * stored.  Path 0 needs the shapes qmm_gemv_swiglu takes; path 1 needs K a
+ * multiple of 256 (512 for Q6_K); otherwise QMM_ERR_SHAPE.
+ *   gate_blob, up_blob  device blobs of one dtype and shape M x K
+ *   X                   device f32 [N][K], 16-B aligned
+ *   out                 device f32 [N][M], 4-B aligned; overwritten */
+int qmm_gemm_swiglu(const void *gate_blob, const void *up_blob, int dtype, int64_t M, int64_t K,
+                    int64_t N, const float *X, float *out, void *stream);
+
 /* Which arithmetic qmm_gemm uses for these sizes: 0 = f32 (GEMV family),
  * 1 = f16 matrix-core GEMM, or a negative status for invalid arguments. */
 int qmm_gemm_path(int dtype, int64_t M, int64_t K, int64_t N);

@@ -196,3 +196,30 @@ def test_argmax_without_value_and_gpu_reports_device():
     if torch.cuda.is_available():
         pytest.skip("a GPU is present; covered by the GPU tests")
     assert q.lib().qmm_gemv_argmax(A16, 2, 8, 64, A16, A16, A16, None, None) == q.QMM_ERR_DEVICE
+
+
+@pytest.mark.parametrize("args,code", [
+    ((A16, A16, 5, 8, 1024, 4, A16, A16), q.QMM_ERR_DTYPE),
+    ((A16, A16, 2, 8, 1024, 0, A16, A16), q.QMM_ERR_SHAPE),
+    ((A16, A16, 12, 8, 16640, 1, A16, A16), q.QMM_ERR_SHAPE),   # f32 path: K > 16384
+    ((A16, A16, 2, 8, 96, 2, A16, A16), q.QMM_ERR_SHAPE),       # f32 path: odd Q4_0 block count
+    ((A16, A16, 2, 8, 1088, 64, A16, A16), q.QMM_ERR_SHAPE),    # matrix cores: K not a multiple of 256
+    ((A16, A16, 14, 8, 768, 64, A16, A16), q.QMM_ERR_SHAPE),    # Q6_K: odd super-block count
+    ((0, A16, 2, 8, 1024, 64, A16, A16), q.QMM_ERR_NULL),
+    ((A16, 0, 2, 8, 1024, 64, A16, A16), q.QMM_ERR_NULL),
+    ((A16, A16, 2, 8, 1024, 64, 0, A16), q.QMM_ERR_NULL),
+    ((A16, A16, 2, 8, 1024, 64, A16, 0), q.QMM_ERR_NULL),
+    ((A16, A16 + 4, 2, 8, 1024, 64, A16, A16), q.QMM_ERR_ALIGN),
+    ((A16, A16, 2, 8, 1024, 64, A16 + 8, A16), q.QMM_ERR_ALIGN),
+    ((A16, A16, 2, 8, 1024, 64, A16, A16 + 1), q.QMM_ERR_ALIGN),
+])
+def test_gemm_swiglu_rejects(args, code):
+    assert q.lib().qmm_gemm_swiglu(*args, None) == code
+
+
+def test_gemm_swiglu_without_gpu_reports_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; covered by the GPU tests")
+    assert q.lib().qmm_gemm_swiglu(A16, A16, 12, 8, 1024, 64, A16, A16, None) == q.QMM_ERR_DEVICE
+    assert q.lib().qmm_gemm_swiglu(A16, A16, 2, 8, 1024, 2, A16, A16, None) == q.QMM_ERR_DEVICE

@@ -299,3 +299,64 @@ def test_argmax_lm_head_full_size():
     top2 = np.sort(Y64[0])[-2:]
     if top2[1] - top2[0] > 2 * TAU * S.max():
         assert i == oi, f"clear winner {oi}, got {i}"
+
+
+# ------------------------------------------------------------ SwiGLU, N tokens
+#
+# qmm_gemm_swiglu: on path 0 every token is qmm_gemv_swiglu (same bits); on
+# the matrix cores the SwiGLU bound above holds with tau = 2e-3.
+
+def check_swiglu_tau(out, r, tau, label):
+    out = out.astype(np.float64)
+    g, u, sg, su, exact = r["g"], r["u"], r["sg"], r["su"], r["out64"]
+    with np.errstate(over="ignore"):
+        silu_g = g / (1.0 + np.exp(-g))
+    bound = tau * (1.1 * sg * (np.abs(u) + tau * su) + np.abs(silu_g) * su) + 4 * 2.0 ** -24 * np.abs(exact)
+    assert np.all(np.isfinite(out)), f"{label}: non-finite output"
+    zero = (sg == 0) | (su == 0)
+    assert np.all(out[zero] == 0), f"{label}: a zero projection must give exactly 0"
+    bad = np.abs(out - exact) > bound
+    assert not bad.any(), f"{label}: {int(bad.sum())} outputs outside the bound"
+
+
+def gemm_swiglu_shapes(dt):
+    return [(67, 512), (300, 1024), (129, 4096)]
+
+
+@pytest.mark.parametrize("dt", DTYPES, ids=NAME.get)
+def test_gemm_swiglu(dt):
+    for i, (M, K) in enumerate(gemm_swiglu_shapes(dt)):
+        gate = make_blob(dt, M, K, rng_for(900 + dt, i))
+        up = make_blob(dt, M, K, rng_for(900 + dt, 100 + i))
+        gd, ud = to_dev(gate), to_dev(up)
+        for N in (2, 3, 5, 17, 64, 130):
+            X = make_x(N, K, rng_for(900 + dt, 1000 * N + i))
+            Xd = to_dev(X)
+            out = torch.full((N, M), float("nan"), device="cuda")
+            q.qmm_gemm_swiglu(gd, ud, dt, M, K, N, Xd, out)
+            torch.cuda.synchronize()
+            label = f"{NAME[dt]} gemm swiglu M={M} K={K} N={N}"
+            tau = q.tolerance(dt, M, K, N)
+            r = oracle.swiglu(dt, gate, up, M, K, X)
+            check_swiglu_tau(out.cpu().numpy(), r, tau, label)
+            if q.gemm_path(dt, M, K, N) == 0:
+                for n in range(N):
+                    o1 = torch.empty(M, device="cuda")
+                    q.qmm_gemv_swiglu(gd, ud, dt, M, K, Xd[n], o1)
+                    torch.cuda.synchronize()
+                    assert torch.equal(o1, out[n]), f"{label}: token {n} differs from qmm_gemv_swiglu"
+
+
+def test_gemm_swiglu_llama8b_prefill():
+    """LLaMA-8B gate/up (14336 x 4096, Q4_K) over 512 tokens, sampled rows."""
+    dt, M, K, N = q.QMM_Q4_K, 14336, 4096, 512
+    gate = make_blob(dt, M, K, rng_for(950, 0))
+    up = make_blob(dt, M, K, rng_for(950, 1))
+    X = make_x(N, K, rng_for(950, 2))
+    out = torch.full((N, M), float("nan"), device="cuda")
+    q.qmm_gemm_swiglu(to_dev(gate), to_dev(up), dt, M, K, N, to_dev(X), out)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(3), M - 1 - np.arange(3),
+                                     np.random.default_rng(951).choice(M, 120, replace=False)]))
+    r = oracle.swiglu(dt, gate, up, M, K, X, rows=rows)
+    check_swiglu_tau(out.cpu().numpy()[:, rows], r, 2e-3, "Q4_K gemm swiglu 14336x4096 N=512")
