@@ -141,6 +141,9 @@ int qmm_gemv_swiglu(const void *gate_blob, const void *up_blob, int dtype, int64
  *           caller-owned; needs no initial value; clobbered
  *   index   device int64, 8-B aligned
  *   value   device f32 or NULL
+ * An embedding table used as a tied LM head may carry padding rows past the
+ * vocabulary (page "cera 0.5.0 src/model/llama.rs", project_logits_batched):
+ * pass M = the vocabulary size; rows past M are never read.
  * Two launches on `stream` (the rows, then the winner).  Needs K a multiple
  * of 64, at most 16384, and an even number of blocks per row for Q4_0, Q4_1,
  * Q8_0 and Q6_K; otherwise QMM_ERR_SHAPE.  Concurrent calls need separate work
