@@ -56,6 +56,10 @@ def _bind(lib):
     lib.oracle_silu.restype = ctypes.c_double
     lib.oracle_swiglu_rows.argtypes = [ctypes.c_int, vp, vp, i64, i64, i64, vp, i64, vp, vp, vp, vp, vp, vp, vp]
     lib.oracle_argmax.argtypes = [ctypes.c_int, vp, i64, i64, vp, vp, vp, vp]
+    lib.oracle_float_to_half.argtypes = [ctypes.c_float]
+    lib.oracle_float_to_half.restype = ctypes.c_uint16
+    lib.oracle_quantize_q8_0.argtypes = [vp, i64, i64, vp, vp]
+    lib.oracle_matmul_q8act_rows.argtypes = [ctypes.c_int, vp, i64, i64, i64, vp, vp, i64, vp, vp, vp, vp, vp]
     return lib
 
 
@@ -191,3 +195,57 @@ def argmax(dtype: int, blob: np.ndarray, M: int, K: int, x: np.ndarray, L=None):
 
 def num_threads() -> int:
     return lib().oracle_num_threads()
+
+
+def float_to_half(v: float, L=None) -> int:
+    """The binary16 bits of f32 v, rounded to nearest even."""
+    return (L or lib()).oracle_float_to_half(float(np.float32(v)))
+
+
+def quantize_q8_0(X: np.ndarray, L=None):
+    """X f32 [N][K] (K % 32 == 0) -> (scales f32 [N][K/32], quants int8 [N][K])."""
+    X = np.ascontiguousarray(X, dtype=np.float32)
+    if X.ndim == 1:
+        X = X[None, :]
+    N, K = X.shape
+    scales = np.empty((N, K // 32), dtype=np.float32)
+    quants = np.empty((N, K), dtype=np.int8)
+    _check((L or lib()).oracle_quantize_q8_0(_ptr(X), N, K, _ptr(scales), _ptr(quants)), "quantize_q8_0")
+    return scales, quants
+
+
+def dequant_q8_0_act(scales: np.ndarray, quants: np.ndarray) -> np.ndarray:
+    """Xq[n][k] = scales[n][k/32] * quants[n][k], exact in f64."""
+    q = np.asarray(quants, dtype=np.float64)
+    return q * np.repeat(np.asarray(scales, dtype=np.float64), 32, axis=-1)
+
+
+def matmul_q8act(dtype: int, blob: np.ndarray, M: int, K: int, scales: np.ndarray, quants: np.ndarray,
+                 rows=None, L=None):
+    """Y[N][R] f32, Y64, S and Splus [N][R] f64 with Q8_0-quantized activations.
+
+    scales f32 [N][K/32] and quants int8 [N][K] as quantize_q8_0 returns them;
+    Splus is the rounding scale of the int8 kernels (S plus the weights'
+    offset terms taken separately).
+    """
+    blob = np.ascontiguousarray(blob, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.float32)
+    quants = np.ascontiguousarray(quants, dtype=np.int8)
+    if quants.ndim == 1:
+        quants, scales = quants[None, :], scales[None, :]
+    N = quants.shape[0]
+    if quants.shape[1] != K or scales.shape != (N, K // 32):
+        raise ValueError("activation codes or scales have the wrong shape")
+    if blob.size < blob_bytes(dtype, M, K, L):
+        raise ValueError("blob too small")
+    if rows is None:
+        nrows, rows_p = M, None
+    else:
+        rows_arr = np.ascontiguousarray(rows, dtype=np.int64)
+        nrows, rows_p = rows_arr.size, _ptr(rows_arr)
+    Y = np.empty((N, nrows), dtype=np.float32)
+    Y64, S, Sp = (np.empty((N, nrows), dtype=np.float64) for _ in range(3))
+    rc = (L or lib()).oracle_matmul_q8act_rows(dtype, _ptr(blob), M, K, N, _ptr(scales), _ptr(quants), nrows,
+                                               rows_p, _ptr(Y), _ptr(Y64), _ptr(S), _ptr(Sp))
+    _check(rc, "matmul_q8act")
+    return Y, Y64, S, Sp

@@ -19,7 +19,12 @@
  *   G, U the f64 sums above for the gate and the up matrix;
  *
  * and, for greedy decoding, the argmax over m of the f64 sums of one token
- * (the smallest index among equal maxima).
+ * (the smallest index among equal maxima);
+ *
+ * and, for the int8-activation variant, the page's Q8_0 quantization of the
+ * activations (scale = f16(amax/127), codes = RNE(v / d), see
+ * oracle_quantize_q8_0) and the same f64 sum with X replaced by the
+ * dequantized codes, Xq[n,k] = scale[n][k/32] * q[n,k] (exact in f64).
  *
  * Source of the definition: page "cera 0.5.2 src/backend/cpu.rs", section
  * "Matrix multiplication" -- the scalar reference matmuls matmul_f32,
@@ -74,7 +79,10 @@
  *          q   = lo4 | hi2<<4;       w = d*sc[j/16]*(q-32)
  *
  * Parity pins: hand-built blocks, the all-ones closed form, unit vectors and
- * exact rational brute force (tests/test_oracle_pins.py); SiLU at closed-form
+ * exact rational brute force; the f16 rounding against numpy's binary16
+ * conversion; the Q8_0 activation quantizer against hand-derived blocks
+ * (tests/golden/q8_0_act.txt) and its closed-form error bound; and
+ * (tests/test_oracle_pins.py); SiLU at closed-form
  * points (sigmoid(ln 3) = 3/4, the minimum -W(1/e)) and SwiGLU on fixture
  * blocks with unit vectors.  The Q4_K scale
  * packing and the Q6_K bit layout are a reading of the GGUF convention that
@@ -414,4 +422,149 @@ int oracle_argmax(int dtype, const uint8_t *blob, int64_t M, int64_t K, const fl
     }
     free(y); free(y64); free(s);
     return rc;
+}
+
+/* ---- activations quantized to Q8_0 (the int8-activation variant) ------ */
+
+/* f32 -> IEEE binary16, round to nearest, ties to even, from the format's
+ * definition: the value is placed on the half grid of its binade (2^-24 for
+ * the subnormals), rounded with rint() in the default rounding mode; values
+ * at or beyond 65520 (half an ulp above the largest finite half, 65504)
+ * become Inf; NaN stays NaN. */
+uint16_t oracle_float_to_half(float f) {
+    double v = (double)f, a = fabs(v);
+    uint16_t sign = signbit(v) ? 0x8000 : 0;
+    if (isnan(v)) return (uint16_t)(sign | 0x7E00);
+    if (a >= 65520.0) return (uint16_t)(sign | 0x7C00);
+    if (a < ldexp(1.0, -14)) return (uint16_t)(sign | (uint16_t)rint(ldexp(a, 24)));
+    int E;
+    frexp(a, &E);                          /* a in [2^(E-1), 2^E) */
+    double m = rint(ldexp(a, 11 - E));     /* 1024 <= m <= 2048 */
+    int e = E - 1 + 15;
+    if (m == 2048.0) {
+        m = 1024.0;
+        e++;
+    }
+    if (e >= 31) return (uint16_t)(sign | 0x7C00);
+    return (uint16_t)(sign | (e << 10) | ((int)m - 1024));
+}
+
+/* X f32 [N][K] -> Q8_0 activation blocks: scales f32 [N][K/32] and quants
+ * int8 [N][K] (page "cera 0.5.2 src/backend/cpu.rs", the portable Q8_0
+ * quantizer quantize_f32_to_q8_0_scalar and its caller-owned scale / quant
+ * buffers).  Per block of 32, all in f32:
+ *   amax  = the largest |v| (a NaN element is skipped, as a max that ignores
+ *           NaN does);
+ *   d     = amax / 127;
+ *   id    = 1 / d when d != 0 and 1/d is finite, else 0 (the page's guard for
+ *           zero, subnormal and non-finite blocks);
+ *   scale = d rounded to f16 and back (stored as f32);
+ *   q     = v * id rounded to nearest, ties to even, clamped to [-128, 127];
+ *           a NaN product gives 0 (a saturating float -> int8 conversion).
+ * The codes use the unrounded 1/d, the stored scale the f16-rounded d, as on
+ * the page.  Returns -3 unless N >= 1 and K is a positive multiple of 32. */
+int oracle_quantize_q8_0(const float *X, int64_t N, int64_t K, float *scales, int8_t *quants) {
+    if (N < 1 || K < 32 || K % 32 != 0) return -3;
+    const int64_t nb = K / 32;
+    for (int64_t n = 0; n < N; n++) {
+        for (int64_t b = 0; b < nb; b++) {
+            const float *v = X + n * K + 32 * b;
+            float amax = 0.0f;
+            for (int t = 0; t < 32; t++) {
+                float a = fabsf(v[t]);
+                if (a > amax) amax = a;
+            }
+            float d = amax / 127.0f;
+            float r = 1.0f / d;
+            float id = (d != 0.0f && isfinite(r)) ? r : 0.0f;
+            scales[n * nb + b] = (float)oracle_half_to_double(oracle_float_to_half(d));
+            for (int t = 0; t < 32; t++) {
+                float q = rintf(v[t] * id);
+                int8_t c;
+                if (isnan(q)) c = 0;
+                else if (q < -128.0f) c = -128;
+                else if (q > 127.0f) c = 127;
+                else c = (int8_t)q;
+                quants[n * K + 32 * b + t] = c;
+            }
+        }
+    }
+    return 0;
+}
+
+/* The part of each weight that does not scale with its code: m for Q4_1,
+ * -dmin*m_i for Q4_K and Q5_K, nothing for the others.  The int8 kernels take
+ * that term through per-block sums of the activation codes (page "cera 0.5.2
+ * src/backend/cpu.rs", the Q4_1 and K-quant int8 GEMMs, whose min term goes
+ * through the activation column sums), so it sets their rounding scale. */
+static void offset_block(int dtype, const uint8_t *b, double *o) {
+    int bs = oracle_block_elems(dtype);
+    for (int j = 0; j < bs; j++) o[j] = 0.0;
+    if (dtype == OR_Q4_1) {
+        double m = half_at(b + 2);
+        for (int j = 0; j < 32; j++) o[j] = m;
+    } else if (dtype == OR_Q4_K || dtype == OR_Q5_K) {
+        double dmin = half_at(b + 2);
+        for (int i = 0; i < 8; i++) {
+            int sc, mn;
+            q4k_scale_min(b + 4, i, &sc, &mn);
+            for (int e = 0; e < 32; e++) o[32 * i + e] = -(dmin * (double)mn);
+        }
+    }
+}
+
+/* Y[n,m] = sum_k W[m,k] * Xq[n,k] with Xq[n,k] = scales[n][k/32] * quants[n][k]
+ * (exact in f64), accumulated in f64 over sequential k and rounded once to
+ * f32; S[n,m] = sum_k |W Xq|; Splus[n,m] = sum_k (|W - O| + |O|) |Xq| with O
+ * the offset part above (Splus == S when O == 0).  Rows as in
+ * oracle_matmul_rows; Y64, S and Splus may be NULL. */
+int oracle_matmul_q8act_rows(int dtype, const uint8_t *blob, int64_t M, int64_t K, int64_t N,
+                             const float *scales, const int8_t *quants, int64_t nrows, const int64_t *rows,
+                             float *Y, double *Y64, double *S, double *Splus) {
+    int rc = check_shape(dtype, M, K);
+    if (rc) return rc;
+    if (K % 32 != 0 || N < 1 || nrows < 1) return -3;
+    if (rows) {
+        for (int64_t r = 0; r < nrows; r++)
+            if (rows[r] < 0 || rows[r] >= M) return -3;
+    } else if (nrows != M) {
+        return -3;
+    }
+    const int bs = oracle_block_elems(dtype), bb = oracle_block_bytes(dtype);
+    const int64_t nb = K / bs, nb32 = K / 32;
+    int err = 0;
+#pragma omp parallel
+    {
+        double *w = (double *)malloc(sizeof(double) * (size_t)K);
+        double *o = (double *)malloc(sizeof(double) * (size_t)K);
+        if (!w || !o) {
+#pragma omp atomic write
+            err = -7;
+        }
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t r = 0; r < nrows; r++) {
+            if (!w || !o) continue;
+            int64_t m = rows ? rows[r] : r;
+            if (dequant_row(dtype, blob, K, m, w)) continue;
+            const uint8_t *row = blob + (m * nb) * bb;
+            for (int64_t b = 0; b < nb; b++) offset_block(dtype, row + b * bb, o + b * bs);
+            for (int64_t n = 0; n < N; n++) {
+                double sum = 0.0, sum_abs = 0.0, magp = 0.0;
+                for (int64_t j = 0; j < K; j++) {
+                    double xq = (double)scales[n * nb32 + j / 32] * (double)quants[n * K + j];
+                    double p = w[j] * xq;
+                    sum += p;
+                    sum_abs += fabs(p);
+                    magp += (fabs(w[j] - o[j]) + fabs(o[j])) * fabs(xq);
+                }
+                Y[n * nrows + r] = (float)sum;
+                if (Y64) Y64[n * nrows + r] = sum;
+                if (S) S[n * nrows + r] = sum_abs;
+                if (Splus) Splus[n * nrows + r] = magp;
+            }
+        }
+        free(w);
+        free(o);
+    }
+    return err;
 }

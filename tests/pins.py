@@ -21,6 +21,15 @@ run against deliberately broken builds of the oracle (test_oracle_mutants).
   pin_argmax          greedy argmax on fixture blocks with unit vectors (the
                       design values pick the winner), planted ties and a
                       planted maximum in the last row
+  pin_q8_act_golden   the Q8_0 activation quantizer on hand-derived blocks
+                      (tests/golden/q8_0_act.txt): ties to even, the f16
+                      scale, the zero / NaN / Inf / subnormal guards
+  pin_float_to_half   f32 -> f16 rounding against numpy's conversion
+  pin_q8_act_bound    quantizer closed-form error bound, block maximum -> 127,
+                      sign and power-of-two symmetry
+  pin_q8_matmul       weights x quantized activations: exact rational brute
+                      force (with the offset-term scale), all-ones closed
+                      form, one scaled block, token and row placement
 """
 from __future__ import annotations
 
@@ -498,5 +507,186 @@ def pin_argmax(L=None):
         assert idx == 2, f"{name}: the maximum sits in the last row, got {idx}"
 
 
+# ------------------------------------------------- Q8_0-quantized activations
+
+def _f32(s: str) -> np.float32:
+    s = s.strip().lower()
+    if s in ("nan", "inf", "-inf"):
+        return np.float32(float(s))
+    return np.float32(_num(s))
+
+
+def load_q8_act_golden():
+    """[(record name, x f32[32], scale, codes int8[32])] from tests/golden/q8_0_act.txt."""
+    recs, cur, key = [], None, None
+    with open(os.path.join(GOLDEN, "q8_0_act.txt")) as f:
+        for raw in f:
+            line = raw.rstrip("\n")
+            if not line.strip() or line.lstrip().startswith("#"):
+                continue
+            if line.startswith("["):
+                cur = {"name": line.strip("[] "), "x": [], "scale": [], "q": []}
+                recs.append(cur)
+                continue
+            for k in ("x", "scale", "q"):
+                if line.startswith(k + ":"):
+                    key, line = k, line[len(k) + 1:]
+            cur[key] += line.split()
+    out = []
+    for r in recs:
+        x = np.array(_expand(r["x"], _f32), dtype=np.float32)
+        q = np.array(_expand(r["q"], int), dtype=np.int8)
+        out.append((r["name"], x, _f32(r["scale"][0]), q))
+    return out
+
+
+def pin_q8_act_golden(L=None):
+    recs = load_q8_act_golden()
+    assert len(recs) >= 8
+    for name, x, scale, q in recs:
+        assert x.size == 32 and q.size == 32, f"{name}: a record is one block of 32"
+        sc, qq = oracle.quantize_q8_0(x[None, :], L=L)
+        assert (sc[0, 0] == scale) or (scale != scale and sc[0, 0] != sc[0, 0]), \
+            f"{name}: scale {float(sc[0, 0])!r}, hand-derived {float(scale)!r}"
+        bad = np.nonzero(qq[0] != q)[0]
+        assert bad.size == 0, f"{name}: code {bad[0]} is {qq[0][bad[0]]}, hand-derived {q[bad[0]]}"
+    # blocks are independent and tokens are rows: the records stacked as one
+    # token of 32*R values and as R tokens give the same scales and codes
+    X = np.stack([r[1] for r in recs])
+    s2, q2 = oracle.quantize_q8_0(X, L=L)
+    s1, q1 = oracle.quantize_q8_0(X.reshape(1, -1), L=L)
+    assert np.array_equal(q2.reshape(-1), q1.reshape(-1))
+    assert np.array_equal(s2.reshape(-1), s1.reshape(-1), equal_nan=True)
+
+
+def pin_float_to_half(L=None):
+    """f32 -> binary16 rounding against numpy's conversion (nearest, ties to even)."""
+    rng = np.random.default_rng(7)
+    vals = [np.float32(v) for v in (0.0, -0.0, 1.0, 65504.0, 65519.99, 65520.0, -65520.0, 1e6, 2.0 ** -24,
+                                    2.0 ** -25, 2.0 ** -25 * 1.0001, 3 * 2.0 ** -26, 2.0 ** -14, 6.1e-5,
+                                    np.inf, -np.inf)]
+    # every half-way point between adjacent finite halves (exact in f32)
+    h = np.arange(0, 0x7C00, 37, dtype=np.uint16)
+    a = h.view(np.float16).astype(np.float32)
+    b = (h + 1).view(np.float16).astype(np.float32)
+    vals += list((a + b) / np.float32(2))
+    vals += list(rng.standard_normal(2000).astype(np.float32) * np.float32(2.0) ** rng.integers(-30, 17, 2000))
+    for v in vals:
+        for sv in (v, -v):
+            with np.errstate(over="ignore"):
+                want = int(np.array(sv, np.float32).astype(np.float16).view(np.uint16))
+            got = oracle.float_to_half(sv, L)
+            assert got == want, f"f16({float(sv)!r}) = {got:#06x}, numpy gives {want:#06x}"
+    assert oracle.float_to_half(np.float32(np.nan), L) & 0x7C00 == 0x7C00
+    assert oracle.float_to_half(np.float32(np.nan), L) & 0x03FF != 0
+
+
+def pin_q8_act_bound(L=None):
+    """Codes and scales of random activations against the quantizer's closed-form bound.
+
+    With d = amax/127 and codes rounded from v/d, |q d - v| <= d/2 (up to the
+    f32 rounding of v/d), and the stored scale differs from d by at most half
+    an f16 ulp, so |q scale - v| <= d (1/2 + 2^-16) + 127 |scale - d|.  The
+    element of largest |v| gets |q| = 127; negating x negates the codes;
+    scaling x by 2^j scales the scales and keeps the codes.
+    """
+    rng = rng_for(990, 0)
+    for mag in (1e-3, 1.0, 37.0, 3e4):
+        X = (rng.standard_normal((3, 256)) * mag).astype(np.float32)
+        X[1, 32:96] = 0.0                      # blocks 1 and 2 of token 1: all zero
+        sc, q = oracle.quantize_q8_0(X, L=L)
+        blocks = X.reshape(3, 8, 32).astype(np.float64)
+        amax = np.abs(blocks).max(axis=2)
+        d = amax / 127.0
+        assert np.all(np.abs(q.astype(np.int32)) <= 127)
+        err = np.abs(q.reshape(3, 8, 32) * sc[..., None].astype(np.float64) - blocks)
+        bound = d * (0.5 + 2.0 ** -16) + 127 * np.abs(sc.astype(np.float64) - d)
+        assert np.all(err <= bound[..., None] * (1 + 1e-6)), f"mag {mag}: |q scale - x| above the bound"
+        assert np.all(np.abs(sc.astype(np.float64) - d) <= d * 2.0 ** -11 + 2.0 ** -25), "scale is not f16(d)"
+        top = np.abs(blocks).argmax(axis=2)
+        qb = q.reshape(3, 8, 32)
+        for n in range(3):
+            for b in range(8):
+                if amax[n, b] > 0:
+                    assert abs(int(qb[n, b, top[n, b]])) == 127, f"mag {mag}: block max does not get 127"
+        assert np.all(sc[1, 1:3] == 0) and np.all(qb[1, 1:3] == 0), "a zero block needs scale 0, codes 0"
+        sn, qn = oracle.quantize_q8_0(-X, L=L)
+        assert np.array_equal(sn, sc) and np.array_equal(qn, -q), "negating x must negate the codes"
+        if mag <= 37.0:
+            s4, q4 = oracle.quantize_q8_0(X * np.float32(4.0), L=L)
+            assert np.array_equal(q4, q), "x * 4 changed the codes"
+            normal = sc >= 2.0 ** -14                  # on the subnormal f16 grid the scale rounds differently
+            assert np.array_equal(s4[normal], sc[normal] * np.float32(4.0)), "x * 4 did not scale the scales"
+
+
+def exact_offsets(dt: int, blk: bytes) -> list:
+    """The code-independent term of every weight of one block (0 for formats without one)."""
+    bs = 256 if dt in (oracle.Q4_K, oracle.Q5_K, oracle.Q6_K) else 32
+    if dt == oracle.Q4_1:
+        return [_h(blk, 2)] * 32
+    if dt in (oracle.Q4_K, oracle.Q5_K):
+        dmin, s = _h(blk, 2), blk[4:16]
+        out = []
+        for i in range(8):
+            mn = s[i + 4] % 64 if i < 4 else s[i + 4] // 16 + 16 * (s[i] // 64)
+            out += [-dmin * mn] * 32
+        return out
+    return [Fraction(0)] * bs
+
+
+def pin_q8_matmul(L=None):
+    """Weights x Q8_0 activations: exact rational brute force, the closed form, tokens and rows."""
+    shapes = [(1, 1), (3, 2), (4, 3)]
+    for i, dt in enumerate(DTYPES):
+        name = oracle.NAMES[dt]
+        bs, bb = oracle.block_elems(dt, L), oracle.block_bytes(dt, L)
+        for j, (M, N) in enumerate(shapes):
+            K = 2 * bs if bs == 256 else 8 * bs
+            blob = make_blob(dt, M, K, rng_for(960 + i, j))
+            sc, q = oracle.quantize_q8_0(make_x(N, K, rng_for(960 + i, 100 + j)), L=L)
+            Y, Y64, S, Sp = oracle.matmul_q8act(dt, blob, M, K, sc, q, L=L)
+            raw, nb = blob.tobytes(), K // bs
+            for m in range(M):
+                w, o = [], []
+                for b in range(nb):
+                    blk = raw[(m * nb + b) * bb:(m * nb + b + 1) * bb]
+                    w += exact_weights(dt, blk)
+                    o += exact_offsets(dt, blk)
+                for n in range(N):
+                    xs = [Fraction(float(sc[n, k // 32])) * int(q[n, k]) for k in range(K)]
+                    exact = sum((wk * xk for wk, xk in zip(w, xs)), Fraction(0))
+                    mag = sum((abs(wk * xk) for wk, xk in zip(w, xs)), Fraction(0))
+                    magp = sum(((abs(wk - ok) + abs(ok)) * abs(xk) for wk, ok, xk in zip(w, o, xs)), Fraction(0))
+                    bound = Fraction(K) * Fraction(2) ** -50 * magp
+                    assert abs(Fraction(float(Y64[n, m])) - exact) <= bound, f"{name}: y[{n},{m}] f64 is off"
+                    assert abs(Fraction(float(S[n, m])) - mag) <= bound, f"{name}: S is not sum |w xq|"
+                    assert abs(Fraction(float(Sp[n, m])) - magp) <= bound, f"{name}: Splus misses an offset term"
+                    want = round_f32(exact)
+                    if Y[n, m] != want:
+                        mid = (Fraction(float(min(Y[n, m], want))) + Fraction(float(max(Y[n, m], want)))) / 2
+                        assert abs(mid - exact) <= bound, f"{name}: y[{n},{m}] not correctly rounded"
+        # closed form: every code 1 with scale 1 is x = all ones
+        M, K = 5, 2 * bs if bs == 256 else 8 * bs
+        blob = make_blob(dt, M, K, rng_for(970 + i, 0))
+        _, Y64, _, _ = oracle.matmul_q8act(dt, blob, M, K, np.ones((1, K // 32), np.float32),
+                                           np.ones((1, K), np.int8), L=L)
+        assert np.array_equal(Y64[0], closed_form_row_sums(dt, blob, M, K)), f"{name}: all-ones codes"
+        # scale 2^-3 on one block only: y = 2^-3 * that block's columns summed
+        scl = np.zeros((1, K // 32), np.float32)
+        scl[0, 1] = 0.125
+        _, Y64, _, _ = oracle.matmul_q8act(dt, blob, M, K, scl, np.ones((1, K), np.int8), L=L)
+        W = np.array([[float(v) for b in range(K // bs)
+                       for v in exact_weights(dt, blob.tobytes()[(m * (K // bs) + b) * bb:(m * (K // bs) + b + 1) * bb])]
+                      for m in range(M)])
+        assert np.array_equal(Y64[0], W[:, 32:64].sum(axis=1) * 0.125), f"{name}: block scale misplaced"
+        # the second token's codes are its own; a row subset is the same numbers
+        q2 = np.zeros((2, K), np.int8)
+        q2[1, 3] = -7
+        _, Y64, _, _ = oracle.matmul_q8act(dt, blob, M, K, np.ones((2, K // 32), np.float32), q2, rows=[4, 0], L=L)
+        assert np.array_equal(Y64[0], [0.0, 0.0]) and np.array_equal(Y64[1], -7.0 * W[[4, 0], 3]), \
+            f"{name}: token or row mix-up"
+
+
 ALL_PINS = [pin_golden, pin_unit_vectors, pin_closed_form, pin_bruteforce, pin_invariants,
-            pin_half, pin_sizes, pin_silu, pin_swiglu, pin_argmax]
+            pin_half, pin_sizes, pin_silu, pin_swiglu, pin_argmax, pin_q8_act_golden, pin_float_to_half,
+            pin_q8_act_bound, pin_q8_matmul]

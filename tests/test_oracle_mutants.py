@@ -59,6 +59,25 @@ MUTANTS = {
     "argmax_min": ("if (bi < 0 || y64[m] > y64[bi]) bi = m;", "if (bi < 0 || y64[m] < y64[bi]) bi = m;"),
     "argmax_skips_last": ("for (int64_t m = 0; m < M; m++) {\n            if (y64[m] != y64[m]) continue;",
                           "for (int64_t m = 0; m + 1 < M; m++) {\n            if (y64[m] != y64[m]) continue;"),
+    "q8a_ties_away": ("float q = rintf(v[t] * id);", "float q = roundf(v[t] * id);"),
+    "q8a_unrounded_scale": ("scales[n * nb + b] = (float)oracle_half_to_double(oracle_float_to_half(d));",
+                            "scales[n * nb + b] = d;"),
+    "q8a_codes_from_f16_scale": ("float r = 1.0f / d;", "float r = 1.0f / (float)oracle_half_to_double(oracle_float_to_half(d));"),
+    "q8a_signed_max": ("float a = fabsf(v[t]);", "float a = v[t];"),
+    "q8a_no_finite_guard": ("float id = (d != 0.0f && isfinite(r)) ? r : 0.0f;", "float id = (d != 0.0f) ? r : 0.0f;"),
+    "q8a_nan_code": ("if (isnan(q)) c = 0;", "if (isnan(q)) c = 127;"),
+    "q8a_divide_by_128": ("float d = amax / 127.0f;", "float d = amax / 128.0f;"),
+    "q8a_first_block_scale": ("(double)scales[n * nb32 + j / 32]", "(double)scales[n * nb32]"),
+    "q8a_sum_drops_first": ("for (int64_t j = 0; j < K; j++) {", "for (int64_t j = 1; j < K; j++) {"),
+    "q8a_token0_codes": ("(double)quants[n * K + j]", "(double)quants[j]"),
+    "q8a_splus_no_offset": ("magp += (fabs(w[j] - o[j]) + fabs(o[j])) * fabs(xq);", "magp += fabs(w[j]) * fabs(xq);"),
+    "q8a_offset_sign": ("for (int e = 0; e < 32; e++) o[32 * i + e] = -(dmin * (double)mn);",
+                        "for (int e = 0; e < 32; e++) o[32 * i + e] = (dmin * (double)mn);"),
+    "q8a_q4_1_offset_missing": ("for (int j = 0; j < 32; j++) o[j] = m;", "for (int j = 0; j < 32; j++) o[j] = 0.0 * m;"),
+    "half_ties_away": ("double m = rint(ldexp(a, 11 - E));", "double m = round(ldexp(a, 11 - E));"),
+    "half_overflow_threshold": ("if (a >= 65520.0) return", "if (a >= 65504.0) return"),
+    "half_subnormal_truncates": ("rint(ldexp(a, 24))", "floor(ldexp(a, 24))"),
+    "half_exponent_bias": ("int e = E - 1 + 15;", "int e = E + 15;"),
     "f32_rounding": ("Y[n * nrows + r] = (float)acc;", "Y[n * nrows + r] = (float)(acc * (1.0 + 0x1p-23));"),
 }
 
