@@ -144,6 +144,19 @@ def main():
         q.qmm_gemv_swiglu(copies[1][c], copies[2][c], dg, Mg, Kg, xs[1], swiglu_y, stream=stream)
         q.qmm_gemv(copies[3][c], dd, Md, Kd, xs[3], ys[3], stream=stream)
 
+    # int8 activations: each distinct input quantized once per step
+    # (qmm_quantize_q8_0), then one qmm_gemm_q8act launch per matrix
+    q8_in = (0, 1, 1, 3)  # gate and up share one input, as in step_fused
+    q8sc = {i: torch.empty((1, mats[i][3] // 32), device=dev) for i in set(q8_in)}
+    q8q = {i: torch.empty((1, mats[i][3]), dtype=torch.int8, device=dev) for i in set(q8_in)}
+
+    def step_q8act(c):
+        for i in sorted(q8sc):
+            q.qmm_quantize_q8_0(xs[i], 1, mats[i][3], q8sc[i], q8q[i], stream=stream)
+        for i, (name, dt, M, K, _) in enumerate(mats):
+            j = q8_in[i]
+            q.qmm_gemm_q8act(copies[i][c], dt, M, K, 1, q8sc[j], q8q[j], ys[i], stream=stream)
+
     def time_layer(step):
         """(span ms over args.steps steps, host seconds), events only at step boundaries."""
         for s in range(args.warmup):
@@ -159,10 +172,11 @@ def main():
         return ev[0].elapsed_time(ev[args.steps]), time.perf_counter() - t0
 
     span_ms, wall_dec = time_layer(step_fused)
-    span_unf = span_swi = None
+    span_unf = span_swi = span_q8 = None
     if not args.headline_only:
         span_unf, _ = time_layer(step_unfused)
         span_swi, _ = time_layer(step_swiglu)
+        span_q8, _ = time_layer(step_q8act)
     dec_bytes_total = step_bytes * args.steps
     value = dec_bytes_total / (span_ms * 1e-3) / 1e9
     launches = 3
@@ -195,6 +209,12 @@ def main():
         per_matrix["gate+up swiglu"] = time_calls(
             lambda c: q.qmm_gemv_swiglu(copies[1][c], copies[2][c], dg, Mg, Kg, xs[1], swiglu_y, stream=stream),
             gu_bytes)
+        for i, (name, dt, M, K, _) in enumerate(mats):
+            j = q8_in[i]
+            per_matrix[name + " q8act"] = time_calls(
+                lambda c, i=i, j=j, dt=dt, M=M, K=K: q.qmm_gemm_q8act(copies[i][c], dt, M, K, 1, q8sc[j], q8q[j],
+                                                                      ys[i], stream=stream),
+                copies[i][0].numel())
 
     def layer_rate(span):
         if span is None:
@@ -248,6 +268,10 @@ def main():
             "decode_unfused": {"launches": 4, **(layer_rate(span_unf) or {})},
             "decode_swiglu": {"launches": 3, **(layer_rate(span_swi) or {}),
                               "note": "gate/up through qmm_gemv_swiglu (outputs silu(g)*u instead of g and u)"},
+            "decode_q8act": {"launches": 7, **(layer_rate(span_q8) or {}),
+                             "note": "int8 activations: 3 qmm_quantize_q8_0 + 4 qmm_gemm_q8act launches (x "
+                                     "quantized to Q8_0 blocks, integer block dots; different numbers from the "
+                                     "f32 path)"},
             "timing": "HIP events on the launch stream at step boundaries; per-launch = span / launches",
             "per_matrix": per_matrix,
             "gpu": props.name,

@@ -16,6 +16,10 @@ there is no CPU fallback.
                                                      index = argmax_m (W x)[m]
     qmm_gemm_swiglu(gate, up, dtype, M, K, N, X, out, stream=None)
                                                      out = silu(X Wg^T) * (X Wu^T)
+    qmm_quantize_q8_0(X, N, K, scales, quants, stream=None)
+                                                     X -> Q8_0 activation blocks
+    qmm_gemm_q8act(w, dtype, M, K, N, scales, quants, Y, stream=None)
+                                                     Y = Xq W^T (int8 activations)
 """
 from __future__ import annotations
 
@@ -36,7 +40,8 @@ QMM_GEMV_MAX_MATS = 4
 QMM_ARGMAX_WORK_BYTES = 32768
 
 EXPORTS = ("qmm_gemv", "qmm_gemv_concat", "qmm_gemv_swiglu", "qmm_gemv_argmax", "qmm_gemm", "qmm_gemm_swiglu",
-           "qmm_gemm_path", "qmm_blob_bytes", "qmm_block_elems", "qmm_block_bytes", "qmm_strerror")
+           "qmm_quantize_q8_0", "qmm_gemm_q8act", "qmm_gemm_path", "qmm_blob_bytes", "qmm_block_elems",
+           "qmm_block_bytes", "qmm_strerror")
 
 _lib = None
 
@@ -67,6 +72,10 @@ def lib():
         L.qmm_gemm_swiglu.restype = ci
         L.qmm_gemm.argtypes = [vp, ci, i64, i64, i64, vp, vp, vp]
         L.qmm_gemm.restype = ci
+        L.qmm_quantize_q8_0.argtypes = [vp, i64, i64, vp, vp, vp]
+        L.qmm_quantize_q8_0.restype = ci
+        L.qmm_gemm_q8act.argtypes = [vp, ci, i64, i64, i64, vp, vp, vp, vp]
+        L.qmm_gemm_q8act.restype = ci
         L.qmm_gemm_path.argtypes = [ci, i64, i64, i64]
         L.qmm_gemm_path.restype = ci
         L.qmm_blob_bytes.argtypes = [ci, i64, i64]
@@ -193,3 +202,24 @@ def qmm_gemm_swiglu(gate, up, dtype: int, M: int, K: int, N: int, X, out, stream
                                _stream(stream))
     if rc != QMM_OK:
         raise QmmError(rc, "qmm_gemm_swiglu")
+
+
+def qmm_quantize_q8_0(X, N: int, K: int, scales, quants, stream=None) -> None:
+    import torch
+    nb = K // 32 if K > 0 else 0
+    rc = lib().qmm_quantize_q8_0(_addr(X, 4 * N * K, "X", torch.float32), N, K,
+                                 _addr(scales, 4 * N * nb, "scales", torch.float32),
+                                 _addr(quants, N * K, "quants", torch.int8), _stream(stream))
+    if rc != QMM_OK:
+        raise QmmError(rc, "qmm_quantize_q8_0")
+
+
+def qmm_gemm_q8act(w, dtype: int, M: int, K: int, N: int, scales, quants, Y, stream=None) -> None:
+    import torch
+    nb = blob_bytes(dtype, M, K)
+    rc = lib().qmm_gemm_q8act(_addr(w, nb or None, "w_blob"), dtype, M, K, N,
+                              _addr(scales, 4 * N * (K // 32), "scales", torch.float32),
+                              _addr(quants, N * K, "quants", torch.int8), _addr(Y, 4 * N * M, "Y", torch.float32),
+                              _stream(stream))
+    if rc != QMM_OK:
+        raise QmmError(rc, "qmm_gemm_q8act")

@@ -216,6 +216,30 @@ int qmm_gemm_swiglu(const void *gate_blob, const void *up_blob, int dtype, int64
     return e == hipSuccess ? QMM_OK : QMM_ERR_LAUNCH;
 }
 
+int qmm_quantize_q8_0(const float *X, int64_t N, int64_t K, float *scales, int8_t *quants, void *stream) {
+    if (N < 1 || K < 32 || K % 32 != 0 || N > (int64_t(1) << 40) || K > (int64_t(1) << 40)) return QMM_ERR_SHAPE;
+    if (!X || !scales || !quants) return QMM_ERR_NULL;
+    if (!aligned(X, 16) || !aligned(scales, 16) || !aligned(quants, 16)) return QMM_ERR_ALIGN;
+    int cus = 0;
+    const int rc = current_device(&cus);
+    if (rc != QMM_OK) return rc;
+    const hipError_t e = qmm::launch_quantize_q8_0(X, N, K, scales, quants, (hipStream_t)stream);
+    return e == hipSuccess ? QMM_OK : QMM_ERR_LAUNCH;
+}
+
+int qmm_gemm_q8act(const void *w_blob, int dtype, int64_t M, int64_t K, int64_t N, const float *scales,
+                   const int8_t *quants, float *Y, void *stream) {
+    int rc = check_shape(dtype, M, K, N);
+    if (rc != QMM_OK) return rc;
+    if (!w_blob || !scales || !quants || !Y) return QMM_ERR_NULL;
+    if (!aligned(w_blob, 16) || !aligned(scales, 16) || !aligned(quants, 16) || !aligned(Y, 4)) return QMM_ERR_ALIGN;
+    int cus = 0;
+    rc = current_device(&cus);
+    if (rc != QMM_OK) return rc;
+    const hipError_t e = qmm::launch_gemm_q8act(dtype, w_blob, M, K, N, scales, quants, Y, (hipStream_t)stream, cus);
+    return e == hipSuccess ? QMM_OK : QMM_ERR_LAUNCH;
+}
+
 int qmm_gemm(const void *w_blob, int dtype, int64_t M, int64_t K, int64_t N, const float *X, float *Y,
              void *stream) {
     int rc = check_shape(dtype, M, K, N);

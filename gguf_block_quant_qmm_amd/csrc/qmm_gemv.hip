@@ -343,6 +343,222 @@ template <> struct Unit<QMM_Q6_K> {
     }
 };
 
+// ------------------------------------------ Q8_0-quantized activations ----
+// The int8-activation variant (page "cera 0.5.2 src/backend/cpu.rs", the
+// Q8_0 activation path: the activations are quantized to blocks of 32 int8
+// codes with one scale each, and every weight block meets them in integer
+// dot products).  A lane keeps, per token, the 64 activation codes of its
+// unit (16 dwords, bytes ordered like the unit's weight bytes), the scales of
+// the activation blocks the unit touches and the per-block code sums that
+// the weights' offsets need.  Per activation block (per 16-weight sub-scale
+// group for Q6_K) the integer sum of code products is exact
+// (v_dot4_i32_i8); it is scaled once in f32:
+//   Q8_0  (d xs) * sum q c                  Q4_0  (d xs) * (sum q c - 8 sum c)
+//   Q4_1  (d xs) * sum q c + (m xs) * sum c
+//   Q4_K, Q5_K  (d xs) * (sc * sum q c) - (dmin xs) * (m * sum c)
+//   Q6_K  (d xs) * (sc * (sum q c - 32 sum c))
+// The offsets -8 and -32 stay inside the exact integer sums; the Q4_1 and
+// K-quant minimum terms are scaled separately, so their rounding is relative
+// to sum |w - o| |xq| + sum |o| |xq| (o the weight's offset part).
+struct XA {
+    uint32_t c[16];  // codes, in the byte order dot() pairs them with
+    float s[4];      // activation scales (2 used, 4 for Q6_K)
+    int o[4];        // per-block integer offsets (see prep)
+};
+
+__device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int acc) {
+    return __builtin_amdgcn_sdot4((int)a, (int)b, acc, false);
+}
+// sum of the 4 signed bytes of v
+__device__ __forceinline__ int bsum4(uint32_t v, int acc) { return dot4(v, 0x01010101u, acc); }
+
+template <int DT> struct U8;
+
+template <> struct U8<QMM_Q4_0> {
+    static constexpr int NS = 2;
+    __device__ static int s_index(int u) { return 2 * u; }
+    __device__ static void prep(XA &a) {
+        // block 0's weight dwords are [qs0 qs1 qs14 qs15], qs2..5, qs6..9,
+        // qs10..13 (the unit starts with d0); block 1's are natural
+        int s[2] = {0, 0};
+#pragma unroll
+        for (int i = 0; i < 16; i++) s[i >> 3] = bsum4(a.c[i], s[i >> 3]);
+        a.o[0] = -8 * s[0];
+        a.o[1] = -8 * s[1];
+#pragma unroll
+        for (int h = 0; h < 2; h++) {  // low nibbles: codes 0..15, high: 16..31
+            const uint32_t c0 = a.c[4 * h], c1 = a.c[4 * h + 1], c2 = a.c[4 * h + 2], c3 = a.c[4 * h + 3];
+            a.c[4 * h] = __builtin_amdgcn_perm(c3, c0, 0x07060100u);
+            a.c[4 * h + 1] = __builtin_amdgcn_alignbyte(c1, c0, 2);
+            a.c[4 * h + 2] = __builtin_amdgcn_alignbyte(c2, c1, 2);
+            a.c[4 * h + 3] = __builtin_amdgcn_alignbyte(c3, c2, 2);
+        }
+    }
+    __device__ static float dot(const uint32_t (&v)[Unit<QMM_Q4_0>::NL], const XA &a, const Unit<QMM_Q4_0>::Off &) {
+        const uint32_t D[2][4] = {{__builtin_amdgcn_alignbyte(v[4], v[0], 2), v[1], v[2], v[3]},
+                                  {v[5], v[6], v[7], v[8]}};
+        int s[2];
+#pragma unroll
+        for (int b = 0; b < 2; b++) {
+            int acc = a.o[b];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                acc = dot4(D[b][i] & 0x0F0F0F0Fu, a.c[8 * b + i], acc);
+                acc = dot4((D[b][i] >> 4) & 0x0F0F0F0Fu, a.c[8 * b + 4 + i], acc);
+            }
+            s[b] = acc;
+        }
+        return fmaf(h2f(v[4] >> 16) * a.s[1], (float)s[1], (h2f(v[0]) * a.s[0]) * (float)s[0]);
+    }
+};
+
+template <> struct U8<QMM_Q4_1> {
+    static constexpr int NS = 2;
+    __device__ static int s_index(int u) { return 2 * u; }
+    __device__ static void prep(XA &a) {
+        int s[2] = {0, 0};
+#pragma unroll
+        for (int i = 0; i < 16; i++) s[i >> 3] = bsum4(a.c[i], s[i >> 3]);
+        a.o[0] = s[0];
+        a.o[1] = s[1];
+    }
+    __device__ static float dot(const uint32_t (&v)[Unit<QMM_Q4_1>::NL], const XA &a, const Unit<QMM_Q4_1>::Off &) {
+        float t[2];
+#pragma unroll
+        for (int b = 0; b < 2; b++) {
+            int acc = 0;
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const uint32_t dw = v[5 * b + 1 + i];
+                acc = dot4(dw & 0x0F0F0F0Fu, a.c[8 * b + i], acc);
+                acc = dot4((dw >> 4) & 0x0F0F0F0Fu, a.c[8 * b + 4 + i], acc);
+            }
+            const float d = h2f(v[5 * b]), m = h2f(v[5 * b] >> 16);
+            t[b] = fmaf(d * a.s[b], (float)acc, (m * a.s[b]) * (float)a.o[b]);
+        }
+        return t[0] + t[1];
+    }
+};
+
+template <> struct U8<QMM_Q8_0> {
+    static constexpr int NS = 2;
+    __device__ static int s_index(int u) { return 2 * u; }
+    __device__ static void prep(XA &) {}
+    __device__ static float dot(const uint32_t (&v)[Unit<QMM_Q8_0>::NL], const XA &a, const Unit<QMM_Q8_0>::Off &) {
+        int s[2];
+#pragma unroll
+        for (int b = 0; b < 2; b++) {
+            int acc = 0;
+#pragma unroll
+            for (int i = 0; i < 8; i++)
+                acc = dot4(b == 0 ? __builtin_amdgcn_alignbyte(v[i + 1], v[i], 2) : v[9 + i], a.c[8 * b + i], acc);
+            s[b] = acc;
+        }
+        return fmaf(h2f(v[8] >> 16) * a.s[1], (float)s[1], (h2f(v[0]) * a.s[0]) * (float)s[0]);
+    }
+};
+
+// Q4_K and Q5_K: the unit is chunk c of a super-block, sub-blocks 2c (low
+// nibbles) and 2c+1 (high nibbles), activation blocks 2u and 2u+1.
+__device__ __forceinline__ float kquant_pair(float d, float dmin, uint32_t s0w, uint32_t s1w, uint32_t s2w, int c,
+                                             int acc0, int acc1, const XA &a) {
+    int sc0, m0, sc1, m1;
+    q4k_scale_min(s0w, s1w, s2w, 2 * c, sc0, m0);
+    q4k_scale_min(s0w, s1w, s2w, 2 * c + 1, sc1, m1);
+    const float t0 = fmaf(d * a.s[0], (float)(sc0 * acc0), -((dmin * a.s[0]) * (float)(m0 * a.o[0])));
+    const float t1 = fmaf(d * a.s[1], (float)(sc1 * acc1), -((dmin * a.s[1]) * (float)(m1 * a.o[1])));
+    return t0 + t1;
+}
+
+template <> struct U8<QMM_Q4_K> {
+    static constexpr int NS = 2;
+    __device__ static int s_index(int u) { return 2 * u; }
+    __device__ static void prep(XA &a) { U8<QMM_Q4_1>::prep(a); }
+    __device__ static float dot(const uint32_t (&v)[Unit<QMM_Q4_K>::NL], const XA &a, const Unit<QMM_Q4_K>::Off &o) {
+        int acc0 = 0, acc1 = 0;
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const uint32_t dw = v[4 + i];
+            acc0 = dot4(dw & 0x0F0F0F0Fu, a.c[i], acc0);
+            acc1 = dot4((dw >> 4) & 0x0F0F0F0Fu, a.c[8 + i], acc1);
+        }
+        return kquant_pair(h2f(v[0]), h2f(v[0] >> 16), v[1], v[2], v[3], o.c, acc0, acc1, a);
+    }
+};
+
+template <> struct U8<QMM_Q5_K> {
+    static constexpr int NS = 2;
+    __device__ static int s_index(int u) { return 2 * u; }
+    __device__ static void prep(XA &a) { U8<QMM_Q4_1>::prep(a); }
+    __device__ static float dot(const uint32_t (&v)[Unit<QMM_Q5_K>::NL], const XA &a, const Unit<QMM_Q5_K>::Off &o) {
+        int acc0 = 0, acc1 = 0;
+        const int sh = 2 * o.c;
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const uint32_t dw = v[12 + i], hq = v[4 + i] >> sh;  // qh bits 2c, 2c+1 at 0, 1
+            acc0 = dot4((dw & 0x0F0F0F0Fu) | ((hq & 0x01010101u) << 4), a.c[i], acc0);
+            acc1 = dot4(((dw >> 4) & 0x0F0F0F0Fu) | ((hq & 0x02020202u) << 3), a.c[8 + i], acc1);
+        }
+        return kquant_pair(h2f(v[0]), h2f(v[0] >> 16), v[1], v[2], v[3], o.c, acc0, acc1, a);
+    }
+};
+
+template <> struct U8<QMM_Q6_K> {
+    // unit u = 4b + 2h + lh: group g (16 weights, sub-scale sc[8h + 2g + lh])
+    // lies in activation block 8b + 4h + g; codes dword 4g + t of the unit
+    static constexpr int NS = 4;
+    __device__ static int s_index(int u) { return 8 * (u >> 2) + 4 * ((u >> 1) & 1); }
+    __device__ static void prep(XA &a) {
+#pragma unroll
+        for (int g = 0; g < 4; g++) {
+            int s = 0;
+#pragma unroll
+            for (int t = 0; t < 4; t++) s = bsum4(a.c[4 * g + t], s);
+            a.o[g] = -32 * s;
+        }
+    }
+    __device__ static float dot(const uint32_t (&v)[Unit<QMM_Q6_K>::NL], const XA &a, const Unit<QMM_Q6_K>::Off &o) {
+        const float d = h2f(v[14]);
+        float total = 0.f;
+#pragma unroll
+        for (int g = 0; g < 4; g++) {
+            int acc = a.o[g];
+#pragma unroll
+            for (int t = 0; t < 4; t++) {
+                const uint32_t L = (g & 1) ? v[4 + t] : v[t];
+                const uint32_t C = v[8 + t];
+                const uint32_t hi = (g < 2 ? (C << (4 - 2 * g)) : (C >> (2 * g - 4))) & 0x30303030u;
+                const uint32_t q = ((g < 2 ? L : (L >> 4)) & 0x0F0F0F0Fu) | hi;
+                acc = dot4(q, a.c[4 * g + t], acc);
+            }
+            const uint32_t scw = (g < 2) ? v[12] : v[13];
+            const int sbyte = (int)__builtin_amdgcn_sbfe((int)scw, 16 * (g & 1) + 8 * o.lh, 8);  // sc[8h + 2g + lh]
+            total = fmaf(d * a.s[g], (float)(sbyte * acc), total);
+        }
+        return total;
+    }
+};
+
+// Issue the loads of one token's codes and scales for unit u (K = 64 U
+// codes, K / 32 scales); U8<DT>::prep finishes the set once they arrive.
+template <int DT>
+__device__ __forceinline__ void load_xa(const int8_t *xq, const float *xsc, int u, XA &a) {
+    const u32x4_t *q = reinterpret_cast<const u32x4_t *>(xq);
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const u32x4_t v = q[Unit<DT>::x4(u, 4 * j) >> 2];
+        a.c[4 * j] = v.x; a.c[4 * j + 1] = v.y; a.c[4 * j + 2] = v.z; a.c[4 * j + 3] = v.w;
+    }
+    const int si = U8<DT>::s_index(u);
+    if constexpr (U8<DT>::NS == 4) {
+        const floatx4 s = *reinterpret_cast<const floatx4 *>(xsc + si);
+        a.s[0] = s.x; a.s[1] = s.y; a.s[2] = s.z; a.s[3] = s.w;
+    } else {
+        const float2 s = *reinterpret_cast<const float2 *>(xsc + si);
+        a.s[0] = s.x; a.s[1] = s.y; a.s[2] = 0.f; a.s[3] = 0.f;
+    }
+}
+
 // Activations go through LDS with the float4 index XOR-swizzled within groups
 // of 16, so that 16 lanes reading their own unit hit distinct banks.
 __device__ __forceinline__ int xslot(int f) { return (f & ~15) | ((f & 15) ^ ((f >> 4) & 15)); }
@@ -453,14 +669,23 @@ __device__ __forceinline__ int64_t lo_of(const GemvMats &m, int i) {
     return v;
 }
 
-template <int DT, int R, int D, bool WAVE_ROWS, bool FLAT, int MODE>
+//
+// NT = 0: f32 activations x.  NT >= 1: Q8_0-quantized activations of NT
+// tokens per weight read (codes xq [ntok][K], scales xsc [ntok][K/32]; token
+// group blockIdx.y covers tokens NT*blockIdx.y ..; outputs y[tok][M]); GEMV_ONE
+// only.
+template <int DT, int R, int D, bool WAVE_ROWS, bool FLAT, int MODE, int NT>
 __global__ void __launch_bounds__(256) gemv_kernel(const GemvMats mats, int64_t row_bytes, int U,
-                                                   const float *__restrict__ x, int64_t per_owner, int64_t extra) {
+                                                   const float *__restrict__ x, int64_t per_owner, int64_t extra,
+                                                   const int8_t *__restrict__ xq, const float *__restrict__ xsc,
+                                                   int64_t ntok) {
+    static_assert(NT == 0 || MODE == GEMV_ONE, "int8 activations: one matrix");
     constexpr int NL = Unit<DT>::NL;
     constexpr int RR = MODE == GEMV_SWIGLU ? 2 * R : R;  // row dots per row group
+    constexpr int TK = NT > 0 ? NT : 1;                  // tokens per row dot
     extern __shared__ __attribute__((aligned(16))) floatx4 xs[];
     constexpr int RED_G = 16;
-    __shared__ float red[WAVE_ROWS ? 1 : RED_G][RR][4];
+    __shared__ float red[WAVE_ROWS ? 1 : RED_G][RR * TK][4];
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6), nwaves = blockDim.x >> 6;
     const int u = WAVE_ROWS ? lane : t;
@@ -494,8 +719,12 @@ __global__ void __launch_bounds__(256) gemv_kernel(const GemvMats mats, int64_t 
     // results of row r of group g (every lane that calls holds the sums)
     float best_v = 0.f;  // GEMV_ARGMAX: this thread's best row so far (rows < 2^31)
     int best_row = -1;
-    auto put = [&](int64_t g, int r, float v, float vu) {
-        if constexpr (MODE == GEMV_ARGMAX) {
+    const int64_t tok0 = (int64_t)blockIdx.y * TK;
+    auto put = [&](int64_t g, int r, float v, float vu, int tn) {
+        if constexpr (NT > 0) {
+            const int64_t row = g * R + r;
+            if (row < mats.M[0] && tok0 + tn < ntok) mats.y[0][(tok0 + tn) * mats.M[0] + row] = v;
+        } else if constexpr (MODE == GEMV_ARGMAX) {
             const int64_t row = g * R + r;
             if (row < mats.M[0] && beats(v, (int)row, best_v, best_row)) {
                 best_v = v;
@@ -511,14 +740,30 @@ __global__ void __launch_bounds__(256) gemv_kernel(const GemvMats mats, int64_t 
                 (MODE == GEMV_CONCAT ? pick(mats.y, mi) : mats.y[0])[row] = v;
         }
     };
-    floatx4 xr[WAVE_ROWS ? 4 : 16];
-    load_x(x, U, xr);
+    float xv[NT > 0 ? 1 : 64];
+    XA xa[TK];
+    if constexpr (NT > 0) {
+        // every lane fetches its own unit's codes (64 bytes per token) before
+        // the weights; tokens past the end repeat the last one (not stored)
+        const int64_t K = 64 * (int64_t)U;
 #pragma unroll
-    for (int s = 0; s < (FLAT ? D + 1 : D); s++) fetch(g0 + s, buf[s]);
-    store_x(xr, U, xs);
-    __syncthreads();
-    float xv[64];
-    x_from_lds<DT>(xs, active ? u : 0, xv);
+        for (int n = 0; n < TK; n++) {
+            const int64_t tk = tok0 + n < ntok ? tok0 + n : ntok - 1;
+            load_xa<DT>(xq + tk * K, xsc + tk * (K / 32), active ? u : 0, xa[n]);
+        }
+#pragma unroll
+        for (int s = 0; s < (FLAT ? D + 1 : D); s++) fetch(g0 + s, buf[s]);
+#pragma unroll
+        for (int n = 0; n < TK; n++) U8<DT>::prep(xa[n]);
+    } else {
+        floatx4 xr[WAVE_ROWS ? 4 : 16];
+        load_x(x, U, xr);
+#pragma unroll
+        for (int s = 0; s < (FLAT ? D + 1 : D); s++) fetch(g0 + s, buf[s]);
+        store_x(xr, U, xs);
+        __syncthreads();
+        x_from_lds<DT>(xs, active ? u : 0, xv);
+    }
 
     for (int64_t i0 = 0; i0 < n; i0 += D + 1) {
 #pragma unroll
@@ -526,16 +771,24 @@ __global__ void __launch_bounds__(256) gemv_kernel(const GemvMats mats, int64_t 
             const int64_t i = i0 + s;
             if (!FLAT) fetch(g0 + i + D, buf[(s + D) % (D + 1)]);
             if (i < n) {
-                float acc[RR];
+                float acc[RR * TK];  // [row][token]
 #pragma unroll
                 for (int r = 0; r < RR; r++) {
-                    const float d = Unit<DT>::dot(buf[s][r], xv, off);
-                    acc[r] = wave_sum_to_lane63(active ? d : 0.f);
+#pragma unroll
+                    for (int tn = 0; tn < TK; tn++) {
+                        float d;
+                        if constexpr (NT > 0) d = U8<DT>::dot(buf[s][r], xa[tn], off);
+                        else d = Unit<DT>::dot(buf[s][r], xv, off);
+                        acc[r * TK + tn] = wave_sum_to_lane63(active ? d : 0.f);
+                    }
                 }
                 if (WAVE_ROWS) {
                     if (lane == 63) {
 #pragma unroll
-                        for (int r = 0; r < R; r++) put(g0 + i, r, acc[r], acc[MODE == GEMV_SWIGLU ? R + r : r]);
+                        for (int r = 0; r < R; r++)
+#pragma unroll
+                            for (int tn = 0; tn < TK; tn++)
+                                put(g0 + i, r, acc[r * TK + tn], acc[MODE == GEMV_SWIGLU ? R + r : r], tn);
                     }
                 } else {
                     // partial sums of up to RED_G row groups wait in LDS; one
@@ -544,19 +797,19 @@ __global__ void __launch_bounds__(256) gemv_kernel(const GemvMats mats, int64_t 
                     const int slot = (int)(i % RED_G);
                     if (lane == 63) {
 #pragma unroll
-                        for (int r = 0; r < RR; r++) red[slot][r][wave] = acc[r];
+                        for (int r = 0; r < RR * TK; r++) red[slot][r][wave] = acc[r];
                     }
                     if (slot == RED_G - 1 || i == n - 1) {
                         __syncthreads();
-                        if (t < (slot + 1) * R) {
-                            const int gi = t / R, r = t % R;
-                            float sum = red[gi][r][0], su = 0.f;
-                            for (int w = 1; w < nwaves; w++) sum += red[gi][r][w];
+                        if (t < (slot + 1) * R * TK) {
+                            const int gi = t / (R * TK), r = (t % (R * TK)) / TK, tn = t % TK;
+                            float sum = red[gi][r * TK + tn][0], su = 0.f;
+                            for (int w = 1; w < nwaves; w++) sum += red[gi][r * TK + tn][w];
                             if constexpr (MODE == GEMV_SWIGLU) {
                                 su = red[gi][R + r][0];
                                 for (int w = 1; w < nwaves; w++) su += red[gi][R + r][w];
                             }
-                            put(g0 + i - slot + gi, r, sum, su);
+                            put(g0 + i - slot + gi, r, sum, su, tn);
                         }
                         __syncthreads();
                     }
@@ -930,14 +1183,23 @@ static int64_t gemv_wave_owners(int dtype, int64_t nrg, int cus) {
     return (int64_t)cus * ((dtype == QMM_Q4_0 || dtype == QMM_Q8_0) ? 16 : 8);
 }
 
+// Q8_0-quantized activations of ntok tokens (codes [ntok][K], scales
+// [ntok][K/32]); unused (q == nullptr) for f32 activations.
+struct XQ8 {
+    const int8_t *q;
+    const float *s;
+    int64_t ntok;
+};
+
 // Launch one fast-kernel variant: FLAT with D+1 = the most row groups an
 // owner gets when that is at most 4, else the ring with D row groups ahead.
-template <int DT, int R, int D, bool WAVE_ROWS, int MODE>
+template <int DT, int R, int D, bool WAVE_ROWS, int MODE, int NT>
 static void launch_variant(int64_t nmax, dim3 grid, dim3 block, size_t lds, hipStream_t st, const GemvMats &mats,
-                           int64_t row_bytes, int U, const float *x, int64_t per_owner, int64_t extra) {
+                           int64_t row_bytes, int U, const float *x, int64_t per_owner, int64_t extra,
+                           const XQ8 &xq8) {
 #define QMM_GEMV_LAUNCH(F, DD) \
-    hipLaunchKernelGGL((gemv_kernel<DT, R, DD, WAVE_ROWS, F, MODE>), grid, block, lds, st, mats, row_bytes, U, x, \
-                       per_owner, extra)
+    hipLaunchKernelGGL((gemv_kernel<DT, R, DD, WAVE_ROWS, F, MODE, NT>), grid, block, lds, st, mats, row_bytes, U, x, \
+                       per_owner, extra, xq8.q, xq8.s, xq8.ntok)
     // Q4_K: with more than one row group fetched up front the compiler hoists
     // the scale unpacking of all of them and runs out of registers
     constexpr int64_t flat_max = (DT == QMM_Q4_K || DT == QMM_Q5_K) ? 1 : 4;
@@ -956,49 +1218,37 @@ constexpr int64_t ARGMAX_PARTS = 4096;
 
 // The fast kernel over the row groups of `mats` (g_lo filled in by the
 // caller); *grid_out receives the workgroup count.
-template <int DT, int R, int D, int MODE>
+//
+// NT >= 1: int8 activations from xq8, NT tokens per weight read, one token
+// group per grid row.
+template <int DT, int R, int D, int MODE, int NT = 0>
 static hipError_t launch_fast(const GemvMats &mats, int64_t K, const float *x, hipStream_t st, int cus,
-                              int64_t *grid_out = nullptr) {
+                              int64_t *grid_out = nullptr, const XQ8 &xq8 = XQ8{nullptr, nullptr, 1}) {
     constexpr int BS = Geo<DT>::BS, BB = Geo<DT>::BB;
     const int64_t row_bytes = (K / BS) * BB;
     const int U = (int)(K / 64);
     const int64_t nrg = mats.g_lo[GEMV_MAX_MATS];
-    const size_t lds = (size_t)U * 256;  // the activations
+    const size_t lds = NT > 0 ? 0 : (size_t)U * 256;  // the f32 activations
+    const unsigned gy = NT > 0 ? (unsigned)((xq8.ntok + NT - 1) / NT) : 1u;
     if (U <= 64) {
         const int64_t waves = gemv_wave_owners(DT, nrg, cus);
         const int64_t grid = (waves + 3) / 4, owners = grid * 4;
         const int64_t per = nrg / owners, extra = nrg % owners;
         if (MODE == GEMV_ARGMAX && grid > ARGMAX_PARTS) return hipErrorInvalidConfiguration;
         if (grid_out) *grid_out = grid;
-        launch_variant<DT, R, D, true, MODE>(per + (extra ? 1 : 0), dim3((unsigned)grid), dim3(256), lds, st, mats,
-                                             row_bytes, U, x, per, extra);
+        launch_variant<DT, R, D, true, MODE, NT>(per + (extra ? 1 : 0), dim3((unsigned)grid, gy), dim3(256), lds, st,
+                                                 mats, row_bytes, U, x, per, extra, xq8);
     } else if (U <= 256) {
         const int W = (U + 63) / 64;
         const int lever = gemv_waves_lever();
         const int64_t grid = std::min<int64_t>(nrg, (int64_t)cus * std::max(1, (lever ? lever : 8) / W));
-        if (lds > 64 * 1024) {
-            static const hipError_t attr = [] {
-                auto big_lds = [](const void *f) {
-                    return hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, 64 * 1024 + 1024);
-                };
-                hipError_t e = big_lds(reinterpret_cast<const void *>(&gemv_kernel<DT, R, 0, false, true, MODE>));
-                if (e == hipSuccess) e = big_lds(reinterpret_cast<const void *>(&gemv_kernel<DT, R, D, false, false, MODE>));
-                if constexpr (DT != QMM_Q4_K && DT != QMM_Q5_K) {
-                    if (e == hipSuccess) e = big_lds(reinterpret_cast<const void *>(&gemv_kernel<DT, R, 1, false, true, MODE>));
-                    if (e == hipSuccess) e = big_lds(reinterpret_cast<const void *>(&gemv_kernel<DT, R, 2, false, true, MODE>));
-                    if (e == hipSuccess) e = big_lds(reinterpret_cast<const void *>(&gemv_kernel<DT, R, 3, false, true, MODE>));
-                }
-                return e;
-            }();
-            if (attr != hipSuccess) return attr;
-        }
         const int64_t per = nrg / grid, extra = nrg % grid;
         if (MODE == GEMV_ARGMAX && grid > ARGMAX_PARTS) return hipErrorInvalidConfiguration;
         if (grid_out) *grid_out = grid;
-        launch_variant<DT, R, D, false, MODE>(per + (extra ? 1 : 0), dim3((unsigned)grid), dim3(64 * W), lds, st,
-                                              mats, row_bytes, U, x, per, extra);
+        launch_variant<DT, R, D, false, MODE, NT>(per + (extra ? 1 : 0), dim3((unsigned)grid, gy), dim3(64 * W), lds,
+                                                  st, mats, row_bytes, U, x, per, extra, xq8);
     } else {
-        if constexpr (MODE != GEMV_ONE) return hipErrorNotSupported;
+        if constexpr (MODE != GEMV_ONE || NT > 0) return hipErrorNotSupported;
         const int64_t M = mats.M[0];
         const int64_t grid = std::min<int64_t>(nrg, (int64_t)cus * 2);
         hipLaunchKernelGGL((gemv_multi_kernel<DT, R>), dim3((unsigned)grid), dim3(256), 0, st, mats.blob[0], M,
@@ -1186,6 +1436,248 @@ hipError_t launch_gemv(int dtype, const void *blob_v, int64_t M, int64_t K, cons
     case QMM_Q6_K: return fast ? launch_one<QMM_Q6_K, 1, 4>(blob, M, K, x, y, st, cus) : launch_generic<QMM_Q6_K>(blob, M, K, x, y, st, cus);
     default: return hipErrorInvalidValue;
     }
+}
+
+
+// ------------------------------------------------ Q8_0 activation path ----
+// Quantizer (page "cera 0.5.2 src/backend/cpu.rs", the portable Q8_0
+// quantizer): per block of 32 activations, in f32,
+//   amax = max |v| (NaN elements never win the comparison),
+//   d = amax / 127, id = 1 / d when d != 0 and 1 / d is finite, else 0,
+//   code = round-to-nearest-even(v * id), clamped to [-128, 127], NaN -> 0,
+//   stored scale = d rounded to f16 (and widened back to f32).
+// The codes use the unrounded 1/d and the stored scale the rounded d, as on
+// the page.  Eight lanes share a block (one float4 each); the block maximum
+// is exchanged with three xor shuffles.  Division and reciprocal are the
+// correctly rounded f32 operations, so every code and scale is the unique
+// result the definition gives.
+__global__ void __launch_bounds__(256) quantize_q8_0_kernel(const floatx4 *__restrict__ X, int64_t nblocks,
+                                                            float *__restrict__ scales,
+                                                            uint32_t *__restrict__ quants) {
+    const int64_t gt = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t b = gt >> 3;
+    const bool in = b < nblocks;
+    const floatx4 v = in ? X[gt] : floatx4{0.f, 0.f, 0.f, 0.f};
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const float a = fabsf(v[i]);
+        amax = a > amax ? a : amax;
+    }
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) {
+        const float a = __shfl_xor(amax, o, 64);
+        amax = a > amax ? a : amax;
+    }
+    const float d = amax / 127.0f;
+    const float r = 1.0f / d;
+    const float id = (d != 0.0f && __builtin_isfinite(r)) ? r : 0.0f;
+    uint32_t packed = 0;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const float q = rintf(v[i] * id);
+        const int c = q != q ? 0 : (q < -128.0f ? -128 : (q > 127.0f ? 127 : (int)q));
+        packed |= ((uint32_t)c & 0xFFu) << (8 * i);
+    }
+    if (in) {
+        quants[gt] = packed;
+        if ((gt & 7) == 0) scales[b] = (float)(_Float16)d;
+    }
+}
+
+hipError_t launch_quantize_q8_0(const float *X, int64_t N, int64_t K, float *scales, int8_t *quants,
+                                hipStream_t st) {
+    const int64_t nblocks = N * (K / 32);
+    // a dispatch counts its work-items in 32 bits: at most 2^29 per launch
+    const int64_t max_blocks = (int64_t)1 << 26;
+    for (int64_t b0 = 0; b0 < nblocks; b0 += max_blocks) {
+        const int64_t nb = std::min<int64_t>(max_blocks, nblocks - b0);
+        const int64_t grid = (nb * 8 + 255) / 256;
+        hipLaunchKernelGGL(quantize_q8_0_kernel, dim3((unsigned)grid), dim3(256), 0, st,
+                           reinterpret_cast<const floatx4 *>(X) + b0 * 8, nb, scales + b0,
+                           reinterpret_cast<uint32_t *>(quants) + b0 * 8);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+// Any layout (one weight block per thread, byte loads): the same integer
+// sums per activation block and the same scaling as the fast kernel.
+// c = the block's activation codes, s = their scales (one per 32).
+template <int DT>
+__device__ float block_dot8_generic(const uint8_t *p, const int8_t *c, const float *s);
+
+template <>
+__device__ float block_dot8_generic<QMM_Q4_0>(const uint8_t *p, const int8_t *c, const float *s) {
+    int acc = 0;
+    for (int j = 0; j < 16; j++) acc += ((int)(p[2 + j] & 15) - 8) * c[j] + ((int)(p[2 + j] >> 4) - 8) * c[16 + j];
+    return (h2f((uint32_t)p[0] | ((uint32_t)p[1] << 8)) * s[0]) * (float)acc;
+}
+
+template <>
+__device__ float block_dot8_generic<QMM_Q4_1>(const uint8_t *p, const int8_t *c, const float *s) {
+    int acc = 0, cs = 0;
+    for (int j = 0; j < 16; j++) {
+        acc += (int)(p[4 + j] & 15) * c[j] + (int)(p[4 + j] >> 4) * c[16 + j];
+        cs += c[j] + c[16 + j];
+    }
+    const float d = h2f((uint32_t)p[0] | ((uint32_t)p[1] << 8)), m = h2f((uint32_t)p[2] | ((uint32_t)p[3] << 8));
+    return fmaf(d * s[0], (float)acc, (m * s[0]) * (float)cs);
+}
+
+template <>
+__device__ float block_dot8_generic<QMM_Q8_0>(const uint8_t *p, const int8_t *c, const float *s) {
+    int acc = 0;
+    for (int j = 0; j < 32; j++) acc += (int)(int8_t)p[2 + j] * c[j];
+    return (h2f((uint32_t)p[0] | ((uint32_t)p[1] << 8)) * s[0]) * (float)acc;
+}
+
+template <int DT>
+__device__ float kquant_dot8_generic(const uint8_t *p, const int8_t *c, const float *s) {
+    constexpr int QS = DT == QMM_Q5_K ? 48 : 16;  // offset of the nibbles
+    const float d = h2f((uint32_t)p[0] | ((uint32_t)p[1] << 8));
+    const float dmin = h2f((uint32_t)p[2] | ((uint32_t)p[3] << 8));
+    uint32_t w[3];
+    for (int i = 0; i < 3; i++)
+        w[i] = (uint32_t)p[4 + 4 * i] | ((uint32_t)p[5 + 4 * i] << 8) | ((uint32_t)p[6 + 4 * i] << 16) |
+               ((uint32_t)p[7 + 4 * i] << 24);
+    float total = 0.f;
+#pragma unroll 1
+    for (int i = 0; i < 8; i++) {
+        int sc, mn;
+        q4k_scale_min(w[0], w[1], w[2], i, sc, mn);
+        int acc = 0, cs = 0;
+        for (int e = 0; e < 32; e++) {
+            const uint8_t b = p[QS + 32 * (i >> 1) + e];
+            int q = (i & 1) ? (b >> 4) : (b & 15);
+            if (DT == QMM_Q5_K) q |= ((p[16 + e] >> i) & 1) << 4;
+            acc += q * c[32 * i + e];
+            cs += c[32 * i + e];
+        }
+        total += fmaf(d * s[i], (float)(sc * acc), -((dmin * s[i]) * (float)(mn * cs)));
+    }
+    return total;
+}
+template <>
+__device__ float block_dot8_generic<QMM_Q4_K>(const uint8_t *p, const int8_t *c, const float *s) {
+    return kquant_dot8_generic<QMM_Q4_K>(p, c, s);
+}
+template <>
+__device__ float block_dot8_generic<QMM_Q5_K>(const uint8_t *p, const int8_t *c, const float *s) {
+    return kquant_dot8_generic<QMM_Q5_K>(p, c, s);
+}
+
+template <>
+__device__ float block_dot8_generic<QMM_Q6_K>(const uint8_t *p, const int8_t *c, const float *s) {
+    const float d = h2f((uint32_t)p[208] | ((uint32_t)p[209] << 8));
+    float total = 0.f;
+    for (int g = 0; g < 16; g++) {  // 16 groups of 16 weights sharing one sub-scale
+        int acc = 0;
+        for (int i = 0; i < 16; i++) {
+            const int j = 16 * g + i, h = j >> 7, q4 = (j & 127) >> 5, l = j & 31;
+            const uint8_t lb = p[64 * h + 32 * (q4 & 1) + l];
+            const int lo = (q4 < 2) ? (lb & 15) : (lb >> 4);
+            const int hi = (p[128 + 32 * h + l] >> (2 * q4)) & 3;
+            acc += ((lo | (hi << 4)) - 32) * c[j];
+        }
+        total = fmaf(d * s[g >> 1], (float)((int)(int8_t)p[192 + g] * acc), total);
+    }
+    return total;
+}
+
+// Y[tok][m] for the tokens of grid row blockIdx.y (one each).
+template <int DT, int R>
+__global__ void __launch_bounds__(256) gemv_q8_generic_kernel(const uint8_t *__restrict__ blob, int64_t M, int64_t K,
+                                                              const int8_t *__restrict__ xq,
+                                                              const float *__restrict__ xsc, float *__restrict__ Y) {
+    constexpr int BS = Geo<DT>::BS, BB = Geo<DT>::BB;
+    __shared__ float red[R][4];
+    const int t = threadIdx.x, T = blockDim.x, lane = t & 63, wave = t >> 6, nwaves = T >> 6;
+    const int64_t tok = blockIdx.y;
+    const int8_t *c = xq + tok * K;
+    const float *s = xsc + tok * (K / 32);
+    float *y = Y + tok * M;
+    const int64_t nb = K / BS, row_bytes = nb * BB, nrg = (M + R - 1) / R;
+    for (int64_t rg = blockIdx.x; rg < nrg; rg += gridDim.x) {
+        const int64_t row0 = rg * R;
+        float acc[R];
+        for (int r = 0; r < R; r++) acc[r] = 0.f;
+        for (int64_t b = t; b < nb; b += T)
+            for (int r = 0; r < R; r++)
+                if (row0 + r < M)
+                    acc[r] += block_dot8_generic<DT>(blob + (row0 + r) * row_bytes + b * BB, c + b * BS,
+                                                     s + b * (BS / 32));
+        for (int r = 0; r < R; r++) {
+            const float v = wave_sum_to_lane63(acc[r]);
+            if (lane == 63) red[r][wave] = v;
+        }
+        __syncthreads();
+        if (t < R && row0 + t < M) {
+            float v = 0.f;
+            for (int w = 0; w < nwaves; w++) v += red[t][w];
+            y[row0 + t] = v;
+        }
+        __syncthreads();
+    }
+}
+
+// Tokens per weight read of the int8-activation fast kernel.
+constexpr int Q8A_TOKENS = 4;
+
+template <int DT, int R, int D, int NT>
+static hipError_t launch_q8a_fast(const uint8_t *blob, int64_t M, int64_t K, int64_t N, const int8_t *xq,
+                                  const float *xsc, float *Y, hipStream_t st, int cus) {
+    GemvMats m{};
+    m.blob[0] = blob;
+    m.y[0] = Y;
+    m.M[0] = M;
+    for (int j = 1; j <= GEMV_MAX_MATS; j++) m.g_lo[j] = (M + R - 1) / R;
+    return launch_fast<DT, R, D, GEMV_ONE, NT>(m, K, nullptr, st, cus, nullptr, XQ8{xq, xsc, N});
+}
+
+template <int DT, int R1, int D1>
+static hipError_t launch_q8a_dt(const uint8_t *blob, int64_t M, int64_t K, int64_t N, const int8_t *xq,
+                                const float *xsc, float *Y, hipStream_t st, int cus) {
+    if (N == 1) return launch_q8a_fast<DT, R1, D1, 1>(blob, M, K, N, xq, xsc, Y, st, cus);
+    return launch_q8a_fast<DT, 1, 1, Q8A_TOKENS>(blob, M, K, N, xq, xsc, Y, st, cus);
+}
+
+template <int DT>
+static hipError_t launch_q8a_generic(const uint8_t *blob, int64_t M, int64_t K, int64_t N, const int8_t *xq,
+                                     const float *xsc, float *Y, hipStream_t st, int cus) {
+    constexpr int R = 4;
+    const int64_t nrg = (M + R - 1) / R;
+    const int64_t grid = nrg < (int64_t)cus * 8 ? nrg : (int64_t)cus * 8;
+    hipLaunchKernelGGL((gemv_q8_generic_kernel<DT, R>), dim3((unsigned)grid, (unsigned)N), dim3(256), 0, st, blob, M,
+                       K, xq, xsc, Y);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_q8act(int dtype, const void *blob_v, int64_t M, int64_t K, int64_t N, const float *xsc,
+                             const int8_t *xq, float *Y, hipStream_t st, int cus) {
+    const uint8_t *blob = static_cast<const uint8_t *>(blob_v);
+    const bool fast = gemv_fused_ok(dtype, K);
+    // the grid's second dimension holds token groups: at most 65535 per launch
+    const int64_t chunk = fast ? (N == 1 ? 1 : (int64_t)65535 * Q8A_TOKENS) : 65535;
+    for (int64_t n0 = 0; n0 < N; n0 += chunk) {
+        const int64_t nt = std::min<int64_t>(chunk, N - n0);
+        const int8_t *q = xq + n0 * K;
+        const float *s = xsc + n0 * (K / 32);
+        float *y = Y + n0 * M;
+        hipError_t e;
+        switch (dtype) {
+        case QMM_Q4_0: e = fast ? launch_q8a_dt<QMM_Q4_0, 2, 3>(blob, M, K, nt, q, s, y, st, cus) : launch_q8a_generic<QMM_Q4_0>(blob, M, K, nt, q, s, y, st, cus); break;
+        case QMM_Q4_1: e = fast ? launch_q8a_dt<QMM_Q4_1, 2, 3>(blob, M, K, nt, q, s, y, st, cus) : launch_q8a_generic<QMM_Q4_1>(blob, M, K, nt, q, s, y, st, cus); break;
+        case QMM_Q8_0: e = fast ? launch_q8a_dt<QMM_Q8_0, 1, 4>(blob, M, K, nt, q, s, y, st, cus) : launch_q8a_generic<QMM_Q8_0>(blob, M, K, nt, q, s, y, st, cus); break;
+        case QMM_Q4_K: e = fast ? launch_q8a_dt<QMM_Q4_K, 2, 3>(blob, M, K, nt, q, s, y, st, cus) : launch_q8a_generic<QMM_Q4_K>(blob, M, K, nt, q, s, y, st, cus); break;
+        case QMM_Q5_K: e = fast ? launch_q8a_dt<QMM_Q5_K, 1, 3>(blob, M, K, nt, q, s, y, st, cus) : launch_q8a_generic<QMM_Q5_K>(blob, M, K, nt, q, s, y, st, cus); break;
+        case QMM_Q6_K: e = fast ? launch_q8a_dt<QMM_Q6_K, 1, 4>(blob, M, K, nt, q, s, y, st, cus) : launch_q8a_generic<QMM_Q6_K>(blob, M, K, nt, q, s, y, st, cus); break;
+        default: return hipErrorInvalidValue;
+        }
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace qmm

@@ -42,4 +42,14 @@ hipError_t launch_gemm_swiglu(int dtype, const void *gate, const void *up, int64
 hipError_t launch_gemm_mfma(int dtype, const void *blob, int64_t M, int64_t K, int64_t N, const float *X,
                             float *Y, hipStream_t st);
 
+// Q8_0 quantization of N activation rows of K (K % 32 == 0): scales f32
+// [N][K/32], codes int8 [N][K].
+hipError_t launch_quantize_q8_0(const float *X, int64_t N, int64_t K, float *scales, int8_t *quants,
+                                hipStream_t st);
+
+// Y[N][M] = W Xq^T with Q8_0-quantized activations (integer block dots, f32
+// scaling); up to 4 tokens per weight read.
+hipError_t launch_gemm_q8act(int dtype, const void *blob, int64_t M, int64_t K, int64_t N, const float *xsc,
+                             const int8_t *xq, float *Y, hipStream_t st, int cus);
+
 }  // namespace qmm

@@ -190,6 +190,48 @@ int qmm_gemm(const void *w_blob, int dtype, int64_t M, int64_t K, int64_t N,
 int qmm_gemm_swiglu(const void *gate_blob, const void *up_blob, int dtype, int64_t M, int64_t K,
                     int64_t N, const float *X, float *out, void *stream);
 
+/* Q8_0 quantization of activations, the int8-activation variant's first step
+ * (page "cera 0.5.2 src/backend/cpu.rs", the portable Q8_0 quantizer and its
+ * caller-owned scale / quant buffers).  For each row n and each block b of 32
+ * consecutive values v = X[n][32b .. 32b+32), in f32:
+ *     amax = max |v| (NaN elements are skipped), d = amax / 127,
+ *     id = 1/d when d != 0 and 1/d is finite, else 0,
+ *     quants[n][32b+j] = round-half-even(v[j] * id) clamped to [-128, 127]
+ *                        (a NaN product gives 0),
+ *     scales[n][b] = d rounded to binary16 (round-half-even), stored as f32.
+ * The codes use the unrounded 1/d, the scale the rounded d, as the page does.
+ * Every output is the unique value this definition gives (correctly rounded
+ * division and reciprocal), so results are bit-exact and deterministic.
+ *   X       device f32 [N][K] row-major, 16-B aligned
+ *   scales  device f32 [N][K/32], 16-B aligned; overwritten
+ *   quants  device int8 [N][K], 16-B aligned; overwritten
+ * N >= 1 and K a positive multiple of 32, else QMM_ERR_SHAPE. */
+int qmm_quantize_q8_0(const float *X, int64_t N, int64_t K, float *scales, int8_t *quants,
+                      void *stream);
+
+/* The matmul on Q8_0-quantized activations (page "cera 0.5.2
+ * src/backend/cpu.rs": the int8 GEMV/GEMM paths that take the activations as
+ * Q8_0 blocks; the weights' offsets go through per-block sums of the
+ * activation codes):
+ *     Y[n][m] = sum_k W[m][k] * scales[n][k/32] * quants[n][k]
+ * Each weight block meets the codes in exact integer dot products (one per
+ * activation block of 32, one per 16-weight sub-scale group for Q6_K) that
+ * are scaled once in f32: Q8_0 and Q4_0 by d*xs, Q6_K by d*xs*sc, Q4_K and
+ * Q5_K by d*xs*sc with the minimum term dmin*xs*m times the block's code sum,
+ * Q4_1 by d*xs with m*xs times the code sum.  Error bound: 1e-5 of
+ * sum_k (|w - o| + |o|) |xq| per output, o the weight's offset part (m for
+ * Q4_1, -dmin*m for Q4_K and Q5_K, none for the others), xq the dequantized
+ * activation.  Up to 4 tokens share one read of the weights (K a multiple of
+ * 64 up to 16384, even block count per row for Q4_0, Q4_1, Q8_0, Q6_K; other
+ * shapes run one weight block per thread).
+ *   w_blob  device blob as for qmm_gemm, 16-B aligned
+ *   scales  device f32 [N][K/32] as qmm_quantize_q8_0 writes them, 16-B aligned
+ *   quants  device int8 [N][K], 16-B aligned
+ *   Y       device f32 [N][M] row-major, 4-B aligned; overwritten
+ * Errors as qmm_gemm. */
+int qmm_gemm_q8act(const void *w_blob, int dtype, int64_t M, int64_t K, int64_t N,
+                   const float *scales, const int8_t *quants, float *Y, void *stream);
+
 /* Which arithmetic qmm_gemm uses for these sizes: 0 = f32 (GEMV family),
  * 1 = f16 matrix-core GEMM, or a negative status for invalid arguments. */
 int qmm_gemm_path(int dtype, int64_t M, int64_t K, int64_t N);

@@ -223,3 +223,44 @@ def test_gemm_swiglu_without_gpu_reports_device():
         pytest.skip("a GPU is present; covered by the GPU tests")
     assert q.lib().qmm_gemm_swiglu(A16, A16, 12, 8, 1024, 64, A16, A16, None) == q.QMM_ERR_DEVICE
     assert q.lib().qmm_gemm_swiglu(A16, A16, 2, 8, 1024, 2, A16, A16, None) == q.QMM_ERR_DEVICE
+
+
+@pytest.mark.parametrize("args,code", [
+    ((A16, 0, 64, A16, A16), q.QMM_ERR_SHAPE),
+    ((A16, 2, 0, A16, A16), q.QMM_ERR_SHAPE),
+    ((A16, 2, 48, A16, A16), q.QMM_ERR_SHAPE),          # K % 32
+    ((0, 2, 64, A16, A16), q.QMM_ERR_NULL),
+    ((A16, 2, 64, 0, A16), q.QMM_ERR_NULL),
+    ((A16, 2, 64, A16, 0), q.QMM_ERR_NULL),
+    ((A16 + 4, 2, 64, A16, A16), q.QMM_ERR_ALIGN),
+    ((A16, 2, 64, A16 + 8, A16), q.QMM_ERR_ALIGN),
+    ((A16, 2, 64, A16, A16 + 4), q.QMM_ERR_ALIGN),
+])
+def test_quantize_q8_0_rejects(args, code):
+    assert q.lib().qmm_quantize_q8_0(*args, None) == code
+
+
+@pytest.mark.parametrize("args,code", [
+    ((A16, 5, 8, 64, 1, A16, A16, A16), q.QMM_ERR_DTYPE),
+    ((A16, 2, 8, 64, 0, A16, A16, A16), q.QMM_ERR_SHAPE),
+    ((A16, 12, 8, 128, 1, A16, A16, A16), q.QMM_ERR_SHAPE),
+    ((A16, 2, 0, 64, 1, A16, A16, A16), q.QMM_ERR_SHAPE),
+    ((0, 2, 8, 64, 1, A16, A16, A16), q.QMM_ERR_NULL),
+    ((A16, 2, 8, 64, 1, 0, A16, A16), q.QMM_ERR_NULL),
+    ((A16, 2, 8, 64, 1, A16, 0, A16), q.QMM_ERR_NULL),
+    ((A16, 2, 8, 64, 1, A16, A16, 0), q.QMM_ERR_NULL),
+    ((A16 + 2, 2, 8, 64, 1, A16, A16, A16), q.QMM_ERR_ALIGN),
+    ((A16, 2, 8, 64, 1, A16 + 8, A16, A16), q.QMM_ERR_ALIGN),
+    ((A16, 2, 8, 64, 1, A16, A16 + 4, A16), q.QMM_ERR_ALIGN),
+    ((A16, 2, 8, 64, 1, A16, A16, A16 + 2), q.QMM_ERR_ALIGN),
+])
+def test_gemm_q8act_rejects(args, code):
+    assert q.lib().qmm_gemm_q8act(*args, None) == code
+
+
+def test_q8act_calls_without_gpu_report_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; covered by the GPU tests")
+    assert q.lib().qmm_quantize_q8_0(A16, 2, 64, A16, A16, None) == q.QMM_ERR_DEVICE
+    assert q.lib().qmm_gemm_q8act(A16, 14, 8, 256, 3, A16, A16, A16, None) == q.QMM_ERR_DEVICE

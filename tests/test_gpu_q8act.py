@@ -1,0 +1,206 @@
+"""The int8-activation variant on the GPU against the CPU oracle, through the C ABI.
+
+  * qmm_quantize_q8_0: scales and codes bit-identical to the oracle's
+    quantizer (a floating-point decision that yields integers, taken in f32 on
+    both sides): hand-derived blocks, special values (zeros, NaN, +-Inf,
+    overflowing and subnormal scales, ties), random rows up to 512 x 14336.
+  * qmm_gemm_q8act: |Y_gpu - Y_exact| <= 1e-5 * Splus per output, Y_exact the
+    oracle's f64 sum over the dequantized codes and Splus = sum_k
+    (|w - o| + |o|) |xq| (o the weight's offset part; Splus = S for Q8_0, Q4_0
+    and Q6_K); the codes the GPU reads are the oracle's.  Small shapes with
+    ragged M, odd block counts (the byte-load kernel), K beyond 4096 (the
+    K-split workgroups), N from 1 to 9; full-size workloads on sampled rows.
+  * Bitwise: a token of an N-token call equals the single-token call; two
+    runs give equal bits.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gguf_block_quant_qmm_amd as q
+import oracle
+from qmm_inputs import WORKLOADS, make_blob, make_x, rng_for
+from pins import load_q8_act_golden
+
+pytestmark = pytest.mark.gpu
+
+DTYPES = [q.QMM_Q4_0, q.QMM_Q8_0, q.QMM_Q4_K, q.QMM_Q6_K, q.QMM_Q4_1, q.QMM_Q5_K]
+NAME = {2: "Q4_0", 3: "Q4_1", 8: "Q8_0", 12: "Q4_K", 13: "Q5_K", 14: "Q6_K"}
+TAU = 1e-5
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.set_device(0)
+
+
+def to_dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def bs_of(dt):
+    return 256 if dt in (q.QMM_Q4_K, q.QMM_Q5_K, q.QMM_Q6_K) else 32
+
+
+def gpu_quantize(X):
+    N, K = X.shape
+    sc = torch.full((N, K // 32), float("nan"), device="cuda")
+    qq = torch.full((N, K), 99, dtype=torch.int8, device="cuda")
+    q.qmm_quantize_q8_0(to_dev(X), N, K, sc, qq)
+    torch.cuda.synchronize()
+    return sc.cpu().numpy(), qq.cpu().numpy()
+
+
+def gpu_q8act(dt, blob_d, M, K, sc, qq):
+    N = qq.shape[0]
+    Y = torch.full((N, M), float("nan"), device="cuda")
+    q.qmm_gemm_q8act(blob_d, dt, M, K, N, to_dev(sc), to_dev(qq), Y)
+    torch.cuda.synchronize()
+    return Y.cpu().numpy()
+
+
+def same_bits(a, b):
+    return np.array_equal(np.asarray(a).view(np.uint32), np.asarray(b).view(np.uint32))
+
+
+def check(Yg, Y64, Sp, label):
+    assert Yg.shape == Y64.shape, label
+    assert np.all(np.isfinite(Yg)), f"{label}: non-finite output"
+    err = np.abs(Yg.astype(np.float64) - Y64)
+    zero = Sp == 0
+    assert np.all(Yg[zero] == 0), f"{label}: Splus = 0 but output is not exactly 0"
+    if (~zero).any():
+        ratio = err[~zero] / Sp[~zero]
+        worst = int(np.argmax(ratio))
+        assert ratio[worst] <= TAU, f"{label}: |err|/Splus = {ratio[worst]:.3g} > {TAU} at flat index {worst}"
+
+
+# ------------------------------------------------------------ quantizer ----
+
+def check_quantizer(X, label):
+    s_o, q_o = oracle.quantize_q8_0(X)
+    s_g, q_g = gpu_quantize(X)
+    assert same_bits(s_g, s_o), f"{label}: scales differ at {np.argwhere(s_g.view(np.uint32) != s_o.view(np.uint32))[:4].tolist()}"
+    bad = np.argwhere(q_g != q_o)
+    assert bad.size == 0, f"{label}: codes differ at {bad[:4].tolist()}"
+
+
+def test_quantizer_hand_derived_blocks():
+    recs = load_q8_act_golden()
+    X = np.stack([r[1] for r in recs])
+    s_g, q_g = gpu_quantize(X)
+    for i, (name, _, scale, codes) in enumerate(recs):
+        assert s_g[i, 0] == scale or (scale != scale and s_g[i, 0] != s_g[i, 0]), name
+        assert np.array_equal(q_g[i], codes), name
+    check_quantizer(X, "golden blocks")
+
+
+def test_quantizer_special_values():
+    rng = rng_for(900, 0)
+    rows = []
+    base = rng.standard_normal(64).astype(np.float32)
+    rows.append(np.zeros(64, np.float32))                               # d = 0: id = 0, all codes 0
+    r = base.copy(); r[3] = np.nan; rows.append(r)                      # NaN skipped by amax, code 0
+    r = base.copy(); r[40] = np.inf; rows.append(r)                     # amax = Inf: scale Inf, codes 0
+    r = base.copy(); r[5] = -np.inf; r[6] = np.nan; rows.append(r)
+    rows.append(base * np.float32(1e7))                                 # d > 65504: f16 scale Inf
+    rows.append(base * np.float32(1e-39))                               # subnormal d: 1/d overflows, id = 0
+    rows.append(base * np.float32(1e-30))                               # small normal d, f16 scale 0 or subnormal
+    r = (np.arange(64, dtype=np.float32) - 31.5)                        # ties: k + 0.5 with d = 1
+    r[0] = 127.0; r[32] = -127.0; rows.append(r.astype(np.float32))
+    rows.append(np.full(64, -3.0e-5, np.float32))                       # f16-subnormal scale
+    rows.append(np.float32(3.4e38) * np.sign(base).astype(np.float32))  # amax near f32 max
+    check_quantizer(np.stack(rows).astype(np.float32), "special rows")
+
+
+@pytest.mark.parametrize("N,K", [(1, 32), (3, 96), (7, 4096), (5, 14336), (512, 4096), (2, 65600)])
+def test_quantizer_random(N, K):
+    X = make_x(N, K, rng_for(901, N * 100000 + K))
+    X[0, :32] *= np.float32(1e3)
+    check_quantizer(X, f"N={N} K={K}")
+
+
+# ------------------------------------------------------- int8 matmul ----
+
+def shapes(dt):
+    if bs_of(dt) == 32:
+        # odd block count -> byte-load kernel; K > 4096 -> K-split workgroups;
+        # K > 16384 -> byte-load kernel
+        return [(1, 64), (3, 96), (67, 256), (300, 1024), (129, 4160), (50, 14336), (33, 16416)]
+    return [(1, 256), (3, 512), (67, 768), (300, 2048), (50, 4096), (9, 16640)]
+
+
+@pytest.mark.parametrize("dt", DTYPES, ids=NAME.get)
+@pytest.mark.parametrize("N", [1, 2, 3, 4, 5, 9])
+def test_q8act_small(dt, N):
+    for i, (M, K) in enumerate(shapes(dt)):
+        blob = make_blob(dt, M, K, rng_for(910 + dt, i))
+        sc, qq = oracle.quantize_q8_0(make_x(N, K, rng_for(910 + dt, 100 * N + i)))
+        _, Y64, _, Sp = oracle.matmul_q8act(dt, blob, M, K, sc, qq)
+        Yg = gpu_q8act(dt, to_dev(blob), M, K, sc, qq)
+        check(Yg, Y64, Sp, f"{NAME[dt]} q8act M={M} K={K} N={N}")
+
+
+@pytest.mark.parametrize("dt", DTYPES, ids=NAME.get)
+def test_q8act_tokens_match_single_token_bitwise(dt):
+    for i, (M, K) in enumerate([(301, 4 * bs_of(dt) * 4), (97, 8192 if bs_of(dt) == 256 else 4160)]):
+        blob_d = to_dev(make_blob(dt, M, K, rng_for(920 + dt, i)))
+        sc, qq = oracle.quantize_q8_0(make_x(7, K, rng_for(920 + dt, 10 + i)))
+        Y = gpu_q8act(dt, blob_d, M, K, sc, qq)
+        assert same_bits(Y, gpu_q8act(dt, blob_d, M, K, sc, qq)), f"{NAME[dt]}: two runs differ"
+        for n in range(7):
+            y1 = gpu_q8act(dt, blob_d, M, K, sc[n:n + 1], qq[n:n + 1])
+            assert same_bits(Y[n:n + 1], y1), f"{NAME[dt]} M={M} K={K}: token {n} of 7 differs from its own call"
+
+
+def test_q8act_planted_cancellation():
+    # Q4_K rows whose weights are mostly the minimum term: the offset part is
+    # taken through the code sums, so the bound is relative to Splus, and the
+    # result must still meet it where S alone is much smaller
+    dt, M, K = q.QMM_Q4_K, 64, 2048
+    blob = make_blob(dt, M, K, rng_for(930, 0)).reshape(M, K // 256, 144)
+    blob[:, :, 16:] = 0x11                     # every code 1: w = d*sc - dmin*m
+    blob = blob.reshape(-1)
+    sc, qq = oracle.quantize_q8_0(make_x(2, K, rng_for(930, 1)))
+    _, Y64, S, Sp = oracle.matmul_q8act(dt, blob, M, K, sc, qq)
+    Yg = gpu_q8act(dt, to_dev(blob), M, K, sc, qq)
+    check(Yg, Y64, Sp, "Q4_K planted offsets")
+
+
+def sample_rows(M, n, seed):
+    rows = rng_for(940, seed).choice(M, size=min(n, M), replace=False)
+    return np.unique(np.concatenate([rows, [0, M - 1]]))
+
+
+@pytest.mark.parametrize("wid,N", [(1, 1), (2, 1), (3, 1), (4, 1), (5, 1), (5, 4), (6, 32), (8, 8), (10, 3)])
+def test_q8act_full_size_workloads(wid, N):
+    label, dt, M, K, _ = WORKLOADS[wid]
+    blob = make_blob(dt, M, K, rng_for(wid, 0))
+    X = make_x(N, K, rng_for(wid, 1000 + N))
+    # the quantizer at full size, then the matmul on the oracle's codes
+    check_quantizer(X, label)
+    sc, qq = oracle.quantize_q8_0(X)
+    rows = sample_rows(M, 96, wid * 10 + N)
+    _, Y64, _, Sp = oracle.matmul_q8act(dt, blob, M, K, sc, qq, rows=rows)
+    Yg = gpu_q8act(dt, to_dev(blob), M, K, sc, qq)
+    assert np.all(np.isfinite(Yg)), label
+    check(Yg[:, rows], Y64, Sp, f"{label} q8act N={N}")
+
+
+def test_quantize_then_matmul_on_device():
+    # the two entry points chained on device buffers, against the oracle's
+    # quantizer and matmul end to end
+    dt, M, K, N = q.QMM_Q6_K, 513, 4096, 3
+    blob = make_blob(dt, M, K, rng_for(950, 0))
+    X = make_x(N, K, rng_for(950, 1))
+    sc_d = torch.empty((N, K // 32), device="cuda")
+    qq_d = torch.empty((N, K), dtype=torch.int8, device="cuda")
+    Y = torch.empty((N, M), device="cuda")
+    q.qmm_quantize_q8_0(to_dev(X), N, K, sc_d, qq_d)
+    q.qmm_gemm_q8act(to_dev(blob), dt, M, K, N, sc_d, qq_d, Y)
+    torch.cuda.synchronize()
+    sc, qq = oracle.quantize_q8_0(X)
+    _, Y64, _, Sp = oracle.matmul_q8act(dt, blob, M, K, sc, qq)
+    check(Y.cpu().numpy(), Y64, Sp, "quantize + q8act on device")
