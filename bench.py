@@ -11,8 +11,9 @@ qmm_gemv_concat (one launch, one read of x; each output has the bits of a
 separate qmm_gemv call).  `value` is the step's weight bytes over its measured
 GPU time.  The same layer as four separate launches (each through qmm_gemm
 with N = 1, i.e. path selection -> the f32 GEMV) is reported as
-"decode_unfused", and with gate/up through qmm_gemv_swiglu as
-"decode_swiglu".  Weight copies are rotated so
+"decode_unfused", with gate/up through qmm_gemv_swiglu as "decode_swiglu",
+and with int8 activations (each input quantized by qmm_quantize_q8_0, then one
+qmm_gemm_q8act per matrix) as "decode_q8act".  Weight copies are rotated so
 that more than 1 GiB of distinct weights is cycled (more than the 256 MB
 last-level cache): every step streams its weights from HBM.  Inputs are
 resident in HBM before timing starts.
