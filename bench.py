@@ -12,8 +12,9 @@ separate qmm_gemv call).  `value` is the step's weight bytes over its measured
 GPU time.  The same layer as four separate launches (each through qmm_gemm
 with N = 1, i.e. path selection -> the f32 GEMV) is reported as
 "decode_unfused", with gate/up through qmm_gemv_swiglu as "decode_swiglu",
-and with int8 activations (each input quantized by qmm_quantize_q8_0, then one
-qmm_gemm_q8act per matrix) as "decode_q8act".  Weight copies are rotated so
+and with int8 activations (the same three launches through qmm_gemv_q8act /
+qmm_gemv_concat_q8act, which quantize x to Q8_0 inside the launch) as
+"decode_q8act".  Weight copies are rotated so
 that more than 1 GiB of distinct weights is cycled (more than the 256 MB
 last-level cache): every step streams its weights from HBM.  Inputs are
 resident in HBM before timing starts.
@@ -145,18 +146,13 @@ def main():
         q.qmm_gemv_swiglu(copies[1][c], copies[2][c], dg, Mg, Kg, xs[1], swiglu_y, stream=stream)
         q.qmm_gemv(copies[3][c], dd, Md, Kd, xs[3], ys[3], stream=stream)
 
-    # int8 activations: each distinct input quantized once per step
-    # (qmm_quantize_q8_0), then one qmm_gemm_q8act launch per matrix
-    q8_in = (0, 1, 1, 3)  # gate and up share one input, as in step_fused
-    q8sc = {i: torch.empty((1, mats[i][3] // 32), device=dev) for i in set(q8_in)}
-    q8q = {i: torch.empty((1, mats[i][3]), dtype=torch.int8, device=dev) for i in set(q8_in)}
-
+    # int8 activations (the CPU page's Q8_0 decode path): the same three
+    # launches, each quantizing its x to Q8_0 inside the launch
     def step_q8act(c):
-        for i in sorted(q8sc):
-            q.qmm_quantize_q8_0(xs[i], 1, mats[i][3], q8sc[i], q8q[i], stream=stream)
-        for i, (name, dt, M, K, _) in enumerate(mats):
-            j = q8_in[i]
-            q.qmm_gemm_q8act(copies[i][c], dt, M, K, 1, q8sc[j], q8q[j], ys[i], stream=stream)
+        (_, dq, Mq, Kq, _), (_, dg, Mg, Kg, _), _, (_, dd, Md, Kd, _) = mats
+        q.qmm_gemv_q8act(copies[0][c], dq, Mq, Kq, xs[0], ys[0], stream=stream)
+        q.qmm_gemv_concat_q8act([copies[1][c], copies[2][c]], dg, [Mg, Mg], Kg, xs[1], gate_up_ys, stream=stream)
+        q.qmm_gemv_q8act(copies[3][c], dd, Md, Kd, xs[3], ys[3], stream=stream)
 
     def time_layer(step):
         """(span ms over args.steps steps, host seconds), events only at step boundaries."""
@@ -211,11 +207,15 @@ def main():
             lambda c: q.qmm_gemv_swiglu(copies[1][c], copies[2][c], dg, Mg, Kg, xs[1], swiglu_y, stream=stream),
             gu_bytes)
         for i, (name, dt, M, K, _) in enumerate(mats):
-            j = q8_in[i]
             per_matrix[name + " q8act"] = time_calls(
-                lambda c, i=i, j=j, dt=dt, M=M, K=K: q.qmm_gemm_q8act(copies[i][c], dt, M, K, 1, q8sc[j], q8q[j],
-                                                                      ys[i], stream=stream),
+                lambda c, i=i, dt=dt, M=M, K=K: q.qmm_gemv_q8act(copies[i][c], dt, M, K, xs[i], ys[i], stream=stream),
                 copies[i][0].numel())
+        per_matrix["gate+up concat q8act"] = time_calls(
+            lambda c: q.qmm_gemv_concat_q8act([copies[1][c], copies[2][c]], dg, [Mg, Mg], Kg, xs[1], gate_up_ys,
+                                              stream=stream), gu_bytes)
+        per_matrix["gate+up swiglu q8act"] = time_calls(
+            lambda c: q.qmm_gemv_swiglu_q8act(copies[1][c], copies[2][c], dg, Mg, Kg, xs[1], swiglu_y,
+                                              stream=stream), gu_bytes)
 
     def layer_rate(span):
         if span is None:
@@ -269,10 +269,10 @@ def main():
             "decode_unfused": {"launches": 4, **(layer_rate(span_unf) or {})},
             "decode_swiglu": {"launches": 3, **(layer_rate(span_swi) or {}),
                               "note": "gate/up through qmm_gemv_swiglu (outputs silu(g)*u instead of g and u)"},
-            "decode_q8act": {"launches": 7, **(layer_rate(span_q8) or {}),
-                             "note": "int8 activations: 3 qmm_quantize_q8_0 + 4 qmm_gemm_q8act launches (x "
-                                     "quantized to Q8_0 blocks, integer block dots; different numbers from the "
-                                     "f32 path)"},
+            "decode_q8act": {"launches": 3, **(layer_rate(span_q8) or {}),
+                             "note": "int8 activations: qmm_gemv_q8act (q_proj, down) and qmm_gemv_concat_q8act "
+                                     "(gate+up), each quantizing x to Q8_0 inside the launch; integer block dots, "
+                                     "different numbers from the f32 path"},
             "timing": "HIP events on the launch stream at step boundaries; per-launch = span / launches",
             "per_matrix": per_matrix,
             "gpu": props.name,

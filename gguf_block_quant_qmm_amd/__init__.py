@@ -20,6 +20,9 @@ there is no CPU fallback.
                                                      X -> Q8_0 activation blocks
     qmm_gemm_q8act(w, dtype, M, K, N, scales, quants, Y, stream=None)
                                                      Y = Xq W^T (int8 activations)
+    qmm_gemv_q8act / qmm_gemv_concat_q8act / qmm_gemv_swiglu_q8act
+                                                     the decode calls above with x
+                                                     quantized inside the launch
 """
 from __future__ import annotations
 
@@ -40,7 +43,8 @@ QMM_GEMV_MAX_MATS = 4
 QMM_ARGMAX_WORK_BYTES = 32768
 
 EXPORTS = ("qmm_gemv", "qmm_gemv_concat", "qmm_gemv_swiglu", "qmm_gemv_argmax", "qmm_gemm", "qmm_gemm_swiglu",
-           "qmm_quantize_q8_0", "qmm_gemm_q8act", "qmm_gemm_path", "qmm_blob_bytes", "qmm_block_elems",
+           "qmm_quantize_q8_0", "qmm_gemm_q8act", "qmm_gemv_q8act", "qmm_gemv_concat_q8act",
+           "qmm_gemv_swiglu_q8act", "qmm_gemm_path", "qmm_blob_bytes", "qmm_block_elems",
            "qmm_block_bytes", "qmm_strerror")
 
 _lib = None
@@ -76,6 +80,12 @@ def lib():
         L.qmm_quantize_q8_0.restype = ci
         L.qmm_gemm_q8act.argtypes = [vp, ci, i64, i64, i64, vp, vp, vp, vp]
         L.qmm_gemm_q8act.restype = ci
+        L.qmm_gemv_q8act.argtypes = [vp, ci, i64, i64, vp, vp, vp]
+        L.qmm_gemv_q8act.restype = ci
+        L.qmm_gemv_concat_q8act.argtypes = [ci, vp, vp, ci, i64, vp, vp, vp]
+        L.qmm_gemv_concat_q8act.restype = ci
+        L.qmm_gemv_swiglu_q8act.argtypes = [vp, vp, ci, i64, i64, vp, vp, vp]
+        L.qmm_gemv_swiglu_q8act.restype = ci
         L.qmm_gemm_path.argtypes = [ci, i64, i64, i64]
         L.qmm_gemm_path.restype = ci
         L.qmm_blob_bytes.argtypes = [ci, i64, i64]
@@ -223,3 +233,39 @@ def qmm_gemm_q8act(w, dtype: int, M: int, K: int, N: int, scales, quants, Y, str
                               _stream(stream))
     if rc != QMM_OK:
         raise QmmError(rc, "qmm_gemm_q8act")
+
+
+def qmm_gemv_q8act(w, dtype: int, M: int, K: int, x, y, stream=None) -> None:
+    import torch
+    nb = blob_bytes(dtype, M, K)
+    rc = lib().qmm_gemv_q8act(_addr(w, nb or None, "w_blob"), dtype, M, K,
+                              _addr(x, 4 * K, "x", torch.float32), _addr(y, 4 * M, "y", torch.float32),
+                              _stream(stream))
+    if rc != QMM_OK:
+        raise QmmError(rc, "qmm_gemv_q8act")
+
+
+def qmm_gemv_concat_q8act(ws, dtype: int, Ms, K: int, x, ys, stream=None) -> None:
+    import torch
+    n = len(ws)
+    if not (len(Ms) == n == len(ys)):
+        raise ValueError("ws, Ms and ys need one entry per matrix")
+    blobs = (ctypes.c_void_p * max(n, 1))(*[_addr(w, blob_bytes(dtype, M, K) or None, f"ws[{i}]")
+                                            for i, (w, M) in enumerate(zip(ws, Ms))])
+    rows = (ctypes.c_int64 * max(n, 1))(*[int(M) for M in Ms])
+    outs = (ctypes.c_void_p * max(n, 1))(*[_addr(y, 4 * M, f"ys[{i}]", torch.float32)
+                                           for i, (y, M) in enumerate(zip(ys, Ms))])
+    rc = lib().qmm_gemv_concat_q8act(n, blobs, rows, dtype, K, _addr(x, 4 * K, "x", torch.float32), outs,
+                                     _stream(stream))
+    if rc != QMM_OK:
+        raise QmmError(rc, "qmm_gemv_concat_q8act")
+
+
+def qmm_gemv_swiglu_q8act(gate, up, dtype: int, M: int, K: int, x, out, stream=None) -> None:
+    import torch
+    nb = blob_bytes(dtype, M, K) or None
+    rc = lib().qmm_gemv_swiglu_q8act(_addr(gate, nb, "gate"), _addr(up, nb, "up"), dtype, M, K,
+                                     _addr(x, 4 * K, "x", torch.float32), _addr(out, 4 * M, "out", torch.float32),
+                                     _stream(stream))
+    if rc != QMM_OK:
+        raise QmmError(rc, "qmm_gemv_swiglu_q8act")

@@ -240,6 +240,58 @@ int qmm_gemm_q8act(const void *w_blob, int dtype, int64_t M, int64_t K, int64_t 
     return e == hipSuccess ? QMM_OK : QMM_ERR_LAUNCH;
 }
 
+int qmm_gemv_q8act(const void *w_blob, int dtype, int64_t M, int64_t K, const float *x, float *y, void *stream) {
+    int rc = check_shape(dtype, M, K, 1);
+    if (rc != QMM_OK) return rc;
+    if (!qmm::gemv_fused_ok(dtype, K)) return QMM_ERR_SHAPE;
+    if (!w_blob || !x || !y) return QMM_ERR_NULL;
+    if (!aligned(w_blob, 16) || !aligned(x, 16) || !aligned(y, 4)) return QMM_ERR_ALIGN;
+    int cus = 0;
+    rc = current_device(&cus);
+    if (rc != QMM_OK) return rc;
+    const void *blobs[1] = {w_blob};
+    const int64_t Ms[1] = {M};
+    float *ys[1] = {y};
+    const hipError_t e = qmm::launch_gemv_q8in(0, 1, blobs, Ms, dtype, K, x, ys, (hipStream_t)stream, cus);
+    return e == hipSuccess ? QMM_OK : QMM_ERR_LAUNCH;
+}
+
+int qmm_gemv_concat_q8act(int n, const void *const *w_blobs, const int64_t *Ms, int dtype, int64_t K,
+                          const float *x, float *const *ys, void *stream) {
+    if (n < 1 || n > QMM_GEMV_MAX_MATS) return QMM_ERR_SHAPE;
+    if (!w_blobs || !Ms || !ys || !x) return QMM_ERR_NULL;
+    for (int i = 0; i < n; i++) {
+        const int rc = check_shape(dtype, Ms[i], K, 1);
+        if (rc != QMM_OK) return rc;
+        if (!w_blobs[i] || !ys[i]) return QMM_ERR_NULL;
+        if (!aligned(w_blobs[i], 16) || !aligned(ys[i], 4)) return QMM_ERR_ALIGN;
+    }
+    if (!qmm::gemv_fused_ok(dtype, K)) return QMM_ERR_SHAPE;
+    if (!aligned(x, 16)) return QMM_ERR_ALIGN;
+    int cus = 0;
+    const int rc = current_device(&cus);
+    if (rc != QMM_OK) return rc;
+    const hipError_t e = qmm::launch_gemv_q8in(1, n, w_blobs, Ms, dtype, K, x, ys, (hipStream_t)stream, cus);
+    return e == hipSuccess ? QMM_OK : QMM_ERR_LAUNCH;
+}
+
+int qmm_gemv_swiglu_q8act(const void *gate_blob, const void *up_blob, int dtype, int64_t M, int64_t K,
+                          const float *x, float *out, void *stream) {
+    int rc = check_shape(dtype, M, K, 1);
+    if (rc != QMM_OK) return rc;
+    if (!qmm::gemv_fused_ok(dtype, K)) return QMM_ERR_SHAPE;
+    if (!gate_blob || !up_blob || !x || !out) return QMM_ERR_NULL;
+    if (!aligned(gate_blob, 16) || !aligned(up_blob, 16) || !aligned(x, 16) || !aligned(out, 4)) return QMM_ERR_ALIGN;
+    int cus = 0;
+    rc = current_device(&cus);
+    if (rc != QMM_OK) return rc;
+    const void *blobs[2] = {gate_blob, up_blob};
+    const int64_t Ms[2] = {M, M};
+    float *ys[2] = {out, out};
+    const hipError_t e = qmm::launch_gemv_q8in(2, 2, blobs, Ms, dtype, K, x, ys, (hipStream_t)stream, cus);
+    return e == hipSuccess ? QMM_OK : QMM_ERR_LAUNCH;
+}
+
 int qmm_gemm(const void *w_blob, int dtype, int64_t M, int64_t K, int64_t N, const float *X, float *Y,
              void *stream) {
     int rc = check_shape(dtype, M, K, N);

@@ -366,6 +366,38 @@ struct XA {
     int o[4];        // per-block integer offsets (see prep)
 };
 
+// Q8_0 quantization of four activations of a block whose other 28 sit in the
+// seven neighbouring lanes (lanes 8j .. 8j+7 hold one block): the block's
+// amax by three xor shuffles (a NaN never wins the comparison), d = amax/127,
+// id = 1/d unless d is 0 or 1/d is not finite, codes = rint(v * id) clamped to
+// [-128, 127] (NaN -> 0), packed little-endian; *d_out = d (the caller stores
+// it rounded to f16).  Every lane of the wavefront must call it.
+__device__ __forceinline__ uint32_t q8_quant4(const floatx4 &v, float *d_out) {
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const float a = fabsf(v[i]);
+        amax = a > amax ? a : amax;
+    }
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) {
+        const float a = __shfl_xor(amax, o, 64);
+        amax = a > amax ? a : amax;
+    }
+    const float d = amax / 127.0f;
+    const float r = 1.0f / d;
+    const float id = (d != 0.0f && __builtin_isfinite(r)) ? r : 0.0f;
+    uint32_t packed = 0;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const float q = rintf(v[i] * id);
+        const int c = q != q ? 0 : (q < -128.0f ? -128 : (q > 127.0f ? 127 : (int)q));
+        packed |= ((uint32_t)c & 0xFFu) << (8 * i);
+    }
+    *d_out = d;
+    return packed;
+}
+
 __device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int acc) {
     return __builtin_amdgcn_sdot4((int)a, (int)b, acc, false);
 }
@@ -673,13 +705,15 @@ __device__ __forceinline__ int64_t lo_of(const GemvMats &m, int i) {
 // NT = 0: f32 activations x.  NT >= 1: Q8_0-quantized activations of NT
 // tokens per weight read (codes xq [ntok][K], scales xsc [ntok][K/32]; token
 // group blockIdx.y covers tokens NT*blockIdx.y ..; outputs y[tok][M]); GEMV_ONE
-// only.
+// only.  NT = -1: one token of f32 activations x, quantized to Q8_0 by the
+// workgroup itself (into LDS, the quantizer kernel's arithmetic, so the codes
+// are the ones qmm_quantize_q8_0 writes), then the int8 dots; every MODE.
 template <int DT, int R, int D, bool WAVE_ROWS, bool FLAT, int MODE, int NT>
 __global__ void __launch_bounds__(256) gemv_kernel(const GemvMats mats, int64_t row_bytes, int U,
                                                    const float *__restrict__ x, int64_t per_owner, int64_t extra,
                                                    const int8_t *__restrict__ xq, const float *__restrict__ xsc,
                                                    int64_t ntok) {
-    static_assert(NT == 0 || MODE == GEMV_ONE, "int8 activations: one matrix");
+    static_assert(NT <= 0 || MODE == GEMV_ONE, "several int8 tokens: one matrix");
     constexpr int NL = Unit<DT>::NL;
     constexpr int RR = MODE == GEMV_SWIGLU ? 2 * R : R;  // row dots per row group
     constexpr int TK = NT > 0 ? NT : 1;                  // tokens per row dot
@@ -740,9 +774,46 @@ __global__ void __launch_bounds__(256) gemv_kernel(const GemvMats mats, int64_t 
                 (MODE == GEMV_CONCAT ? pick(mats.y, mi) : mats.y[0])[row] = v;
         }
     };
-    float xv[NT > 0 ? 1 : 64];
+    float xv[NT != 0 ? 1 : 64];
     XA xa[TK];
-    if constexpr (NT > 0) {
+    if constexpr (NT < 0) {
+        // x f32 -> Q8_0 codes (dwords [0, 16U)) and scales (floats after
+        // them) in LDS; eight consecutive threads share a block
+        constexpr int QPT = WAVE_ROWS ? 4 : 16;  // float4 of x per thread: 16 U <= QPT * blockDim
+        const int nf = 16 * U;
+        const floatx4 *xg = reinterpret_cast<const floatx4 *>(x);
+        floatx4 xr[QPT];
+#pragma unroll
+        for (int i = 0; i < QPT; i++) {
+            const int f = t + i * (int)blockDim.x;
+            xr[i] = xg[f < nf ? f : nf - 1];  // whole 8-lane groups are in or out of range
+        }
+#pragma unroll
+        for (int s = 0; s < (FLAT ? D + 1 : D); s++) fetch(g0 + s, buf[s]);
+        uint32_t *cs = reinterpret_cast<uint32_t *>(xs);
+        float *ss = reinterpret_cast<float *>(cs + nf);
+#pragma unroll
+        for (int i = 0; i < QPT; i++) {
+            const int f = t + i * (int)blockDim.x;
+            float d;
+            const uint32_t packed = q8_quant4(xr[i], &d);
+            if (f < nf) {
+                cs[f] = packed;
+                if ((f & 7) == 0) ss[f >> 3] = (float)(_Float16)d;
+            }
+        }
+        __syncthreads();
+        const int uu = active ? u : 0;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const u32x4_t v = *reinterpret_cast<const u32x4_t *>(cs + Unit<DT>::x4(uu, 4 * j));
+            xa[0].c[4 * j] = v.x; xa[0].c[4 * j + 1] = v.y; xa[0].c[4 * j + 2] = v.z; xa[0].c[4 * j + 3] = v.w;
+        }
+        const int si = U8<DT>::s_index(uu);
+#pragma unroll
+        for (int j = 0; j < 4; j++) xa[0].s[j] = j < U8<DT>::NS ? ss[si + j] : 0.f;
+        U8<DT>::prep(xa[0]);
+    } else if constexpr (NT > 0) {
         // every lane fetches its own unit's codes (64 bytes per token) before
         // the weights; tokens past the end repeat the last one (not stored)
         const int64_t K = 64 * (int64_t)U;
@@ -777,7 +848,7 @@ __global__ void __launch_bounds__(256) gemv_kernel(const GemvMats mats, int64_t 
 #pragma unroll
                     for (int tn = 0; tn < TK; tn++) {
                         float d;
-                        if constexpr (NT > 0) d = U8<DT>::dot(buf[s][r], xa[tn], off);
+                        if constexpr (NT != 0) d = U8<DT>::dot(buf[s][r], xa[tn], off);
                         else d = Unit<DT>::dot(buf[s][r], xv, off);
                         acc[r * TK + tn] = wave_sum_to_lane63(active ? d : 0.f);
                     }
@@ -1228,7 +1299,9 @@ static hipError_t launch_fast(const GemvMats &mats, int64_t K, const float *x, h
     const int64_t row_bytes = (K / BS) * BB;
     const int U = (int)(K / 64);
     const int64_t nrg = mats.g_lo[GEMV_MAX_MATS];
-    const size_t lds = NT > 0 ? 0 : (size_t)U * 256;  // the f32 activations
+    // the f32 activations; none for pre-quantized codes; codes + scales when
+    // the workgroup quantizes
+    const size_t lds = NT > 0 ? 0 : (NT < 0 ? (size_t)U * 72 : (size_t)U * 256);
     const unsigned gy = NT > 0 ? (unsigned)((xq8.ntok + NT - 1) / NT) : 1u;
     if (U <= 64) {
         const int64_t waves = gemv_wave_owners(DT, nrg, cus);
@@ -1248,7 +1321,7 @@ static hipError_t launch_fast(const GemvMats &mats, int64_t K, const float *x, h
         launch_variant<DT, R, D, false, MODE, NT>(per + (extra ? 1 : 0), dim3((unsigned)grid, gy), dim3(64 * W), lds,
                                                   st, mats, row_bytes, U, x, per, extra, xq8);
     } else {
-        if constexpr (MODE != GEMV_ONE || NT > 0) return hipErrorNotSupported;
+        if constexpr (MODE != GEMV_ONE || NT != 0) return hipErrorNotSupported;
         const int64_t M = mats.M[0];
         const int64_t grid = std::min<int64_t>(nrg, (int64_t)cus * 2);
         hipLaunchKernelGGL((gemv_multi_kernel<DT, R>), dim3((unsigned)grid), dim3(256), 0, st, mats.blob[0], M,
@@ -1279,7 +1352,7 @@ static hipError_t launch_generic(const uint8_t *blob, int64_t M, int64_t K, cons
 }
 
 // Several matrices (CONCAT) or a gate/up pair (SWIGLU) in one launch.
-template <int DT, int R, int D, int MODE>
+template <int DT, int R, int D, int MODE, int NT = 0>
 static hipError_t launch_mats(int n, const void *const *blobs, const int64_t *Ms, int64_t K, const float *x,
                               float *const *ys, hipStream_t st, int cus, float2 *part = nullptr,
                               int64_t *grid_out = nullptr) {
@@ -1296,7 +1369,7 @@ static hipError_t launch_mats(int n, const void *const *blobs, const int64_t *Ms
         }
     }
     m.g_lo[GEMV_MAX_MATS] = g;
-    return launch_fast<DT, R, D, MODE>(m, K, x, st, cus, grid_out);
+    return launch_fast<DT, R, D, MODE, NT>(m, K, x, st, cus, grid_out);
 }
 
 bool gemv_fused_ok(int dtype, int64_t K) {
@@ -1458,27 +1531,8 @@ __global__ void __launch_bounds__(256) quantize_q8_0_kernel(const floatx4 *__res
     const int64_t b = gt >> 3;
     const bool in = b < nblocks;
     const floatx4 v = in ? X[gt] : floatx4{0.f, 0.f, 0.f, 0.f};
-    float amax = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const float a = fabsf(v[i]);
-        amax = a > amax ? a : amax;
-    }
-#pragma unroll
-    for (int o = 1; o < 8; o <<= 1) {
-        const float a = __shfl_xor(amax, o, 64);
-        amax = a > amax ? a : amax;
-    }
-    const float d = amax / 127.0f;
-    const float r = 1.0f / d;
-    const float id = (d != 0.0f && __builtin_isfinite(r)) ? r : 0.0f;
-    uint32_t packed = 0;
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const float q = rintf(v[i] * id);
-        const int c = q != q ? 0 : (q < -128.0f ? -128 : (q > 127.0f ? 127 : (int)q));
-        packed |= ((uint32_t)c & 0xFFu) << (8 * i);
-    }
+    float d;
+    const uint32_t packed = q8_quant4(v, &d);
     if (in) {
         quants[gt] = packed;
         if ((gt & 7) == 0) scales[b] = (float)(_Float16)d;
@@ -1652,6 +1706,31 @@ static hipError_t launch_q8a_generic(const uint8_t *blob, int64_t M, int64_t K, 
     hipLaunchKernelGGL((gemv_q8_generic_kernel<DT, R>), dim3((unsigned)grid, (unsigned)N), dim3(256), 0, st, blob, M,
                        K, xq, xsc, Y);
     return hipGetLastError();
+}
+
+// One token of f32 activations, quantized inside the launch: MODE GEMV_ONE
+// (n = 1), GEMV_CONCAT (n <= 4 matrices of one K) or GEMV_SWIGLU (gate, up).
+// Rows per group and ring depth as the f32 GEMV's.  Needs gemv_fused_ok.
+hipError_t launch_gemv_q8in(int mode, int n, const void *const *blobs, const int64_t *Ms, int dtype, int64_t K,
+                            const float *x, float *const *ys, hipStream_t st, int cus) {
+    if (!gemv_fused_ok(dtype, K) || n < 1 || n > GEMV_MAX_MATS) return hipErrorInvalidValue;
+#define QMM_Q8IN(DT, R, D, RS, DS)                                                                            \
+    switch (mode) {                                                                                         \
+    case GEMV_ONE: return launch_mats<DT, R, D, GEMV_ONE, -1>(1, blobs, Ms, K, x, ys, st, cus);            \
+    case GEMV_CONCAT: return launch_mats<DT, R, D, GEMV_CONCAT, -1>(n, blobs, Ms, K, x, ys, st, cus);      \
+    case GEMV_SWIGLU: return launch_mats<DT, RS, DS, GEMV_SWIGLU, -1>(2, blobs, Ms, K, x, ys, st, cus);    \
+    default: return hipErrorInvalidValue;                                                                   \
+    }
+    switch (dtype) {
+    case QMM_Q4_0: QMM_Q8IN(QMM_Q4_0, 2, 3, 1, 3)
+    case QMM_Q4_1: QMM_Q8IN(QMM_Q4_1, 2, 3, 1, 3)
+    case QMM_Q8_0: QMM_Q8IN(QMM_Q8_0, 1, 4, 1, 2)
+    case QMM_Q4_K: QMM_Q8IN(QMM_Q4_K, 2, 3, 1, 3)
+    case QMM_Q5_K: QMM_Q8IN(QMM_Q5_K, 1, 3, 1, 2)
+    case QMM_Q6_K: QMM_Q8IN(QMM_Q6_K, 1, 4, 1, 2)
+    default: return hipErrorInvalidValue;
+    }
+#undef QMM_Q8IN
 }
 
 hipError_t launch_gemm_q8act(int dtype, const void *blob_v, int64_t M, int64_t K, int64_t N, const float *xsc,

@@ -52,4 +52,12 @@ hipError_t launch_quantize_q8_0(const float *X, int64_t N, int64_t K, float *sca
 hipError_t launch_gemm_q8act(int dtype, const void *blob, int64_t M, int64_t K, int64_t N, const float *xsc,
                              const int8_t *xq, float *Y, hipStream_t st, int cus);
 
+// One token of f32 activations quantized to Q8_0 inside the launch, then the
+// int8 dots (codes and results bit-identical to launch_quantize_q8_0 followed
+// by launch_gemm_q8act with N = 1).  mode 0: one matrix, 1: n <= 4 matrices
+// sharing K and x, 2: gate/up with SwiGLU (blobs = {gate, up}, one output).
+// Needs gemv_fused_ok(dtype, K).
+hipError_t launch_gemv_q8in(int mode, int n, const void *const *blobs, const int64_t *Ms, int dtype, int64_t K,
+                            const float *x, float *const *ys, hipStream_t st, int cus);
+
 }  // namespace qmm

@@ -232,6 +232,30 @@ int qmm_quantize_q8_0(const float *X, int64_t N, int64_t K, float *scales, int8_
 int qmm_gemm_q8act(const void *w_blob, int dtype, int64_t M, int64_t K, int64_t N,
                    const float *scales, const int8_t *quants, float *Y, void *stream);
 
+/* Decode with int8 activations in one launch (page "cera 0.5.2
+ * src/backend/cpu.rs": the decode GEMVs quantize the token's activations to
+ * Q8_0 once and run integer block dots against every projection).  Each
+ * workgroup quantizes x itself, with exactly the arithmetic of
+ * qmm_quantize_q8_0, so the results are bit-identical to qmm_quantize_q8_0
+ * followed by qmm_gemm_q8act with N = 1 (and so is the error bound).
+ *   qmm_gemv_q8act         y[M] = W xq
+ *   qmm_gemv_concat_q8act  ys[i] = W_i xq for n <= QMM_GEMV_MAX_MATS matrices
+ *                          sharing dtype and K, one launch
+ *   qmm_gemv_swiglu_q8act  out = silu(W_gate xq) * (W_up xq) (silu as
+ *                          qmm_gemv_swiglu), neither projection stored
+ *   x       device f32 [K], 16-B aligned (not modified)
+ *   y, ys[i], out  device f32, 4-B aligned; overwritten
+ * Shapes: K a multiple of 64 up to 16384 with an even block count per row
+ * for Q4_0, Q4_1, Q8_0 and Q6_K (the one-launch kernel); others return
+ * QMM_ERR_SHAPE (use qmm_quantize_q8_0 + qmm_gemm_q8act).  Other errors as
+ * qmm_gemv. */
+int qmm_gemv_q8act(const void *w_blob, int dtype, int64_t M, int64_t K, const float *x, float *y,
+                   void *stream);
+int qmm_gemv_concat_q8act(int n, const void *const *w_blobs, const int64_t *Ms, int dtype, int64_t K,
+                          const float *x, float *const *ys, void *stream);
+int qmm_gemv_swiglu_q8act(const void *gate_blob, const void *up_blob, int dtype, int64_t M, int64_t K,
+                          const float *x, float *out, void *stream);
+
 /* Which arithmetic qmm_gemm uses for these sizes: 0 = f32 (GEMV family),
  * 1 = f16 matrix-core GEMM, or a negative status for invalid arguments. */
 int qmm_gemm_path(int dtype, int64_t M, int64_t K, int64_t N);

@@ -264,3 +264,48 @@ def test_q8act_calls_without_gpu_report_device():
         pytest.skip("a GPU is present; covered by the GPU tests")
     assert q.lib().qmm_quantize_q8_0(A16, 2, 64, A16, A16, None) == q.QMM_ERR_DEVICE
     assert q.lib().qmm_gemm_q8act(A16, 14, 8, 256, 3, A16, A16, A16, None) == q.QMM_ERR_DEVICE
+
+
+@pytest.mark.parametrize("args,code", [
+    ((A16, 5, 8, 64, A16, A16), q.QMM_ERR_DTYPE),
+    ((A16, 2, 8, 96, A16, A16), q.QMM_ERR_SHAPE),      # odd Q4_0 block count: no one-launch kernel
+    ((A16, 12, 8, 16640, A16, A16), q.QMM_ERR_SHAPE),  # K > 16384
+    ((A16, 2, 0, 64, A16, A16), q.QMM_ERR_SHAPE),
+    ((0, 2, 8, 64, A16, A16), q.QMM_ERR_NULL),
+    ((A16, 2, 8, 64, 0, A16), q.QMM_ERR_NULL),
+    ((A16 + 2, 2, 8, 64, A16, A16), q.QMM_ERR_ALIGN),
+    ((A16, 2, 8, 64, A16 + 4, A16), q.QMM_ERR_ALIGN),
+    ((A16, 2, 8, 64, A16, A16 + 2), q.QMM_ERR_ALIGN),
+])
+def test_gemv_q8act_rejects(args, code):
+    assert q.lib().qmm_gemv_q8act(*args, None) == code
+    # the SwiGLU form takes the same checks with the blob given twice
+    a = (args[0], args[0]) + args[1:]
+    assert q.lib().qmm_gemv_swiglu_q8act(*a, None) == code
+
+
+def test_gemv_concat_q8act_rejects():
+    arr = lambda ct, v: (ct * len(v))(*v)
+    L = q.lib()
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    assert L.qmm_gemv_concat_q8act(0, arr(vp, [A16]), arr(i64, [8]), 2, 64, A16, arr(vp, [A16]), None) == q.QMM_ERR_SHAPE
+    assert L.qmm_gemv_concat_q8act(5, arr(vp, [A16] * 5), arr(i64, [8] * 5), 2, 64, A16, arr(vp, [A16] * 5),
+                                   None) == q.QMM_ERR_SHAPE
+    assert L.qmm_gemv_concat_q8act(2, arr(vp, [A16, 0]), arr(i64, [8, 8]), 2, 64, A16, arr(vp, [A16, A16]),
+                                   None) == q.QMM_ERR_NULL
+    assert L.qmm_gemv_concat_q8act(2, arr(vp, [A16, A16]), arr(i64, [8, 8]), 2, 96, A16, arr(vp, [A16, A16]),
+                                   None) == q.QMM_ERR_SHAPE
+    assert L.qmm_gemv_concat_q8act(1, arr(vp, [A16]), arr(i64, [8]), 2, 64, A16 + 4, arr(vp, [A16]),
+                                   None) == q.QMM_ERR_ALIGN
+
+
+def test_one_launch_q8act_without_gpu_reports_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; covered by the GPU tests")
+    arr = lambda ct, v: (ct * len(v))(*v)
+    L = q.lib()
+    assert L.qmm_gemv_q8act(A16, 14, 8, 4096, A16, A16, None) == q.QMM_ERR_DEVICE
+    assert L.qmm_gemv_swiglu_q8act(A16, A16, 2, 8, 4096, A16, A16, None) == q.QMM_ERR_DEVICE
+    assert L.qmm_gemv_concat_q8act(2, arr(ctypes.c_void_p, [A16, A16]), arr(ctypes.c_int64, [8, 9]), 2, 4096, A16,
+                                   arr(ctypes.c_void_p, [A16, A16]), None) == q.QMM_ERR_DEVICE

@@ -12,6 +12,11 @@
     K-split workgroups), N from 1 to 9; full-size workloads on sampled rows.
   * Bitwise: a token of an N-token call equals the single-token call; two
     runs give equal bits.
+  * The one-launch decode calls (qmm_gemv_q8act, qmm_gemv_concat_q8act,
+    qmm_gemv_swiglu_q8act), which quantize x inside the launch: bit-identical
+    to qmm_quantize_q8_0 + qmm_gemm_q8act (concat: to one call per matrix),
+    and against the oracle within 1e-5 of Splus; the SwiGLU form within the
+    SwiGLU bound carried from the int8 projections' bound.
 """
 import numpy as np
 import pytest
@@ -204,3 +209,126 @@ def test_quantize_then_matmul_on_device():
     sc, qq = oracle.quantize_q8_0(X)
     _, Y64, _, Sp = oracle.matmul_q8act(dt, blob, M, K, sc, qq)
     check(Y.cpu().numpy(), Y64, Sp, "quantize + q8act on device")
+
+
+# ------------------------------------- one-launch decode (quantize inside) ----
+
+def fused_shapes(dt):
+    # K <= 4096: whole-row wavefronts; beyond: K-split workgroups (max 16384)
+    if bs_of(dt) == 32:
+        return [(1, 64), (5, 128), (67, 1024), (300, 4096), (50, 4160), (33, 14336), (9, 16384)]
+    # Q6_K needs an even super-block count per row
+    return [(1, 512 if dt == q.QMM_Q6_K else 256), (3, 512), (67, 1024), (300, 4096), (50, 8192), (9, 16384)]
+
+
+def test_gemv_q8act_rejects_odd_q6_k_blocks():
+    blob_d = to_dev(make_blob(q.QMM_Q6_K, 4, 768, rng_for(965, 0)))
+    x_d = to_dev(make_x(1, 768, rng_for(965, 1)).reshape(-1))
+    with pytest.raises(q.QmmError) as e:
+        one_launch(q.QMM_Q6_K, blob_d, 4, 768, x_d)
+    assert e.value.code == q.QMM_ERR_SHAPE
+
+
+def two_step(dt, blob_d, M, K, x_d):
+    sc = torch.empty((1, K // 32), device="cuda")
+    qq = torch.empty((1, K), dtype=torch.int8, device="cuda")
+    y = torch.full((1, M), float("nan"), device="cuda")
+    q.qmm_quantize_q8_0(x_d, 1, K, sc, qq)
+    q.qmm_gemm_q8act(blob_d, dt, M, K, 1, sc, qq, y)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()[0]
+
+
+def one_launch(dt, blob_d, M, K, x_d):
+    y = torch.full((M,), float("nan"), device="cuda")
+    q.qmm_gemv_q8act(blob_d, dt, M, K, x_d, y)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+@pytest.mark.parametrize("dt", DTYPES, ids=NAME.get)
+def test_gemv_q8act_is_quantize_then_q8act(dt):
+    for i, (M, K) in enumerate(fused_shapes(dt)):
+        blob = make_blob(dt, M, K, rng_for(960 + dt, i))
+        x = make_x(1, K, rng_for(960 + dt, 100 + i))
+        x[0, :7] *= np.float32(50.0)  # a block with a larger maximum
+        blob_d, x_d = to_dev(blob), to_dev(x.reshape(-1))
+        y = one_launch(dt, blob_d, M, K, x_d)
+        assert same_bits(y, two_step(dt, blob_d, M, K, x_d)), f"{NAME[dt]} M={M} K={K}: not the two-step bits"
+        sc, qq = oracle.quantize_q8_0(x)
+        _, Y64, _, Sp = oracle.matmul_q8act(dt, blob, M, K, sc, qq)
+        check(y[None, :], Y64, Sp, f"{NAME[dt]} gemv_q8act M={M} K={K}")
+
+
+@pytest.mark.parametrize("dt", DTYPES, ids=NAME.get)
+def test_gemv_concat_q8act(dt):
+    K = 4 * bs_of(dt) * (4 if bs_of(dt) == 32 else 1)
+    for K in (K, 8192):
+        Ms = [300, 77, 1]
+        blobs = [to_dev(make_blob(dt, M, K, rng_for(970 + dt, j))) for j, M in enumerate(Ms)]
+        x_d = to_dev(make_x(1, K, rng_for(970 + dt, 9)).reshape(-1))
+        ys = [torch.full((M,), float("nan"), device="cuda") for M in Ms]
+        q.qmm_gemv_concat_q8act(blobs, dt, Ms, K, x_d, ys)
+        torch.cuda.synchronize()
+        for j, (b, M, y) in enumerate(zip(blobs, Ms, ys)):
+            assert same_bits(y.cpu().numpy(), one_launch(dt, b, M, K, x_d)), f"{NAME[dt]} K={K}: matrix {j}"
+
+
+def check_swiglu_q8(out, g64, u64, sg, su, g_gpu, u_gpu, label):
+    out = out.astype(np.float64)
+    silu = np.vectorize(oracle.silu)
+    exact = silu(g64) * u64
+    with np.errstate(over="ignore"):
+        silu_g = g64 / (1.0 + np.exp(-g64))
+    bound = TAU * (1.1 * sg * (np.abs(u64) + TAU * su) + np.abs(silu_g) * su) + 4 * 2.0 ** -24 * np.abs(exact)
+    assert np.all(np.isfinite(out)), f"{label}: non-finite output"
+    zero = (sg == 0) | (su == 0)
+    assert np.all(out[zero] == 0), f"{label}: a zero projection must give exactly 0"
+    bad = np.abs(out - exact) > bound
+    assert not bad.any(), f"{label}: {int(bad.sum())} outputs outside the bound"
+    g2, u2 = g_gpu.astype(np.float64), u_gpu.astype(np.float64)
+    with np.errstate(over="ignore"):
+        mine = g2 / (1.0 + np.exp(-g2)) * u2
+    lim = 4 * 2.0 ** -24 * np.abs(mine) + 2.0 ** -119 * np.abs(u2)
+    assert np.all(np.abs(out - mine) <= lim), f"{label}: not silu(g) * u of the int8 projections"
+
+
+@pytest.mark.parametrize("dt", DTYPES, ids=NAME.get)
+def test_gemv_swiglu_q8act(dt):
+    for i, (M, K) in enumerate([(300, 1024 if bs_of(dt) == 32 else 2048), (67, 8192)]):
+        gate = make_blob(dt, M, K, rng_for(980 + dt, i))
+        up = make_blob(dt, M, K, rng_for(980 + dt, 10 + i))
+        x = make_x(1, K, rng_for(980 + dt, 20 + i)) * np.float32(2.0)
+        g_d, u_d, x_d = to_dev(gate), to_dev(up), to_dev(x.reshape(-1))
+        out = torch.full((M,), float("nan"), device="cuda")
+        q.qmm_gemv_swiglu_q8act(g_d, u_d, dt, M, K, x_d, out)
+        torch.cuda.synchronize()
+        sc, qq = oracle.quantize_q8_0(x)
+        _, G64, _, SG = oracle.matmul_q8act(dt, gate, M, K, sc, qq)
+        _, U64, _, SU = oracle.matmul_q8act(dt, up, M, K, sc, qq)
+        check_swiglu_q8(out.cpu().numpy(), G64[0], U64[0], SG[0], SU[0], one_launch(dt, g_d, M, K, x_d),
+                        one_launch(dt, u_d, M, K, x_d), f"{NAME[dt]} swiglu_q8act M={M} K={K}")
+
+
+def test_one_launch_decode_layer_full_size():
+    # the llama8b Q4_0 decode layer as the bench runs it, and the Q6_K head
+    for wid, sub in ((2, None), (3, None), (4, None), (5, None)):
+        label, dt, M, K, _ = WORKLOADS[wid]
+        blob = make_blob(dt, M, K, rng_for(wid, 0))
+        x = make_x(1, K, rng_for(wid, 1001))
+        blob_d, x_d = to_dev(blob), to_dev(x.reshape(-1))
+        y = one_launch(dt, blob_d, M, K, x_d)
+        assert same_bits(y, two_step(dt, blob_d, M, K, x_d)), f"{label}: not the two-step bits"
+        sc, qq = oracle.quantize_q8_0(x)
+        rows = sample_rows(M, 64, wid)
+        _, Y64, _, Sp = oracle.matmul_q8act(dt, blob, M, K, sc, qq, rows=rows)
+        check(y[None, rows], Y64, Sp, f"{label} gemv_q8act")
+    # gate + up in one launch
+    _, dt, M, K, _ = WORKLOADS[3]
+    blobs = [to_dev(make_blob(dt, M, K, rng_for(3, j))) for j in range(2)]
+    x_d = to_dev(make_x(1, K, rng_for(3, 1001)).reshape(-1))
+    ys = [torch.empty(M, device="cuda") for _ in range(2)]
+    q.qmm_gemv_concat_q8act(blobs, dt, [M, M], K, x_d, ys)
+    torch.cuda.synchronize()
+    for b, y in zip(blobs, ys):
+        assert same_bits(y.cpu().numpy(), one_launch(dt, b, M, K, x_d)), "gate+up concat q8act"
