@@ -14,7 +14,8 @@ with N = 1, i.e. path selection -> the f32 GEMV) is reported as
 "decode_unfused", with gate/up through qmm_gemv_swiglu as "decode_swiglu",
 and with int8 activations (the same three launches through qmm_gemv_q8act /
 qmm_gemv_concat_q8act, which quantize x to Q8_0 inside the launch) as
-"decode_q8act".  Weight copies are rotated so
+"decode_q8act".  The Q6_K LM head (128256 x 4096) is timed alone, f32 and
+int8, under "lm_head".  Weight copies are rotated so
 that more than 1 GiB of distinct weights is cycled (more than the 256 MB
 last-level cache): every step streams its weights from HBM.  Inputs are
 resident in HBM before timing starts.
@@ -217,6 +218,28 @@ def main():
             lambda c: q.qmm_gemv_swiglu_q8act(copies[1][c], copies[2][c], dg, Mg, Kg, xs[1], swiglu_y,
                                               stream=stream), gu_bytes)
 
+    # the 128256 x 4096 Q6_K LM head (the largest decode GEMV): f32 and
+    # int8 activations (quantized inside the launch)
+    lm_head = None
+    if not args.headline_only:
+        _, hdt, HM, HK, _ = WORKLOADS[5]
+        hblob = torch.from_numpy(make_blob(hdt, HM, HK, rng_for(5, 0))).to(dev)
+        HR = max(2, -(-ROTATE_BYTES // hblob.numel()))
+        hcopies = [hblob] + [hblob.clone() for _ in range(HR - 1)]
+        hx = torch.from_numpy(make_x(1, HK, rng_for(5, 1001))).to(dev).reshape(-1)
+        hy = torch.empty(HM, device=dev)
+        for s in range(args.warmup):
+            q.qmm_gemv(hcopies[s % HR], hdt, HM, HK, hx, hy, stream=stream)
+        lm_head = {"workload": "Q6_K 128256x4096, N=1, x f32 ~ N(0,1)", "weight_bytes": hblob.numel(),
+                   "rotation_copies": HR}
+        for key, fn in (("f32", lambda c: q.qmm_gemv(hcopies[c % HR], hdt, HM, HK, hx, hy, stream=stream)),
+                        ("q8act", lambda c: q.qmm_gemv_q8act(hcopies[c % HR], hdt, HM, HK, hx, hy, stream=stream))):
+            r = time_calls(fn, hblob.numel())
+            r["hbm_frac"] = round(r["GB/s"] / HBM_PEAK_GBS, 4)
+            lm_head[key] = r
+        del hcopies, hblob
+        torch.cuda.empty_cache()
+
     def layer_rate(span):
         if span is None:
             return None
@@ -275,6 +298,7 @@ def main():
                                      "different numbers from the f32 path"},
             "timing": "HIP events on the launch stream at step boundaries; per-launch = span / launches",
             "per_matrix": per_matrix,
+            "lm_head": lm_head,
             "gpu": props.name,
             "cus": props.multi_processor_count,
         },
