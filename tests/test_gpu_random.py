@@ -6,7 +6,8 @@ where the paths switch), and random matrix counts for the fused calls.  The
 bar is the same as the fixed-shape tests: 1e-5 * S on the f32 paths, 2e-3 * S
 on the matrix-core path (whichever qmm_gemm_path reports), the GEMV's bits for
 qmm_gemv_concat and for qmm_gemm below the crossover, and a valid maximum for
-qmm_gemv_argmax.
+qmm_gemv_argmax; for the int8-activation calls the oracle's quantizer bits and
+1e-5 * Splus.
 """
 import numpy as np
 import pytest
@@ -120,3 +121,40 @@ def test_random_fused(dt):
                 q.qmm_gemv_argmax(bds[0], dt, M0, K, xd, torch.empty(q.QMM_ARGMAX_WORK_BYTES, dtype=torch.uint8,
                                                                      device="cuda"),
                                   torch.empty(1, dtype=torch.int64, device="cuda"))
+
+
+@pytest.mark.parametrize("dt", DTYPES, ids=NAME.get)
+def test_random_q8act(dt):
+    """Random shapes through the int8-activation entry points: the quantizer
+    bit-exact with the oracle's, qmm_gemm_q8act within 1e-5 of Splus, and the
+    one-launch calls bit-identical to quantize + qmm_gemm_q8act where they take
+    the shape (QMM_ERR_SHAPE otherwise)."""
+    rng = np.random.default_rng(4800 + dt)
+    for case in range(8):
+        M, K, N = random_shape(rng, dt)
+        N = min(N, 40)
+        blob = make_blob(dt, M, K, rng_for(4900 + dt, case))
+        X = make_x(N, K, rng_for(5000 + dt, case))
+        bd, Xd = dev(blob), dev(X)
+        sc = torch.empty((N, K // 32), device="cuda")
+        qq = torch.empty((N, K), dtype=torch.int8, device="cuda")
+        Y = torch.full((N, M), float("nan"), device="cuda")
+        q.qmm_quantize_q8_0(Xd, N, K, sc, qq)
+        q.qmm_gemm_q8act(bd, dt, M, K, N, sc, qq, Y)
+        torch.cuda.synchronize()
+        label = f"{NAME[dt]} q8act case {case} M={M} K={K} N={N}"
+        so, qo = oracle.quantize_q8_0(X)
+        assert np.array_equal(sc.cpu().numpy().view(np.uint32), so.view(np.uint32)), f"{label}: scales"
+        assert np.array_equal(qq.cpu().numpy(), qo), f"{label}: codes"
+        _, Y64, _, Sp = oracle.matmul_q8act(dt, blob, M, K, so, qo)
+        Yg = Y.cpu().numpy()
+        within(Yg, Y64, Sp, 1e-5, label)
+        y = torch.full((M,), float("nan"), device="cuda")
+        if fused_ok(dt, K):
+            q.qmm_gemv_q8act(bd, dt, M, K, Xd[0], y)
+            torch.cuda.synchronize()
+            assert np.array_equal(y.cpu().numpy().view(np.uint32), Yg[0].view(np.uint32)), \
+                f"{label}: one-launch call differs from quantize + q8act"
+        else:
+            with pytest.raises(q.QmmError):
+                q.qmm_gemv_q8act(bd, dt, M, K, Xd[0], y)
