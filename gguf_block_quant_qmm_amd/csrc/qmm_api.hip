@@ -49,8 +49,11 @@ int check_shape(int dtype, int64_t M, int64_t K, int64_t N) {
     const int bs = block_elems(dtype);
     if (bs == 0) return QMM_ERR_DTYPE;
     if (M < 1 || N < 1 || K < bs || K % bs != 0) return QMM_ERR_SHAPE;
-    // keep every byte offset and grid size inside 63 bits / the launch limits
-    if (M > (int64_t(1) << 40) || K > (int64_t(1) << 40) || N > (int64_t(1) << 40)) return QMM_ERR_SHAPE;
+    // keep every byte offset and grid size inside 63 bits / the launch limits:
+    // each size and each product of two of them
+    constexpr int64_t kMax = int64_t(1) << 40, kMaxProd = int64_t(1) << 56;
+    if (M > kMax || K > kMax || N > kMax) return QMM_ERR_SHAPE;
+    if (M > kMaxProd / K || N > kMaxProd / K || N > kMaxProd / M) return QMM_ERR_SHAPE;
     return QMM_OK;
 }
 
@@ -217,7 +220,9 @@ int qmm_gemm_swiglu(const void *gate_blob, const void *up_blob, int dtype, int64
 }
 
 int qmm_quantize_q8_0(const float *X, int64_t N, int64_t K, float *scales, int8_t *quants, void *stream) {
-    if (N < 1 || K < 32 || K % 32 != 0 || N > (int64_t(1) << 40) || K > (int64_t(1) << 40)) return QMM_ERR_SHAPE;
+    if (N < 1 || K < 32 || K % 32 != 0 || N > (int64_t(1) << 40) || K > (int64_t(1) << 40) ||
+        N > (int64_t(1) << 56) / K)
+        return QMM_ERR_SHAPE;
     if (!X || !scales || !quants) return QMM_ERR_NULL;
     if (!aligned(X, 16) || !aligned(scales, 16) || !aligned(quants, 16)) return QMM_ERR_ALIGN;
     int cus = 0;

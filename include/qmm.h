@@ -77,7 +77,8 @@ extern "C" {
 #define QMM_OK 0
 #define QMM_ERR_NULL (-1)    /* a required pointer is NULL                          */
 #define QMM_ERR_DTYPE (-2)   /* dtype is not one of the six tags above              */
-#define QMM_ERR_SHAPE (-3)   /* M < 1, N < 1, K < block_elems or K % block_elems    */
+#define QMM_ERR_SHAPE (-3)   /* M < 1, N < 1, K < block_elems or K % block_elems,
+                                a size above 2^40 or a product of two above 2^56   */
 #define QMM_ERR_ALIGN (-4)   /* blob not 16-B aligned, x/X not 16-B, y/Y not 4-B    */
 #define QMM_ERR_DEVICE (-5)  /* no current HIP device, or it is not gfx950          */
 #define QMM_ERR_LAUNCH (-6)  /* the kernel launch itself failed                     */

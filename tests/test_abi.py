@@ -309,3 +309,14 @@ def test_one_launch_q8act_without_gpu_reports_device():
     assert L.qmm_gemv_swiglu_q8act(A16, A16, 2, 8, 4096, A16, A16, None) == q.QMM_ERR_DEVICE
     assert L.qmm_gemv_concat_q8act(2, arr(ctypes.c_void_p, [A16, A16]), arr(ctypes.c_int64, [8, 9]), 2, 4096, A16,
                                    arr(ctypes.c_void_p, [A16, A16]), None) == q.QMM_ERR_DEVICE
+
+
+def test_oversized_products_are_rejected():
+    # each size within 2^40, but a product of two beyond 2^56: no launch, no wrap-around
+    big = 1 << 39
+    assert q.lib().qmm_gemm(A16, 2, big, big, 1, A16, A16, None) == q.QMM_ERR_SHAPE
+    assert q.lib().qmm_gemm(A16, 2, 8, big, big, A16, A16, None) == q.QMM_ERR_SHAPE
+    assert q.lib().qmm_gemm(A16, 2, big, 64, big, A16, A16, None) == q.QMM_ERR_SHAPE
+    assert q.lib().qmm_gemm_q8act(A16, 2, 8, big, big, A16, A16, A16, None) == q.QMM_ERR_SHAPE
+    assert q.lib().qmm_quantize_q8_0(A16, big, big, A16, A16, None) == q.QMM_ERR_SHAPE
+    assert q.blob_bytes(q.QMM_Q4_0, big, big) == 0
