@@ -26,9 +26,9 @@ After the decode loop the same number of steps of the Q4_K prefill GEMM
 sample of the same workloads ("cpu_baseline").
 
 Kernel durations come from HIP events recorded on the stream the kernels run
-on (torch's current stream) at the boundaries of the timed regions; a
-region's launches run back to back, and the per-launch figure is the region
-time over its launch count.
+on (torch's current stream) before and after each timed region, with nothing
+in between; a region's launches run back to back, and the per-launch figure
+is the region time over its launch count.
 
 Extra: ``--sweep`` prints one JSON line per (workload, N) for every
 configuration of the workload table (C1-C5) instead of the main line.
@@ -156,18 +156,20 @@ def main():
         q.qmm_gemv_q8act(copies[3][c], dd, Md, Kd, xs[3], ys[3], stream=stream)
 
     def time_layer(step):
-        """(span ms over args.steps steps, host seconds), events only at step boundaries."""
+        """(span ms over args.steps steps, host seconds): one event before the
+        first step and one after the last (an event between kernels puts a
+        timestamp packet between them, which the decode loop does not have)."""
         for s in range(args.warmup):
             step(s % R)
         torch.cuda.synchronize()
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
-        ev[0].record(stream)
+        a.record(stream)
         for s in range(args.steps):
             step((args.warmup + s) % R)
-            ev[s + 1].record(stream)
+        b.record(stream)
         torch.cuda.synchronize()
-        return ev[0].elapsed_time(ev[args.steps]), time.perf_counter() - t0
+        return a.elapsed_time(b), time.perf_counter() - t0
 
     span_ms, wall_dec = time_layer(step_fused)
     span_unf = span_swi = span_q8 = None
@@ -296,7 +298,7 @@ def main():
                              "note": "int8 activations: qmm_gemv_q8act (q_proj, down) and qmm_gemv_concat_q8act "
                                      "(gate+up), each quantizing x to Q8_0 inside the launch; integer block dots, "
                                      "different numbers from the f32 path"},
-            "timing": "HIP events on the launch stream at step boundaries; per-launch = span / launches",
+            "timing": "HIP events on the launch stream before the first and after the last timed step; per-launch = span / launches",
             "per_matrix": per_matrix,
             "lm_head": lm_head,
             "gpu": props.name,
