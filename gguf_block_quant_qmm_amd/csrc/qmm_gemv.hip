@@ -497,8 +497,11 @@ __device__ __forceinline__ float kquant_pair(float d, float dmin, uint32_t s0w, 
     int sc0, m0, sc1, m1;
     q4k_scale_min(s0w, s1w, s2w, 2 * c, sc0, m0);
     q4k_scale_min(s0w, s1w, s2w, 2 * c + 1, sc1, m1);
-    const float t0 = fmaf(d * a.s[0], (float)(sc0 * acc0), -((dmin * a.s[0]) * (float)(m0 * a.o[0])));
-    const float t1 = fmaf(d * a.s[1], (float)(sc1 * acc1), -((dmin * a.s[1]) * (float)(m1 * a.o[1])));
+    // sc * acc (< 2^22) and m * sum (< 2^19) are exact as f32 products of
+    // their exact f32 factors: the same values as the integer products, without
+    // the quarter-rate integer multiply
+    const float t0 = fmaf(d * a.s[0], (float)sc0 * (float)acc0, -((dmin * a.s[0]) * ((float)m0 * (float)a.o[0])));
+    const float t1 = fmaf(d * a.s[1], (float)sc1 * (float)acc1, -((dmin * a.s[1]) * ((float)m1 * (float)a.o[1])));
     return t0 + t1;
 }
 
@@ -565,7 +568,8 @@ template <> struct U8<QMM_Q6_K> {
             }
             const uint32_t scw = (g < 2) ? v[12] : v[13];
             const int sbyte = (int)__builtin_amdgcn_sbfe((int)scw, 16 * (g & 1) + 8 * o.lh, 8);  // sc[8h + 2g + lh]
-            total = fmaf(d * a.s[g], (float)(sbyte * acc), total);
+            // |sc * acc| < 2^22: the f32 product of the exact factors is exact
+            total = fmaf(d * a.s[g], (float)sbyte * (float)acc, total);
         }
         return total;
     }
@@ -1247,10 +1251,14 @@ static int gemv_waves_lever() {
     }();
     return v;
 }
-static int64_t gemv_wave_owners(int dtype, int64_t nrg, int cus) {
+static int64_t gemv_wave_owners(int dtype, int64_t nrg, int cus, bool q8_in_launch = false) {
     const int lever = gemv_waves_lever();
     if (lever) return std::min<int64_t>(nrg, (int64_t)cus * lever);
     if (nrg <= (int64_t)cus * 64) return nrg;
+    // Q6_K with x quantized in the launch (the 128256-row head): 4 per CU with
+    // a ring of 2, 76.5-77.2 us against 78.7-78.9 at 8 per CU with a ring of 4
+    // (pre-quantized codes keep 8 per CU and a ring of 4: 81-82 against 86-88)
+    if (q8_in_launch && dtype == QMM_Q6_K) return (int64_t)cus * 4;
     return (int64_t)cus * ((dtype == QMM_Q4_0 || dtype == QMM_Q8_0) ? 16 : 8);
 }
 
@@ -1304,7 +1312,7 @@ static hipError_t launch_fast(const GemvMats &mats, int64_t K, const float *x, h
     const size_t lds = NT > 0 ? 0 : (NT < 0 ? (size_t)U * 72 : (size_t)U * 256);
     const unsigned gy = NT > 0 ? (unsigned)((xq8.ntok + NT - 1) / NT) : 1u;
     if (U <= 64) {
-        const int64_t waves = gemv_wave_owners(DT, nrg, cus);
+        const int64_t waves = gemv_wave_owners(DT, nrg, cus, NT < 0);
         const int64_t grid = (waves + 3) / 4, owners = grid * 4;
         const int64_t per = nrg / owners, extra = nrg % owners;
         if (MODE == GEMV_ARGMAX && grid > ARGMAX_PARTS) return hipErrorInvalidConfiguration;
@@ -1727,7 +1735,7 @@ hipError_t launch_gemv_q8in(int mode, int n, const void *const *blobs, const int
     case QMM_Q8_0: QMM_Q8IN(QMM_Q8_0, 1, 4, 1, 2)
     case QMM_Q4_K: QMM_Q8IN(QMM_Q4_K, 2, 3, 1, 3)
     case QMM_Q5_K: QMM_Q8IN(QMM_Q5_K, 1, 3, 1, 2)
-    case QMM_Q6_K: QMM_Q8IN(QMM_Q6_K, 1, 4, 1, 2)
+    case QMM_Q6_K: QMM_Q8IN(QMM_Q6_K, 1, 2, 1, 2)
     default: return hipErrorInvalidValue;
     }
 #undef QMM_Q8IN
