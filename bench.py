@@ -14,8 +14,9 @@ with N = 1, i.e. path selection -> the f32 GEMV) is reported as
 "decode_unfused", with gate/up through qmm_gemv_swiglu as "decode_swiglu",
 and with int8 activations (the same three launches through qmm_gemv_q8act /
 qmm_gemv_concat_q8act, which quantize x to Q8_0 inside the launch) as
-"decode_q8act".  The Q6_K LM head (128256 x 4096) is timed alone, f32 and
-int8, under "lm_head".  Weight copies are rotated so
+"decode_q8act".  The Q6_K LM head (128256 x 4096) is timed alone under
+"lm_head": its GEMV and its greedy argmax, each with f32 and with int8
+activations.  Weight copies are rotated so
 that more than 1 GiB of distinct weights is cycled (more than the 256 MB
 last-level cache): every step streams its weights from HBM.  Inputs are
 resident in HBM before timing starts.
@@ -234,8 +235,14 @@ def main():
             q.qmm_gemv(hcopies[s % HR], hdt, HM, HK, hx, hy, stream=stream)
         lm_head = {"workload": "Q6_K 128256x4096, N=1, x f32 ~ N(0,1)", "weight_bytes": hblob.numel(),
                    "rotation_copies": HR}
+        hwork = torch.empty(q.QMM_ARGMAX_WORK_BYTES, dtype=torch.uint8, device=dev)
+        hidx = torch.empty(1, dtype=torch.int64, device=dev)
         for key, fn in (("f32", lambda c: q.qmm_gemv(hcopies[c % HR], hdt, HM, HK, hx, hy, stream=stream)),
-                        ("q8act", lambda c: q.qmm_gemv_q8act(hcopies[c % HR], hdt, HM, HK, hx, hy, stream=stream))):
+                        ("q8act", lambda c: q.qmm_gemv_q8act(hcopies[c % HR], hdt, HM, HK, hx, hy, stream=stream)),
+                        ("argmax_f32", lambda c: q.qmm_gemv_argmax(hcopies[c % HR], hdt, HM, HK, hx, hwork, hidx,
+                                                                   stream=stream)),
+                        ("argmax_q8act", lambda c: q.qmm_gemv_argmax_q8act(hcopies[c % HR], hdt, HM, HK, hx, hwork,
+                                                                           hidx, stream=stream))):
             r = time_calls(fn, hblob.numel())
             r["hbm_frac"] = round(r["GB/s"] / HBM_PEAK_GBS, 4)
             lm_head[key] = r

@@ -20,8 +20,8 @@ there is no CPU fallback.
                                                      X -> Q8_0 activation blocks
     qmm_gemm_q8act(w, dtype, M, K, N, scales, quants, Y, stream=None)
                                                      Y = Xq W^T (int8 activations)
-    qmm_gemv_q8act / qmm_gemv_concat_q8act / qmm_gemv_swiglu_q8act
-                                                     the decode calls above with x
+    qmm_gemv_q8act / qmm_gemv_concat_q8act / qmm_gemv_swiglu_q8act /
+    qmm_gemv_argmax_q8act                            the decode calls above with x
                                                      quantized inside the launch
 """
 from __future__ import annotations
@@ -44,7 +44,7 @@ QMM_ARGMAX_WORK_BYTES = 32768
 
 EXPORTS = ("qmm_gemv", "qmm_gemv_concat", "qmm_gemv_swiglu", "qmm_gemv_argmax", "qmm_gemm", "qmm_gemm_swiglu",
            "qmm_quantize_q8_0", "qmm_gemm_q8act", "qmm_gemv_q8act", "qmm_gemv_concat_q8act",
-           "qmm_gemv_swiglu_q8act", "qmm_gemm_path", "qmm_blob_bytes", "qmm_block_elems",
+           "qmm_gemv_swiglu_q8act", "qmm_gemv_argmax_q8act", "qmm_gemm_path", "qmm_blob_bytes", "qmm_block_elems",
            "qmm_block_bytes", "qmm_strerror")
 
 _lib = None
@@ -86,6 +86,8 @@ def lib():
         L.qmm_gemv_concat_q8act.restype = ci
         L.qmm_gemv_swiglu_q8act.argtypes = [vp, vp, ci, i64, i64, vp, vp, vp]
         L.qmm_gemv_swiglu_q8act.restype = ci
+        L.qmm_gemv_argmax_q8act.argtypes = [vp, ci, i64, i64, vp, vp, vp, vp, vp]
+        L.qmm_gemv_argmax_q8act.restype = ci
         L.qmm_gemm_path.argtypes = [ci, i64, i64, i64]
         L.qmm_gemm_path.restype = ci
         L.qmm_blob_bytes.argtypes = [ci, i64, i64]
@@ -269,3 +271,13 @@ def qmm_gemv_swiglu_q8act(gate, up, dtype: int, M: int, K: int, x, out, stream=N
                                      _stream(stream))
     if rc != QMM_OK:
         raise QmmError(rc, "qmm_gemv_swiglu_q8act")
+
+
+def qmm_gemv_argmax_q8act(w, dtype: int, M: int, K: int, x, work, index, value=None, stream=None) -> None:
+    import torch
+    rc = lib().qmm_gemv_argmax_q8act(_addr(w, blob_bytes(dtype, M, K) or None, "w_blob"), dtype, M, K,
+                                     _addr(x, 4 * K, "x", torch.float32), _addr(work, QMM_ARGMAX_WORK_BYTES, "work"),
+                                     _addr(index, 8, "index", torch.int64), _addr(value, 4, "value", torch.float32),
+                                     _stream(stream))
+    if rc != QMM_OK:
+        raise QmmError(rc, "qmm_gemv_argmax_q8act")

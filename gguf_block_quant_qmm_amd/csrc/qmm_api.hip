@@ -196,6 +196,23 @@ int qmm_gemv_argmax(const void *w_blob, int dtype, int64_t M, int64_t K, const f
     return e == hipSuccess ? QMM_OK : QMM_ERR_LAUNCH;
 }
 
+int qmm_gemv_argmax_q8act(const void *w_blob, int dtype, int64_t M, int64_t K, const float *x, void *work,
+                          int64_t *index, float *value, void *stream) {
+    int rc = check_shape(dtype, M, K, 1);
+    if (rc != QMM_OK) return rc;
+    if (M > INT32_MAX || !qmm::gemv_fused_ok(dtype, K)) return QMM_ERR_SHAPE;
+    if (!w_blob || !x || !work || !index) return QMM_ERR_NULL;
+    if (!aligned(w_blob, 16) || !aligned(x, 16) || !aligned(work, 16) || !aligned(index, 8) ||
+        (value && !aligned(value, 4)))
+        return QMM_ERR_ALIGN;
+    int cus = 0;
+    rc = current_device(&cus);
+    if (rc != QMM_OK) return rc;
+    const hipError_t e =
+        qmm::launch_gemv_argmax(dtype, w_blob, M, K, x, work, index, value, (hipStream_t)stream, cus, true);
+    return e == hipSuccess ? QMM_OK : QMM_ERR_LAUNCH;
+}
+
 int qmm_gemm_swiglu(const void *gate_blob, const void *up_blob, int dtype, int64_t M, int64_t K, int64_t N,
                     const float *X, float *out, void *stream) {
     int rc = check_shape(dtype, M, K, N);

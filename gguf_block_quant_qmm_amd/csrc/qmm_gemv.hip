@@ -1425,8 +1425,10 @@ hipError_t launch_gemv_swiglu(int dtype, const void *gate, const void *up, int64
     }
 }
 
-hipError_t launch_gemv_argmax(int dtype, const void *blob, int64_t M, int64_t K, const float *x, void *work,
-                              int64_t *index, float *value, hipStream_t st, int cus) {
+// NT = 0: f32 activations; NT = -1: x quantized to Q8_0 inside the launch.
+template <int NT>
+static hipError_t launch_argmax_nt(int dtype, const void *blob, int64_t M, int64_t K, const float *x, void *work,
+                                   int64_t *index, float *value, hipStream_t st, int cus) {
     if (!gemv_fused_ok(dtype, K)) return hipErrorInvalidValue;
     const void *blobs[1] = {blob};
     const int64_t Ms[1] = {M};
@@ -1434,19 +1436,26 @@ hipError_t launch_gemv_argmax(int dtype, const void *blob, int64_t M, int64_t K,
     float2 *part = static_cast<float2 *>(work);
     int64_t grid = 0;
     hipError_t e;
+    constexpr int DQ6 = NT < 0 ? 2 : 4;  // the int8 head's ring depth, as qmm_gemv_q8act
     switch (dtype) {
-    case QMM_Q4_0: e = launch_mats<QMM_Q4_0, 2, 3, GEMV_ARGMAX>(1, blobs, Ms, K, x, ys, st, cus, part, &grid); break;
-    case QMM_Q4_1: e = launch_mats<QMM_Q4_1, 2, 3, GEMV_ARGMAX>(1, blobs, Ms, K, x, ys, st, cus, part, &grid); break;
-    case QMM_Q8_0: e = launch_mats<QMM_Q8_0, 1, 4, GEMV_ARGMAX>(1, blobs, Ms, K, x, ys, st, cus, part, &grid); break;
-    case QMM_Q4_K: e = launch_mats<QMM_Q4_K, 2, 3, GEMV_ARGMAX>(1, blobs, Ms, K, x, ys, st, cus, part, &grid); break;
-    case QMM_Q5_K: e = launch_mats<QMM_Q5_K, 1, 3, GEMV_ARGMAX>(1, blobs, Ms, K, x, ys, st, cus, part, &grid); break;
-    case QMM_Q6_K: e = launch_mats<QMM_Q6_K, 1, 4, GEMV_ARGMAX>(1, blobs, Ms, K, x, ys, st, cus, part, &grid); break;
+    case QMM_Q4_0: e = launch_mats<QMM_Q4_0, 2, 3, GEMV_ARGMAX, NT>(1, blobs, Ms, K, x, ys, st, cus, part, &grid); break;
+    case QMM_Q4_1: e = launch_mats<QMM_Q4_1, 2, 3, GEMV_ARGMAX, NT>(1, blobs, Ms, K, x, ys, st, cus, part, &grid); break;
+    case QMM_Q8_0: e = launch_mats<QMM_Q8_0, 1, 4, GEMV_ARGMAX, NT>(1, blobs, Ms, K, x, ys, st, cus, part, &grid); break;
+    case QMM_Q4_K: e = launch_mats<QMM_Q4_K, 2, 3, GEMV_ARGMAX, NT>(1, blobs, Ms, K, x, ys, st, cus, part, &grid); break;
+    case QMM_Q5_K: e = launch_mats<QMM_Q5_K, 1, 3, GEMV_ARGMAX, NT>(1, blobs, Ms, K, x, ys, st, cus, part, &grid); break;
+    case QMM_Q6_K: e = launch_mats<QMM_Q6_K, 1, DQ6, GEMV_ARGMAX, NT>(1, blobs, Ms, K, x, ys, st, cus, part, &grid); break;
     default: return hipErrorInvalidValue;
     }
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(gemv_argmax_finish, dim3(1), dim3(256), 0, st, static_cast<const float2 *>(part), (int)grid,
                        index, value);
     return hipGetLastError();
+}
+
+hipError_t launch_gemv_argmax(int dtype, const void *blob, int64_t M, int64_t K, const float *x, void *work,
+                              int64_t *index, float *value, hipStream_t st, int cus, bool q8) {
+    return q8 ? launch_argmax_nt<-1>(dtype, blob, M, K, x, work, index, value, st, cus)
+              : launch_argmax_nt<0>(dtype, blob, M, K, x, work, index, value, st, cus);
 }
 
 // Tokens per pass of the several-token kernel and its shape limits.  Rows

@@ -22,9 +22,10 @@ bool gemv_fused_ok(int dtype, int64_t K);
 
 // index = the smallest row with the largest f32 GEMV output (bits of
 // launch_gemv), value = that output; two launches (rows, then the winner
-// among QMM_ARGMAX_WORK_BYTES / 8 workgroup candidates in `work`).
+// among QMM_ARGMAX_WORK_BYTES / 8 workgroup candidates in `work`).  q8: the
+// outputs of the int8 GEMV with x quantized in the launch instead.
 hipError_t launch_gemv_argmax(int dtype, const void *blob, int64_t M, int64_t K, const float *x, void *work,
-                              int64_t *index, float *value, hipStream_t st, int cus);
+                              int64_t *index, float *value, hipStream_t st, int cus, bool q8 = false);
 
 // Y[N][M] for a few tokens with the GEMV's f32 arithmetic, the weights read
 // once per 4 tokens; each Y[n] has the bits launch_gemv gives for X[n].

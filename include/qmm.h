@@ -257,6 +257,14 @@ int qmm_gemv_concat_q8act(int n, const void *const *w_blobs, const int64_t *Ms, 
 int qmm_gemv_swiglu_q8act(const void *gate_blob, const void *up_blob, int dtype, int64_t M, int64_t K,
                           const float *x, float *out, void *stream);
 
+/* Greedy argmax with int8 activations (page "cera 0.5.2 src/backend/cpu.rs":
+ * the greedy argmax GEMV runs on the Q8_0-quantized token): index = the
+ * smallest row with the largest output of qmm_gemv_q8act (its bits, compared
+ * in f32), value = that output.  Arguments, work buffer, shapes and errors as
+ * qmm_gemv_argmax. */
+int qmm_gemv_argmax_q8act(const void *w_blob, int dtype, int64_t M, int64_t K, const float *x,
+                          void *work, int64_t *index, float *value, void *stream);
+
 /* Which arithmetic qmm_gemm uses for these sizes: 0 = f32 (GEMV family),
  * 1 = f16 matrix-core GEMM, or a negative status for invalid arguments. */
 int qmm_gemm_path(int dtype, int64_t M, int64_t K, int64_t N);

@@ -320,3 +320,25 @@ def test_oversized_products_are_rejected():
     assert q.lib().qmm_gemm_q8act(A16, 2, 8, big, big, A16, A16, A16, None) == q.QMM_ERR_SHAPE
     assert q.lib().qmm_quantize_q8_0(A16, big, big, A16, A16, None) == q.QMM_ERR_SHAPE
     assert q.blob_bytes(q.QMM_Q4_0, big, big) == 0
+
+
+@pytest.mark.parametrize("args,code", [
+    ((A16, 5, 8, 64, A16, A16, A16, 0), q.QMM_ERR_DTYPE),
+    ((A16, 2, 8, 96, A16, A16, A16, 0), q.QMM_ERR_SHAPE),
+    ((A16, 2, 1 << 31, 64, A16, A16, A16, 0), q.QMM_ERR_SHAPE),   # rows beyond int32
+    ((A16, 2, 8, 64, A16, 0, A16, 0), q.QMM_ERR_NULL),
+    ((A16, 2, 8, 64, A16, A16, 0, 0), q.QMM_ERR_NULL),
+    ((A16, 2, 8, 64, A16 + 4, A16, A16, 0), q.QMM_ERR_ALIGN),
+    ((A16, 2, 8, 64, A16, A16 + 8, A16, 0), q.QMM_ERR_ALIGN),
+    ((A16, 2, 8, 64, A16, A16, A16 + 4, 0), q.QMM_ERR_ALIGN),
+    ((A16, 2, 8, 64, A16, A16, A16, A16 + 2), q.QMM_ERR_ALIGN),
+])
+def test_gemv_argmax_q8act_rejects(args, code):
+    assert q.lib().qmm_gemv_argmax_q8act(*args, None) == code
+
+
+def test_argmax_q8act_without_gpu_reports_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; covered by the GPU tests")
+    assert q.lib().qmm_gemv_argmax_q8act(A16, 14, 8, 4096, A16, A16, A16, None, None) == q.QMM_ERR_DEVICE

@@ -332,3 +332,47 @@ def test_one_launch_decode_layer_full_size():
     torch.cuda.synchronize()
     for b, y in zip(blobs, ys):
         assert same_bits(y.cpu().numpy(), one_launch(dt, b, M, K, x_d)), "gate+up concat q8act"
+
+
+def run_argmax_q8(dt, blob_d, M, K, x_d):
+    work = torch.empty(q.QMM_ARGMAX_WORK_BYTES, dtype=torch.uint8, device="cuda")
+    idx = torch.full((1,), -7, dtype=torch.int64, device="cuda")
+    val = torch.full((1,), float("nan"), device="cuda")
+    q.qmm_gemv_argmax_q8act(blob_d, dt, M, K, x_d, work, idx, val)
+    torch.cuda.synchronize()
+    return int(idx.item()), float(val.item())
+
+
+@pytest.mark.parametrize("dt", DTYPES, ids=NAME.get)
+def test_gemv_argmax_q8act(dt):
+    for i, (M, K) in enumerate([(1, 512), (777, 1024), (300, 8192), (5000, 4096)]):
+        blob = make_blob(dt, M, K, rng_for(990 + dt, i))
+        x = make_x(1, K, rng_for(990 + dt, 10 + i))
+        blob_d, x_d = to_dev(blob), to_dev(x.reshape(-1))
+        y = one_launch(dt, blob_d, M, K, x_d)
+        idx, val = run_argmax_q8(dt, blob_d, M, K, x_d)
+        first = int(np.flatnonzero(y == y.max())[0])
+        assert idx == first and val == y[first], f"{NAME[dt]} M={M} K={K}: argmax {idx} vs {first}"
+        # against the exact int8 logits: the pick is a maximum within the bound
+        sc, qq = oracle.quantize_q8_0(x)
+        _, Y64, _, Sp = oracle.matmul_q8act(dt, blob, M, K, sc, qq)
+        best = int(np.argmax(Y64[0]))
+        assert Y64[0, idx] >= Y64[0, best] - TAU * (Sp[0, idx] + Sp[0, best]), f"{NAME[dt]}: not a maximum"
+        if M > 1 and first > 0:
+            # plant a tie: an earlier row becomes a copy of the winner
+            rb = blob.size // M
+            tied = blob.copy()
+            tied[(first - 1) * rb:first * rb] = blob[first * rb:(first + 1) * rb]
+            idx2, _ = run_argmax_q8(dt, to_dev(tied), M, K, x_d)
+            assert idx2 == first - 1, f"{NAME[dt]}: a tie must go to the smaller row"
+
+
+def test_gemv_argmax_q8act_lm_head():
+    label, dt, M, K, _ = WORKLOADS[5]
+    blob = make_blob(dt, M, K, rng_for(5, 0))
+    x = make_x(1, K, rng_for(5, 1001))
+    blob_d, x_d = to_dev(blob), to_dev(x.reshape(-1))
+    y = one_launch(dt, blob_d, M, K, x_d)
+    idx, val = run_argmax_q8(dt, blob_d, M, K, x_d)
+    first = int(np.flatnonzero(y == y.max())[0])
+    assert idx == first and val == y[first], f"{label}: argmax {idx} vs {first}"
