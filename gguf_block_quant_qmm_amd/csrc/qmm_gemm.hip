@@ -891,7 +891,12 @@ __global__ void __launch_bounds__(64 * W) gemm_wb_kernel(const uint8_t *__restri
 // 32 x BN tiles are summed once at the end through LDS, in wavefront order
 // (deterministic).  Weights and activations use the same bounds-checked
 // buffer loads, decoders and permuted-k layout as the kernel above.
-template <int DT, int BN, int W, int WD, int XD>
+//
+// FM weight-row fragments of 32 per wavefront (a workgroup owns 32 FM rows):
+// every activation fragment read from LDS feeds FM matrix-core steps, so the
+// activation traffic per weight row falls by FM.  Each output's sum has the
+// same order for every FM (same k-steps, same wavefront order).
+template <int DT, int BN, int W, int WD, int XD, int FM = 1>
 __global__ void __launch_bounds__(64 * W) gemm_sk_kernel(const uint8_t *__restrict__ blob, int64_t M, int64_t K,
                                                         int64_t N, int64_t row_bytes, const float *__restrict__ X,
                                                         float *__restrict__ Y, int n_ntiles) {
@@ -906,13 +911,15 @@ __global__ void __launch_bounds__(64 * W) gemm_sk_kernel(const uint8_t *__restri
     const int t = threadIdx.x, lane = t & 63, kh = lane >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int64_t mt = blockIdx.x / n_ntiles, nt = blockIdx.x % n_ntiles;
-    const int64_t m0 = mt * 32, n0 = nt * BN;
+    const int64_t m0 = mt * (32 * FM), n0 = nt * BN;
     const int64_t per = (K / BK) / W, kt0 = wave * per;  // per is a multiple of 4
     _Float16 *xw = sk_lds + wave * (2 * BN * LDK);
 
-    const int64_t wrows = M - m0 < 32 ? M - m0 : 32;
+    const int64_t wrows = M - m0 < 32 * FM ? M - m0 : 32 * FM;
     const Rsrc wrs = make_rsrc_uniform(blob + m0 * row_bytes, (uint32_t)(wrows * row_bytes));
-    const uint32_t roff = (uint32_t)((lane & 31) * row_bytes);
+    uint32_t roff[FM];
+#pragma unroll
+    for (int j = 0; j < FM; j++) roff[j] = (uint32_t)((32 * j + (lane & 31)) * row_bytes);
     const int64_t xrows = N - n0 < BN ? N - n0 : BN;
     const Rsrc xrs = make_rsrc_uniform(X + n0 * K, (uint32_t)(xrows * K * 4));
     uint32_t xoff[NXF];
@@ -922,16 +929,17 @@ __global__ void __launch_bounds__(64 * W) gemm_sk_kernel(const uint8_t *__restri
         xoff[i] = (uint32_t)((r * K + 4 * c4) * 4);
     }
 
-    uint32_t wr[WD][BD::NW];
+    uint32_t wr[WD][FM][BD::NW];
     floatx4 xr[XD][NXF];
-    half8 bf[2][4];
-    typename BD::State st;
+    half8 bf[2][FM][4];
+    typename BD::State st[FM];
     const int64_t kend = kt0 + per;
     // c = kt % 4 (a compile-time constant at every call); tiles past the
     // range repeat its last super-block (never used)
-    auto wload = [&](int64_t kt, int c, uint32_t (&w)[BD::NW]) {
+    auto wload = [&](int64_t kt, int c, uint32_t (&w)[FM][BD::NW]) {
         const int64_t kc = kt < kend ? kt : kend - 4 + c;
-        BD::loadb(wrs, roff, kc * BK, kh, c, w);
+#pragma unroll
+        for (int j = 0; j < FM; j++) BD::loadb(wrs, roff[j], kc * BK, kh, c, w[j]);
     };
     auto xload = [&](int64_t kt, floatx4 (&x)[NXF]) {
         const uint32_t kb = (uint32_t)((kt < kend ? kt : kend - 1) * BK * 4);
@@ -952,17 +960,20 @@ __global__ void __launch_bounds__(64 * W) gemm_sk_kernel(const uint8_t *__restri
         }
     };
 
-    floatx16 acc[FN];
+    floatx16 acc[FN][FM];
 #pragma unroll
     for (int i = 0; i < FN; i++)
 #pragma unroll
-        for (int v = 0; v < 16; v++) acc[i][v] = 0.f;
+        for (int j = 0; j < FM; j++)
+#pragma unroll
+            for (int v = 0; v < 16; v++) acc[i][j][v] = 0.f;
 
 #pragma unroll
     for (int d = 0; d < WD; d++) wload(kt0 + d, d % 4, wr[d]);
 #pragma unroll
     for (int d = 0; d < XD; d++) xload(kt0 + d, xr[d]);
-    BD::decode(wr[0], st, kh, 0, kt0 * BK, bf[0]);
+#pragma unroll
+    for (int j = 0; j < FM; j++) BD::decode(wr[0][j], st[j], kh, 0, kt0 * BK, bf[0][j]);
     xstore(xr[0], xw);
     wload(kt0 + WD, WD % 4, wr[0]);
     xload(kt0 + XD, xr[0]);
@@ -983,8 +994,14 @@ __global__ void __launch_bounds__(64 * W) gemm_sk_kernel(const uint8_t *__restri
             for (int s = 0; s < BK / 16; s++) {
 #pragma unroll
                 for (int i = 0; i < FN; i++)
-                    acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[s][i], bf[u & 1][s], acc[i], 0, 0, 0);
-                if (s == 0) BD::decode(wr[(u + 1) % WD], st, kh, (u + 1) % 4, (kt + 1) * BK, bf[(u + 1) & 1]);
+#pragma unroll
+                    for (int j = 0; j < FM; j++)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[s][i], bf[u & 1][j][s], acc[i][j], 0, 0, 0);
+                if (s == 0) {
+#pragma unroll
+                    for (int j = 0; j < FM; j++)
+                        BD::decode(wr[(u + 1) % WD][j], st[j], kh, (u + 1) % 4, (kt + 1) * BK, bf[(u + 1) & 1][j]);
+                }
                 if (s == 1) wload(kt + 1 + WD, (u + 1 + WD) % 4, wr[(u + 1) % WD]);
                 if (s == 2) xstore(xr[(u + 1) % XD], xw + ((u + 1) & 1) * (BN * LDK));
                 if (s == 3) xload(kt + 1 + XD, xr[(u + 1) % XD]);
@@ -994,39 +1011,42 @@ __global__ void __launch_bounds__(64 * W) gemm_sk_kernel(const uint8_t *__restri
 
     // sum the W partial tiles in wavefront order
     __syncthreads();
-    float *red = reinterpret_cast<float *>(sk_lds);  // [W][FN * 16][64]
+    constexpr int NF = FN * FM;  // 32 x 32 fragments per wavefront, index i * FM + j
+    float *red = reinterpret_cast<float *>(sk_lds);  // [W][NF * 16][64]
 #pragma unroll
     for (int i = 0; i < FN; i++)
 #pragma unroll
-        for (int v = 0; v < 16; v++) red[(wave * FN * 16 + i * 16 + v) * 64 + lane] = acc[i][v];
+        for (int j = 0; j < FM; j++)
+#pragma unroll
+            for (int v = 0; v < 16; v++) red[(wave * NF * 16 + (i * FM + j) * 16 + v) * 64 + lane] = acc[i][j][v];
     __syncthreads();
-    for (int o = t; o < FN * 16 * 64; o += 64 * W) {
+    for (int o = t; o < NF * 16 * 64; o += 64 * W) {
         float sum = red[o];
-        for (int w = 1; w < W; w++) sum += red[w * FN * 16 * 64 + o];
-        const int L = o & 63, v = (o >> 6) & 15, i = o >> 10;
-        const int64_t m = m0 + (L & 31), n = n0 + 32 * i + 8 * (v >> 2) + 4 * (L >> 5) + (v & 3);
+        for (int w = 1; w < W; w++) sum += red[w * NF * 16 * 64 + o];
+        const int L = o & 63, v = (o >> 6) & 15, f = o >> 10, i = f / FM, j = f % FM;
+        const int64_t m = m0 + 32 * j + (L & 31), n = n0 + 32 * i + 8 * (v >> 2) + 4 * (L >> 5) + (v & 3);
         if (m < M && n < N) Y[n * M + m] = sum;
     }
 }
 
-template <int DT, int BN, int W, int WD, int XD>
+template <int DT, int BN, int W, int WD, int XD, int FM = 1>
 static hipError_t launch_sk(const uint8_t *blob, int64_t M, int64_t K, int64_t N, const float *X, float *Y,
                             hipStream_t st) {
     constexpr int BS = Geo<DT>::BS, BB = Geo<DT>::BB;
     const int64_t row_bytes = (K / BS) * BB;
-    const int64_t mtiles = (M + 31) / 32, ntiles = (N + BN - 1) / BN;
+    const int64_t mtiles = (M + 32 * FM - 1) / (32 * FM), ntiles = (N + BN - 1) / BN;
     const int64_t grid = mtiles * ntiles;
     if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    constexpr size_t xs_bytes = (size_t)W * 2 * BN * LDK * 2, red_bytes = (size_t)W * (BN / 32) * 16 * 64 * 4;
+    constexpr size_t xs_bytes = (size_t)W * 2 * BN * LDK * 2, red_bytes = (size_t)W * (BN / 32) * FM * 16 * 64 * 4;
     constexpr size_t lds = xs_bytes > red_bytes ? xs_bytes : red_bytes;
     if (lds > 64 * 1024) {
         static const hipError_t attr = hipFuncSetAttribute(
-            reinterpret_cast<const void *>(&gemm_sk_kernel<DT, BN, W, WD, XD>),
+            reinterpret_cast<const void *>(&gemm_sk_kernel<DT, BN, W, WD, XD, FM>),
             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (attr != hipSuccess) return attr;
     }
-    hipLaunchKernelGGL((gemm_sk_kernel<DT, BN, W, WD, XD>), dim3((unsigned)grid), dim3(64 * W), lds, st, blob, M, K,
-                       N, row_bytes, X, Y, (int)ntiles);
+    hipLaunchKernelGGL((gemm_sk_kernel<DT, BN, W, WD, XD, FM>), dim3((unsigned)grid), dim3(64 * W), lds, st, blob, M,
+                       K, N, row_bytes, X, Y, (int)ntiles);
     return hipGetLastError();
 }
 
@@ -1104,10 +1124,15 @@ static hipError_t launch_dt(const uint8_t *blob, int64_t M, int64_t K, int64_t N
     const bool wb_ok = !gen && (K % (4 * BK)) == 0 && K * 4 * 128 < ((int64_t)1 << 31);
     const bool sk_ok = wb_ok && (K / BK) % 16 == 0;  // 4 wavefronts x whole super-blocks
     int choice = gemm_kernel_choice();
-    if (choice == 4 && !sk_ok) choice = -1;
-    if (choice < 0 || choice > 4 || (choice > 0 && !wb_ok)) {
+    if ((choice == 4 || choice == 5) && !sk_ok) choice = -1;
+    if (choice < 0 || choice > 5 || (choice > 0 && !wb_ok)) {
         if (!wb_ok) choice = 0;
-        else if (sk_ok && ((N <= 32 && (M + 31) / 32 <= 1024) || ((M + 31) / 32) * ((N + 31) / 32) <= 512)) choice = 4;
+        else if (sk_ok && ((N <= 32 && (M + 31) / 32 <= 1024) || ((M + 31) / 32) * ((N + 31) / 32) <= 512))
+            // two row fragments per wavefront halve the activation traffic
+            // where they still give >= 192 workgroups (14336 x 4096 Q4_K:
+            // N = 32 21.3 vs 26.1 us, N = 16 19.0 vs 22.7 us; on 4096 rows
+            // the 64 workgroups leave CUs idle: 20.3 vs 13.6 us)
+            choice = (N <= 32 && (M + 63) / 64 >= 192) ? 5 : 4;
         else if (N <= 32) choice = 3;
         else if (((M + 255) / 256) * ((N + 127) / 128) >= 200) choice = 1;
         else choice = 2;
@@ -1117,6 +1142,7 @@ static hipError_t launch_dt(const uint8_t *blob, int64_t M, int64_t K, int64_t N
     case 2: return launch_wb<DT, 32, 64, 4, 4, 0, 4>(blob, M, K, N, X, Y, st);
     case 3: return launch_wb<DT, 32, 32, 4, 4, 0, 4>(blob, M, K, N, X, Y, st);
     case 4: return launch_sk<DT, 32, 4, 2, 2>(blob, M, K, N, X, Y, st);
+    case 5: return launch_sk<DT, 32, 4, 2, 2, 2>(blob, M, K, N, X, Y, st);
     default: break;
     }
     if (N <= 32) return launch_tile<DT, 128, 32, 1, 4>(blob, M, K, N, X, Y, st, gen);
