@@ -441,10 +441,20 @@ def spec_verify(args, q, torch, dev, WORKLOADS, make_blob, make_x, rng_for):
         Y = torch.empty((N, M), device=dev)
         per_row = timed(lambda c: [q.qmm_gemv(copies[c], dt, M, K, X[n], Y[n], stream=stream) for n in range(N)])
         batched = timed(lambda c: q.qmm_gemm(copies[c], dt, M, K, N, X, Y, stream=stream))
+        # int8 activations: the N positions quantized (one launch) and one
+        # qmm_gemm_q8act call reading the head once per 4 positions
+        sc = torch.empty((N, K // 32), device=dev)
+        qq = torch.empty((N, K), dtype=torch.int8, device=dev)
+
+        def q8(c):
+            q.qmm_quantize_q8_0(X, N, K, sc, qq, stream=stream)
+            q.qmm_gemm_q8act(copies[c], dt, M, K, N, sc, qq, Y, stream=stream)
+        int8 = timed(q8)
         rec = {"workload": f"{label}, verify {N} positions", "N": N, "M": M, "K": K, "dtype": "Q6_K",
                "per_row_us": round(per_row, 2), "batched_us": round(batched, 2),
                "batched_path": "f16-mfma" if q.gemm_path(dt, M, K, N) else "f32 (bits of the GEMV)",
-               "batched_weight_GBps": round(blob.numel() / (batched * 1e-6) / 1e9, 1)}
+               "batched_weight_GBps": round(blob.numel() / (batched * 1e-6) / 1e9, 1),
+               "int8_quantize_plus_q8act_us": round(int8, 2)}
         if N == 1:
             rec["argmax_us"] = round(timed(lambda c: q.qmm_gemv_argmax(copies[c], dt, M, K, X[0], work, idx,
                                                                         stream=stream)), 2)
