@@ -840,6 +840,16 @@ __global__ void __launch_bounds__(256) gemv_kernel(const GemvMats mats, int64_t 
         x_from_lds<DT>(xs, active ? u : 0, xv);
     }
 
+    // one matrix, whole-row wavefronts: a wavefront's rows are consecutive,
+    // so their sums are parked one per lane and written 64 at a time with one
+    // coalesced store (single-lane 4-byte stores are partial-line writes)
+    constexpr bool BATCH = WAVE_ROWS && MODE == GEMV_ONE && NT <= 1;
+    float obuf = 0.f;
+    const int64_t orow0 = g0 * R;  // first row of the wavefront's range
+    auto flush = [&](int64_t k0, int cnt) {  // rows orow0 + k0 + [0, cnt) from lanes [0, cnt)
+        const int64_t row = orow0 + k0 + lane;
+        if (lane < cnt && row < mats.M[0]) mats.y[0][row] = obuf;
+    };
     for (int64_t i0 = 0; i0 < n; i0 += D + 1) {
 #pragma unroll
         for (int s = 0; s <= D; s++) {
@@ -857,7 +867,16 @@ __global__ void __launch_bounds__(256) gemv_kernel(const GemvMats mats, int64_t 
                         acc[r * TK + tn] = wave_sum_to_lane63(active ? d : 0.f);
                     }
                 }
-                if (WAVE_ROWS) {
+                if constexpr (BATCH) {
+#pragma unroll
+                    for (int r = 0; r < R; r++) {
+                        const int64_t k = i * R + r;  // row offset in the range
+                        const float v = __builtin_bit_cast(
+                            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, acc[r]), 63));
+                        if (lane == (int)(k & 63)) obuf = v;
+                        if ((k & 63) == 63) flush(k - 63, 64);
+                    }
+                } else if (WAVE_ROWS) {
                     if (lane == 63) {
 #pragma unroll
                         for (int r = 0; r < R; r++)
@@ -891,6 +910,10 @@ __global__ void __launch_bounds__(256) gemv_kernel(const GemvMats mats, int64_t 
                 }
             }
         }
+    }
+    if constexpr (BATCH) {
+        const int64_t total = n * R;  // rows of the range (past-M rows are not stored)
+        if ((total & 63) != 0) flush(total & ~(int64_t)63, (int)(total & 63));
     }
     if constexpr (MODE == GEMV_ARGMAX) {
         // the best of the workgroup: lane 63 of every wavefront (whole rows) or
