@@ -1106,8 +1106,11 @@ static hipError_t launch_wb(const uint8_t *blob, int64_t M, int64_t K, int64_t N
 //     grid nearly fills the chip, else 4 x 32 rows x 64 tokens;
 //   * the LDS-staged kernel when the layout rules the others out (K not a
 //     multiple of 256, odd block counts).
-// QMM_GEMM_KERNEL = 0 / 1 / 2 / 3 / 4 forces LDS-staged / 8x32x128 / 4x32x64 /
-// 4x32x32 / skinny where the layout allows (a measurement lever, read once).
+//   * the skinny kernel with two 32-row fragments per wavefront for N <= 32
+//     when that still gives >= 192 workgroups (half the activation traffic);
+// QMM_GEMM_KERNEL = 0 / 1 / 2 / 3 / 4 / 5 forces LDS-staged / 8x32x128 /
+// 4x32x64 / 4x32x32 / skinny / skinny with two row fragments where the layout
+// allows (a measurement lever, read once).
 static int gemm_kernel_choice() {
     static int v = [] {
         const char *e = getenv("QMM_GEMM_KERNEL");
