@@ -287,3 +287,18 @@ def test_lm_head_verify_batch_matches_decode():
     rows = sample_rows(M, 256, 41)
     _, Y64, S = oracle.matmul(dt, blob, M, K, X, rows=rows)
     check(Yg[:, rows], Y64, S, 1e-5, "Q6_K LM head N=4")
+
+
+@pytest.mark.parametrize("dt", DTYPES, ids=NAME.get)
+def test_gemm_skinny_two_fragments_ragged(dt):
+    # N <= 32 on >= 192 two-fragment row tiles selects the split-K kernel with
+    # two 32-row fragments per wavefront; M ends in a partial 64-row tile (and
+    # a partial 32-row fragment), N in a partial token tile
+    M, K, N = 12350, 1024, 17
+    blob = make_blob(dt, M, K, rng_for(660 + dt, 0))
+    X = make_x(N, K, rng_for(660 + dt, 1))
+    rows = np.unique(np.concatenate([sample_rows(M, 40, 660 + dt), np.arange(M - 70, M)]))
+    _, Y64, S = oracle.matmul(dt, blob, M, K, X, rows=rows)
+    Yg = gpu_gemm(dt, to_dev(blob), M, K, X)
+    assert np.all(np.isfinite(Yg))
+    check(Yg[:, rows], Y64, S, q.tolerance(dt, M, K, N), f"{NAME[dt]} two-fragment skinny gemm M={M} K={K} N={N}")
