@@ -100,8 +100,14 @@ int64_t mfma_from_n(int dtype, int64_t M, int64_t K) {
         return (int64_t)(v >= 1 && v <= 1024 ? v : 0);
     }();
     if (lever) return lever;
-    (void)M;
-    if (qmm::gemv_tokens_ok(dtype, K)) return (dtype == QMM_Q4_K || dtype == QMM_Q5_K) ? 3 : 5;
+    if (qmm::gemv_tokens_ok(dtype, K)) {
+        if (dtype == QMM_Q4_K || dtype == QMM_Q5_K) return 3;
+        // tall Q4_1 (>= 192 two-fragment row tiles, where the small-N GEMM
+        // halves its activation traffic): the matrix cores win from N = 4
+        // (14336 x 4096: 21.2 vs 22.9-23.1 us)
+        if (dtype == QMM_Q4_1 && (M + 63) / 64 >= 192) return 4;
+        return 5;
+    }
     return (dtype == QMM_Q4_0 || dtype == QMM_Q6_K) ? 3 : 2;
 }
 

@@ -165,7 +165,8 @@ int qmm_gemv_argmax(const void *w_blob, int dtype, int64_t M, int64_t K, const f
  * src/backend/cpu.rs": decode and prefill must agree bit for bit).  With K a
  * multiple of 64 up to 4096 and an even number of blocks per row (Q4_0, Q4_1,
  * Q8_0, Q6_K) up to 4 tokens share one read of the weights and the crossover
- * is N = 5 (Q4_0, Q4_1, Q8_0, Q6_K) or 3 (Q4_K, Q5_K); otherwise each token is
+ * is N = 5 (Q4_0, Q4_1, Q8_0, Q6_K; 4 for Q4_1 with M >= 12225) or 3 (Q4_K,
+ * Q5_K); otherwise each token is
  * one GEMV launch and the crossover is 3 (Q4_0, Q6_K) or 2 (Q4_1, Q8_0, Q4_K,
  * Q5_K).  The path
  * qmm_gemm_path names: 0 = all-f32 arithmetic (tolerance 1e-5 of

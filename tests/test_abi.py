@@ -104,6 +104,8 @@ def test_gemm_path_selection():
     assert q.gemm_path(q.QMM_Q8_0, 4096, 8192, 2) == 1
     assert q.gemm_path(q.QMM_Q6_K, 4096, 8192, 2) == 0
     assert q.gemm_path(q.QMM_Q4_1, 4096, 4096, 4) == 0
+    assert q.gemm_path(q.QMM_Q4_1, 14336, 4096, 3) == 0   # tall Q4_1: matrix cores from N = 4
+    assert q.gemm_path(q.QMM_Q4_1, 14336, 4096, 4) == 1
     assert q.gemm_path(q.QMM_Q4_1, 4096, 4096, 5) == 1
     assert q.gemm_path(q.QMM_Q4_1, 4096, 8192, 2) == 1
     assert q.gemm_path(q.QMM_Q5_K, 4096, 4096, 2) == 0
