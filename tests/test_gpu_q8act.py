@@ -376,3 +376,17 @@ def test_gemv_argmax_q8act_lm_head():
     idx, val = run_argmax_q8(dt, blob_d, M, K, x_d)
     first = int(np.flatnonzero(y == y.max())[0])
     assert idx == first and val == y[first], f"{label}: argmax {idx} vs {first}"
+
+
+@pytest.mark.parametrize("dt", [q.QMM_Q4_0, q.QMM_Q6_K, q.QMM_Q4_K], ids=NAME.get)
+def test_q8act_many_tokens(dt):
+    # 600 tokens = 150 token groups of 4 on the fast kernel (the last group
+    # full), and 600 grid rows on the byte-load kernel (odd block count)
+    for i, (M, K) in enumerate([(130, 4 * bs_of(dt) * (4 if bs_of(dt) == 32 else 1)),
+                                (70, 3 * bs_of(dt))]):
+        N = 600
+        blob = make_blob(dt, M, K, rng_for(995 + dt, i))
+        sc, qq = oracle.quantize_q8_0(make_x(N, K, rng_for(995 + dt, 10 + i)))
+        _, Y64, _, Sp = oracle.matmul_q8act(dt, blob, M, K, sc, qq)
+        Yg = gpu_q8act(dt, to_dev(blob), M, K, sc, qq)
+        check(Yg, Y64, Sp, f"{NAME[dt]} q8act M={M} K={K} N={N}")
