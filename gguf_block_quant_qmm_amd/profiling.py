@@ -20,6 +20,16 @@ Subcommands (run from the repository root):
            Stored under NAME with the hash of the kernel sources, so that a
            reader can tell when a kernel has changed since the counters were
            taken.
+
+  mfma     --csv <counter_collection.csv> --key REGEX --flops F --simds S
+           Matrix-core utilisation of the dispatches whose kernel name matches
+           REGEX, from a run collecting SQ_VALU_MFMA_BUSY_CYCLES,
+           SQ_INSTS_VALU_MFMA_MOPS_F16 and GRBM_GUI_ACTIVE (rocprofv3 reports
+           each summed over the device: GRBM_GUI_ACTIVE over its --xccs
+           dies): busy fraction = MFMA busy cycles / (GUI-active cycles per
+           die x S SIMDs), the clock = GUI-active cycles per die / duration,
+           the f16 matrix FLOPs the counters saw (MOPS x 512) against the
+           algorithmic F per dispatch, and the TFLOP/s of F over the duration.
 """
 from __future__ import annotations
 
@@ -132,6 +142,37 @@ def _traffic(args):
         fh.write("\n")
 
 
+def _mfma(args):
+    rx = re.compile(args.key)
+    per = defaultdict(lambda: defaultdict(float))
+    dur = {}
+    for r in csv.DictReader(open(args.csv)):
+        if not rx.search(r["Kernel_Name"]):
+            continue
+        d = int(r["Dispatch_Id"])
+        name = r["Counter_Name"]
+        val = float(r["Counter_Value"])
+        per[d][name] += val
+        dur[d] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    if not per:
+        sys.exit("no matching dispatches")
+    rows = []
+    for d in sorted(per):
+        c = per[d]
+        gui = c["GRBM_GUI_ACTIVE"] / args.xccs  # cycles of one die
+        busy = c["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui * args.simds)
+        flops_seen = c["SQ_INSTS_VALU_MFMA_MOPS_F16"] * 512
+        rows.append((d, busy, gui / dur[d] / 1e9, flops_seen / args.flops, args.flops / dur[d] / 1e12,
+                     dur[d] * 1e6))
+    print("| dispatch | MFMA busy | clock GHz | counted f16 FLOPs / algorithmic | TFLOP/s (algorithmic / duration) | us |")
+    print("|---:|---:|---:|---:|---:|---:|")
+    for d, busy, ghz, ratio, tf, us in rows:
+        print(f"| {d} | {busy * 100:.1f} % | {ghz:.2f} | {ratio:.3f} | {tf:.1f} | {us:.1f} |")
+    n = len(rows)
+    mean = [sum(r[i] for r in rows) / n for i in range(1, 6)]
+    print(f"| mean of {n} | {mean[0] * 100:.1f} % | {mean[1]:.2f} | {mean[2]:.3f} | {mean[3]:.1f} | {mean[4]:.1f} |")
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd_name", required=True)
@@ -153,8 +194,14 @@ def main(argv=None):
     t.add_argument("--calib-regex", default=r"copy|elementwise")
     t.add_argument("--key", action="append", required=True)
     t.add_argument("--out", default=os.path.join(ROOT, "profiles", "counters.json"))
+    m = sub.add_parser("mfma")
+    m.add_argument("--csv", required=True)
+    m.add_argument("--key", required=True)
+    m.add_argument("--flops", type=float, required=True)
+    m.add_argument("--simds", type=int, default=1024)
+    m.add_argument("--xccs", type=int, default=8)
     a = ap.parse_args(argv)
-    {"copy": _copy, "stats": _stats, "traffic": _traffic}[a.cmd_name](a)
+    {"copy": _copy, "stats": _stats, "traffic": _traffic, "mfma": _mfma}[a.cmd_name](a)
 
 
 if __name__ == "__main__":
