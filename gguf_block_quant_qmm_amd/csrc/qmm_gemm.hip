@@ -1108,9 +1108,12 @@ static hipError_t launch_wb(const uint8_t *blob, int64_t M, int64_t K, int64_t N
 //     multiple of 256, odd block counts).
 //   * the skinny kernel with two 32-row fragments per wavefront for N <= 32
 //     when that still gives >= 192 workgroups (half the activation traffic);
-// QMM_GEMM_KERNEL = 0 / 1 / 2 / 3 / 4 / 5 forces LDS-staged / 8x32x128 /
-// 4x32x64 / 4x32x32 / skinny / skinny with two row fragments where the layout
-// allows (a measurement lever, read once).
+//   * for N > 32, the skinny kernel with 64-token tiles (32 or 64 rows) when
+//     it fits one round of <= 256 workgroups and the 32-token tile does not;
+// QMM_GEMM_KERNEL = 0 / 1 / 2 / 3 / 4 / 5 / 6 / 7 forces LDS-staged /
+// 8x32x128 / 4x32x64 / 4x32x32 / skinny / skinny with two row fragments /
+// skinny 32 x 64 tokens / skinny 64 x 64 tokens where the layout allows (a
+// measurement lever, read once).
 static int gemm_kernel_choice() {
     static int v = [] {
         const char *e = getenv("QMM_GEMM_KERNEL");
@@ -1127,9 +1130,16 @@ static hipError_t launch_dt(const uint8_t *blob, int64_t M, int64_t K, int64_t N
     const bool wb_ok = !gen && (K % (4 * BK)) == 0 && K * 4 * 128 < ((int64_t)1 << 31);
     const bool sk_ok = wb_ok && (K / BK) % 16 == 0;  // 4 wavefronts x whole super-blocks
     int choice = gemm_kernel_choice();
-    if ((choice == 4 || choice == 5) && !sk_ok) choice = -1;
-    if (choice < 0 || choice > 5 || (choice > 0 && !wb_ok)) {
+    if (choice >= 4 && choice <= 7 && !sk_ok) choice = -1;
+    if (choice < 0 || choice > 7 || (choice > 0 && !wb_ok)) {
+        // split-K tiles of 64 tokens (one wavefront per SIMD) pay where they
+        // give one round of <= 256 workgroups and the 32-token tile would not
+        // (4096 x 4096 Q4_K N = 128: 32-row tiles 20.7 vs 23.8 us; N = 256:
+        // 64-row tiles 28.6 vs 35.4 us; 14336 x 4096 N = 64: 30.2 vs 36.6 us)
+        const int64_t mt32 = (M + 31) / 32, mt64 = (M + 63) / 64, nt32 = (N + 31) / 32, nt64 = (N + 63) / 64;
         if (!wb_ok) choice = 0;
+        else if (sk_ok && N > 32 && mt32 * nt32 > 256 && mt32 * nt64 <= 256) choice = 6;
+        else if (sk_ok && N > 32 && mt32 * nt32 > 256 && mt64 * nt64 <= 256) choice = 7;
         else if (sk_ok && ((N <= 32 && (M + 31) / 32 <= 1024) || ((M + 31) / 32) * ((N + 31) / 32) <= 512))
             // two row fragments per wavefront halve the activation traffic
             // where they still give >= 192 workgroups (14336 x 4096 Q4_K:
@@ -1146,6 +1156,8 @@ static hipError_t launch_dt(const uint8_t *blob, int64_t M, int64_t K, int64_t N
     case 3: return launch_wb<DT, 32, 32, 4, 4, 0, 4>(blob, M, K, N, X, Y, st);
     case 4: return launch_sk<DT, 32, 4, 2, 2>(blob, M, K, N, X, Y, st);
     case 5: return launch_sk<DT, 32, 4, 2, 2, 2>(blob, M, K, N, X, Y, st);
+    case 6: return launch_sk<DT, 64, 4, 2, 2, 1>(blob, M, K, N, X, Y, st);
+    case 7: return launch_sk<DT, 64, 4, 2, 2, 2>(blob, M, K, N, X, Y, st);
     default: break;
     }
     if (N <= 32) return launch_tile<DT, 128, 32, 1, 4>(blob, M, K, N, X, Y, st, gen);

@@ -302,3 +302,19 @@ def test_gemm_skinny_two_fragments_ragged(dt):
     Yg = gpu_gemm(dt, to_dev(blob), M, K, X)
     assert np.all(np.isfinite(Yg))
     check(Yg[:, rows], Y64, S, q.tolerance(dt, M, K, N), f"{NAME[dt]} two-fragment skinny gemm M={M} K={K} N={N}")
+
+
+@pytest.mark.parametrize("dt", DTYPES, ids=NAME.get)
+@pytest.mark.parametrize("N", [100, 130])
+def test_gemm_skinny_64_token_tiles_ragged(dt, N):
+    # 4000 rows: N = 100 selects split-K tiles of 32 rows x 64 tokens, N = 130
+    # tiles of 64 rows x 64 tokens (one round of <= 256 workgroups each); M
+    # and N end in partial tiles
+    M, K = 4000, 1024
+    blob = make_blob(dt, M, K, rng_for(670 + dt, N))
+    X = make_x(N, K, rng_for(670 + dt, 1000 + N))
+    rows = np.unique(np.concatenate([sample_rows(M, 40, 670 + dt + N), np.arange(M - 70, M)]))
+    _, Y64, S = oracle.matmul(dt, blob, M, K, X, rows=rows)
+    Yg = gpu_gemm(dt, to_dev(blob), M, K, X)
+    assert np.all(np.isfinite(Yg))
+    check(Yg[:, rows], Y64, S, q.tolerance(dt, M, K, N), f"{NAME[dt]} 64-token skinny gemm M={M} K={K} N={N}")
