@@ -94,8 +94,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(row sharding is described in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(a caller shards rows across GPUs); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
