@@ -368,10 +368,21 @@ struct XA {
 
 // Q8_0 quantization of four activations of a block whose other 28 sit in the
 // seven neighbouring lanes (lanes 8j .. 8j+7 hold one block): the block's
-// amax by three xor shuffles (a NaN never wins the comparison), d = amax/127,
-// id = 1/d unless d is 0 or 1/d is not finite, codes = rint(v * id) clamped to
-// [-128, 127] (NaN -> 0), packed little-endian; *d_out = d (the caller stores
-// it rounded to f16).  Every lane of the wavefront must call it.
+// amax (a NaN never wins the comparison), d = amax/127, id = 1/d unless d is
+// 0 or 1/d is not finite, codes = rint(v * id) clamped to [-128, 127] (NaN ->
+// 0), packed little-endian; *d_out = d (the caller stores it rounded to f16).
+// Every lane of the wavefront must call it.
+//
+// The lane maxima are combined across the 8 lanes with DPP moves inside the
+// VALU (swap neighbours, swap pairs, mirror the half-row of 8: the same
+// pattern as the first three steps of the wavefront sum), not with LDS
+// permutes; a lane maximum is never NaN, so a plain max is exact there.  The
+// clamp is done on the float before the conversion (NaN replaced first), so
+// it compiles to selects, not branches.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
 __device__ __forceinline__ uint32_t q8_quant4(const floatx4 &v, float *d_out) {
     float amax = 0.f;
 #pragma unroll
@@ -379,11 +390,9 @@ __device__ __forceinline__ uint32_t q8_quant4(const floatx4 &v, float *d_out) {
         const float a = fabsf(v[i]);
         amax = a > amax ? a : amax;
     }
-#pragma unroll
-    for (int o = 1; o < 8; o <<= 1) {
-        const float a = __shfl_xor(amax, o, 64);
-        amax = a > amax ? a : amax;
-    }
+    amax = fmaxf(amax, dpp_f<0xB1>(amax));   // quad_perm 1,0,3,2
+    amax = fmaxf(amax, dpp_f<0x4E>(amax));   // quad_perm 2,3,0,1
+    amax = fmaxf(amax, dpp_f<0x141>(amax));  // row_half_mirror
     const float d = amax / 127.0f;
     const float r = 1.0f / d;
     const float id = (d != 0.0f && __builtin_isfinite(r)) ? r : 0.0f;
@@ -391,8 +400,8 @@ __device__ __forceinline__ uint32_t q8_quant4(const floatx4 &v, float *d_out) {
 #pragma unroll
     for (int i = 0; i < 4; i++) {
         const float q = rintf(v[i] * id);
-        const int c = q != q ? 0 : (q < -128.0f ? -128 : (q > 127.0f ? 127 : (int)q));
-        packed |= ((uint32_t)c & 0xFFu) << (8 * i);
+        const float qc = q != q ? 0.0f : fminf(fmaxf(q, -128.0f), 127.0f);
+        packed |= ((uint32_t)(int)qc & 0xFFu) << (8 * i);
     }
     *d_out = d;
     return packed;
