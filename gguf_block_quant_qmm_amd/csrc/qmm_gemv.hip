@@ -383,7 +383,8 @@ template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
 }
-__device__ __forceinline__ uint32_t q8_quant4(const floatx4 &v, float *d_out) {
+// the block maximum of |v| over the 8 lanes of the block
+__device__ __forceinline__ float q8_block_amax(const floatx4 &v) {
     float amax = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
@@ -392,10 +393,14 @@ __device__ __forceinline__ uint32_t q8_quant4(const floatx4 &v, float *d_out) {
     }
     amax = fmaxf(amax, dpp_f<0xB1>(amax));   // quad_perm 1,0,3,2
     amax = fmaxf(amax, dpp_f<0x4E>(amax));   // quad_perm 2,3,0,1
-    amax = fmaxf(amax, dpp_f<0x141>(amax));  // row_half_mirror
-    const float d = amax / 127.0f;
+    return fmaxf(amax, dpp_f<0x141>(amax));  // row_half_mirror
+}
+__device__ __forceinline__ void q8_scale(float amax, float &d, float &id) {
+    d = amax / 127.0f;
     const float r = 1.0f / d;
-    const float id = (d != 0.0f && __builtin_isfinite(r)) ? r : 0.0f;
+    id = (d != 0.0f && __builtin_isfinite(r)) ? r : 0.0f;
+}
+__device__ __forceinline__ uint32_t q8_codes4(const floatx4 &v, float id) {
     uint32_t packed = 0;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
@@ -403,8 +408,34 @@ __device__ __forceinline__ uint32_t q8_quant4(const floatx4 &v, float *d_out) {
         const float qc = q != q ? 0.0f : fminf(fmaxf(q, -128.0f), 127.0f);
         packed |= ((uint32_t)(int)qc & 0xFFu) << (8 * i);
     }
-    *d_out = d;
     return packed;
+}
+__device__ __forceinline__ uint32_t q8_quant4(const floatx4 &v, float *d_out) {
+    float d, id;
+    q8_scale(q8_block_amax(v), d, id);
+    *d_out = d;
+    return q8_codes4(v, id);
+}
+// v of lane k of each group of 8 lanes, to all 8: a quad_perm broadcast of
+// lane k & 3 within each quad, then the other quad's copy by mirroring the
+// half-row
+template <int K>
+__device__ __forceinline__ float bcast8(float v) {
+    const float t = dpp_f<0x55 * (K & 3)>(v);
+    const float u = dpp_f<0x141>(t);
+    return (((threadIdx.x & 4) != 0) == (K >= 4)) ? t : u;
+}
+__device__ __forceinline__ float bcast8_k(float v, int k) {  // k a constant after unrolling
+    switch (k) {
+    case 0: return bcast8<0>(v);
+    case 1: return bcast8<1>(v);
+    case 2: return bcast8<2>(v);
+    case 3: return bcast8<3>(v);
+    case 4: return bcast8<4>(v);
+    case 5: return bcast8<5>(v);
+    case 6: return bcast8<6>(v);
+    default: return bcast8<7>(v);
+    }
 }
 
 __device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int acc) {
@@ -805,14 +836,29 @@ __global__ void __launch_bounds__(256) gemv_kernel(const GemvMats mats, int64_t 
         for (int s = 0; s < (FLAT ? D + 1 : D); s++) fetch(g0 + s, buf[s]);
         uint32_t *cs = reinterpret_cast<uint32_t *>(xs);
         float *ss = reinterpret_cast<float *>(cs + nf);
+        // every float4 round i quantizes one block per 8 lanes.  The block
+        // maxima of 8 rounds are gathered so that lane k of a group of 8
+        // holds round 8j + k's, one division pair serves all 8 rounds, that
+        // lane stores the block's scale, and the reciprocal goes back to the
+        // block's 8 lanes (same arithmetic as q8_quant4, one division per 8)
+        float am[QPT];
 #pragma unroll
-        for (int i = 0; i < QPT; i++) {
-            const int f = t + i * (int)blockDim.x;
-            float d;
-            const uint32_t packed = q8_quant4(xr[i], &d);
-            if (f < nf) {
-                cs[f] = packed;
-                if ((f & 7) == 0) ss[f >> 3] = (float)(_Float16)d;
+        for (int i = 0; i < QPT; i++) am[i] = q8_block_amax(xr[i]);
+        const int k8 = lane & 7;
+#pragma unroll
+        for (int j = 0; j < (QPT + 7) / 8; j++) {
+            float g = 0.f;
+#pragma unroll
+            for (int k = 0; k < 8 && 8 * j + k < QPT; k++) g = k8 == k ? am[8 * j + k] : g;
+            float d, id;
+            q8_scale(g, d, id);
+            const int fb = (t & ~7) + (8 * j + k8) * (int)blockDim.x;  // first float4 of that block
+            if (8 * j + k8 < QPT && fb < nf) ss[fb >> 3] = (float)(_Float16)d;
+#pragma unroll
+            for (int k = 0; k < 8 && 8 * j + k < QPT; k++) {
+                const int i = 8 * j + k, f = t + i * (int)blockDim.x;
+                const uint32_t packed = q8_codes4(xr[i], bcast8_k(id, k));
+                if (f < nf) cs[f] = packed;
             }
         }
         __syncthreads();

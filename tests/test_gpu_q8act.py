@@ -260,6 +260,45 @@ def test_gemv_q8act_is_quantize_then_q8act(dt):
         check(y[None, :], Y64, Sp, f"{NAME[dt]} gemv_q8act M={M} K={K}")
 
 
+def special_blocks(rng):
+    # 32-activation blocks whose scales stay finite in f16: all zeros, a NaN
+    # element (skipped by the maximum, code 0), a subnormal scale (1/d
+    # overflows: codes 0), a tiny normal scale, rounding ties, an
+    # f16-subnormal scale
+    base = rng.standard_normal(32).astype(np.float32)
+    out = [np.zeros(32, np.float32)]
+    r = base.copy(); r[3] = np.nan; out.append(r)
+    r = base.copy(); r[0] = np.nan; r[31] = np.nan; out.append(r)
+    out.append(base * np.float32(1e-39))
+    out.append(base * np.float32(1e-30))
+    r = np.arange(32, dtype=np.float32) - np.float32(15.5); r[0] = 127.0; out.append(r)
+    out.append(np.full(32, -3.0e-5, np.float32))
+    return out
+
+
+@pytest.mark.parametrize("dt", [q.QMM_Q4_0, q.QMM_Q8_0, q.QMM_Q4_K, q.QMM_Q6_K], ids=NAME.get)
+def test_gemv_q8act_special_activations(dt):
+    # special blocks spread over x so that they land in every lane of an
+    # 8-lane block group and in every quantization round of a thread, for
+    # whole-row wavefronts (K = 4096) and K-split workgroups (K = 16384): the
+    # in-launch quantizer must give the standalone quantizer's bits
+    for i, K in enumerate((4096, 16384)):
+        M = 67
+        rng = rng_for(990 + dt, i)
+        blob = make_blob(dt, M, K, rng)
+        x = make_x(1, K, rng_for(990 + dt, 10 + i)).reshape(-1)
+        specials = special_blocks(rng)
+        for j, b in enumerate(range(1, K // 32, 3)):
+            x[32 * b:32 * b + 32] = specials[j % len(specials)]
+        blob_d, x_d = to_dev(blob), to_dev(x)
+        y = one_launch(dt, blob_d, M, K, x_d)
+        assert np.all(np.isfinite(y)), f"{NAME[dt]} K={K}: non-finite output"
+        assert same_bits(y, two_step(dt, blob_d, M, K, x_d)), f"{NAME[dt]} K={K}: not the two-step bits"
+        sc, qq = oracle.quantize_q8_0(x.reshape(1, K))
+        _, Y64, _, Sp = oracle.matmul_q8act(dt, blob, M, K, sc, qq)
+        check(y[None, :], Y64, Sp, f"{NAME[dt]} gemv_q8act special K={K}")
+
+
 @pytest.mark.parametrize("dt", DTYPES, ids=NAME.get)
 def test_gemv_concat_q8act(dt):
     K = 4 * bs_of(dt) * (4 if bs_of(dt) == 32 else 1)
