@@ -1400,7 +1400,14 @@ static hipError_t launch_fast(const GemvMats &mats, int64_t K, const float *x, h
     } else if (U <= 256) {
         const int W = (U + 63) / 64;
         const int lever = gemv_waves_lever();
-        const int64_t grid = std::min<int64_t>(nrg, (int64_t)cus * std::max(1, (lever ? lever : 8) / W));
+        // 8 wavefronts per CU; but with x quantized in the launch every
+        // workgroup quantizes all of it, and for Q4_0 and Q4_K with 3-4
+        // wavefronts per row one workgroup per CU is faster (4096 x 14336:
+        // Q4_0 10.3 against 12.3 us, Q4_K 10.8-11.1 against 13.0; 4096 x
+        // 12288 Q4_K 10.0 against 11.7; Q8_0 and Q6_K measured no better)
+        const bool q8_one = NT < 0 && (DT == QMM_Q4_0 || DT == QMM_Q4_K) && W >= 3;
+        const int per_cu = lever ? std::max(1, lever / W) : (q8_one ? 1 : std::max(1, 8 / W));
+        const int64_t grid = std::min<int64_t>(nrg, (int64_t)cus * per_cu);
         const int64_t per = nrg / grid, extra = nrg % grid;
         if (MODE == GEMV_ARGMAX && grid > ARGMAX_PARTS) return hipErrorInvalidConfiguration;
         if (grid_out) *grid_out = grid;

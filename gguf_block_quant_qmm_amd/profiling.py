@@ -173,6 +173,42 @@ def _mfma(args):
     print(f"| mean of {n} | {mean[0] * 100:.1f} % | {mean[1]:.2f} | {mean[2]:.3f} | {mean[3]:.1f} | {mean[4]:.1f} |")
 
 
+def _valu(args):
+    """VALU issue per launch shape: a wave64 VALU instruction occupies a SIMD
+    (16 lanes) for 4 cycles, so SQ_INSTS_VALU x 4 / (number of SIMDs) is the
+    SIMD time spent issuing VALU work, shown against the dispatch duration at
+    the given clocks.  Dispatches are grouped by grid size."""
+    rx = re.compile(args.key)
+    per = defaultdict(float)
+    meta = {}
+    for r in csv.DictReader(open(args.csv)):
+        if not rx.search(r["Kernel_Name"]) or r["Counter_Name"] != "SQ_INSTS_VALU":
+            continue
+        d = int(r["Dispatch_Id"])
+        per[d] += float(r["Counter_Value"])
+        meta[d] = (int(r["Grid_Size"]), int(r["Workgroup_Size"]),
+                   (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3)
+    if not per:
+        sys.exit("no matching dispatches")
+    names = dict(spec.split("=", 1) for spec in (args.name or []))
+    lo, hi = args.ghz
+    groups = defaultdict(list)
+    for d in sorted(per):
+        grid, wg, us = meta[d]
+        cyc = per[d] * 4 / args.simds  # VALU issue cycles per SIMD
+        groups[(grid, wg)].append((per[d] / (grid / 64), cyc, us))
+    print(f"| launch | workgroups x threads | dispatches | VALU instructions per wavefront | VALU cycles per SIMD "
+          f"| that at {hi:g} / {lo:g} GHz, us | dispatch us | VALU share of the dispatch |")
+    print("|---|---:|---:|---:|---:|---:|---:|---:|")
+    for (grid, wg), rows in groups.items():
+        n = len(rows)
+        per_wave, cyc, us = (sum(r[i] for r in rows) / n for i in range(3))
+        t_hi, t_lo = cyc / (hi * 1e3), cyc / (lo * 1e3)
+        label = names.get(str(grid), str(grid))
+        print(f"| {label} | {grid // wg} x {wg} | {n} | {per_wave:.0f} | {cyc:.0f} | {t_hi:.2f} / {t_lo:.2f} | {us:.2f} "
+              f"| {100 * t_hi / us:.0f}-{100 * t_lo / us:.0f} % |")
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd_name", required=True)
@@ -200,8 +236,14 @@ def main(argv=None):
     m.add_argument("--flops", type=float, required=True)
     m.add_argument("--simds", type=int, default=1024)
     m.add_argument("--xccs", type=int, default=8)
+    v = sub.add_parser("valu")
+    v.add_argument("--csv", required=True)
+    v.add_argument("--key", required=True)
+    v.add_argument("--name", action="append", help="GRID=label (grid size in threads)")
+    v.add_argument("--simds", type=int, default=1024)
+    v.add_argument("--ghz", type=float, nargs=2, default=(2.1, 2.4), help="clock range (low high)")
     a = ap.parse_args(argv)
-    {"copy": _copy, "stats": _stats, "traffic": _traffic, "mfma": _mfma}[a.cmd_name](a)
+    {"copy": _copy, "stats": _stats, "traffic": _traffic, "mfma": _mfma, "valu": _valu}[a.cmd_name](a)
 
 
 if __name__ == "__main__":

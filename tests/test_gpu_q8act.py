@@ -214,11 +214,14 @@ def test_quantize_then_matmul_on_device():
 # ------------------------------------- one-launch decode (quantize inside) ----
 
 def fused_shapes(dt):
-    # K <= 4096: whole-row wavefronts; beyond: K-split workgroups (max 16384)
+    # K <= 4096: whole-row wavefronts; beyond: K-split workgroups (max 16384).
+    # 1000 rows at K = 12288 or 14336 give the K-split workgroups several row
+    # groups each (a ring), with x quantized once per workgroup
     if bs_of(dt) == 32:
-        return [(1, 64), (5, 128), (67, 1024), (300, 4096), (50, 4160), (33, 14336), (9, 16384)]
+        return [(1, 64), (5, 128), (67, 1024), (300, 4096), (50, 4160), (33, 14336), (9, 16384), (1000, 14336)]
     # Q6_K needs an even super-block count per row
-    return [(1, 512 if dt == q.QMM_Q6_K else 256), (3, 512), (67, 1024), (300, 4096), (50, 8192), (9, 16384)]
+    return [(1, 512 if dt == q.QMM_Q6_K else 256), (3, 512), (67, 1024), (300, 4096), (50, 8192), (9, 16384),
+            (1000, 12288 if dt == q.QMM_Q6_K else 14336)]
 
 
 def test_gemv_q8act_rejects_odd_q6_k_blocks():
