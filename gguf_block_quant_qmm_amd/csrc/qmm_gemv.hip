@@ -1318,7 +1318,8 @@ static bool fast_layout_ok(int dtype, int64_t nb) {
 //     ring for 14336 x 4096 and for concatenated gate + up);
 //   * larger matrices: a ring per wavefront, 16 wavefronts per CU for Q4_0
 //     and Q8_0, else 8;
-//   * a workgroup splitting K: 8 wavefronts per CU.
+//   * a workgroup splitting K: 8 wavefronts per CU (one workgroup per CU
+//     for Q4_0 and Q4_K with x quantized in the launch; see launch_fast).
 // QMM_GEMV_WAVES_PER_CU = n (1..4096) replaces all of this with n per CU (a
 // tuning lever, read once).
 static int gemv_waves_lever() {
