@@ -752,8 +752,16 @@ __device__ __forceinline__ int64_t lo_of(const GemvMats &m, int i) {
 // only.  NT = -1: one token of f32 activations x, quantized to Q8_0 by the
 // workgroup itself (into LDS, the quantizer kernel's arithmetic, so the codes
 // are the ones qmm_quantize_q8_0 writes), then the int8 dots; every MODE.
+//
+// Workgroup size: 256 threads, except whole-row wavefronts with x quantized
+// in the launch (not Q6_K, whose head runs 4 wavefronts per CU): 512, so the
+// quantization of x, done once per workgroup, is shared by 8 wavefronts and
+// each thread quantizes 2 float4 rounds instead of 4.
+constexpr int gemv_block_threads(int dt, bool wave_rows, int nt) {
+    return (wave_rows && nt < 0 && dt != QMM_Q6_K) ? 512 : 256;
+}
 template <int DT, int R, int D, bool WAVE_ROWS, bool FLAT, int MODE, int NT>
-__global__ void __launch_bounds__(256) gemv_kernel(const GemvMats mats, int64_t row_bytes, int U,
+__global__ void __launch_bounds__(gemv_block_threads(DT, WAVE_ROWS, NT)) gemv_kernel(const GemvMats mats, int64_t row_bytes, int U,
                                                    const float *__restrict__ x, int64_t per_owner, int64_t extra,
                                                    const int8_t *__restrict__ xq, const float *__restrict__ xsc,
                                                    int64_t ntok) {
@@ -823,7 +831,8 @@ __global__ void __launch_bounds__(256) gemv_kernel(const GemvMats mats, int64_t 
     if constexpr (NT < 0) {
         // x f32 -> Q8_0 codes (dwords [0, 16U)) and scales (floats after
         // them) in LDS; eight consecutive threads share a block
-        constexpr int QPT = WAVE_ROWS ? 4 : 16;  // float4 of x per thread: 16 U <= QPT * blockDim
+        // float4 of x per thread: 16 U <= QPT * blockDim (U <= 64 with whole rows)
+        constexpr int QPT = WAVE_ROWS ? 1024 / gemv_block_threads(DT, WAVE_ROWS, NT) : 16;
         const int nf = 16 * U;
         const floatx4 *xg = reinterpret_cast<const floatx4 *>(x);
         floatx4 xr[QPT];
@@ -973,7 +982,7 @@ __global__ void __launch_bounds__(256) gemv_kernel(const GemvMats mats, int64_t 
     if constexpr (MODE == GEMV_ARGMAX) {
         // the best of the workgroup: lane 63 of every wavefront (whole rows) or
         // the reducing threads (split K) hold candidates
-        constexpr int NC = WAVE_ROWS ? 4 : RED_G * R;
+        constexpr int NC = WAVE_ROWS ? gemv_block_threads(DT, WAVE_ROWS, NT) / 64 : RED_G * R;
         __shared__ float cv[NC];
         __shared__ int cr[NC];
         const int c = WAVE_ROWS ? (lane == 63 ? wave : -1) : (t < NC ? t : -1);
@@ -1392,11 +1401,12 @@ static hipError_t launch_fast(const GemvMats &mats, int64_t K, const float *x, h
     const unsigned gy = NT > 0 ? (unsigned)((xq8.ntok + NT - 1) / NT) : 1u;
     if (U <= 64) {
         const int64_t waves = gemv_wave_owners(DT, nrg, cus, NT < 0);
-        const int64_t grid = (waves + 3) / 4, owners = grid * 4;
+        constexpr int WPB = gemv_block_threads(DT, true, NT) / 64;  // wavefronts per workgroup
+        const int64_t grid = (waves + WPB - 1) / WPB, owners = grid * WPB;
         const int64_t per = nrg / owners, extra = nrg % owners;
         if (MODE == GEMV_ARGMAX && grid > ARGMAX_PARTS) return hipErrorInvalidConfiguration;
         if (grid_out) *grid_out = grid;
-        launch_variant<DT, R, D, true, MODE, NT>(per + (extra ? 1 : 0), dim3((unsigned)grid, gy), dim3(256), lds, st,
+        launch_variant<DT, R, D, true, MODE, NT>(per + (extra ? 1 : 0), dim3((unsigned)grid, gy), dim3(64 * WPB), lds, st,
                                                  mats, row_bytes, U, x, per, extra, xq8);
     } else if (U <= 256) {
         const int W = (U + 63) / 64;
