@@ -673,7 +673,8 @@ __device__ __forceinline__ void x_from_lds(const floatx4 *xs, int u, float (&xv)
 }
 
 // ------------------------------------------------------------ fast kernel ----
-// WAVE_ROWS: K <= 4096, 4 independent wavefronts per workgroup, each with its
+// WAVE_ROWS: K <= 4096, independent wavefronts (4 per workgroup; 8 for most
+// int8 one-launch calls, see gemv_block_threads), each with its
 // own range of row groups.  Otherwise the workgroup's ceil(U/64) wavefronts
 // split K and reduce each row group through LDS.  D row groups are in flight
 // while one is decoded (a ring of D+1 register buffers, unrolled so that no
