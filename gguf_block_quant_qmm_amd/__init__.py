@@ -44,7 +44,7 @@ QMM_ARGMAX_WORK_BYTES = 32768
 
 EXPORTS = ("qmm_gemv", "qmm_gemv_concat", "qmm_gemv_swiglu", "qmm_gemv_argmax", "qmm_gemm", "qmm_gemm_swiglu",
            "qmm_quantize_q8_0", "qmm_gemm_q8act", "qmm_gemv_q8act", "qmm_gemv_concat_q8act",
-           "qmm_gemv_swiglu_q8act", "qmm_gemv_argmax_q8act", "qmm_gemm_path", "qmm_blob_bytes", "qmm_block_elems",
+           "qmm_gemv_swiglu_q8act", "qmm_gemv_argmax_q8act", "qmm_gemm_path", "qmm_gemm_kernel", "qmm_blob_bytes", "qmm_block_elems",
            "qmm_block_bytes", "qmm_strerror")
 
 _lib = None
@@ -90,6 +90,8 @@ def lib():
         L.qmm_gemv_argmax_q8act.restype = ci
         L.qmm_gemm_path.argtypes = [ci, i64, i64, i64]
         L.qmm_gemm_path.restype = ci
+        L.qmm_gemm_kernel.argtypes = [ci, i64, i64, i64]
+        L.qmm_gemm_kernel.restype = ci
         L.qmm_blob_bytes.argtypes = [ci, i64, i64]
         L.qmm_blob_bytes.restype = i64
         L.qmm_block_elems.argtypes = [ci]
@@ -118,6 +120,14 @@ def blob_bytes(dtype: int, M: int, K: int) -> int:
 
 def gemm_path(dtype: int, M: int, K: int, N: int) -> int:
     return lib().qmm_gemm_path(dtype, M, K, N)
+
+
+QMM_KERNEL_GEMV, QMM_KERNEL_GEMV_TOKENS = 100, 101
+
+
+def gemm_kernel(dtype: int, M: int, K: int, N: int) -> int:
+    """Id of the kernel qmm_gemm runs for these sizes (see include/qmm.h)."""
+    return lib().qmm_gemm_kernel(dtype, M, K, N)
 
 
 def tolerance(dtype: int, M: int, K: int, N: int) -> float:

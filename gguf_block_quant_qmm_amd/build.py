@@ -20,7 +20,6 @@ HIPCC_FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     # no packed-f32 VALU instructions in generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
@@ -30,22 +29,45 @@ def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
 
 
-def build(verbose: bool = False) -> str:
-    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIB + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
-           *sources(), "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
+    return subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)
+
+
+def _finish(p, verbose):
+    _, err = p.communicate()
     noise = "is not a recognized feature for this target"
-    err = "\n".join(l for l in (res.stderr or "").splitlines() if noise not in l)
-    if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
+    err = "\n".join(l for l in (err or "").splitlines() if noise not in l)
+    if p.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({p.returncode}):\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+
+
+def build(verbose: bool = False, out: str | None = None, defines: list[str] | None = None) -> str:
+    """Compile every source (in parallel, one object each) and link libqmm.so.
+
+    out: another path for the library; defines: extra -D flags (e.g. QMM_TUNING
+    for a measurement build that reads its tuning levers from the environment).
+    """
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    lib = out or LIB
+    objdir = os.path.join(ROOT, "_build", os.path.basename(lib) + ".obj")
+    os.makedirs(objdir, exist_ok=True)
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc")]
+    dflags = [f"-D{d}" for d in (defines or [])]
+    objs, procs = [], []
+    for src in sources():
+        obj = os.path.join(objdir, os.path.basename(src) + ".o")
+        objs.append(obj)
+        procs.append(_run([hipcc, *HIPCC_FLAGS, *dflags, *inc, "-c", src, "-o", obj], verbose))
+    for p in procs:
+        _finish(p, verbose)
+    tmp = lib + ".tmp"
+    _finish(_run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose), verbose)
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

@@ -4,7 +4,6 @@
 
 #include <atomic>
 #include <cstdint>
-#include <cstdlib>
 #include <cstring>
 #include <mutex>
 
@@ -59,8 +58,9 @@ int check_shape(int dtype, int64_t M, int64_t K, int64_t N) {
 
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
-// Current device must be gfx950; returns its compute-unit count through *cus.
-int current_device(int *cus) {
+// Current device must be gfx950; returns its compute-unit count through *cus
+// (and its index through *dev_out).
+int current_device(int *cus, int *dev_out = nullptr) {
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return QMM_ERR_DEVICE;
     DeviceInfo &d = g_dev[dev];
@@ -79,6 +79,7 @@ int current_device(int *cus) {
     }
     if (st != 1) return QMM_ERR_DEVICE;
     *cus = d.cus;
+    if (dev_out) *dev_out = dev;
     return QMM_OK;
 }
 
@@ -92,11 +93,11 @@ int current_device(int *cus) {
 //     to 2 for Q4_K (17 vs 21 us at N = 2, 21 vs 20 us at N = 3);
 //   * elsewhere one GEMV launch per token: two tie with the GEMM at N = 2
 //     for Q4_0 and beat it for Q6_K; for Q8_0 and Q4_K the GEMM already wins.
-// QMM_GEMM_MFMA_FROM_N = n overrides it (a measurement lever, read once).
+// A measurement build (QMM_TUNING) takes QMM_GEMM_MFMA_FROM_N = n to move it;
+// the shipped library reads no environment.
 int64_t mfma_from_n(int dtype, int64_t M, int64_t K) {
     static const int64_t lever = [] {
-        const char *e = getenv("QMM_GEMM_MFMA_FROM_N");
-        const long v = e ? atol(e) : 0;
+        const int v = qmm::tuning_lever("QMM_GEMM_MFMA_FROM_N", 0);
         return (int64_t)(v >= 1 && v <= 1024 ? v : 0);
     }();
     if (lever) return lever;
@@ -140,6 +141,14 @@ int qmm_gemm_path(int dtype, int64_t M, int64_t K, int64_t N) {
     const int rc = check_shape(dtype, M, K, N);
     if (rc != QMM_OK) return rc;
     return N >= mfma_from_n(dtype, M, K) ? 1 : 0;
+}
+
+int qmm_gemm_kernel(int dtype, int64_t M, int64_t K, int64_t N) {
+    const int rc = check_shape(dtype, M, K, N);
+    if (rc != QMM_OK) return rc;
+    if (N < mfma_from_n(dtype, M, K))
+        return (N > 1 && qmm::gemv_tokens_ok(dtype, K)) ? QMM_KERNEL_GEMV_TOKENS : QMM_KERNEL_GEMV;
+    return qmm::gemm_kernel_choice(dtype, M, K, N);
 }
 
 int qmm_gemv(const void *w_blob, int dtype, int64_t M, int64_t K, const float *x, float *y, void *stream) {

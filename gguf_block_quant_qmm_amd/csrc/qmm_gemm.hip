@@ -19,8 +19,6 @@
 //     consecutive lanes hit distinct banks.
 // Each weight is rounded once to f16 from its exact value (Q4_K: from the
 // f32 fma(d*sc, q, -dmin*m)); activations are rounded to nearest f16.
-#include <cstdlib>
-
 #include "qmm_device.hpp"
 #include "qmm_internal.hpp"
 
@@ -1096,73 +1094,92 @@ static hipError_t launch_wb(const uint8_t *blob, int64_t M, int64_t K, int64_t N
     return hipGetLastError();
 }
 
+// Kernel ids (gemm_kernel_choice): the LDS-staged kernel, the register-B
+// kernel at three tile shapes, the skinny split-K kernel at four.
+enum {
+    GEMM_K_LDS = 0,       // gemm_kernel: weights decoded into an LDS tile
+    GEMM_K_WB_8x128 = 1,  // gemm_wb_kernel, 8 wavefronts x 32 rows x 128 tokens
+    GEMM_K_WB_4x64 = 2,   // gemm_wb_kernel, 4 wavefronts x 32 rows x 64 tokens
+    GEMM_K_WB_4x32 = 3,   // gemm_wb_kernel, 4 wavefronts x 32 rows x 32 tokens
+    GEMM_K_SK = 4,        // gemm_sk_kernel, 32 rows x 32 tokens
+    GEMM_K_SK_FM2 = 5,    // gemm_sk_kernel, 64 rows x 32 tokens
+    GEMM_K_SK_64 = 6,     // gemm_sk_kernel, 32 rows x 64 tokens
+    GEMM_K_SK_FM2_64 = 7, // gemm_sk_kernel, 64 rows x 64 tokens
+    GEMM_K_COUNT = 8
+};
+
 // Kernel choice (measured on 4096 x 4096 and 14336 x 4096 weights):
 //   * the skinny split-K kernel (32 rows x 32 tokens, 4 wavefronts splitting
 //     K) when the 32 x 32 tile grid is small, or N <= 32 with at most 1024
 //     row tiles -- small N leaves too few row x token tiles to fill the chip
 //     otherwise; taller matrices (a 128256-row head) have tiles enough and
 //     run 4 x 32 rows x 32 tokens without the split (240 vs 300 us there);
+//   * the skinny kernel with two 32-row fragments per wavefront for N <= 32
+//     when that still gives >= 192 workgroups (half the activation traffic);
+//   * for N > 32, the skinny kernel with 64-token tiles (32 or 64 rows) when
+//     it fits one round of <= 256 workgroups and the 32-token tile does not
+//     (4096 x 4096 Q4_K N = 128: 32-row tiles 20.7 vs 23.8 us; N = 256:
+//     64-row tiles 28.6 vs 35.4 us; 14336 x 4096 N = 64: 30.2 vs 36.6 us);
 //   * the buffered kernel with 8 wavefronts x 32 rows x 128 tokens when that
 //     grid nearly fills the chip, else 4 x 32 rows x 64 tokens;
 //   * the LDS-staged kernel when the layout rules the others out (K not a
 //     multiple of 256, odd block counts).
-//   * the skinny kernel with two 32-row fragments per wavefront for N <= 32
-//     when that still gives >= 192 workgroups (half the activation traffic);
-//   * for N > 32, the skinny kernel with 64-token tiles (32 or 64 rows) when
-//     it fits one round of <= 256 workgroups and the 32-token tile does not;
-// QMM_GEMM_KERNEL = 0 / 1 / 2 / 3 / 4 / 5 / 6 / 7 forces LDS-staged /
-// 8x32x128 / 4x32x64 / 4x32x32 / skinny / skinny with two row fragments /
-// skinny 32 x 64 tokens / skinny 64 x 64 tokens where the layout allows (a
-// measurement lever, read once).
-static int gemm_kernel_choice() {
-    static int v = [] {
-        const char *e = getenv("QMM_GEMM_KERNEL");
-        return e ? atoi(e) : -1;
-    }();
-    return v;
+// A measurement build (QMM_TUNING) takes QMM_GEMM_KERNEL = an id to force
+// where the layout allows.
+template <int DT>
+static int choice_dt(int64_t M, int64_t K, int64_t N) {
+    const bool gen = !aligned_layout(DT, K / Geo<DT>::BS);
+    // buffer resources cover at most 128 token rows of X: 32-bit byte counts
+    const bool wb_ok = !gen && (K % (4 * BK)) == 0 && K * 4 * 128 < ((int64_t)1 << 31);
+    const bool sk_ok = wb_ok && (K / BK) % 16 == 0;  // 4 wavefronts x whole super-blocks
+    int choice = tuning_lever("QMM_GEMM_KERNEL", -1);
+    if (choice >= GEMM_K_SK && choice < GEMM_K_COUNT && !sk_ok) choice = -1;
+    if (choice > GEMM_K_LDS && choice < GEMM_K_COUNT && !wb_ok) choice = -1;
+    if (choice >= 0 && choice < GEMM_K_COUNT) return choice;
+    const int64_t mt32 = (M + 31) / 32, mt64 = (M + 63) / 64, nt32 = (N + 31) / 32, nt64 = (N + 63) / 64;
+    if (!wb_ok) return GEMM_K_LDS;
+    if (sk_ok && N > 32 && mt32 * nt32 > 256 && mt32 * nt64 <= 256) return GEMM_K_SK_64;
+    if (sk_ok && N > 32 && mt32 * nt32 > 256 && mt64 * nt64 <= 256) return GEMM_K_SK_FM2_64;
+    if (sk_ok && ((N <= 32 && mt32 <= 1024) || mt32 * nt32 <= 512))
+        // two row fragments per wavefront halve the activation traffic
+        // where they still give >= 192 workgroups (14336 x 4096 Q4_K:
+        // N = 32 21.3 vs 26.1 us, N = 16 19.0 vs 22.7 us; on 4096 rows
+        // the 64 workgroups leave CUs idle: 20.3 vs 13.6 us)
+        return (N <= 32 && mt64 >= 192) ? GEMM_K_SK_FM2 : GEMM_K_SK;
+    if (N <= 32) return GEMM_K_WB_4x32;
+    if (((M + 255) / 256) * ((N + 127) / 128) >= 200) return GEMM_K_WB_8x128;
+    return GEMM_K_WB_4x64;
 }
 
 template <int DT>
 static hipError_t launch_dt(const uint8_t *blob, int64_t M, int64_t K, int64_t N, const float *X, float *Y,
                             hipStream_t st) {
     const bool gen = !aligned_layout(DT, K / Geo<DT>::BS);
-    // buffer resources cover at most 128 token rows of X: 32-bit byte counts
-    const bool wb_ok = !gen && (K % (4 * BK)) == 0 && K * 4 * 128 < ((int64_t)1 << 31);
-    const bool sk_ok = wb_ok && (K / BK) % 16 == 0;  // 4 wavefronts x whole super-blocks
-    int choice = gemm_kernel_choice();
-    if (choice >= 4 && choice <= 7 && !sk_ok) choice = -1;
-    if (choice < 0 || choice > 7 || (choice > 0 && !wb_ok)) {
-        // split-K tiles of 64 tokens (one wavefront per SIMD) pay where they
-        // give one round of <= 256 workgroups and the 32-token tile would not
-        // (4096 x 4096 Q4_K N = 128: 32-row tiles 20.7 vs 23.8 us; N = 256:
-        // 64-row tiles 28.6 vs 35.4 us; 14336 x 4096 N = 64: 30.2 vs 36.6 us)
-        const int64_t mt32 = (M + 31) / 32, mt64 = (M + 63) / 64, nt32 = (N + 31) / 32, nt64 = (N + 63) / 64;
-        if (!wb_ok) choice = 0;
-        else if (sk_ok && N > 32 && mt32 * nt32 > 256 && mt32 * nt64 <= 256) choice = 6;
-        else if (sk_ok && N > 32 && mt32 * nt32 > 256 && mt64 * nt64 <= 256) choice = 7;
-        else if (sk_ok && ((N <= 32 && (M + 31) / 32 <= 1024) || ((M + 31) / 32) * ((N + 31) / 32) <= 512))
-            // two row fragments per wavefront halve the activation traffic
-            // where they still give >= 192 workgroups (14336 x 4096 Q4_K:
-            // N = 32 21.3 vs 26.1 us, N = 16 19.0 vs 22.7 us; on 4096 rows
-            // the 64 workgroups leave CUs idle: 20.3 vs 13.6 us)
-            choice = (N <= 32 && (M + 63) / 64 >= 192) ? 5 : 4;
-        else if (N <= 32) choice = 3;
-        else if (((M + 255) / 256) * ((N + 127) / 128) >= 200) choice = 1;
-        else choice = 2;
-    }
-    switch (choice) {
-    case 1: return launch_wb<DT, 32, 128, 2, 8, 4, 2>(blob, M, K, N, X, Y, st);
-    case 2: return launch_wb<DT, 32, 64, 4, 4, 0, 4>(blob, M, K, N, X, Y, st);
-    case 3: return launch_wb<DT, 32, 32, 4, 4, 0, 4>(blob, M, K, N, X, Y, st);
-    case 4: return launch_sk<DT, 32, 4, 2, 2>(blob, M, K, N, X, Y, st);
-    case 5: return launch_sk<DT, 32, 4, 2, 2, 2>(blob, M, K, N, X, Y, st);
-    case 6: return launch_sk<DT, 64, 4, 2, 2, 1>(blob, M, K, N, X, Y, st);
-    case 7: return launch_sk<DT, 64, 4, 2, 2, 2>(blob, M, K, N, X, Y, st);
+    switch (choice_dt<DT>(M, K, N)) {
+    case GEMM_K_WB_8x128: return launch_wb<DT, 32, 128, 2, 8, 4, 2>(blob, M, K, N, X, Y, st);
+    case GEMM_K_WB_4x64: return launch_wb<DT, 32, 64, 4, 4, 0, 4>(blob, M, K, N, X, Y, st);
+    case GEMM_K_WB_4x32: return launch_wb<DT, 32, 32, 4, 4, 0, 4>(blob, M, K, N, X, Y, st);
+    case GEMM_K_SK: return launch_sk<DT, 32, 4, 2, 2>(blob, M, K, N, X, Y, st);
+    case GEMM_K_SK_FM2: return launch_sk<DT, 32, 4, 2, 2, 2>(blob, M, K, N, X, Y, st);
+    case GEMM_K_SK_64: return launch_sk<DT, 64, 4, 2, 2, 1>(blob, M, K, N, X, Y, st);
+    case GEMM_K_SK_FM2_64: return launch_sk<DT, 64, 4, 2, 2, 2>(blob, M, K, N, X, Y, st);
     default: break;
     }
     if (N <= 32) return launch_tile<DT, 128, 32, 1, 4>(blob, M, K, N, X, Y, st, gen);
     if (N <= 64) return launch_tile<DT, 128, 64, 1, 4>(blob, M, K, N, X, Y, st, gen);
     return launch_tile<DT, 128, 128, 2, 2>(blob, M, K, N, X, Y, st, gen);
+}
+
+int gemm_kernel_choice(int dtype, int64_t M, int64_t K, int64_t N) {
+    switch (dtype) {
+    case QMM_Q4_0: return choice_dt<QMM_Q4_0>(M, K, N);
+    case QMM_Q4_1: return choice_dt<QMM_Q4_1>(M, K, N);
+    case QMM_Q8_0: return choice_dt<QMM_Q8_0>(M, K, N);
+    case QMM_Q4_K: return choice_dt<QMM_Q4_K>(M, K, N);
+    case QMM_Q5_K: return choice_dt<QMM_Q5_K>(M, K, N);
+    case QMM_Q6_K: return choice_dt<QMM_Q6_K>(M, K, N);
+    default: return -1;
+    }
 }
 
 // The gate/up projection with SwiGLU on the matrix cores: 4 wavefronts x 32
@@ -1174,10 +1191,7 @@ bool gemm_swiglu_ok(int dtype, int64_t K) {
 }
 
 static int swiglu_choice() {
-    static int v = [] {
-        const char *e = getenv("QMM_SWIGLU_KERNEL");
-        return e ? atoi(e) : 0;
-    }();
+    static const int v = tuning_lever("QMM_SWIGLU_KERNEL", 0);
     return v;
 }
 
@@ -1190,8 +1204,8 @@ static int swiglu_choice() {
 //   beyond:           BN = 128  (N = 512: 201 vs 176 us: the one case where
 //                     two GEMMs plus a separate pass would be faster, given
 //                     scratch for both projections)
-// QMM_SWIGLU_KERNEL = 1..4 forces BN = 32 / 64 / 128 / 64 with 8 wavefronts
-// (a measurement lever, read once).
+// A measurement build (QMM_TUNING) takes QMM_SWIGLU_KERNEL = 1..4 to force
+// BN = 32 / 64 / 128 / 64 with 8 wavefronts.
 template <int DT>
 static hipError_t launch_swiglu_dt(const uint8_t *g, const uint8_t *u, int64_t M, int64_t K, int64_t N,
                                    const float *X, float *Y, hipStream_t st) {

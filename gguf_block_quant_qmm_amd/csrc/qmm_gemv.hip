@@ -1330,12 +1330,11 @@ static bool fast_layout_ok(int dtype, int64_t nb) {
 //     and Q8_0, else 8;
 //   * a workgroup splitting K: 8 wavefronts per CU (one workgroup per CU
 //     for Q4_0 and Q4_K with x quantized in the launch; see launch_fast).
-// QMM_GEMV_WAVES_PER_CU = n (1..4096) replaces all of this with n per CU (a
-// tuning lever, read once).
+// A measurement build (QMM_TUNING) takes QMM_GEMV_WAVES_PER_CU = n (1..4096)
+// to replace all of this with n per CU.
 static int gemv_waves_lever() {
-    static int v = [] {
-        const char *e = getenv("QMM_GEMV_WAVES_PER_CU");
-        const int n = e ? atoi(e) : 0;
+    static const int v = [] {
+        const int n = tuning_lever("QMM_GEMV_WAVES_PER_CU", 0);
         return (n >= 1 && n <= 4096) ? n : 0;
     }();
     return v;

@@ -3,8 +3,23 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 namespace qmm {
+
+// Tuning levers.  A measurement build (compiled with -DQMM_TUNING) reads
+// them from the environment, once per process; the shipped library reads no
+// environment at all and always takes the measured default, so a caller's
+// environment can never move a call to another kernel or another tolerance.
+inline int tuning_lever(const char *name, int dflt) {
+#ifdef QMM_TUNING
+    const char *e = getenv(name);
+    return e ? atoi(e) : dflt;
+#else
+    (void)name;
+    return dflt;
+#endif
+}
 
 // y[M] = W x, f32 arithmetic.  `cus` = compute units of the current device.
 hipError_t launch_gemv(int dtype, const void *blob, int64_t M, int64_t K, const float *x, float *y,
@@ -38,6 +53,10 @@ hipError_t launch_gemv_tokens(int dtype, const void *blob, int64_t M, int64_t K,
 bool gemm_swiglu_ok(int dtype, int64_t K);
 hipError_t launch_gemm_swiglu(int dtype, const void *gate, const void *up, int64_t M, int64_t K, int64_t N,
                               const float *X, float *Y, hipStream_t st);
+
+// Which matrix-core kernel launch_gemm_mfma runs for these sizes (one of the
+// GEMM_K_* ids in qmm_gemm.hip), or -1 if dtype is unknown.
+int gemm_kernel_choice(int dtype, int64_t M, int64_t K, int64_t N);
 
 // Y[N][M] = X W^T on the matrix cores (f16 operands, f32 accumulation).
 hipError_t launch_gemm_mfma(int dtype, const void *blob, int64_t M, int64_t K, int64_t N, const float *X,

@@ -270,6 +270,18 @@ int qmm_gemv_argmax_q8act(const void *w_blob, int dtype, int64_t M, int64_t K, c
  * 1 = f16 matrix-core GEMM, or a negative status for invalid arguments. */
 int qmm_gemm_path(int dtype, int64_t M, int64_t K, int64_t N);
 
+/* Which kernel qmm_gemm launches for these sizes (a diagnostic: the tests use
+ * it to show that their shapes reach every kernel):
+ *   QMM_KERNEL_GEMV         the f32 GEMV, one launch per token
+ *   QMM_KERNEL_GEMV_TOKENS  the f32 GEMV arithmetic, up to 4 tokens per read
+ *                           of the weights
+ *   0 .. 99                 a matrix-core kernel (the id names the kernel and
+ *                           tile shape inside this library build)
+ *   < 0                     a status code for invalid arguments */
+#define QMM_KERNEL_GEMV 100
+#define QMM_KERNEL_GEMV_TOKENS 101
+int qmm_gemm_kernel(int dtype, int64_t M, int64_t K, int64_t N);
+
 /* Bytes of a blob of M rows x K weights; 0 if dtype or shape is invalid. */
 int64_t qmm_blob_bytes(int dtype, int64_t M, int64_t K);
 

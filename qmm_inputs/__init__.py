@@ -50,8 +50,11 @@ def _f16_bytes(vals_f32: np.ndarray) -> np.ndarray:
     return h.view(np.uint8).reshape(-1, 2)
 
 
-def make_blob(dtype: int, M: int, K: int, rng: np.random.Generator) -> np.ndarray:
-    """Random row-major blob of M rows x K weights, as a flat uint8 array."""
+def make_blob(dtype: int, M: int, K: int, rng: np.random.Generator, q8_full_range: bool = False) -> np.ndarray:
+    """Random row-major blob of M rows x K weights, as a flat uint8 array.
+
+    q8_full_range: Q8_0 codes drawn from the whole int8 range [-128, 127]
+    (the format allows -128; the workload distribution stops at -127)."""
     bs, bb = GEOMETRY[dtype]
     if K % bs:
         raise ValueError(f"K={K} is not a multiple of {bs}")
@@ -59,7 +62,8 @@ def make_blob(dtype: int, M: int, K: int, rng: np.random.Generator) -> np.ndarra
     blk = np.empty((nblk, bb), dtype=np.uint8)
     if dtype == Q8_0:
         blk[:, 0:2] = _f16_bytes(rng.uniform(0.002, 0.02, nblk).astype(np.float32))
-        blk[:, 2:34] = rng.integers(-127, 128, size=(nblk, 32), dtype=np.int8).view(np.uint8)
+        lo = -128 if q8_full_range else -127
+        blk[:, 2:34] = rng.integers(lo, 128, size=(nblk, 32), dtype=np.int8).view(np.uint8)
     elif dtype == Q4_0:
         blk[:, 0:2] = _f16_bytes(rng.uniform(0.005, 0.05, nblk).astype(np.float32))
         blk[:, 2:18] = rng.integers(0, 256, size=(nblk, 16), dtype=np.uint8)

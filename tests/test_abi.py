@@ -344,3 +344,26 @@ def test_argmax_q8act_without_gpu_reports_device():
     if torch.cuda.is_available():
         pytest.skip("a GPU is present; covered by the GPU tests")
     assert q.lib().qmm_gemv_argmax_q8act(A16, 14, 8, 4096, A16, A16, A16, None, None) == q.QMM_ERR_DEVICE
+
+
+def test_library_reads_no_tuning_environment():
+    """The shipped library takes no lever from the environment: a caller's
+    environment cannot move a call to another kernel or tolerance class."""
+    import subprocess
+    import sys
+    code = ("import gguf_block_quant_qmm_amd as q; "
+            "print(q.gemm_path(12, 14336, 4096, 1), q.gemm_path(12, 14336, 4096, 512), "
+            "q.gemm_kernel(12, 14336, 4096, 512), q.gemm_kernel(2, 300, 96, 40))")
+    env = dict(os.environ, PYTHONPATH=ROOT)
+    base = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, check=True).stdout
+    env.update(QMM_GEMM_MFMA_FROM_N="1", QMM_GEMM_KERNEL="0", QMM_SWIGLU_KERNEL="2", QMM_GEMV_WAVES_PER_CU="3")
+    lev = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, check=True).stdout
+    assert base == lev and base.split()[:2] == ["0", "1"]
+
+
+def test_gemm_kernel_reports_each_path():
+    assert q.gemm_kernel(q.QMM_Q4_K, 14336, 4096, 1) == q.QMM_KERNEL_GEMV
+    assert q.gemm_kernel(q.QMM_Q4_0, 4096, 4096, 3) == q.QMM_KERNEL_GEMV_TOKENS
+    assert 0 <= q.gemm_kernel(q.QMM_Q4_K, 14336, 4096, 512) < 100
+    assert q.gemm_kernel(q.QMM_Q4_K, 14336, 100, 512) == q.QMM_ERR_SHAPE
+    assert q.gemm_kernel(5, 14336, 4096, 512) == q.QMM_ERR_DTYPE

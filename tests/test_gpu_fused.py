@@ -237,7 +237,7 @@ def run_argmax(dt, blob_d, M, K, x_d):
     return int(idx.item()), val.cpu().numpy()[0]
 
 
-def check_argmax(dt, blob, M, K, x, label, rows_sample=None):
+def check_argmax(dt, blob, M, K, x, label, rows_sample=None, full_rows=False):
     bd, xd = to_dev(blob), to_dev(x.reshape(-1))
     i, v = run_argmax(dt, bd, M, K, xd)
     y = gemv(dt, bd, M, K, xd).cpu().numpy()
@@ -248,6 +248,10 @@ def check_argmax(dt, blob, M, K, x, label, rows_sample=None):
     oi, obest, os_ = oracle.argmax(dt, blob, M, K, x)
     _, Y64, S = oracle.matmul(dt, blob, M, K, x, rows=[i])
     assert Y64[0, 0] >= obest - TAU * (S[0, 0] + os_), f"{label}: row {i} is not a maximum (oracle {oi})"
+    if full_rows:
+        # every output the argmax compared, against the oracle
+        _, Y64, S = oracle.matmul(dt, blob, M, K, x)
+        check_f32(y, Y64[0], S[0], f"{label}: qmm_gemv rows")
     return i, oi
 
 
@@ -294,7 +298,7 @@ def test_argmax_lm_head_full_size():
     dt, M, K = q.QMM_Q6_K, 128256, 4096
     blob = make_blob(dt, M, K, rng_for(5, 0))
     x = make_x(1, K, rng_for(5, 1))
-    i, oi = check_argmax(dt, blob, M, K, x, "Q6_K LM head argmax")
+    i, oi = check_argmax(dt, blob, M, K, x, "Q6_K LM head argmax", full_rows=True)
     _, Y64, S = oracle.matmul(dt, blob, M, K, x)
     top2 = np.sort(Y64[0])[-2:]
     if top2[1] - top2[0] > 2 * TAU * S.max():

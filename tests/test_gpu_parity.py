@@ -120,12 +120,14 @@ def test_gemm_small(dt, N):
         check(Yg, Y64, S, q.tolerance(dt, M, K, N), f"{NAME[dt]} gemm M={M} K={K} N={N}")
 
 
-@pytest.mark.parametrize("dt", [q.QMM_Q4_0, q.QMM_Q4_K, q.QMM_Q4_1, q.QMM_Q5_K], ids=NAME.get)
+@pytest.mark.parametrize("dt", DTYPES, ids=NAME.get)
 def test_gemm_register_b_kernel_ragged(dt):
-    # M/256 x N/128 >= 224 workgroups selects the register-B kernel for the
-    # 4-bit formats; M and N both end in partial tiles.  Sampled rows include
+    # M/256 x N/128 >= 200 workgroups selects the register-B kernel with 8
+    # wavefronts x 128 tokens for every dtype (K = 512 keeps the Q6_K block
+    # count even); M and N both end in partial tiles.  Sampled rows include
     # the last (partial) row tile.
     M, K, N = 7200, 512, 1000
+    assert q.gemm_kernel(dt, M, K, N) == 1
     blob = make_blob(dt, M, K, rng_for(650 + dt, 0))
     X = make_x(N, K, rng_for(650 + dt, 1))
     rows = np.unique(np.concatenate([sample_rows(M, 40, 650 + dt), np.arange(M - 40, M)]))
@@ -234,7 +236,9 @@ def test_workload_full_size(wid):
     blob_d = to_dev(blob)
     for N in ns:
         X = make_x(N, K, rng_for(wid, 1000 + N))
-        rows = sample_rows(M, 96 if N <= 64 else 48, wid * 7919 + N)
+        # one token: every row (the C oracle takes about a second even for the
+        # 128256-row head); several tokens: sampled rows
+        rows = np.arange(M) if N == 1 else sample_rows(M, 96 if N <= 64 else 48, wid * 7919 + N)
         _, Y64, S = oracle.matmul(dt, blob, M, K, X, rows=rows)
         Yg = gpu_gemv(dt, blob_d, M, K, X)[None, :] if N == 1 else gpu_gemm(dt, blob_d, M, K, X)
         assert np.all(np.isfinite(Yg)), f"{label} N={N}: non-finite output"
