@@ -14,6 +14,9 @@ there is no CPU fallback.
                                                      out = silu(W_gate x) * (W_up x)
     qmm_gemv_argmax(w, dtype, M, K, x, work, index, value=None, stream=None)
                                                      index = argmax_m (W x)[m]
+    qmm_gemv_argmax_noalloc(w, dtype, M, K, x, index, value=None, stream=None)
+                                                     the same, scratch in a static
+                                                     device array (no work buffer)
     qmm_gemm_swiglu(gate, up, dtype, M, K, N, X, out, stream=None)
                                                      out = silu(X Wg^T) * (X Wu^T)
     qmm_quantize_q8_0(X, N, K, scales, quants, stream=None)
@@ -37,12 +40,13 @@ QMM_Q4_0, QMM_Q4_1, QMM_Q8_0, QMM_Q4_K, QMM_Q5_K, QMM_Q6_K = 2, 3, 8, 12, 13, 14
 DTYPES = {"Q4_0": QMM_Q4_0, "Q4_1": QMM_Q4_1, "Q8_0": QMM_Q8_0, "Q4_K": QMM_Q4_K, "Q5_K": QMM_Q5_K,
           "Q6_K": QMM_Q6_K}
 QMM_OK, QMM_ERR_NULL, QMM_ERR_DTYPE, QMM_ERR_SHAPE = 0, -1, -2, -3
-QMM_ERR_ALIGN, QMM_ERR_DEVICE, QMM_ERR_LAUNCH = -4, -5, -6
+QMM_ERR_ALIGN, QMM_ERR_DEVICE, QMM_ERR_LAUNCH, QMM_ERR_SCRATCH = -4, -5, -6, -7
 
 QMM_GEMV_MAX_MATS = 4
 QMM_ARGMAX_WORK_BYTES = 32768
+QMM_NOALLOC_SCRATCH_BYTES = 32768
 
-EXPORTS = ("qmm_gemv", "qmm_gemv_concat", "qmm_gemv_swiglu", "qmm_gemv_argmax", "qmm_gemm", "qmm_gemm_swiglu",
+EXPORTS = ("qmm_gemv", "qmm_gemv_concat", "qmm_gemv_swiglu", "qmm_gemv_argmax", "qmm_gemv_argmax_noalloc", "qmm_gemm", "qmm_gemm_swiglu",
            "qmm_quantize_q8_0", "qmm_gemm_q8act", "qmm_gemv_q8act", "qmm_gemv_concat_q8act",
            "qmm_gemv_swiglu_q8act", "qmm_gemv_argmax_q8act", "qmm_gemm_path", "qmm_gemm_kernel", "qmm_blob_bytes", "qmm_block_elems",
            "qmm_block_bytes", "qmm_strerror")
@@ -72,6 +76,8 @@ def lib():
         L.qmm_gemv_swiglu.restype = ci
         L.qmm_gemv_argmax.argtypes = [vp, ci, i64, i64, vp, vp, vp, vp, vp]
         L.qmm_gemv_argmax.restype = ci
+        L.qmm_gemv_argmax_noalloc.argtypes = [vp, ci, i64, i64, vp, vp, vp, vp]
+        L.qmm_gemv_argmax_noalloc.restype = ci
         L.qmm_gemm_swiglu.argtypes = [vp, vp, ci, i64, i64, i64, vp, vp, vp]
         L.qmm_gemm_swiglu.restype = ci
         L.qmm_gemm.argtypes = [vp, ci, i64, i64, i64, vp, vp, vp]
@@ -214,6 +220,15 @@ def qmm_gemv_argmax(w, dtype: int, M: int, K: int, x, work, index, value=None, s
                                _stream(stream))
     if rc != QMM_OK:
         raise QmmError(rc, "qmm_gemv_argmax")
+
+
+def qmm_gemv_argmax_noalloc(w, dtype: int, M: int, K: int, x, index, value=None, stream=None) -> None:
+    import torch
+    rc = lib().qmm_gemv_argmax_noalloc(_addr(w, blob_bytes(dtype, M, K) or None, "w_blob"), dtype, M, K,
+                                       _addr(x, 4 * K, "x", torch.float32), _addr(index, 8, "index", torch.int64),
+                                       _addr(value, 4, "value", torch.float32), _stream(stream))
+    if rc != QMM_OK:
+        raise QmmError(rc, "qmm_gemv_argmax_noalloc")
 
 
 def qmm_gemm_swiglu(gate, up, dtype: int, M: int, K: int, N: int, X, out, stream=None) -> None:

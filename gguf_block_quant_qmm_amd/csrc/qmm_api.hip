@@ -83,6 +83,29 @@ int current_device(int *cus, int *dev_out = nullptr) {
     return QMM_OK;
 }
 
+// The scratch of the entry points that take no workspace (for callers that
+// cannot allocate): one array per GPU, held until the process ends.  Host code
+// never uses the array's name as an address (on the host it is only a
+// stand-in): the device address of each GPU's copy is looked up once, with
+// that GPU current, and kept in g_scratch.
+__device__ __attribute__((aligned(256))) unsigned char scratch[QMM_NOALLOC_SCRATCH_BYTES];
+std::atomic<void *> g_scratch[kMaxDevices];
+
+// The device address of the current GPU's scratch (dev = its index).
+int scratch_of(int dev, void **p) {
+    void *v = g_scratch[dev].load(std::memory_order_acquire);
+    if (!v) {
+        std::lock_guard<std::mutex> lk(g_dev_mu);
+        v = g_scratch[dev].load(std::memory_order_relaxed);
+        if (!v) {
+            if (hipGetSymbolAddress(&v, HIP_SYMBOL(scratch)) != hipSuccess || !v) return QMM_ERR_DEVICE;
+            g_scratch[dev].store(v, std::memory_order_release);
+        }
+    }
+    *p = v;
+    return QMM_OK;
+}
+
 // N at and above which the f16 matrix-core GEMM runs; below it the f32 GEMV
 // arithmetic runs for every token.  Measured on 4096-, 14336- and
 // 128256-row weights:
@@ -133,6 +156,7 @@ const char *qmm_strerror(int code) {
     case QMM_ERR_ALIGN: return "misaligned pointer (blob and x/X need 16-byte, y/Y 4-byte alignment)";
     case QMM_ERR_DEVICE: return "no current HIP device, or it is not gfx950";
     case QMM_ERR_LAUNCH: return "kernel launch failed";
+    case QMM_ERR_SCRATCH: return "the call needs more scratch than the library's static buffer holds";
     default: return "unknown status code";
     }
 }
@@ -208,6 +232,27 @@ int qmm_gemv_argmax(const void *w_blob, int dtype, int64_t M, int64_t K, const f
     rc = current_device(&cus);
     if (rc != QMM_OK) return rc;
     const hipError_t e = qmm::launch_gemv_argmax(dtype, w_blob, M, K, x, work, index, value, (hipStream_t)stream, cus);
+    return e == hipSuccess ? QMM_OK : QMM_ERR_LAUNCH;
+}
+
+int qmm_gemv_argmax_noalloc(const void *w_blob, int dtype, int64_t M, int64_t K, const float *x, int64_t *index,
+                            float *value, void *stream) {
+    int rc = check_shape(dtype, M, K, 1);
+    if (rc != QMM_OK) return rc;
+    if (M > INT32_MAX || !qmm::gemv_fused_ok(dtype, K)) return QMM_ERR_SHAPE;
+    if (!w_blob || !x || !index) return QMM_ERR_NULL;
+    if (!aligned(w_blob, 16) || !aligned(x, 16) || !aligned(index, 8) || (value && !aligned(value, 4)))
+        return QMM_ERR_ALIGN;
+    int cus = 0, dev = -1;
+    rc = current_device(&cus, &dev);
+    if (rc != QMM_OK) return rc;
+    void *work = nullptr;
+    rc = scratch_of(dev, &work);
+    if (rc != QMM_OK) return rc;
+    // the candidates of every valid shape fit (at most QMM_NOALLOC_SCRATCH_BYTES / 8
+    // workgroups); a launch that would need more is refused before it starts
+    const hipError_t e = qmm::launch_gemv_argmax(dtype, w_blob, M, K, x, work, index, value, (hipStream_t)stream, cus);
+    if (e == hipErrorInvalidConfiguration) return QMM_ERR_SCRATCH;
     return e == hipSuccess ? QMM_OK : QMM_ERR_LAUNCH;
 }
 

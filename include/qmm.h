@@ -82,6 +82,7 @@ extern "C" {
 #define QMM_ERR_ALIGN (-4)   /* blob not 16-B aligned, x/X not 16-B, y/Y not 4-B    */
 #define QMM_ERR_DEVICE (-5)  /* no current HIP device, or it is not gfx950          */
 #define QMM_ERR_LAUNCH (-6)  /* the kernel launch itself failed                     */
+#define QMM_ERR_SCRATCH (-7) /* needs more than the static scratch (no-alloc calls) */
 
 /* Decode GEMV (one token), page "cera 0.5.2 src/backend/cpu.rs", section
  * "GEMV (matrix-vector multiply)": y[m] = sum_k W[m][k] * x[k].
@@ -152,6 +153,22 @@ int qmm_gemv_swiglu(const void *gate_blob, const void *up_blob, int dtype, int64
 #define QMM_ARGMAX_WORK_BYTES 32768
 int qmm_gemv_argmax(const void *w_blob, int dtype, int64_t M, int64_t K, const float *x,
                     void *work, int64_t *index, float *value, void *stream);
+
+/* qmm_gemv_argmax without the work argument, for callers that cannot
+ * allocate device memory (code under graph capture, serving loops that may
+ * not call hipMalloc, harnesses that forbid it).  The workgroup candidates go
+ * to a static device array of QMM_NOALLOC_SCRATCH_BYTES that the library holds
+ * on every GPU it runs on until the process ends; nothing is allocated or
+ * freed by the call.  Results, arguments and errors are those of
+ * qmm_gemv_argmax (same kernels, bit-identical index and value); every valid
+ * shape fits the array, and a launch that would need more returns
+ * QMM_ERR_SCRATCH without launching.  All calls on one GPU share that GPU's
+ * array: calls that overlap in time on one GPU (two streams, two threads)
+ * race and must be serialised by the caller.  The array needs no initial
+ * value (each call writes every slot it reads). */
+#define QMM_NOALLOC_SCRATCH_BYTES 32768
+int qmm_gemv_argmax_noalloc(const void *w_blob, int dtype, int64_t M, int64_t K, const float *x,
+                            int64_t *index, float *value, void *stream);
 
 /* Prefill / verify GEMM over N tokens (page "cera 0.3.1 src/model/gpu_lfm2.rs",
  * mul_mat_reg_tile: weights decoded once per k-tile and reused across all
