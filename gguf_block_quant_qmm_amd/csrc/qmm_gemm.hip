@@ -407,32 +407,22 @@ __global__ void __launch_bounds__(256) gemm_kernel(const uint8_t *__restrict__ b
 constexpr float TWO24 = 16777216.0f;
 
 // Two weights (scale * code + bias, each rounded once to f16) from the two
-// f16 code lanes of a dword.  ASM: as one v_fma_mixlo_f16 / v_fma_mixhi_f16
-// pair (2 instructions); else as the compiler forms it (usually two f32
-// fma_mix and a pack).  Which is faster depends on the format (measured:
-// the pair for Q4_0, the compiler's form for Q4_K).
-template <bool ASM>
+// f16 code lanes of a dword.  Written as plain code (the compiler forms
+// v_fma_mix_f32 / v_fma_mixlo_f16 pairs and the conversions itself): an
+// inline-asm form hides its register writes from the compiler's hazard
+// checks next to the matrix-core instructions reading the same registers,
+// and was measured to give wrong sums in one register allocation.
 __device__ __forceinline__ uint32_t mix_pair(uint32_t codes, float scale, float bias) {
-    if constexpr (ASM) {
-        uint32_t r;
-        asm("v_fma_mixlo_f16 %0, %1, %2, %3 op_sel_hi:[1,0,0]\n\t"
-            "v_fma_mixhi_f16 %0, %1, %2, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
-            : "=&v"(r)
-            : "v"(codes), "v"(scale), "v"(bias));
-        return r;
-    } else {
-        const half2_t c = __builtin_bit_cast(half2_t, codes);
-        half2_t o;
-        o.x = (_Float16)fmaf((float)c.x, scale, bias);
-        o.y = (_Float16)fmaf((float)c.y, scale, bias);
-        return __builtin_bit_cast(uint32_t, o);
-    }
+    const half2_t c = __builtin_bit_cast(half2_t, codes);
+    half2_t o;
+    o.x = (_Float16)fmaf((float)c.x, scale, bias);
+    o.y = (_Float16)fmaf((float)c.y, scale, bias);
+    return __builtin_bit_cast(uint32_t, o);
 }
 // four weights from the two code pairs of a dword, into f[at .. at+4)
-template <bool ASM = true>
 __device__ __forceinline__ void quad(uint32_t p02, uint32_t p13, float scale, float bias, half8 &f, int at) {
-    const half2_t a = __builtin_bit_cast(half2_t, mix_pair<ASM>(p02, scale, bias));
-    const half2_t b = __builtin_bit_cast(half2_t, mix_pair<ASM>(p13, scale, bias));
+    const half2_t a = __builtin_bit_cast(half2_t, mix_pair(p02, scale, bias));
+    const half2_t b = __builtin_bit_cast(half2_t, mix_pair(p13, scale, bias));
     f[at] = a.x;
     f[at + 1] = a.y;
     f[at + 2] = b.x;
@@ -580,8 +570,8 @@ template <> struct PDec<QMM_Q4_K> {
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             const uint32_t w = r[4 + i], t = w >> 8;
-            quad<false>(w & 0x000F000Fu, t & 0x000F000Fu, s0, n0, f[i >> 1], 4 * (i & 1));
-            quad<false>(w & 0x00F000F0u, t & 0x00F000F0u, s1, n1, f[2 + (i >> 1)], 4 * (i & 1));
+            quad(w & 0x000F000Fu, t & 0x000F000Fu, s0, n0, f[i >> 1], 4 * (i & 1));
+            quad(w & 0x00F000F0u, t & 0x00F000F0u, s1, n1, f[2 + (i >> 1)], 4 * (i & 1));
         }
     }
 };
@@ -625,9 +615,9 @@ template <> struct PDec<QMM_Q5_K> {
         for (int i = 0; i < 4; i++) {
             const uint32_t w = r[4 + i], t = w >> 8;
             const uint32_t hq = r[8 + i] >> (2 * c), ht = hq >> 8;
-            quad<false>((w & 0x000F000Fu) | ((hq << 4) & 0x00100010u), (t & 0x000F000Fu) | ((ht << 4) & 0x00100010u),
+            quad((w & 0x000F000Fu) | ((hq << 4) & 0x00100010u), (t & 0x000F000Fu) | ((ht << 4) & 0x00100010u),
                         s0, n0, f[i >> 1], 4 * (i & 1));
-            quad<false>((w & 0x00F000F0u) | ((hq << 7) & 0x01000100u), (t & 0x00F000F0u) | ((ht << 7) & 0x01000100u),
+            quad((w & 0x00F000F0u) | ((hq << 7) & 0x01000100u), (t & 0x00F000F0u) | ((ht << 7) & 0x01000100u),
                         s1, n1, f[2 + (i >> 1)], 4 * (i & 1));
         }
     }
