@@ -91,7 +91,10 @@ def main():
     ap.add_argument("--headline-only", action="store_true",
                     help="time only the headline decode step and the prefill GEMM (profiler runs: every GEMV "
                          "launch then belongs to the headline step)")
+    ap.add_argument("--oracle-child", action="store_true", help=argparse.SUPPRESS)
     args = ap.parse_args()
+    if args.oracle_child:
+        return oracle_child()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
@@ -145,7 +148,7 @@ def main():
     def step_swiglu(c):
         (_, dq, Mq, Kq, _), (_, dg, Mg, Kg, _), _, (_, dd, Md, Kd, _) = mats
         q.qmm_gemv(copies[0][c], dq, Mq, Kq, xs[0], ys[0], stream=stream)
-        q.qmm_gemv_swiglu(copies[1][c], copies[2][c], dg, Mg, Kg, xs[1], swiglu_y, stream=stream)
+        q.qmm_gemv_swiglu(copies[1][c % R], copies[2][c % R], dg, Mg, Kg, xs[1], swiglu_y, stream=stream)
         q.qmm_gemv(copies[3][c], dd, Md, Kd, xs[3], ys[3], stream=stream)
 
     # int8 activations (the CPU page's Q8_0 decode path): the same three
@@ -153,7 +156,7 @@ def main():
     def step_q8act(c):
         (_, dq, Mq, Kq, _), (_, dg, Mg, Kg, _), _, (_, dd, Md, Kd, _) = mats
         q.qmm_gemv_q8act(copies[0][c], dq, Mq, Kq, xs[0], ys[0], stream=stream)
-        q.qmm_gemv_concat_q8act([copies[1][c], copies[2][c]], dg, [Mg, Mg], Kg, xs[1], gate_up_ys, stream=stream)
+        q.qmm_gemv_concat_q8act([copies[1][c % R], copies[2][c % R]], dg, [Mg, Mg], Kg, xs[1], gate_up_ys, stream=stream)
         q.qmm_gemv_q8act(copies[3][c], dd, Md, Kd, xs[3], ys[3], stream=stream)
 
     def time_layer(step):
@@ -191,34 +194,86 @@ def main():
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
         for s in range(args.steps):
-            fn(s % R)
+            fn(s)
         b.record(stream)
         torch.cuda.synchronize()
         us = a.elapsed_time(b) * 1e3 / args.steps
         return {"us": round(us, 3), "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1)}
 
+    # A GPU-side spin before each span keeps the queue ahead of the host: the
+    # binding enqueues a call in ~6 us, about the duration of the smallest
+    # launches, so without it a span of small kernels would time the host.
+    # The spin is calibrated to last about 1.5 ms and is outside the span.
+    t_a, t_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(1 << 20)
+    t_a.record(stream)
+    torch.cuda._sleep(1 << 20)
+    t_b.record(stream)
+    torch.cuda.synchronize()
+    sleep_cycles = int((1 << 20) * 1.5 / max(t_a.elapsed_time(t_b), 1e-3))
+
+    def spans(fn, n_spans=5, per_span=None):
+        """Per-call time (median, min) in us over n_spans separate spans of
+        per_span calls each, every span between its own two events with the
+        GPU queue kept ahead of the host (a calibrated spin before the span)."""
+        per_span = per_span or max(10, args.steps // n_spans)
+        out, c = [], 0
+        for _ in range(n_spans):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda._sleep(sleep_cycles)
+            a.record(stream)
+            for _ in range(per_span):
+                fn(c)
+                c += 1
+            b.record(stream)
+            torch.cuda.synchronize()
+            out.append(a.elapsed_time(b) * 1e3 / per_span)
+        return float(np.median(out)), float(np.min(out))
+
+    def read_probe_us(copies_list):
+        """A plain streaming read of the same bytes over the same rotated
+        copies (qmm_read_probe): the launch-size ceiling of a read."""
+        pout = torch.empty(q.QMM_READ_PROBE_OUT_FLOATS, device=dev)
+        return spans(lambda c: q.qmm_read_probe(copies_list[c % len(copies_list)],
+                                                copies_list[c % len(copies_list)].numel(), pout, stream=stream))[0]
+
+    def leg(fn, nbytes, probe_copies=None, flops=None):
+        r = time_calls(fn, nbytes)
+        med, mn = spans(fn)
+        r.update({"us_median": round(med, 3), "us_min": round(mn, 3),
+                  "GB/s_median": round(nbytes / (med * 1e-6) / 1e9, 1)})
+        if flops:
+            r["TFLOP/s_median"] = round(flops / (med * 1e-6) / 1e12, 2)
+        if probe_copies is not None:
+            p = read_probe_us(probe_copies)
+            r["read_probe_us"] = round(p, 3)
+            r["frac_of_read_probe"] = round(p / med, 3)
+        return r
+
     for i, (name, dt, M, K, _) in enumerate(mats if not args.headline_only else []):
-        per_matrix[name] = time_calls(lambda c, i=i, dt=dt, M=M, K=K: q.qmm_gemm(copies[i][c], dt, M, K, 1, xs[i], ys[i],
-                                                                                 stream=stream),
-                                      copies[i][0].numel())
+        per_matrix[name] = leg(lambda c, i=i, dt=dt, M=M, K=K: q.qmm_gemm(copies[i][c % R], dt, M, K, 1, xs[i], ys[i],
+                                                                          stream=stream),
+                               copies[i][0].numel(), probe_copies=copies[i])
     gu_bytes = copies[1][0].numel() + copies[2][0].numel()
     (_, dg, Mg, Kg, _) = mats[1]
     if not args.headline_only:
-        per_matrix["gate+up concat"] = time_calls(
-            lambda c: q.qmm_gemv_concat([copies[1][c], copies[2][c]], dg, [Mg, Mg], Kg, xs[1], gate_up_ys,
-                                        stream=stream), gu_bytes)
+        gu_probe = [torch.cat([copies[1][c], copies[2][c]]) for c in range(min(R, 4))]
+        per_matrix["gate+up concat"] = leg(
+            lambda c: q.qmm_gemv_concat([copies[1][c % R], copies[2][c % R]], dg, [Mg, Mg], Kg, xs[1], gate_up_ys,
+                                        stream=stream), gu_bytes, probe_copies=gu_probe)
+        del gu_probe
         per_matrix["gate+up swiglu"] = time_calls(
-            lambda c: q.qmm_gemv_swiglu(copies[1][c], copies[2][c], dg, Mg, Kg, xs[1], swiglu_y, stream=stream),
+            lambda c: q.qmm_gemv_swiglu(copies[1][c % R], copies[2][c % R], dg, Mg, Kg, xs[1], swiglu_y, stream=stream),
             gu_bytes)
         for i, (name, dt, M, K, _) in enumerate(mats):
             per_matrix[name + " q8act"] = time_calls(
-                lambda c, i=i, dt=dt, M=M, K=K: q.qmm_gemv_q8act(copies[i][c], dt, M, K, xs[i], ys[i], stream=stream),
+                lambda c, i=i, dt=dt, M=M, K=K: q.qmm_gemv_q8act(copies[i][c % R], dt, M, K, xs[i], ys[i], stream=stream),
                 copies[i][0].numel())
         per_matrix["gate+up concat q8act"] = time_calls(
-            lambda c: q.qmm_gemv_concat_q8act([copies[1][c], copies[2][c]], dg, [Mg, Mg], Kg, xs[1], gate_up_ys,
+            lambda c: q.qmm_gemv_concat_q8act([copies[1][c % R], copies[2][c % R]], dg, [Mg, Mg], Kg, xs[1], gate_up_ys,
                                               stream=stream), gu_bytes)
         per_matrix["gate+up swiglu q8act"] = time_calls(
-            lambda c: q.qmm_gemv_swiglu_q8act(copies[1][c], copies[2][c], dg, Mg, Kg, xs[1], swiglu_y,
+            lambda c: q.qmm_gemv_swiglu_q8act(copies[1][c % R], copies[2][c % R], dg, Mg, Kg, xs[1], swiglu_y,
                                               stream=stream), gu_bytes)
 
     # the 128256 x 4096 Q6_K LM head (the largest decode GEMV): f32 and
@@ -241,13 +296,47 @@ def main():
                         ("q8act", lambda c: q.qmm_gemv_q8act(hcopies[c % HR], hdt, HM, HK, hx, hy, stream=stream)),
                         ("argmax_f32", lambda c: q.qmm_gemv_argmax(hcopies[c % HR], hdt, HM, HK, hx, hwork, hidx,
                                                                    stream=stream)),
+                        ("argmax_f32_noalloc", lambda c: q.qmm_gemv_argmax_noalloc(hcopies[c % HR], hdt, HM, HK, hx,
+                                                                                   hidx, stream=stream)),
                         ("argmax_q8act", lambda c: q.qmm_gemv_argmax_q8act(hcopies[c % HR], hdt, HM, HK, hx, hwork,
                                                                            hidx, stream=stream))):
-            r = time_calls(fn, hblob.numel())
+            r = leg(fn, hblob.numel(), probe_copies=hcopies if key == "f32" else None)
             r["hbm_frac"] = round(r["GB/s"] / HBM_PEAK_GBS, 4)
+            r["hbm_frac_median"] = round(r["GB/s_median"] / HBM_PEAK_GBS, 4)
             lm_head[key] = r
+        lm_head["argmax_minus_gemv_us_median"] = round(lm_head["argmax_f32"]["us_median"] - lm_head["f32"]["us_median"],
+                                                       3)
         del hcopies, hblob
         torch.cuda.empty_cache()
+
+    # C1 (Q8_0 1024x1024 GEMV) and C4a (Q4_K 14336x4096 GEMM at N = 32): the
+    # other single-launch configurations, each rotated over >= 1 GiB of weight
+    # copies and also warm (one copy, its bytes served from the caches)
+    small = {}
+    if not args.headline_only:
+        for key, wid, N in (("C1 q8_0 gemv 1024x1024", 1, 1), ("C4a q4_k gemm 14336x4096 N=32", 6, 32)):
+            _, sdt, SM, SK, _ = WORKLOADS[wid]
+            sblob = torch.from_numpy(make_blob(sdt, SM, SK, rng_for(wid, 0))).to(dev)
+            SR = max(2, -(-ROTATE_BYTES // sblob.numel()))
+            scop = [sblob] + [sblob.clone() for _ in range(SR - 1)]
+            SX = torch.from_numpy(make_x(N, SK, rng_for(wid, 1000 + N))).to(dev)
+            SY = torch.empty((N, SM), device=dev)
+            fl = 2.0 * SM * N * SK
+            for s_ in range(args.warmup):
+                q.qmm_gemm(scop[s_ % SR], sdt, SM, SK, N, SX, SY, stream=stream)
+            r = leg(lambda c: q.qmm_gemm(scop[c % SR], sdt, SM, SK, N, SX, SY, stream=stream), sblob.numel(),
+                    probe_copies=scop, flops=fl)
+            wm, wn = spans(lambda c: q.qmm_gemm(sblob, sdt, SM, SK, N, SX, SY, stream=stream))
+            r.update({"kernel_id": q.gemm_kernel(sdt, SM, SK, N), "weight_bytes": sblob.numel(),
+                      "hbm_frac_median": round(r["GB/s_median"] / HBM_PEAK_GBS, 4),
+                      "warm_us_median": round(wm, 3), "warm_us_min": round(wn, 3),
+                      "warm_note": "one weight copy, re-read from the caches: not an HBM figure"})
+            small[key] = r
+            del scop, sblob
+        torch.cuda.empty_cache()
+
+    # the decode step again, as 5 spans (per-step median and min)
+    dec_med, dec_min = spans(lambda c: step_fused(c % R))
 
     def layer_rate(span):
         if span is None:
@@ -276,6 +365,7 @@ def main():
     pre_ms = pa.elapsed_time(pb)
     flops = 2.0 * PM * PN * PK
     tflops = flops * args.steps / (pre_ms * 1e-3) / 1e12
+    pre_med, pre_min = spans(lambda c: q.qmm_gemm(pcopies[c % PR], pdt, PM, PK, PN, PX, PY, stream=stream))
     ptraffic = load_traffic("gemm_q4_k_n512")
 
     out = {
@@ -286,6 +376,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round((wall_dec + wall_pre) * 1e3 / args.steps, 4),
+        "ms_per_step_note": "host wall clock of the two timed loops (K decode-layer steps, then K N=512 GEMM "
+                            "calls) per step; the decode step alone is config.decode_ms_per_step",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -298,6 +390,9 @@ def main():
             "rotation_copies": R,
             "hbm_frac": round(value / HBM_PEAK_GBS, 4),
             "decode_ms_per_step": round(span_ms / args.steps, 5),
+            "decode_step_us_median_of_5_spans": round(dec_med, 3),
+            "decode_step_us_min_of_5_spans": round(dec_min, 3),
+            "decode_GBps_median_of_5_spans": round(step_bytes / (dec_med * 1e-6) / 1e9, 1),
             "decode_unfused": {"launches": 4, **(layer_rate(span_unf) or {})},
             "decode_swiglu": {"launches": 3, **(layer_rate(span_swi) or {}),
                               "note": "gate/up through qmm_gemv_swiglu (outputs silu(g)*u instead of g and u)"},
@@ -305,9 +400,13 @@ def main():
                              "note": "int8 activations: qmm_gemv_q8act (q_proj, down) and qmm_gemv_concat_q8act "
                                      "(gate+up), each quantizing x to Q8_0 inside the launch; integer block dots, "
                                      "different numbers from the f32 path"},
-            "timing": "HIP events on the launch stream before the first and after the last timed step; per-launch = span / launches",
+            "timing": "HIP events on the launch stream before the first and after the last timed step; per-launch = "
+                      "span / launches; the *_median/*_min fields: 5 further spans, each after a GPU-side spin "
+                      "that keeps the queue ahead of the host (so small launches are not timed by the host's "
+                      "enqueue rate)",
             "per_matrix": per_matrix,
             "lm_head": lm_head,
+            "other_configs": small,
             "gpu": props.name,
             "cus": props.multi_processor_count,
         },
@@ -327,6 +426,9 @@ def main():
             "workload": "Q4_K 14336x4096, N=512 tokens, X f32 ~ N(0,1), f16 matrix cores, f32 accumulate",
             "tflops": round(tflops, 2),
             "ms_per_call": round(pre_ms / args.steps, 5),
+            "us_median_of_5_spans": round(pre_med, 3),
+            "us_min_of_5_spans": round(pre_min, 3),
+            "tflops_median_of_5_spans": round(flops / (pre_med * 1e-6) / 1e12, 2),
             "rotation_copies": PR,
             "roofline": {
                 "bound": "mfma",
@@ -343,6 +445,51 @@ def main():
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args, np, mats, WORKLOADS, make_blob, make_x, rng_for, step_bytes)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_model() -> dict:
+    """Host CPU description from /proc/cpuinfo (model, sockets, cores, threads)."""
+    info = {"threads": os.cpu_count()}
+    try:
+        txt = open("/proc/cpuinfo").read()
+        blocks = [b for b in txt.split("\n\n") if b.strip()]
+        kv = [dict((l.split(":", 1)[0].strip(), l.split(":", 1)[1].strip()) for l in b.splitlines() if ":" in l)
+              for b in blocks]
+        info["model"] = kv[0].get("model name", "?")
+        info["sockets"] = len({d.get("physical id") for d in kv})
+        info["cores"] = len({(d.get("physical id"), d.get("core id")) for d in kv})
+    except OSError:
+        pass
+    return info
+
+
+# single-thread oracle samples of C1-C3: (label, workload id, row stride)
+ORACLE_1T = (("C1 q8_0 1024x1024", 1, 1), ("C2a q4_0 4096x4096", 2, 1), ("C2b q4_0 14336x4096", 3, 1),
+             ("C2c q4_0 4096x14336", 4, 1), ("C3 q6_k 128256x4096", 5, 4))
+
+
+def oracle_child():
+    """Runs in a child process with OMP_NUM_THREADS=1 (no GPU use): the oracle
+    on C1-C3, whole matrices or every n-th row, weight GB/s per config."""
+    import numpy as np
+    import oracle
+    from qmm_inputs import WORKLOADS, make_blob, make_x, rng_for
+    out = {"threads": oracle.num_threads()}
+    for label, wid, stride in ORACLE_1T:
+        _, dt, M, K, _ = WORKLOADS[wid]
+        blob = make_blob(dt, M, K, rng_for(wid, 0))
+        x = make_x(1, K, rng_for(wid, 1001))
+        rows = np.arange(0, M, stride)
+        ts = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            oracle.matmul(dt, blob, M, K, x, rows=rows if stride > 1 else None)
+            ts.append(time.perf_counter() - t0)
+        dt_s = float(np.median(ts))
+        nbytes = blob.size * len(rows) / M
+        out[label] = {"GB/s": round(nbytes / dt_s / 1e9, 4), "s_median_of_3": round(dt_s, 4),
+                      "sample": "all rows" if stride == 1 else f"every {stride}th row ({len(rows)} rows)"}
     print(json.dumps(out), flush=True)
 
 
@@ -372,6 +519,25 @@ def cpu_baseline(args, np, mats, WORKLOADS, make_blob, make_x, rng_for, step_byt
         if time.perf_counter() - t0 >= args.cpu_seconds:
             break
     dt_pre = time.perf_counter() - t0
+    # every config on all cores (C1, C3 head sampled), and C1-C3 on one thread
+    all_cores = {}
+    for label, wid, stride in ORACLE_1T:
+        _, dt, M, K, _ = WORKLOADS[wid]
+        blob = make_blob(dt, M, K, rng_for(wid, 0))
+        x = make_x(1, K, rng_for(wid, 1001))
+        ts = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            oracle.matmul(dt, blob, M, K, x)
+            ts.append(time.perf_counter() - t0)
+        dts = float(np.median(ts))
+        all_cores[label] = {"GB/s": round(blob.size / dts / 1e9, 4), "s_median_of_3": round(dts, 4)}
+    import subprocess
+    env = dict(os.environ, OMP_NUM_THREADS="1")
+    child = subprocess.run([sys.executable, os.path.abspath(__file__), "--oracle-child"], env=env,
+                           capture_output=True, text=True, timeout=600)
+    one_thread = json.loads(child.stdout.strip().splitlines()[-1]) if child.returncode == 0 else \
+        {"error": child.stderr[-500:]}
     return {
         "value": round(step_bytes * passes / dt_dec / 1e9, 4),
         "unit": "GB/s",
@@ -381,6 +547,9 @@ def cpu_baseline(args, np, mats, WORKLOADS, make_blob, make_x, rng_for, step_byt
         "prefill_gemm_tflops": round(2.0 * rows * 512 * PK / dt_pre / 1e12, 6),
         "prefill_sample": f"{rows} output rows (64 at a time, cycling over the {PM}) x 512 tokens of the "
                           f"Q4_K GEMM in {dt_pre:.1f} s",
+        "all_cores_per_config": all_cores,
+        "one_thread_per_config": one_thread,
+        "cpu": cpu_model(),
     }
 
 

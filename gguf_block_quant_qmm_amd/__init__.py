@@ -45,10 +45,11 @@ QMM_ERR_ALIGN, QMM_ERR_DEVICE, QMM_ERR_LAUNCH, QMM_ERR_SCRATCH = -4, -5, -6, -7
 QMM_GEMV_MAX_MATS = 4
 QMM_ARGMAX_WORK_BYTES = 32768
 QMM_NOALLOC_SCRATCH_BYTES = 32768
+QMM_READ_PROBE_OUT_FLOATS = 4096
 
 EXPORTS = ("qmm_gemv", "qmm_gemv_concat", "qmm_gemv_swiglu", "qmm_gemv_argmax", "qmm_gemv_argmax_noalloc", "qmm_gemm", "qmm_gemm_swiglu",
            "qmm_quantize_q8_0", "qmm_gemm_q8act", "qmm_gemv_q8act", "qmm_gemv_concat_q8act",
-           "qmm_gemv_swiglu_q8act", "qmm_gemv_argmax_q8act", "qmm_gemm_path", "qmm_gemm_kernel", "qmm_blob_bytes", "qmm_block_elems",
+           "qmm_gemv_swiglu_q8act", "qmm_gemv_argmax_q8act", "qmm_gemm_path", "qmm_gemm_kernel", "qmm_read_probe", "qmm_blob_bytes", "qmm_block_elems",
            "qmm_block_bytes", "qmm_strerror")
 
 _lib = None
@@ -98,6 +99,8 @@ def lib():
         L.qmm_gemm_path.restype = ci
         L.qmm_gemm_kernel.argtypes = [ci, i64, i64, i64]
         L.qmm_gemm_kernel.restype = ci
+        L.qmm_read_probe.argtypes = [vp, i64, vp, vp]
+        L.qmm_read_probe.restype = ci
         L.qmm_blob_bytes.argtypes = [ci, i64, i64]
         L.qmm_blob_bytes.restype = i64
         L.qmm_block_elems.argtypes = [ci]
@@ -134,6 +137,15 @@ QMM_KERNEL_GEMV, QMM_KERNEL_GEMV_TOKENS = 100, 101
 def gemm_kernel(dtype: int, M: int, K: int, N: int) -> int:
     """Id of the kernel qmm_gemm runs for these sizes (see include/qmm.h)."""
     return lib().qmm_gemm_kernel(dtype, M, K, N)
+
+
+def qmm_read_probe(buf, nbytes: int, out, stream=None) -> None:
+    """A plain streaming read of nbytes of buf (diagnostic read ceiling)."""
+    import torch
+    rc = lib().qmm_read_probe(_addr(buf, nbytes, "buf"), nbytes,
+                              _addr(out, 4 * QMM_READ_PROBE_OUT_FLOATS, "out", torch.float32), _stream(stream))
+    if rc != QMM_OK:
+        raise QmmError(rc, "qmm_read_probe")
 
 
 def tolerance(dtype: int, M: int, K: int, N: int) -> float:

@@ -175,6 +175,17 @@ int qmm_gemm_kernel(int dtype, int64_t M, int64_t K, int64_t N) {
     return qmm::gemm_kernel_choice(dtype, M, K, N);
 }
 
+int qmm_read_probe(const void *buf, int64_t bytes, float *out, void *stream) {
+    if (bytes < 1 || bytes > (int64_t(1) << 40)) return QMM_ERR_SHAPE;
+    if (!buf || !out) return QMM_ERR_NULL;
+    if (!aligned(buf, 16) || !aligned(out, 4)) return QMM_ERR_ALIGN;
+    int cus = 0;
+    const int rc = current_device(&cus);
+    if (rc != QMM_OK) return rc;
+    const hipError_t e = qmm::launch_read_probe(buf, bytes, out, (hipStream_t)stream, cus);
+    return e == hipSuccess ? QMM_OK : QMM_ERR_LAUNCH;
+}
+
 int qmm_gemv(const void *w_blob, int dtype, int64_t M, int64_t K, const float *x, float *y, void *stream) {
     int rc = check_shape(dtype, M, K, 1);
     if (rc != QMM_OK) return rc;

@@ -1625,6 +1625,47 @@ hipError_t launch_gemv(int dtype, const void *blob_v, int64_t M, int64_t K, cons
 }
 
 
+// ------------------------------------------------------ read ceiling ----
+// A plain streaming read of a buffer (the ceiling a launch that reads the same
+// bytes can reach): 16-byte bounds-checked buffer loads in a grid-stride loop,
+// four in flight per thread, folded into one value per workgroup so that no
+// load is dead.  The loads are the GEMV's own kind, with none of its decode.
+__global__ void __launch_bounds__(256) read_probe_kernel(const uint8_t *__restrict__ buf, int64_t bytes,
+                                                         float *__restrict__ out) {
+    const int64_t chunk = (int64_t)1 << 30;  // bytes per buffer resource
+    const int64_t stride = (int64_t)gridDim.x * 256 * 64;  // bytes per sweep: 4 loads of 16 B per thread
+    uint32_t acc = 0;
+    for (int64_t base = 0; base < bytes; base += chunk) {
+        const int64_t n = bytes - base < chunk ? bytes - base : chunk;
+        const Rsrc rs = make_rsrc(buf + base, (uint32_t)n);
+        for (int64_t o = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 64; o < n; o += stride) {
+            u32x4_t v[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) v[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)(o + 16 * i), 0, 0);
+#pragma unroll
+            for (int i = 0; i < 4; i++) acc ^= v[i].x ^ v[i].y ^ v[i].z ^ v[i].w;
+        }
+    }
+    __shared__ uint32_t red[256];
+    red[threadIdx.x] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t a = 0;
+        for (int i = 0; i < 256; i++) a ^= red[i];
+        out[blockIdx.x] = __uint_as_float(a);
+    }
+}
+
+hipError_t launch_read_probe(const void *buf, int64_t bytes, float *out, hipStream_t st, int cus) {
+    const int64_t per_sweep = 256 * 64;
+    int64_t grid = std::min<int64_t>(std::min<int64_t>((int64_t)cus * 4, QMM_READ_PROBE_OUT_FLOATS),
+                                     (bytes + per_sweep - 1) / per_sweep);
+    grid = std::max<int64_t>(grid, 1);
+    hipLaunchKernelGGL(read_probe_kernel, dim3((unsigned)grid), dim3(256), 0, st,
+                       static_cast<const uint8_t *>(buf), bytes, out);
+    return hipGetLastError();
+}
+
 // ------------------------------------------------ Q8_0 activation path ----
 // Quantizer (page "cera 0.5.2 src/backend/cpu.rs", the portable Q8_0
 // quantizer): per block of 32 activations, in f32,

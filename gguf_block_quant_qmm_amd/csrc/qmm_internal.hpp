@@ -62,6 +62,10 @@ int gemm_kernel_choice(int dtype, int64_t M, int64_t K, int64_t N);
 hipError_t launch_gemm_mfma(int dtype, const void *blob, int64_t M, int64_t K, int64_t N, const float *X,
                             float *Y, hipStream_t st);
 
+// A plain streaming read of `bytes` bytes of buf (at most cus * 4 workgroups,
+// one float per workgroup written to out).
+hipError_t launch_read_probe(const void *buf, int64_t bytes, float *out, hipStream_t st, int cus);
+
 // Q8_0 quantization of N activation rows of K (K % 32 == 0): scales f32
 // [N][K/32], codes int8 [N][K].
 hipError_t launch_quantize_q8_0(const float *X, int64_t N, int64_t K, float *scales, int8_t *quants,

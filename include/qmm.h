@@ -299,6 +299,15 @@ int qmm_gemm_path(int dtype, int64_t M, int64_t K, int64_t N);
 #define QMM_KERNEL_GEMV_TOKENS 101
 int qmm_gemm_kernel(int dtype, int64_t M, int64_t K, int64_t N);
 
+/* A plain streaming read of `bytes` bytes of buf (a diagnostic: the ceiling
+ * that any launch reading the same bytes can reach, which the bench puts each
+ * GEMV launch against).  16-byte loads of the GEMV's kind, no arithmetic
+ * beyond a fold; one float per workgroup is written to out.
+ *   buf     device, 16-B aligned, `bytes` readable bytes (1 .. 2^40)
+ *   out     device f32 [QMM_READ_PROBE_OUT_FLOATS], 4-B aligned; clobbered */
+#define QMM_READ_PROBE_OUT_FLOATS 4096
+int qmm_read_probe(const void *buf, int64_t bytes, float *out, void *stream);
+
 /* Bytes of a blob of M rows x K weights; 0 if dtype or shape is invalid. */
 int64_t qmm_blob_bytes(int dtype, int64_t M, int64_t K);
 

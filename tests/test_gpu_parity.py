@@ -322,3 +322,25 @@ def test_gemm_skinny_64_token_tiles_ragged(dt, N):
     Yg = gpu_gemm(dt, to_dev(blob), M, K, X)
     assert np.all(np.isfinite(Yg))
     check(Yg[:, rows], Y64, S, q.tolerance(dt, M, K, N), f"{NAME[dt]} 64-token skinny gemm M={M} K={K} N={N}")
+
+
+# --------------------------------------------------------- read ceiling ----
+
+@pytest.mark.parametrize("nbytes", [16, 4096, 33030144, (1 << 31) + 4096])
+def test_read_probe_reads_every_dword(nbytes):
+    """qmm_read_probe (the bench's read ceiling) reads every dword once: the
+    XOR of its per-workgroup folds is the XOR of the buffer's dwords."""
+    rng = np.random.default_rng(nbytes % 1000)
+    if nbytes > (1 << 30):
+        buf = torch.randint(-2**31, 2**31 - 1, (nbytes // 4,), dtype=torch.int32, device="cuda")
+        host = buf.cpu().numpy().view(np.uint32)
+        want = int(np.bitwise_xor.reduce(host))
+    else:
+        host = rng.integers(0, 2**32, nbytes // 4, dtype=np.uint32)
+        buf = torch.from_numpy(host.view(np.int32)).cuda()
+        want = int(np.bitwise_xor.reduce(host))
+    out = torch.zeros(q.QMM_READ_PROBE_OUT_FLOATS, device="cuda")
+    q.qmm_read_probe(buf, nbytes, out)
+    torch.cuda.synchronize()
+    got = int(np.bitwise_xor.reduce(out.cpu().numpy().view(np.uint32)))
+    assert got == want
