@@ -52,6 +52,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 F16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense f16 matrix cores, TFLOP/s
+I8_MFMA_PEAK_TOPS = 5000.0  # MI355X dense int8 matrix cores, TOP/s
 ROTATE_BYTES = 1 << 30
 
 
@@ -367,6 +368,28 @@ def main():
     tflops = flops * args.steps / (pre_ms * 1e-3) / 1e12
     pre_med, pre_min = spans(lambda c: q.qmm_gemm(pcopies[c % PR], pdt, PM, PK, PN, PX, PY, stream=stream))
     ptraffic = load_traffic("gemm_q4_k_n512")
+    # The same GEMM with int8 activations: X quantized to Q8_0 once (its codes
+    # resident like X), then qmm_gemm_q8act, which takes the int8 matrix cores
+    # at this size; and the quantizer plus the matmul as one step.
+    pre_q8 = None
+    if not args.headline_only:
+        psc = torch.empty((PN, PK // 32), device=dev)
+        pqq = torch.empty((PN, PK), dtype=torch.int8, device=dev)
+        q.qmm_quantize_q8_0(PX, PN, PK, psc, pqq, stream=stream)
+        q8_med, q8_min = spans(lambda c: q.qmm_gemm_q8act(pcopies[c % PR], pdt, PM, PK, PN, psc, pqq, PY,
+                                                          stream=stream))
+
+        def q8_step(c):
+            q.qmm_quantize_q8_0(PX, PN, PK, psc, pqq, stream=stream)
+            q.qmm_gemm_q8act(pcopies[c % PR], pdt, PM, PK, PN, psc, pqq, PY, stream=stream)
+        q8s_med, _ = spans(q8_step)
+        pre_q8 = {"path": "int8 matrix cores" if q.q8act_kernel(pdt, PM, PK, PN) == 1 else "token groups",
+                  "us_median_of_5_spans": round(q8_med, 3), "us_min_of_5_spans": round(q8_min, 3),
+                  "tops_median": round(flops / (q8_med * 1e-6) / 1e12, 2),
+                  "frac_of_int8_mfma_peak": round(flops / (q8_med * 1e-6) / 1e12 / I8_MFMA_PEAK_TOPS, 4),
+                  "quantize_plus_gemm_us_median": round(q8s_med, 3),
+                  "note": "qmm_gemm_q8act on the activations quantized to Q8_0 (integer block sums, each scaled "
+                          "once in f32: bounded by that scaling, not by the matrix rate)"}
 
     out = {
         "metric": "decode GEMV weight GB/s (% HBM peak) + prefill GEMM TFLOP/s at N=512",
@@ -430,6 +453,7 @@ def main():
             "us_min_of_5_spans": round(pre_min, 3),
             "tflops_median_of_5_spans": round(flops / (pre_med * 1e-6) / 1e12, 2),
             "rotation_copies": PR,
+            "q8act": pre_q8,
             "roofline": {
                 "bound": "mfma",
                 "kernel": "qmm::gemm_wb_kernel<12,32,128,2,8,4,2> (Q4_K)",

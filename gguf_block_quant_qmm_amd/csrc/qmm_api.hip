@@ -175,6 +175,12 @@ int qmm_gemm_kernel(int dtype, int64_t M, int64_t K, int64_t N) {
     return qmm::gemm_kernel_choice(dtype, M, K, N);
 }
 
+int qmm_gemm_q8act_path(int dtype, int64_t M, int64_t K, int64_t N) {
+    const int rc = check_shape(dtype, M, K, N);
+    if (rc != QMM_OK) return rc;
+    return qmm::q8_use_mfma(dtype, M, K, N) ? 1 : 0;
+}
+
 int qmm_read_probe(const void *buf, int64_t bytes, float *out, void *stream) {
     if (bytes < 1 || bytes > (int64_t(1) << 40)) return QMM_ERR_SHAPE;
     if (!buf || !out) return QMM_ERR_NULL;

@@ -1887,9 +1887,32 @@ hipError_t launch_gemv_q8in(int mode, int n, const void *const *blobs, const int
 #undef QMM_Q8IN
 }
 
+// Whether qmm_gemm_q8act runs on the int8 matrix cores (where gemm_i8_ok
+// holds) or in token groups of 4 per weight read (each token then has the bits
+// of its single-token call).  Measured at K = 4096 (14336 and 4096 rows): a
+// token-group launch costs about max(5.5, 1.2e-3 M) us (Q8_0: 1.45e-3 M), one
+// round of matrix-core workgroups (256 rows x 64 tokens, 256 at a time) about
+// 110 us (Q4_K), 130 (Q4_0), 160 (Q8_0); both scale with K.  E.g. 14336 x 4096
+// Q4_K: N = 16 70 vs 110 us, N = 32 133 vs 111, N = 512 1988 vs 238; 4096 x
+// 4096: N = 32 41 vs 109, N = 128 153 vs 109.  Below 32 tokens the token
+// groups always run.  A measurement build (QMM_TUNING) takes
+// QMM_Q8_MFMA_FROM_N = n to use the matrix cores from n tokens on instead.
+bool q8_use_mfma(int dtype, int64_t M, int64_t K, int64_t N) {
+    if (!gemm_i8_ok(dtype, M, K, N)) return false;
+    static const int lever = tuning_lever("QMM_Q8_MFMA_FROM_N", 0);
+    if (lever > 0) return N >= lever;
+    if (N < 32) return false;
+    const double t_group = std::max(5.5, (dtype == QMM_Q8_0 ? 1.45e-3 : 1.2e-3) * (double)M);
+    const double t_old = (double)((N + 3) / 4) * t_group;
+    const double t_round = dtype == QMM_Q4_K ? 110.0 : dtype == QMM_Q4_0 ? 130.0 : 160.0;
+    const double rounds = (double)((((M + 255) / 256) * ((N + 63) / 64) + 255) / 256);
+    return t_old > t_round * rounds;
+}
+
 hipError_t launch_gemm_q8act(int dtype, const void *blob_v, int64_t M, int64_t K, int64_t N, const float *xsc,
                              const int8_t *xq, float *Y, hipStream_t st, int cus) {
     const uint8_t *blob = static_cast<const uint8_t *>(blob_v);
+    if (q8_use_mfma(dtype, M, K, N)) return launch_gemm_q8act_mfma(dtype, blob_v, M, K, N, xsc, xq, Y, st);
     const bool fast = gemv_fused_ok(dtype, K);
     // the grid's second dimension holds token groups: at most 65535 per launch
     const int64_t chunk = fast ? (N == 1 ? 1 : (int64_t)65535 * Q8A_TOKENS) : 65535;

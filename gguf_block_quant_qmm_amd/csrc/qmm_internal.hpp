@@ -76,6 +76,15 @@ hipError_t launch_quantize_q8_0(const float *X, int64_t N, int64_t K, float *sca
 hipError_t launch_gemm_q8act(int dtype, const void *blob, int64_t M, int64_t K, int64_t N, const float *xsc,
                              const int8_t *xq, float *Y, hipStream_t st, int cus);
 
+// The int8-activation matmul on the matrix cores (Q8_0, Q4_0, Q4_K; see
+// gemm_i8_ok for the shapes): one int8 matrix step per activation block, each
+// block sum scaled once in f32.
+bool gemm_i8_ok(int dtype, int64_t M, int64_t K, int64_t N);
+// Whether launch_gemm_q8act runs these sizes on the int8 matrix cores.
+bool q8_use_mfma(int dtype, int64_t M, int64_t K, int64_t N);
+hipError_t launch_gemm_q8act_mfma(int dtype, const void *blob, int64_t M, int64_t K, int64_t N, const float *xsc,
+                                  const int8_t *xq, float *Y, hipStream_t st);
+
 // One token of f32 activations quantized to Q8_0 inside the launch, then the
 // int8 dots (codes and results bit-identical to launch_quantize_q8_0 followed
 // by launch_gemm_q8act with N = 1).  mode 0: one matrix, 1: n <= 4 matrices

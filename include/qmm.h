@@ -242,7 +242,13 @@ int qmm_quantize_q8_0(const float *X, int64_t N, int64_t K, float *scales, int8_
  * Q4_1, -dmin*m for Q4_K and Q5_K, none for the others), xq the dequantized
  * activation.  Up to 4 tokens share one read of the weights (K a multiple of
  * 64 up to 16384, even block count per row for Q4_0, Q4_1, Q8_0, Q6_K; other
- * shapes run one weight block per thread).
+ * shapes run one weight block per thread), and each token then has the bits
+ * of its own single-token call.  From N = 32 tokens, where the grid is large
+ * enough to pay (a measured cost model: e.g. 14336 x 4096 from N = 32, 4096 x
+ * 4096 from N ~ 80), Q8_0, Q4_0 (K a multiple of 64) and Q4_K (K a multiple
+ * of 256), K at most 16384, run on the int8 matrix cores: one 32-deep integer
+ * step per activation block, each block sum scaled once in f32 (the same
+ * bound; the bits differ from the single-token call).
  *   w_blob  device blob as for qmm_gemm, 16-B aligned
  *   scales  device f32 [N][K/32] as qmm_quantize_q8_0 writes them, 16-B aligned
  *   quants  device int8 [N][K], 16-B aligned
@@ -282,6 +288,11 @@ int qmm_gemv_swiglu_q8act(const void *gate_blob, const void *up_blob, int dtype,
  * qmm_gemv_argmax. */
 int qmm_gemv_argmax_q8act(const void *w_blob, int dtype, int64_t M, int64_t K, const float *x,
                           void *work, int64_t *index, float *value, void *stream);
+
+/* Which kernel qmm_gemm_q8act uses for these sizes: 0 = token groups (each
+ * token's result has the bits of its single-token call), 1 = the int8 matrix
+ * cores; a negative status for invalid arguments.  The bound is the same. */
+int qmm_gemm_q8act_path(int dtype, int64_t M, int64_t K, int64_t N);
 
 /* Which arithmetic qmm_gemm uses for these sizes: 0 = f32 (GEMV family),
  * 1 = f16 matrix-core GEMM, or a negative status for invalid arguments. */

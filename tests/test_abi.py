@@ -353,12 +353,27 @@ def test_library_reads_no_tuning_environment():
     import sys
     code = ("import gguf_block_quant_qmm_amd as q; "
             "print(q.gemm_path(12, 14336, 4096, 1), q.gemm_path(12, 14336, 4096, 512), "
-            "q.gemm_kernel(12, 14336, 4096, 512), q.gemm_kernel(2, 300, 96, 40))")
+            "q.gemm_kernel(12, 14336, 4096, 512), q.gemm_kernel(2, 300, 96, 40), "
+            "q.q8act_kernel(12, 14336, 4096, 512), q.q8act_kernel(12, 4096, 4096, 40))")
     env = dict(os.environ, PYTHONPATH=ROOT)
     base = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, check=True).stdout
-    env.update(QMM_GEMM_MFMA_FROM_N="1", QMM_GEMM_KERNEL="0", QMM_SWIGLU_KERNEL="2", QMM_GEMV_WAVES_PER_CU="3")
+    env.update(QMM_GEMM_MFMA_FROM_N="1", QMM_GEMM_KERNEL="0", QMM_SWIGLU_KERNEL="2", QMM_GEMV_WAVES_PER_CU="3",
+               QMM_Q8_MFMA_FROM_N="1000")
     lev = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, check=True).stdout
-    assert base == lev and base.split()[:2] == ["0", "1"]
+    assert base == lev and base.split()[:2] == ["0", "1"] and base.split()[4:] == ["1", "0"]
+
+
+def test_q8act_path_reports_each_path():
+    """The int8 matrix cores take large grids from N = 32; few tokens, small grids, Q6_K and
+    the dtypes or K the int8 kernel does not take stay on the token groups."""
+    assert q.q8act_kernel(q.QMM_Q4_K, 14336, 4096, 512) == 1
+    assert q.q8act_kernel(q.QMM_Q8_0, 14336, 4096, 32) == 1
+    assert q.q8act_kernel(q.QMM_Q4_0, 14336, 4096, 16) == 0
+    assert q.q8act_kernel(q.QMM_Q4_0, 4096, 4096, 40) == 0
+    assert q.q8act_kernel(q.QMM_Q6_K, 14336, 4096, 512) == 0
+    assert q.q8act_kernel(q.QMM_Q4_1, 14336, 4096, 512) == 0
+    assert q.q8act_kernel(q.QMM_Q8_0, 14336, 16416, 512) == 0  # K above 16384
+    assert q.q8act_kernel(q.QMM_Q4_K, 14336, 4096, 0) == q.QMM_ERR_SHAPE
 
 
 def test_gemm_kernel_reports_each_path():

@@ -273,6 +273,23 @@ def check_splus(Yg, Y64, Sp, label):
     check(Yg, Y64, Sp, TAU, label)
 
 
+@pytest.mark.parametrize("dt", [q.QMM_Q8_0, q.QMM_Q4_0, q.QMM_Q4_K], ids=NAME.get)
+def test_q8act_matrix_cores_edge_blocks(dt):
+    """The golden blocks through the int8 matrix cores."""
+    M, K, N = 14000, 1024, 40
+    blob = golden_blob(dt, M, K, shift=3)
+    X = unit_and_normal(K, 12, 500 * dt)
+    X = np.concatenate([X, make_x(N - X.shape[0], K, rng_for(1360 + dt, 0))])[:N]
+    assert q.q8act_kernel(dt, M, K, N) == 1
+    so, qo = oracle.quantize_q8_0(X)
+    rows = sample_rows(M, 200, 1370 + dt)
+    _, Y64, _, Sp = oracle.matmul_q8act(dt, blob, M, K, so, qo, rows=rows)
+    Y = torch.full((N, M), float("nan"), device="cuda")
+    q.qmm_gemm_q8act(to_dev(blob), dt, M, K, N, to_dev(so), to_dev(qo), Y)
+    torch.cuda.synchronize()
+    check_splus(Y.cpu().numpy()[:, rows], Y64, Sp, f"{NAME[dt]} int8 matrix cores, golden blocks")
+
+
 @pytest.mark.parametrize("dt", DTYPES, ids=NAME.get)
 def test_q8act_edge_blocks(dt):
     for i, (M, K) in enumerate(((77, 4096), (33, 8192))):

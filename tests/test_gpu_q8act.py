@@ -432,3 +432,70 @@ def test_q8act_many_tokens(dt):
         _, Y64, _, Sp = oracle.matmul_q8act(dt, blob, M, K, sc, qq)
         Yg = gpu_q8act(dt, to_dev(blob), M, K, sc, qq)
         check(Yg, Y64, Sp, f"{NAME[dt]} q8act M={M} K={K} N={N}")
+
+
+# ------------------------------------------------- int8 matrix cores ----
+#
+# From N = 32 tokens (large enough grids), Q8_0, Q4_0 and Q4_K run on the int8 matrix cores: one
+# 32-deep integer step per activation block, the block sums scaled once in f32
+# and summed in two levels (bound 1e-5 * Splus, as the few-token kernels).
+
+MFMA_I8 = [q.QMM_Q8_0, q.QMM_Q4_0, q.QMM_Q4_K]
+
+
+def i8_shapes(dt):
+    # ragged M (partial 32-row fragments and 256-row workgroups) tall enough
+    # for the matrix cores, K from one k-tile up to 16384 (the longest
+    # two-level sum)
+    if bs_of(dt) == 32:
+        return [(14337, 64), (14401, 1024), (14433, 4160), (14339, 16384)]
+    return [(14337, 256), (14401, 1024), (14433, 4352), (14339, 16384)]
+
+
+@pytest.mark.parametrize("dt", MFMA_I8, ids=NAME.get)
+@pytest.mark.parametrize("N", [40, 65, 130])
+def test_q8act_matrix_cores(dt, N):
+    for i, (M, K) in enumerate(i8_shapes(dt)):
+        blob = make_blob(dt, M, K, rng_for(1500 + dt, i), q8_full_range=True)
+        sc, qq = oracle.quantize_q8_0(make_x(N, K, rng_for(1500 + dt, 100 * N + i)))
+        assert q.q8act_kernel(dt, M, K, N) == 1, "shape not on the matrix cores"
+        rows = np.unique(np.concatenate([sample_rows(M, 60, 1501 + i), M - 1 - np.arange(33)]))
+        _, Y64, _, Sp = oracle.matmul_q8act(dt, blob, M, K, sc, qq, rows=rows)
+        Yg = gpu_q8act(dt, to_dev(blob), M, K, sc, qq)
+        assert np.all(np.isfinite(Yg))
+        check(Yg[:, rows], Y64, Sp, f"{NAME[dt]} int8 matrix cores M={M} K={K} N={N}")
+
+
+@pytest.mark.parametrize("dt", MFMA_I8, ids=NAME.get)
+def test_q8act_matrix_cores_deterministic_and_cancelling(dt):
+    M, K, N = 16129, 2048, 40
+    assert q.q8act_kernel(dt, M, K, N) == 1
+    blob = make_blob(dt, M, K, rng_for(1510 + dt, 0))
+    if dt == q.QMM_Q4_K:
+        b = blob.reshape(M, K // 256, 144)
+        b[::3, :, 16:] = 0x11          # rows whose weights are mostly the minimum term
+        blob = b.reshape(-1)
+    elif dt == q.QMM_Q4_0:
+        b = blob.reshape(M, K // 32, 18)
+        b[::3, :, 2:] = 0x88           # every code 8: w = 0, S = 0, exact zeros required
+        blob = b.reshape(-1)
+    sc, qq = oracle.quantize_q8_0(make_x(N, K, rng_for(1510 + dt, 1)))
+    rows = np.unique(np.concatenate([np.arange(0, 600), M - 1 - np.arange(40)]))
+    _, Y64, _, Sp = oracle.matmul_q8act(dt, blob, M, K, sc, qq, rows=rows)
+    bd = to_dev(blob)
+    Y1 = gpu_q8act(dt, bd, M, K, sc, qq)
+    Y2 = gpu_q8act(dt, bd, M, K, sc, qq)
+    assert same_bits(Y1, Y2), f"{NAME[dt]}: two runs differ"
+    check(Y1[:, rows], Y64, Sp, f"{NAME[dt]} int8 matrix cores, planted rows")
+
+
+def test_q8act_matrix_cores_full_size_n512():
+    """The Q4_K 14336 x 4096 prefill shape at N = 512, sampled rows."""
+    dt, M, K, N = q.QMM_Q4_K, 14336, 4096, 512
+    blob = make_blob(dt, M, K, rng_for(6, 0))
+    sc, qq = oracle.quantize_q8_0(make_x(N, K, rng_for(6, 1512)))
+    rows = sample_rows(M, 48, 1520)
+    _, Y64, _, Sp = oracle.matmul_q8act(dt, blob, M, K, sc, qq, rows=rows)
+    Yg = gpu_q8act(dt, to_dev(blob), M, K, sc, qq)
+    assert np.all(np.isfinite(Yg))
+    check(Yg[:, rows], Y64, Sp, "Q4_K 14336x4096 N=512 int8 matrix cores")
