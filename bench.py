@@ -201,35 +201,7 @@ def main():
         us = a.elapsed_time(b) * 1e3 / args.steps
         return {"us": round(us, 3), "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1)}
 
-    # A GPU-side spin before each span keeps the queue ahead of the host: the
-    # binding enqueues a call in ~6 us, about the duration of the smallest
-    # launches, so without it a span of small kernels would time the host.
-    # The spin is calibrated to last about 1.5 ms and is outside the span.
-    t_a, t_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda._sleep(1 << 20)
-    t_a.record(stream)
-    torch.cuda._sleep(1 << 20)
-    t_b.record(stream)
-    torch.cuda.synchronize()
-    sleep_cycles = int((1 << 20) * 1.5 / max(t_a.elapsed_time(t_b), 1e-3))
-
-    def spans(fn, n_spans=5, per_span=None):
-        """Per-call time (median, min) in us over n_spans separate spans of
-        per_span calls each, every span between its own two events with the
-        GPU queue kept ahead of the host (a calibrated spin before the span)."""
-        per_span = per_span or max(10, args.steps // n_spans)
-        out, c = [], 0
-        for _ in range(n_spans):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            torch.cuda._sleep(sleep_cycles)
-            a.record(stream)
-            for _ in range(per_span):
-                fn(c)
-                c += 1
-            b.record(stream)
-            torch.cuda.synchronize()
-            out.append(a.elapsed_time(b) * 1e3 / per_span)
-        return float(np.median(out)), float(np.min(out))
+    spans = span_timer(args, np, torch, stream)
 
     def read_probe_us(copies_list):
         """A plain streaming read of the same bytes over the same rotated
@@ -577,8 +549,46 @@ def cpu_baseline(args, np, mats, WORKLOADS, make_blob, make_x, rng_for, step_byt
     }
 
 
+def span_timer(args, np, torch, stream):
+    """spans(fn) -> per-call time (median, min) in us over 5 separate spans of
+    max(10, steps / 5) calls each, every span between its own two events.
+
+    A GPU-side spin before each span keeps the queue ahead of the host: the
+    binding enqueues a call in ~6 us, about the duration of the smallest
+    launches, so without it a span of small kernels would time the host.  The
+    spin is calibrated to last about 1.5 ms and is outside the span."""
+    t_a, t_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(1 << 20)
+    t_a.record(stream)
+    torch.cuda._sleep(1 << 20)
+    t_b.record(stream)
+    torch.cuda.synchronize()
+    sleep_cycles = int((1 << 20) * 1.5 / max(t_a.elapsed_time(t_b), 1e-3))
+
+    def spans(fn, n_spans=5, per_span=None):
+        per_span = per_span or max(10, args.steps // n_spans)
+        out, c = [], 0
+        for _ in range(n_spans):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda._sleep(sleep_cycles)
+            a.record(stream)
+            for _ in range(per_span):
+                fn(c)
+                c += 1
+            b.record(stream)
+            torch.cuda.synchronize()
+            out.append(a.elapsed_time(b) * 1e3 / per_span)
+        return float(np.median(out)), float(np.min(out))
+    return spans
+
+
 def sweep(args, q, np, torch, dev, WORKLOADS, make_blob, make_x, rng_for):
+    """One JSON line per (workload, N): qmm_gemm's per-call time, median and
+    min of 5 spans over rotated weight copies, with the path and kernel the
+    library chose."""
     stream = torch.cuda.current_stream()
+    spans = span_timer(args, np, torch, stream)
+    names = {2: "Q4_0", 3: "Q4_1", 8: "Q8_0", 12: "Q4_K", 13: "Q5_K", 14: "Q6_K"}
     for wid in sorted(WORKLOADS):
         label, dt, M, K, ns = WORKLOADS[wid]
         blob = torch.from_numpy(make_blob(dt, M, K, rng_for(wid, 0))).to(dev)
@@ -589,17 +599,12 @@ def sweep(args, q, np, torch, dev, WORKLOADS, make_blob, make_x, rng_for):
             Y = torch.empty((N, M), device=dev)
             for s in range(args.warmup):
                 q.qmm_gemm(copies[s % R], dt, M, K, N, X, Y, stream=stream)
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            for s in range(args.steps):
-                q.qmm_gemm(copies[s % R], dt, M, K, N, X, Y, stream=stream)
-            b.record(stream)
-            torch.cuda.synchronize()
-            med = a.elapsed_time(b) * 1e3 / args.steps
+            med, mn = spans(lambda c: q.qmm_gemm(copies[c % R], dt, M, K, N, X, Y, stream=stream))
             wb = blob.numel()
-            rec = {"workload": label, "N": N, "dtype": {2: "Q4_0", 3: "Q4_1", 8: "Q8_0", 12: "Q4_K", 13: "Q5_K", 14: "Q6_K"}[dt],
-                   "M": M, "K": K, "path": "f16-mfma" if q.gemm_path(dt, M, K, N) else "f32-gemv",
-                   "us_per_call": round(med, 3),
+            rec = {"workload": label, "N": N, "dtype": names[dt], "M": M, "K": K,
+                   "path": "f16-mfma" if q.gemm_path(dt, M, K, N) else "f32-gemv",
+                   "kernel_id": q.gemm_kernel(dt, M, K, N),
+                   "us_median": round(med, 3), "us_min": round(mn, 3),
                    "weight_GBps": round(wb / (med * 1e-6) / 1e9, 1),
                    "hbm_frac": round(wb / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                    "TFLOPs": round(2.0 * M * N * K / (med * 1e-6) / 1e12, 2)}

@@ -1627,23 +1627,28 @@ hipError_t launch_gemv(int dtype, const void *blob_v, int64_t M, int64_t K, cons
 
 // ------------------------------------------------------ read ceiling ----
 // A plain streaming read of a buffer (the ceiling a launch that reads the same
-// bytes can reach): 16-byte bounds-checked buffer loads in a grid-stride loop,
-// four in flight per thread, folded into one value per workgroup so that no
+// bytes can reach): 16-byte bounds-checked buffer loads in a coalesced
+// grid-stride loop, four in flight per thread, folded into one value per workgroup so that no
 // load is dead.  The loads are the GEMV's own kind, with none of its decode.
 __global__ void __launch_bounds__(256) read_probe_kernel(const uint8_t *__restrict__ buf, int64_t bytes,
                                                          float *__restrict__ out) {
     const int64_t chunk = (int64_t)1 << 30;  // bytes per buffer resource
-    const int64_t stride = (int64_t)gridDim.x * 256 * 64;  // bytes per sweep: 4 loads of 16 B per thread
+    // In 16-byte pieces: each of a thread's four loads is one grid stride
+    // apart, so every load instruction of a wavefront reads 1 KB in a row.
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    const int64_t tid = (int64_t)blockIdx.x * 256 + threadIdx.x;
     uint32_t acc = 0;
     for (int64_t base = 0; base < bytes; base += chunk) {
         const int64_t n = bytes - base < chunk ? bytes - base : chunk;
+        const int64_t n16 = (n + 15) / 16;
         const Rsrc rs = make_rsrc(buf + base, (uint32_t)n);
-        for (int64_t o = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 64; o < n; o += stride) {
+        for (int64_t i = tid; i < n16; i += 4 * stride) {
             u32x4_t v[4];
 #pragma unroll
-            for (int i = 0; i < 4; i++) v[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)(o + 16 * i), 0, 0);
+            for (int u = 0; u < 4; u++)  // past n the bounds check returns zeros
+                v[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)(16 * (i + u * stride)), 0, 0);
 #pragma unroll
-            for (int i = 0; i < 4; i++) acc ^= v[i].x ^ v[i].y ^ v[i].z ^ v[i].w;
+            for (int u = 0; u < 4; u++) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
         }
     }
     __shared__ uint32_t red[256];
@@ -1657,7 +1662,7 @@ __global__ void __launch_bounds__(256) read_probe_kernel(const uint8_t *__restri
 }
 
 hipError_t launch_read_probe(const void *buf, int64_t bytes, float *out, hipStream_t st, int cus) {
-    const int64_t per_sweep = 256 * 64;
+    const int64_t per_sweep = 256 * 64;  // bytes per workgroup per loop trip
     int64_t grid = std::min<int64_t>(std::min<int64_t>((int64_t)cus * 4, QMM_READ_PROBE_OUT_FLOATS),
                                      (bytes + per_sweep - 1) / per_sweep);
     grid = std::max<int64_t>(grid, 1);

@@ -21,6 +21,17 @@ Subcommands (run from the repository root):
            reader can tell when a kernel has changed since the counters were
            taken.
 
+  gemm     --dtype Q4_K --M 14336 --K 4096 --N 32 --reps R
+           Runs qmm_gemm R times on the seeded synthetic blob and activations
+           of that shape, over enough copies of the blob to fill 1 GiB (so
+           that every launch reads its weights from HBM): the program the
+           per-shape counter runs profile.
+
+  counters --csv <counter_collection.csv> --key REGEX --title T --cmd C
+           Markdown table of every counter in a --pmc run, the mean per
+           dispatch (summed over the device) of the dispatches whose kernel
+           name matches REGEX, with the mean dispatch duration.
+
   mfma     --csv <counter_collection.csv> --key REGEX --flops F --simds S
            Matrix-core utilisation of the dispatches whose kernel name matches
            REGEX, from a run collecting SQ_VALU_MFMA_BUSY_CYCLES,
@@ -63,6 +74,48 @@ def _copy(args):
         b.copy_(a)
     torch.cuda.synchronize()
     print(f"copied {args.mib} MiB x {args.reps}", flush=True)
+
+
+def _gemm(args):
+    import torch
+
+    import gguf_block_quant_qmm_amd as q
+    from qmm_inputs import BY_NAME, make_blob, make_x, rng_for
+    dt = BY_NAME[args.dtype]
+    blob = torch.from_numpy(make_blob(dt, args.M, args.K, rng_for(90, 0))).cuda()
+    copies = [blob] + [blob.clone() for _ in range(max(0, -(-(1 << 30) // blob.numel()) - 1))]
+    X = torch.from_numpy(make_x(args.N, args.K, rng_for(90, 1))).cuda()
+    Y = torch.empty((args.N, args.M), device="cuda")
+    for r in range(args.reps):
+        q.qmm_gemm(copies[r % len(copies)], dt, args.M, args.K, args.N, X, Y)
+    torch.cuda.synchronize()
+    print(f"qmm_gemm {args.dtype} {args.M}x{args.K} N={args.N} x {args.reps} (kernel id "
+          f"{q.gemm_kernel(dt, args.M, args.K, args.N)}, {len(copies)} copies)", flush=True)
+
+
+def _counters(args):
+    rx = re.compile(args.key)
+    per = defaultdict(lambda: defaultdict(float))
+    dur = {}
+    for r in csv.DictReader(open(args.csv)):
+        if not rx.search(r["Kernel_Name"]):
+            continue
+        d = int(r["Dispatch_Id"])
+        per[r["Counter_Name"]][d] += float(r["Counter_Value"])
+        dur[d] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3
+    if not per:
+        sys.exit("no matching dispatches")
+    lines = [f"# {args.title}", "", "Command (from the repository root):", "", "```", args.cmd, "```", "",
+             f"{len(dur)} dispatches, mean duration {sum(dur.values()) / len(dur):.2f} us (under the profiler).", "",
+             "| counter | mean per dispatch (device total) |", "|---|---:|"]
+    for name in sorted(per):
+        v = per[name]
+        lines.append(f"| {name} | {sum(v.values()) / len(v):,.0f} |")
+    text = "\n".join(lines) + "\n"
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write(text)
+    print(text)
 
 
 def _groups(specs):
@@ -230,6 +283,18 @@ def main(argv=None):
     t.add_argument("--calib-regex", default=r"copy|elementwise")
     t.add_argument("--key", action="append", required=True)
     t.add_argument("--out", default=os.path.join(ROOT, "profiles", "counters.json"))
+    g = sub.add_parser("gemm")
+    g.add_argument("--dtype", default="Q4_K")
+    g.add_argument("--M", type=int, default=14336)
+    g.add_argument("--K", type=int, default=4096)
+    g.add_argument("--N", type=int, default=32)
+    g.add_argument("--reps", type=int, default=20)
+    k = sub.add_parser("counters")
+    k.add_argument("--csv", required=True)
+    k.add_argument("--key", required=True)
+    k.add_argument("--title", default="rocprofv3 counters")
+    k.add_argument("--cmd", required=True)
+    k.add_argument("--out")
     m = sub.add_parser("mfma")
     m.add_argument("--csv", required=True)
     m.add_argument("--key", required=True)
@@ -243,7 +308,8 @@ def main(argv=None):
     v.add_argument("--simds", type=int, default=1024)
     v.add_argument("--ghz", type=float, nargs=2, default=(2.1, 2.4), help="clock range (low high)")
     a = ap.parse_args(argv)
-    {"copy": _copy, "stats": _stats, "traffic": _traffic, "mfma": _mfma, "valu": _valu}[a.cmd_name](a)
+    {"copy": _copy, "gemm": _gemm, "counters": _counters, "stats": _stats, "traffic": _traffic, "mfma": _mfma,
+     "valu": _valu}[a.cmd_name](a)
 
 
 if __name__ == "__main__":

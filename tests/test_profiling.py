@@ -129,3 +129,20 @@ def test_bench_traffic_lookup_requires_the_current_sources(tmp_path, monkeypatch
     assert bench.load_traffic("g") is None
     (tmp_path / "profiles" / "counters.json").write_text("not json")
     assert bench.load_traffic("g") is None
+
+
+def test_counters_table_is_the_mean_per_dispatch(tmp_path):
+    p = tmp_path / "c.csv"
+    # two matching dispatches; each counter reported in two instances that sum per dispatch
+    write_counters(p, [(1, "qmm::gemm_sk_kernel<12>", 64, 256, "SQ_WAVES", 100.0, 0, 10000),
+                       (1, "qmm::gemm_sk_kernel<12>", 64, 256, "SQ_WAVES", 50.0, 0, 10000),
+                       (2, "qmm::gemm_sk_kernel<12>", 64, 256, "SQ_WAVES", 250.0, 0, 30000),
+                       (1, "qmm::gemm_sk_kernel<12>", 64, 256, "TCP_TCC_READ_REQ_sum", 4000.0, 0, 10000),
+                       (2, "qmm::gemm_sk_kernel<12>", 64, 256, "TCP_TCC_READ_REQ_sum", 6000.0, 0, 30000),
+                       (3, "other_kernel", 64, 256, "SQ_WAVES", 1e9, 0, 1)])
+    out = tmp_path / "c.md"
+    profiling.main(["counters", "--csv", str(p), "--key", "gemm_sk_kernel<12>", "--cmd", "cmd", "--out", str(out)])
+    text = out.read_text()
+    assert "| SQ_WAVES | 200 |" in text  # (150 + 250) / 2
+    assert "| TCP_TCC_READ_REQ_sum | 5,000 |" in text
+    assert "2 dispatches, mean duration 20.00 us" in text
