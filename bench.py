@@ -363,6 +363,33 @@ def main():
                   "note": "qmm_gemm_q8act on the activations quantized to Q8_0 (integer block sums, each scaled "
                           "once in f32: bounded by that scaling, not by the matrix rate)"}
 
+    # Q6_K at the prefill shape: the GEMM on the GGUF bytes and on the
+    # repacked copy (qmm_repack, built once, timed alone too)
+    pre_q6 = None
+    if not args.headline_only:
+        q6 = q.QMM_Q6_K
+        q6blob = torch.from_numpy(make_blob(q6, PM, PK, rng_for(6, 14))).to(dev)
+        Q6R = -(-ROTATE_BYTES // q6blob.numel())
+        q6copies = [q6blob] + [q6blob.clone() for _ in range(Q6R - 1)]
+        nbr = q.repack_bytes(q6, PM, PK)
+        q6packs = [torch.empty(nbr, dtype=torch.uint8, device=dev) for _ in range(-(-ROTATE_BYTES // nbr))]
+        for c, pk in enumerate(q6packs):
+            q.qmm_repack(q6copies[c % Q6R], q6, PM, PK, pk, stream=stream)
+        g_med, g_min = spans(lambda c: q.qmm_gemm(q6copies[c % Q6R], q6, PM, PK, PN, PX, PY, stream=stream))
+        r_med, r_min = spans(lambda c: q.qmm_gemm_repacked(q6packs[c % len(q6packs)], q6, PM, PK, PN, PX, PY,
+                                                           stream=stream))
+        rp_med, _ = spans(lambda c: q.qmm_repack(q6copies[c % Q6R], q6, PM, PK, q6packs[c % len(q6packs)],
+                                                 stream=stream))
+        pre_q6 = {"workload": "Q6_K 14336x4096, N=512, X f32 ~ N(0,1)",
+                  "gguf_us_median": round(g_med, 3), "gguf_us_min": round(g_min, 3),
+                  "gguf_tflops_median": round(flops / (g_med * 1e-6) / 1e12, 2),
+                  "repacked_us_median": round(r_med, 3), "repacked_us_min": round(r_min, 3),
+                  "repacked_tflops_median": round(flops / (r_med * 1e-6) / 1e12, 2),
+                  "repack_once_us_median": round(rp_med, 3),
+                  "bytes": {"gguf": q6blob.numel(), "repacked": nbr},
+                  "note": "qmm_gemm_repacked gives qmm_gemm's bits here (same f16 weights and matrix-core steps)"}
+        del q6copies, q6packs, q6blob
+
     out = {
         "metric": "decode GEMV weight GB/s (% HBM peak) + prefill GEMM TFLOP/s at N=512",
         "value": round(value, 2),
@@ -426,6 +453,7 @@ def main():
             "tflops_median_of_5_spans": round(flops / (pre_med * 1e-6) / 1e12, 2),
             "rotation_copies": PR,
             "q8act": pre_q8,
+            "q6_k": pre_q6,
             "roofline": {
                 "bound": "mfma",
                 "kernel": "qmm::gemm_wb_kernel<12,32,128,2,8,4,2> (Q4_K)",
@@ -594,6 +622,13 @@ def sweep(args, q, np, torch, dev, WORKLOADS, make_blob, make_x, rng_for):
         blob = torch.from_numpy(make_blob(dt, M, K, rng_for(wid, 0))).to(dev)
         R = max(1, -(-ROTATE_BYTES // blob.numel()))
         copies = [blob] + [blob.clone() for _ in range(R - 1)]
+        # Q6_K: the repacked copy (qmm_repack) timed beside the GGUF bytes
+        packs = []
+        if q.repack_bytes(dt, M, K):
+            nbr = q.repack_bytes(dt, M, K)
+            for c in range(max(1, -(-ROTATE_BYTES // nbr))):
+                packs.append(torch.empty(nbr, dtype=torch.uint8, device=dev))
+                q.qmm_repack(copies[c % R], dt, M, K, packs[-1], stream=stream)
         for N in ns:
             X = torch.from_numpy(make_x(N, K, rng_for(wid, 1000 + N))).to(dev)
             Y = torch.empty((N, M), device=dev)
@@ -608,8 +643,14 @@ def sweep(args, q, np, torch, dev, WORKLOADS, make_blob, make_x, rng_for):
                    "weight_GBps": round(wb / (med * 1e-6) / 1e9, 1),
                    "hbm_frac": round(wb / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                    "TFLOPs": round(2.0 * M * N * K / (med * 1e-6) / 1e12, 2)}
+            if packs:
+                rmed, rmn = spans(lambda c: q.qmm_gemm_repacked(packs[c % len(packs)], dt, M, K, N, X, Y,
+                                                                stream=stream))
+                rec["repacked"] = {"us_median": round(rmed, 3), "us_min": round(rmn, 3),
+                                   "kernel_id": q.gemm_repacked_kernel(dt, M, K, N),
+                                   "TFLOPs": round(2.0 * M * N * K / (rmed * 1e-6) / 1e12, 2)}
             print(json.dumps(rec), flush=True)
-        del copies, blob
+        del copies, blob, packs
         torch.cuda.empty_cache()
 
 

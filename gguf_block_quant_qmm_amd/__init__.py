@@ -23,6 +23,9 @@ there is no CPU fallback.
                                                      X -> Q8_0 activation blocks
     qmm_gemm_q8act(w, dtype, M, K, N, scales, quants, Y, stream=None)
                                                      Y = Xq W^T (int8 activations)
+    qmm_repack(w, dtype, M, K, packed, stream=None)  Q6_K -> the GEMM's repacked layout
+    qmm_gemm_repacked(packed, dtype, M, K, N, X, Y, stream=None)
+                                                     Y[N][M] = X W^T from the repacked copy
     qmm_gemv_q8act / qmm_gemv_concat_q8act / qmm_gemv_swiglu_q8act /
     qmm_gemv_argmax_q8act                            the decode calls above with x
                                                      quantized inside the launch
@@ -49,7 +52,8 @@ QMM_READ_PROBE_OUT_FLOATS = 4096
 
 EXPORTS = ("qmm_gemv", "qmm_gemv_concat", "qmm_gemv_swiglu", "qmm_gemv_argmax", "qmm_gemv_argmax_noalloc", "qmm_gemm", "qmm_gemm_swiglu",
            "qmm_quantize_q8_0", "qmm_gemm_q8act", "qmm_gemv_q8act", "qmm_gemv_concat_q8act",
-           "qmm_gemv_swiglu_q8act", "qmm_gemv_argmax_q8act", "qmm_gemm_path", "qmm_gemm_q8act_path", "qmm_gemm_kernel", "qmm_read_probe", "qmm_blob_bytes", "qmm_block_elems",
+           "qmm_gemv_swiglu_q8act", "qmm_gemv_argmax_q8act", "qmm_repack_bytes", "qmm_repack", "qmm_gemm_repacked", "qmm_gemm_repacked_kernel",
+           "qmm_gemm_path", "qmm_gemm_q8act_path", "qmm_gemm_kernel", "qmm_read_probe", "qmm_blob_bytes", "qmm_block_elems",
            "qmm_block_bytes", "qmm_strerror")
 
 _lib = None
@@ -95,6 +99,14 @@ def lib():
         L.qmm_gemv_swiglu_q8act.restype = ci
         L.qmm_gemv_argmax_q8act.argtypes = [vp, ci, i64, i64, vp, vp, vp, vp, vp]
         L.qmm_gemv_argmax_q8act.restype = ci
+        L.qmm_repack_bytes.argtypes = [ci, i64, i64]
+        L.qmm_repack_bytes.restype = i64
+        L.qmm_repack.argtypes = [vp, ci, i64, i64, vp, vp]
+        L.qmm_repack.restype = ci
+        L.qmm_gemm_repacked.argtypes = [vp, ci, i64, i64, i64, vp, vp, vp]
+        L.qmm_gemm_repacked.restype = ci
+        L.qmm_gemm_repacked_kernel.argtypes = [ci, i64, i64, i64]
+        L.qmm_gemm_repacked_kernel.restype = ci
         L.qmm_gemm_path.argtypes = [ci, i64, i64, i64]
         L.qmm_gemm_path.restype = ci
         L.qmm_gemm_q8act_path.argtypes = [ci, i64, i64, i64]
@@ -203,6 +215,30 @@ def qmm_gemm(w, dtype: int, M: int, K: int, N: int, X, Y, stream=None) -> None:
                         _stream(stream))
     if rc != QMM_OK:
         raise QmmError(rc, "qmm_gemm")
+
+
+def repack_bytes(dtype: int, M: int, K: int) -> int:
+    return lib().qmm_repack_bytes(dtype, M, K)
+
+
+def gemm_repacked_kernel(dtype: int, M: int, K: int, N: int) -> int:
+    return lib().qmm_gemm_repacked_kernel(dtype, M, K, N)
+
+
+def qmm_repack(w, dtype: int, M: int, K: int, packed, stream=None) -> None:
+    rc = lib().qmm_repack(_addr(w, blob_bytes(dtype, M, K) or None, "w_blob"), dtype, M, K,
+                          _addr(packed, repack_bytes(dtype, M, K) or None, "packed"), _stream(stream))
+    if rc != QMM_OK:
+        raise QmmError(rc, "qmm_repack")
+
+
+def qmm_gemm_repacked(packed, dtype: int, M: int, K: int, N: int, X, Y, stream=None) -> None:
+    import torch
+    rc = lib().qmm_gemm_repacked(_addr(packed, repack_bytes(dtype, M, K) or None, "packed"), dtype, M, K, N,
+                                 _addr(X, 4 * N * K, "X", torch.float32), _addr(Y, 4 * N * M, "Y", torch.float32),
+                                 _stream(stream))
+    if rc != QMM_OK:
+        raise QmmError(rc, "qmm_gemm_repacked")
 
 
 def qmm_gemv_concat(ws, dtype: int, Ms, K: int, x, ys, stream=None) -> None:

@@ -181,6 +181,47 @@ int qmm_gemm_q8act_path(int dtype, int64_t M, int64_t K, int64_t N) {
     return qmm::q8_use_mfma(dtype, M, K, N) ? 1 : 0;
 }
 
+int64_t qmm_repack_bytes(int dtype, int64_t M, int64_t K) {
+    if (dtype != QMM_Q6_K || check_shape(dtype, M, K, 1) != QMM_OK) return 0;
+    return M * (K / 256) * 320;
+}
+
+int qmm_repack(const void *w_blob, int dtype, int64_t M, int64_t K, void *packed, void *stream) {
+    int rc = check_shape(dtype, M, K, 1);
+    if (rc != QMM_OK) return rc;
+    if (dtype != QMM_Q6_K) return QMM_ERR_DTYPE;
+    if (!w_blob || !packed) return QMM_ERR_NULL;
+    if (!aligned(w_blob, 16) || !aligned(packed, 16)) return QMM_ERR_ALIGN;
+    int cus = 0;
+    rc = current_device(&cus);
+    if (rc != QMM_OK) return rc;
+    const hipError_t e = qmm::launch_repack_q6_k(w_blob, M, K, packed, (hipStream_t)stream);
+    return e == hipSuccess ? QMM_OK : QMM_ERR_LAUNCH;
+}
+
+int qmm_gemm_repacked(const void *packed, int dtype, int64_t M, int64_t K, int64_t N, const float *X, float *Y,
+                      void *stream) {
+    int rc = check_shape(dtype, M, K, N);
+    if (rc != QMM_OK) return rc;
+    if (dtype != QMM_Q6_K) return QMM_ERR_DTYPE;
+    if (!qmm::gemm_repacked_ok(K)) return QMM_ERR_SHAPE;
+    if (!packed || !X || !Y) return QMM_ERR_NULL;
+    if (!aligned(packed, 16) || !aligned(X, 16) || !aligned(Y, 4)) return QMM_ERR_ALIGN;
+    int cus = 0;
+    rc = current_device(&cus);
+    if (rc != QMM_OK) return rc;
+    const hipError_t e = qmm::launch_gemm_repacked(packed, M, K, N, X, Y, (hipStream_t)stream);
+    return e == hipSuccess ? QMM_OK : QMM_ERR_LAUNCH;
+}
+
+int qmm_gemm_repacked_kernel(int dtype, int64_t M, int64_t K, int64_t N) {
+    const int rc = check_shape(dtype, M, K, N);
+    if (rc != QMM_OK) return rc;
+    if (dtype != QMM_Q6_K) return QMM_ERR_DTYPE;
+    if (!qmm::gemm_repacked_ok(K)) return QMM_ERR_SHAPE;
+    return qmm::gemm_repacked_kernel_choice(M, K, N);
+}
+
 int qmm_read_probe(const void *buf, int64_t bytes, float *out, void *stream) {
     if (bytes < 1 || bytes > (int64_t(1) << 40)) return QMM_ERR_SHAPE;
     if (!buf || !out) return QMM_ERR_NULL;

@@ -22,6 +22,12 @@ template <> struct Geo<QMM_Q5_K> { static constexpr int BS = 256, BB = 176; };
 template <> struct Geo<QMM_Q8_0> { static constexpr int BS = 32, BB = 34; };
 template <> struct Geo<QMM_Q4_K> { static constexpr int BS = 256, BB = 144; };
 template <> struct Geo<QMM_Q6_K> { static constexpr int BS = 256, BB = 210; };
+// Q6_K repacked for the matrix-core GEMM (qmm_repack): per super-block of 256
+// weights, 256 code bytes (q in 0..63, one per weight, in the order the GEMM's
+// lanes read them) and the 16 sub-block scales d * sc as f32.  An internal
+// type id: the C ABI names it by its source type and the repack entry points.
+constexpr int QMM_Q6_K_R = 114;
+template <> struct Geo<QMM_Q6_K_R> { static constexpr int BS = 256, BB = 320; };
 
 __device__ __forceinline__ float h2f(uint32_t bits16) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)(bits16 & 0xFFFFu));

@@ -691,6 +691,42 @@ template <> struct PDec<QMM_Q8_0> {
     }
 };
 
+template <> struct PDec<QMM_Q6_K_R> {
+    // The repacked Q6_K layout: per super-block 256 code bytes, then the 16
+    // sub-block scales d * sc as f32.  In k-tile c lane half kh reads the 32
+    // code bytes at 64c + 32kh; byte 8s + j is the code of k = 64c + 16s +
+    // 8kh + j, so every lane and step holds the k that BDec<QMM_Q6_K> gives
+    // it, and step s lies in sub-block 4c + s.  Each weight is the same
+    // single rounding of d * sc * (q - 32) as from the GGUF bytes: the
+    // matrix-core steps get the same operands and the sums the same bits.
+    static constexpr int NW = 12;
+    static constexpr bool SWAP = true;
+    __device__ static int xpos(int c4) { return BDec<QMM_Q6_K>::xpos(c4); }
+    struct State {};
+    __device__ static void loadb(Rsrc rs, uint32_t roff, int64_t k0, int kh, int c, uint32_t (&r)[NW]) {
+        const uint32_t sb = (uint32_t)(320 * (k0 / 256));
+        uint32_t q[8], sc[4];
+        ldb(rs, roff + 32u * kh, sb + 64u * (uint32_t)c, q);
+        ldb(rs, roff, sb + 256u + 16u * (uint32_t)c, sc);
+#pragma unroll
+        for (int i = 0; i < 8; i++) r[i] = q[i];
+#pragma unroll
+        for (int i = 0; i < 4; i++) r[8 + i] = sc[i];
+    }
+    __device__ static void decode(const uint32_t (&r)[NW], State &, int, int, int64_t, half8 (&f)[4]) {
+#pragma unroll
+        for (int s = 0; s < 4; s++) {
+            const float dsc = __builtin_bit_cast(float, r[8 + s]);
+            const float s24 = dsc * TWO24, n = -32.f * dsc;
+#pragma unroll
+            for (int h = 0; h < 2; h++) {
+                const uint32_t w = r[2 * s + h];  // codes of j = 4h .. 4h + 3
+                quad(w & 0x00FF00FFu, (w >> 8) & 0x00FF00FFu, s24, n, f[s], 4 * h);
+            }
+        }
+    }
+};
+
 template <int DT> struct WbDec { using type = PDec<DT>; };
 template <> struct WbDec<QMM_Q6_K> { using type = BDec<QMM_Q6_K>; };
 
@@ -1047,7 +1083,8 @@ static bool aligned_layout(int dtype, int64_t nb) {
     case QMM_Q6_K: return (nb % 2) == 0;
     case QMM_Q4_1:
     case QMM_Q4_K:
-    case QMM_Q5_K: return true;
+    case QMM_Q5_K:
+    case QMM_Q6_K_R: return true;
     default: return false;
     }
 }
@@ -1155,9 +1192,13 @@ static hipError_t launch_dt(const uint8_t *blob, int64_t M, int64_t K, int64_t N
     case GEMM_K_SK_FM2_64: return launch_sk<DT, 64, 4, 2, 2, 2>(blob, M, K, N, X, Y, st);
     default: break;
     }
-    if (N <= 32) return launch_tile<DT, 128, 32, 1, 4>(blob, M, K, N, X, Y, st, gen);
-    if (N <= 64) return launch_tile<DT, 128, 64, 1, 4>(blob, M, K, N, X, Y, st, gen);
-    return launch_tile<DT, 128, 128, 2, 2>(blob, M, K, N, X, Y, st, gen);
+    if constexpr (DT == QMM_Q6_K_R) {
+        return hipErrorInvalidValue;  // no LDS-tile decoder
+    } else {
+        if (N <= 32) return launch_tile<DT, 128, 32, 1, 4>(blob, M, K, N, X, Y, st, gen);
+        if (N <= 64) return launch_tile<DT, 128, 64, 1, 4>(blob, M, K, N, X, Y, st, gen);
+        return launch_tile<DT, 128, 128, 2, 2>(blob, M, K, N, X, Y, st, gen);
+    }
 }
 
 int gemm_kernel_choice(int dtype, int64_t M, int64_t K, int64_t N) {
@@ -1170,6 +1211,18 @@ int gemm_kernel_choice(int dtype, int64_t M, int64_t K, int64_t N) {
     case QMM_Q6_K: return choice_dt<QMM_Q6_K>(M, K, N);
     default: return -1;
     }
+}
+
+// The repacked Q6_K layout runs the register-B and split-K kernels only (it
+// has no LDS-tile decoder): K must give the register-B layout.
+bool gemm_repacked_ok(int64_t K) { return (K % 256) == 0 && (K % (4 * BK)) == 0 && K * 4 * 128 < ((int64_t)1 << 31); }
+
+int gemm_repacked_kernel_choice(int64_t M, int64_t K, int64_t N) { return choice_dt<QMM_Q6_K_R>(M, K, N); }
+
+hipError_t launch_gemm_repacked(const void *packed, int64_t M, int64_t K, int64_t N, const float *X, float *Y,
+                                hipStream_t st) {
+    if (!gemm_repacked_ok(K)) return hipErrorInvalidValue;
+    return launch_dt<QMM_Q6_K_R>(static_cast<const uint8_t *>(packed), M, K, N, X, Y, st);
 }
 
 // The gate/up projection with SwiGLU on the matrix cores: 4 wavefronts x 32

@@ -294,6 +294,39 @@ int qmm_gemv_argmax_q8act(const void *w_blob, int dtype, int64_t M, int64_t K, c
  * cores; a negative status for invalid arguments.  The bound is the same. */
 int qmm_gemm_q8act_path(int dtype, int64_t M, int64_t K, int64_t N);
 
+/* Load-time repack for the prefill GEMM (page "cera 0.5.2 src/backend/cpu.rs",
+ * the Q4_0 / Q4_K weight repacking: a second copy of a prefill weight,
+ * built once at load and kept beside the GGUF bytes, laid out for the GEMM
+ * with the per-block scale products baked in; decode keeps the original).
+ * Q6_K only.  The repacked super-block is 320 bytes (the GGUF one 210):
+ * 256 bytes of 6-bit codes, one per weight, in the order the matrix-core
+ * lanes read them, then the 16 sub-block scales d * sc[i] as f32.  Every
+ * offset is 16-byte aligned and a weight's code is one byte, where the GGUF
+ * super-block is 2 bytes off a dword on every other block and splits each
+ * code over a nibble and two bits elsewhere.
+ *
+ * qmm_repack_bytes: bytes of the repacked copy of M x K weights (1.52 x
+ *   qmm_blob_bytes); 0 if dtype has no repacked form or the shape is invalid.
+ * qmm_repack: fills `packed` from the GGUF blob (one launch on `stream`).
+ *   w_blob  device, 16-B aligned, qmm_blob_bytes(dtype, M, K) bytes
+ *   packed  device, 16-B aligned, qmm_repack_bytes(dtype, M, K) bytes;
+ *           overwritten; caller-owned, like w_blob
+ *   dtype   QMM_Q6_K (any other valid dtype: QMM_ERR_DTYPE)
+ * qmm_gemm_repacked: Y[n][m] = sum_k W[m][k] * X[n][k] from the repacked
+ *   copy, on the matrix cores for every N (the f16 class of qmm_gemm: 2e-3 of
+ *   sum |w x|).  Where qmm_gemm runs the matrix cores too (qmm_gemm_path 1)
+ *   and the row has an even number of super-blocks, Y has exactly qmm_gemm's
+ *   bits: each weight is the same single rounding of d * sc * (q - 32) to f16
+ *   and every matrix-core step sees the same operands.  K must be a multiple
+ *   of 256 below 2^22 (QMM_ERR_SHAPE otherwise); X, Y, N as for qmm_gemm.
+ * qmm_gemm_repacked_kernel: which matrix-core kernel it runs (the ids of
+ *   qmm_gemm_kernel), or a negative status. */
+int64_t qmm_repack_bytes(int dtype, int64_t M, int64_t K);
+int qmm_repack(const void *w_blob, int dtype, int64_t M, int64_t K, void *packed, void *stream);
+int qmm_gemm_repacked(const void *packed, int dtype, int64_t M, int64_t K, int64_t N, const float *X,
+                      float *Y, void *stream);
+int qmm_gemm_repacked_kernel(int dtype, int64_t M, int64_t K, int64_t N);
+
 /* Which arithmetic qmm_gemm uses for these sizes: 0 = f32 (GEMV family),
  * 1 = f16 matrix-core GEMM, or a negative status for invalid arguments. */
 int qmm_gemm_path(int dtype, int64_t M, int64_t K, int64_t N);

@@ -382,3 +382,33 @@ def test_gemm_kernel_reports_each_path():
     assert 0 <= q.gemm_kernel(q.QMM_Q4_K, 14336, 4096, 512) < 100
     assert q.gemm_kernel(q.QMM_Q4_K, 14336, 100, 512) == q.QMM_ERR_SHAPE
     assert q.gemm_kernel(5, 14336, 4096, 512) == q.QMM_ERR_DTYPE
+
+
+def test_repack_sizes_and_argument_checks():
+    """qmm_repack / qmm_gemm_repacked: Q6_K only, 320 bytes per super-block; the
+    checks that come before any device call."""
+    L = q.lib()
+    assert q.repack_bytes(q.QMM_Q6_K, 3, 512) == 3 * 2 * 320
+    assert q.repack_bytes(q.QMM_Q6_K, 14336, 4096) == 14336 * 16 * 320
+    for dt in (q.QMM_Q4_0, q.QMM_Q8_0, q.QMM_Q4_K, q.QMM_Q4_1, q.QMM_Q5_K, 5):
+        assert q.repack_bytes(dt, 3, 512) == 0
+        assert L.qmm_repack(A16, dt, 3, 512, A16, None) in (q.QMM_ERR_DTYPE,)
+    assert q.repack_bytes(q.QMM_Q6_K, 3, 500) == 0
+    assert L.qmm_repack(A16, q.QMM_Q6_K, 3, 500, A16, None) == q.QMM_ERR_SHAPE
+    assert L.qmm_repack(None, q.QMM_Q6_K, 3, 512, A16, None) == q.QMM_ERR_NULL
+    assert L.qmm_repack(A16, q.QMM_Q6_K, 3, 512, A16 + 4, None) == q.QMM_ERR_ALIGN
+    assert L.qmm_gemm_repacked(A16, q.QMM_Q4_K, 3, 512, 4, A16, A16, None) == q.QMM_ERR_DTYPE
+    assert L.qmm_gemm_repacked(A16, q.QMM_Q6_K, 3, 1 << 22, 4, A16, A16, None) == q.QMM_ERR_SHAPE
+    assert L.qmm_gemm_repacked(A16, q.QMM_Q6_K, 3, 512, 4, A16 + 8, A16, None) == q.QMM_ERR_ALIGN
+    assert L.qmm_gemm_repacked(A16, q.QMM_Q6_K, 3, 512, 4, A16, None, None) == q.QMM_ERR_NULL
+
+
+def test_repacked_kernel_choice_matches_the_gguf_form():
+    """With an even number of super-blocks per row the repacked GEMM runs the
+    kernel qmm_gemm runs on the GGUF bytes (so the two give the same bits);
+    with an odd number it still runs a register-B kernel."""
+    for M, K, N in [(14336, 4096, 512), (4096, 4096, 512), (4096, 4096, 32), (14336, 4096, 32),
+                    (4096, 4096, 128), (4096, 4096, 256), (128256, 4096, 9), (1000, 1536, 20)]:
+        assert q.gemm_repacked_kernel(q.QMM_Q6_K, M, K, N) == q.gemm_kernel(q.QMM_Q6_K, M, K, N)
+    assert q.gemm_kernel(q.QMM_Q6_K, 300, 768, 40) == 0  # the LDS-tile kernel for odd block counts
+    assert 0 < q.gemm_repacked_kernel(q.QMM_Q6_K, 300, 768, 40) < 100
