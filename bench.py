@@ -363,32 +363,34 @@ def main():
                   "note": "qmm_gemm_q8act on the activations quantized to Q8_0 (integer block sums, each scaled "
                           "once in f32: bounded by that scaling, not by the matrix rate)"}
 
-    # Q6_K at the prefill shape: the GEMM on the GGUF bytes and on the
-    # repacked copy (qmm_repack, built once, timed alone too)
-    pre_q6 = None
+    # Q6_K and Q8_0 at the prefill shape: the GEMM on the GGUF bytes and on
+    # the repacked copy (qmm_repack, built once, timed alone too)
+    pre_rp = None
     if not args.headline_only:
-        q6 = q.QMM_Q6_K
-        q6blob = torch.from_numpy(make_blob(q6, PM, PK, rng_for(6, 14))).to(dev)
-        Q6R = -(-ROTATE_BYTES // q6blob.numel())
-        q6copies = [q6blob] + [q6blob.clone() for _ in range(Q6R - 1)]
-        nbr = q.repack_bytes(q6, PM, PK)
-        q6packs = [torch.empty(nbr, dtype=torch.uint8, device=dev) for _ in range(-(-ROTATE_BYTES // nbr))]
-        for c, pk in enumerate(q6packs):
-            q.qmm_repack(q6copies[c % Q6R], q6, PM, PK, pk, stream=stream)
-        g_med, g_min = spans(lambda c: q.qmm_gemm(q6copies[c % Q6R], q6, PM, PK, PN, PX, PY, stream=stream))
-        r_med, r_min = spans(lambda c: q.qmm_gemm_repacked(q6packs[c % len(q6packs)], q6, PM, PK, PN, PX, PY,
-                                                           stream=stream))
-        rp_med, _ = spans(lambda c: q.qmm_repack(q6copies[c % Q6R], q6, PM, PK, q6packs[c % len(q6packs)],
-                                                 stream=stream))
-        pre_q6 = {"workload": "Q6_K 14336x4096, N=512, X f32 ~ N(0,1)",
-                  "gguf_us_median": round(g_med, 3), "gguf_us_min": round(g_min, 3),
-                  "gguf_tflops_median": round(flops / (g_med * 1e-6) / 1e12, 2),
-                  "repacked_us_median": round(r_med, 3), "repacked_us_min": round(r_min, 3),
-                  "repacked_tflops_median": round(flops / (r_med * 1e-6) / 1e12, 2),
-                  "repack_once_us_median": round(rp_med, 3),
-                  "bytes": {"gguf": q6blob.numel(), "repacked": nbr},
-                  "note": "qmm_gemm_repacked gives qmm_gemm's bits here (same f16 weights and matrix-core steps)"}
-        del q6copies, q6packs, q6blob
+        pre_rp = {}
+        for rdt, rname in ((q.QMM_Q6_K, "q6_k"), (q.QMM_Q8_0, "q8_0")):
+            rblob = torch.from_numpy(make_blob(rdt, PM, PK, rng_for(6, rdt))).to(dev)
+            RR = -(-ROTATE_BYTES // rblob.numel())
+            rcopies = [rblob] + [rblob.clone() for _ in range(RR - 1)]
+            nbr = q.repack_bytes(rdt, PM, PK)
+            rpacks = [torch.empty(nbr, dtype=torch.uint8, device=dev) for _ in range(-(-ROTATE_BYTES // nbr))]
+            for c, pk in enumerate(rpacks):
+                q.qmm_repack(rcopies[c % RR], rdt, PM, PK, pk, stream=stream)
+            g_med, g_min = spans(lambda c: q.qmm_gemm(rcopies[c % RR], rdt, PM, PK, PN, PX, PY, stream=stream))
+            r_med, r_min = spans(lambda c: q.qmm_gemm_repacked(rpacks[c % len(rpacks)], rdt, PM, PK, PN, PX, PY,
+                                                               stream=stream))
+            rp_med, _ = spans(lambda c: q.qmm_repack(rcopies[c % RR], rdt, PM, PK, rpacks[c % len(rpacks)],
+                                                     stream=stream))
+            pre_rp[rname] = {"workload": f"{rname.upper()} {PM}x{PK}, N={PN}, X f32 ~ N(0,1)",
+                             "gguf_us_median": round(g_med, 3), "gguf_us_min": round(g_min, 3),
+                             "gguf_tflops_median": round(flops / (g_med * 1e-6) / 1e12, 2),
+                             "repacked_us_median": round(r_med, 3), "repacked_us_min": round(r_min, 3),
+                             "repacked_tflops_median": round(flops / (r_med * 1e-6) / 1e12, 2),
+                             "repack_once_us_median": round(rp_med, 3),
+                             "bytes": {"gguf": rblob.numel(), "repacked": nbr}}
+            del rcopies, rpacks, rblob
+        pre_rp["note"] = ("qmm_gemm_repacked gives qmm_gemm's bits at these shapes (same f16 weights and "
+                          "matrix-core steps)")
 
     out = {
         "metric": "decode GEMV weight GB/s (% HBM peak) + prefill GEMM TFLOP/s at N=512",
@@ -453,7 +455,7 @@ def main():
             "tflops_median_of_5_spans": round(flops / (pre_med * 1e-6) / 1e12, 2),
             "rotation_copies": PR,
             "q8act": pre_q8,
-            "q6_k": pre_q6,
+            "repacked": pre_rp,
             "roofline": {
                 "bound": "mfma",
                 "kernel": "qmm::gemm_wb_kernel<12,32,128,2,8,4,2> (Q4_K)",

@@ -23,7 +23,7 @@ there is no CPU fallback.
                                                      X -> Q8_0 activation blocks
     qmm_gemm_q8act(w, dtype, M, K, N, scales, quants, Y, stream=None)
                                                      Y = Xq W^T (int8 activations)
-    qmm_repack(w, dtype, M, K, packed, stream=None)  Q6_K -> the GEMM's repacked layout
+    qmm_repack(w, dtype, M, K, packed, stream=None)  Q6_K / Q8_0 -> the GEMM's repacked layout
     qmm_gemm_repacked(packed, dtype, M, K, N, X, Y, stream=None)
                                                      Y[N][M] = X W^T from the repacked copy
     qmm_gemv_q8act / qmm_gemv_concat_q8act / qmm_gemv_swiglu_q8act /

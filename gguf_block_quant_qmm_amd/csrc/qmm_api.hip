@@ -181,21 +181,24 @@ int qmm_gemm_q8act_path(int dtype, int64_t M, int64_t K, int64_t N) {
     return qmm::q8_use_mfma(dtype, M, K, N) ? 1 : 0;
 }
 
+// The repacked forms: Q6_K 320 bytes per 256 weights, Q8_0 72 bytes per 64
+// (K a multiple of 256 for both, as the GEMM on them needs).
 int64_t qmm_repack_bytes(int dtype, int64_t M, int64_t K) {
-    if (dtype != QMM_Q6_K || check_shape(dtype, M, K, 1) != QMM_OK) return 0;
-    return M * (K / 256) * 320;
+    if ((dtype != QMM_Q6_K && dtype != QMM_Q8_0) || check_shape(dtype, M, K, 1) != QMM_OK || K % 256 != 0) return 0;
+    return dtype == QMM_Q6_K ? M * (K / 256) * 320 : M * (K / 64) * 72;
 }
 
 int qmm_repack(const void *w_blob, int dtype, int64_t M, int64_t K, void *packed, void *stream) {
     int rc = check_shape(dtype, M, K, 1);
     if (rc != QMM_OK) return rc;
-    if (dtype != QMM_Q6_K) return QMM_ERR_DTYPE;
+    if (dtype != QMM_Q6_K && dtype != QMM_Q8_0) return QMM_ERR_DTYPE;
+    if (K % 256 != 0) return QMM_ERR_SHAPE;
     if (!w_blob || !packed) return QMM_ERR_NULL;
     if (!aligned(w_blob, 16) || !aligned(packed, 16)) return QMM_ERR_ALIGN;
     int cus = 0;
     rc = current_device(&cus);
     if (rc != QMM_OK) return rc;
-    const hipError_t e = qmm::launch_repack_q6_k(w_blob, M, K, packed, (hipStream_t)stream);
+    const hipError_t e = qmm::launch_repack(dtype, w_blob, M, K, packed, (hipStream_t)stream);
     return e == hipSuccess ? QMM_OK : QMM_ERR_LAUNCH;
 }
 
@@ -203,23 +206,23 @@ int qmm_gemm_repacked(const void *packed, int dtype, int64_t M, int64_t K, int64
                       void *stream) {
     int rc = check_shape(dtype, M, K, N);
     if (rc != QMM_OK) return rc;
-    if (dtype != QMM_Q6_K) return QMM_ERR_DTYPE;
-    if (!qmm::gemm_repacked_ok(K)) return QMM_ERR_SHAPE;
+    if (dtype != QMM_Q6_K && dtype != QMM_Q8_0) return QMM_ERR_DTYPE;
+    if (!qmm::gemm_repacked_ok(dtype, K)) return QMM_ERR_SHAPE;
     if (!packed || !X || !Y) return QMM_ERR_NULL;
     if (!aligned(packed, 16) || !aligned(X, 16) || !aligned(Y, 4)) return QMM_ERR_ALIGN;
     int cus = 0;
     rc = current_device(&cus);
     if (rc != QMM_OK) return rc;
-    const hipError_t e = qmm::launch_gemm_repacked(packed, M, K, N, X, Y, (hipStream_t)stream);
+    const hipError_t e = qmm::launch_gemm_repacked(dtype, packed, M, K, N, X, Y, (hipStream_t)stream);
     return e == hipSuccess ? QMM_OK : QMM_ERR_LAUNCH;
 }
 
 int qmm_gemm_repacked_kernel(int dtype, int64_t M, int64_t K, int64_t N) {
     const int rc = check_shape(dtype, M, K, N);
     if (rc != QMM_OK) return rc;
-    if (dtype != QMM_Q6_K) return QMM_ERR_DTYPE;
-    if (!qmm::gemm_repacked_ok(K)) return QMM_ERR_SHAPE;
-    return qmm::gemm_repacked_kernel_choice(M, K, N);
+    if (dtype != QMM_Q6_K && dtype != QMM_Q8_0) return QMM_ERR_DTYPE;
+    if (!qmm::gemm_repacked_ok(dtype, K)) return QMM_ERR_SHAPE;
+    return qmm::gemm_repacked_kernel_choice(dtype, M, K, N);
 }
 
 int qmm_read_probe(const void *buf, int64_t bytes, float *out, void *stream) {

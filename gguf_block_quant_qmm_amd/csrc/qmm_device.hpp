@@ -28,6 +28,10 @@ template <> struct Geo<QMM_Q6_K> { static constexpr int BS = 256, BB = 210; };
 // type id: the C ABI names it by its source type and the repack entry points.
 constexpr int QMM_Q6_K_R = 114;
 template <> struct Geo<QMM_Q6_K_R> { static constexpr int BS = 256, BB = 320; };
+// Q8_0 repacked the same way: per 64 weights (two GGUF blocks), 64 code bytes
+// q + 128 (unsigned) in order, then the two block scales d as f32.
+constexpr int QMM_Q8_0_R = 108;
+template <> struct Geo<QMM_Q8_0_R> { static constexpr int BS = 64, BB = 72; };
 
 __device__ __forceinline__ float h2f(uint32_t bits16) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)(bits16 & 0xFFFFu));

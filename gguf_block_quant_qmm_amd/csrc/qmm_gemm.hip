@@ -727,6 +727,36 @@ template <> struct PDec<QMM_Q6_K_R> {
     }
 };
 
+template <> struct PDec<QMM_Q8_0_R> {
+    // The repacked Q8_0 layout: per k-tile (two GGUF blocks) 64 code bytes
+    // q + 128, then d of both blocks as f32.  Lane half kh reads block kh's
+    // 32 codes at 32kh; step s takes k = 32kh + 8s + sigma(j), the k that
+    // PDec<QMM_Q8_0> gives it, and each weight is the same single rounding of
+    // d * q to f16, so the matrix-core steps see the same operands.
+    static constexpr int NW = 9;
+    static constexpr bool SWAP = true;
+    __device__ static int xpos(int c4) { return PDec<QMM_Q8_0>::xpos(c4); }
+    struct State {};
+    __device__ static void loadb(Rsrc rs, uint32_t roff, int64_t k0, int kh, int, uint32_t (&r)[NW]) {
+        const uint32_t base = (uint32_t)(72 * (k0 / 64));
+        uint32_t q[8], d[1];
+        ldb(rs, roff + 32u * kh, base, q);
+        ldb(rs, roff + 4u * kh, base + 64u, d);
+#pragma unroll
+        for (int i = 0; i < 8; i++) r[i] = q[i];
+        r[8] = d[0];
+    }
+    __device__ static void decode(const uint32_t (&r)[NW], State &, int, int, int64_t, half8 (&f)[4]) {
+        const float d = __builtin_bit_cast(float, r[8]);
+        const float s24 = d * TWO24, n = -128.f * d;  // codes enter as q + 128
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const uint32_t w = r[i];
+            quad(w & 0x00FF00FFu, (w >> 8) & 0x00FF00FFu, s24, n, f[i >> 1], 4 * (i & 1));
+        }
+    }
+};
+
 template <int DT> struct WbDec { using type = PDec<DT>; };
 template <> struct WbDec<QMM_Q6_K> { using type = BDec<QMM_Q6_K>; };
 
@@ -1084,7 +1114,8 @@ static bool aligned_layout(int dtype, int64_t nb) {
     case QMM_Q4_1:
     case QMM_Q4_K:
     case QMM_Q5_K:
-    case QMM_Q6_K_R: return true;
+    case QMM_Q6_K_R:
+    case QMM_Q8_0_R: return true;
     default: return false;
     }
 }
@@ -1192,7 +1223,7 @@ static hipError_t launch_dt(const uint8_t *blob, int64_t M, int64_t K, int64_t N
     case GEMM_K_SK_FM2_64: return launch_sk<DT, 64, 4, 2, 2, 2>(blob, M, K, N, X, Y, st);
     default: break;
     }
-    if constexpr (DT == QMM_Q6_K_R) {
+    if constexpr (DT == QMM_Q6_K_R || DT == QMM_Q8_0_R) {
         return hipErrorInvalidValue;  // no LDS-tile decoder
     } else {
         if (N <= 32) return launch_tile<DT, 128, 32, 1, 4>(blob, M, K, N, X, Y, st, gen);
@@ -1213,16 +1244,21 @@ int gemm_kernel_choice(int dtype, int64_t M, int64_t K, int64_t N) {
     }
 }
 
-// The repacked Q6_K layout runs the register-B and split-K kernels only (it
-// has no LDS-tile decoder): K must give the register-B layout.
-bool gemm_repacked_ok(int64_t K) { return (K % 256) == 0 && (K % (4 * BK)) == 0 && K * 4 * 128 < ((int64_t)1 << 31); }
+// The repacked layouts run the register-B and split-K kernels only (they
+// have no LDS-tile decoder): K must give the register-B layout.
+bool gemm_repacked_ok(int dtype, int64_t K) {
+    return (dtype == QMM_Q6_K || dtype == QMM_Q8_0) && (K % (4 * BK)) == 0 && K * 4 * 128 < ((int64_t)1 << 31);
+}
 
-int gemm_repacked_kernel_choice(int64_t M, int64_t K, int64_t N) { return choice_dt<QMM_Q6_K_R>(M, K, N); }
+int gemm_repacked_kernel_choice(int dtype, int64_t M, int64_t K, int64_t N) {
+    return dtype == QMM_Q6_K ? choice_dt<QMM_Q6_K_R>(M, K, N) : choice_dt<QMM_Q8_0_R>(M, K, N);
+}
 
-hipError_t launch_gemm_repacked(const void *packed, int64_t M, int64_t K, int64_t N, const float *X, float *Y,
-                                hipStream_t st) {
-    if (!gemm_repacked_ok(K)) return hipErrorInvalidValue;
-    return launch_dt<QMM_Q6_K_R>(static_cast<const uint8_t *>(packed), M, K, N, X, Y, st);
+hipError_t launch_gemm_repacked(int dtype, const void *packed, int64_t M, int64_t K, int64_t N, const float *X,
+                                float *Y, hipStream_t st) {
+    if (!gemm_repacked_ok(dtype, K)) return hipErrorInvalidValue;
+    const uint8_t *p = static_cast<const uint8_t *>(packed);
+    return dtype == QMM_Q6_K ? launch_dt<QMM_Q6_K_R>(p, M, K, N, X, Y, st) : launch_dt<QMM_Q8_0_R>(p, M, K, N, X, Y, st);
 }
 
 // The gate/up projection with SwiGLU on the matrix cores: 4 wavefronts x 32

@@ -62,15 +62,15 @@ int gemm_kernel_choice(int dtype, int64_t M, int64_t K, int64_t N);
 hipError_t launch_gemm_mfma(int dtype, const void *blob, int64_t M, int64_t K, int64_t N, const float *X,
                             float *Y, hipStream_t st);
 
-// Q6_K repacked for the GEMM: M rows of K weights from the GGUF blob into the
-// QMM_Q6_K_R layout (K % 256 == 0); and the matrix-core GEMM on it, with the
-// kernel choice of gemm_kernel_choice(QMM_Q6_K, ...) (gemm_repacked_ok: the
-// register-B kernels take K).
-hipError_t launch_repack_q6_k(const void *src, int64_t M, int64_t K, void *dst, hipStream_t st);
-bool gemm_repacked_ok(int64_t K);
-int gemm_repacked_kernel_choice(int64_t M, int64_t K, int64_t N);
-hipError_t launch_gemm_repacked(const void *packed, int64_t M, int64_t K, int64_t N, const float *X, float *Y,
-                                hipStream_t st);
+// Q6_K / Q8_0 repacked for the GEMM: M rows of K weights from the GGUF blob
+// into the QMM_Q6_K_R / QMM_Q8_0_R layout (K % 256 == 0); and the matrix-core
+// GEMM on it, with the kernel choice of gemm_kernel_choice(dtype, ...)
+// (gemm_repacked_ok: a repacked dtype whose K the register-B kernels take).
+hipError_t launch_repack(int dtype, const void *src, int64_t M, int64_t K, void *dst, hipStream_t st);
+bool gemm_repacked_ok(int dtype, int64_t K);
+int gemm_repacked_kernel_choice(int dtype, int64_t M, int64_t K, int64_t N);
+hipError_t launch_gemm_repacked(int dtype, const void *packed, int64_t M, int64_t K, int64_t N, const float *X,
+                                float *Y, hipStream_t st);
 
 // A plain streaming read of `bytes` bytes of buf (at most cus * 4 workgroups,
 // one float per workgroup written to out).

@@ -1,5 +1,5 @@
-// qmm_repack.hip -- load-time repacking of Q6_K weights for the matrix-core
-// GEMM (page "cera 0.5.2 src/backend/cpu.rs", the Q4_0 / Q4_K weight
+// qmm_repack.hip -- load-time repacking of Q6_K and Q8_0 weights for the
+// matrix-core GEMM (page "cera 0.5.2 src/backend/cpu.rs", the Q4_0 / Q4_K weight
 // repacking: a second copy of a prefill weight, built once at load and kept
 // beside the GGUF bytes, laid out for the GEMM's lanes with the per-block
 // scale products baked in; decode keeps reading the original).
@@ -18,6 +18,12 @@
 //
 // One thread per 16-weight sub-block: it reads its 16 low nibbles (ql), 16
 // high-bit pairs (qh), sc[i] and d, and writes 2 x 8 code bytes and 1 scale.
+//
+// Q8_0 (32 weights, 34 bytes: f16 d, int8 q[32]; 2 bytes off a dword on every
+// other block) is repacked per pair of blocks into 72 bytes:
+//   [0, 64)    the 64 codes as q + 128 (unsigned bytes), in order;
+//   [64, 72)   d of both blocks as f32.
+// 1.06 x the source bytes.  One thread per block.
 #include "qmm_device.hpp"
 #include "qmm_internal.hpp"
 
@@ -58,7 +64,23 @@ __global__ void __launch_bounds__(256) repack_q6_k_kernel(const uint8_t *__restr
     *reinterpret_cast<float *>(o + 256 + 4 * i) = dsc;
 }
 
-}  // namespace
+__global__ void __launch_bounds__(256) repack_q8_0_kernel(const uint8_t *__restrict__ src, int64_t nblk,
+                                                          uint8_t *__restrict__ dst) {
+    const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (b >= nblk) return;
+    const uint8_t *p = src + 34 * b;
+    uint32_t w[8];
+#pragma unroll
+    for (int k = 0; k < 8; k++)
+        w[k] = ((uint32_t)p[2 + 4 * k] | ((uint32_t)p[3 + 4 * k] << 8) | ((uint32_t)p[4 + 4 * k] << 16) |
+                ((uint32_t)p[5 + 4 * k] << 24)) ^ 0x80808080u;  // q + 128 in each byte
+    const float d = (float)__builtin_bit_cast(_Float16, (uint16_t)(p[0] | (p[1] << 8)));
+    uint8_t *o = dst + 72 * (b >> 1);
+    const int h = (int)(b & 1);
+    *reinterpret_cast<uint4 *>(o + 32 * h) = uint4{w[0], w[1], w[2], w[3]};
+    *reinterpret_cast<uint4 *>(o + 32 * h + 16) = uint4{w[4], w[5], w[6], w[7]};
+    *reinterpret_cast<float *>(o + 64 + 4 * h) = d;
+}
 
 hipError_t launch_repack_q6_k(const void *src, int64_t M, int64_t K, void *dst, hipStream_t st) {
     const int64_t nsub = M * (K / 256) * 16;
@@ -74,6 +96,30 @@ hipError_t launch_repack_q6_k(const void *src, int64_t M, int64_t K, void *dst, 
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
+}
+
+hipError_t launch_repack_q8_0(const void *src, int64_t M, int64_t K, void *dst, hipStream_t st) {
+    const int64_t nblk = M * (K / 32);
+    const int64_t max_blk = (int64_t)1 << 26;  // even: chunks start on a block pair
+    for (int64_t b0 = 0; b0 < nblk; b0 += max_blk) {
+        const int64_t n = nblk - b0 < max_blk ? nblk - b0 : max_blk;
+        hipLaunchKernelGGL(repack_q8_0_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                           static_cast<const uint8_t *>(src) + b0 * 34, n,
+                           static_cast<uint8_t *>(dst) + (b0 / 2) * 72);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_repack(int dtype, const void *src, int64_t M, int64_t K, void *dst, hipStream_t st) {
+    switch (dtype) {
+    case QMM_Q6_K: return launch_repack_q6_k(src, M, K, dst, st);
+    case QMM_Q8_0: return launch_repack_q8_0(src, M, K, dst, st);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace qmm

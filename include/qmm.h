@@ -298,27 +298,30 @@ int qmm_gemm_q8act_path(int dtype, int64_t M, int64_t K, int64_t N);
  * the Q4_0 / Q4_K weight repacking: a second copy of a prefill weight,
  * built once at load and kept beside the GGUF bytes, laid out for the GEMM
  * with the per-block scale products baked in; decode keeps the original).
- * Q6_K only.  The repacked super-block is 320 bytes (the GGUF one 210):
- * 256 bytes of 6-bit codes, one per weight, in the order the matrix-core
- * lanes read them, then the 16 sub-block scales d * sc[i] as f32.  Every
- * offset is 16-byte aligned and a weight's code is one byte, where the GGUF
- * super-block is 2 bytes off a dword on every other block and splits each
- * code over a nibble and two bits elsewhere.
+ * Q6_K and Q8_0, whose GGUF blocks are 2 bytes off a dword on every other
+ * block.  Every offset of a repacked copy is 16-byte aligned and a weight's
+ * code is one byte, in the order the matrix-core lanes read them:
+ *   Q6_K  320 bytes per 256 weights (GGUF: 210): 256 code bytes q (0..63),
+ *         then the 16 sub-block scales d * sc[i] as f32 (GGUF splits each
+ *         code over a nibble and two bits elsewhere);
+ *   Q8_0  72 bytes per 64 weights (GGUF: 68): 64 code bytes q + 128, then the
+ *         two block scales d as f32.
  *
- * qmm_repack_bytes: bytes of the repacked copy of M x K weights (1.52 x
- *   qmm_blob_bytes); 0 if dtype has no repacked form or the shape is invalid.
+ * qmm_repack_bytes: bytes of the repacked copy of M x K weights (Q6_K 1.52 x,
+ *   Q8_0 1.06 x qmm_blob_bytes); 0 if dtype has no repacked form or the shape
+ *   is invalid (K must be a multiple of 256).
  * qmm_repack: fills `packed` from the GGUF blob (one launch on `stream`).
  *   w_blob  device, 16-B aligned, qmm_blob_bytes(dtype, M, K) bytes
  *   packed  device, 16-B aligned, qmm_repack_bytes(dtype, M, K) bytes;
  *           overwritten; caller-owned, like w_blob
- *   dtype   QMM_Q6_K (any other valid dtype: QMM_ERR_DTYPE)
+ *   dtype   QMM_Q6_K or QMM_Q8_0 (any other valid dtype: QMM_ERR_DTYPE)
  * qmm_gemm_repacked: Y[n][m] = sum_k W[m][k] * X[n][k] from the repacked
  *   copy, on the matrix cores for every N (the f16 class of qmm_gemm: 2e-3 of
  *   sum |w x|).  Where qmm_gemm runs the matrix cores too (qmm_gemm_path 1)
- *   and the row has an even number of super-blocks, Y has exactly qmm_gemm's
- *   bits: each weight is the same single rounding of d * sc * (q - 32) to f16
- *   and every matrix-core step sees the same operands.  K must be a multiple
- *   of 256 below 2^22 (QMM_ERR_SHAPE otherwise); X, Y, N as for qmm_gemm.
+ *   and the row has an even number of blocks, Y has exactly qmm_gemm's bits:
+ *   each weight is the same single rounding of its exact value to f16 and
+ *   every matrix-core step sees the same operands.  K must be a multiple of
+ *   256 below 2^22 (QMM_ERR_SHAPE otherwise); X, Y, N as for qmm_gemm.
  * qmm_gemm_repacked_kernel: which matrix-core kernel it runs (the ids of
  *   qmm_gemm_kernel), or a negative status. */
 int64_t qmm_repack_bytes(int dtype, int64_t M, int64_t K);

@@ -390,7 +390,10 @@ def test_repack_sizes_and_argument_checks():
     L = q.lib()
     assert q.repack_bytes(q.QMM_Q6_K, 3, 512) == 3 * 2 * 320
     assert q.repack_bytes(q.QMM_Q6_K, 14336, 4096) == 14336 * 16 * 320
-    for dt in (q.QMM_Q4_0, q.QMM_Q8_0, q.QMM_Q4_K, q.QMM_Q4_1, q.QMM_Q5_K, 5):
+    assert q.repack_bytes(q.QMM_Q8_0, 3, 512) == 3 * 8 * 72
+    assert q.repack_bytes(q.QMM_Q8_0, 3, 96) == 0  # K not a multiple of 256
+    assert L.qmm_repack(A16, q.QMM_Q8_0, 3, 96, A16, None) == q.QMM_ERR_SHAPE
+    for dt in (q.QMM_Q4_0, q.QMM_Q4_K, q.QMM_Q4_1, q.QMM_Q5_K, 5):
         assert q.repack_bytes(dt, 3, 512) == 0
         assert L.qmm_repack(A16, dt, 3, 512, A16, None) in (q.QMM_ERR_DTYPE,)
     assert q.repack_bytes(q.QMM_Q6_K, 3, 500) == 0
@@ -409,6 +412,7 @@ def test_repacked_kernel_choice_matches_the_gguf_form():
     with an odd number it still runs a register-B kernel."""
     for M, K, N in [(14336, 4096, 512), (4096, 4096, 512), (4096, 4096, 32), (14336, 4096, 32),
                     (4096, 4096, 128), (4096, 4096, 256), (128256, 4096, 9), (1000, 1536, 20)]:
-        assert q.gemm_repacked_kernel(q.QMM_Q6_K, M, K, N) == q.gemm_kernel(q.QMM_Q6_K, M, K, N)
+        for dt in (q.QMM_Q6_K, q.QMM_Q8_0):
+            assert q.gemm_repacked_kernel(dt, M, K, N) == q.gemm_kernel(dt, M, K, N)
     assert q.gemm_kernel(q.QMM_Q6_K, 300, 768, 40) == 0  # the LDS-tile kernel for odd block counts
     assert 0 < q.gemm_repacked_kernel(q.QMM_Q6_K, 300, 768, 40) < 100

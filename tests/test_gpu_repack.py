@@ -1,21 +1,21 @@
-"""The load-time Q6_K repack and the GEMM on the repacked copy.
+"""The load-time Q6_K / Q8_0 repack and the GEMM on the repacked copy.
 
 The pages repack prefill weights once at load into a second, kernel-friendly
 copy kept beside the GGUF bytes (page "cera 0.5.2 src/backend/cpu.rs", the
-Q4_0 / Q4_K weight repacking).  Here Q6_K is repacked for the matrix-core
-GEMM (qmm_repack) and qmm_gemm_repacked runs on that copy.
+Q4_0 / Q4_K weight repacking).  Here Q6_K and Q8_0 are repacked for the
+matrix-core GEMM (qmm_repack) and qmm_gemm_repacked runs on that copy.
 
   * the repacked bytes, bit for bit, against a re-layout written here from the
-    GGUF Q6_K reading (ql / qh / sc / d, the oracle's reading) and the layout
-    qmm.h documents: one code byte per weight at its lane position, then the
-    16 sub-block scales d * sc as f32 (exact products);
+    GGUF readings (Q6_K ql / qh / sc / d and Q8_0 d / q, the oracle's
+    readings) and the layouts qmm.h documents: one code byte per weight at
+    its lane position, then the scales as f32 (exact products);
   * qmm_gemm_repacked against the oracle on the ORIGINAL blob at the
     matrix-core tolerance (2e-3 of sum |w x|), N = 1 .. 513, ragged M;
   * bit for bit against qmm_gemm on the original blob wherever qmm_gemm runs
     the matrix cores with an even number of super-blocks per row (the same
     f16 weights and the same matrix-core steps), over every kernel id;
-  * the hand-built Q6_K edge blocks (negative and subnormal d, sub-scales of
-    both signs) with unit-vector and N(0, 1) activations;
+  * the hand-built edge blocks (negative and subnormal d, Q6_K sub-scales of
+    both signs, Q8_0 codes of -128) with unit-vector and N(0, 1) activations;
   * the full 14336 x 4096 N = 512 shape on sampled rows.
 """
 import numpy as np
@@ -29,7 +29,9 @@ from test_gpu_edge_blocks import golden_blob, unit_and_normal
 
 pytestmark = pytest.mark.gpu
 
-Q6 = q.QMM_Q6_K
+Q6, Q8 = q.QMM_Q6_K, q.QMM_Q8_0
+DTS = [Q6, Q8]
+NAME = {Q6: "Q6_K", Q8: "Q8_0"}
 TAU = 2e-3
 
 
@@ -44,8 +46,8 @@ def to_dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-def relayout(blob, M, K):
-    """The repacked bytes, from the GGUF Q6_K layout: element j of a super-block
+def relayout_q6_k(blob, M, K):
+    """The repacked Q6_K bytes, from the GGUF Q6_K layout: element j of a super-block
     (h = j / 128, g = (j % 128) / 32, l = j % 32) has the low (g < 2) or high
     nibble of ql[64h + 32(g & 1) + l] and bits 2g, 2g+1 of qh[32h + l] as
     bits 4, 5; its scale is sc[j / 16] (int8) times d (f16).  Repacked:
@@ -69,25 +71,42 @@ def relayout(blob, M, K):
     return out.reshape(-1)
 
 
-def gpu_repack(blob, M, K):
-    packed = torch.full((q.repack_bytes(Q6, M, K),), 0xA5, dtype=torch.uint8, device="cuda")
-    q.qmm_repack(to_dev(blob), Q6, M, K, packed)
+def relayout_q8_0(blob, M, K):
+    """The repacked Q8_0 bytes, from the GGUF Q8_0 layout (f16 d, then int8
+    q[32]): per pair of blocks, the 64 codes q + 128 in order, then both d as
+    f32."""
+    npair = M * (K // 64)
+    b = blob.reshape(npair, 2, 34)
+    out = np.zeros((npair, 72), np.uint8)
+    out[:, :64] = (b[:, :, 2:].reshape(npair, 64).view(np.int8).astype(np.int16) + 128).astype(np.uint8)
+    d = b[:, :, 0:2].copy().reshape(npair, 4).view("<f2").astype(np.float32)  # [npair, 2]
+    out[:, 64:] = d.astype("<f4").view(np.uint8)
+    return out.reshape(-1)
+
+
+def relayout(dt, blob, M, K):
+    return relayout_q6_k(blob, M, K) if dt == Q6 else relayout_q8_0(blob, M, K)
+
+
+def gpu_repack(dt, blob, M, K):
+    packed = torch.full((q.repack_bytes(dt, M, K),), 0xA5, dtype=torch.uint8, device="cuda")
+    q.qmm_repack(to_dev(blob), dt, M, K, packed)
     torch.cuda.synchronize()
     return packed
 
 
-def gpu_gemm_repacked(packed, M, K, X):
+def gpu_gemm_repacked(dt, packed, M, K, X):
     N = X.shape[0]
     Y = torch.full((N, M), float("nan"), device="cuda")
-    q.qmm_gemm_repacked(packed, Q6, M, K, N, to_dev(X), Y)
+    q.qmm_gemm_repacked(packed, dt, M, K, N, to_dev(X), Y)
     torch.cuda.synchronize()
     return Y.cpu().numpy()
 
 
-def gpu_gemm(bd, M, K, X):
+def gpu_gemm(dt, bd, M, K, X):
     N = X.shape[0]
     Y = torch.full((N, M), float("nan"), device="cuda")
-    q.qmm_gemm(bd, Q6, M, K, N, to_dev(X), Y)
+    q.qmm_gemm(bd, dt, M, K, N, to_dev(X), Y)
     torch.cuda.synchronize()
     return Y.cpu().numpy()
 
@@ -104,33 +123,34 @@ def check(Yg, Y64, S, label):
         assert ratio[worst] <= TAU, f"{label}: |err|/S = {ratio[worst]:.3g} > {TAU} at flat index {worst}"
 
 
+@pytest.mark.parametrize("dt", DTS, ids=NAME.get)
 @pytest.mark.parametrize("M,K", [(1, 256), (37, 512), (300, 1280), (129, 4096)])
-def test_repack_bytes(M, K):
-    for blob in (make_blob(Q6, M, K, rng_for(1400, M)), golden_blob(Q6, M, K)):
-        assert q.repack_bytes(Q6, M, K) == M * (K // 256) * 320
-        got = gpu_repack(blob, M, K).cpu().numpy()
-        want = relayout(blob, M, K)
+def test_repack_bytes(dt, M, K):
+    for blob in (make_blob(dt, M, K, rng_for(1400, M), q8_full_range=True), golden_blob(dt, M, K)):
+        got = gpu_repack(dt, blob, M, K).cpu().numpy()
+        want = relayout(dt, blob, M, K)
+        assert got.size == want.size == q.repack_bytes(dt, M, K)
         bad = np.flatnonzero(got != want)
-        assert bad.size == 0, f"M={M} K={K}: {bad.size} bytes differ, first at {bad[:5]}"
+        assert bad.size == 0, f"{NAME[dt]} M={M} K={K}: {bad.size} bytes differ, first at {bad[:5]}"
 
 
-def test_repack_many_launches_tail():
-    # more sub-blocks than one launch takes in the chunked launcher is too big
-    # for a test; a row count that leaves a ragged last workgroup is not
-    M, K = 1001, 768  # 3003 super-blocks, 48048 sub-blocks: 187.7 workgroups
-    blob = make_blob(Q6, M, K, rng_for(1401, 0))
-    got = gpu_repack(blob, M, K).cpu().numpy()
-    assert np.array_equal(got, relayout(blob, M, K))
+@pytest.mark.parametrize("dt", DTS, ids=NAME.get)
+def test_repack_ragged_last_workgroup(dt):
+    M, K = 1001, 768  # Q6_K: 48048 sub-blocks, Q8_0: 24024 blocks -- a partial last workgroup
+    blob = make_blob(dt, M, K, rng_for(1401, 0))
+    got = gpu_repack(dt, blob, M, K).cpu().numpy()
+    assert np.array_equal(got, relayout(dt, blob, M, K))
 
 
+@pytest.mark.parametrize("dt", DTS, ids=NAME.get)
 @pytest.mark.parametrize("N", [1, 2, 5, 17, 32, 33, 64, 65, 130, 513])
-def test_gemm_repacked_matches_oracle(N):
+def test_gemm_repacked_matches_oracle(dt, N):
     for i, (M, K) in enumerate([(70, 512), (129, 768), (300, 1024), (97, 2304)]):
-        blob = make_blob(Q6, M, K, rng_for(1410, i))
+        blob = make_blob(dt, M, K, rng_for(1410, i), q8_full_range=True)
         X = make_x(N, K, rng_for(1410, 1000 * N + i))
-        _, Y64, S = oracle.matmul(Q6, blob, M, K, X)
-        Yg = gpu_gemm_repacked(gpu_repack(blob, M, K), M, K, X)
-        check(Yg, Y64, S, f"repacked Q6_K M={M} K={K} N={N}")
+        _, Y64, S = oracle.matmul(dt, blob, M, K, X)
+        Yg = gpu_gemm_repacked(dt, gpu_repack(dt, blob, M, K), M, K, X)
+        check(Yg, Y64, S, f"repacked {NAME[dt]} M={M} K={K} N={N}")
 
 
 # (M, K, N) chosen to reach every matrix-core kernel the repacked GEMM can run
@@ -138,48 +158,52 @@ BITWISE = [(14336, 1024, 512), (4096, 1024, 512), (1000, 1536, 20), (4096, 1024,
            (4096, 1024, 128), (4096, 1024, 256), (777, 2048, 77), (333, 512, 5)]
 
 
-def test_gemm_repacked_reaches_every_kernel():
-    ids = {q.gemm_repacked_kernel(Q6, M, K, N) for M, K, N in BITWISE}
+@pytest.mark.parametrize("dt", DTS, ids=NAME.get)
+def test_gemm_repacked_reaches_every_kernel(dt):
+    ids = {q.gemm_repacked_kernel(dt, M, K, N) for M, K, N in BITWISE}
     assert ids == set(range(1, 8)), ids
 
 
+@pytest.mark.parametrize("dt", DTS, ids=NAME.get)
 @pytest.mark.parametrize("M,K,N", BITWISE)
-def test_gemm_repacked_bitwise_equals_qmm_gemm(M, K, N):
-    assert q.gemm_path(Q6, M, K, N) == 1 and (K // 256) % 2 == 0
-    assert q.gemm_repacked_kernel(Q6, M, K, N) == q.gemm_kernel(Q6, M, K, N)
-    blob = make_blob(Q6, M, K, rng_for(1420, M + N))
+def test_gemm_repacked_bitwise_equals_qmm_gemm(dt, M, K, N):
+    assert q.gemm_path(dt, M, K, N) == 1
+    assert q.gemm_repacked_kernel(dt, M, K, N) == q.gemm_kernel(dt, M, K, N)
+    blob = make_blob(dt, M, K, rng_for(1420, M + N), q8_full_range=True)
     X = make_x(N, K, rng_for(1420, 7 * N + K))
-    Yr = gpu_gemm_repacked(gpu_repack(blob, M, K), M, K, X)
-    Yo = gpu_gemm(to_dev(blob), M, K, X)
-    assert np.array_equal(Yr.view(np.uint32), Yo.view(np.uint32)), f"M={M} K={K} N={N}: bits differ"
+    Yr = gpu_gemm_repacked(dt, gpu_repack(dt, blob, M, K), M, K, X)
+    Yo = gpu_gemm(dt, to_dev(blob), M, K, X)
+    assert np.array_equal(Yr.view(np.uint32), Yo.view(np.uint32)), f"{NAME[dt]} M={M} K={K} N={N}: bits differ"
     rows = np.unique(np.concatenate([np.random.default_rng(M).choice(M, min(M, 40), replace=False), [0, M - 1]]))
-    _, Y64, S = oracle.matmul(Q6, blob, M, K, X, rows=rows)
-    check(Yr[:, rows], Y64, S, f"repacked Q6_K M={M} K={K} N={N}")
+    _, Y64, S = oracle.matmul(dt, blob, M, K, X, rows=rows)
+    check(Yr[:, rows], Y64, S, f"repacked {NAME[dt]} M={M} K={K} N={N}")
 
 
+@pytest.mark.parametrize("dt", DTS, ids=NAME.get)
 @pytest.mark.parametrize("N", [1, 7, 40, 300])
-def test_gemm_repacked_edge_blocks(N):
+def test_gemm_repacked_edge_blocks(dt, N):
     M, K = 97, 2048
     for shift in (0, 5):
-        blob = golden_blob(Q6, M, K, shift)
+        blob = golden_blob(dt, M, K, shift)
         X = unit_and_normal(K, max(2, N - 2), 1430 + N + shift)[:N] if N > 2 else make_x(N, K, rng_for(1430, N))
-        _, Y64, S = oracle.matmul(Q6, blob, M, K, X)
-        Yr = gpu_gemm_repacked(gpu_repack(blob, M, K), M, K, X)
-        check(Yr, Y64, S, f"repacked edge blocks N={N} shift={shift}")
-        if q.gemm_path(Q6, M, K, N) == 1:
-            assert np.array_equal(Yr.view(np.uint32), gpu_gemm(to_dev(blob), M, K, X).view(np.uint32))
+        _, Y64, S = oracle.matmul(dt, blob, M, K, X)
+        Yr = gpu_gemm_repacked(dt, gpu_repack(dt, blob, M, K), M, K, X)
+        check(Yr, Y64, S, f"repacked {NAME[dt]} edge blocks N={N} shift={shift}")
+        if q.gemm_path(dt, M, K, N) == 1:
+            assert np.array_equal(Yr.view(np.uint32), gpu_gemm(dt, to_dev(blob), M, K, X).view(np.uint32))
 
 
-def test_gemm_repacked_full_size():
+@pytest.mark.parametrize("dt", DTS, ids=NAME.get)
+def test_gemm_repacked_full_size(dt):
     M, K, N = 14336, 4096, 512
-    blob = make_blob(Q6, M, K, rng_for(1440, 0))
+    blob = make_blob(dt, M, K, rng_for(1440, 0))
     X = make_x(N, K, rng_for(1440, 1))
-    packed = gpu_repack(blob, M, K)
-    Yr = gpu_gemm_repacked(packed, M, K, X)
-    assert np.array_equal(Yr.view(np.uint32), gpu_gemm(to_dev(blob), M, K, X).view(np.uint32))
+    packed = gpu_repack(dt, blob, M, K)
+    Yr = gpu_gemm_repacked(dt, packed, M, K, X)
+    assert np.array_equal(Yr.view(np.uint32), gpu_gemm(dt, to_dev(blob), M, K, X).view(np.uint32))
     rows = np.unique(np.concatenate([np.random.default_rng(3).choice(M, 48, replace=False), [0, M - 1]]))
-    _, Y64, S = oracle.matmul(Q6, blob, M, K, X, rows=rows)
-    check(Yr[:, rows], Y64, S, "repacked Q6_K 14336x4096 N=512")
+    _, Y64, S = oracle.matmul(dt, blob, M, K, X, rows=rows)
+    check(Yr[:, rows], Y64, S, f"repacked {NAME[dt]} 14336x4096 N=512")
 
 
 def test_repack_argument_errors():
@@ -190,10 +214,11 @@ def test_repack_argument_errors():
     L = q.lib()
     s = torch.cuda.current_stream().cuda_stream
     assert L.qmm_repack(blob.data_ptr(), q.QMM_Q4_K, 8, 512, packed.data_ptr(), s) == q.QMM_ERR_DTYPE
+    assert L.qmm_repack(blob.data_ptr(), Q8, 8, 64, packed.data_ptr(), s) == q.QMM_ERR_SHAPE
     assert L.qmm_repack(blob.data_ptr(), Q6, 8, 500, packed.data_ptr(), s) == q.QMM_ERR_SHAPE
     assert L.qmm_repack(blob.data_ptr(), Q6, 8, 512, packed.data_ptr() + 8, s) == q.QMM_ERR_ALIGN
     assert L.qmm_repack(None, Q6, 8, 512, packed.data_ptr(), s) == q.QMM_ERR_NULL
-    assert L.qmm_gemm_repacked(packed.data_ptr(), q.QMM_Q8_0, 8, 512, 4, X.data_ptr(), Y.data_ptr(), s) == \
+    assert L.qmm_gemm_repacked(packed.data_ptr(), q.QMM_Q4_0, 8, 512, 4, X.data_ptr(), Y.data_ptr(), s) == \
         q.QMM_ERR_DTYPE
     assert L.qmm_gemm_repacked(packed.data_ptr() + 4, Q6, 8, 512, 4, X.data_ptr(), Y.data_ptr(), s) == \
         q.QMM_ERR_ALIGN
