@@ -53,7 +53,7 @@ QMM_READ_PROBE_OUT_FLOATS = 4096
 EXPORTS = ("qmm_gemv", "qmm_gemv_concat", "qmm_gemv_swiglu", "qmm_gemv_argmax", "qmm_gemv_argmax_noalloc", "qmm_gemm", "qmm_gemm_swiglu",
            "qmm_quantize_q8_0", "qmm_gemm_q8act", "qmm_gemv_q8act", "qmm_gemv_concat_q8act",
            "qmm_gemv_swiglu_q8act", "qmm_gemv_argmax_q8act", "qmm_repack_bytes", "qmm_repack", "qmm_gemm_repacked", "qmm_gemm_repacked_kernel",
-           "qmm_gemm_path", "qmm_gemm_q8act_path", "qmm_gemm_kernel", "qmm_read_probe", "qmm_blob_bytes", "qmm_block_elems",
+           "qmm_gemm_path", "qmm_gemm_q8act_path", "qmm_gemm_kernel", "qmm_gemm_swiglu_kernel", "qmm_read_probe", "qmm_blob_bytes", "qmm_block_elems",
            "qmm_block_bytes", "qmm_strerror")
 
 _lib = None
@@ -111,6 +111,8 @@ def lib():
         L.qmm_gemm_path.restype = ci
         L.qmm_gemm_q8act_path.argtypes = [ci, i64, i64, i64]
         L.qmm_gemm_q8act_path.restype = ci
+        L.qmm_gemm_swiglu_kernel.argtypes = [ci, i64, i64, i64]
+        L.qmm_gemm_swiglu_kernel.restype = ci
         L.qmm_gemm_kernel.argtypes = [ci, i64, i64, i64]
         L.qmm_gemm_kernel.restype = ci
         L.qmm_read_probe.argtypes = [vp, i64, vp, vp]
@@ -151,6 +153,11 @@ QMM_KERNEL_GEMV, QMM_KERNEL_GEMV_TOKENS = 100, 101
 def q8act_kernel(dtype: int, M: int, K: int, N: int) -> int:
     """0: qmm_gemm_q8act runs token groups (single-token bits); 1: the int8 matrix cores."""
     return lib().qmm_gemm_q8act_path(dtype, M, K, N)
+
+
+def swiglu_kernel(dtype: int, M: int, K: int, N: int) -> int:
+    """Form qmm_gemm_swiglu runs for these sizes (see include/qmm.h)."""
+    return lib().qmm_gemm_swiglu_kernel(dtype, M, K, N)
 
 
 def gemm_kernel(dtype: int, M: int, K: int, N: int) -> int:

@@ -175,6 +175,14 @@ int qmm_gemm_kernel(int dtype, int64_t M, int64_t K, int64_t N) {
     return qmm::gemm_kernel_choice(dtype, M, K, N);
 }
 
+int qmm_gemm_swiglu_kernel(int dtype, int64_t M, int64_t K, int64_t N) {
+    const int rc = check_shape(dtype, M, K, N);
+    if (rc != QMM_OK) return rc;
+    if (N < mfma_from_n(dtype, M, K)) return qmm::gemv_fused_ok(dtype, K) ? QMM_KERNEL_GEMV : QMM_ERR_SHAPE;
+    if (!qmm::gemm_swiglu_ok(dtype, K)) return QMM_ERR_SHAPE;
+    return qmm::swiglu_tile(M, N);
+}
+
 int qmm_gemm_q8act_path(int dtype, int64_t M, int64_t K, int64_t N) {
     const int rc = check_shape(dtype, M, K, N);
     if (rc != QMM_OK) return rc;

@@ -771,18 +771,26 @@ template <> struct WbDec<QMM_Q6_K> { using type = BDec<QMM_Q6_K>; };
 // weights to all token tiles.
 //
 // SWI (gate/up projection with SwiGLU, page "cera 0.5.2 src/backend/cpu.rs":
-// the fused gate + up + SiLU GEMM dispatch): TM = 64 and each wavefront's
-// two 32-row fragments are the same 32 rows of the gate matrix (blob) and of
-// the up matrix (blob_up); the epilogue writes silu(gate) * up for those 32
-// output rows, so neither projection is ever stored.
+// the fused gate + up + SiLU GEMM dispatch), neither projection ever stored:
+//   TM = 64: each wavefront's two 32-row fragments are the same 32 rows of
+//     the gate matrix (blob) and of the up matrix (blob_up); the epilogue
+//     writes silu(gate) * up for those 32 output rows;
+//   TM = 32 (the wavefront pair form): wavefront w < W/2 computes 32 rows of
+//     the gate matrix and wavefront w + W/2 the same rows of the up matrix,
+//     each the plain kernel's tile; the up tiles go through LDS to their gate
+//     partners, which write silu(gate) * up.  The registers of the plain
+//     8 x 32-row x 128-token tile, where a wavefront holding both fragments
+//     of 128 tokens would not fit two per SIMD.
 template <int DT, int TM, int BN, int WD, int W, int INTERLEAVE, int XD, bool SWI = false>
 __global__ void __launch_bounds__(64 * W) gemm_wb_kernel(const uint8_t *__restrict__ blob,
                                                         const uint8_t *__restrict__ blob_up, int64_t M, int64_t K,
                                                         int64_t N, int64_t row_bytes, const float *__restrict__ X,
                                                         float *__restrict__ Y, int n_mtiles, int n_ntiles) {
     constexpr int FM = TM / 32, FN = BN / 32;
-    constexpr int OT = SWI ? 32 : TM;  // output rows per wavefront
-    static_assert(!SWI || FM == 2, "the SwiGLU form pairs one gate and one up fragment");
+    constexpr bool PAIR = SWI && FM == 1;  // gate and up in two wavefronts
+    constexpr int OT = SWI ? 32 : TM;      // output rows per wavefront
+    constexpr int OW = PAIR ? W / 2 : W;   // wavefronts per workgroup with distinct output rows
+    static_assert(!SWI || FM == 2 || (FM == 1 && W % 2 == 0), "the SwiGLU forms pair a gate and an up fragment");
     constexpr int NT = 64 * W;
     constexpr int NX4 = BN * (BK / 4);          // float4 of X per k-tile
     constexpr int NXF = (NX4 + NT - 1) / NT;    // per thread (the last ones repeat a valid float4)
@@ -796,11 +804,13 @@ __global__ void __launch_bounds__(64 * W) gemm_wb_kernel(const uint8_t *__restri
     const int total = n_mtiles * n_ntiles, b = blockIdx.x, xcd = b & 7, local = b >> 3;
     const int tile = xcd * (total >> 3) + (xcd < (total & 7) ? xcd : (total & 7)) + local;
     const int64_t mt = tile / n_ntiles, nt = tile % n_ntiles;
-    const int64_t n0 = nt * BN, mw = mt * (W * OT) + wave * OT;
+    const int half = PAIR ? wave / OW : 0;  // PAIR: 0 gate, 1 up (wave-uniform)
+    const int64_t n0 = nt * BN, mw = mt * (OW * OT) + (wave % OW) * OT;
     const int64_t nkt = K / BK;
 
     const int64_t wrows = M - mw < 0 ? 0 : (M - mw < OT ? M - mw : OT);
-    const Rsrc wrs = make_rsrc_uniform(blob + (wrows ? mw : 0) * row_bytes, (uint32_t)(wrows * row_bytes));
+    const Rsrc wrs = make_rsrc_uniform((PAIR && half ? blob_up : blob) + (wrows ? mw : 0) * row_bytes,
+                                       (uint32_t)(wrows * row_bytes));
     const Rsrc wrs_up = make_rsrc_uniform((SWI ? blob_up : blob) + (wrows ? mw : 0) * row_bytes,
                                           (uint32_t)(wrows * row_bytes));
     uint32_t roff[FM];
@@ -908,7 +918,36 @@ __global__ void __launch_bounds__(64 * W) gemm_wb_kernel(const uint8_t *__restri
         }
     }
 
-    if constexpr (SWI) {
+    if constexpr (PAIR) {
+        // the up tiles reach their gate partners through the activation
+        // buffer (free after the k-loop's last barrier), two token fragments
+        // at a time: [OW][2][16][64] floats = 32 KB for W = 8
+        static_assert(OW * 2 * 16 * 64 * 4 <= 2 * BN * LDK * 2, "exchange fits the activation buffer");
+        float *ex = reinterpret_cast<float *>(&Xs[0][0]);
+#pragma unroll
+        for (int i0 = 0; i0 < FN; i0 += 2) {
+            if (half) {
+#pragma unroll
+                for (int ii = 0; ii < 2 && i0 + ii < FN; ii++)
+#pragma unroll
+                    for (int v = 0; v < 16; v++)
+                        ex[(((wave - OW) * 2 + ii) * 16 + v) * 64 + lane] = acc[i0 + ii][0][v];
+            }
+            __syncthreads();
+            if (!half) {
+                const int64_t m = mw + (lane & 31);
+#pragma unroll
+                for (int ii = 0; ii < 2 && i0 + ii < FN; ii++)
+#pragma unroll
+                    for (int v = 0; v < 16; v++) {
+                        const int64_t n = n0 + 32 * (i0 + ii) + 8 * (v >> 2) + 4 * kh + (v & 3);
+                        const float u = ex[((wave * 2 + ii) * 16 + v) * 64 + lane];
+                        if (m < M && n < N) Y[n * M + m] = silu(acc[i0 + ii][0][v]) * u;
+                    }
+            }
+            __syncthreads();
+        }
+    } else if constexpr (SWI) {
 #pragma unroll
         for (int i = 0; i < FN; i++) {
             const int64_t m = mw + (lane & 31);
@@ -1143,8 +1182,9 @@ static hipError_t launch_wb(const uint8_t *blob, int64_t M, int64_t K, int64_t N
                             hipStream_t st, const uint8_t *blob_up = nullptr) {
     constexpr int BS = Geo<DT>::BS, BB = Geo<DT>::BB;
     constexpr int OT = SWI ? 32 : TM;
+    constexpr int OW = (SWI && TM == 32) ? W / 2 : W;  // the wavefront pair form: W/2 output row groups
     const int64_t row_bytes = (K / BS) * BB;
-    const int64_t mtiles = (M + W * OT - 1) / (W * OT), ntiles = (N + BN - 1) / BN;
+    const int64_t mtiles = (M + OW * OT - 1) / (OW * OT), ntiles = (N + BN - 1) / BN;
     const int64_t grid = mtiles * ntiles;
     if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((gemm_wb_kernel<DT, TM, BN, WD, W, IL, XD, SWI>), dim3((unsigned)grid), dim3(64 * W), 0, st,
@@ -1179,7 +1219,7 @@ enum {
 //     (4096 x 4096 Q4_K N = 128: 32-row tiles 20.7 vs 23.8 us; N = 256:
 //     64-row tiles 28.6 vs 35.4 us; 14336 x 4096 N = 64: 30.2 vs 36.6 us);
 //   * the buffered kernel with 8 wavefronts x 32 rows x 128 tokens when that
-//     grid nearly fills the chip, else 4 x 32 rows x 64 tokens;
+//     grid gives at least 160 workgroups, else 4 x 32 rows x 64 tokens;
 //   * the LDS-staged kernel when the layout rules the others out (K not a
 //     multiple of 256, odd block counts).
 // A measurement build (QMM_TUNING) takes QMM_GEMM_KERNEL = an id to force
@@ -1205,7 +1245,9 @@ static int choice_dt(int64_t M, int64_t K, int64_t N) {
         // the 64 workgroups leave CUs idle: 20.3 vs 13.6 us)
         return (N <= 32 && mt64 >= 192) ? GEMM_K_SK_FM2 : GEMM_K_SK;
     if (N <= 32) return GEMM_K_WB_4x32;
-    if (((M + 255) / 256) * ((N + 127) / 128) >= 200) return GEMM_K_WB_8x128;
+    // 14336 x 4096 Q4_K: N = 320 81 vs 98 us, N = 384 85 vs 105 us (Q4_0 88
+    // vs 108, Q6_K 155 vs 192); N = 256 66 vs 73 us the other way
+    if (((M + 255) / 256) * ((N + 127) / 128) >= 160) return GEMM_K_WB_8x128;
     return GEMM_K_WB_4x64;
 }
 
@@ -1274,26 +1316,41 @@ static int swiglu_choice() {
     return v;
 }
 
-// Tile for the SwiGLU form (4 wavefronts x 32 output rows; tokens per tile
-// BN), measured on the 14336 x 4096 gate/up pair against two plain GEMMs:
-//   N <= 64:          BN = 32   (Q4_K N = 64: 51.6 vs 71.8 us)
-//   N <= 160:         BN = 64   (N = 128: 66.0 vs 76.8 us)
-//   N <= 320:         BN = 128  (N = 256: 91.8 vs 124.5 us)
-//   N <= 448:         BN = 64   (N = 384: 172 vs 199 us)
-//   beyond:           BN = 128  (N = 512: 201 vs 176 us: the one case where
-//                     two GEMMs plus a separate pass would be faster, given
-//                     scratch for both projections)
-// A measurement build (QMM_TUNING) takes QMM_SWIGLU_KERNEL = 1..4 to force
-// BN = 32 / 64 / 128 / 64 with 8 wavefronts.
+// Tile of the SwiGLU form, measured on the 14336 x 4096 Q4_K gate/up pair
+// (us; two plain GEMMs in brackets) and on 4096 x 4096:
+//   1  4 wavefronts x 32 output rows x 32 tokens, both fragments per wavefront
+//   2  the same with 64 tokens
+//   3  the same with 128 tokens
+//   4  8 wavefronts x 32 output rows x 64 tokens
+//   5  the wavefront pair form: 8 wavefronts, 4 x 32 gate rows and the same
+//      4 x 32 up rows, 128 tokens
+//   N <= 64: 1 (N = 64: 51.6 vs 71.8).  4096 rows: 2 (N = 256: 58 vs 74 with
+//   3, 69 with 5; N = 512: 64 vs 79 with 3, 74 with 5 (77)).  14336 rows:
+//   N <= 128: 2 (N = 128: 67 vs 78 with 5 (78)); above, 5 where its
+//   workgroups fill one round (112 x ceil(N/128) <= 256: N = 192 83 vs 101
+//   with 2, 90 with 3 (116); N = 256 88 vs 93 with 3 (123)) or well over one
+//   (N = 448 166 vs 194 with 2 (157); N = 512 171 vs 182 with 3 (162)), else 2
+//   (N = 320 151 vs 155 with 5 (178); N = 384 158 vs 162 (186)).
+// A measurement build (QMM_TUNING) takes QMM_SWIGLU_KERNEL = 1..5.
+int swiglu_tile(int64_t M, int64_t N) {
+    const int lever = swiglu_choice();
+    if (lever >= 1 && lever <= 5) return lever;
+    if (N <= 64) return 1;
+    if (M >= 12288 && N > 128) {
+        const int64_t t5 = ((M + 127) / 128) * ((N + 127) / 128);  // pair-form workgroups
+        if (t5 <= 256 || t5 > 384) return 5;
+    }
+    return 2;
+}
+
 template <int DT>
 static hipError_t launch_swiglu_dt(const uint8_t *g, const uint8_t *u, int64_t M, int64_t K, int64_t N,
                                    const float *X, float *Y, hipStream_t st) {
-    int choice = swiglu_choice();
-    if (choice < 1 || choice > 4) choice = N <= 64 ? 1 : N <= 160 ? 2 : N <= 320 ? 3 : N <= 448 ? 2 : 3;
-    switch (choice) {
+    switch (swiglu_tile(M, N)) {
     case 1: return launch_wb<DT, 64, 32, 2, 4, 0, 2, true>(g, M, K, N, X, Y, st, u);
     case 2: return launch_wb<DT, 64, 64, 2, 4, 0, 2, true>(g, M, K, N, X, Y, st, u);
     case 3: return launch_wb<DT, 64, 128, 2, 4, 4, 2, true>(g, M, K, N, X, Y, st, u);
+    case 5: return launch_wb<DT, 32, 128, 2, 8, 4, 2, true>(g, M, K, N, X, Y, st, u);
     default: return launch_wb<DT, 64, 64, 2, 8, 0, 2, true>(g, M, K, N, X, Y, st, u);
     }
 }

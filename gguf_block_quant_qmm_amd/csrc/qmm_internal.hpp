@@ -51,6 +51,9 @@ hipError_t launch_gemv_tokens(int dtype, const void *blob, int64_t M, int64_t K,
 
 // Y[N][M] = silu(X Wg^T) * (X Wu^T) on the matrix cores (one launch).
 bool gemm_swiglu_ok(int dtype, int64_t K);
+// Which SwiGLU tile launch_gemm_swiglu runs for these sizes (1..5, see
+// qmm_gemm.hip).
+int swiglu_tile(int64_t M, int64_t N);
 hipError_t launch_gemm_swiglu(int dtype, const void *gate, const void *up, int64_t M, int64_t K, int64_t N,
                               const float *X, float *Y, hipStream_t st);
 

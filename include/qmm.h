@@ -346,6 +346,11 @@ int qmm_gemm_path(int dtype, int64_t M, int64_t K, int64_t N);
 #define QMM_KERNEL_GEMV_TOKENS 101
 int qmm_gemm_kernel(int dtype, int64_t M, int64_t K, int64_t N);
 
+/* Which form qmm_gemm_swiglu launches for these sizes (a diagnostic, like
+ * qmm_gemm_kernel): QMM_KERNEL_GEMV for the per-token f32 path, 1 .. 99 a
+ * matrix-core tile (id inside this library build), < 0 a status code. */
+int qmm_gemm_swiglu_kernel(int dtype, int64_t M, int64_t K, int64_t N);
+
 /* A plain streaming read of `bytes` bytes of buf (a diagnostic: the ceiling
  * that any launch reading the same bytes can reach, which the bench puts each
  * GEMV launch against).  16-byte loads of the GEMV's kind, no arithmetic

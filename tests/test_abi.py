@@ -416,3 +416,17 @@ def test_repacked_kernel_choice_matches_the_gguf_form():
             assert q.gemm_repacked_kernel(dt, M, K, N) == q.gemm_kernel(dt, M, K, N)
     assert q.gemm_kernel(q.QMM_Q6_K, 300, 768, 40) == 0  # the LDS-tile kernel for odd block counts
     assert 0 < q.gemm_repacked_kernel(q.QMM_Q6_K, 300, 768, 40) < 100
+
+
+def test_swiglu_kernel_reports_each_form():
+    """The SwiGLU forms qmm_gemm_swiglu picks (tile ids of qmm_gemm.hip)."""
+    dt = q.QMM_Q4_K
+    assert q.swiglu_kernel(dt, 14336, 4096, 2) == q.QMM_KERNEL_GEMV
+    assert q.swiglu_kernel(dt, 14336, 4096, 40) == 1
+    assert q.swiglu_kernel(dt, 14336, 4096, 128) == 2
+    assert q.swiglu_kernel(dt, 14336, 4096, 200) == 5   # the wavefront pair form, one round
+    assert q.swiglu_kernel(dt, 14336, 4096, 384) == 2
+    assert q.swiglu_kernel(dt, 14336, 4096, 512) == 5
+    assert q.swiglu_kernel(dt, 4096, 4096, 512) == 2
+    assert q.swiglu_kernel(dt, 14336, 100, 512) == q.QMM_ERR_SHAPE
+    assert q.swiglu_kernel(5, 14336, 4096, 512) == q.QMM_ERR_DTYPE

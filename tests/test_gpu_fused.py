@@ -351,6 +351,27 @@ def test_gemm_swiglu(dt):
                     assert torch.equal(o1, out[n]), f"{label}: token {n} differs from qmm_gemv_swiglu"
 
 
+@pytest.mark.parametrize("dt", DTYPES, ids=NAME.get)
+def test_gemm_swiglu_pair_form(dt):
+    """The wavefront pair form (gate rows and the same up rows in two
+    wavefronts, the up tile handed over through LDS) on a tall matrix with a
+    ragged last workgroup, one round of workgroups (N = 200) and more (450)."""
+    M, K = 12301, 1024
+    gate = make_blob(dt, M, K, rng_for(960 + dt, 0))
+    up = make_blob(dt, M, K, rng_for(960 + dt, 1))
+    gd, ud = to_dev(gate), to_dev(up)
+    for N in (200, 450):
+        assert q.swiglu_kernel(dt, M, K, N) == 5
+        X = make_x(N, K, rng_for(960 + dt, N))
+        out = torch.full((N, M), float("nan"), device="cuda")
+        q.qmm_gemm_swiglu(gd, ud, dt, M, K, N, to_dev(X), out)
+        torch.cuda.synchronize()
+        rows = np.unique(np.concatenate([np.arange(4), M - 1 - np.arange(40),
+                                         np.random.default_rng(961 + N).choice(M, 60, replace=False)]))
+        r = oracle.swiglu(dt, gate, up, M, K, X, rows=rows)
+        check_swiglu_tau(out.cpu().numpy()[:, rows], r, 2e-3, f"{NAME[dt]} gemm swiglu pair form N={N}")
+
+
 def test_gemm_swiglu_llama8b_prefill():
     """LLaMA-8B gate/up (14336 x 4096, Q4_K) over 512 tokens, sampled rows."""
     dt, M, K, N = q.QMM_Q4_K, 14336, 4096, 512
