@@ -781,7 +781,12 @@ template <> struct WbDec<QMM_Q6_K> { using type = BDec<QMM_Q6_K>; };
 //     partners, which write silu(gate) * up.  The registers of the plain
 //     8 x 32-row x 128-token tile, where a wavefront holding both fragments
 //     of 128 tokens would not fit two per SIMD.
-template <int DT, int TM, int BN, int WD, int W, int INTERLEAVE, int XD, bool SWI = false>
+//
+// BE: one workgroup barrier every BE k-tiles.  The activation tiles sit in
+// 2 BE LDS buffers and each is stored BE k-tiles ahead of its use, so that a
+// barrier always separates a tile's stores from its reads and its reads from
+// the next store into the same buffer.
+template <int DT, int TM, int BN, int WD, int W, int INTERLEAVE, int XD, bool SWI = false, int BE = 1>
 __global__ void __launch_bounds__(64 * W) gemm_wb_kernel(const uint8_t *__restrict__ blob,
                                                         const uint8_t *__restrict__ blob_up, int64_t M, int64_t K,
                                                         int64_t N, int64_t row_bytes, const float *__restrict__ X,
@@ -797,7 +802,10 @@ __global__ void __launch_bounds__(64 * W) gemm_wb_kernel(const uint8_t *__restri
     constexpr int UNR = 4;  // k-tiles per trip: a Q4_K super-block; K is a multiple of 4 k-tiles
     static_assert(UNR % WD == 0 && UNR % XD == 0, "ring sizes");
     using BD = typename WbDec<DT>::type;
-    __shared__ __attribute__((aligned(16))) _Float16 Xs[2][BN * LDK];
+    // (2 BE buffers indexed by the k-tile's place in the unrolled trip)
+    static_assert((BE == 1 || BE == 2) && BE <= XD, "barrier cadence and activation ring");
+    constexpr int NB = 2 * BE, SD = BE;  // LDS activation buffers; store distance in k-tiles
+    __shared__ __attribute__((aligned(16))) _Float16 Xs[NB][BN * LDK];
 
     const int t = threadIdx.x, lane = t & 63, kh = lane >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -870,16 +878,20 @@ __global__ void __launch_bounds__(64 * W) gemm_wb_kernel(const uint8_t *__restri
     for (int d = 0; d < XD; d++) xload(d, xr[d]);
 #pragma unroll
     for (int j = 0; j < FM; j++) BD::decode(wr[0][j], st[j], kh, 0, 0, bf[0][j]);
-    xstore(xr[0], Xs[0]);
     wload(WD, WD % 4, wr[0]);
-    xload(XD, xr[0]);
+    // the first SD activation tiles into LDS; the ring then holds tiles SD ..
+#pragma unroll
+    for (int d = 0; d < SD; d++) {
+        xstore(xr[d], Xs[d]);
+        xload(d + XD, xr[d]);
+    }
     __syncthreads();
 
     for (int64_t kb = 0; kb < nkt; kb += UNR) {
 #pragma unroll
         for (int u = 0; u < UNR; u++) {
             const int64_t kt = kb + u;
-            const _Float16 *xs = Xs[u & 1];
+            const _Float16 *xs = Xs[u % NB];
             // all A fragments of the k-tile are read up front, so the MFMAs
             // wait for LDS only once per k-tile
             half8 a[BK / 16][FN];
@@ -903,8 +915,9 @@ __global__ void __launch_bounds__(64 * W) gemm_wb_kernel(const uint8_t *__restri
                         BD::decode(wr[(u + 1) % WD][j], st[j], kh, (u + 1) % 4, (kt + 1) * BK, bf[(u + 1) & 1][j]);
                 }
                 if (s == 1) wload(kt + 1 + WD, (u + 1 + WD) % 4, wr[(u + 1) % WD]);
-                if (s == 2) xstore(xr[(u + 1) % XD], Xs[(u + 1) & 1]);
-                if (s == 3) xload(kt + 1 + XD, xr[(u + 1) % XD]);
+                // activation tile kt + SD into LDS, tile kt + SD + XD into its ring slot
+                if (s == 2) xstore(xr[(u + SD) % XD], Xs[(u + SD) % NB]);
+                if (s == 3) xload(kt + SD + XD, xr[(u + SD) % XD]);
             }
             if constexpr (INTERLEAVE > 0) {
                 // one MFMA, then INTERLEAVE vector instructions, repeated
@@ -914,7 +927,7 @@ __global__ void __launch_bounds__(64 * W) gemm_wb_kernel(const uint8_t *__restri
                     __builtin_amdgcn_sched_group_barrier(0x002, INTERLEAVE, 0);
                 }
             }
-            __syncthreads();
+            if (u % BE == BE - 1) __syncthreads();
         }
     }
 
@@ -1177,7 +1190,7 @@ static hipError_t launch_tile(const uint8_t *blob, int64_t M, int64_t K, int64_t
 }
 
 
-template <int DT, int TM, int BN, int WD, int W, int IL = 0, int XD = 2, bool SWI = false>
+template <int DT, int TM, int BN, int WD, int W, int IL = 0, int XD = 2, bool SWI = false, int BE = 1>
 static hipError_t launch_wb(const uint8_t *blob, int64_t M, int64_t K, int64_t N, const float *X, float *Y,
                             hipStream_t st, const uint8_t *blob_up = nullptr) {
     constexpr int BS = Geo<DT>::BS, BB = Geo<DT>::BB;
@@ -1187,7 +1200,7 @@ static hipError_t launch_wb(const uint8_t *blob, int64_t M, int64_t K, int64_t N
     const int64_t mtiles = (M + OW * OT - 1) / (OW * OT), ntiles = (N + BN - 1) / BN;
     const int64_t grid = mtiles * ntiles;
     if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((gemm_wb_kernel<DT, TM, BN, WD, W, IL, XD, SWI>), dim3((unsigned)grid), dim3(64 * W), 0, st,
+    hipLaunchKernelGGL((gemm_wb_kernel<DT, TM, BN, WD, W, IL, XD, SWI, BE>), dim3((unsigned)grid), dim3(64 * W), 0, st,
                        blob, blob_up, M, K, N, row_bytes, X, Y, (int)mtiles, (int)ntiles);
     return hipGetLastError();
 }
@@ -1256,9 +1269,11 @@ static hipError_t launch_dt(const uint8_t *blob, int64_t M, int64_t K, int64_t N
                             hipStream_t st) {
     const bool gen = !aligned_layout(DT, K / Geo<DT>::BS);
     switch (choice_dt<DT>(M, K, N)) {
-    case GEMM_K_WB_8x128: return launch_wb<DT, 32, 128, 2, 8, 4, 2>(blob, M, K, N, X, Y, st);
-    case GEMM_K_WB_4x64: return launch_wb<DT, 32, 64, 4, 4, 0, 4>(blob, M, K, N, X, Y, st);
-    case GEMM_K_WB_4x32: return launch_wb<DT, 32, 32, 4, 4, 0, 4>(blob, M, K, N, X, Y, st);
+    // a barrier every 2 k-tiles (14336 x 4096 N = 512: Q4_K 93 -> 86-93 us,
+    // Q6_K 165 -> 154, Q8_0 124 -> 120; 4096 x 4096 N = 256 35.2 -> 32.6)
+    case GEMM_K_WB_8x128: return launch_wb<DT, 32, 128, 2, 8, 4, 2, false, 2>(blob, M, K, N, X, Y, st);
+    case GEMM_K_WB_4x64: return launch_wb<DT, 32, 64, 4, 4, 0, 4, false, 2>(blob, M, K, N, X, Y, st);
+    case GEMM_K_WB_4x32: return launch_wb<DT, 32, 32, 4, 4, 0, 4, false, 2>(blob, M, K, N, X, Y, st);
     case GEMM_K_SK: return launch_sk<DT, 32, 4, 2, 2>(blob, M, K, N, X, Y, st);
     case GEMM_K_SK_FM2: return launch_sk<DT, 32, 4, 2, 2, 2>(blob, M, K, N, X, Y, st);
     case GEMM_K_SK_64: return launch_sk<DT, 64, 4, 2, 2, 1>(blob, M, K, N, X, Y, st);
@@ -1347,11 +1362,11 @@ template <int DT>
 static hipError_t launch_swiglu_dt(const uint8_t *g, const uint8_t *u, int64_t M, int64_t K, int64_t N,
                                    const float *X, float *Y, hipStream_t st) {
     switch (swiglu_tile(M, N)) {
-    case 1: return launch_wb<DT, 64, 32, 2, 4, 0, 2, true>(g, M, K, N, X, Y, st, u);
-    case 2: return launch_wb<DT, 64, 64, 2, 4, 0, 2, true>(g, M, K, N, X, Y, st, u);
-    case 3: return launch_wb<DT, 64, 128, 2, 4, 4, 2, true>(g, M, K, N, X, Y, st, u);
-    case 5: return launch_wb<DT, 32, 128, 2, 8, 4, 2, true>(g, M, K, N, X, Y, st, u);
-    default: return launch_wb<DT, 64, 64, 2, 8, 0, 2, true>(g, M, K, N, X, Y, st, u);
+    case 1: return launch_wb<DT, 64, 32, 2, 4, 0, 2, true, 2>(g, M, K, N, X, Y, st, u);
+    case 2: return launch_wb<DT, 64, 64, 2, 4, 0, 2, true, 2>(g, M, K, N, X, Y, st, u);
+    case 3: return launch_wb<DT, 64, 128, 2, 4, 4, 2, true, 2>(g, M, K, N, X, Y, st, u);
+    case 5: return launch_wb<DT, 32, 128, 2, 8, 4, 2, true, 2>(g, M, K, N, X, Y, st, u);
+    default: return launch_wb<DT, 64, 64, 2, 8, 0, 2, true, 2>(g, M, K, N, X, Y, st, u);
     }
 }
 
