@@ -88,6 +88,19 @@ def test_gemv_small(dt):
 
 
 @pytest.mark.parametrize("dt", DTYPES, ids=NAME.get)
+def test_gemv_long_rows(dt):
+    # K = 14336 split over 4 wavefronts on 2048+ rows: one row per group and a
+    # short ring for Q4_0 / Q4_1 / Q4_K; uneven row ranges per workgroup
+    K = 14336
+    for i, M in enumerate((2048, 4099, 8193)):
+        blob = make_blob(dt, M, K, rng_for(530 + dt, i))
+        x = make_x(1, K, rng_for(530 + dt, 100 + i))
+        _, Y64, S = oracle.matmul(dt, blob, M, K, x)
+        yg = gpu_gemv(dt, to_dev(blob), M, K, x)
+        check(yg[None, :], Y64, S, 1e-5, f"{NAME[dt]} gemv M={M} K={K}")
+
+
+@pytest.mark.parametrize("dt", DTYPES, ids=NAME.get)
 def test_gemv_rows_per_wavefront(dt):
     # M spans the launch variants: 1..4 row groups per wavefront fetched up
     # front, and the prefetch ring beyond; K = 4096 (independent wavefronts)
