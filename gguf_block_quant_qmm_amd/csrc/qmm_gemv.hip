@@ -1621,6 +1621,9 @@ hipError_t launch_gemv(int dtype, const void *blob_v, int64_t M, int64_t K, cons
     switch (dtype) {
     case QMM_Q4_0:
         if (long_rows) return launch_one<QMM_Q4_0, 1, 2>(blob, M, K, x, y, st, cus);
+        // whole-row wavefronts on up to 8192 rows: one row per wavefront
+        // (4096 x 4096: 4.74 against 4.98 us; 12289 rows and up keep 2)
+        if (fast && K / 64 <= 64 && M <= 8192) return launch_one<QMM_Q4_0, 1, 3>(blob, M, K, x, y, st, cus);
         return fast ? launch_one<QMM_Q4_0, 2, 3>(blob, M, K, x, y, st, cus) : launch_generic<QMM_Q4_0>(blob, M, K, x, y, st, cus);
     case QMM_Q4_1:
         if (long_rows) return launch_one<QMM_Q4_1, 1, 1>(blob, M, K, x, y, st, cus);
