@@ -216,9 +216,11 @@ def test_quantize_then_matmul_on_device():
 def fused_shapes(dt):
     # K <= 4096: whole-row wavefronts; beyond: K-split workgroups (max 16384).
     # 1000 rows at K = 12288 or 14336 give the K-split workgroups several row
-    # groups each (a ring), with x quantized once per workgroup
+    # groups each (a ring), with x quantized once per workgroup; 2051 rows take
+    # one-row groups (Q4_1)
     if bs_of(dt) == 32:
-        return [(1, 64), (5, 128), (67, 1024), (300, 4096), (50, 4160), (33, 14336), (9, 16384), (1000, 14336)]
+        return [(1, 64), (5, 128), (67, 1024), (300, 4096), (50, 4160), (33, 14336), (9, 16384), (1000, 14336),
+                (2051, 14336)]
     # Q6_K needs an even super-block count per row
     return [(1, 512 if dt == q.QMM_Q6_K else 256), (3, 512), (67, 1024), (300, 4096), (50, 8192), (9, 16384),
             (1000, 12288 if dt == q.QMM_Q6_K else 14336)]
