@@ -642,7 +642,9 @@ __device__ __forceinline__ int xslot(int f) { return (f & ~15) | ((f & 15) ^ ((f
 // The activations are fetched into registers before any weight load is
 // issued and written to LDS afterwards: vector-memory loads return in order,
 // so fetching x after the weight prefetch would make the first product wait
-// for every prefetched weight byte.  XPT = float4 per thread (16 U <= XPT *
+// for every prefetched weight byte.  Callers put a scheduling barrier between
+// load_x and the weight fetches: left alone, the compiler moves weight loads
+// ahead of activation loads.  XPT = float4 per thread (16 U <= XPT *
 // blockDim).
 template <int XPT>
 __device__ __forceinline__ void load_x(const float *x, int U, floatx4 (&r)[XPT]) {
@@ -654,12 +656,16 @@ __device__ __forceinline__ void load_x(const float *x, int U, floatx4 (&r)[XPT])
         r[i] = xg[f < last ? f : last];  // unconditional: no divergent load to wait on
     }
 }
+// Stores past the last float4 go to the last one with its own value (load_x
+// read it there): no branch, so the compiler cannot sink a load into one and
+// make its store wait for every load issued after it.
 template <int XPT>
 __device__ __forceinline__ void store_x(const floatx4 (&r)[XPT], int U, floatx4 *xs) {
+    const int last = 16 * U - 1;
 #pragma unroll
     for (int i = 0; i < XPT; i++) {
         const int f = threadIdx.x + i * blockDim.x;
-        if (f < 16 * U) xs[xslot(f)] = r[i];
+        xs[xslot(f < last ? f : last)] = r[i];
     }
 }
 
@@ -891,6 +897,7 @@ __global__ void __launch_bounds__(gemv_block_threads(DT, WAVE_ROWS, NT)) gemv_ke
             const int64_t tk = tok0 + n < ntok ? tok0 + n : ntok - 1;
             load_xa<DT>(xq + tk * K, xsc + tk * (K / 32), active ? u : 0, xa[n]);
         }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int s = 0; s < (FLAT ? D + 1 : D); s++) fetch(g0 + s, buf[s]);
 #pragma unroll
@@ -898,6 +905,7 @@ __global__ void __launch_bounds__(gemv_block_threads(DT, WAVE_ROWS, NT)) gemv_ke
     } else {
         floatx4 xr[WAVE_ROWS ? 4 : 16];
         load_x(x, U, xr);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int s = 0; s < (FLAT ? D + 1 : D); s++) fetch(g0 + s, buf[s]);
         store_x(xr, U, xs);
@@ -1080,6 +1088,7 @@ __global__ void __launch_bounds__(256) gemv_tokens_kernel(const uint8_t *__restr
         floatx4 xr[NT][4];
 #pragma unroll
         for (int j = 0; j < NT; j++) load_x(X + (j < ntok ? j : ntok - 1) * K, U, xr[j]);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int s = 0; s < D; s++) fetch(g0 + s, buf[s]);
 #pragma unroll
