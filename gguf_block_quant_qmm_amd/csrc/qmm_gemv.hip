@@ -635,9 +635,19 @@ __device__ __forceinline__ void load_xa(const int8_t *xq, const float *xsc, int 
     }
 }
 
-// Activations go through LDS with the float4 index XOR-swizzled within groups
-// of 16, so that 16 lanes reading their own unit hit distinct banks.
-__device__ __forceinline__ int xslot(int f) { return (f & ~15) | ((f & 15) ^ ((f >> 4) & 15)); }
+// Activations go through LDS laid out so that the 16 lanes of a read phase,
+// each reading its own unit, hit distinct banks:
+//   PAD    one float4 of padding after every 16 (17 float4s per 64 values):
+//          a lane's 16 reads are one base address plus constant offsets
+//          (whole-row wavefronts, 272 bytes per unit);
+//   else   the float4 index XOR-swizzled within groups of 16 (256 bytes per
+//          unit; per-read address arithmetic).
+template <bool PAD>
+__device__ __forceinline__ int xslot(int f) {
+    if constexpr (PAD) return f + (f >> 4);
+    else return (f & ~15) | ((f & 15) ^ ((f >> 4) & 15));
+}
+constexpr size_t xs_unit_bytes(bool pad) { return pad ? 272 : 256; }
 
 // The activations are fetched into registers before any weight load is
 // issued and written to LDS afterwards: vector-memory loads return in order,
@@ -659,21 +669,27 @@ __device__ __forceinline__ void load_x(const float *x, int U, floatx4 (&r)[XPT])
 // Stores past the last float4 go to the last one with its own value (load_x
 // read it there): no branch, so the compiler cannot sink a load into one and
 // make its store wait for every load issued after it.
-template <int XPT>
+template <bool PAD, int XPT>
 __device__ __forceinline__ void store_x(const floatx4 (&r)[XPT], int U, floatx4 *xs) {
     const int last = 16 * U - 1;
 #pragma unroll
     for (int i = 0; i < XPT; i++) {
         const int f = threadIdx.x + i * blockDim.x;
-        xs[xslot(f < last ? f : last)] = r[i];
+        xs[xslot<PAD>(f < last ? f : last)] = r[i];
     }
 }
 
-template <int DT>
+// With PAD the offsets of a unit's float4s from its first one do not depend
+// on the lane: every unit layout starts at a multiple of 16 or at 4 more, and
+// its float4s lie at offsets o (< 28) with (first % 16) + (o % 16) < 16, so
+// xslot(first + o) = xslot(first) + o + o / 16.
+template <int DT, bool PAD>
 __device__ __forceinline__ void x_from_lds(const floatx4 *xs, int u, float (&xv)[64]) {
+    const int first = Unit<DT>::x4(u, 0);
 #pragma unroll
     for (int i = 0; i < 16; i++) {
-        const floatx4 v = xs[xslot(Unit<DT>::x4(u, i))];
+        const int o = Unit<DT>::x4(u, i) - first;
+        const floatx4 v = PAD ? xs[xslot<true>(first) + o + (o >> 4)] : xs[xslot<false>(Unit<DT>::x4(u, i))];
         xv[4 * i] = v.x; xv[4 * i + 1] = v.y; xv[4 * i + 2] = v.z; xv[4 * i + 3] = v.w;
     }
 }
@@ -908,9 +924,9 @@ __global__ void __launch_bounds__(gemv_block_threads(DT, WAVE_ROWS, NT)) gemv_ke
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int s = 0; s < (FLAT ? D + 1 : D); s++) fetch(g0 + s, buf[s]);
-        store_x(xr, U, xs);
+        store_x<WAVE_ROWS>(xr, U, xs);
         __syncthreads();
-        x_from_lds<DT>(xs, active ? u : 0, xv);
+        x_from_lds<DT, WAVE_ROWS>(xs, active ? u : 0, xv);
     }
 
     // one matrix, whole-row wavefronts: a wavefront's rows are consecutive,
@@ -1092,7 +1108,7 @@ __global__ void __launch_bounds__(256) gemv_tokens_kernel(const uint8_t *__restr
 #pragma unroll
         for (int s = 0; s < D; s++) fetch(g0 + s, buf[s]);
 #pragma unroll
-        for (int j = 0; j < NT; j++) store_x(xr[j], U, xs + j * 16 * U);
+        for (int j = 0; j < NT; j++) store_x<false>(xr[j], U, xs + j * 16 * U);
     }
     __syncthreads();
     float xv[64];
@@ -1107,7 +1123,7 @@ __global__ void __launch_bounds__(256) gemv_tokens_kernel(const uint8_t *__restr
 #pragma unroll
                 for (int j = 0; j < NT; j++) {
                     if (j < ntok) {
-                        x_from_lds<DT>(xs + j * 16 * U, active ? lane : 0, xv);
+                        x_from_lds<DT, false>(xs + j * 16 * U, active ? lane : 0, xv);
                         float acc[R];
 #pragma unroll
                         for (int r = 0; r < R; r++) {
@@ -1406,7 +1422,8 @@ static hipError_t launch_fast(const GemvMats &mats, int64_t K, const float *x, h
     const int64_t nrg = mats.g_lo[GEMV_MAX_MATS];
     // the f32 activations; none for pre-quantized codes; codes + scales when
     // the workgroup quantizes
-    const size_t lds = NT > 0 ? 0 : (NT < 0 ? (size_t)U * 72 : (size_t)U * 256);
+    // whole-row wavefronts (U <= 64) take the padded layout
+    const size_t lds = NT > 0 ? 0 : (NT < 0 ? (size_t)U * 72 : (size_t)U * xs_unit_bytes(U <= 64));
     const unsigned gy = NT > 0 ? (unsigned)((xq8.ntok + NT - 1) / NT) : 1u;
     if (U <= 64) {
         const int64_t waves = gemv_wave_owners(DT, nrg, cus, NT < 0);
