@@ -918,15 +918,35 @@ __global__ void __launch_bounds__(gemv_block_threads(DT, WAVE_ROWS, NT)) gemv_ke
         for (int s = 0; s < (FLAT ? D + 1 : D); s++) fetch(g0 + s, buf[s]);
 #pragma unroll
         for (int n = 0; n < TK; n++) U8<DT>::prep(xa[n]);
+    } else if constexpr (WAVE_ROWS) {
+        // 256 threads x 4 float4 = 64 units, every slot of the padded LDS
+        // layout (sized for 64 units): bounds-checked buffer loads return
+        // zeros past 16 U float4s, stored where no lane reads, so the
+        // addresses are one lane offset plus constants and nothing is clamped
+        static_assert(gemv_block_threads(DT, true, NT) == 256, "4 float4 of x per thread");
+        const Rsrc xrs = make_rsrc(x, (uint32_t)U * 256u);
+        floatx4 xr[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+            xr[i] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(xrs, 16u * t, 4096u * i, 0));
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int s = 0; s < (FLAT ? D + 1 : D); s++) fetch(g0 + s, buf[s]);
+#pragma unroll
+        for (int i = 0; i < 4; i++) xs[xslot<true>(t + 256 * i)] = xr[i];
+        __syncthreads();
+        x_from_lds<DT, true>(xs, active ? u : 0, xv);
+        // the activation reads go out before the wait for the first weights
+        __builtin_amdgcn_sched_barrier(0);
     } else {
-        floatx4 xr[WAVE_ROWS ? 4 : 16];
+        floatx4 xr[16];
         load_x(x, U, xr);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int s = 0; s < (FLAT ? D + 1 : D); s++) fetch(g0 + s, buf[s]);
-        store_x<WAVE_ROWS>(xr, U, xs);
+        store_x<false>(xr, U, xs);
         __syncthreads();
-        x_from_lds<DT, WAVE_ROWS>(xs, active ? u : 0, xv);
+        x_from_lds<DT, false>(xs, active ? u : 0, xv);
     }
 
     // one matrix, whole-row wavefronts: a wavefront's rows are consecutive,
@@ -1422,8 +1442,8 @@ static hipError_t launch_fast(const GemvMats &mats, int64_t K, const float *x, h
     const int64_t nrg = mats.g_lo[GEMV_MAX_MATS];
     // the f32 activations; none for pre-quantized codes; codes + scales when
     // the workgroup quantizes
-    // whole-row wavefronts (U <= 64) take the padded layout
-    const size_t lds = NT > 0 ? 0 : (NT < 0 ? (size_t)U * 72 : (size_t)U * xs_unit_bytes(U <= 64));
+    // whole-row wavefronts (U <= 64) take the padded layout, sized for 64 units
+    const size_t lds = NT > 0 ? 0 : (NT < 0 ? (size_t)U * 72 : (U <= 64 ? 64 * xs_unit_bytes(true) : (size_t)U * 256));
     const unsigned gy = NT > 0 ? (unsigned)((xq8.ntok + NT - 1) / NT) : 1u;
     if (U <= 64) {
         const int64_t waves = gemv_wave_owners(DT, nrg, cus, NT < 0);
