@@ -783,26 +783,37 @@ __device__ __forceinline__ int64_t lo_of(const GemvMats &m, int i) {
 constexpr int gemv_block_threads(int dt, bool wave_rows, int nt) {
     return (wave_rows && nt < 0 && dt != QMM_Q6_K) ? 512 : 256;
 }
-template <int DT, int R, int D, bool WAVE_ROWS, bool FLAT, int MODE, int NT>
-__global__ void __launch_bounds__(gemv_block_threads(DT, WAVE_ROWS, NT)) gemv_kernel(const GemvMats mats, int64_t row_bytes, int U,
+template <int DT, int R, int D, bool WAVE_ROWS, bool FLAT, int MODE, int NT, int PH = 1>
+__global__ void __launch_bounds__(gemv_block_threads(DT, WAVE_ROWS, NT) * PH) gemv_kernel(const GemvMats mats, int64_t row_bytes, int U,
                                                    const float *__restrict__ x, int64_t per_owner, int64_t extra,
                                                    const int8_t *__restrict__ xq, const float *__restrict__ xsc,
                                                    int64_t ntok) {
     static_assert(NT <= 0 || MODE == GEMV_ONE, "several int8 tokens: one matrix");
+    static_assert(PH == 1 || (!WAVE_ROWS && MODE == GEMV_ONE && NT == 0), "row phases: f32 K-split, one matrix");
     constexpr int NL = Unit<DT>::NL;
     constexpr int RR = MODE == GEMV_SWIGLU ? 2 * R : R;  // row dots per row group
     constexpr int TK = NT > 0 ? NT : 1;                  // tokens per row dot
     extern __shared__ __attribute__((aligned(16))) floatx4 xs[];
     constexpr int RED_G = 16;
-    __shared__ float red[WAVE_ROWS ? 1 : RED_G][RR * TK][4];
+    __shared__ float red[PH][WAVE_ROWS ? 1 : RED_G][RR * TK][4];
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6), nwaves = blockDim.x >> 6;
-    const int u = WAVE_ROWS ? lane : t;
+    // K-split: PH row phases of nwaves / PH wavefronts each; a phase is an
+    // owner of its own (the workgroup stages x once for all of them)
+    const int kw = nwaves / PH;                               // wavefronts per row
+    const int phase = WAVE_ROWS ? 0 : wave / kw;
+    const int wk = wave - phase * kw;                         // K slice of the wavefront
+    const int tp = t - phase * 64 * kw;                       // thread within its phase
+    const int u = WAVE_ROWS ? lane : tp;
     const bool active = u < U;
     // owner o gets per_owner row groups, plus one more for the first `extra` owners
-    const int64_t owner = WAVE_ROWS ? (int64_t)blockIdx.x * nwaves + wave : (int64_t)blockIdx.x;
+    const int64_t owner = WAVE_ROWS ? (int64_t)blockIdx.x * nwaves + wave : (int64_t)blockIdx.x * PH + phase;
     const int64_t g0 = owner * per_owner + (owner < extra ? owner : extra);
     const int64_t n = per_owner + (owner < extra ? 1 : 0);
+    // row-group steps: with phases every phase takes the most any owner has
+    // (an owner with one fewer decodes zeros once and stores nothing), so all
+    // wavefronts meet the same barriers
+    const int64_t nloop = PH > 1 ? per_owner + (extra > 0 ? 1 : 0) : n;
     const int64_t nrg = mats.g_lo[GEMV_MAX_MATS];
     const int64_t gend = g0 + n < nrg ? g0 + n : nrg;  // past the wavefront's last row group
     const typename Unit<DT>::Off off = Unit<DT>::lane_off(active ? u : 0);
@@ -939,7 +950,7 @@ __global__ void __launch_bounds__(gemv_block_threads(DT, WAVE_ROWS, NT)) gemv_ke
         // the activation reads go out before the wait for the first weights
         __builtin_amdgcn_sched_barrier(0);
     } else {
-        floatx4 xr[16];
+        floatx4 xr[16 / PH];  // 16 U <= (16 / PH) * blockDim
         load_x(x, U, xr);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -959,12 +970,12 @@ __global__ void __launch_bounds__(gemv_block_threads(DT, WAVE_ROWS, NT)) gemv_ke
         const int64_t row = orow0 + k0 + lane;
         if (lane < cnt && row < mats.M[0]) mats.y[0][row] = obuf;
     };
-    for (int64_t i0 = 0; i0 < n; i0 += D + 1) {
+    for (int64_t i0 = 0; i0 < nloop; i0 += D + 1) {
 #pragma unroll
         for (int s = 0; s <= D; s++) {
             const int64_t i = i0 + s;
             if (!FLAT) fetch(g0 + i + D, buf[(s + D) % (D + 1)]);
-            if (i < n) {
+            if (i < nloop) {
                 float acc[RR * TK];  // [row][token]
 #pragma unroll
                 for (int r = 0; r < RR; r++) {
@@ -1000,17 +1011,18 @@ __global__ void __launch_bounds__(gemv_block_threads(DT, WAVE_ROWS, NT)) gemv_ke
                     const int slot = (int)(i % RED_G);
                     if (lane == 63) {
 #pragma unroll
-                        for (int r = 0; r < RR * TK; r++) red[slot][r][wave] = acc[r];
+                        for (int r = 0; r < RR * TK; r++) red[phase][slot][r][wk] = acc[r];
                     }
-                    if (slot == RED_G - 1 || i == n - 1) {
+                    if (slot == RED_G - 1 || i == nloop - 1) {
                         __syncthreads();
-                        if (t < (slot + 1) * R * TK) {
-                            const int gi = t / (R * TK), r = (t % (R * TK)) / TK, tn = t % TK;
-                            float sum = red[gi][r * TK + tn][0], su = 0.f;
-                            for (int w = 1; w < nwaves; w++) sum += red[gi][r * TK + tn][w];
+                        // groups past the owner's count (phases only) are not stored
+                        if (tp < (slot + 1) * R * TK && i - slot + tp / (R * TK) < n) {
+                            const int gi = tp / (R * TK), r = (tp % (R * TK)) / TK, tn = tp % TK;
+                            float sum = red[phase][gi][r * TK + tn][0], su = 0.f;
+                            for (int w = 1; w < kw; w++) sum += red[phase][gi][r * TK + tn][w];
                             if constexpr (MODE == GEMV_SWIGLU) {
-                                su = red[gi][R + r][0];
-                                for (int w = 1; w < nwaves; w++) su += red[gi][R + r][w];
+                                su = red[phase][gi][R + r][0];
+                                for (int w = 1; w < kw; w++) su += red[phase][gi][R + r][w];
                             }
                             put(g0 + i - slot + gi, r, sum, su, tn);
                         }
@@ -1384,6 +1396,22 @@ static int gemv_waves_lever() {
     }();
     return v;
 }
+// Row phases of a K-split workgroup (f32, one matrix): rows of 2 wavefronts
+// (4097 <= K <= 8192) run 2 phases and 16 wavefronts per CU (4 workgroups)
+// instead of 8 wavefronts in 4 workgroups that each stage x for 2: 4096 x
+// 8192 Q4_0 8.25 -> 7.0 us, Q4_K 9.8 -> 7.4, Q6_K 11.4 -> 9.0, Q8_0 11.8 ->
+// 9.6, 8192 x 8192 Q4_0 13.8 -> 10.3, 4096 x 6144 7.5 -> 6.4.  Longer rows
+// measured no better with phases.  A measurement build takes
+// QMM_GEMV_PHASES = 1, 2 or 4 (at most 16 wavefronts per workgroup).
+static int gemv_phases(int W) {
+    static const int lever = [] {
+        const int n = tuning_lever("QMM_GEMV_PHASES", 0);
+        return (n == 1 || n == 2 || n == 4) ? n : 0;
+    }();
+    int ph = lever ? lever : (W == 2 ? 2 : 1);
+    while (ph > 1 && W * ph > 16) ph /= 2;
+    return ph;
+}
 static int64_t gemv_wave_owners(int dtype, int64_t nrg, int cus, bool q8_in_launch = false) {
     const int lever = gemv_waves_lever();
     if (lever) return std::min<int64_t>(nrg, (int64_t)cus * lever);
@@ -1405,12 +1433,12 @@ struct XQ8 {
 
 // Launch one fast-kernel variant: FLAT with D+1 = the most row groups an
 // owner gets when that is at most 4, else the ring with D row groups ahead.
-template <int DT, int R, int D, bool WAVE_ROWS, int MODE, int NT>
+template <int DT, int R, int D, bool WAVE_ROWS, int MODE, int NT, int PH = 1>
 static void launch_variant(int64_t nmax, dim3 grid, dim3 block, size_t lds, hipStream_t st, const GemvMats &mats,
                            int64_t row_bytes, int U, const float *x, int64_t per_owner, int64_t extra,
                            const XQ8 &xq8) {
 #define QMM_GEMV_LAUNCH(F, DD) \
-    hipLaunchKernelGGL((gemv_kernel<DT, R, DD, WAVE_ROWS, F, MODE, NT>), grid, block, lds, st, mats, row_bytes, U, x, \
+    hipLaunchKernelGGL((gemv_kernel<DT, R, DD, WAVE_ROWS, F, MODE, NT, PH>), grid, block, lds, st, mats, row_bytes, U, x, \
                        per_owner, extra, xq8.q, xq8.s, xq8.ntok)
     // Q4_K: with more than one row group fetched up front the compiler hoists
     // the scale unpacking of all of them and runs out of registers
@@ -1463,13 +1491,30 @@ static hipError_t launch_fast(const GemvMats &mats, int64_t K, const float *x, h
         // Q4_0 10.3 against 12.3 us, Q4_K 10.8-11.1 against 13.0; 4096 x
         // 12288 Q4_K 10.0 against 11.7; Q8_0 and Q6_K measured no better)
         const bool q8_one = NT < 0 && (DT == QMM_Q4_0 || DT == QMM_Q4_K) && W >= 3;
-        const int per_cu = lever ? std::max(1, lever / W) : (q8_one ? 1 : std::max(1, 8 / W));
-        const int64_t grid = std::min<int64_t>(nrg, (int64_t)cus * per_cu);
-        const int64_t per = nrg / grid, extra = nrg % grid;
+        // row phases (f32, one matrix): ph groups of W wavefronts share one
+        // staging of x
+        const int ph = (MODE == GEMV_ONE && NT == 0) ? gemv_phases(W) : 1;
+        const int per_cu = lever ? std::max(1, lever / (W * ph))
+                                 : (q8_one ? 1 : std::max(1, (ph > 1 ? 16 : 8) / (W * ph)));
+        const int64_t grid = std::min<int64_t>((nrg + ph - 1) / ph, (int64_t)cus * per_cu);
+        const int64_t owners = grid * ph, per = nrg / owners, extra = nrg % owners;
         if (MODE == GEMV_ARGMAX && grid > ARGMAX_PARTS) return hipErrorInvalidConfiguration;
         if (grid_out) *grid_out = grid;
-        launch_variant<DT, R, D, false, MODE, NT>(per + (extra ? 1 : 0), dim3((unsigned)grid, gy), dim3(64 * W), lds,
-                                                  st, mats, row_bytes, U, x, per, extra, xq8);
+#define QMM_GEMV_PHASED(P)                                                                                            \
+    launch_variant<DT, R, D, false, MODE, NT, P>(per + (extra ? 1 : 0), dim3((unsigned)grid, gy), dim3(64 * W * P), lds, \
+                                                 st, mats, row_bytes, U, x, per, extra, xq8)
+        if constexpr (MODE == GEMV_ONE && NT == 0) {
+            switch (ph) {
+            case 2: QMM_GEMV_PHASED(2); break;
+#ifdef QMM_TUNING
+            case 4: QMM_GEMV_PHASED(4); break;
+#endif
+            default: QMM_GEMV_PHASED(1); break;
+            }
+        } else {
+            QMM_GEMV_PHASED(1);
+        }
+#undef QMM_GEMV_PHASED
     } else {
         if constexpr (MODE != GEMV_ONE || NT != 0) return hipErrorNotSupported;
         const int64_t M = mats.M[0];

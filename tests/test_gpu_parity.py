@@ -101,6 +101,20 @@ def test_gemv_long_rows(dt):
 
 
 @pytest.mark.parametrize("dt", DTYPES, ids=NAME.get)
+def test_gemv_row_phases(dt):
+    # rows of two wavefronts (4097 <= K <= 8192): two row phases share each
+    # workgroup's staging of x; few rows leave phases with one group fewer
+    # than others, or none (they decode zeros and store nothing)
+    for K in (6144, 8192):
+        for i, M in enumerate((1, 5, 130, 4099)):
+            blob = make_blob(dt, M, K, rng_for(540 + dt, 10 * i + K // 2048))
+            x = make_x(1, K, rng_for(540 + dt, 100 + 10 * i + K // 2048))
+            _, Y64, S = oracle.matmul(dt, blob, M, K, x)
+            yg = gpu_gemv(dt, to_dev(blob), M, K, x)
+            check(yg[None, :], Y64, S, 1e-5, f"{NAME[dt]} gemv M={M} K={K}")
+
+
+@pytest.mark.parametrize("dt", DTYPES, ids=NAME.get)
 def test_gemv_rows_per_wavefront(dt):
     # M spans the launch variants: 1..4 row groups per wavefront fetched up
     # front, and the prefetch ring beyond; K = 4096 (independent wavefronts)
