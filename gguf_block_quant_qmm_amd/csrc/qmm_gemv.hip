@@ -1732,44 +1732,40 @@ hipError_t launch_gemv(int dtype, const void *blob_v, int64_t M, int64_t K, cons
 
 // ------------------------------------------------------ read ceiling ----
 // A plain streaming read of a buffer (the ceiling a launch that reads the same
-// bytes can reach): 16-byte bounds-checked buffer loads in a coalesced
-// grid-stride loop, four in flight per thread, folded into one value per workgroup so that no
-// load is dead.  The loads are the GEMV's own kind, with none of its decode.
+// bytes can reach), in the fastest pattern measured for a plain read: every
+// workgroup reads whole 32 KB pieces, eight 16-byte non-temporal loads per
+// thread in flight (each load instruction of a wavefront 1 KB in a row),
+// pieces spread over at most QMM_READ_PROBE_OUT_FLOATS / 4 workgroups.  Each
+// wavefront folds what it read into one value (a cross-lane XOR, no LDS and
+// no barrier) so that no load is dead.  Loads past the end are bounds-checked
+// zeros.
 __global__ void __launch_bounds__(256) read_probe_kernel(const uint8_t *__restrict__ buf, int64_t bytes,
                                                          float *__restrict__ out) {
-    const int64_t chunk = (int64_t)1 << 30;  // bytes per buffer resource
-    // In 16-byte pieces: each of a thread's four loads is one grid stride
-    // apart, so every load instruction of a wavefront reads 1 KB in a row.
-    const int64_t stride = (int64_t)gridDim.x * 256;
-    const int64_t tid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    constexpr int64_t window = (int64_t)1 << 30;  // bytes per buffer resource
+    constexpr uint32_t piece = 32768;
     uint32_t acc = 0;
-    for (int64_t base = 0; base < bytes; base += chunk) {
-        const int64_t n = bytes - base < chunk ? bytes - base : chunk;
-        const int64_t n16 = (n + 15) / 16;
+    for (int64_t base = 0; base < bytes; base += window) {
+        const int64_t n = bytes - base < window ? bytes - base : window;
         const Rsrc rs = make_rsrc(buf + base, (uint32_t)n);
-        for (int64_t i = tid; i < n16; i += 4 * stride) {
-            u32x4_t v[4];
+        const uint32_t pieces = (uint32_t)((n + piece - 1) / piece);
+        for (uint32_t p = blockIdx.x; p < pieces; p += gridDim.x) {
+            u32x4_t v[8];
 #pragma unroll
-            for (int u = 0; u < 4; u++)  // past n the bounds check returns zeros
-                v[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)(16 * (i + u * stride)), 0, 0);
+            for (int u = 0; u < 8; u++)
+                v[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, p * piece + 4096u * u + 16u * threadIdx.x, 0,
+                                                              2 /* non-temporal */);
 #pragma unroll
-            for (int u = 0; u < 4; u++) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+            for (int u = 0; u < 8; u++) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
         }
     }
-    __shared__ uint32_t red[256];
-    red[threadIdx.x] = acc;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        uint32_t a = 0;
-        for (int i = 0; i < 256; i++) a ^= red[i];
-        out[blockIdx.x] = __uint_as_float(a);
-    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, m, 64);
+    if ((threadIdx.x & 63) == 0) out[4 * blockIdx.x + (threadIdx.x >> 6)] = __uint_as_float(acc);
 }
 
-hipError_t launch_read_probe(const void *buf, int64_t bytes, float *out, hipStream_t st, int cus) {
-    const int64_t per_sweep = 256 * 64;  // bytes per workgroup per loop trip
-    int64_t grid = std::min<int64_t>(std::min<int64_t>((int64_t)cus * 4, QMM_READ_PROBE_OUT_FLOATS),
-                                     (bytes + per_sweep - 1) / per_sweep);
+hipError_t launch_read_probe(const void *buf, int64_t bytes, float *out, hipStream_t st, int) {
+    const int64_t first = bytes < ((int64_t)1 << 30) ? bytes : ((int64_t)1 << 30);
+    int64_t grid = std::min<int64_t>(QMM_READ_PROBE_OUT_FLOATS / 4, (first + 32767) / 32768);
     grid = std::max<int64_t>(grid, 1);
     hipLaunchKernelGGL(read_probe_kernel, dim3((unsigned)grid), dim3(256), 0, st,
                        static_cast<const uint8_t *>(buf), bytes, out);

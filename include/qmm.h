@@ -353,8 +353,11 @@ int qmm_gemm_swiglu_kernel(int dtype, int64_t M, int64_t K, int64_t N);
 
 /* A plain streaming read of `bytes` bytes of buf (a diagnostic: the ceiling
  * that any launch reading the same bytes can reach, which the bench puts each
- * GEMV launch against).  16-byte loads of the GEMV's kind, no arithmetic
- * beyond a fold; one float per workgroup is written to out.
+ * GEMV launch against).  Non-temporal 16-byte loads, each wavefront
+ * instruction reading 1 KB in a row, eight per thread in flight, no
+ * arithmetic beyond a fold; one float per wavefront (at most
+ * QMM_READ_PROBE_OUT_FLOATS) is written to out, and the XOR of those folds is
+ * the XOR of the buffer's dwords.
  *   buf     device, 16-B aligned, `bytes` readable bytes (1 .. 2^40)
  *   out     device f32 [QMM_READ_PROBE_OUT_FLOATS], 4-B aligned; clobbered */
 #define QMM_READ_PROBE_OUT_FLOATS 4096
