@@ -32,6 +32,13 @@ Subcommands (run from the repository root):
            dispatch (summed over the device) of the dispatches whose kernel
            name matches REGEX, with the mean dispatch duration.
 
+  sweep    --log <bench --sweep output> --out <file.md>
+           Markdown tables of the JSON lines `bench.py --sweep` prints, one
+           table per workload.
+
+  spec     --log <bench --spec-verify output> --out <file.md>
+           Markdown table of the JSON lines `bench.py --spec-verify` prints.
+
   mfma     --csv <counter_collection.csv> --key REGEX --flops F --simds S
            Matrix-core utilisation of the dispatches whose kernel name matches
            REGEX, from a run collecting SQ_VALU_MFMA_BUSY_CYCLES,
@@ -262,6 +269,66 @@ def _valu(args):
               f"| {100 * t_hi / us:.0f}-{100 * t_lo / us:.0f} % |")
 
 
+def _sweep(args):
+    rows = [json.loads(l) for l in open(args.log) if l.startswith("{")]
+    out = ["# qmm_gemm over N = 1 .. 512: every dtype at 4096x4096, and the single-configuration workloads", "",
+           "Commands (from the repository root): `python3 bench.py --sweep > <log>`, then",
+           "`python3 -m gguf_block_quant_qmm_amd.profiling sweep --log <log> --out <this file>`.", "",
+           "Each figure is the median (and min) per call over 5 spans of 10 calls, each span after a GPU-side spin that "
+           "keeps the",
+           "queue ahead of the host; the weights rotate over >= 1 GiB of copies so that every call reads them from HBM.",
+           "`path`: f32-gemv = the GEMV's f32 arithmetic for every token (kernel id 100: one launch per token, 101: up "
+           "to 4",
+           "tokens per weight read), f16-mfma = the matrix cores (ids 0-7 of qmm_gemm_kernel). `repacked`: "
+           "qmm_gemm_repacked",
+           "on the qmm_repack copy (Q6_K, Q8_0; always the matrix cores).", ""]
+    cur = None
+    for d in rows:
+        if d["workload"] != cur:
+            cur = d["workload"]
+            out += ["", f"## {cur} ({d['dtype']}, M={d['M']}, K={d['K']})", "",
+                    "| N | path | kernel | us median | us min | weight GB/s | TFLOP/s | repacked us (kernel) |",
+                    "|---:|---|---:|---:|---:|---:|---:|---:|"]
+        r = d.get("repacked")
+        rp = f"{r['us_median']:.2f} ({r['kernel_id']})" if r else ""
+        out.append(f"| {d['N']} | {d['path']} | {d['kernel_id']} | {d['us_median']:.2f} | {d['us_min']:.2f} | "
+                   f"{d['weight_GBps']:.0f} | {d['TFLOPs']:.1f} | {rp} |")
+    text = "\n".join(out) + "\n"
+    if args.out:
+        open(args.out, "w").write(text)
+    else:
+        print(text, end="")
+
+
+def _spec(args):
+    rows = [json.loads(l) for l in open(args.log) if l.startswith("{")]
+    out = ["# Verifying N drafted positions on the Q6_K LM head (128256 x 4096): per-row GEMVs against one call", "",
+           "Commands (from the repository root): `python3 bench.py --spec-verify > <log>`, then",
+           "`python3 -m gguf_block_quant_qmm_amd.profiling spec --log <log> --out <this file>`.", "",
+           "Per N: N separate qmm_gemv calls; one qmm_gemm call (below the crossover the GEMV arithmetic for every "
+           "token,",
+           "several tokens per weight read, each token with qmm_gemv's bits; above it the matrix cores); and the int8 "
+           "form",
+           "(qmm_quantize_q8_0 of the N positions + one qmm_gemm_q8act). Each figure is the mean per call over the "
+           "timed steps",
+           "on rotated weight copies (three copies of the 431 MB head).", "",
+           "| N | per-row GEMVs us | one qmm_gemm us | its path | weight GB/s of the one call | int8: quantize + "
+           "qmm_gemm_q8act us |",
+           "|---:|---:|---:|---|---:|---:|"]
+    argmax = None
+    for d in rows:
+        out.append(f"| {d['N']} | {d['per_row_us']:.1f} | {d['batched_us']:.1f} | {d['batched_path']} | "
+                   f"{d['batched_weight_GBps']:.0f} | {d['int8_quantize_plus_q8act_us']:.1f} |")
+        argmax = d.get("argmax_us", argmax)
+    if argmax is not None:
+        out += ["", f"Greedy argmax over the head's outputs (qmm_gemv_argmax, N = 1): {argmax:.1f} us."]
+    text = "\n".join(out) + "\n"
+    if args.out:
+        open(args.out, "w").write(text)
+    else:
+        print(text, end="")
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd_name", required=True)
@@ -307,9 +374,15 @@ def main(argv=None):
     v.add_argument("--name", action="append", help="GRID=label (grid size in threads)")
     v.add_argument("--simds", type=int, default=1024)
     v.add_argument("--ghz", type=float, nargs=2, default=(2.1, 2.4), help="clock range (low high)")
+    w = sub.add_parser("sweep")
+    w.add_argument("--log", required=True)
+    w.add_argument("--out")
+    e = sub.add_parser("spec")
+    e.add_argument("--log", required=True)
+    e.add_argument("--out")
     a = ap.parse_args(argv)
     {"copy": _copy, "gemm": _gemm, "counters": _counters, "stats": _stats, "traffic": _traffic, "mfma": _mfma,
-     "valu": _valu}[a.cmd_name](a)
+     "valu": _valu, "sweep": _sweep, "spec": _spec}[a.cmd_name](a)
 
 
 if __name__ == "__main__":
