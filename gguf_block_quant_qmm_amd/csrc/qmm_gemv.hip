@@ -723,13 +723,22 @@ __device__ __forceinline__ void x_from_lds(const floatx4 *xs, int u, float (&xv)
 //   GEMV_SWIGLU  R rows of the gate matrix and the same R rows of the up
 //                matrix; out = silu(W_gate x) * (W_up x) (same page, the
 //                fused gate + up GEMV with in-register SwiGLU).
+//   GEMV_PAIR    two matrices of equal M (the concatenated call's gate + up
+//                case): a group holds R rows of the first and the same R rows
+//                of the second, as GEMV_SWIGLU, and both sums are stored
+//                (y_0 = W_0 x, y_1 = W_1 x, the single-matrix bits).  Reading
+//                the two matrices' rows side by side was measured faster than
+//                running them one after the other (2 x 14336 x 4096 Q4_0:
+//                13.8 against 15.2 us).
 //   GEMV_ARGMAX  R rows of one matrix; nothing is stored per row: every
 //                workgroup writes the best (value, row) of its rows to
 //                part[blockIdx.x] and gemv_argmax_finish picks the overall
 //                winner (same page, the greedy argmax GEMV that returns the
 //                index without storing the logits).  The values compared are
 //                the single-matrix kernel's f32 sums, bit for bit.
-enum { GEMV_ONE = 0, GEMV_CONCAT = 1, GEMV_SWIGLU = 2, GEMV_ARGMAX = 3 };
+enum { GEMV_ONE = 0, GEMV_CONCAT = 1, GEMV_SWIGLU = 2, GEMV_ARGMAX = 3, GEMV_PAIR = 4 };
+// modes whose row group holds R rows of each of two matrices
+constexpr bool gemv_two_mats(int mode) { return mode == GEMV_SWIGLU || mode == GEMV_PAIR; }
 constexpr int GEMV_MAX_MATS = 4;
 
 struct GemvMats {
@@ -791,7 +800,7 @@ __global__ void __launch_bounds__(gemv_block_threads(DT, WAVE_ROWS, NT) * PH) ge
     static_assert(NT <= 0 || MODE == GEMV_ONE, "several int8 tokens: one matrix");
     static_assert(PH == 1 || (!WAVE_ROWS && MODE == GEMV_ONE && NT == 0), "row phases: f32 K-split, one matrix");
     constexpr int NL = Unit<DT>::NL;
-    constexpr int RR = MODE == GEMV_SWIGLU ? 2 * R : R;  // row dots per row group
+    constexpr int RR = gemv_two_mats(MODE) ? 2 * R : R;  // row dots per row group
     constexpr int TK = NT > 0 ? NT : 1;                  // tokens per row dot
     extern __shared__ __attribute__((aligned(16))) floatx4 xs[];
     constexpr int RED_G = 16;
@@ -830,7 +839,7 @@ __global__ void __launch_bounds__(gemv_block_threads(DT, WAVE_ROWS, NT) * PH) ge
         const Rsrc rs = make_rsrc(base + lg * R * row_bytes, (uint32_t)(rows * row_bytes));
 #pragma unroll
         for (int r = 0; r < R; r++) Unit<DT>::load(rs, (uint32_t)(r * row_bytes), off, b[r]);
-        if constexpr (MODE == GEMV_SWIGLU) {
+        if constexpr (gemv_two_mats(MODE)) {
             const Rsrc ru = make_rsrc(mats.blob[1] + lg * R * row_bytes, (uint32_t)(rows * row_bytes));
 #pragma unroll
             for (int r = 0; r < R; r++) Unit<DT>::load(ru, (uint32_t)(r * row_bytes), off, b[R + r]);
@@ -853,6 +862,12 @@ __global__ void __launch_bounds__(gemv_block_threads(DT, WAVE_ROWS, NT) * PH) ge
         } else if constexpr (MODE == GEMV_SWIGLU) {
             const int64_t row = g * R + r;
             if (row < mats.M[0]) mats.y[0][row] = silu(v) * vu;
+        } else if constexpr (MODE == GEMV_PAIR) {
+            const int64_t row = g * R + r;
+            if (row < mats.M[0]) {
+                mats.y[0][row] = v;
+                mats.y[1][row] = vu;
+            }
         } else {
             const int mi = MODE == GEMV_CONCAT ? mat_of(mats, g) : 0;
             const int64_t row = (g - (MODE == GEMV_CONCAT ? lo_of(mats, mi) : 0)) * R + r;
@@ -1002,7 +1017,7 @@ __global__ void __launch_bounds__(gemv_block_threads(DT, WAVE_ROWS, NT) * PH) ge
                         for (int r = 0; r < R; r++)
 #pragma unroll
                             for (int tn = 0; tn < TK; tn++)
-                                put(g0 + i, r, acc[r * TK + tn], acc[MODE == GEMV_SWIGLU ? R + r : r], tn);
+                                put(g0 + i, r, acc[r * TK + tn], acc[gemv_two_mats(MODE) ? R + r : r], tn);
                     }
                 } else {
                     // partial sums of up to RED_G row groups wait in LDS; one
@@ -1020,7 +1035,7 @@ __global__ void __launch_bounds__(gemv_block_threads(DT, WAVE_ROWS, NT) * PH) ge
                             const int gi = tp / (R * TK), r = (tp % (R * TK)) / TK, tn = tp % TK;
                             float sum = red[phase][gi][r * TK + tn][0], su = 0.f;
                             for (int w = 1; w < kw; w++) sum += red[phase][gi][r * TK + tn][w];
-                            if constexpr (MODE == GEMV_SWIGLU) {
+                            if constexpr (gemv_two_mats(MODE)) {
                                 su = red[phase][gi][R + r][0];
                                 for (int w = 1; w < kw; w++) su += red[phase][gi][R + r][w];
                             }
@@ -1567,6 +1582,13 @@ static hipError_t launch_mats(int n, const void *const *blobs, const int64_t *Ms
     return launch_fast<DT, R, D, MODE, NT>(m, K, x, st, cus, grid_out);
 }
 
+// A measurement build takes QMM_GEMV_PAIR = 0 to run two equal matrices
+// through the one-after-the-other concatenation instead.
+static bool gemv_pair_lever() {
+    static const bool v = tuning_lever("QMM_GEMV_PAIR", 1) != 0;
+    return v;
+}
+
 bool gemv_fused_ok(int dtype, int64_t K) {
     const int64_t bs = (dtype == QMM_Q4_K || dtype == QMM_Q5_K || dtype == QMM_Q6_K) ? 256 : 32;
     return fast_layout_ok(dtype, K / bs) && (K % 64) == 0 && K / 64 <= 256;
@@ -1582,6 +1604,18 @@ hipError_t launch_gemv_concat(int n, const void *const *blobs, const int64_t *Ms
             if (e != hipSuccess) return e;
         }
         return hipSuccess;
+    }
+    if (n == 2 && Ms[0] == Ms[1] && gemv_pair_lever()) {
+        // two matrices of one shape (gate + up): their rows side by side
+        switch (dtype) {
+        case QMM_Q4_0: return launch_mats<QMM_Q4_0, 1, 3, GEMV_PAIR>(2, blobs, Ms, K, x, ys, st, cus);
+        case QMM_Q4_1: return launch_mats<QMM_Q4_1, 1, 3, GEMV_PAIR>(2, blobs, Ms, K, x, ys, st, cus);
+        case QMM_Q8_0: return launch_mats<QMM_Q8_0, 1, 2, GEMV_PAIR>(2, blobs, Ms, K, x, ys, st, cus);
+        case QMM_Q4_K: return launch_mats<QMM_Q4_K, 1, 3, GEMV_PAIR>(2, blobs, Ms, K, x, ys, st, cus);
+        case QMM_Q5_K: return launch_mats<QMM_Q5_K, 1, 2, GEMV_PAIR>(2, blobs, Ms, K, x, ys, st, cus);
+        case QMM_Q6_K: return launch_mats<QMM_Q6_K, 1, 2, GEMV_PAIR>(2, blobs, Ms, K, x, ys, st, cus);
+        default: return hipErrorInvalidValue;
+        }
     }
     switch (dtype) {
     case QMM_Q4_0: return launch_mats<QMM_Q4_0, 2, 3, GEMV_CONCAT>(n, blobs, Ms, K, x, ys, st, cus);
@@ -1977,10 +2011,14 @@ hipError_t launch_gemv_q8in(int mode, int n, const void *const *blobs, const int
 #define QMM_Q8IN(DT, R, D, RS, DS)                                                                            \
     switch (mode) {                                                                                         \
     case GEMV_ONE: return launch_mats<DT, R, D, GEMV_ONE, -1>(1, blobs, Ms, K, x, ys, st, cus);            \
-    case GEMV_CONCAT: return launch_mats<DT, R, D, GEMV_CONCAT, -1>(n, blobs, Ms, K, x, ys, st, cus);      \
+    case GEMV_CONCAT:                                                                                       \
+        if (pair) return launch_mats<DT, RS, DS, GEMV_PAIR, -1>(2, blobs, Ms, K, x, ys, st, cus);          \
+        return launch_mats<DT, R, D, GEMV_CONCAT, -1>(n, blobs, Ms, K, x, ys, st, cus);                    \
     case GEMV_SWIGLU: return launch_mats<DT, RS, DS, GEMV_SWIGLU, -1>(2, blobs, Ms, K, x, ys, st, cus);    \
     default: return hipErrorInvalidValue;                                                                   \
     }
+    // two matrices of one shape (gate + up) side by side, as the f32 concat
+    const bool pair = mode == GEMV_CONCAT && n == 2 && Ms[0] == Ms[1] && gemv_pair_lever();
     // Q4_1 rows split over 3+ wavefronts on 2048+ rows: one row per group
     // (4096 x 14336: 12.9 -> 10.7 us; Q4_0 and Q4_K, one workgroup per CU,
     // measured best with two)

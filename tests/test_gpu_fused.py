@@ -92,6 +92,27 @@ def test_concat_small(dt):
             check_f32(ys[i].cpu().numpy()[None, :], Y64, S, label)
 
 
+@pytest.mark.parametrize("dt", DTYPES, ids=NAME.get)
+def test_concat_equal_pair(dt):
+    """Two matrices of one shape (the gate + up case) run side by side in one
+    launch: ragged M, whole-row and K-split rows; bitwise against qmm_gemv and
+    against the oracle."""
+    bs = bs_of(dt)
+    cases = [(1, 4 * bs * (4 if bs == 32 else 1)), (7, 1024), (130, 4096), (1001, 8192), (77, 16384)]
+    for c, (M, K) in enumerate(cases):
+        blobs = [make_blob(dt, M, K, rng_for(730 + dt, 10 * c + i)) for i in range(2)]
+        x = make_x(1, K, rng_for(730 + dt, 1000 + c))
+        bd, xd = [to_dev(b) for b in blobs], to_dev(x.reshape(-1))
+        ys = [torch.full((M,), float("nan"), device="cuda") for _ in range(2)]
+        q.qmm_gemv_concat(bd, dt, [M, M], K, xd, ys)
+        torch.cuda.synchronize()
+        for i in range(2):
+            label = f"{NAME[dt]} pair case {c} matrix {i} M={M} K={K}"
+            assert torch.equal(ys[i], gemv(dt, bd[i], M, K, xd)), f"{label}: bits differ from qmm_gemv"
+            _, Y64, S = oracle.matmul(dt, blobs[i], M, K, x)
+            check_f32(ys[i].cpu().numpy()[None, :], Y64, S, label)
+
+
 @pytest.mark.parametrize("layout", ["gate_up", "qkv"])
 def test_concat_llama8b_shapes(layout):
     """Q4_0, K = 4096: gate + up (2 x 14336 rows) and q, k, v (4096 + 1024 + 1024

@@ -307,8 +307,7 @@ def test_gemv_q8act_special_activations(dt):
 @pytest.mark.parametrize("dt", DTYPES, ids=NAME.get)
 def test_gemv_concat_q8act(dt):
     K = 4 * bs_of(dt) * (4 if bs_of(dt) == 32 else 1)
-    for K in (K, 8192):
-        Ms = [300, 77, 1]
+    for K, Ms in ((K, [300, 77, 1]), (8192, [300, 77, 1]), (K, [300, 300]), (8192, [129, 129])):
         blobs = [to_dev(make_blob(dt, M, K, rng_for(970 + dt, j))) for j, M in enumerate(Ms)]
         x_d = to_dev(make_x(1, K, rng_for(970 + dt, 9)).reshape(-1))
         ys = [torch.full((M,), float("nan"), device="cuda") for M in Ms]
