@@ -975,10 +975,14 @@ __global__ void __launch_bounds__(gemv_block_threads(DT, WAVE_ROWS, NT) * PH) ge
         x_from_lds<DT, false>(xs, active ? u : 0, xv);
     }
 
-    // one matrix, whole-row wavefronts: a wavefront's rows are consecutive,
-    // so their sums are parked one per lane and written 64 at a time with one
-    // coalesced store (single-lane 4-byte stores are partial-line writes)
-    constexpr bool BATCH = WAVE_ROWS && MODE == GEMV_ONE && NT <= 1;
+    // one matrix, whole-row wavefronts with a ring of row groups: a
+    // wavefront's rows are consecutive, so their sums are parked one per lane
+    // and written 64 at a time with one coalesced store (single-lane 4-byte
+    // stores are partial-line writes).  Wavefronts owning at most D + 1
+    // groups (FLAT) store from lane 63 instead: the parking costs ~15 VALU
+    // instructions per row and saves little on one or two rows (14336 x 4096
+    // Q4_0 9.4 -> 9.1 us, 4096 x 4096 4.5 -> 4.4 us).
+    constexpr bool BATCH = WAVE_ROWS && MODE == GEMV_ONE && NT <= 1 && !FLAT;
     float obuf = 0.f;
     const int64_t orow0 = g0 * R;  // first row of the wavefront's range
     auto flush = [&](int64_t k0, int cnt) {  // rows orow0 + k0 + [0, cnt) from lanes [0, cnt)
