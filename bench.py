@@ -235,17 +235,17 @@ def main():
             lambda c: q.qmm_gemv_concat([copies[1][c % R], copies[2][c % R]], dg, [Mg, Mg], Kg, xs[1], gate_up_ys,
                                         stream=stream), gu_bytes, probe_copies=gu_probe)
         del gu_probe
-        per_matrix["gate+up swiglu"] = time_calls(
+        per_matrix["gate+up swiglu"] = leg(
             lambda c: q.qmm_gemv_swiglu(copies[1][c % R], copies[2][c % R], dg, Mg, Kg, xs[1], swiglu_y, stream=stream),
             gu_bytes)
         for i, (name, dt, M, K, _) in enumerate(mats):
-            per_matrix[name + " q8act"] = time_calls(
+            per_matrix[name + " q8act"] = leg(
                 lambda c, i=i, dt=dt, M=M, K=K: q.qmm_gemv_q8act(copies[i][c % R], dt, M, K, xs[i], ys[i], stream=stream),
                 copies[i][0].numel())
-        per_matrix["gate+up concat q8act"] = time_calls(
+        per_matrix["gate+up concat q8act"] = leg(
             lambda c: q.qmm_gemv_concat_q8act([copies[1][c % R], copies[2][c % R]], dg, [Mg, Mg], Kg, xs[1], gate_up_ys,
                                               stream=stream), gu_bytes)
-        per_matrix["gate+up swiglu q8act"] = time_calls(
+        per_matrix["gate+up swiglu q8act"] = leg(
             lambda c: q.qmm_gemv_swiglu_q8act(copies[1][c % R], copies[2][c % R], dg, Mg, Kg, xs[1], swiglu_y,
                                               stream=stream), gu_bytes)
 
@@ -308,8 +308,15 @@ def main():
             del scop, sblob
         torch.cuda.empty_cache()
 
-    # the decode step again, as 5 spans (per-step median and min)
+    # the decode step again, as 5 spans (per-step median and min), and the
+    # other forms of the layer the same way
     dec_med, dec_min = spans(lambda c: step_fused(c % R))
+    var_med = {}
+    if not args.headline_only:
+        for key, fn in (("decode_unfused", step_unfused), ("decode_swiglu", step_swiglu), ("decode_q8act", step_q8act)):
+            med, mn = spans(lambda c, fn=fn: fn(c % R))
+            var_med[key] = {"us_per_step_median_of_5_spans": round(med, 3), "us_per_step_min_of_5_spans": round(mn, 3),
+                            "GB/s_median": round(step_bytes / (med * 1e-6) / 1e9, 1)}
 
     def layer_rate(span):
         if span is None:
@@ -417,10 +424,10 @@ def main():
             "decode_step_us_median_of_5_spans": round(dec_med, 3),
             "decode_step_us_min_of_5_spans": round(dec_min, 3),
             "decode_GBps_median_of_5_spans": round(step_bytes / (dec_med * 1e-6) / 1e9, 1),
-            "decode_unfused": {"launches": 4, **(layer_rate(span_unf) or {})},
-            "decode_swiglu": {"launches": 3, **(layer_rate(span_swi) or {}),
+            "decode_unfused": {"launches": 4, **(layer_rate(span_unf) or {}), **var_med.get("decode_unfused", {})},
+            "decode_swiglu": {"launches": 3, **(layer_rate(span_swi) or {}), **var_med.get("decode_swiglu", {}),
                               "note": "gate/up through qmm_gemv_swiglu (outputs silu(g)*u instead of g and u)"},
-            "decode_q8act": {"launches": 3, **(layer_rate(span_q8) or {}),
+            "decode_q8act": {"launches": 3, **(layer_rate(span_q8) or {}), **var_med.get("decode_q8act", {}),
                              "note": "int8 activations: qmm_gemv_q8act (q_proj, down) and qmm_gemv_concat_q8act "
                                      "(gate+up), each quantizing x to Q8_0 inside the launch; integer block dots, "
                                      "different numbers from the f32 path"},
