@@ -1415,13 +1415,14 @@ static int gemv_waves_lever() {
     }();
     return v;
 }
-// Row phases of a K-split workgroup (f32, one matrix): rows of 2 wavefronts
-// (4097 <= K <= 8192) run 2 phases and 16 wavefronts per CU (4 workgroups)
-// instead of 8 wavefronts in 4 workgroups that each stage x for 2: 4096 x
-// 8192 Q4_0 8.25 -> 7.0 us, Q4_K 9.8 -> 7.4, Q6_K 11.4 -> 9.0, Q8_0 11.8 ->
-// 9.6, 8192 x 8192 Q4_0 13.8 -> 10.3, 4096 x 6144 7.5 -> 6.4.  Longer rows
-// measured no better with phases.  A measurement build takes
-// QMM_GEMV_PHASES = 1, 2 or 4 (at most 16 wavefronts per workgroup).
+// Row phases of a K-split workgroup (f32, one matrix).  Rows of 2 wavefronts
+// (4097 <= K <= 8192) run 2 phases: 4 workgroups of 4 wavefronts per CU, each
+// staging x once for both phases (16 wavefronts per CU), instead of 4
+// workgroups of 2 wavefronts (8 per CU): 4096 x 8192 Q4_0 8.25 -> 7.0 us,
+// Q4_K 9.8 -> 7.4, Q6_K 11.4 -> 9.0, Q8_0 11.8 -> 9.6, 8192 x 8192 Q4_0
+// 13.8 -> 10.3, 4096 x 6144 7.5 -> 6.4.  Longer rows measured no better with
+// phases.  A measurement build takes QMM_GEMV_PHASES = 1, 2 or 4 (at most 16
+// wavefronts per workgroup).
 static int gemv_phases(int W) {
     static const int lever = [] {
         const int n = tuning_lever("QMM_GEMV_PHASES", 0);
