@@ -125,7 +125,19 @@ int64_t mfma_from_n(int dtype, int64_t M, int64_t K) {
     }();
     if (lever) return lever;
     if (qmm::gemv_tokens_ok(dtype, K)) {
-        if (dtype == QMM_Q4_K || dtype == QMM_Q5_K) return 3;
+        // Up to 4096 rows the matrix-core kernels have few tiles and the GEMV
+        // arithmetic (4 tokens per weight read, one launch per 4 tokens) stays
+        // ahead longer (K = 4096, f32 against matrix cores): Q4_K 4096 rows N =
+        // 3 / 4 8.2 / 9.6 against 10.0 us, 2048 rows 6.1 / 6.8 against 9.8;
+        // Q6_K 4096 rows N = 5 / 7 14.8 / 17.9 against 18.7, 2048 rows N = 5 /
+        // 7 10.8 / 12.9 against 18.1; Q4_0 2048 rows N = 5 / 6 9.2 / 9.9
+        // against 10.8; Q8_0 2048 rows N = 7 12.4 against 12.8.
+        const bool small = M <= 4096, tiny = M <= 2048;
+        if (dtype == QMM_Q4_K) return small ? 5 : 3;
+        if (dtype == QMM_Q5_K) return 3;
+        if (dtype == QMM_Q6_K) return small ? 8 : 5;
+        if (tiny && dtype == QMM_Q4_0) return 7;
+        if (tiny && dtype == QMM_Q8_0) return 8;
         // tall Q4_1 (>= 192 two-fragment row tiles, where the small-N GEMM
         // halves its activation traffic): the matrix cores win from N = 4
         // (14336 x 4096: 21.2 vs 22.9-23.1 us)

@@ -92,11 +92,23 @@ def test_gemm_path_selection():
     # below the crossover every token gets the GEMV's f32 arithmetic
     assert q.gemm_path(q.QMM_Q4_K, 14336, 4096, 1) == 0
     # K <= 4096: several tokens per weight read, crossover 5 (Q4_0, Q8_0, Q6_K) or 3 (Q4_K)
+    # on tall matrices, later on short ones (few matrix-core tiles)
     assert q.gemm_path(q.QMM_Q4_K, 14336, 4096, 2) == 0
     assert q.gemm_path(q.QMM_Q4_K, 14336, 4096, 3) == 1
+    assert q.gemm_path(q.QMM_Q4_K, 4096, 4096, 4) == 0
+    assert q.gemm_path(q.QMM_Q4_K, 4096, 4096, 5) == 1
     for dt in (q.QMM_Q4_0, q.QMM_Q8_0, q.QMM_Q6_K):
+        assert q.gemm_path(dt, 14336, 4096, 4) == 0
+        assert q.gemm_path(dt, 14336, 4096, 5) == 1
+    for dt in (q.QMM_Q4_0, q.QMM_Q8_0):
         assert q.gemm_path(dt, 4096, 4096, 4) == 0
         assert q.gemm_path(dt, 4096, 4096, 5) == 1
+    assert q.gemm_path(q.QMM_Q6_K, 4096, 4096, 7) == 0
+    assert q.gemm_path(q.QMM_Q6_K, 4096, 4096, 8) == 1
+    assert q.gemm_path(q.QMM_Q4_0, 2048, 4096, 6) == 0
+    assert q.gemm_path(q.QMM_Q4_0, 2048, 4096, 7) == 1
+    assert q.gemm_path(q.QMM_Q8_0, 2048, 4096, 7) == 0
+    assert q.gemm_path(q.QMM_Q8_0, 2048, 4096, 8) == 1
     assert q.gemm_path(q.QMM_Q6_K, 128256, 4096, 4) == 0
     # K > 4096: one GEMV launch per token, crossover 3 (Q4_0, Q6_K) or 2 (Q8_0, Q4_K)
     assert q.gemm_path(q.QMM_Q4_0, 4096, 14336, 2) == 0
