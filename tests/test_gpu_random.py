@@ -124,6 +124,27 @@ def test_random_fused(dt):
 
 
 @pytest.mark.parametrize("dt", DTYPES, ids=NAME.get)
+def test_random_pair(dt):
+    """Two matrices of one shape through qmm_gemv_concat (the paired form):
+    random M and K, each output the bits of its own qmm_gemv."""
+    rng = np.random.default_rng(4550 + dt)
+    bs = BS[dt]
+    for case in range(6):
+        K = bs * int(rng.integers(1, (16384 // bs) + 1))
+        M = int(rng.integers(1, 3000))
+        blobs = [make_blob(dt, M, K, rng_for(4650 + dt, 10 * case + i)) for i in range(2)]
+        x = make_x(1, K, rng_for(4750 + dt, case))
+        bds, xd = [dev(b) for b in blobs], dev(x.reshape(-1))
+        ys = [torch.full((M,), float("nan"), device="cuda") for _ in range(2)]
+        q.qmm_gemv_concat(bds, dt, [M, M], K, xd, ys)
+        for i in range(2):
+            ref = torch.empty(M, device="cuda")
+            q.qmm_gemv(bds[i], dt, M, K, xd, ref)
+            torch.cuda.synchronize()
+            assert torch.equal(ys[i], ref), f"{NAME[dt]} pair case {case} M={M} K={K} matrix {i}: bits differ"
+
+
+@pytest.mark.parametrize("dt", DTYPES, ids=NAME.get)
 def test_random_q8act(dt):
     """Random shapes through the int8-activation entry points: the quantizer
     bit-exact with the oracle's, qmm_gemm_q8act within 1e-5 of Splus, and the
